@@ -1,0 +1,202 @@
+"""Python access to the reference decoder in ``oracle.c``.
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The HIP library never imports this
+package and this package never imports the HIP library.
+
+The shared object is built by ``build()`` with gcc in strict IEEE mode
+(``-ffp-contract=off -fno-fast-math``): every operation in ``oracle.c`` is one
+binary32 rounding, in the order written there.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+STRICT_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(out: str = LIB, extra_flags: list[str] | None = None) -> str:
+    """Compile oracle.c into a shared object (``extra_flags`` replaces nothing,
+    it is appended: tests use it to build a deliberately contracted copy)."""
+    cmd = ["gcc", *STRICT_FLAGS, *(extra_flags or []), SRC, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True, cwd=HERE)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+class OrcConfig(C.Structure):
+    _fields_ = [
+        ("dim", C.c_int32), ("n_layers", C.c_int32), ("n_heads", C.c_int32),
+        ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("hidden_dim", C.c_int32),
+        ("vocab_size", C.c_int32), ("tied_embeddings", C.c_int32), ("weight_dtype", C.c_int32),
+        ("rope_theta", C.c_float), ("norm_eps", C.c_float),
+    ]
+
+
+def config_of(shape) -> OrcConfig:
+    """OrcConfig from a synth.ModelShape (same field order)."""
+    return OrcConfig(*shape.as_tuple())
+
+
+_F = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_I = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_U8 = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+_U16 = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
+
+
+def load(path: str = LIB):
+    if not os.path.exists(path):
+        build(path)
+    lib = C.CDLL(path)
+    P = C.POINTER(OrcConfig)
+    sig = {
+        "orc_widen_bf16": (C.c_float, [C.c_uint16]),
+        "orc_widen_bf16_array": (None, [_U16, _F, C.c_size_t]),
+        "orc_matvec": (None, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, _F, _F]),
+        "orc_rmsnorm": (None, [_F, _F, C.c_int32, C.c_float, _F]),
+        "orc_rope_angles": (None, [C.c_int32, C.c_int32, C.c_float, _F, _F]),
+        "orc_rope_apply": (None, [_F, C.c_int32, _F, _F]),
+        "orc_attend": (None, [_F, _F, _F, C.c_int32, C.c_int32, _F, _F]),
+        "orc_silu_mul": (C.c_float, [C.c_float, C.c_float]),
+        "orc_argmax": (C.c_int32, [_F, C.c_int32]),
+        "orc_n_tensors": (C.c_int32, [P]),
+        "orc_tensor_offsets": (C.c_size_t, [P, C.POINTER(C.c_size_t), C.c_int32]),
+        "orc_cache_index": (C.c_size_t, [P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                         C.c_int32, C.c_int32]),
+        "orc_forward": (C.c_int32, [P, _U8, _F, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                    C.c_int32, _F]),
+        "orc_decode_step": (C.c_int32, [P, _U8, _F, C.c_int32, C.c_int32, _I, _I, _I, _F]),
+        "orc_generate": (C.c_int32, [P, _U8, _F, C.c_int32, C.c_int32, C.c_int32, _I, C.c_int32,
+                                     C.c_int32, C.c_int32, _I, C.c_void_p, C.POINTER(C.c_int64)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = load()
+    return _lib
+
+
+# ---- thin numpy-level helpers ------------------------------------------------
+
+def matvec(W: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """W: float32 or uint16 (bf16 bits) [n_out][n_in]; x float32 [n_in]."""
+    W = np.ascontiguousarray(W)
+    wd = 1 if W.dtype == np.uint16 else 0
+    if wd == 0:
+        W = W.astype(np.float32, copy=False)
+    y = np.zeros(W.shape[0], np.float32)
+    lib().orc_matvec(W.ctypes.data, wd, W.shape[0], W.shape[1],
+                     np.ascontiguousarray(x, np.float32), y)
+    return y
+
+
+def rmsnorm(x, g, eps):
+    y = np.zeros(len(x), np.float32)
+    lib().orc_rmsnorm(np.ascontiguousarray(x, np.float32), np.ascontiguousarray(g, np.float32),
+                      len(x), eps, y)
+    return y
+
+
+def rope_angles(pos, head_dim, theta):
+    c = np.zeros(head_dim // 2, np.float32)
+    s = np.zeros(head_dim // 2, np.float32)
+    lib().orc_rope_angles(pos, head_dim, theta, c, s)
+    return c, s
+
+
+def rope_apply(v, pos, theta):
+    v = np.array(v, np.float32)
+    c, s = rope_angles(pos, len(v), theta)
+    lib().orc_rope_apply(v, len(v), c, s)
+    return v
+
+
+def attend(q, K, V):
+    K = np.ascontiguousarray(K, np.float32)
+    Vv = np.ascontiguousarray(V, np.float32)
+    n, D = K.shape
+    probs = np.zeros(n, np.float32)
+    out = np.zeros(D, np.float32)
+    lib().orc_attend(np.ascontiguousarray(q, np.float32), K, Vv, n, D, probs, out)
+    return out, probs
+
+
+def argmax(v):
+    v = np.ascontiguousarray(v, np.float32)
+    return int(lib().orc_argmax(v, len(v)))
+
+
+def tensor_offsets(shape):
+    cfg = config_of(shape)
+    n = lib().orc_n_tensors(C.byref(cfg))
+    off = (C.c_size_t * n)()
+    total = lib().orc_tensor_offsets(C.byref(cfg), off, n)
+    return list(off), int(total)
+
+
+def cache_size(shape, B, T):
+    return shape.n_layers * 2 * B * shape.n_kv_heads * T * shape.head_dim
+
+
+class Model:
+    """The reference decoder over one host weight arena and one host cache."""
+
+    def __init__(self, shape, arena: np.ndarray, B: int, T: int):
+        self.shape, self.B, self.T = shape, B, T
+        self.cfg = config_of(shape)
+        self.arena = np.ascontiguousarray(arena, np.uint8)
+        self.cache = np.zeros(cache_size(shape, B, T), np.float32)
+
+    def cache_view(self):
+        s = self.shape
+        return self.cache.reshape(s.n_layers, 2, self.B, s.n_kv_heads, self.T, s.head_dim)
+
+    def forward(self, b, pos, token):
+        logits = np.zeros(self.shape.vocab_size, np.float32)
+        r = lib().orc_forward(C.byref(self.cfg), self.arena, self.cache, self.B, self.T, b, pos,
+                              int(token), logits)
+        if r < 0:
+            raise ValueError(f"orc_forward failed ({r})")
+        return r, logits
+
+    def decode_step(self, lengths: np.ndarray, tok_in: np.ndarray):
+        """Returns (tok_out, logits [B][V]); lengths (int32) advance in place."""
+        B, V = self.B, self.shape.vocab_size
+        tok_out = np.zeros(B, np.int32)
+        logits = np.zeros(B * V, np.float32)
+        r = lib().orc_decode_step(C.byref(self.cfg), self.arena, self.cache, B, self.T, lengths,
+                                  np.ascontiguousarray(tok_in, np.int32), tok_out, logits)
+        if r < 0:
+            raise ValueError(f"orc_decode_step failed ({r})")
+        return tok_out, logits.reshape(B, V)
+
+    def generate(self, b, prompt, n_new, uncached=False, want_logits=True):
+        V = self.shape.vocab_size
+        toks = np.zeros(n_new, np.int32)
+        logits = np.zeros(n_new * V, np.float32) if want_logits else None
+        passes = C.c_int64(0)
+        r = lib().orc_generate(C.byref(self.cfg), self.arena, self.cache, self.B, self.T, b,
+                               np.ascontiguousarray(prompt, np.int32), len(prompt), n_new,
+                               1 if uncached else 0, toks,
+                               logits.ctypes.data if logits is not None else None,
+                               C.byref(passes))
+        if r < 0:
+            raise ValueError(f"orc_generate failed ({r})")
+        return toks, (logits.reshape(n_new, V) if logits is not None else None), passes.value

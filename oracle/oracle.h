@@ -1,0 +1,77 @@
+/*
+ * oracle.h -- reference decoder for the single-token Llama decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow CPU definition that the
+ * HIP library is checked against.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the product path never does.  It
+ * shares no code, header or table with the HIP library.
+ *
+ * All arithmetic is IEEE binary32, one rounding per operation, in the order
+ * the functions below state, with no fused multiply-add (build with
+ * -ffp-contract=off).  exp, sin, cos and pow are evaluated in binary64 and
+ * rounded once to binary32.
+ */
+#ifndef DS_ORACLE_H
+#define DS_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+typedef struct {
+    int32_t dim, n_layers, n_heads, n_kv_heads, head_dim, hidden_dim, vocab_size;
+    int32_t tied_embeddings;
+    int32_t weight_dtype; /* ORC_F32 or ORC_BF16 for matrices; gains are fp32 */
+    float rope_theta, norm_eps;
+} orc_config;
+
+/* ---- primitives ------------------------------------------------------- */
+float orc_widen_bf16(uint16_t h);
+void orc_widen_bf16_array(const uint16_t* src, float* dst, size_t n);
+void orc_matvec(const void* W, int32_t wdtype, int32_t n_out, int32_t n_in,
+                const float* x, float* y);
+void orc_rmsnorm(const float* x, const float* g, int32_t n, float eps, float* y);
+void orc_rope_angles(int32_t pos, int32_t head_dim, float theta, float* c, float* s);
+void orc_rope_apply(float* v, int32_t head_dim, const float* c, const float* s);
+void orc_attend(const float* q, const float* K, const float* V, int32_t n, int32_t head_dim,
+                float* probs, float* out);
+float orc_silu_mul(float a, float u);
+int32_t orc_argmax(const float* v, int32_t n);
+
+/* ---- arena and cache layout ------------------------------------------ */
+int32_t orc_n_tensors(const orc_config* c);
+size_t orc_tensor_offsets(const orc_config* c, size_t* off, int32_t n);
+size_t orc_cache_index(const orc_config* c, int32_t B, int32_t T, int32_t layer, int32_t kv,
+                       int32_t b, int32_t g, int32_t t);
+
+/* ---- the model -------------------------------------------------------- */
+/* One position of sequence b: reads token, writes K/V rows at pos into the
+ * (L,2,B,Hkv,T,D) fp32 cache, writes V logits, returns the greedy token, or
+ * a negative value on a bad argument. */
+int32_t orc_forward(const orc_config* c, const uint8_t* arena, float* cache, int32_t B,
+                    int32_t T, int32_t b, int32_t pos, int32_t token, float* logits);
+
+/* Advance every sequence by one position: lengths[b] is the position that
+ * tok_in[b] is fed at; on return lengths[b] is one larger. */
+int32_t orc_decode_step(const orc_config* c, const uint8_t* arena, float* cache, int32_t B,
+                        int32_t T, int32_t* lengths, const int32_t* tok_in, int32_t* tok_out,
+                        float* logits);
+
+/* Greedy generation for sequence b from an empty slot.  mode 0 = cached
+ * (prompt once, then one position per new token); mode 1 = uncached (the
+ * slot is cleared and every position recomputed for every new token).
+ * out_logits (n_new x V) may be NULL.  *passes counts forward positions. */
+int32_t orc_generate(const orc_config* c, const uint8_t* arena, float* cache, int32_t B,
+                     int32_t T, int32_t b, const int32_t* prompt, int32_t n_prompt,
+                     int32_t n_new, int32_t mode, int32_t* out_tokens, float* out_logits,
+                     int64_t* passes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
