@@ -1,0 +1,196 @@
+"""Decode-step benchmark on one MI355X.
+
+Default workload: the 135M-shaped Llama (dim 576, 9/3 heads, head_dim 64, 30
+layers, SwiGLU 1536, vocab 49152, tied, bf16 weights), batch 1, 5-token
+prompt, greedy decode at positions 5..11 (the five-prompt / eight-new-token
+generation), cycled: after every 7 steps the cache length is rewound to 5, so
+every timed step is one of those 7 positions.  Steps are chained on the GPU
+(the token written by step k is the token read by step k+1).
+
+Prints one JSON line with decode tok/s, the whole step's algorithmic HBM
+bytes and GB/s, a roofline entry for the dominant kernel (timed with events
+on the stream the library launches it on), and the reference decoder's
+throughput on the host as the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+KERNELS = ["qkv", "attn", "attn_combine", "wo", "w13", "w2", "logits"]
+
+
+def step_bytes(m: synth.ModelShape, lengths_before: np.ndarray) -> int:
+    """Algorithmic HBM bytes of one decode step: every weight matrix once (the
+    tied embedding once, as the vocabulary product), the embedding rows
+    gathered, the norm gains, the K/V rows read (positions 0..n_b) and
+    written, and the fp32 logits written."""
+    table, _ = synth.tensor_table(m)
+    B = len(lengths_before)
+    mats = sum(int(np.prod(s)) * (2 if dt == synth.BF16 else 4) for _, _, s, dt in table if len(s) == 2)
+    gains = sum(int(np.prod(s)) * 4 for _, _, s, dt in table if len(s) == 1)
+    kv_row = m.n_layers * 2 * m.n_kv_heads * m.head_dim * 4
+    gather = B * m.dim * m.wbytes
+    kv_read = int(np.sum(lengths_before.astype(np.int64) + 1)) * kv_row
+    kv_write = B * kv_row
+    logits = B * m.vocab_size * 4
+    return mats + gains + gather + kv_read + kv_write + logits
+
+
+def kernel_bytes(m: synth.ModelShape, which: str, B: int, n_ctx: float) -> float:
+    """Algorithmic bytes of one launch of a step kernel (weights + activations
+    in and out), n_ctx = mean cached positions read by attention."""
+    d, F, V, D = m.dim, m.hidden_dim, m.vocab_size, m.head_dim
+    w = m.wbytes
+    qr, kvr = m.n_heads * D, m.n_kv_heads * D
+    if which == "qkv":
+        return (qr + 2 * kvr) * d * w + B * (d * 4 + d * 4 + (qr + 2 * kvr) * 4)
+    if which == "attn":
+        return B * (2 * kvr * n_ctx * 4 + qr * 4)
+    if which == "wo":
+        return d * qr * w + B * (qr * 4 + 2 * d * 4)
+    if which == "w13":
+        return 2 * F * d * w + B * (d * 4 + d * 4 + F * 4)
+    if which == "w2":
+        return d * F * w + B * (F * 4 + 2 * d * 4)
+    if which == "logits":
+        return V * d * w + B * (d * 4 + d * 4 + V * 4)
+    return 0.0
+
+
+def cpu_baseline(w: synth.Workload, arena: np.ndarray, budget_s: float) -> dict:
+    """The reference decoder (single thread) on the host: prefill the prompt,
+    then decode steps at positions prompt_len .. prompt_len+decode_calls-1,
+    cycled, until `budget_s` seconds of decode work are done."""
+    import oracle
+    m = oracle.Model(w.model, arena, 1, w.ctx)
+    prompt = synth.prompts(w)[0]
+    for t, tk in enumerate(prompt):
+        tok, _ = m.forward(0, t, int(tk))
+    steps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        pos = len(prompt) + steps % w.decode_calls
+        tok, _ = m.forward(0, pos, tok)
+        steps += 1
+    dt = time.perf_counter() - t0
+    return {"value": steps / dt, "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} decode steps of {w.name} (positions {len(prompt)}.."
+                      f"{len(prompt) + w.decode_calls - 1}, cycled) on one host thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=700)
+    ap.add_argument("--warmup", type=int, default=28)
+    ap.add_argument("--workload", default="llama135m_p5")
+    ap.add_argument("--dispatch", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--kernel-reps", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_step_02_amd as dsa
+
+    w = synth.WORKLOADS[args.workload]
+    m = w.model
+    arena = synth.make_arena(m, w.model_seed)
+    prompts = synth.prompts(w)
+    B = w.batch
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        model = dsa.Model(m, arena)
+        kv = dsa.KVCache(model, B, w.ctx)
+        kv.set_dispatch(1 if args.dispatch == "graph" else 0)
+        tok = torch.zeros(B, dtype=torch.int32, device="cuda")
+        kv.prefill_batch([list(p) for p in prompts], tok)
+        base = np.array([len(p) for p in prompts], np.int32)
+        cycle = w.decode_calls
+
+        def run(n, start):
+            for i in range(start, start + n):
+                if i % cycle == 0 and i > 0:
+                    kv.set_lengths(base)
+                kv.decode_step(tok, tok)
+
+        run(args.warmup, 0)
+        kv.set_lengths(base)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        run(args.steps, 0)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_total = ev0.elapsed_time(ev1)
+        kv.check()
+        ms_step = ms_total / args.steps
+
+        # per-kernel launch durations, each timed alone on the library's stream
+        mean_ctx = float(np.mean(base)) + (cycle - 1) / 2.0 + 1.0
+        kern = {}
+        for k, name in enumerate(KERNELS):
+            layer = m.n_layers // 2
+            kv.bench_kernel(k, layer, 5, stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            kv.bench_kernel(k, layer, args.kernel_reps, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / args.kernel_reps
+            per_step = 1 if name == "logits" else m.n_layers
+            kern[name] = {"us_per_launch": us, "launches_per_step": per_step,
+                          "us_per_step": us * per_step,
+                          "bytes_per_launch": kernel_bytes(m, name, B, mean_ctx)}
+        dom = max(kern, key=lambda n: kern[n]["us_per_step"])
+        dk = kern[dom]
+        achieved = dk["bytes_per_launch"] / (dk["us_per_launch"] * 1e-6) / 1e9
+
+    lengths_seq = [base + (i % cycle) for i in range(cycle)]
+    bytes_step = float(np.mean([step_bytes(m, L) for L in lengths_seq]))
+    gbps = bytes_step / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": "decode tok/s (135M-shaped Llama, B=1)" if w.name == "llama135m_p5" else f"decode tok/s ({w.name})",
+        "value": B * args.steps / (ms_total * 1e-3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (bf16 weights widened in registers)",
+        "data": "synthetic (seeded random weights N(0,0.02), uniform prompt ids)",
+        "config": {"workload": w.name, "description": w.description, "batch": B, "ctx": w.ctx,
+                   "decode_positions": [int(base.min()), int(base.max() + cycle - 1)],
+                   "dispatch": args.dispatch},
+        "step_bytes": bytes_step,
+        "achieved_GBps": gbps,
+        "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "us_per_launch": dk["us_per_launch"], "bytes_per_launch": dk["bytes_per_launch"]},
+        "kernels_us_per_step": {n: round(v["us_per_step"], 2) for n, v in kern.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, arena, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

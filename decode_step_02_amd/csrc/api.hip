@@ -1,0 +1,552 @@
+// api.hip -- the C ABI declared in include/ds_decode.h: argument checks on the
+// host, the host mirror of the cache lengths, workspace layout, the RoPE
+// table, and dispatch of the step kernels (eager or HIP-graph replay).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <cstdlib>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "ds_decode.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ds_status fail(ds_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+ds_status ok() {
+    g_err.clear();
+    return DS_OK;
+}
+
+ds_status hip_fail(hipError_t e, const char* what) {
+    return fail(DS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t wsize(const ds_config* c) { return c->weight_dtype == DS_BF16 ? 2 : 4; }
+
+// Shape checks shared by every entry point.  Returns DS_OK or an error with
+// the reason in g_err.
+ds_status check_config(const ds_config* c) {
+    if (!c) return fail(DS_ERR_INVALID_ARG, "config is NULL");
+    if (c->dim <= 0 || c->n_layers <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
+        c->head_dim <= 0 || c->hidden_dim <= 0 || c->vocab_size <= 0)
+        return fail(DS_ERR_INVALID_ARG, "every dimension must be positive");
+    if (c->weight_dtype != DS_F32 && c->weight_dtype != DS_BF16)
+        return fail(DS_ERR_INVALID_ARG, "weight_dtype must be DS_F32 or DS_BF16");
+    if (c->n_heads % c->n_kv_heads != 0)
+        return fail(DS_ERR_INVALID_ARG, "n_heads (%d) is not a multiple of n_kv_heads (%d)", c->n_heads,
+                    c->n_kv_heads);
+    if (c->head_dim % 2 != 0) return fail(DS_ERR_INVALID_ARG, "head_dim must be even");
+    if (!(c->norm_eps > 0.f) || !(c->rope_theta > 0.f))
+        return fail(DS_ERR_INVALID_ARG, "norm_eps and rope_theta must be positive");
+    if (c->head_dim % 8 != 0 || c->head_dim > ds::kMaxD)
+        return fail(DS_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 and at most %d", ds::kMaxD);
+    if (c->n_heads / c->n_kv_heads > ds::kMaxRep)
+        return fail(DS_ERR_UNSUPPORTED, "at most %d query heads per key/value head", ds::kMaxRep);
+    const size_t ws = wsize(c);
+    if ((c->dim * ws) % 16 || (static_cast<size_t>(c->n_heads) * c->head_dim * ws) % 16 ||
+        (c->hidden_dim * ws) % 16)
+        return fail(DS_ERR_UNSUPPORTED, "matrix rows must be whole 16-byte chunks");
+    const size_t lds = sizeof(float) * std::max(std::max(c->dim, c->n_heads * c->head_dim), c->hidden_dim);
+    if (lds > 160 * 1024) return fail(DS_ERR_UNSUPPORTED, "activation vector exceeds 160 KiB of LDS");
+    return DS_OK;
+}
+
+int n_tensors(const ds_config* c) { return 1 + 9 * c->n_layers + 1 + (c->tied_embeddings ? 0 : 1); }
+
+// Canonical arena offsets (weight order of "simple-llm / kasahare", section
+// "On-disk model format (.sllm)", 256-byte aligned, untied head last).
+size_t layout(const ds_config* c, std::vector<size_t>* off) {
+    const size_t d = c->dim, F = c->hidden_dim, V = c->vocab_size, w = wsize(c);
+    const size_t qr = static_cast<size_t>(c->n_heads) * c->head_dim;
+    const size_t kvr = static_cast<size_t>(c->n_kv_heads) * c->head_dim;
+    size_t p = 0;
+    auto put = [&](size_t bytes) {
+        if (off) off->push_back(p);
+        p = round_up(p + bytes, kAlign);
+    };
+    put(V * d * w);
+    for (int l = 0; l < c->n_layers; l++) {
+        put(d * 4);
+        put(qr * d * w);
+        put(kvr * d * w);
+        put(kvr * d * w);
+        put(d * qr * w);
+        put(d * 4);
+        put(F * d * w);
+        put(F * d * w);
+        put(d * F * w);
+    }
+    put(d * 4);
+    if (!c->tied_embeddings) put(V * d * w);
+    return p;
+}
+
+// Workspace carve-up for a (B, T) cache.
+struct WsLayout {
+    size_t x, q, o, h, part_o, part_ml, logits, keys, slot, pos, flag, err, rope_cos, rope_sin, total;
+};
+
+WsLayout ws_layout(const ds_config* c, int B, int T) {
+    WsLayout w{};
+    const size_t S = (static_cast<size_t>(T) + ds::kChunk - 1) / ds::kChunk;
+    const size_t HD = static_cast<size_t>(c->n_heads) * c->head_dim;
+    size_t p = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = p;
+        p = round_up(p + bytes, kAlign);
+        return at;
+    };
+    w.x = take(sizeof(float) * B * c->dim);
+    w.q = take(sizeof(float) * B * HD);
+    w.o = take(sizeof(float) * B * HD);
+    w.h = take(sizeof(float) * B * c->hidden_dim);
+    w.part_o = take(sizeof(float) * B * c->n_heads * S * c->head_dim);
+    w.part_ml = take(sizeof(float) * B * c->n_heads * S * 2);
+    w.logits = take(sizeof(float) * B * static_cast<size_t>(c->vocab_size));
+    w.keys = take(sizeof(unsigned long long) * B);
+    w.slot = take(sizeof(int32_t) * B);
+    w.pos = take(sizeof(int32_t) * B);
+    w.flag = take(sizeof(int32_t) * B);
+    w.err = take(sizeof(int32_t));
+    w.rope_cos = take(sizeof(float) * T * (c->head_dim / 2));
+    w.rope_sin = take(sizeof(float) * T * (c->head_dim / 2));
+    w.total = p;
+    return w;
+}
+
+}  // namespace
+
+struct ds_model {
+    ds_config cfg;
+    const void* arena;
+    std::vector<size_t> off;
+    ds::ModelPtrs ptrs;
+};
+
+struct GraphEntry {
+    hipStream_t stream;
+    const int32_t* tok_in;
+    int32_t* tok_out;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+struct ds_kv {
+    ds_model* model;
+    int B, T;
+    float* cache;
+    int32_t* lengths;
+    uint8_t* ws;
+    WsLayout lay;
+    ds::StepArgs s;
+    std::vector<int32_t> mirror;  // host copy of lengths, updated at enqueue
+    int dispatch;                 // 0 eager, 1 graph
+    bool stepped = false;         // a decode step has filled the per-item state
+    std::vector<GraphEntry> graphs;
+};
+
+extern "C" {
+
+const char* ds_last_error(void) { return g_err.c_str(); }
+
+size_t ds_weights_bytes(const ds_config* cfg) {
+    if (check_config(cfg) != DS_OK) return 0;
+    return layout(cfg, nullptr);
+}
+
+int32_t ds_weights_count(const ds_config* cfg) {
+    if (check_config(cfg) != DS_OK) return 0;
+    return n_tensors(cfg);
+}
+
+ds_status ds_weights_offsets(const ds_config* cfg, size_t* h_off, int32_t n) {
+    ds_status st = check_config(cfg);
+    if (st != DS_OK) return st;
+    if (!h_off || n < n_tensors(cfg)) return fail(DS_ERR_INVALID_ARG, "offset array too small");
+    std::vector<size_t> off;
+    layout(cfg, &off);
+    for (size_t i = 0; i < off.size(); i++) h_off[i] = off[i];
+    return ok();
+}
+
+size_t ds_kv_cache_bytes(const ds_config* cfg, int32_t B, int32_t T) {
+    if (check_config(cfg) != DS_OK || B <= 0 || T <= 0) return 0;
+    return sizeof(float) * static_cast<size_t>(cfg->n_layers) * 2 * B * cfg->n_kv_heads * T * cfg->head_dim;
+}
+
+size_t ds_workspace_bytes(const ds_config* cfg, int32_t B, int32_t T) {
+    if (check_config(cfg) != DS_OK || B <= 0 || T <= 0) return 0;
+    return ws_layout(cfg, B, T).total;
+}
+
+ds_status ds_load_weights(const ds_config* cfg, const void* d_arena, size_t arena_bytes, void* stream,
+                          ds_model** out) {
+    (void)stream;
+    ds_status st = check_config(cfg);
+    if (st != DS_OK) return st;
+    if (!out) return fail(DS_ERR_INVALID_ARG, "out is NULL");
+    if (!d_arena) return fail(DS_ERR_INVALID_ARG, "d_arena is NULL");
+    if (!aligned(d_arena, kAlign)) return fail(DS_ERR_ALIGNMENT, "d_arena is not 256-byte aligned");
+    const size_t need = layout(cfg, nullptr);
+    if (arena_bytes < need)
+        return fail(DS_ERR_WORKSPACE, "arena has %zu bytes, the layout needs %zu", arena_bytes, need);
+    ds_model* m = new (std::nothrow) ds_model();
+    if (!m) return fail(DS_ERR_INVALID_ARG, "out of host memory");
+    m->cfg = *cfg;
+    m->arena = d_arena;
+    layout(cfg, &m->off);
+    const uint8_t* a = static_cast<const uint8_t*>(d_arena);
+    m->ptrs.emb = a + m->off[0];
+    m->ptrs.layers.resize(cfg->n_layers);
+    for (int l = 0; l < cfg->n_layers; l++) {
+        const size_t* o = m->off.data() + 1 + 9 * l;
+        ds::LayerW& w = m->ptrs.layers[l];
+        w.attn_norm = reinterpret_cast<const float*>(a + o[0]);
+        w.wq = a + o[1];
+        w.wk = a + o[2];
+        w.wv = a + o[3];
+        w.wo = a + o[4];
+        w.ffn_norm = reinterpret_cast<const float*>(a + o[5]);
+        w.w1 = a + o[6];
+        w.w3 = a + o[7];
+        w.w2 = a + o[8];
+    }
+    m->ptrs.out_norm = reinterpret_cast<const float*>(a + m->off[1 + 9 * cfg->n_layers]);
+    m->ptrs.wcls = cfg->tied_embeddings ? m->ptrs.emb : a + m->off.back();
+    *out = m;
+    return ok();
+}
+
+void ds_model_destroy(ds_model* model) { delete model; }
+
+ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cache, size_t cache_bytes,
+                             int32_t* d_lengths, void* d_workspace, size_t workspace_bytes, void* stream,
+                             ds_kv** out) {
+    if (!model || !out) return fail(DS_ERR_INVALID_ARG, "model or out is NULL");
+    const ds_config* c = &model->cfg;
+    if (B <= 0 || T <= 0) return fail(DS_ERR_INVALID_ARG, "B and T must be positive");
+    if (!d_cache || !d_lengths || !d_workspace) return fail(DS_ERR_INVALID_ARG, "NULL device buffer");
+    if (!aligned(d_cache, kAlign) || !aligned(d_lengths, kAlign) || !aligned(d_workspace, kAlign))
+        return fail(DS_ERR_ALIGNMENT, "cache, lengths and workspace must be 256-byte aligned");
+    if (cache_bytes < ds_kv_cache_bytes(c, B, T))
+        return fail(DS_ERR_WORKSPACE, "cache has %zu bytes, needs %zu", cache_bytes, ds_kv_cache_bytes(c, B, T));
+    const WsLayout lay = ws_layout(c, B, T);
+    if (workspace_bytes < lay.total)
+        return fail(DS_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    // Dynamic LDS above 64 KiB (activation vectors longer than 16384 floats)
+    // needs the per-kernel opt-in, up to the device's per-block limit.
+    const int need_lds = static_cast<int>(
+        sizeof(float) * std::max(std::max(c->dim, c->n_heads * c->head_dim), c->hidden_dim));
+    static int attr_lds = 64 * 1024;
+    if (need_lds > attr_lds) {
+        int dev = 0, optin = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+        if (need_lds > optin - 1024)
+            return fail(DS_ERR_UNSUPPORTED, "activation vector needs %d bytes of LDS, device allows %d", need_lds,
+                        optin);
+        e = ds::set_kernel_attributes(need_lds);
+        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+        attr_lds = need_lds;
+    }
+
+    // RoPE table: pair i of position p turns by p * theta^(-2i/D) ("GOTOken",
+    // section "Loading the model and tokenizer", pairs (j, j + head_dim/2));
+    // angle, cos and sin in double, rounded once to float.
+    const int half = c->head_dim / 2;
+    std::vector<float> cs(static_cast<size_t>(T) * half), sn(static_cast<size_t>(T) * half);
+    for (int p = 0; p < T; p++)
+        for (int i = 0; i < half; i++) {
+            const double inv = std::pow(static_cast<double>(c->rope_theta),
+                                        -static_cast<double>(2 * i) / static_cast<double>(c->head_dim));
+            const double ang = static_cast<double>(p) * inv;
+            cs[static_cast<size_t>(p) * half + i] = static_cast<float>(std::cos(ang));
+            sn[static_cast<size_t>(p) * half + i] = static_cast<float>(std::sin(ang));
+        }
+    uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+    hipError_t e = hipMemcpyAsync(ws + lay.rope_cos, cs.data(), cs.size() * sizeof(float),
+                                  hipMemcpyHostToDevice, st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(ws + lay.rope_sin, sn.data(), sn.size() * sizeof(float), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = ds::enqueue_fill(d_lengths, B, 0, st);
+    if (e == hipSuccess) e = ds::enqueue_fill(reinterpret_cast<int32_t*>(ws + lay.err), 1, 0, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "cache setup");
+
+    ds_kv* kv = new (std::nothrow) ds_kv();
+    if (!kv) return fail(DS_ERR_INVALID_ARG, "out of host memory");
+    kv->model = model;
+    kv->B = B;
+    kv->T = T;
+    kv->cache = d_cache;
+    kv->lengths = d_lengths;
+    kv->ws = ws;
+    kv->lay = lay;
+    kv->mirror.assign(B, 0);
+    const char* env = std::getenv("DS_DISPATCH");
+    kv->dispatch = (env && std::strcmp(env, "eager") == 0) ? 0 : 1;
+    ds::StepArgs& s = kv->s;
+    s.d = c->dim;
+    s.L = c->n_layers;
+    s.H = c->n_heads;
+    s.Hkv = c->n_kv_heads;
+    s.D = c->head_dim;
+    s.F = c->hidden_dim;
+    s.V = c->vocab_size;
+    s.wdt = c->weight_dtype;
+    s.B = B;
+    s.T = T;
+    s.n_chunks = (T + ds::kChunk - 1) / ds::kChunk;
+    s.eps = c->norm_eps;
+    s.emb = model->ptrs.emb;
+    s.cache = d_cache;
+    s.lengths = d_lengths;
+    s.x = reinterpret_cast<float*>(ws + lay.x);
+    s.q = reinterpret_cast<float*>(ws + lay.q);
+    s.o = reinterpret_cast<float*>(ws + lay.o);
+    s.h = reinterpret_cast<float*>(ws + lay.h);
+    s.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+    s.part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
+    s.logits = reinterpret_cast<float*>(ws + lay.logits);
+    s.keys = reinterpret_cast<unsigned long long*>(ws + lay.keys);
+    s.slot = reinterpret_cast<int32_t*>(ws + lay.slot);
+    s.pos = reinterpret_cast<int32_t*>(ws + lay.pos);
+    s.flag = reinterpret_cast<int32_t*>(ws + lay.flag);
+    s.err = reinterpret_cast<int32_t*>(ws + lay.err);
+    s.rope_cos = reinterpret_cast<const float*>(ws + lay.rope_cos);
+    s.rope_sin = reinterpret_cast<const float*>(ws + lay.rope_sin);
+    *out = kv;
+    return ok();
+}
+
+void ds_kv_cache_destroy(ds_kv* kv) {
+    if (!kv) return;
+    for (GraphEntry& g : kv->graphs) {
+        (void)hipGraphExecDestroy(g.exec);
+        (void)hipGraphDestroy(g.graph);
+    }
+    delete kv;
+}
+
+ds_status ds_kv_cache_reset(ds_kv* kv, int32_t seq, void* stream) {
+    if (!kv) return fail(DS_ERR_INVALID_ARG, "kv is NULL");
+    if (seq < -1 || seq >= kv->B) return fail(DS_ERR_INVALID_ARG, "seq %d outside [-1, %d)", seq, kv->B);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = seq < 0 ? ds::enqueue_fill(kv->lengths, kv->B, 0, st)
+                           : ds::enqueue_fill(kv->lengths + seq, 1, 0, st);
+    if (e != hipSuccess) return hip_fail(e, "reset");
+    if (seq < 0)
+        std::fill(kv->mirror.begin(), kv->mirror.end(), 0);
+    else
+        kv->mirror[seq] = 0;
+    return ok();
+}
+
+ds_status ds_kv_cache_set_lengths(ds_kv* kv, const int32_t* h_lengths, void* stream) {
+    if (!kv || !h_lengths) return fail(DS_ERR_INVALID_ARG, "NULL argument");
+    for (int b = 0; b < kv->B; b++)
+        if (h_lengths[b] < 0 || h_lengths[b] > kv->T)
+            return fail(DS_ERR_INVALID_ARG, "lengths[%d] = %d outside [0, %d]", b, h_lengths[b], kv->T);
+    hipError_t e = ds::enqueue_set_lengths(kv->lengths, h_lengths, 0, kv->B, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "set_lengths");
+    kv->mirror.assign(h_lengths, h_lengths + kv->B);
+    return ok();
+}
+
+ds_status ds_kv_cache_get_lengths(const ds_kv* kv, int32_t* h_lengths) {
+    if (!kv || !h_lengths) return fail(DS_ERR_INVALID_ARG, "NULL argument");
+    std::memcpy(h_lengths, kv->mirror.data(), sizeof(int32_t) * kv->B);
+    return ok();
+}
+
+ds_status ds_kv_cache_check(ds_kv* kv, void* stream) {
+    if (!kv) return fail(DS_ERR_INVALID_ARG, "kv is NULL");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t err = 0;
+    hipError_t e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipMemcpy(&err, kv->s.err, sizeof err, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && err) e = hipMemset(kv->s.err, 0, sizeof(int32_t));
+    if (e != hipSuccess) return hip_fail(e, "check");
+    if (err) return fail(DS_ERR_BAD_TOKEN, "a decode step read a token id outside [0, %d)", kv->s.V);
+    return ok();
+}
+
+ds_status ds_prefill(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_tokens, int32_t n,
+                     int32_t* d_tok_out, void* stream) {
+    if (!model || !kv || kv->model != model) return fail(DS_ERR_INVALID_ARG, "model/kv mismatch");
+    if (seq < 0 || seq >= kv->B) return fail(DS_ERR_INVALID_ARG, "seq %d outside [0, %d)", seq, kv->B);
+    if (n <= 0 || !h_tokens) return fail(DS_ERR_INVALID_ARG, "need n > 0 host tokens");
+    if (kv->mirror[seq] + static_cast<int64_t>(n) > kv->T)
+        return fail(DS_ERR_CONTEXT_FULL, "sequence %d has %d of %d positions; %d more do not fit", seq,
+                    kv->mirror[seq], kv->T, n);
+    for (int j = 0; j < n; j++)
+        if (h_tokens[j] < 0 || h_tokens[j] >= kv->s.V)
+            return fail(DS_ERR_BAD_TOKEN, "token %d at %d outside [0, %d)", h_tokens[j], j, kv->s.V);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    ds::BeginList list;
+    list.n = 1;
+    list.item0 = 0;
+    list.by_value = 1;
+    list.slot[0] = seq;
+    for (int j = 0; j < n; j++) {
+        list.tok[0] = h_tokens[j];
+        list.last[0] = j == n - 1;
+        hipError_t e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, nullptr, 1, j == n - 1, d_tok_out, st);
+        if (e != hipSuccess) return hip_fail(e, "prefill");
+    }
+    kv->mirror[seq] += n;
+    return ok();
+}
+
+ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens, const int32_t* h_counts,
+                           int32_t* d_tok_out, void* stream) {
+    if (!model || !kv || kv->model != model) return fail(DS_ERR_INVALID_ARG, "model/kv mismatch");
+    if (!h_counts) return fail(DS_ERR_INVALID_ARG, "h_counts is NULL");
+    const int B = kv->B;
+    std::vector<int64_t> start(B + 1, 0);
+    int max_n = 0;
+    for (int b = 0; b < B; b++) {
+        if (h_counts[b] < 0) return fail(DS_ERR_INVALID_ARG, "h_counts[%d] < 0", b);
+        if (kv->mirror[b] + static_cast<int64_t>(h_counts[b]) > kv->T)
+            return fail(DS_ERR_CONTEXT_FULL, "sequence %d: %d + %d positions exceed %d", b, kv->mirror[b],
+                        h_counts[b], kv->T);
+        start[b + 1] = start[b] + h_counts[b];
+        max_n = std::max(max_n, h_counts[b]);
+    }
+    if (start[B] > 0 && !h_tokens) return fail(DS_ERR_INVALID_ARG, "h_tokens is NULL");
+    for (int64_t i = 0; i < start[B]; i++)
+        if (h_tokens[i] < 0 || h_tokens[i] >= kv->s.V)
+            return fail(DS_ERR_BAD_TOKEN, "token %d at %lld outside [0, %d)", h_tokens[i],
+                        static_cast<long long>(i), kv->s.V);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::vector<ds::BeginList> lists;
+    for (int j = 0; j < max_n; j++) {
+        lists.clear();
+        int items = 0;
+        bool any_last = false;
+        for (int b = 0; b < B; b++) {
+            if (h_counts[b] <= j) continue;
+            if (lists.empty() || lists.back().n == ds::kMaxItems) {
+                lists.emplace_back();
+                lists.back().item0 = items;
+                lists.back().by_value = 1;
+            }
+            ds::BeginList& l = lists.back();
+            l.slot[l.n] = b;
+            l.tok[l.n] = h_tokens[start[b] + j];
+            l.last[l.n] = (j == h_counts[b] - 1);
+            any_last |= l.last[l.n] != 0;
+            l.n++;
+            items++;
+        }
+        hipError_t e = ds::enqueue_step(kv->s, model->ptrs, lists.data(), static_cast<int>(lists.size()),
+                                        nullptr, items, any_last, d_tok_out, st);
+        if (e != hipSuccess) return hip_fail(e, "prefill_batch");
+    }
+    for (int b = 0; b < B; b++) kv->mirror[b] += h_counts[b];
+    return ok();
+}
+
+ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, int32_t* d_tok_out,
+                         void* stream) {
+    if (!model || !kv || kv->model != model) return fail(DS_ERR_INVALID_ARG, "model/kv mismatch");
+    if (!d_tok_in || !d_tok_out) return fail(DS_ERR_INVALID_ARG, "token buffers are NULL");
+    if (!aligned(d_tok_in, 4) || !aligned(d_tok_out, 4)) return fail(DS_ERR_ALIGNMENT, "token buffers");
+    for (int b = 0; b < kv->B; b++)
+        if (kv->mirror[b] >= kv->T)
+            return fail(DS_ERR_CONTEXT_FULL, "sequence %d already holds all %d positions", b, kv->T);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    ds::BeginList list;
+    list.n = kv->B;
+    list.item0 = 0;
+    list.by_value = 0;
+    hipError_t e = hipSuccess;
+    if (kv->dispatch == 1 && st != nullptr) {
+        GraphEntry* ge = nullptr;
+        for (GraphEntry& g : kv->graphs)
+            if (g.stream == st && g.tok_in == d_tok_in && g.tok_out == d_tok_out) ge = &g;
+        if (!ge) {
+            GraphEntry g{st, d_tok_in, d_tok_out, nullptr, nullptr};
+            e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+            hipError_t ee = ds::enqueue_step(kv->s, model->ptrs, &list, 1, d_tok_in, kv->B, true, d_tok_out, st);
+            e = hipStreamEndCapture(st, &g.graph);
+            if (ee != hipSuccess) return hip_fail(ee, "capture decode step");
+            if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+            e = hipGraphInstantiate(&g.exec, g.graph, nullptr, nullptr, 0);
+            if (e != hipSuccess) {
+                (void)hipGraphDestroy(g.graph);
+                return hip_fail(e, "hipGraphInstantiate");
+            }
+            kv->graphs.push_back(g);
+            ge = &kv->graphs.back();
+        }
+        e = hipGraphLaunch(ge->exec, st);
+        if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+    } else {
+        e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, d_tok_in, kv->B, true, d_tok_out, st);
+        if (e != hipSuccess) return hip_fail(e, "decode step");
+    }
+    for (int b = 0; b < kv->B; b++) kv->mirror[b] += 1;
+    kv->stepped = true;
+    return ok();
+}
+
+ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t layer, int32_t reps,
+                          void* stream) {
+    if (!model || !kv || kv->model != model) return fail(DS_ERR_INVALID_ARG, "model/kv mismatch");
+    if (!kv->stepped) return fail(DS_ERR_STATE, "run ds_decode_step before ds_bench_kernel");
+    if (which < 0 || which > 6) return fail(DS_ERR_INVALID_ARG, "which must be in [0, 6]");
+    if (layer < 0 || layer >= kv->s.L) return fail(DS_ERR_INVALID_ARG, "layer outside [0, L)");
+    if (reps < 1) return fail(DS_ERR_INVALID_ARG, "reps must be positive");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int r = 0; r < reps; r++) {
+        hipError_t e = ds::enqueue_kernel(which, layer, kv->s, model->ptrs, kv->B, st);
+        if (e != hipSuccess) return hip_fail(e, "bench kernel");
+    }
+    return ok();
+}
+
+ds_status ds_logits(const ds_kv* kv, float* d_out, void* stream) {
+    if (!kv || !d_out) return fail(DS_ERR_INVALID_ARG, "NULL argument");
+    hipError_t e = hipMemcpyAsync(d_out, kv->s.logits, sizeof(float) * kv->B * static_cast<size_t>(kv->s.V),
+                                  hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "logits copy");
+    return ok();
+}
+
+ds_status ds_set_dispatch(ds_kv* kv, int32_t mode) {
+    if (!kv) return fail(DS_ERR_INVALID_ARG, "kv is NULL");
+    if (mode != 0 && mode != 1) return fail(DS_ERR_INVALID_ARG, "mode must be 0 (eager) or 1 (graph)");
+    kv->dispatch = mode;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+/*
+ * ds_decode.h -- C ABI of the MI355X (gfx950) single-token Llama decode step.
+ *
+ * The library runs the autoregressive decode step of a Llama-style decoder
+ * ("simple-llm / kasahare" PyPI README 0.4.0, section "Architecture": pre-norm
+ * blocks of RMSNorm, Q/K/V projections without bias, RoPE, grouped-query
+ * attention, Wo plus residual, RMSNorm, SwiGLU W2(silu(W1 x) * W3 x) plus
+ * residual; tied embeddings) with a key/value cache ("Inside nanochat Part 4:
+ * Understanding Inference", sections "KV Cache" and "Cache Architecture")
+ * and greedy argmax selection ("Inside nanochat Part 4", section "Sampling
+ * Strategy").  All arithmetic is fp32; matrices may be stored as bf16, which
+ * is widened by a 16-bit left shift ("GOTOken: An Inference Engine in
+ * QBasic", section "Loading the model and tokenizer").
+ *
+ * Conventions for every call
+ *  - Pointers named d_* are device pointers (hipMalloc / torch CUDA tensors);
+ *    pointers named h_* are host pointers.  The caller allocates every device
+ *    buffer and keeps it alive until the handle that uses it is destroyed;
+ *    the library never allocates or frees caller memory.  Handles (ds_model,
+ *    ds_kv) are small host objects owned by the library.
+ *  - `stream` is a hipStream_t passed as void*.  NULL means the default stream.
+ *  - Arguments are checked on the host before any work is enqueued: a call
+ *    that returns an error has enqueued nothing and changed no state.
+ *  - Apart from creation calls, calls only enqueue work on `stream` and return
+ *    without synchronising.
+ *  - No C++ exception crosses this interface.  ds_last_error() gives a
+ *    message for the last failing call on the calling thread.
+ *  - A handle must not be used from two host threads at once.
+ */
+#ifndef DS_DECODE_H
+#define DS_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DS_OK = 0,
+    DS_ERR_INVALID_ARG = -1,  /* null/inconsistent argument, slot out of range */
+    DS_ERR_UNSUPPORTED = -2,  /* shape the kernels do not handle              */
+    DS_ERR_ALIGNMENT = -3,    /* device pointer not 256-byte aligned           */
+    DS_ERR_CONTEXT_FULL = -4, /* a sequence would pass its T positions         */
+    DS_ERR_BAD_TOKEN = -5,    /* token id outside [0, vocab)                   */
+    DS_ERR_WORKSPACE = -6,    /* a buffer is smaller than the size query says  */
+    DS_ERR_HIP = -7,          /* a HIP runtime call failed                     */
+    DS_ERR_STATE = -8         /* call not valid in the handle's current state  */
+} ds_status;
+
+typedef enum { DS_F32 = 0, DS_BF16 = 1 } ds_dtype;
+
+/* Model shape.  The field order is part of the ABI. */
+typedef struct {
+    int32_t dim;             /* d: residual width                               */
+    int32_t n_layers;        /* L                                               */
+    int32_t n_heads;         /* H query heads                                   */
+    int32_t n_kv_heads;      /* Hkv key/value heads; H % Hkv == 0               */
+    int32_t head_dim;        /* D; even                                         */
+    int32_t hidden_dim;      /* F: SwiGLU width                                 */
+    int32_t vocab_size;      /* V                                               */
+    int32_t tied_embeddings; /* 1: logits use token_emb; 0: a separate wcls     */
+    int32_t weight_dtype;    /* ds_dtype of every matrix; norm gains are fp32   */
+    float rope_theta;        /* RoPE base                                       */
+    float norm_eps;          /* RMSNorm epsilon                                 */
+} ds_config;
+
+typedef struct ds_model ds_model;
+typedef struct ds_kv ds_kv;
+
+/* ---- size and layout queries (host only, no HIP calls) ------------------ */
+
+/* Canonical weight arena: one buffer holding, in this order and each tensor
+ * starting on a 256-byte boundary, token_emb [V][d]; per layer attn_norm [d],
+ * wq [H*D][d], wk [Hkv*D][d], wv [Hkv*D][d], wo [d][H*D], ffn_norm [d],
+ * w1 [F][d], w3 [F][d], w2 [d][F]; output_norm [d]; and wcls [V][d] when
+ * the embeddings are not tied.  This is the weight order of "simple-llm /
+ * kasahare" (section "On-disk model format (.sllm)") with the untied head
+ * appended.  Matrices are row-major [out][in] in weight_dtype, gains fp32.
+ * Returns 0 for an invalid config. */
+size_t ds_weights_bytes(const ds_config* cfg);
+/* Number of tensors in the arena (1 + 9L + 1, plus 1 when untied). */
+int32_t ds_weights_count(const ds_config* cfg);
+/* Byte offset of each arena tensor into h_off[0..n); n must be at least
+ * ds_weights_count(cfg). */
+ds_status ds_weights_offsets(const ds_config* cfg, size_t* h_off, int32_t n);
+/* Device bytes of the key/value cache: an fp32 tensor of shape
+ * (L, 2, B, Hkv, T, D), row-major (the (L,2,B,H,T,D) layout of "Inside
+ * nanochat Part 4", section "Cache Architecture", with H = key/value heads). */
+size_t ds_kv_cache_bytes(const ds_config* cfg, int32_t B, int32_t T);
+/* Device scratch the library needs for a (B, T) cache. */
+size_t ds_workspace_bytes(const ds_config* cfg, int32_t B, int32_t T);
+
+/* ---- model ---------------------------------------------------------------- */
+
+/* Binds a device weight arena (layout above, `arena_bytes` >= ds_weights_bytes)
+ * to a model handle.  The arena is read in place and must stay unchanged
+ * while the handle lives.  Checks: cfg consistent (H % Hkv == 0, D even,
+ * every matrix row 16-byte aligned: dim, H*D and F times the weight size
+ * multiple of 16), d_arena 256-byte aligned.  `stream` is unused (kept for
+ * symmetry).  *out receives the handle. */
+ds_status ds_load_weights(const ds_config* cfg, const void* d_arena, size_t arena_bytes,
+                          void* stream, ds_model** out);
+void ds_model_destroy(ds_model* model);
+
+/* ---- key/value cache ------------------------------------------------------ */
+
+/* Binds a cache of B sequences with T positions each.  d_cache: fp32,
+ * ds_kv_cache_bytes(cfg, B, T) bytes; d_lengths: int32[B], the number of
+ * cached positions per sequence; d_workspace: ds_workspace_bytes(cfg, B, T)
+ * bytes.  All three 256-byte aligned.  Zeroes d_lengths, uploads the RoPE
+ * table into the workspace and synchronises `stream` once.  The library never
+ * writes cache rows at positions >= lengths[b]; the caller must not write
+ * d_lengths other than through the calls below. */
+ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cache,
+                             size_t cache_bytes, int32_t* d_lengths, void* d_workspace,
+                             size_t workspace_bytes, void* stream, ds_kv** out);
+void ds_kv_cache_destroy(ds_kv* kv);
+/* Empties sequence `seq` (or every sequence when seq == -1): lengths := 0,
+ * as the cache reset of "Inside nanochat Part 4", section "KV Cache". */
+ds_status ds_kv_cache_reset(ds_kv* kv, int32_t seq, void* stream);
+/* Sets every lengths[b] from h_lengths[0..B) (each in [0, T]); used to rewind
+ * or to resume from a saved cache. */
+ds_status ds_kv_cache_set_lengths(ds_kv* kv, const int32_t* h_lengths, void* stream);
+/* Copies the host-side mirror of the lengths (no device access). */
+ds_status ds_kv_cache_get_lengths(const ds_kv* kv, int32_t* h_lengths);
+/* Synchronises `stream` and reports device-detected errors since the last
+ * check: DS_ERR_BAD_TOKEN if a decode step read a token id outside [0, V)
+ * (that sequence used row 0 instead); the flag is then cleared. */
+ds_status ds_kv_cache_check(ds_kv* kv, void* stream);
+
+/* ---- the decode path ----------------------------------------------------- */
+
+/* Feeds h_tokens[0..n) (host, each in [0, V)) to sequence `seq` at positions
+ * lengths[seq] .. lengths[seq]+n-1, one position at a time through the same
+ * kernels as ds_decode_step, and appends their keys and values.  After the
+ * call lengths[seq] has grown by n, d_tok_out[seq] holds the greedy token of
+ * the last position and the logits of that position are kept for ds_logits.
+ * d_tok_out is int32[B] (only entry seq is written) and may be NULL.
+ * Errors: DS_ERR_CONTEXT_FULL if lengths[seq] + n > T. */
+ds_status ds_prefill(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_tokens, int32_t n,
+                     int32_t* d_tok_out, void* stream);
+
+/* Ragged prefill of many sequences at once: sequence b receives
+ * h_counts[b] >= 0 tokens, taken in order from h_tokens (the concatenation
+ * over b).  Position by position, every sequence that still has tokens is
+ * advanced in one batched pass.  d_tok_out[b] is written for every b with
+ * h_counts[b] > 0. */
+ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens,
+                           const int32_t* h_counts, int32_t* d_tok_out, void* stream);
+
+/* One decode step for every sequence b in [0, B): reads d_tok_in[b], runs the
+ * token at position lengths[b] through all layers, appends its key and value
+ * rows to the cache at that position, writes the greedy next token to
+ * d_tok_out[b] and advances lengths[b] by one.  d_tok_in and d_tok_out are
+ * device int32[B]; they may be the same buffer.  The fp32 logits [B][V] of
+ * the step stay in the workspace for ds_logits.
+ * Errors: DS_ERR_CONTEXT_FULL if any lengths[b] == T. */
+ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, int32_t* d_tok_out,
+                         void* stream);
+
+/* Copies the fp32 logits [B][V] of the last prefill / decode step into d_out
+ * (device, B*V floats).  Rows of sequences that the last call did not touch
+ * hold what they held before. */
+ds_status ds_logits(const ds_kv* kv, float* d_out, void* stream);
+
+/* Dispatch of ds_decode_step: 0 = one kernel launch per operation (eager),
+ * 1 = the same launches captured once into a HIP graph per (stream, token
+ * buffers) and replayed.  The default comes from the environment variable
+ * DS_DISPATCH ("eager" or "graph"), else graph. */
+ds_status ds_set_dispatch(ds_kv* kv, int32_t mode);
+
+/* Diagnostics: enqueues `reps` back-to-back launches of one kernel of the
+ * decode step -- 0 Q/K/V projection, 1 attention partials, 2 attention
+ * combine, 3 Wo, 4 W1/W3, 5 W2, 6 vocabulary logits -- for layer `layer`,
+ * with exactly the arguments and launch shape of the last ds_decode_step on
+ * this cache (the same positions are rewritten; Wo and W2 add to the
+ * residual again).  Lets a caller time one kernel with events on `stream`.
+ * Errors: DS_ERR_STATE before the first ds_decode_step. */
+ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t layer, int32_t reps,
+                          void* stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* ds_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

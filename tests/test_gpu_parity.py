@@ -1,0 +1,191 @@
+"""Parity of the HIP decode path with the reference decoder (needs a gfx950 GPU).
+
+Every case runs the same seeded synthetic inputs through the library (via its
+C ABI) and through the reference decoder, feeds the GPU the reference's greedy
+tokens (teacher forcing), and compares logits (max |d| <= 5e-4 and relative
+<= 1e-4), greedy tokens (exact, or a near-tie), cache rows (same tolerance),
+untouched cache slots (still the NaN sentinel) and lengths (exact).
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from parity import assert_logits_close, check_tokens, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_run(shape, arena, prompts, feed, T, dispatch=1, use_batch_prefill=True, stream=None):
+    """Prefill the prompts, then one decode step per entry of `feed` (tokens
+    for every sequence).  Returns first tokens/logits, per-step tokens/logits,
+    the cache and lengths as numpy arrays."""
+    torch = _torch()
+    import decode_step_02_amd as dsa
+    B = len(prompts)
+    model = dsa.Model(shape, arena)
+    kv = dsa.KVCache(model, B, T)
+    kv.set_dispatch(dispatch)
+    kv.cache.fill_(float("nan"))
+    tok_out = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    if use_batch_prefill:
+        kv.prefill_batch([list(p) for p in prompts], tok_out, stream)
+    else:
+        for b, p in enumerate(prompts):
+            kv.prefill(b, list(p), tok_out, stream)
+    first_tok = tok_out.cpu().numpy().copy()
+    first_lg = kv.logits(stream).cpu().numpy().copy()
+    toks, lgs = [], []
+    tok_in = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for f in feed:
+        tok_in.copy_(torch.from_numpy(np.asarray(f, np.int32)))
+        kv.decode_step(tok_in, tok_out, stream)
+        toks.append(tok_out.cpu().numpy().copy())
+        lgs.append(kv.logits(stream).cpu().numpy().copy())
+    if stream is not None:
+        stream.synchronize()
+    kv.check(stream)
+    out = dict(first_tok=first_tok, first_lg=first_lg, toks=toks, lgs=lgs,
+               cache=kv.cache_view().cpu().numpy(), lengths=kv.lengths.cpu().numpy(),
+               mirror=np.array(kv.get_lengths()))
+    kv.close()
+    model.close()
+    return out
+
+
+def compare(shape, arena, prompts, decode_calls, T, what, **kw):
+    ref_first, ref_first_lg, ref_toks, ref_lgs, om = oracle_run(shape, arena, prompts, decode_calls, T)
+    feed = [ref_first] + ref_toks[:-1]
+    g = gpu_run(shape, arena, prompts, feed, T, **kw)
+    ties = check_tokens(g["first_tok"], ref_first, ref_first_lg, g["first_lg"], f"{what} prefill")
+    assert_logits_close(g["first_lg"], ref_first_lg, f"{what} prefill")
+    worst = 0.0
+    for k in range(decode_calls):
+        worst = max(worst, assert_logits_close(g["lgs"][k], ref_lgs[k], f"{what} step {k}"))
+        ties += check_tokens(g["toks"][k], ref_toks[k], ref_lgs[k], g["lgs"][k], f"{what} step {k}")
+    lengths = np.array([len(p) + decode_calls for p in prompts], np.int32)
+    assert np.array_equal(g["lengths"], lengths) and np.array_equal(g["mirror"], lengths)
+    ref_cache = om.cache_view()
+    for b, n in enumerate(lengths):
+        got = g["cache"][:, :, b, :, :n]
+        assert_logits_close(got, ref_cache[:, :, b, :, :n], f"{what} cache seq {b}")
+        assert np.all(np.isnan(g["cache"][:, :, b, :, n:])), f"{what}: slot beyond length written"
+    _say(f"{what}: max|dlogit| {worst:.2e}, near-ties {ties}")
+    return g
+
+
+def test_tiny_cached_decode_matches_oracle():
+    w = synth.WORKLOADS["tiny_p5"]
+    arena = synth.make_arena(w.model, w.model_seed)
+    compare(w.model, arena, synth.prompts(w), w.decode_calls, w.ctx, "tiny")
+
+
+def test_tiny_larger_weights_eager_and_graph_bitwise_equal():
+    """std 0.15 weights move the residual stream far from the embedding, so
+    greedy tokens vary; eager and graph dispatch give identical bits."""
+    shape = synth.TINY
+    arena = synth.make_arena(shape, 7, std=0.15, gain_sigma=0.1)
+    prompts = [synth.random_tokens(77, 6, shape.vocab_size)]
+    torch = _torch()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        g_graph = compare(shape, arena, prompts, 20, 64, "tiny std0.15 graph", dispatch=1, stream=st)
+        g_eager = compare(shape, arena, prompts, 20, 64, "tiny std0.15 eager", dispatch=0, stream=st)
+    for a, b in zip(g_graph["lgs"], g_eager["lgs"]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_tiny_uncached_equals_cached_on_gpu():
+    """GOTOken, 'About one token per second': rerunning the whole prefix for
+    every new token gives the cached result bit for bit (68 vs 12 passes)."""
+    torch = _torch()
+    import decode_step_02_amd as dsa
+    w = synth.WORKLOADS["tiny_p5"]
+    shape = w.model
+    arena = synth.make_arena(shape, 3, std=0.15)
+    prompt = list(synth.prompts(w)[0])
+    model = dsa.Model(shape, arena)
+    kv = dsa.KVCache(model, 1, w.ctx)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kv.prefill(0, prompt, out)
+    cached_toks, cached_lg = [int(out.item())], [kv.logits().cpu().numpy().copy()]
+    for _ in range(7):
+        kv.decode_step(out, out)
+        cached_toks.append(int(out.item()))
+        cached_lg.append(kv.logits().cpu().numpy().copy())
+    seq = list(prompt)
+    passes = 0
+    for k in range(8):
+        kv.reset(0)
+        kv.prefill(0, seq, out)
+        passes += len(seq)
+        assert int(out.item()) == cached_toks[k]
+        assert np.array_equal(kv.logits().cpu().numpy().view(np.uint32), cached_lg[k].view(np.uint32))
+        seq.append(int(out.item()))
+    assert passes == 68
+
+
+def test_ragged_batch_tiny_matches_oracle():
+    shape = dataclasses.replace(synth.TINY, n_kv_heads=1)
+    arena = synth.make_arena(shape, 4, std=0.15, gain_sigma=0.1)
+    lens = [1, 9, 4, 70, 2, 33, 5]
+    prompts = [synth.random_tokens(100 + i, n, shape.vocab_size) for i, n in enumerate(lens)]
+    compare(shape, arena, prompts, 6, 128, "tiny ragged B=7 batch-prefill")
+    compare(shape, arena, prompts, 3, 128, "tiny ragged B=7 per-slot prefill", use_batch_prefill=False)
+
+
+def test_attention_chunk_boundaries_tiny():
+    """Lengths around multiples of the 64-position attention chunk, up to T."""
+    shape = synth.small_shape(n_kv_heads=2, head_dim=32, dim=128, n_heads=4)
+    arena = synth.make_arena(shape, 8, std=0.15)
+    lens = [63, 64, 65, 127, 128, 129, 190]
+    prompts = [synth.random_tokens(200 + i, n, shape.vocab_size) for i, n in enumerate(lens)]
+    compare(shape, arena, prompts, 2, 192, "tiny chunk edges")
+
+
+def test_135m_p5_matches_oracle():
+    w = synth.WORKLOADS["llama135m_p5"]
+    arena = synth.make_arena(w.model, w.model_seed)
+    compare(w.model, arena, synth.prompts(w), w.decode_calls, w.ctx, "135m p5")
+
+
+def test_errors_are_reported_without_enqueueing():
+    torch = _torch()
+    import decode_step_02_amd as dsa
+    shape = synth.TINY
+    model = dsa.Model(shape, synth.make_arena(shape, 1))
+    kv = dsa.KVCache(model, 2, 8)
+    out = torch.zeros(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(dsa.DSError) as e:
+        kv.prefill(0, [1, 2, 300])
+    assert e.value.status == -5
+    with pytest.raises(dsa.DSError) as e:
+        kv.prefill(2, [1])
+    assert e.value.status == -1
+    kv.prefill(0, [1] * 8)
+    with pytest.raises(dsa.DSError) as e:
+        kv.decode_step(out, out)
+    assert e.value.status == -4
+    assert kv.get_lengths() == [8, 0]
+    kv.set_lengths([3, 0])
+    bad = torch.tensor([5, 999], dtype=torch.int32, device="cuda")
+    kv.decode_step(bad, out)
+    with pytest.raises(dsa.DSError) as e:
+        kv.check()
+    assert e.value.status == -5
+    kv.check()  # the flag was cleared
+    assert kv.lengths.cpu().tolist() == [4, 1]
