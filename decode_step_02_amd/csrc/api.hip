@@ -72,6 +72,9 @@ ds_status check_config(const ds_config* c) {
         return fail(DS_ERR_UNSUPPORTED, "matrix rows must be whole 16-byte chunks");
     const size_t lds = sizeof(float) * std::max(std::max(c->dim, c->n_heads * c->head_dim), c->hidden_dim);
     if (lds > 160 * 1024) return fail(DS_ERR_UNSUPPORTED, "activation vector exceeds 160 KiB of LDS");
+    // vocabulary blocks of 4 waves, 64/G rows per wave (G <= 32): at least 8 rows per block
+    if ((static_cast<int64_t>(c->vocab_size) + 7) / 8 > ds::kMaxArgmaxBlocks)
+        return fail(DS_ERR_UNSUPPORTED, "vocab_size above %d", 8 * ds::kMaxArgmaxBlocks);
     return DS_OK;
 }
 
@@ -127,7 +130,7 @@ WsLayout ws_layout(const ds_config* c, int B, int T) {
     w.part_o = take(sizeof(float) * B * c->n_heads * S * c->head_dim);
     w.part_ml = take(sizeof(float) * B * c->n_heads * S * 2);
     w.logits = take(sizeof(float) * B * static_cast<size_t>(c->vocab_size));
-    w.keys = take(sizeof(unsigned long long) * B);
+    w.keys = take(sizeof(unsigned long long) * B * static_cast<size_t>(ds::kMaxArgmaxBlocks));
     w.slot = take(sizeof(int32_t) * B);
     w.pos = take(sizeof(int32_t) * B);
     w.flag = take(sizeof(int32_t) * B);
@@ -148,6 +151,7 @@ struct ds_model {
 };
 
 struct GraphEntry {
+    int nload;
     hipStream_t stream;
     const int32_t* tok_in;
     int32_t* tok_out;
@@ -166,6 +170,7 @@ struct ds_kv {
     std::vector<int32_t> mirror;  // host copy of lengths, updated at enqueue
     int dispatch;                 // 0 eager, 1 graph
     bool stepped = false;         // a decode step has filled the per-item state
+    int last_nload = 0;           // short-path rows of the last decode step (0: split-K path)
     std::vector<GraphEntry> graphs;
 };
 
@@ -259,10 +264,14 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
         return fail(DS_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    // Dynamic LDS above 64 KiB (activation vectors longer than 16384 floats)
-    // needs the per-kernel opt-in, up to the device's per-block limit.
-    const int need_lds = static_cast<int>(
-        sizeof(float) * std::max(std::max(c->dim, c->n_heads * c->head_dim), c->hidden_dim));
+    // Dynamic LDS above 64 KiB needs the per-kernel opt-in, up to the device's
+    // per-block limit; the need is computed from the shape below.
+    ds::StepArgs probe{};
+    probe.d = c->dim;
+    probe.H = c->n_heads;
+    probe.D = c->head_dim;
+    probe.F = c->hidden_dim;
+    const int need_lds = static_cast<int>(ds::max_lds_bytes(probe));
     static int attr_lds = 64 * 1024;
     if (need_lds > attr_lds) {
         int dev = 0, optin = 0;
@@ -270,8 +279,7 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
         if (e == hipSuccess) e = hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev);
         if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
         if (need_lds > optin - 1024)
-            return fail(DS_ERR_UNSUPPORTED, "activation vector needs %d bytes of LDS, device allows %d", need_lds,
-                        optin);
+            return fail(DS_ERR_UNSUPPORTED, "kernels need %d bytes of LDS, the device allows %d", need_lds, optin);
         e = ds::set_kernel_attributes(need_lds);
         if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
         attr_lds = need_lds;
@@ -324,6 +332,9 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     s.B = B;
     s.T = T;
     s.n_chunks = (T + ds::kChunk - 1) / ds::kChunk;
+    s.short_n = ds::short_positions(s);
+    const char* sa = std::getenv("DS_SHORT_ATTN");  // "0" turns the fused short-context path off
+    if (sa && std::strcmp(sa, "0") == 0) s.short_n = 0;
     s.eps = c->norm_eps;
     s.emb = model->ptrs.emb;
     s.cache = d_cache;
@@ -418,7 +429,8 @@ ds_status ds_prefill(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_t
     for (int j = 0; j < n; j++) {
         list.tok[0] = h_tokens[j];
         list.last[0] = j == n - 1;
-        hipError_t e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, nullptr, 1, j == n - 1, d_tok_out, st);
+        const int nload = ds::short_rows(kv->s, kv->mirror[seq] + j + 1);
+        hipError_t e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, nullptr, 1, j == n - 1, nload, d_tok_out, st);
         if (e != hipSuccess) return hip_fail(e, "prefill");
     }
     kv->mirror[seq] += n;
@@ -451,6 +463,7 @@ ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens, 
         lists.clear();
         int items = 0;
         bool any_last = false;
+        int max_ctx = 0;
         for (int b = 0; b < B; b++) {
             if (h_counts[b] <= j) continue;
             if (lists.empty() || lists.back().n == ds::kMaxItems) {
@@ -463,11 +476,13 @@ ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens, 
             l.tok[l.n] = h_tokens[start[b] + j];
             l.last[l.n] = (j == h_counts[b] - 1);
             any_last |= l.last[l.n] != 0;
+            max_ctx = std::max(max_ctx, kv->mirror[b] + j + 1);
             l.n++;
             items++;
         }
         hipError_t e = ds::enqueue_step(kv->s, model->ptrs, lists.data(), static_cast<int>(lists.size()),
-                                        nullptr, items, any_last, d_tok_out, st);
+                                        nullptr, items, any_last, ds::short_rows(kv->s, max_ctx), d_tok_out,
+                                        st);
         if (e != hipSuccess) return hip_fail(e, "prefill_batch");
     }
     for (int b = 0; b < B; b++) kv->mirror[b] += h_counts[b];
@@ -487,16 +502,20 @@ ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, in
     list.n = kv->B;
     list.item0 = 0;
     list.by_value = 0;
+    int max_ctx = 0;
+    for (int b = 0; b < kv->B; b++) max_ctx = std::max(max_ctx, kv->mirror[b] + 1);
+    const int nload = ds::short_rows(kv->s, max_ctx);
     hipError_t e = hipSuccess;
     if (kv->dispatch == 1 && st != nullptr) {
         GraphEntry* ge = nullptr;
         for (GraphEntry& g : kv->graphs)
-            if (g.stream == st && g.tok_in == d_tok_in && g.tok_out == d_tok_out) ge = &g;
+            if (g.nload == nload && g.stream == st && g.tok_in == d_tok_in && g.tok_out == d_tok_out) ge = &g;
         if (!ge) {
-            GraphEntry g{st, d_tok_in, d_tok_out, nullptr, nullptr};
+            GraphEntry g{nload, st, d_tok_in, d_tok_out, nullptr, nullptr};
             e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
             if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
-            hipError_t ee = ds::enqueue_step(kv->s, model->ptrs, &list, 1, d_tok_in, kv->B, true, d_tok_out, st);
+            hipError_t ee = ds::enqueue_step(kv->s, model->ptrs, &list, 1, d_tok_in, kv->B, true, nload, d_tok_out,
+                                             st);
             e = hipStreamEndCapture(st, &g.graph);
             if (ee != hipSuccess) return hip_fail(ee, "capture decode step");
             if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
@@ -511,11 +530,12 @@ ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, in
         e = hipGraphLaunch(ge->exec, st);
         if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
     } else {
-        e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, d_tok_in, kv->B, true, d_tok_out, st);
+        e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, d_tok_in, kv->B, true, nload, d_tok_out, st);
         if (e != hipSuccess) return hip_fail(e, "decode step");
     }
     for (int b = 0; b < kv->B; b++) kv->mirror[b] += 1;
     kv->stepped = true;
+    kv->last_nload = nload;
     return ok();
 }
 
@@ -528,7 +548,9 @@ ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t lay
     if (reps < 1) return fail(DS_ERR_INVALID_ARG, "reps must be positive");
     hipStream_t st = static_cast<hipStream_t>(stream);
     for (int r = 0; r < reps; r++) {
-        hipError_t e = ds::enqueue_kernel(which, layer, kv->s, model->ptrs, kv->B, st);
+        if (kv->last_nload > 0 && (which == ds::K_ATTN || which == ds::K_COMBINE))
+            return fail(DS_ERR_STATE, "kernel %d is not part of a short-context step", which);
+        hipError_t e = ds::enqueue_kernel(which, layer, kv->s, model->ptrs, kv->B, kv->last_nload, st);
         if (e != hipSuccess) return hip_fail(e, "bench kernel");
     }
     return ok();

@@ -10,11 +10,13 @@ namespace ds {
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
-constexpr int kChunk = 64;       // cache positions per attention block
+constexpr int kChunk = 64;       // cache positions per split-K attention block
+constexpr int kShort = 64;       // contexts up to this many positions use the fused short path
 constexpr int kMaxRep = 8;       // query heads per key/value head
-constexpr int kMaxD = 256;       // head_dim limit of the attention kernel
+constexpr int kMaxD = 256;       // head_dim limit of the attention kernels
 constexpr int kMaxItems = 64;    // items per k_begin launch
 constexpr int kSetChunk = 128;   // lengths per k_set_lengths launch
+constexpr int kMaxArgmaxBlocks = 16384;  // vocabulary blocks per item (argmax partials)
 
 // Per-layer weight pointers (device), into the caller's arena.
 struct LayerW {
@@ -40,6 +42,7 @@ struct ModelPtrs {
 struct StepArgs {
     int d, L, H, Hkv, D, F, V, wdt;
     int B, T, n_chunks;
+    int short_n;         // contexts up to this many positions take the fused short path (0: never)
     float eps;
     const void* emb;
     float* cache;        // (L, 2, B, Hkv, T, D)
@@ -52,7 +55,7 @@ struct StepArgs {
     float* part_o;       // [items][H][n_chunks][D]
     float* part_ml;      // [items][H][n_chunks][2]
     float* logits;       // [B][V] by slot
-    unsigned long long* keys;  // [items] argmax keys
+    unsigned long long* keys;  // [items][kMaxArgmaxBlocks] argmax partials
     int32_t* slot;       // [items]
     int32_t* pos;        // [items]
     int32_t* flag;       // [items] 1: this item's logits and token are wanted
@@ -78,17 +81,37 @@ struct SetList {
     int32_t val[kSetChunk];
 };
 
-size_t attn_lds_bytes();
+// Kernel ids for enqueue_kernel (diagnostics)
+enum KernelId { K_QKV = 0, K_ATTN = 1, K_COMBINE = 2, K_WO = 3, K_W13 = 4, K_W2 = 5, K_LOGITS = 6 };
+
 hipError_t set_kernel_attributes(int max_lds_bytes);
+// One decode / prefill position for n_items items.  nload > 0: every item's
+// context (pos + 1) is at most nload (<= short_n), and attention runs inside
+// the Wo kernel on nload staged cache rows; nload == 0: split-K attention.
+// d_tok_in != NULL marks a decode step (item i is slot i).
 hipError_t enqueue_step(const StepArgs& s, const ModelPtrs& m, const BeginList* lists, int n_lists,
-                        const int32_t* d_tok_in, int n_items, bool need_logits,
+                        const int32_t* d_tok_in, int n_items, bool need_logits, int nload,
                         int32_t* d_tok_out, hipStream_t st);
-// One launch of a single step kernel (0 qkv, 1 attn, 2 combine, 3 wo, 4 w13,
-// 5 w2, 6 logits) with the arguments of a decode step over n_items items.
-hipError_t enqueue_kernel(int which, int layer, const StepArgs& s, const ModelPtrs& m, int n_items,
+// One launch of a single step kernel with the arguments of a decode step
+// over n_items items (hipErrorInvalidValue if the kernel is not part of the
+// step in that mode).
+hipError_t enqueue_kernel(int which, int layer, const StepArgs& s, const ModelPtrs& m, int n_items, int nload,
                           hipStream_t st);
+// Rows to stage for the short path given the longest context of a step:
+// the smallest power of two >= max_ctx (at least 8, at most short_n, itself
+// a power of two); 0 when max_ctx > short_n (split-K path).
+inline int short_rows(const StepArgs& s, int max_ctx) {
+    if (max_ctx > s.short_n) return 0;
+    int n = 8;
+    while (n < max_ctx) n *= 2;
+    return n < s.short_n ? n : s.short_n;
+}
 hipError_t enqueue_set_lengths(int32_t* d_lengths, const int32_t* h_vals, int first, int n,
                                hipStream_t st);
 hipError_t enqueue_fill(int32_t* p, int n, int32_t v, hipStream_t st);
+size_t max_lds_bytes(const StepArgs& s);
+// Longest context (a power of two <= min(kShort, T)) whose short-path staging fits in
+// 64 KiB of LDS; 0 if head_dim/4 is not a power of two.
+int short_positions(const StepArgs& s);
 
 }  // namespace ds

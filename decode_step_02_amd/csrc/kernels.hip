@@ -1,14 +1,13 @@
 // kernels.hip -- gfx950 kernels of the single-token Llama decode step.
 //
-// One decode step for n_items sequences (work items) is:
+// One decode position for n_items sequences (work items) is:
 //   k_begin                      embedding gather + widen, step bookkeeping
 //   per layer: k_qkv             RMSNorm -> Q/K/V GEMV -> RoPE -> K/V append
-//              k_attn            split-K grouped-query attention partials
-//              k_attn_combine    merge of the split-K partials
-//              k_wo              Wo GEMV + residual
+//              [long contexts]   k_attn (split-K partials) + k_attn_combine
+//              k_wo              [short contexts: attention itself] Wo GEMV + residual
 //              k_w13             RMSNorm -> W1/W3 GEMV -> silu(a)*u
 //              k_w2              W2 GEMV + residual
-//   k_logits                     RMSNorm -> vocabulary GEMV -> argmax partials
+//   k_logits                     RMSNorm -> vocabulary GEMV -> per-block argmax
 //   k_finalize                   greedy token, lengths += 1
 // The block structure is the pre-norm Llama block of "simple-llm / kasahare"
 // (PyPI README 0.4.0), section "Architecture"; the cache is the
@@ -19,56 +18,62 @@
 // covers R = 64/G output rows with G lanes per row.  Lane (r, sub) streams
 // 16-byte chunks sub, sub+G, sub+2G, ... of its row, so the G lanes of a row
 // read G*16 contiguous bytes per load and a wave issues 64 fully used 16-byte
-// loads per instruction.  bf16 chunks are widened in registers by a 16-bit
-// shift ("GOTOken: An Inference Engine in QBasic", section "Loading the model
-// and tokenizer") and accumulated in fp32 against the activation vector,
-// which the workgroup stages once in LDS.  The G partial sums of a row are
-// combined with xor shuffles inside the wave; no LDS or atomics are needed
-// for the reduction.
+// loads per instruction.  The first kPrefetch chunks of every lane are loaded
+// into registers before the block stages its activation vector, so the
+// weight stream is in flight while the RMSNorm prologue runs.  bf16 chunks
+// are widened in registers by a 16-bit shift ("GOTOken: An Inference Engine
+// in QBasic", section "Loading the model and tokenizer") and accumulated in
+// fp32 against the LDS copy of the activation vector; the G partial sums of
+// a row are combined with xor shuffles inside the wave.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "kernels.h"
 
 namespace ds {
 
-constexpr int kBlock = 256;  // 4 waves of 64
+constexpr int kPrefetch = 12;  // 16-byte chunks per lane loaded before the prologue
 
-// ---- weight chunk loads ------------------------------------------------------
+// ---- weight chunks ---------------------------------------------------------------
 
 template <int WDT> struct Wt;
 
 template <> struct Wt<kBF16> {
     static constexpr int EPC = 8;  // elements per 16-byte chunk
-    __device__ static __forceinline__ void load(const void* base, size_t elem, float (&w)[8]) {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
-        w[0] = __uint_as_float(u.x << 16); w[1] = __uint_as_float(u.x & 0xFFFF0000u);
-        w[2] = __uint_as_float(u.y << 16); w[3] = __uint_as_float(u.y & 0xFFFF0000u);
-        w[4] = __uint_as_float(u.z << 16); w[5] = __uint_as_float(u.z & 0xFFFF0000u);
-        w[6] = __uint_as_float(u.w << 16); w[7] = __uint_as_float(u.w & 0xFFFF0000u);
+    __device__ static __forceinline__ uint4 load(const void* base, size_t elem) {
+        return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    }
+    __device__ static __forceinline__ float dot(const uint4 u, const float* xs, float acc) {
+        const float4 a = *reinterpret_cast<const float4*>(xs);
+        const float4 b = *reinterpret_cast<const float4*>(xs + 4);
+        acc = fmaf(__uint_as_float(u.x << 16), a.x, acc);
+        acc = fmaf(__uint_as_float(u.x & 0xFFFF0000u), a.y, acc);
+        acc = fmaf(__uint_as_float(u.y << 16), a.z, acc);
+        acc = fmaf(__uint_as_float(u.y & 0xFFFF0000u), a.w, acc);
+        acc = fmaf(__uint_as_float(u.z << 16), b.x, acc);
+        acc = fmaf(__uint_as_float(u.z & 0xFFFF0000u), b.y, acc);
+        acc = fmaf(__uint_as_float(u.w << 16), b.z, acc);
+        acc = fmaf(__uint_as_float(u.w & 0xFFFF0000u), b.w, acc);
+        return acc;
     }
 };
 
 template <> struct Wt<kF32> {
     static constexpr int EPC = 4;
-    __device__ static __forceinline__ void load(const void* base, size_t elem, float (&w)[4]) {
-        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
-        w[0] = f.x; w[1] = f.y; w[2] = f.z; w[3] = f.w;
+    __device__ static __forceinline__ uint4 load(const void* base, size_t elem) {
+        return *reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
+    }
+    __device__ static __forceinline__ float dot(const uint4 u, const float* xs, float acc) {
+        const float4 a = *reinterpret_cast<const float4*>(xs);
+        acc = fmaf(__uint_as_float(u.x), a.x, acc);
+        acc = fmaf(__uint_as_float(u.y), a.y, acc);
+        acc = fmaf(__uint_as_float(u.z), a.z, acc);
+        acc = fmaf(__uint_as_float(u.w), a.w, acc);
+        return acc;
     }
 };
-
-template <int EPC>
-__device__ __forceinline__ float dot_chunk(const float (&w)[EPC], const float* xs, float acc) {
-#pragma unroll
-    for (int e = 0; e < EPC; e += 4) {
-        const float4 xv = *reinterpret_cast<const float4*>(xs + e);
-        acc = fmaf(w[e + 0], xv.x, acc);
-        acc = fmaf(w[e + 1], xv.y, acc);
-        acc = fmaf(w[e + 2], xv.z, acc);
-        acc = fmaf(w[e + 3], xv.w, acc);
-    }
-    return acc;
-}
 
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
@@ -77,36 +82,67 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-// Partial dot product of one row (lane `sub` of its G-lane group) with the
-// LDS vector xs; `valid` == false makes the lane contribute 0 (masked rows).
+// One lane's share of one row: the first kPrefetch chunks are loaded by
+// start(), the rest while finish() accumulates.  finish() returns the full
+// row dot product in every lane of the row's G-lane group.
 template <int WDT, int G>
-__device__ __forceinline__ float row_dot(const void* W, size_t row, int K, const float* xs,
-                                         int sub, bool valid) {
-    constexpr int EPC = Wt<WDT>::EPC;
-    const int nch = valid ? K / EPC : 0;
-    const size_t base = row * static_cast<size_t>(K);
-    float a0 = 0.f, a1 = 0.f;
-    int c = sub;
-    for (; c + 3 * G < nch; c += 4 * G) {
-        float w0[EPC], w1[EPC], w2[EPC], w3[EPC];
-        Wt<WDT>::load(W, base + static_cast<size_t>(c) * EPC, w0);
-        Wt<WDT>::load(W, base + static_cast<size_t>(c + G) * EPC, w1);
-        Wt<WDT>::load(W, base + static_cast<size_t>(c + 2 * G) * EPC, w2);
-        Wt<WDT>::load(W, base + static_cast<size_t>(c + 3 * G) * EPC, w3);
-        a0 = dot_chunk<EPC>(w0, xs + c * EPC, a0);
-        a1 = dot_chunk<EPC>(w1, xs + (c + G) * EPC, a1);
-        a0 = dot_chunk<EPC>(w2, xs + (c + 2 * G) * EPC, a0);
-        a1 = dot_chunk<EPC>(w3, xs + (c + 3 * G) * EPC, a1);
-    }
-    for (; c < nch; c += G) {
-        float w0[EPC];
-        Wt<WDT>::load(W, base + static_cast<size_t>(c) * EPC, w0);
-        a0 = dot_chunk<EPC>(w0, xs + c * EPC, a0);
-    }
-    return group_sum<G>(a0 + a1);
-}
+struct RowStream {
+    static constexpr int EPC = Wt<WDT>::EPC;
+    uint4 w[kPrefetch];
+    const void* W;
+    size_t base;
+    int nch, sub;
 
-// ---- block helpers -------------------------------------------------------------
+    // Loads are unconditional (the chunk index is clamped into the row, the
+    // value masked afterwards): a guarded load becomes a branch, and the
+    // compiler then waits for every load before the next one.
+    __device__ __forceinline__ void start(const void* W_, size_t row, int K, int sub_, bool valid) {
+        W = W_;
+        base = row * static_cast<size_t>(K);
+        sub = sub_;
+        nch = valid ? K / EPC : 0;
+        const int last = K / EPC - 1;
+#pragma unroll
+        for (int p = 0; p < kPrefetch; p++) {
+            const int c = sub + p * G;
+            w[p] = Wt<WDT>::load(W, base + static_cast<size_t>(min(c, last)) * EPC);
+        }
+#pragma unroll
+        for (int p = 0; p < kPrefetch; p++) {
+            const bool keep = sub + p * G < nch;
+            w[p].x = keep ? w[p].x : 0u;
+            w[p].y = keep ? w[p].y : 0u;
+            w[p].z = keep ? w[p].z : 0u;
+            w[p].w = keep ? w[p].w : 0u;
+        }
+    }
+
+    __device__ __forceinline__ float finish(const float* xs) const {
+        float a0 = 0.f, a1 = 0.f;
+        const int last = nch > 0 ? nch - 1 : 0;
+#pragma unroll
+        for (int p = 0; p < kPrefetch; p += 2) {
+            // masked chunks are zero; the LDS index is clamped so it stays in range
+            a0 = Wt<WDT>::dot(w[p], xs + min(sub + p * G, last) * EPC, a0);
+            if (p + 1 < kPrefetch) a1 = Wt<WDT>::dot(w[p + 1], xs + min(sub + (p + 1) * G, last) * EPC, a1);
+        }
+        int c = sub + kPrefetch * G;
+        for (; c + 3 * G < nch; c += 4 * G) {
+            const uint4 u0 = Wt<WDT>::load(W, base + static_cast<size_t>(c) * EPC);
+            const uint4 u1 = Wt<WDT>::load(W, base + static_cast<size_t>(c + G) * EPC);
+            const uint4 u2 = Wt<WDT>::load(W, base + static_cast<size_t>(c + 2 * G) * EPC);
+            const uint4 u3 = Wt<WDT>::load(W, base + static_cast<size_t>(c + 3 * G) * EPC);
+            a0 = Wt<WDT>::dot(u0, xs + c * EPC, a0);
+            a1 = Wt<WDT>::dot(u1, xs + (c + G) * EPC, a1);
+            a0 = Wt<WDT>::dot(u2, xs + (c + 2 * G) * EPC, a0);
+            a1 = Wt<WDT>::dot(u3, xs + (c + 3 * G) * EPC, a1);
+        }
+        for (; c < nch; c += G) a0 = Wt<WDT>::dot(Wt<WDT>::load(W, base + static_cast<size_t>(c) * EPC), xs + c * EPC, a0);
+        return group_sum<G>(a0 + a1);
+    }
+};
+
+// ---- block helpers -------------------------------------------------------------------
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -120,39 +156,106 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Sum over the 256 threads of a block; every thread gets the result.
-__device__ __forceinline__ float block_sum(float v, float* red4) {
+template <int WAVES>
+__device__ __forceinline__ float block_sum(float v, float* red) {
     v = wave_sum(v);
+    if (WAVES == 1) return v;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) red[wave] = v;
     __syncthreads();
-    if (lane == 0) red4[wave] = v;
-    __syncthreads();
-    return red4[0] + red4[1] + red4[2] + red4[3];
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; w++) t += red[w];
+    return t;
 }
 
-// Stage y = g * (x / sqrt(mean(x^2) + eps)) into LDS (RMSNorm, read as in
-// "simple-llm / kasahare", section "Architecture": attn_norm / ffn_norm).
-__device__ __forceinline__ void stage_rmsnorm(const float* __restrict__ x,
-                                              const float* __restrict__ g, int n, float eps,
-                                              float* xs, float* red4) {
-    float ss = 0.f;
-    for (int j = threadIdx.x; j < n; j += kBlock) {
-        const float v = x[j];
-        ss = fmaf(v, v, ss);
+// Two-phase staging of an n-float activation vector (n % 4 == 0) into LDS.
+// issue() starts the first round of independent 16-byte loads (and of the
+// matching gains when GAIN), so the caller can put other loads in flight
+// before complete_*() waits; vectors longer than U*NT float4 take further
+// rounds inside complete_*().
+template <int NT, int U, bool GAIN>
+struct VecStage {
+    float4 xv[U];
+    float4 gv[GAIN ? U : 1];
+    const float4* x4;
+    const float4* g4;
+    int n4;
+
+    __device__ __forceinline__ void issue(const float* x, const float* g, int n) {
+        x4 = reinterpret_cast<const float4*>(x);
+        g4 = reinterpret_cast<const float4*>(g);
+        n4 = n >> 2;
+#pragma unroll
+        for (int u = 0; u < U; u++) {  // unconditional loads of a clamped index
+            const int j = min(static_cast<int>(threadIdx.x) + u * NT, n4 - 1);
+            xv[u] = x4[j];
+            if (GAIN) gv[u] = g4[j];
+        }
     }
-    ss = block_sum(ss, red4);
-    const float r = 1.0f / sqrtf(ss / static_cast<float>(n) + eps);
-    for (int j = threadIdx.x; j < n; j += kBlock) xs[j] = g[j] * (r * x[j]);
-    __syncthreads();
-}
 
-__device__ __forceinline__ void stage_copy(const float* __restrict__ x, int n, float* xs) {
-    for (int j = threadIdx.x; j < n; j += kBlock) xs[j] = x[j];
-    __syncthreads();
-}
+    // xs = g * (x * r), r = 1 / sqrt(mean(x^2) + eps): the RMSNorm of
+    // "simple-llm / kasahare", section "Architecture" (attn_norm / ffn_norm).
+    template <int WAVES>
+    __device__ __forceinline__ void complete_rms(float* xs, float* red, int n, float eps) {
+        float4* s4 = reinterpret_cast<float4*>(xs);
+        float ss = 0.f;
+        auto put = [&](const float4 v, const float4 gg, int j) {
+            ss = fmaf(v.x, v.x, ss);
+            ss = fmaf(v.y, v.y, ss);
+            ss = fmaf(v.z, v.z, ss);
+            ss = fmaf(v.w, v.w, ss);
+            s4[j] = make_float4(gg.x * v.x, gg.y * v.y, gg.z * v.z, gg.w * v.w);
+        };
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int j = threadIdx.x + u * NT;
+            if (j < n4) put(xv[u], gv[GAIN ? u : 0], j);
+        }
+        for (int base = threadIdx.x + U * NT; base < n4; base += U * NT) {
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int j = base + u * NT;
+                if (j < n4) {
+                    xv[u] = x4[j];
+                    gv[GAIN ? u : 0] = g4[j];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int j = base + u * NT;
+                if (j < n4) put(xv[u], gv[GAIN ? u : 0], j);
+            }
+        }
+        ss = block_sum<WAVES>(ss, red);
+        const float r = 1.0f / sqrtf(ss / static_cast<float>(n) + eps);
+        for (int j = threadIdx.x; j < n4; j += NT) {
+            const float4 v = s4[j];
+            s4[j] = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+        }
+        __syncthreads();
+    }
 
-__device__ __forceinline__ size_t cache_row(const StepArgs& s, int layer, int kv, int slot, int g,
-                                            int t) {
+    __device__ __forceinline__ void complete_copy(float* xs) {
+        float4* s4 = reinterpret_cast<float4*>(xs);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int j = threadIdx.x + u * NT;
+            if (j < n4) s4[j] = xv[u];
+        }
+        for (int base = threadIdx.x + U * NT; base < n4; base += U * NT) {
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (base + u * NT < n4) xv[u] = x4[base + u * NT];
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (base + u * NT < n4) s4[base + u * NT] = xv[u];
+        }
+        __syncthreads();
+    }
+};
+
+__device__ __forceinline__ size_t cache_row(const StepArgs& s, int layer, int kv, int slot, int g, int t) {
     size_t i = static_cast<size_t>(layer);
     i = i * 2 + kv;
     i = i * s.B + slot;
@@ -161,12 +264,10 @@ __device__ __forceinline__ size_t cache_row(const StepArgs& s, int layer, int kv
     return i * s.D;
 }
 
-// ---- k_begin: embedding gather -------------------------------------------------
-// x[item] = widen(token_emb[tok]); records the slot, position and flags of the
-// item and clears its argmax cell.  Token ids outside [0, V) raise the error
-// word and read row 0 instead.
-__global__ __launch_bounds__(kBlock) void k_begin(StepArgs s, BeginList list,
-                                                   const int32_t* __restrict__ d_tok_in) {
+// ---- k_begin: embedding gather -------------------------------------------------------
+// x[item] = widen(token_emb[tok]); records the slot, position and flag of the
+// item.  Token ids outside [0, V) raise the error word and read row 0 instead.
+__global__ __launch_bounds__(256) void k_begin(StepArgs s, BeginList list, const int32_t* __restrict__ d_tok_in) {
     const int li = blockIdx.x;
     if (li >= list.n) return;
     const int item = list.item0 + li;
@@ -181,80 +282,186 @@ __global__ __launch_bounds__(kBlock) void k_begin(StepArgs s, BeginList list,
         s.slot[item] = slot;
         s.pos[item] = pos;
         s.flag[item] = list.by_value ? list.last[li] : 1;
-        s.keys[item] = 0ull;
     }
     float* x = s.x + static_cast<size_t>(item) * s.d;
     const size_t row = static_cast<size_t>(tok) * s.d;
     if (s.wdt == kBF16) {
         const uint16_t* e = static_cast<const uint16_t*>(s.emb) + row;
-        for (int j = threadIdx.x; j < s.d; j += kBlock)
-            x[j] = __uint_as_float(static_cast<uint32_t>(e[j]) << 16);
+        for (int j = threadIdx.x; j < s.d; j += 256) x[j] = __uint_as_float(static_cast<uint32_t>(e[j]) << 16);
     } else {
         const float* e = static_cast<const float*>(s.emb) + row;
-        for (int j = threadIdx.x; j < s.d; j += kBlock) x[j] = e[j];
+        for (int j = threadIdx.x; j < s.d; j += 256) x[j] = e[j];
     }
 }
 
-// ---- k_qkv ---------------------------------------------------------------------
+// ---- k_qkv -----------------------------------------------------------------------------
 // Wave tasks: q rows, then k rows, then v rows, R rows per task.  In the q
-// and k sections a task holds R/2 RoPE pairs (i, i + D/2) of a head ("GOTOken",
-// section "Loading the model and tokenizer": pairs j and j + head_dim/2): rows
-// of the first halves in row slots 0..R/2-1, their partners R/2 rows later,
-// i.e. exactly 32 lanes away, so the rotation is one xor-32 shuffle.
-template <int WDT, int G>
-__global__ __launch_bounds__(kBlock) void k_qkv(StepArgs s, LayerW w, int layer) {
+// and k sections a task holds R/2 RoPE pairs (i, i + D/2) of a head
+// ("GOTOken", section "Loading the model and tokenizer": pairs j and
+// j + head_dim/2): first halves in row slots 0..R/2-1, their partners R/2
+// rows later, i.e. exactly 32 lanes away, so the rotation is one xor-32
+// shuffle.  Rotated q goes to the workspace, rotated k and v to the cache at
+// the item's position.
+template <int WDT, int G, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_qkv(StepArgs s, LayerW w, int layer, int ident) {
     extern __shared__ float xs[];
-    __shared__ float red4[4];
+    __shared__ float red[WAVES];
     constexpr int R = 64 / G;
     const int item = blockIdx.y;
-    stage_rmsnorm(s.x + static_cast<size_t>(item) * s.d, w.attn_norm, s.d, s.eps, xs, red4);
+    const int pos = s.pos[item];
+    const int slot = ident ? item : s.slot[item];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int task = blockIdx.x * 4 + wave;
+    const int task = blockIdx.x * WAVES + wave;
     const int D = s.D, half_d = s.D / 2;
     const int nq = s.H * D / R, nk = s.Hkv * D / R, nv = nk;
-    if (task >= nq + nk + nv) return;
+    const bool valid = task < nq + nk + nv;
     const int rs = lane / G, sub = lane % G;
-    const int slot = s.slot[item], pos = s.pos[item];
-    if (task < nq + nk) {
-        const bool is_q = task < nq;
+    const bool roped = task < nq + nk;
+    const bool is_q = task < nq;
+    int row, i = 0, second = 0;
+    const void* W;
+    if (roped) {
         const int t = is_q ? task : task - nq;
         const int p = t * (R / 2) + (rs % (R / 2));
-        const int second = rs / (R / 2);
-        const int head = p / half_d, i = p % half_d;
-        const int row = head * D + i + second * half_d;
-        const float y = row_dot<WDT, G>(is_q ? w.wq : w.wk, row, s.d, xs, sub, true);
+        second = rs / (R / 2);
+        i = p % half_d;
+        row = (p / half_d) * D + i + second * half_d;
+        W = is_q ? w.wq : w.wk;
+    } else {
+        row = valid ? (task - nq - nk) * R + rs : 0;
+        W = w.wv;
+    }
+    RowStream<WDT, G> st;
+    st.start(W, row, s.d, sub, valid);
+    VecStage<64 * WAVES, 4, true> vs;
+    vs.issue(s.x + static_cast<size_t>(item) * s.d, w.attn_norm, s.d);
+    float c = 1.f, sn = 0.f;
+    if (roped && valid) {
+        c = s.rope_cos[static_cast<size_t>(pos) * half_d + i];
+        sn = s.rope_sin[static_cast<size_t>(pos) * half_d + i];
+    }
+    vs.template complete_rms<WAVES>(xs, red, s.d, s.eps);
+    if (!valid) return;
+    const float y = st.finish(xs);
+    if (roped) {
         const float partner = __shfl_xor(y, 32);
-        const float c = s.rope_cos[static_cast<size_t>(pos) * half_d + i];
-        const float sn = s.rope_sin[static_cast<size_t>(pos) * half_d + i];
         // pair (a, b) -> (a c - b s, a s + b c)
         const float out = second ? fmaf(partner, sn, y * c) : fmaf(-partner, sn, y * c);
         if (sub == 0) {
             if (is_q) {
                 s.q[static_cast<size_t>(item) * s.H * D + row] = out;
             } else {
-                const int g = row / D, e = row % D;
-                s.cache[cache_row(s, layer, 0, slot, g, pos) + e] = out;
+                s.cache[cache_row(s, layer, 0, slot, row / D, pos) + row % D] = out;
             }
         }
-    } else {
-        const int row = (task - nq - nk) * R + rs;
-        const float y = row_dot<WDT, G>(w.wv, row, s.d, xs, sub, true);
-        if (sub == 0) {
-            const int g = row / D, e = row % D;
-            s.cache[cache_row(s, layer, 1, slot, g, pos) + e] = y;
-        }
+    } else if (sub == 0) {
+        s.cache[cache_row(s, layer, 1, slot, row / D, pos) + row % D] = y;
     }
 }
 
-// ---- k_attn: split-K grouped-query attention -------------------------------------
+// ---- short-context attention (inside the Wo kernel) ----------------------------------------
+// For every query head h (key/value head g = h / (H/Hkv), "simple-llm /
+// kasahare", section "Architecture", GQA): softmax(q_h . K_g[0..n) / sqrt(D))
+// weighted sum of V_g[0..n), for n = pos + 1 <= s.short_n.  q and the n
+// cached K/V rows of every group are staged into LDS with independent 16-byte
+// loads (rows padded to D + 4 floats against bank conflicts); the result
+// o [H*D] is left in LDS for the Wo GEMV.
+template <int WAVES>
+__device__ void attention_short(const StepArgs& s, int layer, int item, int slot, int n, int nload, float* o,
+                                float* lds) {
+    constexpr int NT = 64 * WAVES;
+    const int D = s.D, H = s.H, HD = s.H * s.D, rep = s.H / s.Hkv, Hkv = s.Hkv;
+    const int DP = D + 4, NS = s.short_n;
+    float* qs = lds;                          // [H*D]
+    float* ks = qs + HD;                      // [Hkv][NS][DP]
+    float* vs = ks + Hkv * NS * DP;           // [Hkv][NS][DP]
+    // staging: float4 units -- q, then per group nload rows of K, then of V
+    // (nload >= n is a host-chosen bound, so the loads need not wait for pos)
+    const int D4 = D >> 2, q4 = HD >> 2, rows = Hkv * nload, total = q4 + 2 * rows * D4;
+    const float4* qg = reinterpret_cast<const float4*>(s.q + static_cast<size_t>(item) * HD);
+    constexpr int U = 8;
+    const int lg_d4 = __ffs(D4) - 1, lg_nl = __ffs(nload) - 1;  // D4 and nload are powers of two
+    for (int base = threadIdx.x; base < total; base += U * NT) {
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {  // unconditional loads from clamped indices
+            const int f = min(base + u * NT, total - 1);
+            const int r = max(f - q4, 0) >> lg_d4, c = max(f - q4, 0) & (D4 - 1);
+            const int kv = r >= rows, rr = r - kv * rows, g = rr >> lg_nl, t = rr & (nload - 1);
+            const float4* src = f < q4 ? qg + f
+                                       : reinterpret_cast<const float4*>(s.cache + cache_row(s, layer, kv, slot, g, t)) + c;
+            v[u] = *src;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int f = base + u * NT;
+            if (f < q4) {
+                reinterpret_cast<float4*>(qs)[f] = v[u];
+            } else if (f < total) {
+                const int r = (f - q4) >> lg_d4, c = (f - q4) & (D4 - 1);
+                const int kv = r >= rows, rr = r - kv * rows, g = rr >> lg_nl, t = rr & (nload - 1);
+                *reinterpret_cast<float4*>((kv ? vs : ks) + (g * NS + t) * DP + 4 * c) = v[u];
+            }
+        }
+    }
+    __syncthreads();
+    // one wave per query head: lane t scores position t (n <= 64), the
+    // softmax is a pair of wave reductions, and lane e accumulates output
+    // element e with p_t broadcast from lane t
+    const float scale = 1.0f / sqrtf(static_cast<float>(D));
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int h = wave; h < H; h += WAVES) {
+        const int g = h / rep;
+        const float4* q4p = reinterpret_cast<const float4*>(qs + h * D);
+        float sc_t = -INFINITY;
+        if (lane < n) {
+            const float4* k4 = reinterpret_cast<const float4*>(ks + (g * NS + lane) * DP);
+            float a0 = 0.f, a1 = 0.f;
+            for (int c = 0; c < D4; c += 2) {
+                const float4 k0 = k4[c], qv0 = q4p[c];
+                a0 = fmaf(k0.x, qv0.x, a0); a0 = fmaf(k0.y, qv0.y, a0);
+                a0 = fmaf(k0.z, qv0.z, a0); a0 = fmaf(k0.w, qv0.w, a0);
+                const float4 k1 = k4[c + 1], qv1 = q4p[c + 1];
+                a1 = fmaf(k1.x, qv1.x, a1); a1 = fmaf(k1.y, qv1.y, a1);
+                a1 = fmaf(k1.z, qv1.z, a1); a1 = fmaf(k1.w, qv1.w, a1);
+            }
+            sc_t = (a0 + a1) * scale;
+        }
+        const float m = wave_max(sc_t);
+        const float e_t = lane < n ? __expf(sc_t - m) : 0.f;
+        const float p_t = e_t / wave_sum(e_t);
+        const float* vg = vs + g * NS * DP;
+        const int pbits = __float_as_int(p_t);
+        for (int e0 = 0; e0 < D; e0 += 64) {  // uniform loop; readlane needs every lane's p_t in place
+            const int e = e0 + lane;
+            const bool ok = e < D;
+            float a0 = 0.f, a1 = 0.f;
+            int t = 0;
+            for (; t + 1 < n; t += 2) {
+                const float p0 = __int_as_float(__builtin_amdgcn_readlane(pbits, t));
+                const float p1 = __int_as_float(__builtin_amdgcn_readlane(pbits, t + 1));
+                if (ok) {
+                    a0 = fmaf(p0, vg[t * DP + e], a0);
+                    a1 = fmaf(p1, vg[(t + 1) * DP + e], a1);
+                }
+            }
+            if (t < n) {
+                const float p0 = __int_as_float(__builtin_amdgcn_readlane(pbits, t));
+                if (ok) a0 = fmaf(p0, vg[t * DP + e], a0);
+            }
+            if (ok) o[h * D + e] = a0 + a1;
+        }
+    }
+    __syncthreads();
+}
+
+// ---- long-context attention: split-K partials + combine ------------------------------------
 // Block (chunk, kv group g, item) scores positions [chunk*kChunk, ...) of the
-// item's first pos+1 cached positions against the rep = H/Hkv query heads of
-// group g (query head h uses key/value head h / rep, "simple-llm / kasahare",
-// section "Architecture", GQA), and writes the chunk's softmax partials
-// (running max m, sum l, unnormalised output o) for the combine kernel.
-// Thread layout: LPR = D/4 lanes hold one 16-byte slice each of a key/value
-// row, so K and V rows are read with full 16-byte coalesced loads.
-__global__ __launch_bounds__(kBlock) void k_attn(StepArgs s, int layer) {
+// item's pos+1 cached positions against the rep = H/Hkv query heads of
+// group g and writes the chunk's softmax partials (running max m, sum l,
+// unnormalised output o).  LPR = D/4 lanes hold one 16-byte slice each of a
+// key/value row, so K and V rows are read with full 16-byte coalesced loads.
+__global__ __launch_bounds__(256) void k_attn(StepArgs s, int layer) {
     extern __shared__ float sm[];
     const int chunk = blockIdx.x, g = blockIdx.y, item = blockIdx.z;
     const int pos = s.pos[item], slot = s.slot[item];
@@ -263,23 +470,21 @@ __global__ __launch_bounds__(kBlock) void k_attn(StepArgs s, int layer) {
     if (t0 >= n) return;
     const int nt = min(kChunk, n - t0);
     const int D = s.D, rep = s.H / s.Hkv;
-    const int LPR = D / 4, NRG = kBlock / LPR;
+    const int LPR = D / 4, NRG = 256 / LPR;
     const int e4 = threadIdx.x % LPR, rg = threadIdx.x / LPR;
-    float* qs = sm;                           // [rep][D]
-    float* sc = qs + kMaxRep * kMaxD;         // [rep][kChunk]
-    float* red = sc + kMaxRep * kChunk;       // [kBlock][rep*4] reduction scratch
-    float* ml = red + kBlock * kMaxRep * 4;   // [rep][2]
+    float* qs = sm;                          // [rep][D]
+    float* sc = qs + kMaxRep * kMaxD;        // [rep][kChunk]
+    float* red = sc + kMaxRep * kChunk;      // [rep*4][256] reduction scratch
+    float* ml = red + 256 * kMaxRep * 4;     // [rep][2]
     const float* q = s.q + static_cast<size_t>(item) * s.H * D + static_cast<size_t>(g) * rep * D;
-    for (int j = threadIdx.x; j < rep * D; j += kBlock) qs[j] = q[j];
+    for (int j = threadIdx.x; j < rep * D; j += 256) qs[j] = q[j];
     __syncthreads();
     const float* K = s.cache + cache_row(s, layer, 0, slot, g, t0);
     const float* V = s.cache + cache_row(s, layer, 1, slot, g, t0);
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
-    // scores: rows rg, rg + NRG, ...; the trip count is uniform per LPR group
-    for (int t = rg; t < kChunk; t += NRG) {
+    for (int t = rg; t < kChunk; t += NRG) {  // uniform trip count per LPR group
         const bool ok = t < nt;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (ok) kv = *reinterpret_cast<const float4*>(K + static_cast<size_t>(t) * D + e4 * 4);
+        const float4 kv = *reinterpret_cast<const float4*>(K + static_cast<size_t>(min(t, nt - 1)) * D + e4 * 4);
         for (int j = 0; j < rep; j++) {
             const float4 qv = *reinterpret_cast<const float4*>(qs + j * D + e4 * 4);
             float d = kv.x * qv.x;
@@ -291,7 +496,6 @@ __global__ __launch_bounds__(kBlock) void k_attn(StepArgs s, int layer) {
         }
     }
     __syncthreads();
-    // per head: chunk max and exp-sum (one wave per head)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int j = wave; j < rep; j += 4) {
         float m = -INFINITY;
@@ -310,7 +514,6 @@ __global__ __launch_bounds__(kBlock) void k_attn(StepArgs s, int layer) {
         }
     }
     __syncthreads();
-    // o_j = sum_t p_j[t] * V[t]
     float acc[kMaxRep][4];
     for (int j = 0; j < kMaxRep; j++) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
     for (int t = rg; t < nt; t += NRG) {
@@ -327,15 +530,14 @@ __global__ __launch_bounds__(kBlock) void k_attn(StepArgs s, int layer) {
         }
     }
     for (int j = 0; j < rep; j++)
-        for (int c = 0; c < 4; c++) red[(j * 4 + c) * kBlock + threadIdx.x] = acc[j][c];
+        for (int c = 0; c < 4; c++) red[(j * 4 + c) * 256 + threadIdx.x] = acc[j][c];
     __syncthreads();
-    // sum the NRG row groups; thread -> (j, e)
     const int S = s.n_chunks;
-    for (int idx = threadIdx.x; idx < rep * D; idx += kBlock) {
+    for (int idx = threadIdx.x; idx < rep * D; idx += 256) {
         const int j = idx / D, e = idx % D;
         const int te4 = e / 4, c = e % 4;
         float v = 0.f;
-        for (int r = 0; r < NRG; r++) v += red[(j * 4 + c) * kBlock + r * LPR + te4];
+        for (int r = 0; r < NRG; r++) v += red[(j * 4 + c) * 256 + r * LPR + te4];
         const int h = g * rep + j;
         const size_t pidx = (static_cast<size_t>(item) * s.H + h) * S + chunk;
         s.part_o[pidx * D + e] = v;
@@ -367,104 +569,164 @@ __global__ __launch_bounds__(64) void k_attn_combine(StepArgs s) {
     }
 }
 
-// ---- k_wo: x += Wo o --------------------------------------------------------------
-template <int WDT, int G>
-__global__ __launch_bounds__(kBlock) void k_wo(StepArgs s, LayerW w) {
+// ---- k_wo: x += Wo o --------------------------------------------------------------------
+// SHORT: the block first computes the attention output o of every head
+// itself (all cached rows fit in LDS), so no attention kernel runs.
+template <int WDT, int G, int WAVES, bool SHORT>
+__global__ __launch_bounds__(64 * WAVES) void k_wo(StepArgs s, LayerW w, int layer, int ident, int nload) {
     extern __shared__ float xs[];
     constexpr int R = 64 / G;
     const int item = blockIdx.y;
+    int n = 0, slot = 0;
+    if (SHORT) {
+        n = s.pos[item] + 1;
+        slot = ident ? item : s.slot[item];
+    }
     const int K = s.H * s.D;
-    stage_copy(s.o + static_cast<size_t>(item) * K, K, xs);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row = (blockIdx.x * 4 + wave) * R + lane / G, sub = lane % G;
+    const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.d;
-    const float y = row_dot<WDT, G>(w.wo, valid ? row : 0, K, xs, sub, valid);
-    if (valid && sub == 0) s.x[static_cast<size_t>(item) * s.d + row] += y;
+    RowStream<WDT, G> st;
+    st.start(w.wo, valid ? row : 0, K, sub, valid);
+    float* xr = s.x + static_cast<size_t>(item) * s.d + row;
+    const float x_old = (valid && sub == 0) ? *xr : 0.f;
+    if (SHORT) {
+        if (n > nload) {  // the host picks nload >= every context; guard anyway
+            if (threadIdx.x == 0) atomicOr(s.err, 2);
+            n = nload;
+        }
+        attention_short<WAVES>(s, layer, item, slot, n, nload, xs, xs + K);
+    } else {
+        VecStage<64 * WAVES, 8, false> vs;
+        vs.issue(s.o + static_cast<size_t>(item) * K, nullptr, K);
+        vs.complete_copy(xs);
+    }
+    const float y = st.finish(xs);
+    if (valid && sub == 0) *xr = x_old + y;
 }
 
-// ---- k_w13: h = silu(W1 xn) * (W3 xn) -------------------------------------------
-template <int WDT, int G>
-__global__ __launch_bounds__(kBlock) void k_w13(StepArgs s, LayerW w) {
+// ---- k_w13: h = silu(W1 xn) * (W3 xn) -------------------------------------------------------
+template <int WDT, int G, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_w13(StepArgs s, LayerW w) {
     extern __shared__ float xs[];
-    __shared__ float red4[4];
+    __shared__ float red[WAVES];
     constexpr int R = 64 / G;
     const int item = blockIdx.y;
-    stage_rmsnorm(s.x + static_cast<size_t>(item) * s.d, w.ffn_norm, s.d, s.eps, xs, red4);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row = (blockIdx.x * 4 + wave) * R + lane / G, sub = lane % G;
+    const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.F;
-    const float a = row_dot<WDT, G>(w.w1, valid ? row : 0, s.d, xs, sub, valid);
-    const float u = row_dot<WDT, G>(w.w3, valid ? row : 0, s.d, xs, sub, valid);
+    RowStream<WDT, G> s1, s3;
+    s1.start(w.w1, valid ? row : 0, s.d, sub, valid);
+    s3.start(w.w3, valid ? row : 0, s.d, sub, valid);
+    VecStage<64 * WAVES, 4, true> vs;
+    vs.issue(s.x + static_cast<size_t>(item) * s.d, w.ffn_norm, s.d);
+    vs.template complete_rms<WAVES>(xs, red, s.d, s.eps);
+    const float a = s1.finish(xs);
+    const float u = s3.finish(xs);
     if (valid && sub == 0) {
         const float sig = 1.0f / (1.0f + expf(-a));
         s.h[static_cast<size_t>(item) * s.F + row] = (a * sig) * u;
     }
 }
 
-// ---- k_w2: x += W2 h ----------------------------------------------------------------
-template <int WDT, int G>
-__global__ __launch_bounds__(kBlock) void k_w2(StepArgs s, LayerW w) {
+// ---- k_w2: x += W2 h ------------------------------------------------------------------------
+template <int WDT, int G, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_w2(StepArgs s, LayerW w) {
     extern __shared__ float xs[];
     constexpr int R = 64 / G;
     const int item = blockIdx.y;
-    stage_copy(s.h + static_cast<size_t>(item) * s.F, s.F, xs);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row = (blockIdx.x * 4 + wave) * R + lane / G, sub = lane % G;
+    const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.d;
-    const float y = row_dot<WDT, G>(w.w2, valid ? row : 0, s.F, xs, sub, valid);
-    if (valid && sub == 0) s.x[static_cast<size_t>(item) * s.d + row] += y;
+    RowStream<WDT, G> st;
+    st.start(w.w2, valid ? row : 0, s.F, sub, valid);
+    float* xr = s.x + static_cast<size_t>(item) * s.d + row;
+    const float x_old = (valid && sub == 0) ? *xr : 0.f;
+    VecStage<64 * WAVES, 8, false> vs;
+    vs.issue(s.h + static_cast<size_t>(item) * s.F, nullptr, s.F);
+    vs.complete_copy(xs);
+    const float y = st.finish(xs);
+    if (valid && sub == 0) *xr = x_old + y;
 }
 
-// ---- k_logits: logits = Wcls rmsnorm(x), greedy argmax partials ----------------------
+// ---- k_logits: logits = Wcls rmsnorm(x) and per-block argmax ----------------------------------
 // Argmax key: the float's order-preserving 32-bit image in the high word and
-// (2^32 - 1 - index) in the low word, so one 64-bit atomic max selects the
-// largest logit and, among equal logits, the lowest index ("Inside nanochat
-// Part 4", section "Sampling Strategy": greedy decoding is argmax), whatever
-// order the blocks finish in.
+// (2^32 - 1 - index) in the low word, so the largest key is the largest
+// logit and, among equal logits, the lowest index ("Inside nanochat Part 4",
+// section "Sampling Strategy": greedy decoding is argmax), whatever order
+// the blocks run in.  Every block writes its own key; k_finalize reduces.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
     uint32_t u = __float_as_uint(v);
     u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     return (static_cast<unsigned long long>(u) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - idx);
 }
 
-template <int WDT, int G>
-__global__ __launch_bounds__(kBlock) void k_logits(StepArgs s, const float* __restrict__ out_norm,
-                                                    const void* __restrict__ wcls) {
-    extern __shared__ float xs[];
-    __shared__ float red4[4];
-    constexpr int R = 64 / G;
-    const int item = blockIdx.y;
-    if (!s.flag[item]) return;
-    stage_rmsnorm(s.x + static_cast<size_t>(item) * s.d, out_norm, s.d, s.eps, xs, red4);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row = (blockIdx.x * 4 + wave) * R + lane / G, sub = lane % G;
-    const bool valid = row < s.V;
-    const float y = row_dot<WDT, G>(wcls, valid ? row : 0, s.d, xs, sub, valid);
-    unsigned long long key = 0ull;
-    if (valid && sub == 0) {
-        s.logits[static_cast<size_t>(s.slot[item]) * s.V + row] = y;
-        key = argmax_key(y, row);
-    }
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        const unsigned long long other = __shfl_xor(key, o);
-        key = other > key ? other : key;
+        const unsigned long long other = __shfl_xor(k, o);
+        k = other > k ? other : k;
     }
-    if (lane == 0) atomicMax(s.keys + item, key);
+    return k;
 }
 
-// ---- k_finalize ------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_finalize(StepArgs s, int n_items, int32_t* d_tok_out,
-                                                 int want_tok) {
-    for (int item = threadIdx.x; item < n_items; item += 64) {
-        const int slot = s.slot[item];
-        if (want_tok && s.flag[item] && d_tok_out)
-            d_tok_out[slot] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(s.keys[item]));
-        s.lengths[slot] = s.pos[item] + 1;
+template <int WDT, int G, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_logits(StepArgs s, const float* __restrict__ out_norm,
+                                                       const void* __restrict__ wcls) {
+    extern __shared__ float xs[];
+    __shared__ float red[WAVES];
+    __shared__ unsigned long long kred[WAVES];
+    constexpr int R = 64 / G;
+    const int item = blockIdx.y;
+    const int flag = s.flag[item];
+    const int slot = s.slot[item];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
+    const bool valid = row < s.V;
+    RowStream<WDT, G> st;
+    st.start(wcls, valid ? row : 0, s.d, sub, valid);
+    VecStage<64 * WAVES, 4, true> vs;
+    vs.issue(s.x + static_cast<size_t>(item) * s.d, out_norm, s.d);
+    vs.template complete_rms<WAVES>(xs, red, s.d, s.eps);
+    if (!flag) return;
+    const float y = st.finish(xs);
+    unsigned long long key = 0ull;
+    if (valid && sub == 0) {
+        s.logits[static_cast<size_t>(slot) * s.V + row] = y;
+        key = argmax_key(y, row);
+    }
+    key = wave_max_u64(key);
+    if (lane == 0) kred[wave] = key;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long k = kred[0];
+        for (int i = 1; i < WAVES; i++) k = kred[i] > k ? kred[i] : k;
+        s.keys[static_cast<size_t>(item) * kMaxArgmaxBlocks + blockIdx.x] = k;
     }
 }
 
-// ---- small utility kernels ----------------------------------------------------------------
+// ---- k_finalize: reduce the argmax keys, write the token, advance lengths ------------------------
+__global__ __launch_bounds__(256) void k_finalize(StepArgs s, int n_blocks, int32_t* d_tok_out, int want_tok) {
+    __shared__ unsigned long long kred[4];
+    const int item = blockIdx.x;
+    const int slot = s.slot[item];
+    if (want_tok && s.flag[item] && d_tok_out) {
+        unsigned long long k = 0ull;
+        const unsigned long long* keys = s.keys + static_cast<size_t>(item) * kMaxArgmaxBlocks;
+        for (int i = threadIdx.x; i < n_blocks; i += 256) k = keys[i] > k ? keys[i] : k;
+        k = wave_max_u64(k);
+        if ((threadIdx.x & 63) == 0) kred[threadIdx.x >> 6] = k;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int i = 1; i < 4; i++) k = kred[i] > k ? kred[i] : k;
+            k = kred[0] > k ? kred[0] : k;
+            d_tok_out[slot] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k));
+        }
+    }
+    if (threadIdx.x == 0) s.lengths[slot] = s.pos[item] + 1;
+}
+
+// ---- small utility kernels ------------------------------------------------------------------------
 __global__ void k_set_lengths(int32_t* lengths, SetList l) {
     for (int i = threadIdx.x; i < l.n; i += blockDim.x) lengths[l.first + i] = l.val[i];
 }
@@ -473,7 +735,7 @@ __global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
 }
 
-// ---- launchers ---------------------------------------------------------------------------
+// ---- launch configuration ------------------------------------------------------------------------
 
 static int pick_g(int K, int wdt) {
     const int nch = K / (wdt == kBF16 ? 8 : 4);
@@ -482,125 +744,204 @@ static int pick_g(int K, int wdt) {
     return 32;
 }
 
-template <int WDT, int G>
-static hipError_t launch_gemv_set(int which, const StepArgs& s, const LayerW& w, int layer,
-                                  int n_items, hipStream_t st, const float* out_norm,
-                                  const void* wcls) {
+// one-wave blocks while the staged vector is small, 4-wave blocks (sharing it) beyond 4096 floats
+static int pick_waves(int K) { return K <= 2048 ? 1 : 4; }
+
+size_t short_lds(const StepArgs& s, int short_n) {
+    const size_t HD = static_cast<size_t>(s.H) * s.D;
+    return sizeof(float) * (2 * HD + 2 * static_cast<size_t>(s.Hkv) * short_n * (s.D + 4));
+}
+
+int short_positions(const StepArgs& s) {
+    const int d4 = s.D / 4;
+    if (d4 <= 0 || (d4 & (d4 - 1)) != 0) return 0;  // the staging indexes rows with shifts
+    for (int n = kShort; n >= 1; n /= 2)
+        if (n <= s.T && short_lds(s, n) <= 64 * 1024) return n;
+    return 0;
+}
+
+static size_t attn_lds() {
+    return sizeof(float) * (kMaxRep * kMaxD + kMaxRep * kChunk + 256 * kMaxRep * 4 + kMaxRep * 2);
+}
+
+size_t max_lds_bytes(const StepArgs& s) {
+    size_t m = sizeof(float) * static_cast<size_t>(std::max(std::max(s.d, s.H * s.D), s.F));
+    return std::max(m, attn_lds());
+}
+
+enum Gemv { G_QKV, G_WO_SHORT, G_WO_LONG, G_W13, G_W2, G_LOGITS };
+
+struct Launch {
+    int ident = 0;  // item i is slot i (decode steps)
+    int nload = 0;  // cached rows staged by the short-context attention
+};
+
+template <int WDT, int G, int WAVES>
+static hipError_t launch3(Gemv which, const StepArgs& s, const LayerW& w, int layer, int n_items,
+                          hipStream_t st, const float* out_norm, const void* wcls, Launch lc) {
     constexpr int R = 64 / G;
-    const int rows_per_block = 4 * R;
+    constexpr int RB = WAVES * R;  // rows per block
+    const dim3 blk(64 * WAVES);
     switch (which) {
-        case 0: {
+        case G_QKV: {
             const int tasks = (s.H + 2 * s.Hkv) * s.D / R;
-            hipLaunchKernelGGL((k_qkv<WDT, G>), dim3((tasks + 3) / 4, n_items), dim3(kBlock),
-                               s.d * sizeof(float), st, s, w, layer);
+            hipLaunchKernelGGL((k_qkv<WDT, G, WAVES>), dim3((tasks + WAVES - 1) / WAVES, n_items), blk,
+                               sizeof(float) * s.d, st, s, w, layer, lc.ident);
             break;
         }
-        case 1:
-            hipLaunchKernelGGL((k_wo<WDT, G>), dim3((s.d + rows_per_block - 1) / rows_per_block, n_items),
-                               dim3(kBlock), s.H * s.D * sizeof(float), st, s, w);
+        case G_WO_SHORT:
+            hipLaunchKernelGGL((k_wo<WDT, G, WAVES, true>), dim3((s.d + RB - 1) / RB, n_items), blk,
+                               short_lds(s, s.short_n), st, s, w, layer, lc.ident, lc.nload);
             break;
-        case 2:
-            hipLaunchKernelGGL((k_w13<WDT, G>), dim3((s.F + rows_per_block - 1) / rows_per_block, n_items),
-                               dim3(kBlock), s.d * sizeof(float), st, s, w);
+        case G_WO_LONG:
+            hipLaunchKernelGGL((k_wo<WDT, G, WAVES, false>), dim3((s.d + RB - 1) / RB, n_items), blk,
+                               sizeof(float) * s.H * s.D, st, s, w, layer, lc.ident, 0);
             break;
-        case 3:
-            hipLaunchKernelGGL((k_w2<WDT, G>), dim3((s.d + rows_per_block - 1) / rows_per_block, n_items),
-                               dim3(kBlock), s.F * sizeof(float), st, s, w);
+        case G_W13:
+            hipLaunchKernelGGL((k_w13<WDT, G, WAVES>), dim3((s.F + RB - 1) / RB, n_items), blk,
+                               sizeof(float) * s.d, st, s, w);
             break;
-        case 4:
-            hipLaunchKernelGGL((k_logits<WDT, G>), dim3((s.V + rows_per_block - 1) / rows_per_block, n_items),
-                               dim3(kBlock), s.d * sizeof(float), st, s, out_norm, wcls);
+        case G_W2:
+            hipLaunchKernelGGL((k_w2<WDT, G, WAVES>), dim3((s.d + RB - 1) / RB, n_items), blk,
+                               sizeof(float) * s.F, st, s, w);
+            break;
+        case G_LOGITS:
+            hipLaunchKernelGGL((k_logits<WDT, G, WAVES>), dim3((s.V + RB - 1) / RB, n_items), blk,
+                               sizeof(float) * s.d, st, s, out_norm, wcls);
             break;
     }
     return hipGetLastError();
 }
 
+template <int WDT, int G>
+static hipError_t launch2(Gemv which, int waves, const StepArgs& s, const LayerW& w, int layer, int n_items,
+                          hipStream_t st, const float* out_norm, const void* wcls, Launch lc) {
+    if (waves == 1) return launch3<WDT, G, 1>(which, s, w, layer, n_items, st, out_norm, wcls, lc);
+    return launch3<WDT, G, 4>(which, s, w, layer, n_items, st, out_norm, wcls, lc);
+}
+
 template <int WDT>
-static hipError_t launch_gemv(int which, int K, const StepArgs& s, const LayerW& w, int layer,
-                              int n_items, hipStream_t st, const float* out_norm, const void* wcls) {
+static hipError_t launch1(Gemv which, int K, int waves, const StepArgs& s, const LayerW& w, int layer,
+                          int n_items, hipStream_t st, const float* out_norm, const void* wcls, Launch lc) {
     switch (pick_g(K, WDT)) {
-        case 8: return launch_gemv_set<WDT, 8>(which, s, w, layer, n_items, st, out_norm, wcls);
-        case 16: return launch_gemv_set<WDT, 16>(which, s, w, layer, n_items, st, out_norm, wcls);
-        default: return launch_gemv_set<WDT, 32>(which, s, w, layer, n_items, st, out_norm, wcls);
+        case 8: return launch2<WDT, 8>(which, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
+        case 16: return launch2<WDT, 16>(which, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
+        default: return launch2<WDT, 32>(which, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
     }
 }
 
-static hipError_t gemv(int which, int K, const StepArgs& s, const LayerW& w, int layer, int n_items,
-                       hipStream_t st, const float* out_norm = nullptr, const void* wcls = nullptr) {
-    if (s.wdt == kBF16) return launch_gemv<kBF16>(which, K, s, w, layer, n_items, st, out_norm, wcls);
-    return launch_gemv<kF32>(which, K, s, w, layer, n_items, st, out_norm, wcls);
+// logits always use 4-wave blocks (fewer argmax partials per item)
+static int logits_blocks(const StepArgs& s) {
+    const int R = 64 / pick_g(s.d, s.wdt);
+    return (s.V + 4 * R - 1) / (4 * R);
 }
 
-size_t attn_lds_bytes() {
-    return sizeof(float) * (kMaxRep * kMaxD + kMaxRep * kChunk + kBlock * kMaxRep * 4 + kMaxRep * 2);
+static hipError_t gemv(Gemv which, const StepArgs& s, const LayerW& w, int layer, int n_items, hipStream_t st,
+                       Launch lc, const float* out_norm = nullptr, const void* wcls = nullptr) {
+    int K = s.d;
+    if (which == G_WO_SHORT || which == G_WO_LONG) K = s.H * s.D;
+    if (which == G_W2) K = s.F;
+    int waves = pick_waves(K);
+    if (which == G_LOGITS || which == G_WO_SHORT) waves = 4;
+    if (s.wdt == kBF16) return launch1<kBF16>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
+    return launch1<kF32>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
 }
 
-hipError_t set_kernel_attributes(int max_lds_bytes) {
+template <int WDT, int G, int WAVES>
+static hipError_t set_attrs3(int lds) {
     hipError_t e = hipSuccess;
-#define DS_ATTR(fn)                                                                                  \
-    if (e == hipSuccess)                                                                             \
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),                                   \
-                                hipFuncAttributeMaxDynamicSharedMemorySize, max_lds_bytes);
-#define DS_ATTR_SET(WDT, G)                                                                          \
-    DS_ATTR((k_qkv<WDT, G>)) DS_ATTR((k_wo<WDT, G>)) DS_ATTR((k_w13<WDT, G>))                        \
-    DS_ATTR((k_w2<WDT, G>)) DS_ATTR((k_logits<WDT, G>))
-    DS_ATTR_SET(kBF16, 8) DS_ATTR_SET(kBF16, 16) DS_ATTR_SET(kBF16, 32)
-    DS_ATTR_SET(kF32, 8) DS_ATTR_SET(kF32, 16) DS_ATTR_SET(kF32, 32)
-    DS_ATTR(k_attn)
-#undef DS_ATTR_SET
-#undef DS_ATTR
+    auto one = [&](const void* fn) {
+        if (e == hipSuccess) e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    };
+    one(reinterpret_cast<const void*>(k_qkv<WDT, G, WAVES>));
+    one(reinterpret_cast<const void*>(k_wo<WDT, G, WAVES, true>));
+    one(reinterpret_cast<const void*>(k_wo<WDT, G, WAVES, false>));
+    one(reinterpret_cast<const void*>(k_w13<WDT, G, WAVES>));
+    one(reinterpret_cast<const void*>(k_w2<WDT, G, WAVES>));
+    one(reinterpret_cast<const void*>(k_logits<WDT, G, WAVES>));
     return e;
 }
 
+template <int WDT>
+static hipError_t set_attrs1(int lds) {
+    hipError_t e = set_attrs3<WDT, 8, 1>(lds);
+    if (e == hipSuccess) e = set_attrs3<WDT, 8, 4>(lds);
+    if (e == hipSuccess) e = set_attrs3<WDT, 16, 1>(lds);
+    if (e == hipSuccess) e = set_attrs3<WDT, 16, 4>(lds);
+    if (e == hipSuccess) e = set_attrs3<WDT, 32, 1>(lds);
+    if (e == hipSuccess) e = set_attrs3<WDT, 32, 4>(lds);
+    return e;
+}
+
+hipError_t set_kernel_attributes(int lds) {
+    hipError_t e = set_attrs1<kBF16>(lds);
+    if (e == hipSuccess) e = set_attrs1<kF32>(lds);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    return e;
+}
+
+// ---- step enqueue ---------------------------------------------------------------------------------
+
 hipError_t enqueue_step(const StepArgs& s, const ModelPtrs& m, const BeginList* lists, int n_lists,
-                        const int32_t* d_tok_in, int n_items, bool need_logits,
+                        const int32_t* d_tok_in, int n_items, bool need_logits, int nload,
                         int32_t* d_tok_out, hipStream_t st) {
+    Launch lc;
+    lc.ident = d_tok_in != nullptr;
+    lc.nload = nload;
     hipError_t e = hipSuccess;
     for (int i = 0; i < n_lists && e == hipSuccess; i++) {
-        hipLaunchKernelGGL(k_begin, dim3(lists[i].n), dim3(kBlock), 0, st, s, lists[i], d_tok_in);
+        hipLaunchKernelGGL(k_begin, dim3(lists[i].n), dim3(256), 0, st, s, lists[i], d_tok_in);
         e = hipGetLastError();
     }
     for (int l = 0; l < s.L && e == hipSuccess; l++) {
         const LayerW& w = m.layers[l];
-        e = gemv(0, s.d, s, w, l, n_items, st);
+        e = gemv(G_QKV, s, w, l, n_items, st, lc);
         if (e != hipSuccess) break;
-        hipLaunchKernelGGL(k_attn, dim3(s.n_chunks, s.Hkv, n_items), dim3(kBlock), attn_lds_bytes(),
-                           st, s, l);
-        hipLaunchKernelGGL(k_attn_combine, dim3(s.H, n_items), dim3(64), 0, st, s);
-        e = hipGetLastError();
-        if (e == hipSuccess) e = gemv(1, s.H * s.D, s, w, l, n_items, st);
-        if (e == hipSuccess) e = gemv(2, s.d, s, w, l, n_items, st);
-        if (e == hipSuccess) e = gemv(3, s.F, s, w, l, n_items, st);
+        if (nload > 0) {
+            e = gemv(G_WO_SHORT, s, w, l, n_items, st, lc);
+        } else {
+            hipLaunchKernelGGL(k_attn, dim3(s.n_chunks, s.Hkv, n_items), dim3(256), attn_lds(), st, s, l);
+            hipLaunchKernelGGL(k_attn_combine, dim3(s.H, n_items), dim3(64), 0, st, s);
+            e = hipGetLastError();
+            if (e == hipSuccess) e = gemv(G_WO_LONG, s, w, l, n_items, st, lc);
+        }
+        if (e == hipSuccess) e = gemv(G_W13, s, w, l, n_items, st, lc);
+        if (e == hipSuccess) e = gemv(G_W2, s, w, l, n_items, st, lc);
     }
-    if (e == hipSuccess && need_logits) e = gemv(4, s.d, s, LayerW{}, 0, n_items, st, m.out_norm, m.wcls);
+    if (e == hipSuccess && need_logits) e = gemv(G_LOGITS, s, LayerW{}, 0, n_items, st, lc, m.out_norm, m.wcls);
     if (e == hipSuccess) {
-        hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, st, s, n_items, d_tok_out,
+        hipLaunchKernelGGL(k_finalize, dim3(n_items), dim3(256), 0, st, s, logits_blocks(s), d_tok_out,
                            need_logits ? 1 : 0);
         e = hipGetLastError();
     }
     return e;
 }
 
-hipError_t enqueue_kernel(int which, int layer, const StepArgs& s, const ModelPtrs& m, int n_items,
+hipError_t enqueue_kernel(int which, int layer, const StepArgs& s, const ModelPtrs& m, int n_items, int nload,
                           hipStream_t st) {
-    if (which == 0) return gemv(0, s.d, s, m.layers[layer], layer, n_items, st);
-    if (which == 1) {
-        hipLaunchKernelGGL(k_attn, dim3(s.n_chunks, s.Hkv, n_items), dim3(kBlock), attn_lds_bytes(), st, s,
-                           layer);
-        return hipGetLastError();
+    const LayerW& w = m.layers[layer];
+    Launch lc;
+    lc.ident = 1;
+    lc.nload = nload;
+    switch (which) {
+        case K_QKV: return gemv(G_QKV, s, w, layer, n_items, st, lc);
+        case K_ATTN:
+            if (nload > 0) return hipErrorInvalidValue;
+            hipLaunchKernelGGL(k_attn, dim3(s.n_chunks, s.Hkv, n_items), dim3(256), attn_lds(), st, s, layer);
+            return hipGetLastError();
+        case K_COMBINE:
+            if (nload > 0) return hipErrorInvalidValue;
+            hipLaunchKernelGGL(k_attn_combine, dim3(s.H, n_items), dim3(64), 0, st, s);
+            return hipGetLastError();
+        case K_WO: return gemv(nload > 0 ? G_WO_SHORT : G_WO_LONG, s, w, layer, n_items, st, lc);
+        case K_W13: return gemv(G_W13, s, w, layer, n_items, st, lc);
+        case K_W2: return gemv(G_W2, s, w, layer, n_items, st, lc);
+        default: return gemv(G_LOGITS, s, LayerW{}, 0, n_items, st, lc, m.out_norm, m.wcls);
     }
-    if (which == 2) {
-        hipLaunchKernelGGL(k_attn_combine, dim3(s.H, n_items), dim3(64), 0, st, s);
-        return hipGetLastError();
-    }
-    if (which == 3) return gemv(1, s.H * s.D, s, m.layers[layer], layer, n_items, st);
-    if (which == 4) return gemv(2, s.d, s, m.layers[layer], layer, n_items, st);
-    if (which == 5) return gemv(3, s.F, s, m.layers[layer], layer, n_items, st);
-    return gemv(4, s.d, s, LayerW{}, 0, n_items, st, m.out_norm, m.wcls);
 }
 
-hipError_t enqueue_set_lengths(int32_t* d_lengths, const int32_t* h_vals, int first, int n,
-                               hipStream_t st) {
+hipError_t enqueue_set_lengths(int32_t* d_lengths, const int32_t* h_vals, int first, int n, hipStream_t st) {
     hipError_t e = hipSuccess;
     for (int o = 0; o < n && e == hipSuccess; o += kSetChunk) {
         SetList l;
@@ -615,8 +956,8 @@ hipError_t enqueue_set_lengths(int32_t* d_lengths, const int32_t* h_vals, int fi
 
 hipError_t enqueue_fill(int32_t* p, int n, int32_t v, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0,
-                       st, p, n, v);
+    const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+    hipLaunchKernelGGL(k_fill_i32, dim3(blocks), dim3(256), 0, st, p, n, v);
     return hipGetLastError();
 }
 
