@@ -269,20 +269,31 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     ds::StepArgs probe{};
     probe.d = c->dim;
     probe.H = c->n_heads;
+    probe.Hkv = c->n_kv_heads;
     probe.D = c->head_dim;
     probe.F = c->hidden_dim;
+    probe.wdt = c->weight_dtype;
     const int need_lds = static_cast<int>(ds::max_lds_bytes(probe));
-    static int attr_lds = 64 * 1024;
-    if (need_lds > attr_lds) {
+    const int need_mm = ds::mm_supported(probe) ? static_cast<int>(ds::mm_max_lds(probe)) : 0;
+    static int attr_lds = 64 * 1024, attr_mm = 64 * 1024;
+    if (need_lds > attr_lds || need_mm > attr_mm) {
         int dev = 0, optin = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev);
         if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-        if (need_lds > optin - 1024)
-            return fail(DS_ERR_UNSUPPORTED, "kernels need %d bytes of LDS, the device allows %d", need_lds, optin);
-        e = ds::set_kernel_attributes(need_lds);
-        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-        attr_lds = need_lds;
+        if (std::max(need_lds, need_mm) > optin - 4096)
+            return fail(DS_ERR_UNSUPPORTED, "kernels need %d bytes of LDS, the device allows %d",
+                        std::max(need_lds, need_mm), optin);
+        if (need_lds > attr_lds) {
+            e = ds::set_kernel_attributes(need_lds);
+            if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+            attr_lds = need_lds;
+        }
+        if (need_mm > attr_mm) {
+            e = ds::mm_set_attributes(need_mm);
+            if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+            attr_mm = need_mm;
+        }
     }
 
     // RoPE table: pair i of position p turns by p * theta^(-2i/D) ("GOTOken",
@@ -333,6 +344,9 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     s.T = T;
     s.n_chunks = (T + ds::kChunk - 1) / ds::kChunk;
     s.short_n = ds::short_positions(s);
+    s.mm_ok = ds::mm_supported(s) ? 1 : 0;
+    const char* mmenv = std::getenv("DS_MFMA");  // "0" keeps the VALU projections for every batch size
+    if (mmenv && std::strcmp(mmenv, "0") == 0) s.mm_ok = 0;
     const char* sa = std::getenv("DS_SHORT_ATTN");  // "0" turns the fused short-context path off
     if (sa && std::strcmp(sa, "0") == 0) s.short_n = 0;
     s.eps = c->norm_eps;
@@ -548,7 +562,8 @@ ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t lay
     if (reps < 1) return fail(DS_ERR_INVALID_ARG, "reps must be positive");
     hipStream_t st = static_cast<hipStream_t>(stream);
     for (int r = 0; r < reps; r++) {
-        if (kv->last_nload > 0 && (which == ds::K_ATTN || which == ds::K_COMBINE))
+        if (kv->last_nload > 0 && !(kv->s.mm_ok && kv->B >= ds::kMmMin) &&
+            (which == ds::K_ATTN || which == ds::K_COMBINE))
             return fail(DS_ERR_STATE, "kernel %d is not part of a short-context step", which);
         hipError_t e = ds::enqueue_kernel(which, layer, kv->s, model->ptrs, kv->B, kv->last_nload, st);
         if (e != hipSuccess) return hip_fail(e, "bench kernel");

@@ -17,6 +17,8 @@ constexpr int kMaxD = 256;       // head_dim limit of the attention kernels
 constexpr int kMaxItems = 64;    // items per k_begin launch
 constexpr int kSetChunk = 128;   // lengths per k_set_lengths launch
 constexpr int kMaxArgmaxBlocks = 16384;  // vocabulary blocks per item (argmax partials)
+constexpr int kMmItems = 64;     // items per MFMA launch
+constexpr int kMmMin = 16;       // steps with at least this many items use the MFMA projections
 
 // Per-layer weight pointers (device), into the caller's arena.
 struct LayerW {
@@ -43,6 +45,7 @@ struct StepArgs {
     int d, L, H, Hkv, D, F, V, wdt;
     int B, T, n_chunks;
     int short_n;         // contexts up to this many positions take the fused short path (0: never)
+    int mm_ok;           // shapes allow the MFMA projections
     float eps;
     const void* emb;
     float* cache;        // (L, 2, B, Hkv, T, D)
@@ -110,6 +113,13 @@ hipError_t enqueue_set_lengths(int32_t* d_lengths, const int32_t* h_vals, int fi
                                hipStream_t st);
 hipError_t enqueue_fill(int32_t* p, int n, int32_t v, hipStream_t st);
 size_t max_lds_bytes(const StepArgs& s);
+// MFMA projections (mfma.hip): which = 0 qkv, 1 wo, 2 w13, 3 w2, 4 logits.
+bool mm_supported(const StepArgs& s);
+int mm_logits_blocks(const StepArgs& s);
+size_t mm_max_lds(const StepArgs& s);
+hipError_t mm_set_attributes(int lds);
+hipError_t mm_gemv(int which, const StepArgs& s, const LayerW& w, int layer, int n_items, int ident,
+                   const float* out_norm, const void* wcls, hipStream_t st);
 // Longest context (a power of two <= min(kShort, T)) whose short-path staging fits in
 // 64 KiB of LDS; 0 if head_dim/4 is not a power of two.
 int short_positions(const StepArgs& s);

@@ -31,6 +31,7 @@
 #include <algorithm>
 
 #include "kernels.h"
+#include "device.h"
 
 namespace ds {
 
@@ -144,18 +145,6 @@ struct RowStream {
 
 // ---- block helpers -------------------------------------------------------------------
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
 template <int WAVES>
 __device__ __forceinline__ float block_sum(float v, float* red) {
     v = wave_sum(v);
@@ -254,15 +243,6 @@ struct VecStage {
         __syncthreads();
     }
 };
-
-__device__ __forceinline__ size_t cache_row(const StepArgs& s, int layer, int kv, int slot, int g, int t) {
-    size_t i = static_cast<size_t>(layer);
-    i = i * 2 + kv;
-    i = i * s.B + slot;
-    i = i * s.Hkv + g;
-    i = i * s.T + t;
-    return i * s.D;
-}
 
 // ---- k_begin: embedding gather -------------------------------------------------------
 // x[item] = widen(token_emb[tok]); records the slot, position and flag of the
@@ -548,6 +528,124 @@ __global__ __launch_bounds__(256) void k_attn(StepArgs s, int layer) {
     }
 }
 
+// Register-resident variant for head_dim D (a power of two, 16..256): every
+// K and V load of the block's chunk is issued up front (one memory round
+// trip), scores and the softmax stay in registers, and the row groups are
+// combined with xor shuffles inside a wave and one LDS exchange across the
+// four waves.  Thread (row group rg, slice e4) holds rows rg + NRG*i of the
+// chunk, columns 4*e4 .. 4*e4+3.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_d(StepArgs s, int layer) {
+    constexpr int LPR = D / 4;             // lanes per row
+    constexpr int NRG = 256 / LPR;         // row groups in the block
+    constexpr int RPT = (kChunk + NRG - 1) / NRG;  // rows per thread
+    constexpr int GPW = 64 / LPR;          // row groups per wave
+    __shared__ float wred[4][kMaxRep][2];
+    __shared__ float ored[4][kMaxRep][D];
+    const int chunk = blockIdx.x, g = blockIdx.y, item = blockIdx.z;
+    const int pos = s.pos[item], slot = s.slot[item];
+    const int n = pos + 1;
+    const int t0 = chunk * kChunk;
+    if (t0 >= n) return;
+    const int nt = min(kChunk, n - t0);
+    const int rep = s.H / s.Hkv;
+    const int e4 = threadIdx.x % LPR, rg = threadIdx.x / LPR;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const float* K = s.cache + cache_row(s, layer, 0, slot, g, t0) + e4 * 4;
+    const float* V = s.cache + cache_row(s, layer, 1, slot, g, t0) + e4 * 4;
+    float4 kr[RPT], vr[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; i++) {
+        const int t = min(rg + i * NRG, nt - 1);
+        kr[i] = *reinterpret_cast<const float4*>(K + static_cast<size_t>(t) * D);
+        vr[i] = *reinterpret_cast<const float4*>(V + static_cast<size_t>(t) * D);
+    }
+    const float* q = s.q + static_cast<size_t>(item) * s.H * D + static_cast<size_t>(g) * rep * D + e4 * 4;
+    float4 qr[kMaxRep];
+#pragma unroll
+    for (int j = 0; j < kMaxRep; j++)
+        qr[j] = *reinterpret_cast<const float4*>(q + static_cast<size_t>(min(j, rep - 1)) * D);
+    const float scale = 1.0f / sqrtf(static_cast<float>(D));
+    float sc[kMaxRep][RPT];
+#pragma unroll
+    for (int j = 0; j < kMaxRep; j++) {
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            float d = kr[i].x * qr[j].x;
+            d = fmaf(kr[i].y, qr[j].y, d);
+            d = fmaf(kr[i].z, qr[j].z, d);
+            d = fmaf(kr[i].w, qr[j].w, d);
+#pragma unroll
+            for (int o = LPR / 2; o > 0; o >>= 1) d += __shfl_xor(d, o);
+            sc[j][i] = rg + i * NRG < nt ? d * scale : -INFINITY;
+        }
+    }
+    // chunk max and exp-sum per head: thread rows -> wave (xor over row groups) -> block
+    float m[kMaxRep], l[kMaxRep];
+#pragma unroll
+    for (int j = 0; j < kMaxRep; j++) {
+        float mm = sc[j][0];
+#pragma unroll
+        for (int i = 1; i < RPT; i++) mm = fmaxf(mm, sc[j][i]);
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
+        m[j] = mm;
+    }
+    if (lane == 0)
+        for (int j = 0; j < kMaxRep; j++) wred[wave][j][0] = m[j];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMaxRep; j++) m[j] = fmaxf(fmaxf(wred[0][j][0], wred[1][j][0]), fmaxf(wred[2][j][0], wred[3][j][0]));
+    float acc[kMaxRep][4];
+#pragma unroll
+    for (int j = 0; j < kMaxRep; j++) {
+        float ll = 0.f;
+        acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const float p = __expf(sc[j][i] - m[j]);  // exp(-inf) = 0 for masked rows
+            ll += p;
+            acc[j][0] = fmaf(p, vr[i].x, acc[j][0]);
+            acc[j][1] = fmaf(p, vr[i].y, acc[j][1]);
+            acc[j][2] = fmaf(p, vr[i].z, acc[j][2]);
+            acc[j][3] = fmaf(p, vr[i].w, acc[j][3]);
+        }
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) {
+            ll += __shfl_xor(ll, o);
+            acc[j][0] += __shfl_xor(acc[j][0], o);
+            acc[j][1] += __shfl_xor(acc[j][1], o);
+            acc[j][2] += __shfl_xor(acc[j][2], o);
+            acc[j][3] += __shfl_xor(acc[j][3], o);
+        }
+        l[j] = ll;
+    }
+    __syncthreads();  // wred reads above are done before it is reused
+    if (lane < LPR) {
+        for (int j = 0; j < rep; j++) {
+            *reinterpret_cast<float4*>(&ored[wave][j][e4 * 4]) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+            if (lane == 0) wred[wave][j][1] = l[j];
+        }
+    }
+    __syncthreads();
+    const int S = s.n_chunks;
+    for (int idx = threadIdx.x; idx < rep * D; idx += 256) {
+        const int j = idx / D, e = idx % D;
+        const float v = ored[0][j][e] + ored[1][j][e] + ored[2][j][e] + ored[3][j][e];
+        const size_t pidx = (static_cast<size_t>(item) * s.H + g * rep + j) * S + chunk;
+        s.part_o[pidx * D + e] = v;
+        if (e == 0) {
+            s.part_ml[pidx * 2 + 0] = m[j];
+            s.part_ml[pidx * 2 + 1] = wred[0][j][1] + wred[1][j][1] + wred[2][j][1] + wred[3][j][1];
+        }
+    }
+    (void)GPW;
+}
+
+static bool attn_d_supported(int D) { return D == 16 || D == 32 || D == 64 || D == 128 || D == 256; }
+
+static hipError_t launch_attn(const StepArgs& s, int layer, int n_items, hipStream_t st);
+
 // Merge the chunk partials of one (item, head): M = max m_s,
 // o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
 __global__ __launch_bounds__(64) void k_attn_combine(StepArgs s) {
@@ -650,26 +748,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_w2(StepArgs s, LayerW w) {
 }
 
 // ---- k_logits: logits = Wcls rmsnorm(x) and per-block argmax ----------------------------------
-// Argmax key: the float's order-preserving 32-bit image in the high word and
-// (2^32 - 1 - index) in the low word, so the largest key is the largest
-// logit and, among equal logits, the lowest index ("Inside nanochat Part 4",
-// section "Sampling Strategy": greedy decoding is argmax), whatever order
-// the blocks run in.  Every block writes its own key; k_finalize reduces.
-__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
-    uint32_t u = __float_as_uint(v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return (static_cast<unsigned long long>(u) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - idx);
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const unsigned long long other = __shfl_xor(k, o);
-        k = other > k ? other : k;
-    }
-    return k;
-}
-
 template <int WDT, int G, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_logits(StepArgs s, const float* __restrict__ out_norm,
                                                        const void* __restrict__ wcls) {
@@ -883,12 +961,28 @@ hipError_t set_kernel_attributes(int lds) {
 
 // ---- step enqueue ---------------------------------------------------------------------------------
 
+static hipError_t launch_attn(const StepArgs& s, int layer, int n_items, hipStream_t st) {
+    const dim3 grid(s.n_chunks, s.Hkv, n_items);
+    switch (s.D) {
+        case 16: hipLaunchKernelGGL(k_attn_d<16>, grid, dim3(256), 0, st, s, layer); break;
+        case 32: hipLaunchKernelGGL(k_attn_d<32>, grid, dim3(256), 0, st, s, layer); break;
+        case 64: hipLaunchKernelGGL(k_attn_d<64>, grid, dim3(256), 0, st, s, layer); break;
+        case 128: hipLaunchKernelGGL(k_attn_d<128>, grid, dim3(256), 0, st, s, layer); break;
+        case 256: hipLaunchKernelGGL(k_attn_d<256>, grid, dim3(256), 0, st, s, layer); break;
+        default: hipLaunchKernelGGL(k_attn, grid, dim3(256), attn_lds(), st, s, layer); break;
+    }
+    return hipGetLastError();
+}
+
+static bool use_mm(const StepArgs& s, int n_items) { return s.mm_ok && n_items >= kMmMin; }
+
 hipError_t enqueue_step(const StepArgs& s, const ModelPtrs& m, const BeginList* lists, int n_lists,
                         const int32_t* d_tok_in, int n_items, bool need_logits, int nload,
                         int32_t* d_tok_out, hipStream_t st) {
     Launch lc;
     lc.ident = d_tok_in != nullptr;
-    lc.nload = nload;
+    const bool mm = use_mm(s, n_items);
+    lc.nload = mm ? 0 : nload;  // the MFMA path always takes the split-K attention
     hipError_t e = hipSuccess;
     for (int i = 0; i < n_lists && e == hipSuccess; i++) {
         hipLaunchKernelGGL(k_begin, dim3(lists[i].n), dim3(256), 0, st, s, lists[i], d_tok_in);
@@ -896,23 +990,28 @@ hipError_t enqueue_step(const StepArgs& s, const ModelPtrs& m, const BeginList* 
     }
     for (int l = 0; l < s.L && e == hipSuccess; l++) {
         const LayerW& w = m.layers[l];
-        e = gemv(G_QKV, s, w, l, n_items, st, lc);
+        e = mm ? mm_gemv(0, s, w, l, n_items, lc.ident, nullptr, nullptr, st) : gemv(G_QKV, s, w, l, n_items, st, lc);
         if (e != hipSuccess) break;
-        if (nload > 0) {
+        if (lc.nload > 0) {
             e = gemv(G_WO_SHORT, s, w, l, n_items, st, lc);
         } else {
-            hipLaunchKernelGGL(k_attn, dim3(s.n_chunks, s.Hkv, n_items), dim3(256), attn_lds(), st, s, l);
+            e = launch_attn(s, l, n_items, st);
             hipLaunchKernelGGL(k_attn_combine, dim3(s.H, n_items), dim3(64), 0, st, s);
-            e = hipGetLastError();
-            if (e == hipSuccess) e = gemv(G_WO_LONG, s, w, l, n_items, st, lc);
+            if (e == hipSuccess) e = hipGetLastError();
+            if (e == hipSuccess)
+                e = mm ? mm_gemv(1, s, w, l, n_items, lc.ident, nullptr, nullptr, st) : gemv(G_WO_LONG, s, w, l, n_items, st, lc);
         }
-        if (e == hipSuccess) e = gemv(G_W13, s, w, l, n_items, st, lc);
-        if (e == hipSuccess) e = gemv(G_W2, s, w, l, n_items, st, lc);
+        if (e == hipSuccess)
+            e = mm ? mm_gemv(2, s, w, l, n_items, lc.ident, nullptr, nullptr, st) : gemv(G_W13, s, w, l, n_items, st, lc);
+        if (e == hipSuccess)
+            e = mm ? mm_gemv(3, s, w, l, n_items, lc.ident, nullptr, nullptr, st) : gemv(G_W2, s, w, l, n_items, st, lc);
     }
-    if (e == hipSuccess && need_logits) e = gemv(G_LOGITS, s, LayerW{}, 0, n_items, st, lc, m.out_norm, m.wcls);
+    if (e == hipSuccess && need_logits)
+        e = mm ? mm_gemv(4, s, LayerW{}, 0, n_items, lc.ident, m.out_norm, m.wcls, st)
+               : gemv(G_LOGITS, s, LayerW{}, 0, n_items, st, lc, m.out_norm, m.wcls);
     if (e == hipSuccess) {
-        hipLaunchKernelGGL(k_finalize, dim3(n_items), dim3(256), 0, st, s, logits_blocks(s), d_tok_out,
-                           need_logits ? 1 : 0);
+        hipLaunchKernelGGL(k_finalize, dim3(n_items), dim3(256), 0, st, s, mm ? mm_logits_blocks(s) : logits_blocks(s),
+                           d_tok_out, need_logits ? 1 : 0);
         e = hipGetLastError();
     }
     return e;
@@ -921,23 +1020,27 @@ hipError_t enqueue_step(const StepArgs& s, const ModelPtrs& m, const BeginList* 
 hipError_t enqueue_kernel(int which, int layer, const StepArgs& s, const ModelPtrs& m, int n_items, int nload,
                           hipStream_t st) {
     const LayerW& w = m.layers[layer];
+    const bool mm = use_mm(s, n_items);
     Launch lc;
     lc.ident = 1;
-    lc.nload = nload;
+    lc.nload = mm ? 0 : nload;
     switch (which) {
-        case K_QKV: return gemv(G_QKV, s, w, layer, n_items, st, lc);
+        case K_QKV: return mm ? mm_gemv(0, s, w, layer, n_items, 1, nullptr, nullptr, st) : gemv(G_QKV, s, w, layer, n_items, st, lc);
         case K_ATTN:
-            if (nload > 0) return hipErrorInvalidValue;
-            hipLaunchKernelGGL(k_attn, dim3(s.n_chunks, s.Hkv, n_items), dim3(256), attn_lds(), st, s, layer);
-            return hipGetLastError();
+            if (lc.nload > 0) return hipErrorInvalidValue;
+            return launch_attn(s, layer, n_items, st);
         case K_COMBINE:
-            if (nload > 0) return hipErrorInvalidValue;
+            if (lc.nload > 0) return hipErrorInvalidValue;
             hipLaunchKernelGGL(k_attn_combine, dim3(s.H, n_items), dim3(64), 0, st, s);
             return hipGetLastError();
-        case K_WO: return gemv(nload > 0 ? G_WO_SHORT : G_WO_LONG, s, w, layer, n_items, st, lc);
-        case K_W13: return gemv(G_W13, s, w, layer, n_items, st, lc);
-        case K_W2: return gemv(G_W2, s, w, layer, n_items, st, lc);
-        default: return gemv(G_LOGITS, s, LayerW{}, 0, n_items, st, lc, m.out_norm, m.wcls);
+        case K_WO:
+            if (mm) return mm_gemv(1, s, w, layer, n_items, 1, nullptr, nullptr, st);
+            return gemv(lc.nload > 0 ? G_WO_SHORT : G_WO_LONG, s, w, layer, n_items, st, lc);
+        case K_W13: return mm ? mm_gemv(2, s, w, layer, n_items, 1, nullptr, nullptr, st) : gemv(G_W13, s, w, layer, n_items, st, lc);
+        case K_W2: return mm ? mm_gemv(3, s, w, layer, n_items, 1, nullptr, nullptr, st) : gemv(G_W2, s, w, layer, n_items, st, lc);
+        default:
+            return mm ? mm_gemv(4, s, LayerW{}, 0, n_items, 1, m.out_norm, m.wcls, st)
+                      : gemv(G_LOGITS, s, LayerW{}, 0, n_items, st, lc, m.out_norm, m.wcls);
     }
 }
 

@@ -1,0 +1,386 @@
+// mfma.hip -- batched decode projections on the gfx950 matrix cores.
+//
+// With many sequences per step the projections become Y[m][n] = sum_k
+// W[n][k] X[m][k] with M = batch items (up to 64 per launch), N = weight rows
+// and K = input width.  The weights are exactly bf16, so they feed the bf16
+// MFMA unchanged.  The fp32 activations are split into two bf16 terms,
+// x = hi + lo + r with |r| <= 2^-18 |x| (hi = bf16(x), lo = bf16(x - hi),
+// both rounded to nearest even), and every k-step runs two MFMAs with fp32
+// accumulation, keeping the products within fp32-level accuracy of the
+// plain matvec ("GOTOken: An Inference Engine in QBasic", section "About one
+// token per second": every projection is one row-major matvec).
+//
+// Wave tile: 16 weight rows x 16*NG items, v_mfma_f32_16x16x32_bf16 with
+//   A (16 x 32): lane l holds W[row l%16][k0 + (l/16)*8 .. +8]  (one 16-byte load)
+//   B (32 x 16): lane l holds X[item l%16][k0 + (l/16)*8 .. +8] (one 16-byte LDS read)
+//   C (16 x 16): lane l holds rows (l/16)*4 + r, r < 4, of item l%16.
+// A block of 4 waves shares the activation tile staged in LDS (64 items x
+// 64 k as bf16 hi and lo).  RMSNorm is applied per item after the product:
+// W (g * x * r) = r * (W (g * x)), with r from the sum of squares gathered
+// while staging.  Epilogues match the VALU kernels: RoPE pairs sit in tile
+// rows i and i + 8 (lanes l and l ^ 32), residual adds, silu(a) * u, and the
+// per-block argmax keys of the vocabulary product.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "device.h"
+#include "kernels.h"
+
+namespace ds {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+
+enum MMKind { MM_QKV, MM_WO, MM_W13, MM_W2, MM_LOGITS };
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ f32x4 mfma(const uint4 a, const uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+}
+
+template <int KIND, int NG, int KT>
+__global__ __launch_bounds__(256) void k_mm(StepArgs s, LayerW w, int layer, int m0, int n_items, int ident,
+                                             const float* __restrict__ out_norm, const void* __restrict__ wcls) {
+    constexpr bool NORM = KIND == MM_QKV || KIND == MM_W13 || KIND == MM_LOGITS;
+    constexpr int LDK = KT + 8;       // LDS row stride in bf16 (16-byte multiple)
+    constexpr int KS = KT / 32;       // MFMA k-steps per tile
+    constexpr int SV = KT / 16;       // float4 staged per thread per tile (4 threads per item)
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    uint16_t* xh = reinterpret_cast<uint16_t*>(lds);
+    uint16_t* xl = xh + kMmItems * LDK;
+    float* gs = reinterpret_cast<float*>(xl + kMmItems * LDK);  // gains [K] (NORM kinds)
+    __shared__ float rn[kMmItems];
+    __shared__ unsigned long long kred[4][kMmItems];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tile = blockIdx.x * 4 + wave;
+    const int ti = lane & 15, kq = lane >> 4;
+
+    int K = s.d, N = 0;
+    const void* W = nullptr;
+    const void* W3 = nullptr;
+    const float* gain = nullptr;
+    const float* src = s.x;
+    if (KIND == MM_QKV) { N = (s.H + 2 * s.Hkv) * s.D; gain = w.attn_norm; }
+    if (KIND == MM_WO) { K = s.H * s.D; N = s.d; W = w.wo; src = s.o; }
+    if (KIND == MM_W13) { N = s.F; W = w.w1; W3 = w.w3; gain = w.ffn_norm; }
+    if (KIND == MM_W2) { K = s.F; N = s.d; W = w.w2; src = s.h; }
+    if (KIND == MM_LOGITS) { N = s.V; W = wcls; gain = out_norm; }
+
+    // the weight row this lane feeds to the A operand (tile row ti)
+    const int D = s.D, half_d = s.D / 2;
+    const int nq_t = s.H * D / 16, nk_t = s.Hkv * D / 16;
+    int row = 0;
+    bool roped = false, is_q = false, tile_ok = tile * 16 < N;
+    if (KIND == MM_QKV) {
+        roped = tile < nq_t + nk_t;
+        is_q = tile < nq_t;
+        if (roped) {
+            const int p = (is_q ? tile : tile - nq_t) * 8 + (ti & 7);
+            row = (p / half_d) * D + p % half_d + (ti >> 3) * half_d;
+            W = is_q ? w.wq : w.wk;
+        } else {
+            row = tile_ok ? (tile - nq_t - nk_t) * 16 + ti : 0;
+            W = w.wv;
+        }
+    } else {
+        row = min(tile * 16 + ti, N - 1);
+    }
+    const uint16_t* Wrow = static_cast<const uint16_t*>(W) + static_cast<size_t>(row) * K + kq * 8;
+    const uint16_t* W3row = KIND == MM_W13 ? static_cast<const uint16_t*>(W3) + static_cast<size_t>(row) * K + kq * 8
+                                           : Wrow;
+
+    // staging role of this thread: item sm, columns sk .. sk + KT/4 - 1 of each tile
+    const int sm = threadIdx.x >> 2, sk = (threadIdx.x & 3) * (KT / 4);
+    const bool s_ok = sm < n_items;
+    const float* srow = src + static_cast<size_t>(m0 + min(sm, n_items - 1)) * K + sk;
+
+    // issue the first tile's loads, then stage the gains while they fly
+    float4 xv[SV];
+    uint4 wa[KS], wb[KS];
+#pragma unroll
+    for (int q = 0; q < SV; q++) xv[q] = *reinterpret_cast<const float4*>(srow + q * 4);
+#pragma unroll
+    for (int k = 0; k < KS; k++) {
+        wa[k] = *reinterpret_cast<const uint4*>(Wrow + k * 32);
+        wb[k] = KIND == MM_W13 ? *reinterpret_cast<const uint4*>(W3row + k * 32) : wa[k];
+    }
+    if (NORM)
+        for (int j = threadIdx.x; j < (K >> 2); j += 256)
+            reinterpret_cast<float4*>(gs)[j] = reinterpret_cast<const float4*>(gain)[j];
+
+    f32x4 acc[NG], acc3[NG];
+#pragma unroll
+    for (int g = 0; g < NG; g++) {
+        acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc3[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float ss = 0.f;
+    for (int k0 = 0; k0 < K; k0 += KT) {
+        __syncthreads();  // the previous tile's LDS reads are done (and the gains are staged)
+        // fp32 -> bf16 hi + lo into LDS, gains applied
+#pragma unroll
+        for (int q = 0; q < SV; q += 2) {
+            uint32_t hi[4], lo[4];
+            const float xs[8] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w, xv[q + 1].x, xv[q + 1].y, xv[q + 1].z, xv[q + 1].w};
+#pragma unroll
+            for (int c = 0; c < 8; c++) {
+                const float x = s_ok ? xs[c] : 0.f;
+                ss = fmaf(x, x, ss);
+                const float val = NORM ? gs[k0 + sk + q * 4 + c] * x : x;
+                const uint32_t h = bf16_bits_rne(val);
+                const uint32_t l = bf16_bits_rne(val - __uint_as_float(h << 16));
+                if (c & 1) {
+                    hi[c >> 1] |= h << 16;
+                    lo[c >> 1] |= l << 16;
+                } else {
+                    hi[c >> 1] = h;
+                    lo[c >> 1] = l;
+                }
+            }
+            *reinterpret_cast<uint4*>(xh + sm * LDK + sk + q * 4) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4*>(xl + sm * LDK + sk + q * 4) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
+        __syncthreads();
+        // the next tile's loads fly while this tile's MFMAs run
+        uint4 na[KS], nb[KS];
+        const int k1 = k0 + KT < K ? k0 + KT : k0;
+#pragma unroll
+        for (int q = 0; q < SV; q++) xv[q] = *reinterpret_cast<const float4*>(srow + k1 + q * 4);
+#pragma unroll
+        for (int k = 0; k < KS; k++) {
+            na[k] = *reinterpret_cast<const uint4*>(Wrow + k1 + k * 32);
+            nb[k] = KIND == MM_W13 ? *reinterpret_cast<const uint4*>(W3row + k1 + k * 32) : na[k];
+        }
+#pragma unroll
+        for (int k = 0; k < KS; k++) {
+#pragma unroll
+            for (int g = 0; g < NG; g++) {
+                const int off = (g * 16 + ti) * LDK + k * 32 + kq * 8;
+                const uint4 bh = *reinterpret_cast<const uint4*>(xh + off);
+                const uint4 bl = *reinterpret_cast<const uint4*>(xl + off);
+                acc[g] = mfma(wa[k], bh, acc[g]);
+                acc[g] = mfma(wa[k], bl, acc[g]);
+                if (KIND == MM_W13) {
+                    acc3[g] = mfma(wb[k], bh, acc3[g]);
+                    acc3[g] = mfma(wb[k], bl, acc3[g]);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KS; k++) {
+            wa[k] = na[k];
+            wb[k] = nb[k];
+        }
+    }
+    if (NORM) {
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        if ((threadIdx.x & 3) == 0) rn[sm] = 1.0f / sqrtf(ss / static_cast<float>(K) + s.eps);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds rows kq*4 + r of items g*16 + ti -------------------------------
+    unsigned long long key[NG];
+#pragma unroll
+    for (int g = 0; g < NG; g++) {
+        const int m = g * 16 + ti;
+        const bool m_ok = m < n_items;
+        const int item = m0 + min(m, n_items - 1);
+        const float r_m = NORM ? rn[min(m, n_items - 1)] : 1.f;
+        key[g] = 0ull;
+        if (KIND == MM_QKV) {
+            const int pos = s.pos[item];
+            const int slot = ident ? item : s.slot[item];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int i = kq * 4 + r;
+                const float y = acc[g][r] * r_m;
+                const float partner = __shfl_xor(y, 32);
+                if (!tile_ok || !m_ok) continue;
+                if (roped) {
+                    const int p = (is_q ? tile : tile - nq_t) * 8 + (i & 7);
+                    const int ii = p % half_d, second = i >> 3;
+                    const int orow = (p / half_d) * D + ii + second * half_d;
+                    const float c = s.rope_cos[static_cast<size_t>(pos) * half_d + ii];
+                    const float sn = s.rope_sin[static_cast<size_t>(pos) * half_d + ii];
+                    const float out = second ? fmaf(partner, sn, y * c) : fmaf(-partner, sn, y * c);
+                    if (is_q)
+                        s.q[static_cast<size_t>(item) * s.H * D + orow] = out;
+                    else
+                        s.cache[cache_row(s, layer, 0, slot, orow / D, pos) + orow % D] = out;
+                } else {
+                    const int orow = (tile - nq_t - nk_t) * 16 + i;
+                    s.cache[cache_row(s, layer, 1, slot, orow / D, pos) + orow % D] = y;
+                }
+            }
+        } else if (KIND == MM_WO || KIND == MM_W2) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int orow = tile * 16 + kq * 4 + r;
+                if (m_ok && orow < N) s.x[static_cast<size_t>(item) * s.d + orow] += acc[g][r];
+            }
+        } else if (KIND == MM_W13) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int orow = tile * 16 + kq * 4 + r;
+                const float a = acc[g][r] * r_m, u = acc3[g][r] * r_m;
+                if (m_ok && orow < N) s.h[static_cast<size_t>(item) * s.F + orow] = (a / (1.0f + expf(-a))) * u;
+            }
+        } else {  // MM_LOGITS
+            const int slot = ident ? item : s.slot[item];
+            const bool want = m_ok && s.flag[item];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int orow = tile * 16 + kq * 4 + r;
+                const float y = acc[g][r] * r_m;
+                if (orow < N) {
+                    if (want) s.logits[static_cast<size_t>(slot) * s.V + orow] = y;
+                    const unsigned long long kk = argmax_key(y, orow);
+                    key[g] = kk > key[g] ? kk : key[g];
+                }
+            }
+        }
+    }
+    if (KIND == MM_LOGITS) {
+#pragma unroll
+        for (int g = 0; g < NG; g++) {
+            unsigned long long k = key[g];
+            unsigned long long o = __shfl_xor(k, 16);
+            k = o > k ? o : k;
+            o = __shfl_xor(k, 32);
+            k = o > k ? o : k;
+            if (kq == 0) kred[wave][g * 16 + ti] = k;
+        }
+        __syncthreads();
+        for (int m = threadIdx.x; m < n_items; m += 256) {
+            unsigned long long k = kred[0][m];
+            for (int v = 1; v < 4; v++) k = kred[v][m] > k ? kred[v][m] : k;
+            s.keys[static_cast<size_t>(m0 + m) * kMaxArgmaxBlocks + blockIdx.x] = k;
+        }
+    }
+}
+
+// ---- launch ----------------------------------------------------------------------------------
+
+bool mm_supported(const StepArgs& s) {
+    return s.wdt == kBF16 && s.d % 64 == 0 && (s.H * s.D) % 64 == 0 && s.F % 64 == 0 && s.D % 16 == 0 &&
+           ((s.H + 2 * s.Hkv) * s.D) % 16 == 0;
+}
+
+int mm_logits_blocks(const StepArgs& s) { return (s.V + 63) / 64; }
+
+static int pick_kt(int K) {
+    if (K % 256 == 0) return 256;
+    if (K % 192 == 0) return 192;
+    if (K % 128 == 0) return 128;
+    return 64;
+}
+
+static size_t mm_lds(int KT, bool norm, int K) {
+    return sizeof(uint16_t) * 2 * kMmItems * (KT + 8) + (norm ? sizeof(float) * K : 0);
+}
+
+template <int KIND, int NG, int KT>
+static void launch_one(dim3 grid, size_t lds, const StepArgs& s, const LayerW& w, int layer, int m0, int n, int ident,
+                       const float* out_norm, const void* wcls, hipStream_t st) {
+    hipLaunchKernelGGL((k_mm<KIND, NG, KT>), grid, dim3(256), lds, st, s, w, layer, m0, n, ident, out_norm, wcls);
+}
+
+template <int KIND, int KT>
+static void launch_ng(int ng, dim3 grid, size_t lds, const StepArgs& s, const LayerW& w, int layer, int m0, int n,
+                      int ident, const float* out_norm, const void* wcls, hipStream_t st) {
+    switch (ng) {
+        case 1: launch_one<KIND, 1, KT>(grid, lds, s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+        case 2: launch_one<KIND, 2, KT>(grid, lds, s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+        case 3: launch_one<KIND, 3, KT>(grid, lds, s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+        default: launch_one<KIND, 4, KT>(grid, lds, s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+    }
+}
+
+template <int KIND>
+static hipError_t launch_kind(const StepArgs& s, const LayerW& w, int layer, int m0, int n, int ident,
+                              const float* out_norm, const void* wcls, hipStream_t st) {
+    int N = 0, K = s.d;
+    if (KIND == MM_QKV) N = (s.H + 2 * s.Hkv) * s.D;
+    if (KIND == MM_WO) { N = s.d; K = s.H * s.D; }
+    if (KIND == MM_W2) { N = s.d; K = s.F; }
+    if (KIND == MM_W13) N = s.F;
+    if (KIND == MM_LOGITS) N = s.V;
+    constexpr bool norm = KIND == MM_QKV || KIND == MM_W13 || KIND == MM_LOGITS;
+    const dim3 grid((N + 63) / 64);
+    const int ng = (n + 15) / 16;
+    const int kt = pick_kt(K);
+    const size_t lds = mm_lds(kt, norm, K);
+    switch (kt) {
+        case 256: launch_ng<KIND, 256>(ng, grid, lds, s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+        case 192: launch_ng<KIND, 192>(ng, grid, lds, s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+        case 128: launch_ng<KIND, 128>(ng, grid, lds, s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+        default: launch_ng<KIND, 64>(ng, grid, lds, s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+    }
+    return hipGetLastError();
+}
+
+template <int KIND, int KT>
+static hipError_t attrs_ng(int lds) {
+    hipError_t e = hipSuccess;
+    auto one = [&](const void* fn) {
+        if (e == hipSuccess) e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    };
+    one(reinterpret_cast<const void*>(k_mm<KIND, 1, KT>));
+    one(reinterpret_cast<const void*>(k_mm<KIND, 2, KT>));
+    one(reinterpret_cast<const void*>(k_mm<KIND, 3, KT>));
+    one(reinterpret_cast<const void*>(k_mm<KIND, 4, KT>));
+    return e;
+}
+
+template <int KIND>
+static hipError_t attrs_kind(int lds) {
+    hipError_t e = attrs_ng<KIND, 256>(lds);
+    if (e == hipSuccess) e = attrs_ng<KIND, 192>(lds);
+    if (e == hipSuccess) e = attrs_ng<KIND, 128>(lds);
+    if (e == hipSuccess) e = attrs_ng<KIND, 64>(lds);
+    return e;
+}
+
+size_t mm_max_lds(const StepArgs& s) {
+    size_t m = 0;
+    const int Ks[3] = {s.d, s.H * s.D, s.F};
+    for (int K : Ks) m = std::max(m, mm_lds(pick_kt(K), K == s.d, K));
+    return m;
+}
+
+hipError_t mm_set_attributes(int lds) {
+    hipError_t e = attrs_kind<MM_QKV>(lds);
+    if (e == hipSuccess) e = attrs_kind<MM_WO>(lds);
+    if (e == hipSuccess) e = attrs_kind<MM_W13>(lds);
+    if (e == hipSuccess) e = attrs_kind<MM_W2>(lds);
+    if (e == hipSuccess) e = attrs_kind<MM_LOGITS>(lds);
+    return e;
+}
+
+// which: 0 qkv, 1 wo, 2 w13, 3 w2, 4 logits; items [0, n_items) in launches of kMmItems.
+hipError_t mm_gemv(int which, const StepArgs& s, const LayerW& w, int layer, int n_items, int ident,
+                   const float* out_norm, const void* wcls, hipStream_t st) {
+    hipError_t e = hipSuccess;
+    for (int m0 = 0; m0 < n_items && e == hipSuccess; m0 += kMmItems) {
+        const int n = n_items - m0 < kMmItems ? n_items - m0 : kMmItems;
+        switch (which) {
+            case 0: e = launch_kind<MM_QKV>(s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+            case 1: e = launch_kind<MM_WO>(s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+            case 2: e = launch_kind<MM_W13>(s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+            case 3: e = launch_kind<MM_W2>(s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+            default: e = launch_kind<MM_LOGITS>(s, w, layer, m0, n, ident, out_norm, wcls, st); break;
+        }
+    }
+    return e;
+}
+
+}  // namespace ds

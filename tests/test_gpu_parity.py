@@ -189,3 +189,20 @@ def test_errors_are_reported_without_enqueueing():
     assert e.value.status == -5
     kv.check()  # the flag was cleared
     assert kv.lengths.cpu().tolist() == [4, 1]
+
+
+MM_SHAPE = synth.small_shape(dim=128, n_heads=4, n_kv_heads=2, head_dim=32, hidden_dim=256, vocab_size=512,
+                             weight_dtype=synth.BF16)
+
+
+@pytest.mark.parametrize("B", [20, 70])
+def test_batched_mfma_projections_match_oracle(B):
+    """Batches of 16+ sequences take the MFMA projections (bf16 weights, fp32
+    activations split into two bf16 terms): 20 leaves part of a 16-item MFMA
+    column group empty, 70 needs two 64-item launches."""
+    shape = MM_SHAPE
+    arena = synth.make_arena(shape, 11, std=0.1, gain_sigma=0.1)
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, 40, size=B)
+    prompts = [synth.random_tokens(300 + b, int(n), shape.vocab_size) for b, n in enumerate(lens)]
+    compare(shape, arena, prompts, 3, 64, f"mfma B={B}")
