@@ -110,7 +110,8 @@ size_t layout(const ds_config* c, std::vector<size_t>* off) {
 
 // Workspace carve-up for a (B, T) cache.
 struct WsLayout {
-    size_t x, q, o, h, part_o, part_ml, logits, keys, slot, pos, flag, err, rope_cos, rope_sin, total;
+    size_t x, q, o, h, part_o, part_ml, logits, keys, slot, pos, flag, err, rope_cos, rope_sin;
+    size_t ll_x, ll_x2, ll_qkv, ll_part, ll_h, ll_keys, epoch, layers, ll_end, total;
 };
 
 WsLayout ws_layout(const ds_config* c, int B, int T) {
@@ -137,6 +138,17 @@ WsLayout ws_layout(const ds_config* c, int B, int T) {
     w.err = take(sizeof(int32_t));
     w.rope_cos = take(sizeof(float) * T * (c->head_dim / 2));
     w.rope_sin = take(sizeof(float) * T * (c->head_dim / 2));
+    // persistent batch-1 step: LL words (zeroed at creation), epoch, layer table
+    const size_t kvd = static_cast<size_t>(c->n_kv_heads) * c->head_dim;
+    w.ll_x = take(8 * static_cast<size_t>(c->dim));
+    w.ll_x2 = take(8 * static_cast<size_t>(c->dim));
+    w.ll_qkv = take(8 * (HD + 2 * kvd));
+    w.ll_part = take(8 * static_cast<size_t>(c->n_heads) * ds::kPMaxChunks * (c->head_dim + 2));
+    w.ll_h = take(8 * static_cast<size_t>(c->hidden_dim));
+    w.ll_keys = take(8 * static_cast<size_t>(ds::kPKeyWords));
+    w.epoch = take(sizeof(uint32_t));
+    w.ll_end = p;
+    w.layers = take(sizeof(ds::LayerW) * static_cast<size_t>(c->n_layers));
     w.total = p;
     return w;
 }
@@ -172,6 +184,8 @@ struct ds_kv {
     bool stepped = false;         // a decode step has filled the per-item state
     int last_nload = 0;           // short-path rows of the last decode step (0: split-K path)
     std::vector<GraphEntry> graphs;
+    ds::PersistArgs pa{};
+    int persist_ctx = 0;          // longest context of the persistent step (0: off)
 };
 
 extern "C" {
@@ -316,6 +330,12 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
         e = hipMemcpyAsync(ws + lay.rope_sin, sn.data(), sn.size() * sizeof(float), hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = ds::enqueue_fill(d_lengths, B, 0, st);
     if (e == hipSuccess) e = ds::enqueue_fill(reinterpret_cast<int32_t*>(ws + lay.err), 1, 0, st);
+    if (e == hipSuccess)
+        e = ds::enqueue_fill(reinterpret_cast<int32_t*>(ws + lay.ll_x), static_cast<int>((lay.ll_end - lay.ll_x) / 4), 0,
+                             st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(ws + lay.layers, model->ptrs.layers.data(), sizeof(ds::LayerW) * model->ptrs.layers.size(),
+                           hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e, "cache setup");
 
@@ -349,6 +369,27 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     if (mmenv && std::strcmp(mmenv, "0") == 0) s.mm_ok = 0;
     const char* sa = std::getenv("DS_SHORT_ATTN");  // "0" turns the fused short-context path off
     if (sa && std::strcmp(sa, "0") == 0) s.short_n = 0;
+    ds::PersistArgs& pa = kv->pa;
+    pa.layers = reinterpret_cast<const ds::LayerW*>(ws + lay.layers);
+    pa.out_norm = model->ptrs.out_norm;
+    pa.wcls = model->ptrs.wcls;
+    pa.ll_x = reinterpret_cast<uint64_t*>(ws + lay.ll_x);
+    pa.ll_x2 = reinterpret_cast<uint64_t*>(ws + lay.ll_x2);
+    pa.ll_qkv = reinterpret_cast<uint64_t*>(ws + lay.ll_qkv);
+    pa.ll_part = reinterpret_cast<uint64_t*>(ws + lay.ll_part);
+    pa.ll_h = reinterpret_cast<uint64_t*>(ws + lay.ll_h);
+    pa.ll_keys = reinterpret_cast<uint64_t*>(ws + lay.ll_keys);
+    pa.epoch = reinterpret_cast<uint32_t*>(ws + lay.epoch);
+    kv->persist_ctx = ds::persist_max_ctx(s);
+    const char* pe = std::getenv("DS_PERSIST");  // "0" keeps batch-1 steps on one launch per operation
+    if (pe && std::strcmp(pe, "0") == 0) kv->persist_ctx = 0;
+    if (kv->persist_ctx > 0) {
+        hipError_t ee = ds::persist_prepare(s);
+        if (ee != hipSuccess) {
+            delete kv;
+            return hip_fail(ee, "persistent step attributes");
+        }
+    }
     s.eps = c->norm_eps;
     s.emb = model->ptrs.emb;
     s.cache = d_cache;
@@ -443,8 +484,16 @@ ds_status ds_prefill(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_t
     for (int j = 0; j < n; j++) {
         list.tok[0] = h_tokens[j];
         list.last[0] = j == n - 1;
-        const int nload = ds::short_rows(kv->s, kv->mirror[seq] + j + 1);
-        hipError_t e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, nullptr, 1, j == n - 1, nload, d_tok_out, st);
+        const int ctx = kv->mirror[seq] + j + 1;
+        hipError_t e;
+        if (kv->B == 1 && ctx <= kv->persist_ctx) {
+            // the same kernel as a batch-1 decode step at this position, so a
+            // prompt re-fed through prefill reproduces decoded steps bit for bit
+            e = ds::enqueue_persist(kv->s, kv->pa, nullptr, h_tokens[j], j == n - 1 ? d_tok_out : nullptr, st);
+        } else {
+            const int nload = ds::short_rows(kv->s, ctx);
+            e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, nullptr, 1, j == n - 1, nload, d_tok_out, st);
+        }
         if (e != hipSuccess) return hip_fail(e, "prefill");
     }
     kv->mirror[seq] += n;
@@ -455,6 +504,7 @@ ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens, 
                            int32_t* d_tok_out, void* stream) {
     if (!model || !kv || kv->model != model) return fail(DS_ERR_INVALID_ARG, "model/kv mismatch");
     if (!h_counts) return fail(DS_ERR_INVALID_ARG, "h_counts is NULL");
+    if (kv->B == 1) return h_counts[0] > 0 ? ds_prefill(model, kv, 0, h_tokens, h_counts[0], d_tok_out, stream) : ok();
     const int B = kv->B;
     std::vector<int64_t> start(B + 1, 0);
     int max_n = 0;
@@ -518,7 +568,12 @@ ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, in
     list.by_value = 0;
     int max_ctx = 0;
     for (int b = 0; b < kv->B; b++) max_ctx = std::max(max_ctx, kv->mirror[b] + 1);
-    const int nload = ds::short_rows(kv->s, max_ctx);
+    const bool persist = kv->B == 1 && max_ctx <= kv->persist_ctx;
+    const int nload = persist ? -1 : ds::short_rows(kv->s, max_ctx);  // -1 marks the persistent step
+    auto enqueue = [&]() -> hipError_t {
+        if (persist) return ds::enqueue_persist(kv->s, kv->pa, d_tok_in, 0, d_tok_out, st);
+        return ds::enqueue_step(kv->s, model->ptrs, &list, 1, d_tok_in, kv->B, true, nload, d_tok_out, st);
+    };
     hipError_t e = hipSuccess;
     if (kv->dispatch == 1 && st != nullptr) {
         GraphEntry* ge = nullptr;
@@ -528,8 +583,7 @@ ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, in
             GraphEntry g{nload, st, d_tok_in, d_tok_out, nullptr, nullptr};
             e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
             if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
-            hipError_t ee = ds::enqueue_step(kv->s, model->ptrs, &list, 1, d_tok_in, kv->B, true, nload, d_tok_out,
-                                             st);
+            hipError_t ee = enqueue();
             e = hipStreamEndCapture(st, &g.graph);
             if (ee != hipSuccess) return hip_fail(ee, "capture decode step");
             if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
@@ -544,12 +598,12 @@ ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, in
         e = hipGraphLaunch(ge->exec, st);
         if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
     } else {
-        e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, d_tok_in, kv->B, true, nload, d_tok_out, st);
+        e = enqueue();
         if (e != hipSuccess) return hip_fail(e, "decode step");
     }
     for (int b = 0; b < kv->B; b++) kv->mirror[b] += 1;
     kv->stepped = true;
-    kv->last_nload = nload;
+    kv->last_nload = persist ? ds::short_rows(kv->s, max_ctx) : nload;
     return ok();
 }
 

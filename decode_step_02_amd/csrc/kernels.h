@@ -17,6 +17,8 @@ constexpr int kMaxD = 256;       // head_dim limit of the attention kernels
 constexpr int kMaxItems = 64;    // items per k_begin launch
 constexpr int kSetChunk = 128;   // lengths per k_set_lengths launch
 constexpr int kMaxArgmaxBlocks = 16384;  // vocabulary blocks per item (argmax partials)
+constexpr int kPMaxChunks = 16;  // attention chunks the persistent step can hold per head
+constexpr int kPKeyWords = 1024; // argmax words of the persistent step (one per wave)
 constexpr int kMmItems = 64;     // items per MFMA launch
 constexpr int kMmMin = 16;       // steps with at least this many items use the MFMA projections
 
@@ -67,6 +69,20 @@ struct StepArgs {
     const float* rope_sin;  // [T][D/2]
 };
 
+// Device buffers of the persistent batch-1 step (persist.hip).
+struct PersistArgs {
+    const LayerW* layers;   // device copy of the per-layer pointers [L]
+    const float* out_norm;
+    const void* wcls;
+    uint64_t* ll_x;         // [d]      residual after W2 (value, epoch words)
+    uint64_t* ll_x2;        // [d]      residual after Wo
+    uint64_t* ll_qkv;       // [Hkv][(rep + 2) * D] per group: rotated queries, new key, new value
+    uint64_t* ll_part;      // [kPMaxChunks][H][D+2] attention partials (m, l, o), chunk-major
+    uint64_t* ll_h;         // [F]      silu(a)*u
+    uint64_t* ll_keys;      // [kPKeyWords] argmax words
+    uint32_t* epoch;        // epoch base, advanced by every step
+};
+
 // Items of one k_begin launch; by_value = 0 takes tokens from d_tok_in with
 // item == slot (decode), 1 takes slots/tokens from the arrays (prefill).
 struct BeginList {
@@ -113,6 +129,14 @@ hipError_t enqueue_set_lengths(int32_t* d_lengths, const int32_t* h_vals, int fi
                                hipStream_t st);
 hipError_t enqueue_fill(int32_t* p, int n, int32_t v, hipStream_t st);
 size_t max_lds_bytes(const StepArgs& s);
+// Persistent batch-1 step (persist.hip): the longest context it takes (0: none).
+int persist_max_ctx(const StepArgs& s);
+size_t persist_lds();
+hipError_t persist_prepare(const StepArgs& s);
+// One step of sequence 0 (B == 1): the token comes from d_tok_in[0], or from
+// tok_value when d_tok_in is NULL; d_tok_out may be NULL.
+hipError_t enqueue_persist(const StepArgs& s, const PersistArgs& p, const int32_t* d_tok_in, int tok_value,
+                           int32_t* d_tok_out, hipStream_t st);
 // MFMA projections (mfma.hip): which = 0 qkv, 1 wo, 2 w13, 3 w2, 4 logits.
 bool mm_supported(const StepArgs& s);
 int mm_logits_blocks(const StepArgs& s);

@@ -1,0 +1,783 @@
+// persist.hip -- the whole batch-1 decode step as one persistent kernel.
+//
+// At batch 1 a decode step is a chain of dependent all-to-all phases per
+// layer (Q/K/V, attention, Wo, W1/W3, W2), each moving only a few MB of
+// weights, so a launch per phase is dominated by the launch and its cache
+// flush.  Here one launch of 256 resident blocks runs the whole step.
+//
+// Every block has one role for the whole step: Q/K/V rows (role 0),
+// attention partials (role 1, long contexts only), Wo (role 2), W1/W3
+// (role 3) or W2 (role 4), and loops over the layers in it.  As soon as a
+// block has published its outputs of layer l it issues the weight loads of
+// layer l+1, which then have three or four phases to land in registers.
+// Blocks without a role preload vocabulary rows.
+//
+// Outputs reach the next phase through "LL" words: a 32-bit value and the
+// 32-bit epoch of the phase that wrote it, stored together as one 8-byte
+// agent-scope atomic.  The four waves of a consumer block poll the words of
+// the vector they need (a quarter each) until every word carries the
+// expected epoch, then share it through LDS.  Before that they poll a
+// 64-word sample of the phase before, so that blocks whose turn is far off
+// do not hammer the lines being written.  No counter, fence or grid barrier
+// is needed.
+//
+// For contexts of up to 32 positions the Wo blocks recompute attention
+// themselves (one wave per key/value group, its cached rows preloaded in
+// registers): four handoffs per layer instead of five.
+//
+// Every wait is bounded: a wave that does not see its input in about a
+// second sets the error word and carries on, so the grid always drains
+// (ds_kv_cache_check then reports the failure).
+//
+// The arithmetic is that of the pre-norm Llama block ("simple-llm /
+// kasahare" PyPI README 0.4.0, section "Architecture") with the
+// (L, 2, B, Hkv, T, D) cache of "Inside nanochat Part 4: Understanding
+// Inference", section "Cache Architecture".  The new key/value row reaches
+// attention through LL words, because plain stores of the same launch are
+// not guaranteed to be visible to other workgroups.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.h"
+#include "kernels.h"
+
+namespace ds {
+
+constexpr int kPBlocks = 256;
+constexpr int kPThreads = 256;                // 4 waves
+constexpr int kPWaves = kPBlocks * kPThreads / 64;
+constexpr int kPLds = 12288;                  // floats of LDS per block
+constexpr int kPRed = kPLds - 16;             // block-reduction slots at the end of LDS
+constexpr int kPF = 12;                       // weight chunks per lane held in registers
+constexpr int kPNorm = 3;                     // normalised elements per thread (d <= 768)
+constexpr long kPSpin = 1 << 20;              // poll rounds before a wait gives up
+constexpr int kPhases = 5;                    // epochs per layer
+constexpr int kPChunk = 32;                   // positions per attention task
+
+static_assert(kPWaves == kPKeyWords, "one argmax word per wave");
+
+__device__ __forceinline__ void ll_put(uint64_t* p, float v, uint32_t ep) {
+    __hip_atomic_store(p, (static_cast<uint64_t>(ep) << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t ll_get(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool aborted(int32_t* err) {
+    return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+}
+
+__device__ __forceinline__ bool give_up(long& spins, int32_t* err) {
+    if ((++spins & 1023) == 0 && (spins > kPSpin || aborted(err))) {
+        if ((threadIdx.x & 63) == 0) atomicOr(err, 4);
+        return true;
+    }
+    return false;
+}
+
+// A run of LL words: n words from src that must carry epoch ep; values go to dst.
+struct Seg {
+    const uint64_t* src;
+    int n;
+    uint32_t ep;
+    float* dst;
+};
+
+// Wait (per wave) until 64 words spread over src[0..n) carry epoch ep.  Used
+// on the output of the phase before the producer, as a cheap throttle; SLEEP
+// spaces the rounds of waits that are expected to be long.
+template <int SLEEP>
+__device__ void wait_sample(const uint64_t* src, int n, uint32_t ep, int32_t* err) {
+    if (n <= 0) return;
+    const uint64_t* q = src + ((threadIdx.x & 63) * n) / 64;
+    long spins = 0;
+    while (!__all(static_cast<uint32_t>(ll_get(q) >> 32) == ep)) {
+        if (SLEEP > 0) __builtin_amdgcn_s_sleep(SLEEP);
+        if (give_up(spins, err)) break;
+    }
+}
+
+// Block-cooperative fetch of segment a followed by segment b: thread t polls
+// the words t, t + 256, ... of the concatenation, J per round, with
+// unconditional loads of clamped indices so that a round is one memory round
+// trip, and stores the values to LDS once its wave has seen the round
+// complete.  No barrier here.
+template <int J>
+__device__ void block_fetch(const Seg& a, const Seg& b, int32_t* err) {
+    const int tid = threadIdx.x;
+    const int total = a.n + b.n;
+    for (int base = 0; base < total; base += kPThreads * J) {
+        uint64_t w[J];
+        long spins = 0;
+        while (true) {
+#pragma unroll
+            for (int j = 0; j < J; j++) {
+                const int i = min(base + tid + kPThreads * j, total - 1);
+                w[j] = ll_get(i < a.n ? a.src + i : b.src + (i - a.n));
+            }
+            bool ok = true;
+#pragma unroll
+            for (int j = 0; j < J; j++) {
+                const int i = min(base + tid + kPThreads * j, total - 1);
+                ok &= static_cast<uint32_t>(w[j] >> 32) == (i < a.n ? a.ep : b.ep);
+            }
+            if (__all(ok)) break;
+            if (give_up(spins, err)) break;
+        }
+#pragma unroll
+        for (int j = 0; j < J; j++) {
+            const int i = base + tid + kPThreads * j;
+            if (i < total) {
+                float* dst = i < a.n ? a.dst + i : b.dst + (i - a.n);
+                *dst = __uint_as_float(static_cast<uint32_t>(w[j]));
+            }
+        }
+    }
+}
+
+template <int J>
+__device__ __forceinline__ void block_fetch(const Seg& a, int32_t* err) {
+    block_fetch<J>(a, Seg{a.src, 0, a.ep, a.dst}, err);  // an empty second segment (never null)
+}
+
+// RMSNorm of xs[0..n) (n <= 768) for the whole block.  Thread t owns the
+// elements t, t + 256, t + 512 (those block_fetch of a single segment gave
+// it) and multiplies them by their gains in place; the function returns
+// 1 / sqrt(mean(x^2) + eps), by which the caller scales its dot products.
+// Ends with a barrier, after which xs holds g * x.
+__device__ float block_norm(float* xs, int n, const float (&gr)[kPNorm], float eps, float* sm) {
+    const int tid = threadIdx.x;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPNorm; j++) {
+        const int i = tid + kPThreads * j;
+        if (i < n) {
+            const float v = xs[i];
+            ss = fmaf(v, v, ss);
+            xs[i] = gr[j] * v;
+        }
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) sm[kPRed + (tid >> 6)] = ss;
+    __syncthreads();
+    const float tot = (sm[kPRed] + sm[kPRed + 1]) + (sm[kPRed + 2] + sm[kPRed + 3]);
+    return 1.0f / sqrtf(tot / static_cast<float>(n) + eps);
+}
+
+__device__ __forceinline__ void load_gains(float (&gr)[kPNorm], const float* __restrict__ g, int n) {
+#pragma unroll
+    for (int j = 0; j < kPNorm; j++) gr[j] = g[min(static_cast<int>(threadIdx.x) + kPThreads * j, n - 1)];
+}
+
+// The wave's share of one weight row: G lanes per row, lane `sub` takes the
+// 16-byte chunks sub, sub + G, ...  start() loads the first kPF of them into
+// registers, so finish() touches no memory when the row has at most kPF * G
+// chunks (the host picks G so that it has).
+template <int WDT, int G>
+struct PStream {
+    static constexpr int EPC = WDT == kBF16 ? 8 : 4;
+    uint4 w[kPF];
+    const void* W;
+    size_t base;
+    int nch, sub;
+    __device__ __forceinline__ uint4 ld(size_t e) const {
+        return WDT == kBF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + e)
+                            : *reinterpret_cast<const uint4*>(static_cast<const float*>(W) + e);
+    }
+    __device__ __forceinline__ float dot(const uint4 u, const float* xs, float acc) const {
+        if (WDT == kBF16) {
+            const float4 a = *reinterpret_cast<const float4*>(xs);
+            const float4 b = *reinterpret_cast<const float4*>(xs + 4);
+            acc = fmaf(__uint_as_float(u.x << 16), a.x, acc);
+            acc = fmaf(__uint_as_float(u.x & 0xFFFF0000u), a.y, acc);
+            acc = fmaf(__uint_as_float(u.y << 16), a.z, acc);
+            acc = fmaf(__uint_as_float(u.y & 0xFFFF0000u), a.w, acc);
+            acc = fmaf(__uint_as_float(u.z << 16), b.x, acc);
+            acc = fmaf(__uint_as_float(u.z & 0xFFFF0000u), b.y, acc);
+            acc = fmaf(__uint_as_float(u.w << 16), b.z, acc);
+            acc = fmaf(__uint_as_float(u.w & 0xFFFF0000u), b.w, acc);
+        } else {
+            const float4 a = *reinterpret_cast<const float4*>(xs);
+            acc = fmaf(__uint_as_float(u.x), a.x, acc);
+            acc = fmaf(__uint_as_float(u.y), a.y, acc);
+            acc = fmaf(__uint_as_float(u.z), a.z, acc);
+            acc = fmaf(__uint_as_float(u.w), a.w, acc);
+        }
+        return acc;
+    }
+    __device__ __forceinline__ void start(const void* W_, int row, int K, int sub_, bool valid) {
+        W = W_;
+        base = static_cast<size_t>(row) * K;
+        sub = sub_;
+        nch = valid ? K / EPC : 0;
+        const int last = K / EPC - 1;
+#pragma unroll
+        for (int p = 0; p < kPF; p++) w[p] = ld(base + static_cast<size_t>(min(sub + p * G, last)) * EPC);
+    }
+    __device__ __forceinline__ float finish(const float* xs) const {
+        float a0 = 0.f, a1 = 0.f;
+        const int last = nch > 0 ? nch - 1 : 0;
+#pragma unroll
+        for (int p = 0; p < kPF; p += 2) {
+            const float d0 = dot(w[p], xs + min(sub + p * G, last) * EPC, 0.f);
+            const float d1 = dot(w[p + 1], xs + min(sub + (p + 1) * G, last) * EPC, 0.f);
+            a0 += sub + p * G < nch ? d0 : 0.f;
+            a1 += sub + (p + 1) * G < nch ? d1 : 0.f;
+        }
+        for (int c = sub + kPF * G; c < nch; c += G) a0 = dot(ld(base + static_cast<size_t>(c) * EPC), xs + c * EPC, a0);
+        float v = a0 + a1;
+#pragma unroll
+        for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+        return v;
+    }
+};
+
+// Argmax word: ordered float bits (32), (2^17 - 1 - index) (17), epoch (15):
+// the largest word is the largest logit, ties going to the lowest index.
+__device__ __forceinline__ uint64_t key_word(float v, int idx, uint32_t ep) {
+    uint32_t u = __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (static_cast<uint64_t>(u) << 32) | (static_cast<uint64_t>(0x1FFFFu - idx) << 15) | (ep & 0x7FFFu);
+}
+
+// What every role needs to know about the step.  Epochs per layer: 0 Q/K/V
+// words, 1 attention partials, 2 residual after Wo, 3 silu(a)*u, 4 residual
+// after W2; the argmax words use ep(L, 0).
+struct PCtx {
+    uint32_t base;   // epoch base of this step
+    int pos, n, nch, tok;
+    bool fused;      // attention recomputed inside the Wo blocks
+    int32_t* err;
+    __device__ __forceinline__ uint32_t ep(int l, int ph) const {
+        return base + 1u + static_cast<uint32_t>(l * kPhases + ph);
+    }
+};
+
+template <int WDT>
+__device__ __forceinline__ float emb_at(const StepArgs& s, int tok, int j) {
+    const size_t e = static_cast<size_t>(tok) * s.d + j;
+    return WDT == kBF16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(s.emb)[e]) << 16)
+                        : static_cast<const float*>(s.emb)[e];
+}
+
+template <int PD>
+struct KV {
+    static constexpr int LPR = PD / 4;       // lanes per cache row
+    static constexpr int RPI = 64 / LPR;     // rows per load instruction
+    static constexpr int NI = kPChunk / RPI; // load instructions per attention chunk
+    float4 k[NI], v[NI];
+
+    // the wave's cached rows of group g at positions t0 + ii * RPI + r, clamped
+    // to the last row an earlier step wrote (pos - 1, or 0)
+    __device__ __forceinline__ void load(const StepArgs& s, int l, int g, int t0, int pos) {
+        const int lane = threadIdx.x & 63, r = lane / LPR, e4 = lane % LPR;
+        const int tmax = pos > 0 ? pos - 1 : 0;
+#pragma unroll
+        for (int ii = 0; ii < NI; ii++) {
+            const int tt = min(t0 + ii * RPI + r, tmax);
+            k[ii] = *reinterpret_cast<const float4*>(s.cache + cache_row(s, l, 0, 0, g, tt) + e4 * 4);
+            v[ii] = *reinterpret_cast<const float4*>(s.cache + cache_row(s, l, 1, 0, g, tt) + e4 * 4);
+        }
+    }
+
+    // Attention of the query heads of group g over the held positions; rows
+    // past pos are masked and the row at pos is the new key/value from qkv
+    // (LDS, group-major: rep queries, key, value).  For every head j the lanes
+    // of the first row group get emit(j, e4, max score, sum of weights,
+    // weighted sum of values for dims 4 e4 .. 4 e4 + 3).
+    template <typename Emit>
+    __device__ __forceinline__ void attend(const float* qkv, int g, int rep, int t0, int pos, Emit emit) {
+        const int lane = threadIdx.x & 63, r = lane / LPR, e4 = lane % LPR;
+        const int GS = (rep + 2) * PD;
+        const float scale = 1.0f / sqrtf(static_cast<float>(PD));
+        const float4 kn = *reinterpret_cast<const float4*>(qkv + g * GS + rep * PD + e4 * 4);
+        const float4 vn = *reinterpret_cast<const float4*>(qkv + g * GS + (rep + 1) * PD + e4 * 4);
+#pragma unroll
+        for (int ii = 0; ii < NI; ii++) {
+            const int tt = t0 + ii * RPI + r;
+            if (tt == pos) {
+                k[ii] = kn;
+                v[ii] = vn;
+            } else if (tt > pos) {  // past the context: weight 0, and no stale value may enter
+                v[ii] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        for (int j = 0; j < rep; j++) {
+            const float4 q = *reinterpret_cast<const float4*>(qkv + g * GS + j * PD + e4 * 4);
+            float sc[NI];
+            float m = -INFINITY;
+#pragma unroll
+            for (int ii = 0; ii < NI; ii++) {
+                float dd = k[ii].x * q.x;
+                dd = fmaf(k[ii].y, q.y, dd);
+                dd = fmaf(k[ii].z, q.z, dd);
+                dd = fmaf(k[ii].w, q.w, dd);
+#pragma unroll
+                for (int o = LPR / 2; o > 0; o >>= 1) dd += __shfl_xor(dd, o);
+                sc[ii] = t0 + ii * RPI + r <= pos ? dd * scale : -INFINITY;
+                m = fmaxf(m, sc[ii]);
+            }
+#pragma unroll
+            for (int o = LPR; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+            float lsum = 0.f;
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int ii = 0; ii < NI; ii++) {
+                const float pe = __expf(sc[ii] - m);
+                lsum += pe;
+                acc.x = fmaf(pe, v[ii].x, acc.x);
+                acc.y = fmaf(pe, v[ii].y, acc.y);
+                acc.z = fmaf(pe, v[ii].z, acc.z);
+                acc.w = fmaf(pe, v[ii].w, acc.w);
+            }
+            // lanes of one row group hold the same lsum; sum over the row groups
+#pragma unroll
+            for (int o = LPR; o < 64; o <<= 1) {
+                lsum += __shfl_xor(lsum, o);
+                acc.x += __shfl_xor(acc.x, o);
+                acc.y += __shfl_xor(acc.y, o);
+                acc.z += __shfl_xor(acc.z, o);
+                acc.w += __shfl_xor(acc.w, o);
+            }
+            if (r == 0) emit(j, e4, m, lsum, acc);
+        }
+    }
+};
+
+// ---- role 0: Q/K/V rows, RoPE, cache append (a task of R rows per wave) ---------------------------
+template <int WDT, int G, int PD>
+__device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
+    constexpr int R = 64 / G;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int d = s.d, half = PD / 2, HD = s.H * PD, KVD = s.Hkv * PD, rep = s.H / s.Hkv;
+    const int GS = (rep + 2) * PD;
+    const int nq = HD / R, nk = KVD / R, ntask = nq + 2 * nk;
+    const int t = bt * 4 + wv, rs = lane / G, sub = lane % G;
+    const bool active = t < ntask;
+    const bool roped = t < nq + nk, is_q = t < nq;
+    int row = 0, i = 0, second = 0, which = 2;
+    if (active) {
+        if (roped) {
+            // rows i and i + D/2 of a head are rotated together; they sit 32 lanes apart
+            const int pp = (is_q ? t : t - nq) * (R / 2) + (rs % (R / 2));
+            second = rs / (R / 2);
+            i = pp % half;
+            row = (pp / half) * PD + i + second * half;
+            which = is_q ? 0 : 1;
+        } else {
+            row = (t - nq - nk) * R + rs;
+        }
+    }
+    float cs = 1.f, sn = 0.f;
+    if (roped) {
+        cs = s.rope_cos[static_cast<size_t>(c.pos) * half + i];
+        sn = s.rope_sin[static_cast<size_t>(c.pos) * half + i];
+    }
+    auto wmat = [&](int l) {
+        const LayerW& w = p.layers[l];
+        return which == 0 ? w.wq : (which == 1 ? w.wk : w.wv);
+    };
+    PStream<WDT, G> st;
+    float gr[kPNorm];
+    st.start(wmat(0), row, d, sub, active);
+    load_gains(gr, p.layers[0].attn_norm, d);
+    float* xs = sm;
+    for (int l = 0; l < s.L; l++) {
+        __syncthreads();  // nobody reads the previous layer's LDS any more
+        if (l == 0) {
+#pragma unroll
+            for (int j = 0; j < kPNorm; j++) {
+                const int e = threadIdx.x + kPThreads * j;
+                if (e < d) xs[e] = emb_at<WDT>(s, c.tok, e);
+            }
+        } else {
+            wait_sample<1>(p.ll_h, s.F, c.ep(l - 1, 3), c.err);
+            block_fetch<kPNorm>(Seg{p.ll_x, d, c.ep(l - 1, 4), xs}, c.err);
+        }
+        const float rn = block_norm(xs, d, gr, s.eps, sm);
+        if (active) {
+            const float y = rn * st.finish(xs);
+            const int g = row / PD, e = row % PD;
+            if (roped) {
+                const float partner = __shfl_xor(y, 32);
+                const float out = second ? fmaf(partner, sn, y * cs) : fmaf(-partner, sn, y * cs);
+                if (sub == 0) {
+                    if (is_q) {
+                        // query head h = row / D sits in group h / rep at slot h % rep
+                        ll_put(p.ll_qkv + (g / rep) * GS + (g % rep) * PD + e, out, c.ep(l, 0));
+                    } else {
+                        ll_put(p.ll_qkv + g * GS + rep * PD + e, out, c.ep(l, 0));
+                        s.cache[cache_row(s, l, 0, 0, g, c.pos) + e] = out;
+                    }
+                }
+            } else if (sub == 0) {
+                ll_put(p.ll_qkv + g * GS + (rep + 1) * PD + e, y, c.ep(l, 0));
+                s.cache[cache_row(s, l, 1, 0, g, c.pos) + e] = y;
+            }
+        }
+        if (l + 1 < s.L) {
+            st.start(wmat(l + 1), row, d, sub, active);
+            load_gains(gr, p.layers[l + 1].attn_norm, d);
+        }
+    }
+}
+
+// ---- role 1: attention partials per (group, 32-position chunk) (a task per wave) ------------------
+template <int PD>
+__device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
+    const int wv = threadIdx.x >> 6;
+    const int HD = s.H * PD, KVD = s.Hkv * PD, rep = s.H / s.Hkv;
+    const int t = bt * 4 + wv;
+    const bool active = t < s.Hkv * c.nch;
+    const int g = active ? t % s.Hkv : 0, ck = active ? t / s.Hkv : 0;
+    KV<PD> kv;
+    if (active) kv.load(s, 0, g, ck * kPChunk, c.pos);
+    float* qkv = sm;
+    for (int l = 0; l < s.L; l++) {
+        __syncthreads();
+        if (l > 0) wait_sample<1>(p.ll_x, s.d, c.ep(l - 1, 4), c.err);
+        block_fetch<4>(Seg{p.ll_qkv, HD + 2 * KVD, c.ep(l, 0), qkv}, c.err);
+        __syncthreads();
+        if (active) {
+            const uint32_t e1 = c.ep(l, 1);
+            kv.attend(qkv, g, rep, ck * kPChunk, c.pos, [&](int j, int e4, float m, float lsum, float4 acc) {
+                uint64_t* dst = p.ll_part + static_cast<size_t>((g * c.nch + ck) * rep + j) * (PD + 2);
+                ll_put(dst + 2 + e4 * 4 + 0, acc.x, e1);
+                ll_put(dst + 2 + e4 * 4 + 1, acc.y, e1);
+                ll_put(dst + 2 + e4 * 4 + 2, acc.z, e1);
+                ll_put(dst + 2 + e4 * 4 + 3, acc.w, e1);
+                if (e4 == 0) {
+                    ll_put(dst, m, e1);
+                    ll_put(dst + 1, lsum, e1);
+                }
+            });
+            if (l + 1 < s.L) kv.load(s, l + 1, g, ck * kPChunk, c.pos);
+        }
+    }
+}
+
+// ---- role 2: attention output of every head, Wo, residual (4 * R rows per block) ------------------
+template <int WDT, int G, int PD>
+__device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
+    constexpr int R = 64 / G;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int d = s.d, HD = s.H * PD, KVD = s.Hkv * PD, rep = s.H / s.Hkv;
+    const int rs = lane / G, sub = lane % G;
+    const int r0 = bt * 4 * R, nrows = min(4 * R, d - r0);
+    const int row = r0 + wv * R + rs;
+    const bool valid = row < d;
+    const bool attn_wave = wv < s.Hkv;  // wave g handles key/value group g
+    const int g = attn_wave ? wv : 0;
+    // LDS: [Q/K/V words | partials] [o: H*D] [residual rows: 4R]
+    const int in_n = c.fused ? HD + 2 * KVD : c.nch * s.H * (PD + 2);
+    float* in = sm;
+    float* o = sm + ((in_n + 3) & ~3);
+    float* xr = o + HD;
+    PStream<WDT, G> st;
+    KV<PD> kv;
+    st.start(p.layers[0].wo, valid ? row : 0, HD, sub, valid);
+    if (c.fused && attn_wave) kv.load(s, 0, g, 0, c.pos);
+    for (int l = 0; l < s.L; l++) {
+        __syncthreads();
+        Seg rows{p.ll_x, 0, 0u, xr};
+        if (l == 0) {
+            if (static_cast<int>(threadIdx.x) < nrows) xr[threadIdx.x] = emb_at<WDT>(s, c.tok, r0 + threadIdx.x);
+        } else {
+            rows = Seg{p.ll_x + r0, nrows, c.ep(l - 1, 4), xr};
+        }
+        if (c.fused) {
+            if (l > 0) wait_sample<1>(p.ll_x, d, c.ep(l - 1, 4), c.err);
+            block_fetch<4>(Seg{p.ll_qkv, in_n, c.ep(l, 0), in}, rows, c.err);
+        } else {
+            wait_sample<1>(p.ll_qkv, HD + 2 * KVD, c.ep(l, 0), c.err);
+            block_fetch<kPF>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
+        }
+        __syncthreads();
+        if (attn_wave) {
+            if (c.fused) {
+                kv.attend(in, g, rep, 0, c.pos, [&](int j, int e4, float, float lsum, float4 acc) {
+                    const float inv = 1.0f / lsum;
+                    float4 v;
+                    v.x = acc.x * inv;
+                    v.y = acc.y * inv;
+                    v.z = acc.z * inv;
+                    v.w = acc.w * inv;
+                    *reinterpret_cast<float4*>(o + (g * rep + j) * PD + e4 * 4) = v;
+                });
+            } else {
+                // merge the chunk partials of the group's heads (layout [group][chunk][head][m, l, D])
+                const int cstride = rep * (PD + 2);
+                for (int j = 0; j < rep; j++) {
+                    const float* ph = in + static_cast<size_t>(g * c.nch * rep + j) * (PD + 2);
+                    float M = -INFINITY;
+                    for (int cc = 0; cc < c.nch; cc++) M = fmaxf(M, ph[cc * cstride]);
+                    float Lw = 0.f;
+                    for (int cc = 0; cc < c.nch; cc++) Lw += __expf(ph[cc * cstride] - M) * ph[cc * cstride + 1];
+                    const float inv = 1.0f / Lw;
+                    for (int e = lane; e < PD; e += 64) {
+                        float acc = 0.f;
+                        for (int cc = 0; cc < c.nch; cc++)
+                            acc = fmaf(__expf(ph[cc * cstride] - M), ph[cc * cstride + 2 + e], acc);
+                        o[(g * rep + j) * PD + e] = acc * inv;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        const float y = st.finish(o);
+        if (valid && sub == 0) ll_put(p.ll_x2 + row, xr[row - r0] + y, c.ep(l, 2));
+        if (l + 1 < s.L) {
+            st.start(p.layers[l + 1].wo, valid ? row : 0, HD, sub, valid);
+            if (c.fused && attn_wave) kv.load(s, l + 1, g, 0, c.pos);
+        }
+    }
+}
+
+// ---- role 3: RMSNorm, W1 / W3, silu(a) * u (4 * R rows per block) ---------------------------------
+template <int WDT, int G>
+__device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
+    constexpr int R = 64 / G;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int d = s.d, F = s.F;
+    const int rs = lane / G, sub = lane % G;
+    const int row = bt * 4 * R + wv * R + rs;
+    const bool valid = row < F;
+    PStream<WDT, G> s1, s3;
+    float gr[kPNorm];
+    s1.start(p.layers[0].w1, valid ? row : 0, d, sub, valid);
+    s3.start(p.layers[0].w3, valid ? row : 0, d, sub, valid);
+    load_gains(gr, p.layers[0].ffn_norm, d);
+    float* xs = sm;
+    for (int l = 0; l < s.L; l++) {
+        __syncthreads();
+        if (c.fused)
+            wait_sample<1>(p.ll_qkv, (s.H + 2 * s.Hkv) * s.D, c.ep(l, 0), c.err);
+        else
+            wait_sample<1>(p.ll_part, c.nch * s.H * (s.D + 2), c.ep(l, 1), c.err);
+        block_fetch<kPNorm>(Seg{p.ll_x2, d, c.ep(l, 2), xs}, c.err);
+        const float rn = block_norm(xs, d, gr, s.eps, sm);
+        const float a = rn * s1.finish(xs);
+        const float u = rn * s3.finish(xs);
+        if (valid && sub == 0) ll_put(p.ll_h + row, (a / (1.0f + expf(-a))) * u, c.ep(l, 3));
+        if (l + 1 < s.L) {
+            s1.start(p.layers[l + 1].w1, valid ? row : 0, d, sub, valid);
+            s3.start(p.layers[l + 1].w3, valid ? row : 0, d, sub, valid);
+            load_gains(gr, p.layers[l + 1].ffn_norm, d);
+        }
+    }
+}
+
+// ---- role 4: W2, residual (4 * R rows per block) --------------------------------------------------
+template <int WDT, int G>
+__device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
+    constexpr int R = 64 / G;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int d = s.d, F = s.F;
+    const int rs = lane / G, sub = lane % G;
+    const int r0 = bt * 4 * R, nrows = min(4 * R, d - r0);
+    const int row = r0 + wv * R + rs;
+    const bool valid = row < d;
+    float* hs = sm;
+    float* xr = sm + ((F + 3) & ~3);
+    PStream<WDT, G> st;
+    st.start(p.layers[0].w2, valid ? row : 0, F, sub, valid);
+    for (int l = 0; l < s.L; l++) {
+        __syncthreads();
+        wait_sample<1>(p.ll_x2, d, c.ep(l, 2), c.err);
+        block_fetch<8>(Seg{p.ll_h, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + r0, nrows, c.ep(l, 2), xr}, c.err);
+        __syncthreads();
+        const float y = st.finish(hs);
+        if (valid && sub == 0) ll_put(p.ll_x + row, xr[row - r0] + y, c.ep(l, 4));
+        if (l + 1 < s.L) st.start(p.layers[l + 1].w2, valid ? row : 0, F, sub, valid);
+    }
+}
+
+// Blocks per role for a context of nch attention chunks (role 1 is empty when
+// attention is fused into Wo).
+struct Roles {
+    int b[5];
+    __host__ __device__ Roles(int d, int H, int Hkv, int D, int F, int gd, int gh, int gf, int nch) {
+        const int HD = H * D, KVD = Hkv * D;
+        b[0] = ((HD + 2 * KVD) / (64 / gd) + 3) / 4;
+        b[1] = nch <= 1 ? 0 : (Hkv * nch + 3) / 4;
+        b[2] = (d + 4 * (64 / gh) - 1) / (4 * (64 / gh));
+        b[3] = (F + 4 * (64 / gd) - 1) / (4 * (64 / gd));
+        b[4] = (d + 4 * (64 / gf) - 1) / (4 * (64 / gf));
+    }
+    __host__ __device__ int total() const { return b[0] + b[1] + b[2] + b[3] + b[4]; }
+};
+
+template <int WDT, int GD, int GH, int GF, int PD>
+__global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArgs p, const int32_t* __restrict__ d_tok_in,
+                                                           int tok_value, int32_t* __restrict__ d_tok_out) {
+    extern __shared__ float sm[];
+    const int blk = blockIdx.x, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    PCtx c;
+    c.err = s.err;
+    c.base = *p.epoch;
+    c.pos = s.lengths[0];
+    c.n = c.pos + 1;
+    c.nch = (c.n + kPChunk - 1) / kPChunk;
+    c.fused = c.nch == 1;
+    c.tok = d_tok_in ? d_tok_in[0] : tok_value;
+    if (c.tok < 0 || c.tok >= s.V) {
+        if (threadIdx.x == 0 && blk == 0) atomicOr(c.err, 1);
+        c.tok = 0;
+    }
+    const Roles ro(s.d, s.H, s.Hkv, PD, s.F, GD, GH, GF, c.nch);
+    int bt = blk;
+    if (bt < ro.b[0]) {
+        role_qkv<WDT, GD, PD>(s, p, c, bt, sm);
+    } else if ((bt -= ro.b[0]) < ro.b[1]) {
+        role_attn<PD>(s, p, c, bt, sm);
+    } else if ((bt -= ro.b[1]) < ro.b[2]) {
+        role_wo<WDT, GH, PD>(s, p, c, bt, sm);
+    } else if ((bt -= ro.b[2]) < ro.b[3]) {
+        role_w13<WDT, GD>(s, p, c, bt, sm);
+    } else if ((bt -= ro.b[3]) < ro.b[4]) {
+        role_w2<WDT, GF>(s, p, c, bt, sm);
+    }
+
+    // ---- final RMSNorm, vocabulary rows, one argmax word per wave --------------------------------
+    // Wave gw takes the row tasks gw, gw + 1024, ...; two tasks are in flight.
+    const uint32_t epk = c.ep(s.L, 0);
+    {
+        constexpr int R = 64 / GD;
+        const int gw = blk * 4 + wv;
+        const int ntask = (s.V + R - 1) / R;
+        const int rs = lane / GD, sub = lane % GD;
+        PStream<WDT, GD> sa, sb;
+        float gr[kPNorm];
+        int ta = gw, tb = gw + kPWaves;
+        sa.start(p.wcls, min(ta * R + rs, s.V - 1), s.d, sub, ta * R + rs < s.V);
+        sb.start(p.wcls, min(tb * R + rs, s.V - 1), s.d, sub, tb * R + rs < s.V);
+        load_gains(gr, p.out_norm, s.d);
+        float* xs = sm;
+        __syncthreads();
+        wait_sample<32>(p.ll_h, s.F, c.ep(s.L - 1, 3), c.err);
+        block_fetch<kPNorm>(Seg{p.ll_x, s.d, c.ep(s.L - 1, 4), xs}, c.err);
+        const float rn = block_norm(xs, s.d, gr, s.eps, sm);
+        uint64_t key = 0ull;
+        while (ta < ntask) {
+            const int row = ta * R + rs;
+            const float y = rn * sa.finish(xs);
+            if (row < s.V && sub == 0) {
+                s.logits[row] = y;
+                const uint64_t k = key_word(y, row, epk);
+                key = k > key ? k : key;
+            }
+            // the stream just used takes the task after the one in flight
+            const int tn = tb + kPWaves;
+            if (tn < ntask) sa.start(p.wcls, min(tn * R + rs, s.V - 1), s.d, sub, tn * R + rs < s.V);
+            const PStream<WDT, GD> tmp = sa;
+            sa = sb;
+            sb = tmp;
+            ta = tb;
+            tb = tn;
+        }
+        key = wave_max_u64(key);
+        if (lane == 0) {
+            if (key == 0ull) key = epk & 0x7FFFu;  // a wave without rows still reports
+            __hip_atomic_store(p.ll_keys + gw, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    // ---- one wave reduces the argmax words, writes the token and the bookkeeping ------------------
+    if (blk == 0 && wv == 0) {
+        constexpr int JK = kPWaves / 64;
+        uint64_t wds[JK];
+        long spins = 0;
+        while (true) {
+#pragma unroll
+            for (int j = 0; j < JK; j++) wds[j] = ll_get(p.ll_keys + lane + 64 * j);
+            bool ok = true;
+#pragma unroll
+            for (int j = 0; j < JK; j++) ok &= (wds[j] & 0x7FFFu) == (epk & 0x7FFFu);
+            if (__all(ok)) break;
+            if (give_up(spins, c.err)) break;
+        }
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int j = 0; j < JK; j++) best = wds[j] > best ? wds[j] : best;
+        best = wave_max_u64(best);
+        if (lane == 0) {
+            const int idx = static_cast<int>(0x1FFFFu - static_cast<uint32_t>((best >> 15) & 0x1FFFFu));
+            if (d_tok_out) d_tok_out[0] = idx;
+            s.lengths[0] = c.pos + 1;
+            s.pos[0] = c.pos;
+            s.slot[0] = 0;
+            s.flag[0] = 1;
+            *p.epoch = c.base + static_cast<uint32_t>(s.L * kPhases + 2);
+        }
+    }
+}
+
+// ---- host side ----------------------------------------------------------------------------------
+
+// Lanes per row for rows of K elements: the fewest (4 .. 32) that keep each
+// lane's share within the kPF register chunks (0: none does).
+static int pg(int K, int wdt) {
+    const int nch = K / (wdt == kBF16 ? 8 : 4);
+    for (int g = 4; g <= 32; g *= 2)
+        if ((nch + g - 1) / g <= kPF) return g;
+    return 0;
+}
+
+// The instantiated (G for d, G for H*D, G for F) combinations.
+template <int WDT, int PD>
+static const void* pick_g(int gd, int gh, int gf) {
+    if (gd == 4 && gh == 4 && gf == 4) return reinterpret_cast<const void*>(k_persist<WDT, 4, 4, 4, PD>);
+    if (gd == 8 && gh == 8 && gf == 16) return reinterpret_cast<const void*>(k_persist<WDT, 8, 8, 16, PD>);
+    return nullptr;
+}
+
+template <int WDT>
+static const void* pick_pd(int D, int gd, int gh, int gf) {
+    switch (D) {
+        case 16: return pick_g<WDT, 16>(gd, gh, gf);
+        case 32: return pick_g<WDT, 32>(gd, gh, gf);
+        case 64: return pick_g<WDT, 64>(gd, gh, gf);
+        default: return nullptr;
+    }
+}
+
+static const void* persist_fn(const StepArgs& s) {
+    const int gd = pg(s.d, s.wdt), gh = pg(s.H * s.D, s.wdt), gf = pg(s.F, s.wdt);
+    return s.wdt == kBF16 ? pick_pd<kBF16>(s.D, gd, gh, gf) : pick_pd<kF32>(s.D, gd, gh, gf);
+}
+
+int persist_max_ctx(const StepArgs& s) {
+    const int HD = s.H * s.D, KVD = s.Hkv * s.D;
+    if (s.B != 1 || !persist_fn(s)) return 0;
+    if (s.d > kPThreads * kPNorm || s.d < 64 || s.Hkv > 4 || s.V > 0x1FFFF) return 0;
+    // LDS of role 2 (Q/K/V words, o, residual rows) and role 4 (h, residual rows)
+    if (2 * HD + 2 * KVD + 4 + 64 > kPRed || s.F + 4 + 64 > kPRed) return 0;
+    const int gd = pg(s.d, s.wdt), gh = pg(HD, s.wdt), gf = pg(s.F, s.wdt);
+    if (Roles(s.d, s.H, s.Hkv, s.D, s.F, gd, gh, gf, 1).total() > kPBlocks) return 0;
+    // longer contexts add role 1 blocks and keep every partial in role 2's LDS
+    int chunks = 1;
+    while (chunks < kPMaxChunks) {
+        const int nc = chunks + 1;
+        if (Roles(s.d, s.H, s.Hkv, s.D, s.F, gd, gh, gf, nc).total() > kPBlocks) break;
+        if (nc * s.H * (s.D + 2) + 4 + HD + 64 > kPRed) break;
+        chunks = nc;
+    }
+    const int ctx = chunks * kPChunk;
+    return ctx < s.T ? ctx : s.T;
+}
+
+size_t persist_lds() { return sizeof(float) * kPLds; }
+
+hipError_t persist_prepare(const StepArgs& s) {
+    return hipFuncSetAttribute(persist_fn(s), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(persist_lds()));
+}
+
+hipError_t enqueue_persist(const StepArgs& s, const PersistArgs& p, const int32_t* d_tok_in, int tok_value,
+                           int32_t* d_tok_out, hipStream_t st) {
+    void* args[] = {const_cast<StepArgs*>(&s), const_cast<PersistArgs*>(&p), &d_tok_in, &tok_value, &d_tok_out};
+    return hipLaunchKernel(persist_fn(s), dim3(kPBlocks), dim3(kPThreads), args, persist_lds(), st);
+}
+
+}  // namespace ds

@@ -206,3 +206,37 @@ def test_batched_mfma_projections_match_oracle(B):
     lens = rng.integers(1, 40, size=B)
     prompts = [synth.random_tokens(300 + b, int(n), shape.vocab_size) for b, n in enumerate(lens)]
     compare(shape, arena, prompts, 3, 64, f"mfma B={B}")
+
+
+def test_batch1_multi_chunk_attention_tiny():
+    """Batch-1 steps past 32 positions merge per-chunk attention partials
+    (positions 70..99 span three and four 32-position chunks)."""
+    shape = synth.TINY
+    arena = synth.make_arena(shape, 12, std=0.15, gain_sigma=0.1)
+    prompts = [synth.random_tokens(500, 70, shape.vocab_size)]
+    compare(shape, arena, prompts, 30, 128, "tiny B=1 multi-chunk")
+
+
+def test_batch1_multi_chunk_attention_135m():
+    w = synth.WORKLOADS["llama135m_p5"]
+    arena = synth.make_arena(w.model, w.model_seed)
+    prompts = [synth.random_tokens(501, 40, w.model.vocab_size)]
+    compare(w.model, arena, prompts, 6, w.ctx, "135m B=1 positions 40..45")
+
+
+def test_batch1_single_launch_matches_per_operation_launches(monkeypatch):
+    """The single-launch batch-1 step and the one-launch-per-operation path
+    (DS_PERSIST=0) give the same greedy tokens and logits within tolerance."""
+    shape = synth.TINY
+    arena = synth.make_arena(shape, 13, std=0.15, gain_sigma=0.1)
+    prompts = [synth.random_tokens(502, 30, shape.vocab_size)]
+    feed = [[int(t)] for t in synth.random_tokens(503, 12, shape.vocab_size)]
+    a = gpu_run(shape, arena, prompts, feed, 128)
+    monkeypatch.setenv("DS_PERSIST", "0")
+    b = gpu_run(shape, arena, prompts, feed, 128)
+    assert np.array_equal(a["first_tok"], b["first_tok"])
+    assert_logits_close(a["first_lg"], b["first_lg"], "first")
+    for k in range(len(feed)):
+        assert_logits_close(a["lgs"][k], b["lgs"][k], f"step {k}")
+    n = len(prompts[0]) + len(feed)
+    assert_logits_close(a["cache"][:, :, 0, :, :n], b["cache"][:, :, 0, :, :n], "cache")
