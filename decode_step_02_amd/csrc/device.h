@@ -48,4 +48,80 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
     return k;
 }
 
+
+// ---- cross-lane reductions in the VALU -----------------------------------------------------------
+// __shfl_xor goes through the LDS unit (ds_bpermute) and a chain of them
+// waits for each round trip.  Within a 16-lane row, DPP does the same in one
+// VALU instruction (quad_perm for lane ^ 1 and lane ^ 2, the half-row and row
+// mirrors once values are uniform over quads / half rows, row_ror:8 for
+// lane ^ 8); gfx950's permlane16/32 swaps exchange lane ^ 16 and lane ^ 32.
+// Both outputs of a swap of v with itself hold v[l] and v[l ^ 16] (or 32), so
+// their sum or max is the pair's result, in the same order on both lanes.
+// All of these need the whole wave active.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+struct OpSum {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// op(v, v[lane ^ O]) for O in {1, 2, 4, 8, 16, 32}: true exchanges, valid for any values.
+template <int O, typename Op>
+__device__ __forceinline__ float xor_op(float v, Op op) {
+    static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "lane distance");
+    if constexpr (O == 1) {
+        return op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+    } else if constexpr (O == 2) {
+        return op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+    } else if constexpr (O == 4) {
+        return op(v, __shfl_xor(v, 4));
+    } else if constexpr (O == 8) {
+        return op(v, dpp_mov<0x128>(v));  // row_ror:8
+    } else if constexpr (O == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+}
+
+// All-reduce over aligned groups of N lanes (N a power of two <= 64); every
+// lane of a group ends with the same bits.  Levels 4 and 8 use the mirrors,
+// which are exchanges of whole quads / half rows once those are uniform.
+template <int N, typename Op>
+__device__ __forceinline__ float group_reduce(float v, Op op) {
+    if constexpr (N >= 2) v = xor_op<1>(v, op);
+    if constexpr (N >= 4) v = xor_op<2>(v, op);
+    if constexpr (N >= 8) v = op(v, dpp_mov<0x141>(v));   // row_half_mirror
+    if constexpr (N >= 16) v = op(v, dpp_mov<0x140>(v));  // row_mirror
+    if constexpr (N >= 32) v = xor_op<16>(v, op);
+    if constexpr (N >= 64) v = xor_op<32>(v, op);
+    return v;
+}
+
+// Reduce over the lanes lane ^ k, k a multiple of LO (LO a power of two):
+// combines the groups of LO lanes position by position.
+template <int LO, typename Op>
+__device__ __forceinline__ float stride_reduce(float v, Op op) {
+    if constexpr (LO <= 1) v = xor_op<1>(v, op);
+    if constexpr (LO <= 2) v = xor_op<2>(v, op);
+    if constexpr (LO <= 4) v = xor_op<4>(v, op);
+    if constexpr (LO <= 8) v = xor_op<8>(v, op);
+    if constexpr (LO <= 16) v = xor_op<16>(v, op);
+    if constexpr (LO <= 32) v = xor_op<32>(v, op);
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float v) { return group_reduce<N>(v, OpSum{}); }
+template <int N>
+__device__ __forceinline__ float group_max(float v) { return group_reduce<N>(v, OpMax{}); }
+
 }  // namespace ds

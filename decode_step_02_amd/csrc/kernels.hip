@@ -76,13 +76,6 @@ template <> struct Wt<kF32> {
     }
 };
 
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
 // One lane's share of one row: the first kPrefetch chunks are loaded by
 // start(), the rest while finish() accumulates.  finish() returns the full
 // row dot product in every lane of the row's G-lane group.

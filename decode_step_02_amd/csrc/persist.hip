@@ -159,7 +159,7 @@ __device__ float block_norm(float* xs, int n, const float (&gr)[kPNorm], float e
             xs[i] = gr[j] * v;
         }
     }
-    ss = wave_sum(ss);
+    ss = group_sum<64>(ss);
     if ((tid & 63) == 0) sm[kPRed + (tid >> 6)] = ss;
     __syncthreads();
     const float tot = (sm[kPRed] + sm[kPRed + 1]) + (sm[kPRed + 2] + sm[kPRed + 3]);
@@ -171,26 +171,50 @@ __device__ __forceinline__ void load_gains(float (&gr)[kPNorm], const float* __r
     for (int j = 0; j < kPNorm; j++) gr[j] = g[min(static_cast<int>(threadIdx.x) + kPThreads * j, n - 1)];
 }
 
+// The lane's share of the input vector of a row product: the chunks sub,
+// sub + G, ... (EPC floats each, clamped to the last chunk), read from LDS
+// into registers in one batch so that the products wait for LDS once.
+template <int WDT, int NC>
+struct XRegs {
+    static constexpr int EPC = WDT == kBF16 ? 8 : 4;
+    float4 v[NC * EPC / 4];
+    __device__ __forceinline__ void load(const float* xs, int sub, int G, int nchunks) {
+#pragma unroll
+        for (int p = 0; p < NC; p++) {
+            const float4* src = reinterpret_cast<const float4*>(xs + min(sub + p * G, nchunks - 1) * EPC);
+#pragma unroll
+            for (int q = 0; q < EPC / 4; q++) v[p * (EPC / 4) + q] = src[q];
+        }
+    }
+};
+
 // The wave's share of one weight row: G lanes per row, lane `sub` takes the
-// 16-byte chunks sub, sub + G, ...  start() loads the first kPF of them into
-// registers, so finish() touches no memory when the row has at most kPF * G
-// chunks (the host picks G so that it has).
-template <int WDT, int G>
+// 16-byte chunks sub, sub + G, ..., NC of them (the host picks G and NC so
+// that NC * G covers the row).  start() issues their loads into registers;
+// finish() multiplies them with the matching XRegs and reduces over the G
+// lanes, touching no memory.
+template <int WDT, int G, int NC>
 struct PStream {
     static constexpr int EPC = WDT == kBF16 ? 8 : 4;
-    uint4 w[kPF];
-    const void* W;
-    size_t base;
+    uint4 w[NC];
     int nch, sub;
-    __device__ __forceinline__ uint4 ld(size_t e) const {
-        return WDT == kBF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + e)
-                            : *reinterpret_cast<const uint4*>(static_cast<const float*>(W) + e);
+    __device__ __forceinline__ void start(const void* W, int row, int K, int sub_, bool valid) {
+        const size_t base = static_cast<size_t>(row) * K;
+        sub = sub_;
+        nch = valid ? K / EPC : 0;
+        const int last = K / EPC - 1;
+#pragma unroll
+        for (int p = 0; p < NC; p++) {
+            const size_t e = base + static_cast<size_t>(min(sub + p * G, last)) * EPC;
+            w[p] = WDT == kBF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + e)
+                                : *reinterpret_cast<const uint4*>(static_cast<const float*>(W) + e);
+        }
     }
-    __device__ __forceinline__ float dot(const uint4 u, const float* xs, float acc) const {
+    __device__ __forceinline__ static float dot(const uint4 u, const float4* x) {
+        float acc;
         if (WDT == kBF16) {
-            const float4 a = *reinterpret_cast<const float4*>(xs);
-            const float4 b = *reinterpret_cast<const float4*>(xs + 4);
-            acc = fmaf(__uint_as_float(u.x << 16), a.x, acc);
+            const float4 a = x[0], b = x[1];
+            acc = __uint_as_float(u.x << 16) * a.x;
             acc = fmaf(__uint_as_float(u.x & 0xFFFF0000u), a.y, acc);
             acc = fmaf(__uint_as_float(u.y << 16), a.z, acc);
             acc = fmaf(__uint_as_float(u.y & 0xFFFF0000u), a.w, acc);
@@ -199,38 +223,25 @@ struct PStream {
             acc = fmaf(__uint_as_float(u.w << 16), b.z, acc);
             acc = fmaf(__uint_as_float(u.w & 0xFFFF0000u), b.w, acc);
         } else {
-            const float4 a = *reinterpret_cast<const float4*>(xs);
-            acc = fmaf(__uint_as_float(u.x), a.x, acc);
+            const float4 a = x[0];
+            acc = __uint_as_float(u.x) * a.x;
             acc = fmaf(__uint_as_float(u.y), a.y, acc);
             acc = fmaf(__uint_as_float(u.z), a.z, acc);
             acc = fmaf(__uint_as_float(u.w), a.w, acc);
         }
         return acc;
     }
-    __device__ __forceinline__ void start(const void* W_, int row, int K, int sub_, bool valid) {
-        W = W_;
-        base = static_cast<size_t>(row) * K;
-        sub = sub_;
-        nch = valid ? K / EPC : 0;
-        const int last = K / EPC - 1;
-#pragma unroll
-        for (int p = 0; p < kPF; p++) w[p] = ld(base + static_cast<size_t>(min(sub + p * G, last)) * EPC);
-    }
-    __device__ __forceinline__ float finish(const float* xs) const {
+    __device__ __forceinline__ float finish(const XRegs<WDT, NC>& x) const {
         float a0 = 0.f, a1 = 0.f;
-        const int last = nch > 0 ? nch - 1 : 0;
 #pragma unroll
-        for (int p = 0; p < kPF; p += 2) {
-            const float d0 = dot(w[p], xs + min(sub + p * G, last) * EPC, 0.f);
-            const float d1 = dot(w[p + 1], xs + min(sub + (p + 1) * G, last) * EPC, 0.f);
-            a0 += sub + p * G < nch ? d0 : 0.f;
-            a1 += sub + (p + 1) * G < nch ? d1 : 0.f;
+        for (int p = 0; p < NC; p++) {
+            const float d = dot(w[p], x.v + p * (EPC / 4));
+            if (p & 1)
+                a1 += sub + p * G < nch ? d : 0.f;
+            else
+                a0 += sub + p * G < nch ? d : 0.f;
         }
-        for (int c = sub + kPF * G; c < nch; c += G) a0 = dot(ld(base + static_cast<size_t>(c) * EPC), xs + c * EPC, a0);
-        float v = a0 + a1;
-#pragma unroll
-        for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-        return v;
+        return group_sum<G>(a0 + a1);
     }
 };
 
@@ -255,6 +266,15 @@ struct PCtx {
     }
 };
 
+// Compile-time shape class of one instantiation: weight type, head dim,
+// query heads per key/value head, and lanes per row / chunks per lane for
+// rows of d (Q/K/V, W1/W3, vocabulary), H*D (Wo) and F (W2) elements.
+template <int WDT_, int PD_, int REP_, int GD_, int NCD_, int GH_, int NCH_, int GF_, int NCF_>
+struct PCfg {
+    static constexpr int WDT = WDT_, PD = PD_, REP = REP_;
+    static constexpr int GD = GD_, NCD = NCD_, GH = GH_, NCH = NCH_, GF = GF_, NCF = NCF_;
+};
+
 template <int WDT>
 __device__ __forceinline__ float emb_at(const StepArgs& s, int tok, int j) {
     const size_t e = static_cast<size_t>(tok) * s.d + j;
@@ -262,7 +282,7 @@ __device__ __forceinline__ float emb_at(const StepArgs& s, int tok, int j) {
                         : static_cast<const float*>(s.emb)[e];
 }
 
-template <int PD>
+template <int PD, int REP>
 struct KV {
     static constexpr int LPR = PD / 4;       // lanes per cache row
     static constexpr int RPI = 64 / LPR;     // rows per load instruction
@@ -282,18 +302,20 @@ struct KV {
         }
     }
 
-    // Attention of the query heads of group g over the held positions; rows
-    // past pos are masked and the row at pos is the new key/value from qkv
-    // (LDS, group-major: rep queries, key, value).  For every head j the lanes
-    // of the first row group get emit(j, e4, max score, sum of weights,
-    // weighted sum of values for dims 4 e4 .. 4 e4 + 3).
+    // Attention of the REP query heads of group g over the held positions.
+    // Rows past pos are masked, the row at pos is the new key/value from qkv
+    // (LDS, group-major: REP queries, key, value), and slots wholly past pos
+    // are skipped.  The heads are scored together so that their reductions
+    // interleave.  For every head j the lanes of the first row group get
+    // emit(j, e4, max score, sum of weights, weighted sum of values for dims
+    // 4 e4 .. 4 e4 + 3).
     template <typename Emit>
-    __device__ __forceinline__ void attend(const float* qkv, int g, int rep, int t0, int pos, Emit emit) {
+    __device__ __forceinline__ void attend(const float* qkv, int g, int t0, int pos, Emit emit) {
         const int lane = threadIdx.x & 63, r = lane / LPR, e4 = lane % LPR;
-        const int GS = (rep + 2) * PD;
+        constexpr int GS = (REP + 2) * PD;
         const float scale = 1.0f / sqrtf(static_cast<float>(PD));
-        const float4 kn = *reinterpret_cast<const float4*>(qkv + g * GS + rep * PD + e4 * 4);
-        const float4 vn = *reinterpret_cast<const float4*>(qkv + g * GS + (rep + 1) * PD + e4 * 4);
+        const float4 kn = *reinterpret_cast<const float4*>(qkv + g * GS + REP * PD + e4 * 4);
+        const float4 vn = *reinterpret_cast<const float4*>(qkv + g * GS + (REP + 1) * PD + e4 * 4);
 #pragma unroll
         for (int ii = 0; ii < NI; ii++) {
             const int tt = t0 + ii * RPI + r;
@@ -304,55 +326,77 @@ struct KV {
                 v[ii] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
-        for (int j = 0; j < rep; j++) {
-            const float4 q = *reinterpret_cast<const float4*>(qkv + g * GS + j * PD + e4 * 4);
-            float sc[NI];
-            float m = -INFINITY;
+        float4 q[REP];
 #pragma unroll
-            for (int ii = 0; ii < NI; ii++) {
-                float dd = k[ii].x * q.x;
-                dd = fmaf(k[ii].y, q.y, dd);
-                dd = fmaf(k[ii].z, q.z, dd);
-                dd = fmaf(k[ii].w, q.w, dd);
+        for (int j = 0; j < REP; j++) q[j] = *reinterpret_cast<const float4*>(qkv + g * GS + j * PD + e4 * 4);
+        float sc[REP][NI];
 #pragma unroll
-                for (int o = LPR / 2; o > 0; o >>= 1) dd += __shfl_xor(dd, o);
-                sc[ii] = t0 + ii * RPI + r <= pos ? dd * scale : -INFINITY;
-                m = fmaxf(m, sc[ii]);
+        for (int ii = 0; ii < NI; ii++) {
+            const int tb = t0 + ii * RPI;  // first position of the slot (uniform)
+            if (tb <= pos) {
+#pragma unroll
+                for (int j = 0; j < REP; j++) {
+                    float dd = k[ii].x * q[j].x;
+                    dd = fmaf(k[ii].y, q[j].y, dd);
+                    dd = fmaf(k[ii].z, q[j].z, dd);
+                    dd = fmaf(k[ii].w, q[j].w, dd);
+                    dd = group_sum<LPR>(dd);
+                    sc[j][ii] = tb + r <= pos ? dd * scale : -INFINITY;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < REP; j++) sc[j][ii] = -INFINITY;
             }
+        }
+        float m[REP], ls[REP];
+        float4 acc[REP];
 #pragma unroll
-            for (int o = LPR; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-            float lsum = 0.f;
-            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < REP; j++) {
+            m[j] = sc[j][0];
 #pragma unroll
-            for (int ii = 0; ii < NI; ii++) {
-                const float pe = __expf(sc[ii] - m);
-                lsum += pe;
-                acc.x = fmaf(pe, v[ii].x, acc.x);
-                acc.y = fmaf(pe, v[ii].y, acc.y);
-                acc.z = fmaf(pe, v[ii].z, acc.z);
-                acc.w = fmaf(pe, v[ii].w, acc.w);
+            for (int ii = 1; ii < NI; ii++) m[j] = fmaxf(m[j], sc[j][ii]);
+            m[j] = stride_reduce<LPR>(m[j], OpMax{});
+            ls[j] = 0.f;
+            acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int ii = 0; ii < NI; ii++) {
+            if (t0 + ii * RPI <= pos) {
+#pragma unroll
+                for (int j = 0; j < REP; j++) {
+                    const float pe = __expf(sc[j][ii] - m[j]);
+                    ls[j] += pe;
+                    acc[j].x = fmaf(pe, v[ii].x, acc[j].x);
+                    acc[j].y = fmaf(pe, v[ii].y, acc[j].y);
+                    acc[j].z = fmaf(pe, v[ii].z, acc[j].z);
+                    acc[j].w = fmaf(pe, v[ii].w, acc[j].w);
+                }
             }
-            // lanes of one row group hold the same lsum; sum over the row groups
+        }
+        // lanes of one row group hold the same sum; add up the row groups
 #pragma unroll
-            for (int o = LPR; o < 64; o <<= 1) {
-                lsum += __shfl_xor(lsum, o);
-                acc.x += __shfl_xor(acc.x, o);
-                acc.y += __shfl_xor(acc.y, o);
-                acc.z += __shfl_xor(acc.z, o);
-                acc.w += __shfl_xor(acc.w, o);
-            }
-            if (r == 0) emit(j, e4, m, lsum, acc);
+        for (int j = 0; j < REP; j++) {
+            ls[j] = stride_reduce<LPR>(ls[j], OpSum{});
+            acc[j].x = stride_reduce<LPR>(acc[j].x, OpSum{});
+            acc[j].y = stride_reduce<LPR>(acc[j].y, OpSum{});
+            acc[j].z = stride_reduce<LPR>(acc[j].z, OpSum{});
+            acc[j].w = stride_reduce<LPR>(acc[j].w, OpSum{});
+        }
+        if (r == 0) {
+#pragma unroll
+            for (int j = 0; j < REP; j++) emit(j, e4, m[j], ls[j], acc[j]);
         }
     }
 };
 
 // ---- role 0: Q/K/V rows, RoPE, cache append (a task of R rows per wave) ---------------------------
-template <int WDT, int G, int PD>
+template <class C>
 __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
-    constexpr int R = 64 / G;
+    constexpr int G = C::GD, R = 64 / G, PD = C::PD, REP = C::REP;
+    constexpr int EPC = C::WDT == kBF16 ? 8 : 4;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int d = s.d, half = PD / 2, HD = s.H * PD, KVD = s.Hkv * PD, rep = s.H / s.Hkv;
-    const int GS = (rep + 2) * PD;
+    const int d = s.d, half = PD / 2, HD = s.H * PD, KVD = s.Hkv * PD;
+    constexpr int GS = (REP + 2) * PD;
     const int nq = HD / R, nk = KVD / R, ntask = nq + 2 * nk;
     const int t = bt * 4 + wv, rs = lane / G, sub = lane % G;
     const bool active = t < ntask;
@@ -379,7 +423,7 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
         const LayerW& w = p.layers[l];
         return which == 0 ? w.wq : (which == 1 ? w.wk : w.wv);
     };
-    PStream<WDT, G> st;
+    PStream<C::WDT, G, C::NCD> st;
     float gr[kPNorm];
     st.start(wmat(0), row, d, sub, active);
     load_gains(gr, p.layers[0].attn_norm, d);
@@ -390,7 +434,7 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
 #pragma unroll
             for (int j = 0; j < kPNorm; j++) {
                 const int e = threadIdx.x + kPThreads * j;
-                if (e < d) xs[e] = emb_at<WDT>(s, c.tok, e);
+                if (e < d) xs[e] = emb_at<C::WDT>(s, c.tok, e);
             }
         } else {
             wait_sample<1>(p.ll_h, s.F, c.ep(l - 1, 3), c.err);
@@ -398,22 +442,24 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
         }
         const float rn = block_norm(xs, d, gr, s.eps, sm);
         if (active) {
-            const float y = rn * st.finish(xs);
+            XRegs<C::WDT, C::NCD> xr;
+            xr.load(xs, sub, G, d / EPC);
+            const float y = rn * st.finish(xr);
             const int g = row / PD, e = row % PD;
             if (roped) {
                 const float partner = __shfl_xor(y, 32);
                 const float out = second ? fmaf(partner, sn, y * cs) : fmaf(-partner, sn, y * cs);
                 if (sub == 0) {
                     if (is_q) {
-                        // query head h = row / D sits in group h / rep at slot h % rep
-                        ll_put(p.ll_qkv + (g / rep) * GS + (g % rep) * PD + e, out, c.ep(l, 0));
+                        // query head h = row / D sits in group h / REP at slot h % REP
+                        ll_put(p.ll_qkv + (g / REP) * GS + (g % REP) * PD + e, out, c.ep(l, 0));
                     } else {
-                        ll_put(p.ll_qkv + g * GS + rep * PD + e, out, c.ep(l, 0));
+                        ll_put(p.ll_qkv + g * GS + REP * PD + e, out, c.ep(l, 0));
                         s.cache[cache_row(s, l, 0, 0, g, c.pos) + e] = out;
                     }
                 }
             } else if (sub == 0) {
-                ll_put(p.ll_qkv + g * GS + (rep + 1) * PD + e, y, c.ep(l, 0));
+                ll_put(p.ll_qkv + g * GS + (REP + 1) * PD + e, y, c.ep(l, 0));
                 s.cache[cache_row(s, l, 1, 0, g, c.pos) + e] = y;
             }
         }
@@ -425,14 +471,15 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
 }
 
 // ---- role 1: attention partials per (group, 32-position chunk) (a task per wave) ------------------
-template <int PD>
+template <class C>
 __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
+    constexpr int PD = C::PD, REP = C::REP;
     const int wv = threadIdx.x >> 6;
-    const int HD = s.H * PD, KVD = s.Hkv * PD, rep = s.H / s.Hkv;
+    const int HD = s.H * PD, KVD = s.Hkv * PD;
     const int t = bt * 4 + wv;
     const bool active = t < s.Hkv * c.nch;
     const int g = active ? t % s.Hkv : 0, ck = active ? t / s.Hkv : 0;
-    KV<PD> kv;
+    KV<PD, REP> kv;
     if (active) kv.load(s, 0, g, ck * kPChunk, c.pos);
     float* qkv = sm;
     for (int l = 0; l < s.L; l++) {
@@ -442,8 +489,8 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
         __syncthreads();
         if (active) {
             const uint32_t e1 = c.ep(l, 1);
-            kv.attend(qkv, g, rep, ck * kPChunk, c.pos, [&](int j, int e4, float m, float lsum, float4 acc) {
-                uint64_t* dst = p.ll_part + static_cast<size_t>((g * c.nch + ck) * rep + j) * (PD + 2);
+            kv.attend(qkv, g, ck * kPChunk, c.pos, [&](int j, int e4, float m, float lsum, float4 acc) {
+                uint64_t* dst = p.ll_part + static_cast<size_t>((g * c.nch + ck) * REP + j) * (PD + 2);
                 ll_put(dst + 2 + e4 * 4 + 0, acc.x, e1);
                 ll_put(dst + 2 + e4 * 4 + 1, acc.y, e1);
                 ll_put(dst + 2 + e4 * 4 + 2, acc.z, e1);
@@ -459,11 +506,12 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
 }
 
 // ---- role 2: attention output of every head, Wo, residual (4 * R rows per block) ------------------
-template <int WDT, int G, int PD>
+template <class C>
 __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
-    constexpr int R = 64 / G;
+    constexpr int G = C::GH, R = 64 / G, PD = C::PD, REP = C::REP;
+    constexpr int EPC = C::WDT == kBF16 ? 8 : 4;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int d = s.d, HD = s.H * PD, KVD = s.Hkv * PD, rep = s.H / s.Hkv;
+    const int d = s.d, HD = s.H * PD, KVD = s.Hkv * PD;
     const int rs = lane / G, sub = lane % G;
     const int r0 = bt * 4 * R, nrows = min(4 * R, d - r0);
     const int row = r0 + wv * R + rs;
@@ -475,15 +523,15 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     float* in = sm;
     float* o = sm + ((in_n + 3) & ~3);
     float* xr = o + HD;
-    PStream<WDT, G> st;
-    KV<PD> kv;
+    PStream<C::WDT, G, C::NCH> st;
+    KV<PD, REP> kv;
     st.start(p.layers[0].wo, valid ? row : 0, HD, sub, valid);
     if (c.fused && attn_wave) kv.load(s, 0, g, 0, c.pos);
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         Seg rows{p.ll_x, 0, 0u, xr};
         if (l == 0) {
-            if (static_cast<int>(threadIdx.x) < nrows) xr[threadIdx.x] = emb_at<WDT>(s, c.tok, r0 + threadIdx.x);
+            if (static_cast<int>(threadIdx.x) < nrows) xr[threadIdx.x] = emb_at<C::WDT>(s, c.tok, r0 + threadIdx.x);
         } else {
             rows = Seg{p.ll_x + r0, nrows, c.ep(l - 1, 4), xr};
         }
@@ -492,25 +540,25 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
             block_fetch<4>(Seg{p.ll_qkv, in_n, c.ep(l, 0), in}, rows, c.err);
         } else {
             wait_sample<1>(p.ll_qkv, HD + 2 * KVD, c.ep(l, 0), c.err);
-            block_fetch<kPF>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
+            block_fetch<12>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
         }
         __syncthreads();
         if (attn_wave) {
             if (c.fused) {
-                kv.attend(in, g, rep, 0, c.pos, [&](int j, int e4, float, float lsum, float4 acc) {
+                kv.attend(in, g, 0, c.pos, [&](int j, int e4, float, float lsum, float4 acc) {
                     const float inv = 1.0f / lsum;
                     float4 v;
                     v.x = acc.x * inv;
                     v.y = acc.y * inv;
                     v.z = acc.z * inv;
                     v.w = acc.w * inv;
-                    *reinterpret_cast<float4*>(o + (g * rep + j) * PD + e4 * 4) = v;
+                    *reinterpret_cast<float4*>(o + (g * REP + j) * PD + e4 * 4) = v;
                 });
             } else {
                 // merge the chunk partials of the group's heads (layout [group][chunk][head][m, l, D])
-                const int cstride = rep * (PD + 2);
-                for (int j = 0; j < rep; j++) {
-                    const float* ph = in + static_cast<size_t>(g * c.nch * rep + j) * (PD + 2);
+                constexpr int cstride = REP * (PD + 2);
+                for (int j = 0; j < REP; j++) {
+                    const float* ph = in + static_cast<size_t>(g * c.nch * REP + j) * (PD + 2);
                     float M = -INFINITY;
                     for (int cc = 0; cc < c.nch; cc++) M = fmaxf(M, ph[cc * cstride]);
                     float Lw = 0.f;
@@ -520,13 +568,15 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
                         float acc = 0.f;
                         for (int cc = 0; cc < c.nch; cc++)
                             acc = fmaf(__expf(ph[cc * cstride] - M), ph[cc * cstride + 2 + e], acc);
-                        o[(g * rep + j) * PD + e] = acc * inv;
+                        o[(g * REP + j) * PD + e] = acc * inv;
                     }
                 }
             }
         }
         __syncthreads();
-        const float y = st.finish(o);
+        XRegs<C::WDT, C::NCH> ox;
+        ox.load(o, sub, G, HD / EPC);
+        const float y = st.finish(ox);
         if (valid && sub == 0) ll_put(p.ll_x2 + row, xr[row - r0] + y, c.ep(l, 2));
         if (l + 1 < s.L) {
             st.start(p.layers[l + 1].wo, valid ? row : 0, HD, sub, valid);
@@ -536,15 +586,16 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
 }
 
 // ---- role 3: RMSNorm, W1 / W3, silu(a) * u (4 * R rows per block) ---------------------------------
-template <int WDT, int G>
+template <class C>
 __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
-    constexpr int R = 64 / G;
+    constexpr int G = C::GD, R = 64 / G;
+    constexpr int EPC = C::WDT == kBF16 ? 8 : 4;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int d = s.d, F = s.F;
     const int rs = lane / G, sub = lane % G;
     const int row = bt * 4 * R + wv * R + rs;
     const bool valid = row < F;
-    PStream<WDT, G> s1, s3;
+    PStream<C::WDT, G, C::NCD> s1, s3;
     float gr[kPNorm];
     s1.start(p.layers[0].w1, valid ? row : 0, d, sub, valid);
     s3.start(p.layers[0].w3, valid ? row : 0, d, sub, valid);
@@ -558,8 +609,10 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
             wait_sample<1>(p.ll_part, c.nch * s.H * (s.D + 2), c.ep(l, 1), c.err);
         block_fetch<kPNorm>(Seg{p.ll_x2, d, c.ep(l, 2), xs}, c.err);
         const float rn = block_norm(xs, d, gr, s.eps, sm);
-        const float a = rn * s1.finish(xs);
-        const float u = rn * s3.finish(xs);
+        XRegs<C::WDT, C::NCD> xr;
+        xr.load(xs, sub, G, d / EPC);
+        const float a = rn * s1.finish(xr);
+        const float u = rn * s3.finish(xr);
         if (valid && sub == 0) ll_put(p.ll_h + row, (a / (1.0f + expf(-a))) * u, c.ep(l, 3));
         if (l + 1 < s.L) {
             s1.start(p.layers[l + 1].w1, valid ? row : 0, d, sub, valid);
@@ -570,9 +623,10 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
 }
 
 // ---- role 4: W2, residual (4 * R rows per block) --------------------------------------------------
-template <int WDT, int G>
+template <class C>
 __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
-    constexpr int R = 64 / G;
+    constexpr int G = C::GF, R = 64 / G;
+    constexpr int EPC = C::WDT == kBF16 ? 8 : 4;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int d = s.d, F = s.F;
     const int rs = lane / G, sub = lane % G;
@@ -581,14 +635,16 @@ __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     const bool valid = row < d;
     float* hs = sm;
     float* xr = sm + ((F + 3) & ~3);
-    PStream<WDT, G> st;
+    PStream<C::WDT, G, C::NCF> st;
     st.start(p.layers[0].w2, valid ? row : 0, F, sub, valid);
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         wait_sample<1>(p.ll_x2, d, c.ep(l, 2), c.err);
         block_fetch<8>(Seg{p.ll_h, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + r0, nrows, c.ep(l, 2), xr}, c.err);
         __syncthreads();
-        const float y = st.finish(hs);
+        XRegs<C::WDT, C::NCF> hx;
+        hx.load(hs, sub, G, F / EPC);
+        const float y = st.finish(hx);
         if (valid && sub == 0) ll_put(p.ll_x + row, xr[row - r0] + y, c.ep(l, 4));
         if (l + 1 < s.L) st.start(p.layers[l + 1].w2, valid ? row : 0, F, sub, valid);
     }
@@ -609,9 +665,11 @@ struct Roles {
     __host__ __device__ int total() const { return b[0] + b[1] + b[2] + b[3] + b[4]; }
 };
 
-template <int WDT, int GD, int GH, int GF, int PD>
+template <class C>
 __global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArgs p, const int32_t* __restrict__ d_tok_in,
                                                            int tok_value, int32_t* __restrict__ d_tok_out) {
+    constexpr int GD = C::GD;
+    constexpr int EPC = C::WDT == kBF16 ? 8 : 4;
     extern __shared__ float sm[];
     const int blk = blockIdx.x, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     PCtx c;
@@ -626,18 +684,18 @@ __global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArg
         if (threadIdx.x == 0 && blk == 0) atomicOr(c.err, 1);
         c.tok = 0;
     }
-    const Roles ro(s.d, s.H, s.Hkv, PD, s.F, GD, GH, GF, c.nch);
+    const Roles ro(s.d, s.H, s.Hkv, C::PD, s.F, C::GD, C::GH, C::GF, c.nch);
     int bt = blk;
     if (bt < ro.b[0]) {
-        role_qkv<WDT, GD, PD>(s, p, c, bt, sm);
+        role_qkv<C>(s, p, c, bt, sm);
     } else if ((bt -= ro.b[0]) < ro.b[1]) {
-        role_attn<PD>(s, p, c, bt, sm);
+        role_attn<C>(s, p, c, bt, sm);
     } else if ((bt -= ro.b[1]) < ro.b[2]) {
-        role_wo<WDT, GH, PD>(s, p, c, bt, sm);
+        role_wo<C>(s, p, c, bt, sm);
     } else if ((bt -= ro.b[2]) < ro.b[3]) {
-        role_w13<WDT, GD>(s, p, c, bt, sm);
+        role_w13<C>(s, p, c, bt, sm);
     } else if ((bt -= ro.b[3]) < ro.b[4]) {
-        role_w2<WDT, GF>(s, p, c, bt, sm);
+        role_w2<C>(s, p, c, bt, sm);
     }
 
     // ---- final RMSNorm, vocabulary rows, one argmax word per wave --------------------------------
@@ -648,7 +706,7 @@ __global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArg
         const int gw = blk * 4 + wv;
         const int ntask = (s.V + R - 1) / R;
         const int rs = lane / GD, sub = lane % GD;
-        PStream<WDT, GD> sa, sb;
+        PStream<C::WDT, GD, C::NCD> sa, sb;
         float gr[kPNorm];
         int ta = gw, tb = gw + kPWaves;
         sa.start(p.wcls, min(ta * R + rs, s.V - 1), s.d, sub, ta * R + rs < s.V);
@@ -659,10 +717,12 @@ __global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArg
         wait_sample<32>(p.ll_h, s.F, c.ep(s.L - 1, 3), c.err);
         block_fetch<kPNorm>(Seg{p.ll_x, s.d, c.ep(s.L - 1, 4), xs}, c.err);
         const float rn = block_norm(xs, s.d, gr, s.eps, sm);
+        XRegs<C::WDT, C::NCD> xr;
+        xr.load(xs, sub, GD, s.d / EPC);
         uint64_t key = 0ull;
         while (ta < ntask) {
             const int row = ta * R + rs;
-            const float y = rn * sa.finish(xs);
+            const float y = rn * sa.finish(xr);
             if (row < s.V && sub == 0) {
                 s.logits[row] = y;
                 const uint64_t k = key_word(y, row, epk);
@@ -671,7 +731,7 @@ __global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArg
             // the stream just used takes the task after the one in flight
             const int tn = tb + kPWaves;
             if (tn < ntask) sa.start(p.wcls, min(tn * R + rs, s.V - 1), s.d, sub, tn * R + rs < s.V);
-            const PStream<WDT, GD> tmp = sa;
+            const PStream<C::WDT, GD, C::NCD> tmp = sa;
             sa = sb;
             sb = tmp;
             ta = tb;
@@ -715,36 +775,39 @@ __global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArg
 
 // ---- host side ----------------------------------------------------------------------------------
 
-// Lanes per row for rows of K elements: the fewest (4 .. 32) that keep each
-// lane's share within the kPF register chunks (0: none does).
+// Lanes per row for rows of K elements: the fewest (4 .. 16) that keep each
+// lane's share within kPF register chunks (0: none does), and the chunks per lane.
 static int pg(int K, int wdt) {
     const int nch = K / (wdt == kBF16 ? 8 : 4);
-    for (int g = 4; g <= 32; g *= 2)
+    for (int g = 4; g <= 16; g *= 2)
         if ((nch + g - 1) / g <= kPF) return g;
     return 0;
 }
+static int pnc(int K, int wdt, int g) { return g ? (K / (wdt == kBF16 ? 8 : 4) + g - 1) / g : 0; }
 
-// The instantiated (G for d, G for H*D, G for F) combinations.
-template <int WDT, int PD>
-static const void* pick_g(int gd, int gh, int gf) {
-    if (gd == 4 && gh == 4 && gf == 4) return reinterpret_cast<const void*>(k_persist<WDT, 4, 4, 4, PD>);
-    if (gd == 8 && gh == 8 && gf == 16) return reinterpret_cast<const void*>(k_persist<WDT, 8, 8, 16, PD>);
-    return nullptr;
-}
-
-template <int WDT>
-static const void* pick_pd(int D, int gd, int gh, int gf) {
-    switch (D) {
-        case 16: return pick_g<WDT, 16>(gd, gh, gf);
-        case 32: return pick_g<WDT, 32>(gd, gh, gf);
-        case 64: return pick_g<WDT, 64>(gd, gh, gf);
-        default: return nullptr;
-    }
-}
+// The instantiated shape classes: the 135M-class model with bf16 weights and
+// the small fp32 test model.  Other shapes take the per-operation path.
+struct PKernel {
+    int wdt, D, rep, gd, ncd, gh, nch, gf, ncf;
+    const void* fn;
+};
+using CfgM135 = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12>;
+using CfgTiny = PCfg<kF32, 16, 2, 4, 4, 4, 4, 4, 11>;
+static const PKernel kPKernels[] = {
+    {kBF16, 64, 3, 8, 9, 8, 9, 16, 12, reinterpret_cast<const void*>(k_persist<CfgM135>)},
+    {kF32, 16, 2, 4, 4, 4, 4, 4, 11, reinterpret_cast<const void*>(k_persist<CfgTiny>)},
+};
 
 static const void* persist_fn(const StepArgs& s) {
-    const int gd = pg(s.d, s.wdt), gh = pg(s.H * s.D, s.wdt), gf = pg(s.F, s.wdt);
-    return s.wdt == kBF16 ? pick_pd<kBF16>(s.D, gd, gh, gf) : pick_pd<kF32>(s.D, gd, gh, gf);
+    const int HD = s.H * s.D;
+    const int gd = pg(s.d, s.wdt), gh = pg(HD, s.wdt), gf = pg(s.F, s.wdt);
+    if (!gd || !gh || !gf || s.Hkv <= 0 || s.H % s.Hkv) return nullptr;
+    for (const PKernel& k : kPKernels) {
+        if (k.wdt != s.wdt || k.D != s.D || k.rep != s.H / s.Hkv || k.gd != gd || k.gh != gh || k.gf != gf) continue;
+        if (k.ncd < pnc(s.d, s.wdt, gd) || k.nch < pnc(HD, s.wdt, gh) || k.ncf < pnc(s.F, s.wdt, gf)) continue;
+        return k.fn;
+    }
+    return nullptr;
 }
 
 int persist_max_ctx(const StepArgs& s) {
