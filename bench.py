@@ -10,7 +10,9 @@ every timed step is one of those 7 positions.  Steps are chained on the GPU
 Prints one JSON line with decode tok/s, the whole step's algorithmic HBM
 bytes and GB/s, a roofline entry for the dominant kernel (timed with events
 on the stream the library launches it on), and the reference decoder's
-throughput on the host as the CPU baseline.
+throughput on the host as the CPU baseline.  At batch 1 the whole step is one
+persistent kernel; its roofline entry divides the step's algorithmic bytes by
+that kernel's mean launch duration.
 """
 from __future__ import annotations
 
@@ -69,6 +71,33 @@ def kernel_bytes(m: synth.ModelShape, which: str, B: int, n_ctx: float) -> float
     return 0.0
 
 
+def kernel_sources_hash() -> str:
+    """First 16 hex digits of the sha256 of the single-launch step's sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("persist.hip", "device.h", "kernels.h"):
+        with open(os.path.join(ROOT, "decode_step_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the single-launch step from the committed
+    FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", f"k_persist_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None, "no counter summary for this workload"
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_sources_sha256_16"):
+                k, v = line.split(":", 1)
+                fields[k] = v.strip()
+    if fields.get("kernel_sources_sha256_16") != kernel_sources_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(fields["traffic_bytes_per_launch"]), "FETCH_SIZE + WRITE_SIZE, copy-calibrated (" + os.path.relpath(path, ROOT) + ")"
+
+
 def cpu_baseline(w: synth.Workload, arena: np.ndarray, budget_s: float) -> dict:
     """The reference decoder (single thread) on the host: prefill the prompt,
     then decode steps at positions prompt_len .. prompt_len+decode_calls-1,
@@ -99,6 +128,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="first run a plain copy kernel (read N MB, write N MB) three times, as the "
+                         "known-size reference for hardware byte counters; its rate is reported")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -113,7 +145,24 @@ def main():
     prompts = synth.prompts(w)
     B = w.batch
     stream = torch.cuda.Stream()
+    copy_cal = None
     with torch.cuda.stream(stream):
+        if args.calibrate_copy_mb > 0:
+            n = args.calibrate_copy_mb * (1 << 20) // 4
+            src = torch.ones(n, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            torch.mul(src, 1.0, out=dst)
+            torch.cuda.synchronize()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            for _ in range(3):
+                torch.mul(src, 1.0, out=dst)
+            c1.record(stream)
+            torch.cuda.synchronize()
+            us = c0.elapsed_time(c1) * 1000.0 / 3
+            copy_cal = {"bytes_read": 4 * n, "bytes_written": 4 * n, "us_per_launch": us,
+                        "GBps": 8 * n / (us * 1e-6) / 1e9}
+            del src, dst
         model = dsa.Model(m, arena)
         kv = dsa.KVCache(model, B, w.ctx)
         kv.set_dispatch(1 if args.dispatch == "graph" else 0)
@@ -140,34 +189,61 @@ def main():
         kv.check()
         ms_step = ms_total / args.steps
 
-        # per-kernel launch durations, each timed alone on the library's stream
-        mean_ctx = float(np.mean(base)) + (cycle - 1) / 2.0 + 1.0
+        lengths_seq = [base + (i % cycle) for i in range(cycle)]
+        bytes_step = float(np.mean([step_bytes(m, L) for L in lengths_seq]))
+        single = B == 1 and kv.single_launch_ctx() >= int(base.max()) + cycle
         kern = {}
-        for k, name in enumerate(KERNELS):
-            layer = m.n_layers // 2
-            try:
-                kv.bench_kernel(k, layer, 5, stream)
-            except dsa.DSError as e:
-                if e.status != -8:  # DS_ERR_STATE: not part of this step's kernel sequence
-                    raise
-                continue
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            kv.bench_kernel(k, layer, args.kernel_reps, stream)
-            e1.record(stream)
+        if single:
+            # The whole step is one persistent kernel.  Time each launch with
+            # events around it on the library's stream (eager dispatch, so the
+            # events bracket the kernel itself), over the same step sequence.
+            kv.set_dispatch(0)
+            kv.set_lengths(base)
+            run(args.warmup % cycle or cycle, 0)
+            kv.set_lengths(base)
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1000.0 / args.kernel_reps
-            per_step = 1 if name == "logits" else m.n_layers
-            kern[name] = {"us_per_launch": us, "launches_per_step": per_step,
-                          "us_per_step": us * per_step,
-                          "bytes_per_launch": kernel_bytes(m, name, B, mean_ctx)}
-        dom = max(kern, key=lambda n: kern[n]["us_per_step"])
-        dk = kern[dom]
+            pairs = []
+            for i in range(args.steps):
+                if i % cycle == 0 and i > 0:
+                    kv.set_lengths(base)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                kv.decode_step(tok, tok)
+                b.record(stream)
+                pairs.append((a, b))
+            torch.cuda.synchronize()
+            kv.check()
+            us = 1000.0 * sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+            dom = "k_persist (whole step)"
+            dk = {"us_per_launch": us, "launches_per_step": 1, "us_per_step": us, "bytes_per_launch": bytes_step}
+            kern[dom] = dk
+        else:
+            # one launch per operation: each kernel timed alone on the library's stream
+            mean_ctx = float(np.mean(base)) + (cycle - 1) / 2.0 + 1.0
+            for k, name in enumerate(KERNELS):
+                layer = m.n_layers // 2
+                try:
+                    kv.bench_kernel(k, layer, 5, stream)
+                except dsa.DSError as e:
+                    if e.status != -8:  # DS_ERR_STATE: not part of this step's kernel sequence
+                        raise
+                    continue
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                kv.bench_kernel(k, layer, args.kernel_reps, stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1000.0 / args.kernel_reps
+                per_step = 1 if name == "logits" else m.n_layers
+                kern[name] = {"us_per_launch": us, "launches_per_step": per_step,
+                              "us_per_step": us * per_step,
+                              "bytes_per_launch": kernel_bytes(m, name, B, mean_ctx)}
+            dom = max(kern, key=lambda n: kern[n]["us_per_step"])
+            dk = kern[dom]
         achieved = dk["bytes_per_launch"] / (dk["us_per_launch"] * 1e-6) / 1e9
 
-    lengths_seq = [base + (i % cycle) for i in range(cycle)]
-    bytes_step = float(np.mean([step_bytes(m, L) for L in lengths_seq]))
     gbps = bytes_step / (ms_step * 1e-3) / 1e9
+    traffic, traffic_note = measured_traffic(w.name) if single else (None, "counters taken for the single-launch step only")
     out = {
         "metric": "decode tok/s (135M-shaped Llama, B=1)" if w.name == "llama135m_p5" else f"decode tok/s ({w.name})",
         "value": B * args.steps / (ms_total * 1e-3),
@@ -183,15 +259,18 @@ def main():
         "data": "synthetic (seeded random weights N(0,0.02), uniform prompt ids)",
         "config": {"workload": w.name, "description": w.description, "batch": B, "ctx": w.ctx,
                    "decode_positions": [int(base.min()), int(base.max() + cycle - 1)],
-                   "dispatch": args.dispatch},
+                   "dispatch": args.dispatch, "single_launch_step": bool(single)},
         "step_bytes": bytes_step,
         "achieved_GBps": gbps,
         "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "us_per_launch": dk["us_per_launch"], "bytes_per_launch": dk["bytes_per_launch"]},
         "kernels_us_per_step": {n: round(v["us_per_step"], 2) for n, v in kern.items()},
+        "traffic_note": traffic_note,
     }
+    if copy_cal:
+        out["copy_calibration"] = copy_cal
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, arena, args.cpu_seconds)
     print(json.dumps(out), flush=True)

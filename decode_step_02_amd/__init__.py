@@ -65,6 +65,7 @@ _SIGS = {
     "ds_kv_cache_set_lengths": (C.c_int, [_P, C.POINTER(C.c_int32), _P]),
     "ds_kv_cache_get_lengths": (C.c_int, [_P, C.POINTER(C.c_int32)]),
     "ds_kv_cache_check": (C.c_int, [_P, _P]),
+    "ds_kv_cache_single_launch_ctx": (C.c_int32, [_P]),
     "ds_prefill": (C.c_int, [_P, _P, C.c_int32, C.POINTER(C.c_int32), C.c_int32, _P, _P]),
     "ds_prefill_batch": (C.c_int, [_P, _P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), _P, _P]),
     "ds_decode_step": (C.c_int, [_P, _P, _P, _P, _P]),
@@ -157,6 +158,10 @@ def ds_kv_cache_get_lengths(kv, B):
     out = (C.c_int32 * B)()
     _check(_lib.ds_kv_cache_get_lengths(kv, out))
     return list(out)
+
+
+def ds_kv_cache_single_launch_ctx(kv) -> int:
+    return int(_lib.ds_kv_cache_single_launch_ctx(kv))
 
 
 def ds_kv_cache_check(kv, stream=None):
@@ -274,6 +279,11 @@ class KVCache:
 
     def get_lengths(self):
         return ds_kv_cache_get_lengths(self.handle, self.B)
+
+    def single_launch_ctx(self) -> int:
+        """Longest context (positions after the step) of batch-1 steps that run
+        as one persistent launch; 0 if none do."""
+        return ds_kv_cache_single_launch_ctx(self.handle)
 
     def reset(self, seq=-1, stream=None):
         ds_kv_cache_reset(self.handle, seq, stream)

@@ -607,6 +607,8 @@ ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, in
     return ok();
 }
 
+int32_t ds_kv_cache_single_launch_ctx(const ds_kv* kv) { return kv ? kv->persist_ctx : -1; }
+
 ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t layer, int32_t reps,
                           void* stream) {
     if (!model || !kv || kv->model != model) return fail(DS_ERR_INVALID_ARG, "model/kv mismatch");

@@ -160,6 +160,19 @@ ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens,
 ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, int32_t* d_tok_out,
                          void* stream);
 
+/* Launch shape of batch-1 steps.  When B == 1 and the sequence holds at most
+ * the returned number of positions after the step, ds_decode_step (and each
+ * position of ds_prefill) runs as ONE persistent kernel launch that carries
+ * the whole step -- every layer, the vocabulary product and the argmax --
+ * with the phases of a layer handing their outputs to each other through
+ * device memory instead of kernel boundaries.  Otherwise (B > 1, longer
+ * contexts, shapes without a single-launch variant, or DS_PERSIST=0 in the
+ * environment when the cache was created) every operation is its own launch.
+ * Both give the same results within floating-point rounding.  Returns 0 when
+ * batch-1 steps never take the single launch.  No device access; never fails
+ * for a valid handle (returns -1 for NULL). */
+int32_t ds_kv_cache_single_launch_ctx(const ds_kv* kv);
+
 /* Copies the fp32 logits [B][V] of the last prefill / decode step into d_out
  * (device, B*V floats).  Rows of sequences that the last call did not touch
  * hold what they held before. */
