@@ -460,6 +460,10 @@ ds_status ds_kv_cache_check(ds_kv* kv, void* stream) {
     if (e == hipSuccess) e = hipMemcpy(&err, kv->s.err, sizeof err, hipMemcpyDeviceToHost);
     if (e == hipSuccess && err) e = hipMemset(kv->s.err, 0, sizeof(int32_t));
     if (e != hipSuccess) return hip_fail(e, "check");
+    if (err & ~1)
+        return fail(DS_ERR_DEVICE, "device-side check failed (flags 0x%x: 2 = launch-shape guard, "
+                    "4 = a wait of the single-launch step gave up)%s", err & ~1,
+                    (err & 1) ? "; a token id was also out of range" : "");
     if (err) return fail(DS_ERR_BAD_TOKEN, "a decode step read a token id outside [0, %d)", kv->s.V);
     return ok();
 }

@@ -46,7 +46,8 @@ typedef enum {
     DS_ERR_BAD_TOKEN = -5,    /* token id outside [0, vocab)                   */
     DS_ERR_WORKSPACE = -6,    /* a buffer is smaller than the size query says  */
     DS_ERR_HIP = -7,          /* a HIP runtime call failed                     */
-    DS_ERR_STATE = -8         /* call not valid in the handle's current state  */
+    DS_ERR_STATE = -8,        /* call not valid in the handle's current state  */
+    DS_ERR_DEVICE = -9        /* a device-side consistency check tripped       */
 } ds_status;
 
 typedef enum { DS_F32 = 0, DS_BF16 = 1 } ds_dtype;
@@ -126,8 +127,13 @@ ds_status ds_kv_cache_set_lengths(ds_kv* kv, const int32_t* h_lengths, void* str
 /* Copies the host-side mirror of the lengths (no device access). */
 ds_status ds_kv_cache_get_lengths(const ds_kv* kv, int32_t* h_lengths);
 /* Synchronises `stream` and reports device-detected errors since the last
- * check: DS_ERR_BAD_TOKEN if a decode step read a token id outside [0, V)
- * (that sequence used row 0 instead); the flag is then cleared. */
+ * check, then clears them:
+ *  - DS_ERR_DEVICE if a step's own consistency checks tripped: a wait of the
+ *    single-launch batch-1 step gave up (every wait in it is bounded, about a
+ *    second, so the launch always ends), or a launch-shape guard fired.  The
+ *    steps since the last check are then not valid.
+ *  - else DS_ERR_BAD_TOKEN if a decode step read a token id outside [0, V)
+ *    (that sequence used row 0 instead). */
 ds_status ds_kv_cache_check(ds_kv* kv, void* stream);
 
 /* ---- the decode path ----------------------------------------------------- */
