@@ -48,8 +48,7 @@ constexpr int kPThreads = 256;                // 4 waves
 constexpr int kPWaves = kPBlocks * kPThreads / 64;
 constexpr int kPLds = 12288;                  // floats of LDS per block
 constexpr int kPRed = kPLds - 16;             // block-reduction slots at the end of LDS
-constexpr int kPF = 12;                       // weight chunks per lane held in registers
-constexpr int kPNorm = 3;                     // normalised elements per thread (d <= 768)
+constexpr int kPNorm = 4;                     // normalised elements per thread (d <= 1024)
 constexpr long kPSpin = 1 << 20;              // poll rounds before a wait gives up
 constexpr int kPhases = 5;                    // epochs per layer
 constexpr int kPChunk = 32;                   // positions per attention task
@@ -137,22 +136,115 @@ __device__ void block_fetch(const Seg& a, const Seg& b, int32_t* err) {
     }
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One poll round of J 16-byte loads (two LL words each) with the cache
+// policy of an agent-scope atomic load (sc1), completed inside the same asm
+// block so that no result is read before it has arrived.  Every 8-byte word
+// is written by a single aligned 8-byte store, so a 16-byte load may see one
+// word old and the other new, but never half a word.
+template <int J>
+__device__ __forceinline__ void poll_wide(u32x4 (&w)[J], const uint64_t* const (&p)[J]) {
+    static_assert(J >= 1 && J <= 4, "poll_wide: 1..4 loads");
+    if constexpr (J == 1) {
+        asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=&v"(w[0]) : "v"(p[0]) : "memory");
+    } else if constexpr (J == 2) {
+        asm volatile(
+            "global_load_dwordx4 %0, %2, off sc1\n\t"
+            "global_load_dwordx4 %1, %3, off sc1\n\t"
+            "s_waitcnt vmcnt(0)"
+            : "=&v"(w[0]), "=&v"(w[1]) : "v"(p[0]), "v"(p[1]) : "memory");
+    } else if constexpr (J == 3) {
+        asm volatile(
+            "global_load_dwordx4 %0, %3, off sc1\n\t"
+            "global_load_dwordx4 %1, %4, off sc1\n\t"
+            "global_load_dwordx4 %2, %5, off sc1\n\t"
+            "s_waitcnt vmcnt(0)"
+            : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]) : "v"(p[0]), "v"(p[1]), "v"(p[2]) : "memory");
+    } else {
+        asm volatile(
+            "global_load_dwordx4 %0, %4, off sc1\n\t"
+            "global_load_dwordx4 %1, %5, off sc1\n\t"
+            "global_load_dwordx4 %2, %6, off sc1\n\t"
+            "global_load_dwordx4 %3, %7, off sc1\n\t"
+            "s_waitcnt vmcnt(0)"
+            : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
+            : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+            : "memory");
+    }
+}
+
+// block_fetch with two words per load: thread t polls the word pairs
+// (2t, 2t+1), (2t+512, 2t+513), ... of the concatenation, J pairs per round.
+// Needs a.n and b.n even (a pair never straddles the segments) and 16-byte
+// aligned segment starts; otherwise it falls back to block_fetch.
+template <int J>
+__device__ void block_fetch2(const Seg& a, const Seg& b, int32_t* err) {
+    const bool ok_shape = ((a.n | b.n) & 1) == 0 &&
+                          ((reinterpret_cast<uintptr_t>(a.src) | reinterpret_cast<uintptr_t>(b.src)) & 15) == 0;
+    if (!ok_shape) {
+        block_fetch<2 * J>(a, b, err);
+        return;
+    }
+    const int tid = threadIdx.x;
+    const int total = a.n + b.n;
+    for (int base = 0; base < total; base += 2 * kPThreads * J) {
+        u32x4 w[J];
+        const uint64_t* src[J];
+        uint32_t ep[J];
+#pragma unroll
+        for (int j = 0; j < J; j++) {
+            const int i = min(base + 2 * (tid + kPThreads * j), total - 2);
+            src[j] = i < a.n ? a.src + i : b.src + (i - a.n);
+            ep[j] = i < a.n ? a.ep : b.ep;
+        }
+        long spins = 0;
+        while (true) {
+            poll_wide<J>(w, src);
+            bool ok = true;
+#pragma unroll
+            for (int j = 0; j < J; j++) ok &= w[j].y == ep[j] && w[j].w == ep[j];
+            if (__all(ok)) break;
+            if (give_up(spins, err)) break;
+        }
+#pragma unroll
+        for (int j = 0; j < J; j++) {
+            const int i = base + 2 * (tid + kPThreads * j);
+            if (i < total) {
+                float* dst = i < a.n ? a.dst + i : b.dst + (i - a.n);
+                dst[0] = __uint_as_float(w[j].x);
+                dst[1] = __uint_as_float(w[j].z);
+            }
+        }
+    }
+}
+
+template <int J>
+__device__ __forceinline__ void block_fetch2(const Seg& a, int32_t* err) {
+    block_fetch2<J>(a, Seg{a.src, 0, a.ep, a.dst}, err);
+}
+
 template <int J>
 __device__ __forceinline__ void block_fetch(const Seg& a, int32_t* err) {
     block_fetch<J>(a, Seg{a.src, 0, a.ep, a.dst}, err);  // an empty second segment (never null)
 }
 
-// RMSNorm of xs[0..n) (n <= 768) for the whole block.  Thread t owns the
-// elements t, t + 256, t + 512 (those block_fetch of a single segment gave
-// it) and multiplies them by their gains in place; the function returns
-// 1 / sqrt(mean(x^2) + eps), by which the caller scales its dot products.
-// Ends with a barrier, after which xs holds g * x.
+// The vector elements thread t owns: 2t, 2t + 1, 2t + 512, 2t + 513 (the ones
+// block_fetch2 of a single segment gives it).
+__device__ __forceinline__ int own_elem(int j) {
+    return 2 * static_cast<int>(threadIdx.x) + (j & 1) + 2 * kPThreads * (j >> 1);
+}
+
+// RMSNorm of xs[0..n) (n <= 1024) for the whole block.  Each thread
+// multiplies the elements it owns by their gains in place; the function
+// returns 1 / sqrt(mean(x^2) + eps), by which the caller scales its dot
+// products.  Ends with a barrier, after which xs holds g * x.
 __device__ float block_norm(float* xs, int n, const float (&gr)[kPNorm], float eps, float* sm) {
     const int tid = threadIdx.x;
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < kPNorm; j++) {
-        const int i = tid + kPThreads * j;
+        const int i = own_elem(j);
         if (i < n) {
             const float v = xs[i];
             ss = fmaf(v, v, ss);
@@ -168,7 +260,7 @@ __device__ float block_norm(float* xs, int n, const float (&gr)[kPNorm], float e
 
 __device__ __forceinline__ void load_gains(float (&gr)[kPNorm], const float* __restrict__ g, int n) {
 #pragma unroll
-    for (int j = 0; j < kPNorm; j++) gr[j] = g[min(static_cast<int>(threadIdx.x) + kPThreads * j, n - 1)];
+    for (int j = 0; j < kPNorm; j++) gr[j] = g[min(own_elem(j), n - 1)];
 }
 
 // The lane's share of the input vector of a row product: the chunks sub,
@@ -284,107 +376,149 @@ __device__ __forceinline__ float emb_at(const StepArgs& s, int tok, int j) {
 
 template <int PD, int REP>
 struct KV {
-    static constexpr int LPR = PD / 4;       // lanes per cache row
-    static constexpr int RPI = 64 / LPR;     // rows per load instruction
-    static constexpr int NI = kPChunk / RPI; // load instructions per attention chunk
-    float4 k[NI], v[NI];
+    // keys: 4 lanes per row with PD / 4 dims (KF float4) each, 16 rows per slot
+    static constexpr int KF = PD / 16;
+    static constexpr int NK = kPChunk / 16;
+    // values: PD / 4 lanes per row with one float4 each, RPV rows per slot
+    static constexpr int LPR = PD / 4;
+    static constexpr int RPV = 64 / LPR;
+    static constexpr int NV = kPChunk / RPV;
+    float4 k[NK][KF];
+    float4 v[NV];
 
-    // the wave's cached rows of group g at positions t0 + ii * RPI + r, clamped
-    // to the last row an earlier step wrote (pos - 1, or 0)
+    // the wave's cached rows of group g from position t0 on, clamped to the
+    // last row an earlier step wrote (pos - 1, or 0)
     __device__ __forceinline__ void load(const StepArgs& s, int l, int g, int t0, int pos) {
-        const int lane = threadIdx.x & 63, r = lane / LPR, e4 = lane % LPR;
+        const int lane = threadIdx.x & 63, rk = lane >> 2, qk = lane & 3, rv = lane / LPR, ev = lane % LPR;
         const int tmax = pos > 0 ? pos - 1 : 0;
 #pragma unroll
-        for (int ii = 0; ii < NI; ii++) {
-            const int tt = min(t0 + ii * RPI + r, tmax);
-            k[ii] = *reinterpret_cast<const float4*>(s.cache + cache_row(s, l, 0, 0, g, tt) + e4 * 4);
-            v[ii] = *reinterpret_cast<const float4*>(s.cache + cache_row(s, l, 1, 0, g, tt) + e4 * 4);
+        for (int sl = 0; sl < NK; sl++) {
+            const float* src = s.cache + cache_row(s, l, 0, 0, g, min(t0 + sl * 16 + rk, tmax)) + qk * (PD / 4);
+#pragma unroll
+            for (int f = 0; f < KF; f++) k[sl][f] = reinterpret_cast<const float4*>(src)[f];
+        }
+#pragma unroll
+        for (int ii = 0; ii < NV; ii++) {
+            const int tt = min(t0 + ii * RPV + rv, tmax);
+            v[ii] = *reinterpret_cast<const float4*>(s.cache + cache_row(s, l, 1, 0, g, tt) + ev * 4);
         }
     }
 
     // Attention of the REP query heads of group g over the held positions.
     // Rows past pos are masked, the row at pos is the new key/value from qkv
-    // (LDS, group-major: REP queries, key, value), and slots wholly past pos
-    // are skipped.  The heads are scored together so that their reductions
-    // interleave.  For every head j the lanes of the first row group get
+    // (LDS, group-major: REP queries, key, value), and key slots wholly past
+    // pos are skipped.  Scores use the key layout (a 4-lane reduction per
+    // row); the softmax weights go through the wave's LDS scratch
+    // pw[REP][RPV][NV] to the value layout.  Every LDS input is read up
+    // front.  For every head j the lanes of the first value row get
     // emit(j, e4, max score, sum of weights, weighted sum of values for dims
     // 4 e4 .. 4 e4 + 3).
     template <typename Emit>
-    __device__ __forceinline__ void attend(const float* qkv, int g, int t0, int pos, Emit emit) {
-        const int lane = threadIdx.x & 63, r = lane / LPR, e4 = lane % LPR;
+    __device__ __forceinline__ void attend(const float* qkv, int g, int t0, int pos, float* pw, Emit emit) {
+        const int lane = threadIdx.x & 63, rk = lane >> 2, qk = lane & 3, rv = lane / LPR, ev = lane % LPR;
         constexpr int GS = (REP + 2) * PD;
         const float scale = 1.0f / sqrtf(static_cast<float>(PD));
-        const float4 kn = *reinterpret_cast<const float4*>(qkv + g * GS + REP * PD + e4 * 4);
-        const float4 vn = *reinterpret_cast<const float4*>(qkv + g * GS + (REP + 1) * PD + e4 * 4);
+        float4 q[REP][KF], kn[KF];
 #pragma unroll
-        for (int ii = 0; ii < NI; ii++) {
-            const int tt = t0 + ii * RPI + r;
-            if (tt == pos) {
-                k[ii] = kn;
-                v[ii] = vn;
-            } else if (tt > pos) {  // past the context: weight 0, and no stale value may enter
-                v[ii] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < REP; j++) {
+#pragma unroll
+            for (int f = 0; f < KF; f++)
+                q[j][f] = reinterpret_cast<const float4*>(qkv + g * GS + j * PD + qk * (PD / 4))[f];
+        }
+#pragma unroll
+        for (int f = 0; f < KF; f++) kn[f] = reinterpret_cast<const float4*>(qkv + g * GS + REP * PD + qk * (PD / 4))[f];
+        const float4 vn = *reinterpret_cast<const float4*>(qkv + g * GS + (REP + 1) * PD + ev * 4);
+#pragma unroll
+        for (int sl = 0; sl < NK; sl++) {
+            const bool cur = t0 + sl * 16 + rk == pos;
+#pragma unroll
+            for (int f = 0; f < KF; f++) {
+                k[sl][f].x = cur ? kn[f].x : k[sl][f].x;
+                k[sl][f].y = cur ? kn[f].y : k[sl][f].y;
+                k[sl][f].z = cur ? kn[f].z : k[sl][f].z;
+                k[sl][f].w = cur ? kn[f].w : k[sl][f].w;
             }
         }
-        float4 q[REP];
 #pragma unroll
-        for (int j = 0; j < REP; j++) q[j] = *reinterpret_cast<const float4*>(qkv + g * GS + j * PD + e4 * 4);
-        float sc[REP][NI];
+        for (int ii = 0; ii < NV; ii++) {
+            // the new row at pos; past the context weight 0, and no stale value may enter
+            const int tt = t0 + ii * RPV + rv;
+            const bool cur = tt == pos, past = tt > pos;
+            v[ii].x = cur ? vn.x : (past ? 0.f : v[ii].x);
+            v[ii].y = cur ? vn.y : (past ? 0.f : v[ii].y);
+            v[ii].z = cur ? vn.z : (past ? 0.f : v[ii].z);
+            v[ii].w = cur ? vn.w : (past ? 0.f : v[ii].w);
+        }
+        float sc[REP][NK];
 #pragma unroll
-        for (int ii = 0; ii < NI; ii++) {
-            const int tb = t0 + ii * RPI;  // first position of the slot (uniform)
+        for (int sl = 0; sl < NK; sl++) {
+            const int tb = t0 + sl * 16;  // first position of the slot (uniform)
             if (tb <= pos) {
 #pragma unroll
                 for (int j = 0; j < REP; j++) {
-                    float dd = k[ii].x * q[j].x;
-                    dd = fmaf(k[ii].y, q[j].y, dd);
-                    dd = fmaf(k[ii].z, q[j].z, dd);
-                    dd = fmaf(k[ii].w, q[j].w, dd);
-                    dd = group_sum<LPR>(dd);
-                    sc[j][ii] = tb + r <= pos ? dd * scale : -INFINITY;
+                    float dd = 0.f;
+#pragma unroll
+                    for (int f = 0; f < KF; f++) {
+                        dd = fmaf(k[sl][f].x, q[j][f].x, dd);
+                        dd = fmaf(k[sl][f].y, q[j][f].y, dd);
+                        dd = fmaf(k[sl][f].z, q[j][f].z, dd);
+                        dd = fmaf(k[sl][f].w, q[j][f].w, dd);
+                    }
+                    dd = group_sum<4>(dd);
+                    sc[j][sl] = tb + rk <= pos ? dd * scale : -INFINITY;
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < REP; j++) sc[j][ii] = -INFINITY;
+                for (int j = 0; j < REP; j++) sc[j][sl] = -INFINITY;
             }
         }
+        // softmax statistics over the 16 row groups (values uniform over each quad)
         float m[REP], ls[REP];
-        float4 acc[REP];
 #pragma unroll
         for (int j = 0; j < REP; j++) {
             m[j] = sc[j][0];
 #pragma unroll
-            for (int ii = 1; ii < NI; ii++) m[j] = fmaxf(m[j], sc[j][ii]);
-            m[j] = stride_reduce<LPR>(m[j], OpMax{});
+            for (int sl = 1; sl < NK; sl++) m[j] = fmaxf(m[j], sc[j][sl]);
+            m[j] = group_reduce<64, OpMax, 4>(m[j], OpMax{});
             ls[j] = 0.f;
-            acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
 #pragma unroll
-        for (int ii = 0; ii < NI; ii++) {
-            if (t0 + ii * RPI <= pos) {
-#pragma unroll
-                for (int j = 0; j < REP; j++) {
-                    const float pe = __expf(sc[j][ii] - m[j]);
-                    ls[j] += pe;
-                    acc[j].x = fmaf(pe, v[ii].x, acc[j].x);
-                    acc[j].y = fmaf(pe, v[ii].y, acc[j].y);
-                    acc[j].z = fmaf(pe, v[ii].z, acc[j].z);
-                    acc[j].w = fmaf(pe, v[ii].w, acc[j].w);
-                }
+            for (int sl = 0; sl < NK; sl++) {
+                const float pe = t0 + sl * 16 <= pos ? __expf(sc[j][sl] - m[j]) : 0.f;
+                ls[j] += pe;
+                // position sl * 16 + rk sits in value slot ii = p / RPV at row p % RPV
+                const int p = sl * 16 + rk;
+                if (qk == 0) pw[j * kPChunk + (p % RPV) * NV + p / RPV] = pe;
             }
+            ls[j] = group_reduce<64, OpSum, 4>(ls[j], OpSum{});
         }
-        // lanes of one row group hold the same sum; add up the row groups
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the weights are in LDS
+        __builtin_amdgcn_wave_barrier();
+        float4 acc[REP];
 #pragma unroll
         for (int j = 0; j < REP; j++) {
-            ls[j] = stride_reduce<LPR>(ls[j], OpSum{});
+            float pe[NV];
+#pragma unroll
+            for (int ii = 0; ii < NV; ii++) pe[ii] = pw[j * kPChunk + rv * NV + ii];
+            acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int ii = 0; ii < NV; ii++) {
+                acc[j].x = fmaf(pe[ii], v[ii].x, acc[j].x);
+                acc[j].y = fmaf(pe[ii], v[ii].y, acc[j].y);
+                acc[j].z = fmaf(pe[ii], v[ii].z, acc[j].z);
+                acc[j].w = fmaf(pe[ii], v[ii].w, acc[j].w);
+            }
+        }
+        // add up the value row groups
+#pragma unroll
+        for (int j = 0; j < REP; j++) {
             acc[j].x = stride_reduce<LPR>(acc[j].x, OpSum{});
             acc[j].y = stride_reduce<LPR>(acc[j].y, OpSum{});
             acc[j].z = stride_reduce<LPR>(acc[j].z, OpSum{});
             acc[j].w = stride_reduce<LPR>(acc[j].w, OpSum{});
         }
-        if (r == 0) {
+        if (rv == 0) {
 #pragma unroll
-            for (int j = 0; j < REP; j++) emit(j, e4, m[j], ls[j], acc[j]);
+            for (int j = 0; j < REP; j++) emit(j, ev, m[j], ls[j], acc[j]);
         }
     }
 };
@@ -433,12 +567,12 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
         if (l == 0) {
 #pragma unroll
             for (int j = 0; j < kPNorm; j++) {
-                const int e = threadIdx.x + kPThreads * j;
+                const int e = own_elem(j);
                 if (e < d) xs[e] = emb_at<C::WDT>(s, c.tok, e);
             }
         } else {
             wait_sample<1>(p.ll_h, s.F, c.ep(l - 1, 3), c.err);
-            block_fetch<kPNorm>(Seg{p.ll_x, d, c.ep(l - 1, 4), xs}, c.err);
+            block_fetch2<2>(Seg{p.ll_x, d, c.ep(l - 1, 4), xs}, c.err);
         }
         const float rn = block_norm(xs, d, gr, s.eps, sm);
         if (active) {
@@ -482,14 +616,15 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
     KV<PD, REP> kv;
     if (active) kv.load(s, 0, g, ck * kPChunk, c.pos);
     float* qkv = sm;
+    float* pw = sm + ((HD + 2 * KVD + 3) & ~3) + wv * REP * kPChunk;  // softmax weights of this wave
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         if (l > 0) wait_sample<1>(p.ll_x, s.d, c.ep(l - 1, 4), c.err);
-        block_fetch<4>(Seg{p.ll_qkv, HD + 2 * KVD, c.ep(l, 0), qkv}, c.err);
+        block_fetch2<2>(Seg{p.ll_qkv, HD + 2 * KVD, c.ep(l, 0), qkv}, c.err);
         __syncthreads();
         if (active) {
             const uint32_t e1 = c.ep(l, 1);
-            kv.attend(qkv, g, ck * kPChunk, c.pos, [&](int j, int e4, float m, float lsum, float4 acc) {
+            kv.attend(qkv, g, ck * kPChunk, c.pos, pw, [&](int j, int e4, float m, float lsum, float4 acc) {
                 uint64_t* dst = p.ll_part + static_cast<size_t>((g * c.nch + ck) * REP + j) * (PD + 2);
                 ll_put(dst + 2 + e4 * 4 + 0, acc.x, e1);
                 ll_put(dst + 2 + e4 * 4 + 1, acc.y, e1);
@@ -518,11 +653,12 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     const bool valid = row < d;
     const bool attn_wave = wv < s.Hkv;  // wave g handles key/value group g
     const int g = attn_wave ? wv : 0;
-    // LDS: [Q/K/V words | partials] [o: H*D] [residual rows: 4R]
+    // LDS: [Q/K/V words | partials] [o: H*D] [residual rows: 4R] [softmax weights: 4][REP][32]
     const int in_n = c.fused ? HD + 2 * KVD : c.nch * s.H * (PD + 2);
     float* in = sm;
     float* o = sm + ((in_n + 3) & ~3);
     float* xr = o + HD;
+    float* pw = xr + 64 + wv * REP * kPChunk;
     PStream<C::WDT, G, C::NCH> st;
     KV<PD, REP> kv;
     st.start(p.layers[0].wo, valid ? row : 0, HD, sub, valid);
@@ -537,16 +673,16 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
         }
         if (c.fused) {
             if (l > 0) wait_sample<1>(p.ll_x, d, c.ep(l - 1, 4), c.err);
-            block_fetch<4>(Seg{p.ll_qkv, in_n, c.ep(l, 0), in}, rows, c.err);
+            block_fetch2<2>(Seg{p.ll_qkv, in_n, c.ep(l, 0), in}, rows, c.err);
         } else {
             wait_sample<1>(p.ll_qkv, HD + 2 * KVD, c.ep(l, 0), c.err);
-            block_fetch<12>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
+            block_fetch2<4>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
         }
         __syncthreads();
         if (attn_wave) {
             if (c.fused) {
-                kv.attend(in, g, 0, c.pos, [&](int j, int e4, float, float lsum, float4 acc) {
-                    const float inv = 1.0f / lsum;
+                kv.attend(in, g, 0, c.pos, pw, [&](int j, int e4, float, float lsum, float4 acc) {
+                    const float inv = __builtin_amdgcn_rcpf(lsum);  // lsum >= 1 (the max term is exp(0))
                     float4 v;
                     v.x = acc.x * inv;
                     v.y = acc.y * inv;
@@ -607,7 +743,7 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
             wait_sample<1>(p.ll_qkv, (s.H + 2 * s.Hkv) * s.D, c.ep(l, 0), c.err);
         else
             wait_sample<1>(p.ll_part, c.nch * s.H * (s.D + 2), c.ep(l, 1), c.err);
-        block_fetch<kPNorm>(Seg{p.ll_x2, d, c.ep(l, 2), xs}, c.err);
+        block_fetch2<2>(Seg{p.ll_x2, d, c.ep(l, 2), xs}, c.err);
         const float rn = block_norm(xs, d, gr, s.eps, sm);
         XRegs<C::WDT, C::NCD> xr;
         xr.load(xs, sub, G, d / EPC);
@@ -640,7 +776,7 @@ __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         wait_sample<1>(p.ll_x2, d, c.ep(l, 2), c.err);
-        block_fetch<8>(Seg{p.ll_h, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + r0, nrows, c.ep(l, 2), xr}, c.err);
+        block_fetch2<4>(Seg{p.ll_h, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + r0, nrows, c.ep(l, 2), xr}, c.err);
         __syncthreads();
         XRegs<C::WDT, C::NCF> hx;
         hx.load(hs, sub, G, F / EPC);
@@ -715,7 +851,7 @@ __global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArg
         float* xs = sm;
         __syncthreads();
         wait_sample<32>(p.ll_h, s.F, c.ep(s.L - 1, 3), c.err);
-        block_fetch<kPNorm>(Seg{p.ll_x, s.d, c.ep(s.L - 1, 4), xs}, c.err);
+        block_fetch2<2>(Seg{p.ll_x, s.d, c.ep(s.L - 1, 4), xs}, c.err);
         const float rn = block_norm(xs, s.d, gr, s.eps, sm);
         XRegs<C::WDT, C::NCD> xr;
         xr.load(xs, sub, GD, s.d / EPC);
@@ -775,55 +911,54 @@ __global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArg
 
 // ---- host side ----------------------------------------------------------------------------------
 
-// Lanes per row for rows of K elements: the fewest (4 .. 16) that keep each
-// lane's share within kPF register chunks (0: none does), and the chunks per lane.
-static int pg(int K, int wdt) {
-    const int nch = K / (wdt == kBF16 ? 8 : 4);
-    for (int g = 4; g <= 16; g *= 2)
-        if ((nch + g - 1) / g <= kPF) return g;
-    return 0;
-}
-static int pnc(int K, int wdt, int g) { return g ? (K / (wdt == kBF16 ? 8 : 4) + g - 1) / g : 0; }
+static int epc(int wdt) { return wdt == kBF16 ? 8 : 4; }
+static int pnc(int K, int wdt, int g) { return (K / epc(wdt) + g - 1) / g; }
 
-// The instantiated shape classes: the 135M-class model with bf16 weights and
-// the small fp32 test model.  Other shapes take the per-operation path.
+// The instantiated shape classes, each with its lanes per row (G) and
+// chunks per lane (NC) for rows of d, H*D and F elements: the 135M-class
+// model with bf16 weights and the small fp32 test model.  Other shapes take
+// the per-operation path.
 struct PKernel {
     int wdt, D, rep, gd, ncd, gh, nch, gf, ncf;
     const void* fn;
 };
 using CfgM135 = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12>;
 using CfgTiny = PCfg<kF32, 16, 2, 4, 4, 4, 4, 4, 11>;
-static const PKernel kPKernels[] = {
-    {kBF16, 64, 3, 8, 9, 8, 9, 16, 12, reinterpret_cast<const void*>(k_persist<CfgM135>)},
-    {kF32, 16, 2, 4, 4, 4, 4, 4, 11, reinterpret_cast<const void*>(k_persist<CfgTiny>)},
-};
+template <class C>
+static constexpr PKernel pk() {
+    return {C::WDT, C::PD, C::REP, C::GD, C::NCD, C::GH, C::NCH, C::GF, C::NCF,
+            reinterpret_cast<const void*>(k_persist<C>)};
+}
+static const PKernel kPKernels[] = {pk<CfgM135>(), pk<CfgTiny>()};
 
-static const void* persist_fn(const StepArgs& s) {
-    const int HD = s.H * s.D;
-    const int gd = pg(s.d, s.wdt), gh = pg(HD, s.wdt), gf = pg(s.F, s.wdt);
-    if (!gd || !gh || !gf || s.Hkv <= 0 || s.H % s.Hkv) return nullptr;
+static const PKernel* persist_kernel(const StepArgs& s) {
+    if (s.Hkv <= 0 || s.H % s.Hkv) return nullptr;
     for (const PKernel& k : kPKernels) {
-        if (k.wdt != s.wdt || k.D != s.D || k.rep != s.H / s.Hkv || k.gd != gd || k.gh != gh || k.gf != gf) continue;
-        if (k.ncd < pnc(s.d, s.wdt, gd) || k.nch < pnc(HD, s.wdt, gh) || k.ncf < pnc(s.F, s.wdt, gf)) continue;
-        return k.fn;
+        if (k.wdt != s.wdt || k.D != s.D || k.rep != s.H / s.Hkv) continue;
+        // every lane's chunks must fit its registers, and every G-lane group must have work
+        if (pnc(s.d, s.wdt, k.gd) > k.ncd || pnc(s.H * s.D, s.wdt, k.gh) > k.nch || pnc(s.F, s.wdt, k.gf) > k.ncf)
+            continue;
+        return &k;
     }
     return nullptr;
 }
 
 int persist_max_ctx(const StepArgs& s) {
     const int HD = s.H * s.D, KVD = s.Hkv * s.D;
-    if (s.B != 1 || !persist_fn(s)) return 0;
-    if (s.d > kPThreads * kPNorm || s.d < 64 || s.Hkv > 4 || s.V > 0x1FFFF) return 0;
-    // LDS of role 2 (Q/K/V words, o, residual rows) and role 4 (h, residual rows)
-    if (2 * HD + 2 * KVD + 4 + 64 > kPRed || s.F + 4 + 64 > kPRed) return 0;
-    const int gd = pg(s.d, s.wdt), gh = pg(HD, s.wdt), gf = pg(s.F, s.wdt);
-    if (Roles(s.d, s.H, s.Hkv, s.D, s.F, gd, gh, gf, 1).total() > kPBlocks) return 0;
+    const PKernel* k = s.B == 1 ? persist_kernel(s) : nullptr;
+    if (!k) return 0;
+    // d even (word pairs), d <= 1024 (four owned elements per thread)
+    if (s.d > kPThreads * kPNorm || s.d < 64 || (s.d & 1) || s.Hkv > 4 || s.V > 0x1FFFF) return 0;
+    // LDS of role 2 (Q/K/V words, o, residual rows, softmax weights) and role 4 (h, residual rows)
+    const int pws = 4 * (s.H / s.Hkv) * kPChunk;
+    if (2 * HD + 2 * KVD + 4 + 64 + pws > kPRed || s.F + 4 + 64 > kPRed) return 0;
+    if (Roles(s.d, s.H, s.Hkv, s.D, s.F, k->gd, k->gh, k->gf, 1).total() > kPBlocks) return 0;
     // longer contexts add role 1 blocks and keep every partial in role 2's LDS
     int chunks = 1;
     while (chunks < kPMaxChunks) {
         const int nc = chunks + 1;
-        if (Roles(s.d, s.H, s.Hkv, s.D, s.F, gd, gh, gf, nc).total() > kPBlocks) break;
-        if (nc * s.H * (s.D + 2) + 4 + HD + 64 > kPRed) break;
+        if (Roles(s.d, s.H, s.Hkv, s.D, s.F, k->gd, k->gh, k->gf, nc).total() > kPBlocks) break;
+        if (nc * s.H * (s.D + 2) + 4 + HD + 64 + pws > kPRed) break;
         chunks = nc;
     }
     const int ctx = chunks * kPChunk;
@@ -833,14 +968,14 @@ int persist_max_ctx(const StepArgs& s) {
 size_t persist_lds() { return sizeof(float) * kPLds; }
 
 hipError_t persist_prepare(const StepArgs& s) {
-    return hipFuncSetAttribute(persist_fn(s), hipFuncAttributeMaxDynamicSharedMemorySize,
+    return hipFuncSetAttribute(persist_kernel(s)->fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                static_cast<int>(persist_lds()));
 }
 
 hipError_t enqueue_persist(const StepArgs& s, const PersistArgs& p, const int32_t* d_tok_in, int tok_value,
                            int32_t* d_tok_out, hipStream_t st) {
     void* args[] = {const_cast<StepArgs*>(&s), const_cast<PersistArgs*>(&p), &d_tok_in, &tok_value, &d_tok_out};
-    return hipLaunchKernel(persist_fn(s), dim3(kPBlocks), dim3(kPThreads), args, persist_lds(), st);
+    return hipLaunchKernel(persist_kernel(s)->fn, dim3(kPBlocks), dim3(kPThreads), args, persist_lds(), st);
 }
 
 }  // namespace ds
