@@ -95,13 +95,15 @@ __device__ __forceinline__ float xor_op(float v, Op op) {
 // All-reduce over aligned groups of N lanes (N a power of two <= 64); every
 // lane of a group ends with the same bits.  Levels 4 and 8 use the mirrors,
 // which are exchanges of whole quads / half rows once those are uniform.
-template <int N, typename Op>
+// FROM > 1 takes values that are already uniform over aligned groups of
+// FROM lanes and combines those groups.
+template <int N, typename Op, int FROM = 1>
 __device__ __forceinline__ float group_reduce(float v, Op op) {
-    if constexpr (N >= 2) v = xor_op<1>(v, op);
-    if constexpr (N >= 4) v = xor_op<2>(v, op);
-    if constexpr (N >= 8) v = op(v, dpp_mov<0x141>(v));   // row_half_mirror
-    if constexpr (N >= 16) v = op(v, dpp_mov<0x140>(v));  // row_mirror
-    if constexpr (N >= 32) v = xor_op<16>(v, op);
+    if constexpr (N >= 2 && FROM <= 1) v = xor_op<1>(v, op);
+    if constexpr (N >= 4 && FROM <= 2) v = xor_op<2>(v, op);
+    if constexpr (N >= 8 && FROM <= 4) v = op(v, dpp_mov<0x141>(v));   // row_half_mirror
+    if constexpr (N >= 16 && FROM <= 8) v = op(v, dpp_mov<0x140>(v));  // row_mirror
+    if constexpr (N >= 32 && FROM <= 16) v = xor_op<16>(v, op);
     if constexpr (N >= 64) v = xor_op<32>(v, op);
     return v;
 }
