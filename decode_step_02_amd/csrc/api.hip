@@ -385,6 +385,7 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     if (pe && std::strcmp(pe, "0") == 0) kv->persist_ctx = 0;
     if (kv->persist_ctx > 0) {
         hipError_t ee = ds::persist_prepare(s);
+        if (ee == hipSuccess && !ds::persist_fits_device(s)) kv->persist_ctx = 0;  // e.g. a partitioned GPU
         if (ee != hipSuccess) {
             delete kv;
             return hip_fail(ee, "persistent step attributes");

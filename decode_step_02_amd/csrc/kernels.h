@@ -132,6 +132,7 @@ size_t max_lds_bytes(const StepArgs& s);
 // Persistent batch-1 step (persist.hip): the longest context it takes (0: none).
 int persist_max_ctx(const StepArgs& s);
 size_t persist_lds();
+bool persist_fits_device(const StepArgs& s);  // all workgroups of the single launch can be resident
 hipError_t persist_prepare(const StepArgs& s);
 // One step of sequence 0 (B == 1): the token comes from d_tok_in[0], or from
 // tok_value when d_tok_in is NULL; d_tok_out may be NULL.

@@ -229,26 +229,61 @@ __device__ __forceinline__ void block_fetch(const Seg& a, int32_t* err) {
     block_fetch<J>(a, Seg{a.src, 0, a.ep, a.dst}, err);  // an empty second segment (never null)
 }
 
+// The input vector of a row product, in LDS.  For fp32 weights it is fp32.
+// For bf16 weights every element x is held as two bf16 terms, hi = RNE(x)
+// and lo = RNE(x - hi) (|x - hi - lo| <= 2^-18 |x|), packed in pairs: n/2
+// words of hi pairs followed by n/2 words of lo pairs.  The products then use
+// v_dot2_f32_bf16 on the weight pairs as stored, with no widening.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+    bf16x2 h, l;
+    h.x = static_cast<__bf16>(a);
+    h.y = static_cast<__bf16>(b);
+    l.x = static_cast<__bf16>(a - static_cast<float>(h.x));
+    l.y = static_cast<__bf16>(b - static_cast<float>(h.y));
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// Store the element pair (i, i + 1) of an n-element input vector.
+template <int WDT>
+__device__ __forceinline__ void put_pair(float* vin, int n, int i, float a, float b) {
+    if (WDT == kBF16) {
+        uint32_t hi, lo;
+        split_pair(a, b, hi, lo);
+        uint32_t* u = reinterpret_cast<uint32_t*>(vin);
+        u[i >> 1] = hi;
+        u[(n >> 1) + (i >> 1)] = lo;
+    } else {
+        vin[i] = a;
+        vin[i + 1] = b;
+    }
+}
+
 // The vector elements thread t owns: 2t, 2t + 1, 2t + 512, 2t + 513 (the ones
 // block_fetch2 of a single segment gives it).
 __device__ __forceinline__ int own_elem(int j) {
     return 2 * static_cast<int>(threadIdx.x) + (j & 1) + 2 * kPThreads * (j >> 1);
 }
 
-// RMSNorm of xs[0..n) (n <= 1024) for the whole block.  Each thread
-// multiplies the elements it owns by their gains in place; the function
-// returns 1 / sqrt(mean(x^2) + eps), by which the caller scales its dot
-// products.  Ends with a barrier, after which xs holds g * x.
-__device__ float block_norm(float* xs, int n, const float (&gr)[kPNorm], float eps, float* sm) {
+// RMSNorm of xs[0..n) (n <= 1024, even) for the whole block.  Each thread
+// takes the element pairs it owns, multiplies them by their gains and stores
+// them as the row-product input vin (fp32 or bf16 hi/lo pairs, see put_pair);
+// the function returns 1 / sqrt(mean(x^2) + eps), by which the caller scales
+// its dot products.  Ends with a barrier, after which vin is complete.
+template <int WDT>
+__device__ float block_norm(const float* xs, int n, const float (&gr)[kPNorm], float eps, float* sm, float* vin) {
     const int tid = threadIdx.x;
     float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < kPNorm; j++) {
-        const int i = own_elem(j);
+    for (int jj = 0; jj < kPNorm / 2; jj++) {
+        const int i = own_elem(2 * jj);  // the pair (i, i + 1)
         if (i < n) {
-            const float v = xs[i];
-            ss = fmaf(v, v, ss);
-            xs[i] = gr[j] * v;
+            const float a = xs[i], b = xs[i + 1];
+            ss = fmaf(a, a, ss);
+            ss = fmaf(b, b, ss);
+            put_pair<WDT>(vin, n, i, gr[2 * jj] * a, gr[2 * jj + 1] * b);
         }
     }
     ss = group_sum<64>(ss);
@@ -263,19 +298,33 @@ __device__ __forceinline__ void load_gains(float (&gr)[kPNorm], const float* __r
     for (int j = 0; j < kPNorm; j++) gr[j] = g[min(own_elem(j), n - 1)];
 }
 
-// The lane's share of the input vector of a row product: the chunks sub,
-// sub + G, ... (EPC floats each, clamped to the last chunk), read from LDS
-// into registers in one batch so that the products wait for LDS once.
+// The lane's share of a row product's input: the chunks sub, sub + G, ...
+// (EPC elements each, clamped to the last chunk), read from LDS into
+// registers in one batch so that the products wait for LDS once.
 template <int WDT, int NC>
-struct XRegs {
-    static constexpr int EPC = WDT == kBF16 ? 8 : 4;
-    float4 v[NC * EPC / 4];
-    __device__ __forceinline__ void load(const float* xs, int sub, int G, int nchunks) {
+struct XRegs;
+
+template <int NC>
+struct XRegs<kF32, NC> {
+    float4 v[NC];
+    __device__ __forceinline__ void load(const float* vin, int n, int sub, int G) {
+        const int nchunks = n / 4;
+#pragma unroll
+        for (int p = 0; p < NC; p++) v[p] = reinterpret_cast<const float4*>(vin)[min(sub + p * G, nchunks - 1)];
+    }
+};
+
+template <int NC>
+struct XRegs<kBF16, NC> {
+    uint4 h[NC], l[NC];  // hi and lo pairs of the chunk's 8 elements
+    __device__ __forceinline__ void load(const float* vin, int n, int sub, int G) {
+        const int nchunks = n / 8;
+        const uint4* u = reinterpret_cast<const uint4*>(vin);
 #pragma unroll
         for (int p = 0; p < NC; p++) {
-            const float4* src = reinterpret_cast<const float4*>(xs + min(sub + p * G, nchunks - 1) * EPC);
-#pragma unroll
-            for (int q = 0; q < EPC / 4; q++) v[p * (EPC / 4) + q] = src[q];
+            const int c = min(sub + p * G, nchunks - 1);
+            h[p] = u[c];
+            l[p] = u[(n >> 3) + c];
         }
     }
 };
@@ -302,32 +351,32 @@ struct PStream {
                                 : *reinterpret_cast<const uint4*>(static_cast<const float*>(W) + e);
         }
     }
-    __device__ __forceinline__ static float dot(const uint4 u, const float4* x) {
-        float acc;
-        if (WDT == kBF16) {
-            const float4 a = x[0], b = x[1];
-            acc = __uint_as_float(u.x << 16) * a.x;
-            acc = fmaf(__uint_as_float(u.x & 0xFFFF0000u), a.y, acc);
-            acc = fmaf(__uint_as_float(u.y << 16), a.z, acc);
-            acc = fmaf(__uint_as_float(u.y & 0xFFFF0000u), a.w, acc);
-            acc = fmaf(__uint_as_float(u.z << 16), b.x, acc);
-            acc = fmaf(__uint_as_float(u.z & 0xFFFF0000u), b.y, acc);
-            acc = fmaf(__uint_as_float(u.w << 16), b.z, acc);
-            acc = fmaf(__uint_as_float(u.w & 0xFFFF0000u), b.w, acc);
-        } else {
-            const float4 a = x[0];
-            acc = __uint_as_float(u.x) * a.x;
-            acc = fmaf(__uint_as_float(u.y), a.y, acc);
-            acc = fmaf(__uint_as_float(u.z), a.z, acc);
-            acc = fmaf(__uint_as_float(u.w), a.w, acc);
-        }
-        return acc;
+    __device__ __forceinline__ static float dot2(uint32_t w2, uint32_t x2, float acc) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), __builtin_bit_cast(bf16x2, x2), acc,
+                                                false);
     }
     __device__ __forceinline__ float finish(const XRegs<WDT, NC>& x) const {
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int p = 0; p < NC; p++) {
-            const float d = dot(w[p], x.v + p * (EPC / 4));
+            float d;
+            if constexpr (WDT == kBF16) {
+                // hi and lo terms in two chains
+                float dh = dot2(w[p].x, x.h[p].x, 0.f), dl = dot2(w[p].x, x.l[p].x, 0.f);
+                dh = dot2(w[p].y, x.h[p].y, dh);
+                dl = dot2(w[p].y, x.l[p].y, dl);
+                dh = dot2(w[p].z, x.h[p].z, dh);
+                dl = dot2(w[p].z, x.l[p].z, dl);
+                dh = dot2(w[p].w, x.h[p].w, dh);
+                dl = dot2(w[p].w, x.l[p].w, dl);
+                d = dh + dl;
+            } else {
+                const float4 a = x.v[p];
+                d = __uint_as_float(w[p].x) * a.x;
+                d = fmaf(__uint_as_float(w[p].y), a.y, d);
+                d = fmaf(__uint_as_float(w[p].z), a.z, d);
+                d = fmaf(__uint_as_float(w[p].w), a.w, d);
+            }
             if (p & 1)
                 a1 += sub + p * G < nch ? d : 0.f;
             else
@@ -562,6 +611,7 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     st.start(wmat(0), row, d, sub, active);
     load_gains(gr, p.layers[0].attn_norm, d);
     float* xs = sm;
+    float* vin = C::WDT == kBF16 ? sm + ((d + 3) & ~3) : xs;  // product input (see put_pair)
     for (int l = 0; l < s.L; l++) {
         __syncthreads();  // nobody reads the previous layer's LDS any more
         if (l == 0) {
@@ -574,10 +624,10 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
             wait_sample<1>(p.ll_h, s.F, c.ep(l - 1, 3), c.err);
             block_fetch2<2>(Seg{p.ll_x, d, c.ep(l - 1, 4), xs}, c.err);
         }
-        const float rn = block_norm(xs, d, gr, s.eps, sm);
+        const float rn = block_norm<C::WDT>(xs, d, gr, s.eps, sm, vin);
         if (active) {
             XRegs<C::WDT, C::NCD> xr;
-            xr.load(xs, sub, G, d / EPC);
+            xr.load(vin, d, sub, G);
             const float y = rn * st.finish(xr);
             const int g = row / PD, e = row % PD;
             if (roped) {
@@ -683,12 +733,9 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
             if (c.fused) {
                 kv.attend(in, g, 0, c.pos, pw, [&](int j, int e4, float, float lsum, float4 acc) {
                     const float inv = __builtin_amdgcn_rcpf(lsum);  // lsum >= 1 (the max term is exp(0))
-                    float4 v;
-                    v.x = acc.x * inv;
-                    v.y = acc.y * inv;
-                    v.z = acc.z * inv;
-                    v.w = acc.w * inv;
-                    *reinterpret_cast<float4*>(o + (g * REP + j) * PD + e4 * 4) = v;
+                    const int i = (g * REP + j) * PD + e4 * 4;
+                    put_pair<C::WDT>(o, HD, i, acc.x * inv, acc.y * inv);
+                    put_pair<C::WDT>(o, HD, i + 2, acc.z * inv, acc.w * inv);
                 });
             } else {
                 // merge the chunk partials of the group's heads (layout [group][chunk][head][m, l, D])
@@ -700,18 +747,21 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
                     float Lw = 0.f;
                     for (int cc = 0; cc < c.nch; cc++) Lw += __expf(ph[cc * cstride] - M) * ph[cc * cstride + 1];
                     const float inv = 1.0f / Lw;
-                    for (int e = lane; e < PD; e += 64) {
-                        float acc = 0.f;
-                        for (int cc = 0; cc < c.nch; cc++)
-                            acc = fmaf(__expf(ph[cc * cstride] - M), ph[cc * cstride + 2 + e], acc);
-                        o[(g * REP + j) * PD + e] = acc * inv;
+                    for (int e = 2 * lane; e < PD; e += 128) {
+                        float a0 = 0.f, a1 = 0.f;
+                        for (int cc = 0; cc < c.nch; cc++) {
+                            const float wc = __expf(ph[cc * cstride] - M);
+                            a0 = fmaf(wc, ph[cc * cstride + 2 + e], a0);
+                            a1 = fmaf(wc, ph[cc * cstride + 3 + e], a1);
+                        }
+                        put_pair<C::WDT>(o, HD, (g * REP + j) * PD + e, a0 * inv, a1 * inv);
                     }
                 }
             }
         }
         __syncthreads();
         XRegs<C::WDT, C::NCH> ox;
-        ox.load(o, sub, G, HD / EPC);
+        ox.load(o, HD, sub, G);
         const float y = st.finish(ox);
         if (valid && sub == 0) ll_put(p.ll_x2 + row, xr[row - r0] + y, c.ep(l, 2));
         if (l + 1 < s.L) {
@@ -737,6 +787,7 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     s3.start(p.layers[0].w3, valid ? row : 0, d, sub, valid);
     load_gains(gr, p.layers[0].ffn_norm, d);
     float* xs = sm;
+    float* vin = C::WDT == kBF16 ? sm + ((d + 3) & ~3) : xs;  // product input (see put_pair)
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         if (c.fused)
@@ -744,9 +795,9 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
         else
             wait_sample<1>(p.ll_part, c.nch * s.H * (s.D + 2), c.ep(l, 1), c.err);
         block_fetch2<2>(Seg{p.ll_x2, d, c.ep(l, 2), xs}, c.err);
-        const float rn = block_norm(xs, d, gr, s.eps, sm);
+        const float rn = block_norm<C::WDT>(xs, d, gr, s.eps, sm, vin);
         XRegs<C::WDT, C::NCD> xr;
-        xr.load(xs, sub, G, d / EPC);
+        xr.load(vin, d, sub, G);
         const float a = rn * s1.finish(xr);
         const float u = rn * s3.finish(xr);
         if (valid && sub == 0) ll_put(p.ll_h + row, (a / (1.0f + expf(-a))) * u, c.ep(l, 3));
@@ -771,15 +822,24 @@ __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     const bool valid = row < d;
     float* hs = sm;
     float* xr = sm + ((F + 3) & ~3);
+    float* hv = C::WDT == kBF16 ? xr + 64 : hs;  // product input (see put_pair)
     PStream<C::WDT, G, C::NCF> st;
     st.start(p.layers[0].w2, valid ? row : 0, F, sub, valid);
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         wait_sample<1>(p.ll_x2, d, c.ep(l, 2), c.err);
         block_fetch2<4>(Seg{p.ll_h, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + r0, nrows, c.ep(l, 2), xr}, c.err);
+        if (C::WDT == kBF16) {
+            // the pairs block_fetch2 gave this thread: (2t + 512 j, 2t + 512 j + 1)
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                const int i = 2 * (static_cast<int>(threadIdx.x) + kPThreads * jj);
+                if (i < F) put_pair<C::WDT>(hv, F, i, hs[i], hs[i + 1]);
+            }
+        }
         __syncthreads();
         XRegs<C::WDT, C::NCF> hx;
-        hx.load(hs, sub, G, F / EPC);
+        hx.load(hv, F, sub, G);
         const float y = st.finish(hx);
         if (valid && sub == 0) ll_put(p.ll_x + row, xr[row - r0] + y, c.ep(l, 4));
         if (l + 1 < s.L) st.start(p.layers[l + 1].w2, valid ? row : 0, F, sub, valid);
@@ -802,7 +862,7 @@ struct Roles {
 };
 
 template <class C>
-__global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArgs p, const int32_t* __restrict__ d_tok_in,
+__global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArgs p, const int32_t* __restrict__ d_tok_in,
                                                            int tok_value, int32_t* __restrict__ d_tok_out) {
     constexpr int GD = C::GD;
     constexpr int EPC = C::WDT == kBF16 ? 8 : 4;
@@ -849,12 +909,13 @@ __global__ __launch_bounds__(kPThreads, 2) void k_persist(StepArgs s, PersistArg
         sb.start(p.wcls, min(tb * R + rs, s.V - 1), s.d, sub, tb * R + rs < s.V);
         load_gains(gr, p.out_norm, s.d);
         float* xs = sm;
+        float* vin = C::WDT == kBF16 ? sm + ((s.d + 3) & ~3) : xs;  // product input (see put_pair)
         __syncthreads();
         wait_sample<32>(p.ll_h, s.F, c.ep(s.L - 1, 3), c.err);
         block_fetch2<2>(Seg{p.ll_x, s.d, c.ep(s.L - 1, 4), xs}, c.err);
-        const float rn = block_norm(xs, s.d, gr, s.eps, sm);
+        const float rn = block_norm<C::WDT>(xs, s.d, gr, s.eps, sm, vin);
         XRegs<C::WDT, C::NCD> xr;
-        xr.load(xs, sub, GD, s.d / EPC);
+        xr.load(vin, s.d, sub, GD);
         uint64_t key = 0ull;
         while (ta < ntask) {
             const int row = ta * R + rs;
@@ -951,7 +1012,7 @@ int persist_max_ctx(const StepArgs& s) {
     if (s.d > kPThreads * kPNorm || s.d < 64 || (s.d & 1) || s.Hkv > 4 || s.V > 0x1FFFF) return 0;
     // LDS of role 2 (Q/K/V words, o, residual rows, softmax weights) and role 4 (h, residual rows)
     const int pws = 4 * (s.H / s.Hkv) * kPChunk;
-    if (2 * HD + 2 * KVD + 4 + 64 + pws > kPRed || s.F + 4 + 64 > kPRed) return 0;
+    if (2 * HD + 2 * KVD + 4 + 64 + pws > kPRed || 2 * s.F + 4 + 64 > kPRed || (s.F & 1)) return 0;
     if (Roles(s.d, s.H, s.Hkv, s.D, s.F, k->gd, k->gh, k->gf, 1).total() > kPBlocks) return 0;
     // longer contexts add role 1 blocks and keep every partial in role 2's LDS
     int chunks = 1;
@@ -966,6 +1027,20 @@ int persist_max_ctx(const StepArgs& s) {
 }
 
 size_t persist_lds() { return sizeof(float) * kPLds; }
+
+// Every workgroup of the single launch must be resident at once (they wait
+// on each other's outputs).  True when the current device can hold all
+// kPBlocks of them (one per CU at this kernel's register use).
+bool persist_fits_device(const StepArgs& s) {
+    const PKernel* k = persist_kernel(s);
+    if (!k) return false;
+    int dev = 0, ncu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k->fn, kPThreads, persist_lds()) != hipSuccess)
+        return false;
+    return static_cast<long>(per_cu) * ncu >= kPBlocks;
+}
 
 hipError_t persist_prepare(const StepArgs& s) {
     return hipFuncSetAttribute(persist_kernel(s)->fn, hipFuncAttributeMaxDynamicSharedMemorySize,

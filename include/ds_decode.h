@@ -172,8 +172,13 @@ ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, in
  * the whole step -- every layer, the vocabulary product and the argmax --
  * with the phases of a layer handing their outputs to each other through
  * device memory instead of kernel boundaries.  Otherwise (B > 1, longer
- * contexts, shapes without a single-launch variant, or DS_PERSIST=0 in the
- * environment when the cache was created) every operation is its own launch.
+ * contexts, shapes without a single-launch variant, a device that cannot hold
+ * all 256 workgroups of the launch at once -- such as a partitioned GPU --, or
+ * DS_PERSIST=0 in the environment when the cache was created) every operation
+ * is its own launch.  The single launch occupies every CU while it runs; work
+ * that other streams run at the same time can delay it, and if its workgroups
+ * cannot all start, its bounded waits give up and the next ds_kv_cache_check
+ * returns DS_ERR_DEVICE.
  * Both give the same results within floating-point rounding.  Returns 0 when
  * batch-1 steps never take the single launch.  No device access; never fails
  * for a valid handle (returns -1 for NULL). */

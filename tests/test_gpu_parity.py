@@ -240,3 +240,24 @@ def test_batch1_single_launch_matches_per_operation_launches(monkeypatch):
         assert_logits_close(a["lgs"][k], b["lgs"][k], f"step {k}")
     n = len(prompts[0]) + len(feed)
     assert_logits_close(a["cache"][:, :, 0, :, :n], b["cache"][:, :, 0, :, :n], "cache")
+
+
+def test_single_launch_step_is_taken_at_batch_1():
+    """Batch-1 caches of the instantiated shape classes run their steps as one
+    launch (so the parity cases above exercise it); larger batches do not."""
+    _torch()
+    import decode_step_02_amd as dsa
+    w = synth.WORKLOADS["llama135m_p5"]
+    model = dsa.Model(w.model, synth.make_arena(w.model, w.model_seed))
+    kv = dsa.KVCache(model, 1, w.ctx)
+    assert kv.single_launch_ctx() == 512
+    kv.close()
+    kv = dsa.KVCache(model, 2, 64)
+    assert kv.single_launch_ctx() == 0
+    kv.close()
+    model.close()
+    tiny = dsa.Model(synth.TINY, synth.make_arena(synth.TINY, 1))
+    kv = dsa.KVCache(tiny, 1, 128)
+    assert kv.single_launch_ctx() == 128
+    kv.close()
+    tiny.close()
