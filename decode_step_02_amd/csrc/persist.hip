@@ -428,17 +428,20 @@ struct KV {
     // keys: 4 lanes per row with PD / 4 dims (KF float4) each, 16 rows per slot
     static constexpr int KF = PD / 16;
     static constexpr int NK = kPChunk / 16;
-    // values: PD / 4 lanes per row with one float4 each, RPV rows per slot
-    static constexpr int LPR = PD / 4;
-    static constexpr int RPV = 64 / LPR;
-    static constexpr int NV = kPChunk / RPV;
+    // values: one dim per lane (lane = rv * PD + e), RV rows per slot, NV slots
+    static constexpr int RV = 64 / PD;
+    static constexpr int NV = kPChunk / RV;
+    // softmax weights per head in the wave's LDS scratch: position p of the
+    // chunk at (p % RV) * NV + p / RV (so a lane's NV weights are contiguous),
+    // the new row's weight at kPChunk, padding
+    static constexpr int PWS = kPChunk + 4;
     float4 k[NK][KF];
-    float4 v[NV];
+    float v[NV];
 
     // the wave's cached rows of group g from position t0 on, clamped to the
     // last row an earlier step wrote (pos - 1, or 0)
     __device__ __forceinline__ void load(const StepArgs& s, int l, int g, int t0, int pos) {
-        const int lane = threadIdx.x & 63, rk = lane >> 2, qk = lane & 3, rv = lane / LPR, ev = lane % LPR;
+        const int lane = threadIdx.x & 63, rk = lane >> 2, qk = lane & 3, rv = lane / PD, ev = lane % PD;
         const int tmax = pos > 0 ? pos - 1 : 0;
 #pragma unroll
         for (int sl = 0; sl < NK; sl++) {
@@ -446,57 +449,54 @@ struct KV {
 #pragma unroll
             for (int f = 0; f < KF; f++) k[sl][f] = reinterpret_cast<const float4*>(src)[f];
         }
+        const float* vb = s.cache + cache_row(s, l, 1, 0, g, 0) + ev;
 #pragma unroll
-        for (int ii = 0; ii < NV; ii++) {
-            const int tt = min(t0 + ii * RPV + rv, tmax);
-            v[ii] = *reinterpret_cast<const float4*>(s.cache + cache_row(s, l, 1, 0, g, tt) + ev * 4);
-        }
+        for (int ii = 0; ii < NV; ii++) v[ii] = vb[static_cast<size_t>(min(t0 + ii * RV + rv, tmax)) * PD];
     }
 
-    // Attention of the REP query heads of group g over the held positions.
-    // Rows past pos are masked, the row at pos is the new key/value from qkv
-    // (LDS, group-major: REP queries, key, value), and key slots wholly past
-    // pos are skipped.  Scores use the key layout (a 4-lane reduction per
-    // row); the softmax weights go through the wave's LDS scratch
-    // pw[REP][RPV][NV] to the value layout.  Every LDS input is read up
-    // front.  For every head j the lanes of the first value row get
-    // emit(j, e4, max score, sum of weights, weighted sum of values for dims
-    // 4 e4 .. 4 e4 + 3).
+    // Attention of the REP query heads of group g over positions t0 ..
+    // min(pos, t0 + 31).
+    //  - Scores use the key layout (a 4-lane reduction per row).  The new key
+    //    from qkv (LDS, group-major: REP queries, key, value) is patched into
+    //    the one slot that holds pos; slots wholly past pos are skipped.
+    //  - The softmax weights go through the wave's LDS scratch pw[REP][PWS],
+    //    the new row's weight in its own entry, so the value rows in
+    //    registers are never patched: rows past pos are clamped copies of
+    //    written rows and get weight 0.  At pos == 0 nothing has been written
+    //    yet and the output is the new value.
+    //  - Every lane accumulates one dim; with PD < 64 the RV row groups are
+    //    added up at the end.
+    // For every head j the lanes of the first value row get emit(j, e, max
+    // score, sum of weights, weighted sum of values for dim e, the same for
+    // dim e ^ 1).
     template <typename Emit>
     __device__ __forceinline__ void attend(const float* qkv, int g, int t0, int pos, float* pw, Emit emit) {
-        const int lane = threadIdx.x & 63, rk = lane >> 2, qk = lane & 3, rv = lane / LPR, ev = lane % LPR;
+        const int lane = threadIdx.x & 63, rk = lane >> 2, qk = lane & 3, rv = lane / PD, ev = lane % PD;
         constexpr int GS = (REP + 2) * PD;
         const float scale = 1.0f / sqrtf(static_cast<float>(PD));
-        float4 q[REP][KF], kn[KF];
+        float4 q[REP][KF];
 #pragma unroll
         for (int j = 0; j < REP; j++) {
 #pragma unroll
             for (int f = 0; f < KF; f++)
                 q[j][f] = reinterpret_cast<const float4*>(qkv + g * GS + j * PD + qk * (PD / 4))[f];
         }
-#pragma unroll
-        for (int f = 0; f < KF; f++) kn[f] = reinterpret_cast<const float4*>(qkv + g * GS + REP * PD + qk * (PD / 4))[f];
-        const float4 vn = *reinterpret_cast<const float4*>(qkv + g * GS + (REP + 1) * PD + ev * 4);
+        const float vn = qkv[g * GS + (REP + 1) * PD + ev];
+        const int cur = pos - t0;  // chunk position of the new row (>= kPChunk: not in this chunk)
 #pragma unroll
         for (int sl = 0; sl < NK; sl++) {
-            const bool cur = t0 + sl * 16 + rk == pos;
+            if (cur >= sl * 16 && cur < sl * 16 + 16) {  // uniform: the slot holding the new row
+                const float4* kn = reinterpret_cast<const float4*>(qkv + g * GS + REP * PD + qk * (PD / 4));
+                const bool here = rk == cur - sl * 16;
 #pragma unroll
-            for (int f = 0; f < KF; f++) {
-                k[sl][f].x = cur ? kn[f].x : k[sl][f].x;
-                k[sl][f].y = cur ? kn[f].y : k[sl][f].y;
-                k[sl][f].z = cur ? kn[f].z : k[sl][f].z;
-                k[sl][f].w = cur ? kn[f].w : k[sl][f].w;
+                for (int f = 0; f < KF; f++) {
+                    const float4 x = kn[f];
+                    k[sl][f].x = here ? x.x : k[sl][f].x;
+                    k[sl][f].y = here ? x.y : k[sl][f].y;
+                    k[sl][f].z = here ? x.z : k[sl][f].z;
+                    k[sl][f].w = here ? x.w : k[sl][f].w;
+                }
             }
-        }
-#pragma unroll
-        for (int ii = 0; ii < NV; ii++) {
-            // the new row at pos; past the context weight 0, and no stale value may enter
-            const int tt = t0 + ii * RPV + rv;
-            const bool cur = tt == pos, past = tt > pos;
-            v[ii].x = cur ? vn.x : (past ? 0.f : v[ii].x);
-            v[ii].y = cur ? vn.y : (past ? 0.f : v[ii].y);
-            v[ii].z = cur ? vn.z : (past ? 0.f : v[ii].z);
-            v[ii].w = cur ? vn.w : (past ? 0.f : v[ii].w);
         }
         float sc[REP][NK];
 #pragma unroll
@@ -534,40 +534,49 @@ struct KV {
             for (int sl = 0; sl < NK; sl++) {
                 const float pe = t0 + sl * 16 <= pos ? __expf(sc[j][sl] - m[j]) : 0.f;
                 ls[j] += pe;
-                // position sl * 16 + rk sits in value slot ii = p / RPV at row p % RPV
                 const int p = sl * 16 + rk;
-                if (qk == 0) pw[j * kPChunk + (p % RPV) * NV + p / RPV] = pe;
+                if (qk == 0) {
+                    pw[j * PWS + (p % RV) * NV + p / RV] = p == cur ? 0.f : pe;
+                    if (p == cur) pw[j * PWS + kPChunk] = pe;
+                }
             }
             ls[j] = group_reduce<64, OpSum, 4>(ls[j], OpSum{});
         }
+        if (cur >= kPChunk && lane == 0) {
+#pragma unroll
+            for (int j = 0; j < REP; j++) pw[j * PWS + kPChunk] = 0.f;
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the weights are in LDS
         __builtin_amdgcn_wave_barrier();
-        float4 acc[REP];
+        float acc[REP];
+        if (pos == 0) {
 #pragma unroll
-        for (int j = 0; j < REP; j++) {
-            float pe[NV];
+            for (int j = 0; j < REP; j++) acc[j] = vn;  // one position: weight 1 on the new row
+        } else {
 #pragma unroll
-            for (int ii = 0; ii < NV; ii++) pe[ii] = pw[j * kPChunk + rv * NV + ii];
-            acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int j = 0; j < REP; j++) {
+                const float4* pj = reinterpret_cast<const float4*>(pw + j * PWS + rv * NV);
+                float4 pe[NV / 4];
 #pragma unroll
-            for (int ii = 0; ii < NV; ii++) {
-                acc[j].x = fmaf(pe[ii], v[ii].x, acc[j].x);
-                acc[j].y = fmaf(pe[ii], v[ii].y, acc[j].y);
-                acc[j].z = fmaf(pe[ii], v[ii].z, acc[j].z);
-                acc[j].w = fmaf(pe[ii], v[ii].w, acc[j].w);
+                for (int c4 = 0; c4 < NV / 4; c4++) pe[c4] = pj[c4];  // one batch of broadcast reads
+                // the new row once (row group 0), before the row groups are added up
+                float a0 = rv == 0 ? pw[j * PWS + kPChunk] * vn : 0.f, a1 = 0.f;
+#pragma unroll
+                for (int c4 = 0; c4 < NV / 4; c4++) {  // weights past the context are 0
+                    a0 = fmaf(pe[c4].x, v[4 * c4 + 0], a0);
+                    a1 = fmaf(pe[c4].y, v[4 * c4 + 1], a1);
+                    a0 = fmaf(pe[c4].z, v[4 * c4 + 2], a0);
+                    a1 = fmaf(pe[c4].w, v[4 * c4 + 3], a1);
+                }
+                acc[j] = stride_reduce<PD>(a0 + a1, OpSum{});  // the RV row groups (none when PD == 64)
             }
         }
-        // add up the value row groups
+        float nb[REP];
 #pragma unroll
-        for (int j = 0; j < REP; j++) {
-            acc[j].x = stride_reduce<LPR>(acc[j].x, OpSum{});
-            acc[j].y = stride_reduce<LPR>(acc[j].y, OpSum{});
-            acc[j].z = stride_reduce<LPR>(acc[j].z, OpSum{});
-            acc[j].w = stride_reduce<LPR>(acc[j].w, OpSum{});
-        }
+        for (int j = 0; j < REP; j++) nb[j] = dpp_mov<0xB1>(acc[j]);  // dim e ^ 1
         if (rv == 0) {
 #pragma unroll
-            for (int j = 0; j < REP; j++) emit(j, ev, m[j], ls[j], acc[j]);
+            for (int j = 0; j < REP; j++) emit(j, ev, m[j], ls[j], acc[j], nb[j]);
         }
     }
 };
@@ -666,7 +675,7 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
     KV<PD, REP> kv;
     if (active) kv.load(s, 0, g, ck * kPChunk, c.pos);
     float* qkv = sm;
-    float* pw = sm + ((HD + 2 * KVD + 3) & ~3) + wv * REP * kPChunk;  // softmax weights of this wave
+    float* pw = sm + ((HD + 2 * KVD + 3) & ~3) + wv * REP * KV<PD, REP>::PWS;  // softmax weights of this wave
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         if (l > 0) wait_sample<1>(p.ll_x, s.d, c.ep(l - 1, 4), c.err);
@@ -674,13 +683,10 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
         __syncthreads();
         if (active) {
             const uint32_t e1 = c.ep(l, 1);
-            kv.attend(qkv, g, ck * kPChunk, c.pos, pw, [&](int j, int e4, float m, float lsum, float4 acc) {
+            kv.attend(qkv, g, ck * kPChunk, c.pos, pw, [&](int j, int e, float m, float lsum, float acc, float) {
                 uint64_t* dst = p.ll_part + static_cast<size_t>((g * c.nch + ck) * REP + j) * (PD + 2);
-                ll_put(dst + 2 + e4 * 4 + 0, acc.x, e1);
-                ll_put(dst + 2 + e4 * 4 + 1, acc.y, e1);
-                ll_put(dst + 2 + e4 * 4 + 2, acc.z, e1);
-                ll_put(dst + 2 + e4 * 4 + 3, acc.w, e1);
-                if (e4 == 0) {
+                ll_put(dst + 2 + e, acc, e1);
+                if (e == 0) {
                     ll_put(dst, m, e1);
                     ll_put(dst + 1, lsum, e1);
                 }
@@ -708,7 +714,7 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     float* in = sm;
     float* o = sm + ((in_n + 3) & ~3);
     float* xr = o + HD;
-    float* pw = xr + 64 + wv * REP * kPChunk;
+    float* pw = xr + 64 + wv * REP * KV<PD, REP>::PWS;
     PStream<C::WDT, G, C::NCH> st;
     KV<PD, REP> kv;
     st.start(p.layers[0].wo, valid ? row : 0, HD, sub, valid);
@@ -731,11 +737,9 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
         __syncthreads();
         if (attn_wave) {
             if (c.fused) {
-                kv.attend(in, g, 0, c.pos, pw, [&](int j, int e4, float, float lsum, float4 acc) {
+                kv.attend(in, g, 0, c.pos, pw, [&](int j, int e, float, float lsum, float acc, float acc1) {
                     const float inv = __builtin_amdgcn_rcpf(lsum);  // lsum >= 1 (the max term is exp(0))
-                    const int i = (g * REP + j) * PD + e4 * 4;
-                    put_pair<C::WDT>(o, HD, i, acc.x * inv, acc.y * inv);
-                    put_pair<C::WDT>(o, HD, i + 2, acc.z * inv, acc.w * inv);
+                    if ((e & 1) == 0) put_pair<C::WDT>(o, HD, (g * REP + j) * PD + e, acc * inv, acc1 * inv);
                 });
             } else {
                 // merge the chunk partials of the group's heads (layout [group][chunk][head][m, l, D])
@@ -1011,7 +1015,7 @@ int persist_max_ctx(const StepArgs& s) {
     // d even (word pairs), d <= 1024 (four owned elements per thread)
     if (s.d > kPThreads * kPNorm || s.d < 64 || (s.d & 1) || s.Hkv > 4 || s.V > 0x1FFFF) return 0;
     // LDS of role 2 (Q/K/V words, o, residual rows, softmax weights) and role 4 (h, residual rows)
-    const int pws = 4 * (s.H / s.Hkv) * kPChunk;
+    const int pws = 4 * (s.H / s.Hkv) * (kPChunk + 4);
     if (2 * HD + 2 * KVD + 4 + 64 + pws > kPRed || 2 * s.F + 4 + 64 > kPRed || (s.F & 1)) return 0;
     if (Roles(s.d, s.H, s.Hkv, s.D, s.F, k->gd, k->gh, k->gf, 1).total() > kPBlocks) return 0;
     // longer contexts add role 1 blocks and keep every partial in role 2's LDS
