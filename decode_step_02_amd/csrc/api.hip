@@ -111,7 +111,7 @@ size_t layout(const ds_config* c, std::vector<size_t>* off) {
 // Workspace carve-up for a (B, T) cache.
 struct WsLayout {
     size_t x, q, o, h, part_o, part_ml, logits, keys, slot, pos, flag, err, rope_cos, rope_sin;
-    size_t ll_x, ll_x2, ll_qkv, ll_part, ll_h, ll_keys, epoch, layers, ll_end, total;
+    size_t ll_x, ll_x2, ll_qkv, ll_part, ll_h, ll_keys, epoch, layers, ll_end, total, rstride;
 };
 
 WsLayout ws_layout(const ds_config* c, int B, int T) {
@@ -140,11 +140,16 @@ WsLayout ws_layout(const ds_config* c, int B, int T) {
     w.rope_sin = take(sizeof(float) * T * (c->head_dim / 2));
     // persistent batch-1 step: LL words (zeroed at creation), epoch, layer table
     const size_t kvd = static_cast<size_t>(c->n_kv_heads) * c->head_dim;
-    w.ll_x = take(8 * static_cast<size_t>(c->dim));
-    w.ll_x2 = take(8 * static_cast<size_t>(c->dim));
-    w.ll_qkv = take(8 * (HD + 2 * kvd));
+    // ll_x, ll_x2, ll_qkv and ll_h: kPRep replicas each, 4 KiB apart, so that
+    // the blocks that poll a vector spread over several memory channels
+    const size_t nmax = std::max({static_cast<size_t>(c->dim), HD + 2 * kvd, static_cast<size_t>(c->hidden_dim)});
+    w.rstride = round_up(nmax, 512);
+    const size_t rbytes = 8 * ds::kPRep * w.rstride;
+    w.ll_x = take(rbytes);
+    w.ll_x2 = take(rbytes);
+    w.ll_qkv = take(rbytes);
     w.ll_part = take(8 * static_cast<size_t>(c->n_heads) * ds::kPMaxChunks * (c->head_dim + 2));
-    w.ll_h = take(8 * static_cast<size_t>(c->hidden_dim));
+    w.ll_h = take(rbytes);
     w.ll_keys = take(8 * static_cast<size_t>(ds::kPKeyWords));
     w.epoch = take(sizeof(uint32_t));
     w.ll_end = p;
@@ -380,6 +385,7 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     pa.ll_h = reinterpret_cast<uint64_t*>(ws + lay.ll_h);
     pa.ll_keys = reinterpret_cast<uint64_t*>(ws + lay.ll_keys);
     pa.epoch = reinterpret_cast<uint32_t*>(ws + lay.epoch);
+    pa.rstride = static_cast<int>(lay.rstride);
     kv->persist_ctx = ds::persist_max_ctx(s);
     const char* pe = std::getenv("DS_PERSIST");  // "0" keeps batch-1 steps on one launch per operation
     if (pe && std::strcmp(pe, "0") == 0) kv->persist_ctx = 0;

@@ -19,6 +19,7 @@ constexpr int kSetChunk = 128;   // lengths per k_set_lengths launch
 constexpr int kMaxArgmaxBlocks = 16384;  // vocabulary blocks per item (argmax partials)
 constexpr int kPMaxChunks = 16;  // attention chunks the persistent step can hold per head
 constexpr int kPKeyWords = 1024; // argmax words of the persistent step (one per wave)
+constexpr int kPRep = 8;          // most replicas of a vector the persistent step publishes
 constexpr int kMmItems = 64;     // items per MFMA launch
 constexpr int kMmMin = 16;       // steps with at least this many items use the MFMA projections
 
@@ -74,6 +75,7 @@ struct PersistArgs {
     const LayerW* layers;   // device copy of the per-layer pointers [L]
     const float* out_norm;
     const void* wcls;
+    // ll_x, ll_x2, ll_qkv and ll_h hold kPRep replicas, rstride words apart
     uint64_t* ll_x;         // [d]      residual after W2 (value, epoch words)
     uint64_t* ll_x2;        // [d]      residual after Wo
     uint64_t* ll_qkv;       // [Hkv][(rep + 2) * D] per group: rotated queries, new key, new value
@@ -81,6 +83,7 @@ struct PersistArgs {
     uint64_t* ll_h;         // [F]      silu(a)*u
     uint64_t* ll_keys;      // [kPKeyWords] argmax words
     uint32_t* epoch;        // epoch base, advanced by every step
+    int rstride;            // words between two replicas of a vector
 };
 
 // Items of one k_begin launch; by_value = 0 takes tokens from d_tok_in with

@@ -401,6 +401,7 @@ struct PCtx {
     uint32_t base;   // epoch base of this step
     int pos, n, nch, tok;
     bool fused;      // attention recomputed inside the Wo blocks
+    int rep;         // word offset of the replica this block reads
     int32_t* err;
     __device__ __forceinline__ uint32_t ep(int l, int ph) const {
         return base + 1u + static_cast<uint32_t>(l * kPhases + ph);
@@ -410,10 +411,14 @@ struct PCtx {
 // Compile-time shape class of one instantiation: weight type, head dim,
 // query heads per key/value head, and lanes per row / chunks per lane for
 // rows of d (Q/K/V, W1/W3, vocabulary), H*D (Wo) and F (W2) elements.
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
 template <int WDT_, int PD_, int REP_, int GD_, int NCD_, int GH_, int NCH_, int GF_, int NCF_>
 struct PCfg {
     static constexpr int WDT = WDT_, PD = PD_, REP = REP_;
     static constexpr int GD = GD_, NCD = NCD_, GH = GH_, NCH = NCH_, GF = GF_, NCF = NCF_;
+    // replicas of each published vector: lane `sub` of a row writes replica `sub`
+    static constexpr int LLR = cmin(cmin(GD, GH), cmin(GF, kPRep));
 };
 
 template <int WDT>
@@ -630,8 +635,8 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
                 if (e < d) xs[e] = emb_at<C::WDT>(s, c.tok, e);
             }
         } else {
-            wait_sample<1>(p.ll_h, s.F, c.ep(l - 1, 3), c.err);
-            block_fetch2<2>(Seg{p.ll_x, d, c.ep(l - 1, 4), xs}, c.err);
+            wait_sample<1>(p.ll_h + c.rep, s.F, c.ep(l - 1, 3), c.err);
+            block_fetch2<2>(Seg{p.ll_x + c.rep, d, c.ep(l - 1, 4), xs}, c.err);
         }
         const float rn = block_norm<C::WDT>(xs, d, gr, s.eps, sm, vin);
         if (active) {
@@ -642,18 +647,18 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
             if (roped) {
                 const float partner = __shfl_xor(y, 32);
                 const float out = second ? fmaf(partner, sn, y * cs) : fmaf(-partner, sn, y * cs);
-                if (sub == 0) {
+                if (sub < C::LLR) {
                     if (is_q) {
                         // query head h = row / D sits in group h / REP at slot h % REP
-                        ll_put(p.ll_qkv + (g / REP) * GS + (g % REP) * PD + e, out, c.ep(l, 0));
+                        ll_put(p.ll_qkv + sub * p.rstride + (g / REP) * GS + (g % REP) * PD + e, out, c.ep(l, 0));
                     } else {
-                        ll_put(p.ll_qkv + g * GS + REP * PD + e, out, c.ep(l, 0));
-                        s.cache[cache_row(s, l, 0, 0, g, c.pos) + e] = out;
+                        ll_put(p.ll_qkv + sub * p.rstride + g * GS + REP * PD + e, out, c.ep(l, 0));
+                        if (sub == 0) s.cache[cache_row(s, l, 0, 0, g, c.pos) + e] = out;
                     }
                 }
-            } else if (sub == 0) {
-                ll_put(p.ll_qkv + g * GS + (REP + 1) * PD + e, y, c.ep(l, 0));
-                s.cache[cache_row(s, l, 1, 0, g, c.pos) + e] = y;
+            } else if (sub < C::LLR) {
+                ll_put(p.ll_qkv + sub * p.rstride + g * GS + (REP + 1) * PD + e, y, c.ep(l, 0));
+                if (sub == 0) s.cache[cache_row(s, l, 1, 0, g, c.pos) + e] = y;
             }
         }
         if (l + 1 < s.L) {
@@ -678,8 +683,8 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
     float* pw = sm + ((HD + 2 * KVD + 3) & ~3) + wv * REP * KV<PD, REP>::PWS;  // softmax weights of this wave
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        if (l > 0) wait_sample<1>(p.ll_x, s.d, c.ep(l - 1, 4), c.err);
-        block_fetch2<2>(Seg{p.ll_qkv, HD + 2 * KVD, c.ep(l, 0), qkv}, c.err);
+        if (l > 0) wait_sample<1>(p.ll_x + c.rep, s.d, c.ep(l - 1, 4), c.err);
+        block_fetch2<2>(Seg{p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), qkv}, c.err);
         __syncthreads();
         if (active) {
             const uint32_t e1 = c.ep(l, 1);
@@ -725,13 +730,13 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
         if (l == 0) {
             if (static_cast<int>(threadIdx.x) < nrows) xr[threadIdx.x] = emb_at<C::WDT>(s, c.tok, r0 + threadIdx.x);
         } else {
-            rows = Seg{p.ll_x + r0, nrows, c.ep(l - 1, 4), xr};
+            rows = Seg{p.ll_x + c.rep + r0, nrows, c.ep(l - 1, 4), xr};
         }
         if (c.fused) {
-            if (l > 0) wait_sample<1>(p.ll_x, d, c.ep(l - 1, 4), c.err);
-            block_fetch2<2>(Seg{p.ll_qkv, in_n, c.ep(l, 0), in}, rows, c.err);
+            if (l > 0) wait_sample<1>(p.ll_x + c.rep, d, c.ep(l - 1, 4), c.err);
+            block_fetch2<2>(Seg{p.ll_qkv + c.rep, in_n, c.ep(l, 0), in}, rows, c.err);
         } else {
-            wait_sample<1>(p.ll_qkv, HD + 2 * KVD, c.ep(l, 0), c.err);
+            wait_sample<1>(p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), c.err);
             block_fetch2<4>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
         }
         __syncthreads();
@@ -767,7 +772,7 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
         XRegs<C::WDT, C::NCH> ox;
         ox.load(o, HD, sub, G);
         const float y = st.finish(ox);
-        if (valid && sub == 0) ll_put(p.ll_x2 + row, xr[row - r0] + y, c.ep(l, 2));
+        if (valid && sub < C::LLR) ll_put(p.ll_x2 + sub * p.rstride + row, xr[row - r0] + y, c.ep(l, 2));
         if (l + 1 < s.L) {
             st.start(p.layers[l + 1].wo, valid ? row : 0, HD, sub, valid);
             if (c.fused && attn_wave) kv.load(s, l + 1, g, 0, c.pos);
@@ -795,16 +800,16 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         if (c.fused)
-            wait_sample<1>(p.ll_qkv, (s.H + 2 * s.Hkv) * s.D, c.ep(l, 0), c.err);
+            wait_sample<1>(p.ll_qkv + c.rep, (s.H + 2 * s.Hkv) * s.D, c.ep(l, 0), c.err);
         else
             wait_sample<1>(p.ll_part, c.nch * s.H * (s.D + 2), c.ep(l, 1), c.err);
-        block_fetch2<2>(Seg{p.ll_x2, d, c.ep(l, 2), xs}, c.err);
+        block_fetch2<2>(Seg{p.ll_x2 + c.rep, d, c.ep(l, 2), xs}, c.err);
         const float rn = block_norm<C::WDT>(xs, d, gr, s.eps, sm, vin);
         XRegs<C::WDT, C::NCD> xr;
         xr.load(vin, d, sub, G);
         const float a = rn * s1.finish(xr);
         const float u = rn * s3.finish(xr);
-        if (valid && sub == 0) ll_put(p.ll_h + row, (a / (1.0f + expf(-a))) * u, c.ep(l, 3));
+        if (valid && sub < C::LLR) ll_put(p.ll_h + sub * p.rstride + row, (a / (1.0f + expf(-a))) * u, c.ep(l, 3));
         if (l + 1 < s.L) {
             s1.start(p.layers[l + 1].w1, valid ? row : 0, d, sub, valid);
             s3.start(p.layers[l + 1].w3, valid ? row : 0, d, sub, valid);
@@ -831,8 +836,9 @@ __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     st.start(p.layers[0].w2, valid ? row : 0, F, sub, valid);
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        wait_sample<1>(p.ll_x2, d, c.ep(l, 2), c.err);
-        block_fetch2<4>(Seg{p.ll_h, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + r0, nrows, c.ep(l, 2), xr}, c.err);
+        wait_sample<1>(p.ll_x2 + c.rep, d, c.ep(l, 2), c.err);
+        block_fetch2<4>(Seg{p.ll_h + c.rep, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + c.rep + r0, nrows, c.ep(l, 2), xr},
+                        c.err);
         if (C::WDT == kBF16) {
             // the pairs block_fetch2 gave this thread: (2t + 512 j, 2t + 512 j + 1)
 #pragma unroll
@@ -845,7 +851,7 @@ __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
         XRegs<C::WDT, C::NCF> hx;
         hx.load(hv, F, sub, G);
         const float y = st.finish(hx);
-        if (valid && sub == 0) ll_put(p.ll_x + row, xr[row - r0] + y, c.ep(l, 4));
+        if (valid && sub < C::LLR) ll_put(p.ll_x + sub * p.rstride + row, xr[row - r0] + y, c.ep(l, 4));
         if (l + 1 < s.L) st.start(p.layers[l + 1].w2, valid ? row : 0, F, sub, valid);
     }
 }
@@ -879,6 +885,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
     c.n = c.pos + 1;
     c.nch = (c.n + kPChunk - 1) / kPChunk;
     c.fused = c.nch == 1;
+    c.rep = (blk % C::LLR) * p.rstride;
     c.tok = d_tok_in ? d_tok_in[0] : tok_value;
     if (c.tok < 0 || c.tok >= s.V) {
         if (threadIdx.x == 0 && blk == 0) atomicOr(c.err, 1);
@@ -915,8 +922,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         float* xs = sm;
         float* vin = C::WDT == kBF16 ? sm + ((s.d + 3) & ~3) : xs;  // product input (see put_pair)
         __syncthreads();
-        wait_sample<32>(p.ll_h, s.F, c.ep(s.L - 1, 3), c.err);
-        block_fetch2<2>(Seg{p.ll_x, s.d, c.ep(s.L - 1, 4), xs}, c.err);
+        wait_sample<32>(p.ll_h + c.rep, s.F, c.ep(s.L - 1, 3), c.err);
+        block_fetch2<2>(Seg{p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), xs}, c.err);
         const float rn = block_norm<C::WDT>(xs, s.d, gr, s.eps, sm, vin);
         XRegs<C::WDT, C::NCD> xr;
         xr.load(vin, s.d, sub, GD);
