@@ -84,18 +84,24 @@ struct Seg {
     float* dst;
 };
 
-// Wait (per wave) until 64 words spread over src[0..n) carry epoch ep.  Used
-// on the output of the phase before the producer, as a cheap throttle; SLEEP
-// spaces the rounds of waits that are expected to be long.
-template <int SLEEP>
+// Wait until 64 words spread over src[0..n) carry epoch ep (ANY: until one
+// of them does).  Wave 0 polls, the other waves wait at the barrier, so a
+// waiting block puts one wave's loads on the memory system; SLEEP spaces the
+// rounds.  Used as a throttle in front of a block_fetch.  Block-uniform call.
+template <int SLEEP, bool ANY = false>
 __device__ void wait_sample(const uint64_t* src, int n, uint32_t ep, int32_t* err) {
     if (n <= 0) return;
-    const uint64_t* q = src + ((threadIdx.x & 63) * n) / 64;
-    long spins = 0;
-    while (!__all(static_cast<uint32_t>(ll_get(q) >> 32) == ep)) {
-        if (SLEEP > 0) __builtin_amdgcn_s_sleep(SLEEP);
-        if (give_up(spins, err)) break;
+    if (threadIdx.x < 64) {
+        const uint64_t* q = src + (static_cast<int>(threadIdx.x) * n) / 64;
+        long spins = 0;
+        while (true) {
+            const bool ok = static_cast<uint32_t>(ll_get(q) >> 32) == ep;
+            if (ANY ? __any(ok) : __all(ok)) break;
+            if (SLEEP > 0) __builtin_amdgcn_s_sleep(SLEEP);
+            if (give_up(spins, err)) break;
+        }
     }
+    __syncthreads();
 }
 
 // Block-cooperative fetch of segment a followed by segment b: thread t polls
@@ -635,7 +641,7 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
                 if (e < d) xs[e] = emb_at<C::WDT>(s, c.tok, e);
             }
         } else {
-            wait_sample<1>(p.ll_h + c.rep, s.F, c.ep(l - 1, 3), c.err);
+            wait_sample<4>(p.ll_h + c.rep, s.F, c.ep(l - 1, 3), c.err);
             block_fetch2<2>(Seg{p.ll_x + c.rep, d, c.ep(l - 1, 4), xs}, c.err);
         }
         const float rn = block_norm<C::WDT>(xs, d, gr, s.eps, sm, vin);
@@ -683,7 +689,7 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
     float* pw = sm + ((HD + 2 * KVD + 3) & ~3) + wv * REP * KV<PD, REP>::PWS;  // softmax weights of this wave
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        if (l > 0) wait_sample<1>(p.ll_x + c.rep, s.d, c.ep(l - 1, 4), c.err);
+        if (l > 0) wait_sample<4>(p.ll_x + c.rep, s.d, c.ep(l - 1, 4), c.err);
         block_fetch2<2>(Seg{p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), qkv}, c.err);
         __syncthreads();
         if (active) {
@@ -733,10 +739,10 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
             rows = Seg{p.ll_x + c.rep + r0, nrows, c.ep(l - 1, 4), xr};
         }
         if (c.fused) {
-            if (l > 0) wait_sample<1>(p.ll_x + c.rep, d, c.ep(l - 1, 4), c.err);
+            if (l > 0) wait_sample<4>(p.ll_x + c.rep, d, c.ep(l - 1, 4), c.err);
             block_fetch2<2>(Seg{p.ll_qkv + c.rep, in_n, c.ep(l, 0), in}, rows, c.err);
         } else {
-            wait_sample<1>(p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), c.err);
+            wait_sample<4>(p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), c.err);
             block_fetch2<4>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
         }
         __syncthreads();
@@ -800,9 +806,9 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         if (c.fused)
-            wait_sample<1>(p.ll_qkv + c.rep, (s.H + 2 * s.Hkv) * s.D, c.ep(l, 0), c.err);
+            wait_sample<4>(p.ll_qkv + c.rep, (s.H + 2 * s.Hkv) * s.D, c.ep(l, 0), c.err);
         else
-            wait_sample<1>(p.ll_part, c.nch * s.H * (s.D + 2), c.ep(l, 1), c.err);
+            wait_sample<4>(p.ll_part, c.nch * s.H * (s.D + 2), c.ep(l, 1), c.err);
         block_fetch2<2>(Seg{p.ll_x2 + c.rep, d, c.ep(l, 2), xs}, c.err);
         const float rn = block_norm<C::WDT>(xs, d, gr, s.eps, sm, vin);
         XRegs<C::WDT, C::NCD> xr;
@@ -836,7 +842,7 @@ __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     st.start(p.layers[0].w2, valid ? row : 0, F, sub, valid);
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        wait_sample<1>(p.ll_x2 + c.rep, d, c.ep(l, 2), c.err);
+        wait_sample<4>(p.ll_x2 + c.rep, d, c.ep(l, 2), c.err);
         block_fetch2<4>(Seg{p.ll_h + c.rep, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + c.rep + r0, nrows, c.ep(l, 2), xr},
                         c.err);
         if (C::WDT == kBF16) {
