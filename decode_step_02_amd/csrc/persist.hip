@@ -641,7 +641,7 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
                 if (e < d) xs[e] = emb_at<C::WDT>(s, c.tok, e);
             }
         } else {
-            wait_sample<4>(p.ll_h + c.rep, s.F, c.ep(l - 1, 3), c.err);
+            wait_sample<4, true>(p.ll_x + c.rep, d, c.ep(l - 1, 4), c.err);
             block_fetch2<2>(Seg{p.ll_x + c.rep, d, c.ep(l - 1, 4), xs}, c.err);
         }
         const float rn = block_norm<C::WDT>(xs, d, gr, s.eps, sm, vin);
@@ -689,7 +689,7 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
     float* pw = sm + ((HD + 2 * KVD + 3) & ~3) + wv * REP * KV<PD, REP>::PWS;  // softmax weights of this wave
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        if (l > 0) wait_sample<4>(p.ll_x + c.rep, s.d, c.ep(l - 1, 4), c.err);
+        wait_sample<4, true>(p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), c.err);
         block_fetch2<2>(Seg{p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), qkv}, c.err);
         __syncthreads();
         if (active) {
@@ -739,10 +739,10 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
             rows = Seg{p.ll_x + c.rep + r0, nrows, c.ep(l - 1, 4), xr};
         }
         if (c.fused) {
-            if (l > 0) wait_sample<4>(p.ll_x + c.rep, d, c.ep(l - 1, 4), c.err);
+            wait_sample<4, true>(p.ll_qkv + c.rep, in_n, c.ep(l, 0), c.err);
             block_fetch2<2>(Seg{p.ll_qkv + c.rep, in_n, c.ep(l, 0), in}, rows, c.err);
         } else {
-            wait_sample<4>(p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), c.err);
+            wait_sample<4, true>(p.ll_part, in_n, c.ep(l, 1), c.err);
             block_fetch2<4>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
         }
         __syncthreads();
@@ -805,10 +805,7 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     float* vin = C::WDT == kBF16 ? sm + ((d + 3) & ~3) : xs;  // product input (see put_pair)
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        if (c.fused)
-            wait_sample<4>(p.ll_qkv + c.rep, (s.H + 2 * s.Hkv) * s.D, c.ep(l, 0), c.err);
-        else
-            wait_sample<4>(p.ll_part, c.nch * s.H * (s.D + 2), c.ep(l, 1), c.err);
+        wait_sample<4, true>(p.ll_x2 + c.rep, d, c.ep(l, 2), c.err);
         block_fetch2<2>(Seg{p.ll_x2 + c.rep, d, c.ep(l, 2), xs}, c.err);
         const float rn = block_norm<C::WDT>(xs, d, gr, s.eps, sm, vin);
         XRegs<C::WDT, C::NCD> xr;
@@ -842,7 +839,7 @@ __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     st.start(p.layers[0].w2, valid ? row : 0, F, sub, valid);
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        wait_sample<4>(p.ll_x2 + c.rep, d, c.ep(l, 2), c.err);
+        wait_sample<4, true>(p.ll_h + c.rep, F, c.ep(l, 3), c.err);
         block_fetch2<4>(Seg{p.ll_h + c.rep, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + c.rep + r0, nrows, c.ep(l, 2), xr},
                         c.err);
         if (C::WDT == kBF16) {
@@ -929,6 +926,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         float* vin = C::WDT == kBF16 ? sm + ((s.d + 3) & ~3) : xs;  // product input (see put_pair)
         __syncthreads();
         wait_sample<32>(p.ll_h + c.rep, s.F, c.ep(s.L - 1, 3), c.err);
+        wait_sample<4, true>(p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), c.err);
         block_fetch2<2>(Seg{p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), xs}, c.err);
         const float rn = block_norm<C::WDT>(xs, s.d, gr, s.eps, sm, vin);
         XRegs<C::WDT, C::NCD> xr;
