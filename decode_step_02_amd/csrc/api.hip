@@ -111,7 +111,7 @@ size_t layout(const ds_config* c, std::vector<size_t>* off) {
 // Workspace carve-up for a (B, T) cache.
 struct WsLayout {
     size_t x, q, o, h, part_o, part_ml, logits, keys, slot, pos, flag, err, rope_cos, rope_sin;
-    size_t ll_x, ll_x2, ll_qkv, ll_part, ll_h, ll_keys, epoch, layers, ll_end, total, rstride;
+    size_t ll_x, ll_x2, ll_qkv, ll_part, ll_h, ll_keys, ll_late, epoch, layers, ll_end, total, rstride;
 };
 
 WsLayout ws_layout(const ds_config* c, int B, int T) {
@@ -151,6 +151,7 @@ WsLayout ws_layout(const ds_config* c, int B, int T) {
     w.ll_part = take(8 * static_cast<size_t>(c->n_heads) * ds::kPMaxChunks * (c->head_dim + 2));
     w.ll_h = take(rbytes);
     w.ll_keys = take(8 * static_cast<size_t>(ds::kPKeyWords));
+    w.ll_late = take(8);
     w.epoch = take(sizeof(uint32_t));
     w.ll_end = p;
     w.layers = take(sizeof(ds::LayerW) * static_cast<size_t>(c->n_layers));
@@ -384,6 +385,7 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     pa.ll_part = reinterpret_cast<uint64_t*>(ws + lay.ll_part);
     pa.ll_h = reinterpret_cast<uint64_t*>(ws + lay.ll_h);
     pa.ll_keys = reinterpret_cast<uint64_t*>(ws + lay.ll_keys);
+    pa.ll_late = reinterpret_cast<uint64_t*>(ws + lay.ll_late);
     pa.epoch = reinterpret_cast<uint32_t*>(ws + lay.epoch);
     pa.rstride = static_cast<int>(lay.rstride);
     kv->persist_ctx = ds::persist_max_ctx(s);

@@ -82,6 +82,7 @@ struct PersistArgs {
     uint64_t* ll_part;      // [kPMaxChunks][H][D+2] attention partials (m, l, o), chunk-major
     uint64_t* ll_h;         // [F]      silu(a)*u
     uint64_t* ll_keys;      // [kPKeyWords] argmax words
+    uint64_t* ll_late;      // one word in a line of its own: the last layer has begun
     uint32_t* epoch;        // epoch base, advanced by every step
     int rstride;            // words between two replicas of a vector
 };

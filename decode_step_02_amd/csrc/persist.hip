@@ -104,6 +104,20 @@ __device__ void wait_sample(const uint64_t* src, int n, uint32_t ep, int32_t* er
     __syncthreads();
 }
 
+// Wait until the single word w carries epoch ep: one lane polls, SLEEP
+// spaces the rounds, the block waits at the barrier.  Block-uniform call.
+template <int SLEEP>
+__device__ void wait_word(const uint64_t* w, uint32_t ep, int32_t* err) {
+    if (threadIdx.x == 0) {
+        long spins = 0;
+        while (static_cast<uint32_t>(ll_get(w) >> 32) != ep) {
+            __builtin_amdgcn_s_sleep(SLEEP);
+            if (give_up(spins, err)) break;
+        }
+    }
+    __syncthreads();
+}
+
 // Block-cooperative fetch of segment a followed by segment b: thread t polls
 // the words t, t + 256, ... of the concatenation, J per round, with
 // unconditional loads of clamped indices so that a round is one memory round
@@ -667,6 +681,7 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
                 if (sub == 0) s.cache[cache_row(s, l, 1, 0, g, c.pos) + e] = y;
             }
         }
+        if (l + 1 == s.L && bt == 0 && threadIdx.x == 0) ll_put(p.ll_late, 0.f, c.ep(l, 0));
         if (l + 1 < s.L) {
             st.start(wmat(l + 1), row, d, sub, active);
             load_gains(gr, p.layers[l + 1].attn_norm, d);
@@ -925,7 +940,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         float* xs = sm;
         float* vin = C::WDT == kBF16 ? sm + ((s.d + 3) & ~3) : xs;  // product input (see put_pair)
         __syncthreads();
-        wait_sample<32>(p.ll_h + c.rep, s.F, c.ep(s.L - 1, 3), c.err);
+        wait_word<32>(p.ll_late, c.ep(s.L - 1, 0), c.err);
         wait_sample<4, true>(p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), c.err);
         block_fetch2<2>(Seg{p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), xs}, c.err);
         const float rn = block_norm<C::WDT>(xs, s.d, gr, s.eps, sm, vin);
