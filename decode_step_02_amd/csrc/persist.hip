@@ -479,6 +479,29 @@ struct KV {
         for (int ii = 0; ii < NV; ii++) v[ii] = vb[static_cast<size_t>(min(t0 + ii * RV + rv, tmax)) * PD];
     }
 
+    // acc[j] = sum over the lane's value rows of weight * value for head j,
+    // the first N4 float4 groups of weights (the rest are 0), plus the new
+    // row's term once (row group 0), then the RV row groups added up.
+    template <int N4>
+    __device__ __forceinline__ void weighted_values(const float* pw, float vn, int rv, float (&acc)[REP]) const {
+#pragma unroll
+        for (int j = 0; j < REP; j++) {
+            const float4* pj = reinterpret_cast<const float4*>(pw + j * PWS + rv * NV);
+            float4 pe[N4];
+#pragma unroll
+            for (int c4 = 0; c4 < N4; c4++) pe[c4] = pj[c4];  // one batch of broadcast reads
+            float a0 = rv == 0 ? pw[j * PWS + kPChunk] * vn : 0.f, a1 = 0.f;
+#pragma unroll
+            for (int c4 = 0; c4 < N4; c4++) {
+                a0 = fmaf(pe[c4].x, v[4 * c4 + 0], a0);
+                a1 = fmaf(pe[c4].y, v[4 * c4 + 1], a1);
+                a0 = fmaf(pe[c4].z, v[4 * c4 + 2], a0);
+                a1 = fmaf(pe[c4].w, v[4 * c4 + 3], a1);
+            }
+            acc[j] = stride_reduce<PD>(a0 + a1, OpSum{});  // none when PD == 64
+        }
+    }
+
     // Attention of the REP query heads of group g over positions t0 ..
     // min(pos, t0 + 31).
     //  - Scores use the key layout (a 4-lane reduction per row).  The new key
@@ -560,10 +583,10 @@ struct KV {
                 const float pe = t0 + sl * 16 <= pos ? __expf(sc[j][sl] - m[j]) : 0.f;
                 ls[j] += pe;
                 const int p = sl * 16 + rk;
-                if (qk == 0) {
-                    pw[j * PWS + (p % RV) * NV + p / RV] = p == cur ? 0.f : pe;
-                    if (p == cur) pw[j * PWS + kPChunk] = pe;
-                }
+                // every lane of the row stores (the same value); in the new row's
+                // quad lane 1 stores its weight apart and the others a 0 entry
+                const bool nr = p == cur;
+                pw[j * PWS + (nr && qk == 1 ? kPChunk : (p % RV) * NV + p / RV)] = nr && qk != 1 ? 0.f : pe;
             }
             ls[j] = group_reduce<64, OpSum, 4>(ls[j], OpSum{});
         }
@@ -577,24 +600,10 @@ struct KV {
         if (pos == 0) {
 #pragma unroll
             for (int j = 0; j < REP; j++) acc[j] = vn;  // one position: weight 1 on the new row
+        } else if (cur < 16) {
+            weighted_values<NV / 8>(pw, vn, rv, acc);  // positions 16.. of the chunk have weight 0
         } else {
-#pragma unroll
-            for (int j = 0; j < REP; j++) {
-                const float4* pj = reinterpret_cast<const float4*>(pw + j * PWS + rv * NV);
-                float4 pe[NV / 4];
-#pragma unroll
-                for (int c4 = 0; c4 < NV / 4; c4++) pe[c4] = pj[c4];  // one batch of broadcast reads
-                // the new row once (row group 0), before the row groups are added up
-                float a0 = rv == 0 ? pw[j * PWS + kPChunk] * vn : 0.f, a1 = 0.f;
-#pragma unroll
-                for (int c4 = 0; c4 < NV / 4; c4++) {  // weights past the context are 0
-                    a0 = fmaf(pe[c4].x, v[4 * c4 + 0], a0);
-                    a1 = fmaf(pe[c4].y, v[4 * c4 + 1], a1);
-                    a0 = fmaf(pe[c4].z, v[4 * c4 + 2], a0);
-                    a1 = fmaf(pe[c4].w, v[4 * c4 + 3], a1);
-                }
-                acc[j] = stride_reduce<PD>(a0 + a1, OpSum{});  // the RV row groups (none when PD == 64)
-            }
+            weighted_values<NV / 4>(pw, vn, rv, acc);
         }
         float nb[REP];
 #pragma unroll
