@@ -67,8 +67,14 @@ __device__ __forceinline__ float dpp_mov(float v) {
 struct OpSum {
     __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
 };
+// One v_max_f32, without the quieting of signalling NaNs that fmaxf puts in
+// front of operands that come from lane moves (no NaNs are reduced here).
 struct OpMax {
-    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+    __device__ __forceinline__ float operator()(float a, float b) const {
+        float r;
+        asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+        return r;
+    }
 };
 
 // op(v, v[lane ^ O]) for O in {1, 2, 4, 8, 16, 32}: true exchanges, valid for any values.
@@ -106,6 +112,30 @@ __device__ __forceinline__ float group_reduce(float v, Op op) {
     if constexpr (N >= 32 && FROM <= 16) v = xor_op<16>(v, op);
     if constexpr (N >= 64) v = xor_op<32>(v, op);
     return v;
+}
+
+// group_reduce of K independent values, level by level: the K exchanges of a
+// level are independent, so no exchange waits on the result just computed.
+template <int N, typename Op, int FROM = 1, int K>
+__device__ __forceinline__ void group_reduce_n(float (&v)[K], Op op) {
+#pragma unroll
+    for (int k = 0; k < K; k++)
+        if constexpr (N >= 2 && FROM <= 1) v[k] = xor_op<1>(v[k], op);
+#pragma unroll
+    for (int k = 0; k < K; k++)
+        if constexpr (N >= 4 && FROM <= 2) v[k] = xor_op<2>(v[k], op);
+#pragma unroll
+    for (int k = 0; k < K; k++)
+        if constexpr (N >= 8 && FROM <= 4) v[k] = op(v[k], dpp_mov<0x141>(v[k]));
+#pragma unroll
+    for (int k = 0; k < K; k++)
+        if constexpr (N >= 16 && FROM <= 8) v[k] = op(v[k], dpp_mov<0x140>(v[k]));
+#pragma unroll
+    for (int k = 0; k < K; k++)
+        if constexpr (N >= 32 && FROM <= 16) v[k] = xor_op<16>(v[k], op);
+#pragma unroll
+    for (int k = 0; k < K; k++)
+        if constexpr (N >= 64) v[k] = xor_op<32>(v[k], op);
 }
 
 // Reduce over the lanes lane ^ k, k a multiple of LO (LO a power of two):

@@ -551,19 +551,21 @@ struct KV {
         for (int sl = 0; sl < NK; sl++) {
             const int tb = t0 + sl * 16;  // first position of the slot (uniform)
             if (tb <= pos) {
+                float dd[REP];
 #pragma unroll
                 for (int j = 0; j < REP; j++) {
-                    float dd = 0.f;
+                    dd[j] = 0.f;
 #pragma unroll
                     for (int f = 0; f < KF; f++) {
-                        dd = fmaf(k[sl][f].x, q[j][f].x, dd);
-                        dd = fmaf(k[sl][f].y, q[j][f].y, dd);
-                        dd = fmaf(k[sl][f].z, q[j][f].z, dd);
-                        dd = fmaf(k[sl][f].w, q[j][f].w, dd);
+                        dd[j] = fmaf(k[sl][f].x, q[j][f].x, dd[j]);
+                        dd[j] = fmaf(k[sl][f].y, q[j][f].y, dd[j]);
+                        dd[j] = fmaf(k[sl][f].z, q[j][f].z, dd[j]);
+                        dd[j] = fmaf(k[sl][f].w, q[j][f].w, dd[j]);
                     }
-                    dd = group_sum<4>(dd);
-                    sc[j][sl] = tb + rk <= pos ? dd * scale : -INFINITY;
                 }
+                group_reduce_n<4, OpSum>(dd, OpSum{});
+#pragma unroll
+                for (int j = 0; j < REP; j++) sc[j][sl] = tb + rk <= pos ? dd[j] * scale : -INFINITY;
             } else {
 #pragma unroll
                 for (int j = 0; j < REP; j++) sc[j][sl] = -INFINITY;
@@ -575,8 +577,11 @@ struct KV {
         for (int j = 0; j < REP; j++) {
             m[j] = sc[j][0];
 #pragma unroll
-            for (int sl = 1; sl < NK; sl++) m[j] = fmaxf(m[j], sc[j][sl]);
-            m[j] = group_reduce<64, OpMax, 4>(m[j], OpMax{});
+            for (int sl = 1; sl < NK; sl++) m[j] = OpMax{}(m[j], sc[j][sl]);
+        }
+        group_reduce_n<64, OpMax, 4>(m, OpMax{});
+#pragma unroll
+        for (int j = 0; j < REP; j++) {
             ls[j] = 0.f;
 #pragma unroll
             for (int sl = 0; sl < NK; sl++) {
@@ -588,8 +593,8 @@ struct KV {
                 const bool nr = p == cur;
                 pw[j * PWS + (nr && qk == 1 ? kPChunk : (p % RV) * NV + p / RV)] = nr && qk != 1 ? 0.f : pe;
             }
-            ls[j] = group_reduce<64, OpSum, 4>(ls[j], OpSum{});
         }
+        group_reduce_n<64, OpSum, 4>(ls, OpSum{});
         if (cur >= kPChunk && lane == 0) {
 #pragma unroll
             for (int j = 0; j < REP; j++) pw[j * PWS + kPChunk] = 0.f;
