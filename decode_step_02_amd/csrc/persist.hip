@@ -351,24 +351,27 @@ struct XRegs<kBF16, NC> {
 
 // The wave's share of one weight row: G lanes per row, lane `sub` takes the
 // 16-byte chunks sub, sub + G, ..., NC of them (the host picks G and NC so
-// that NC * G covers the row).  start() issues their loads into registers;
-// finish() multiplies them with the matching XRegs and reduces over the G
-// lanes, touching no memory.
+// that NC * G covers the row).  start() issues their loads into registers,
+// with zeros for the chunks past the row's end and for rows that are not
+// valid, so that finish() needs no masks: it multiplies them with the
+// matching XRegs in four running sums and reduces over the G lanes,
+// touching no memory.
 template <int WDT, int G, int NC>
 struct PStream {
     static constexpr int EPC = WDT == kBF16 ? 8 : 4;
     uint4 w[NC];
-    int nch, sub;
-    __device__ __forceinline__ void start(const void* W, int row, int K, int sub_, bool valid) {
+    __device__ __forceinline__ void start(const void* W, int row, int K, int sub, bool valid) {
         const size_t base = static_cast<size_t>(row) * K;
-        sub = sub_;
-        nch = valid ? K / EPC : 0;
-        const int last = K / EPC - 1;
+        const int nchunks = valid ? K / EPC : 0;
 #pragma unroll
         for (int p = 0; p < NC; p++) {
-            const size_t e = base + static_cast<size_t>(min(sub + p * G, last)) * EPC;
-            w[p] = WDT == kBF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + e)
-                                : *reinterpret_cast<const uint4*>(static_cast<const float*>(W) + e);
+            const int c = sub + p * G;
+            w[p] = make_uint4(0u, 0u, 0u, 0u);
+            if (c < nchunks) {
+                const size_t e = base + static_cast<size_t>(c) * EPC;
+                w[p] = WDT == kBF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + e)
+                                    : *reinterpret_cast<const uint4*>(static_cast<const float*>(W) + e);
+            }
         }
     }
     __device__ __forceinline__ static float dot2(uint32_t w2, uint32_t x2, float acc) {
@@ -376,33 +379,29 @@ struct PStream {
                                                 false);
     }
     __device__ __forceinline__ float finish(const XRegs<WDT, NC>& x) const {
-        float a0 = 0.f, a1 = 0.f;
+        float a[4] = {0.f, 0.f, 0.f, 0.f};  // bf16: hi and lo terms of even and odd chunks
 #pragma unroll
         for (int p = 0; p < NC; p++) {
-            float d;
+            float& h = a[2 * (p & 1)];
+            float& l = a[2 * (p & 1) + 1];
             if constexpr (WDT == kBF16) {
-                // hi and lo terms in two chains
-                float dh = dot2(w[p].x, x.h[p].x, 0.f), dl = dot2(w[p].x, x.l[p].x, 0.f);
-                dh = dot2(w[p].y, x.h[p].y, dh);
-                dl = dot2(w[p].y, x.l[p].y, dl);
-                dh = dot2(w[p].z, x.h[p].z, dh);
-                dl = dot2(w[p].z, x.l[p].z, dl);
-                dh = dot2(w[p].w, x.h[p].w, dh);
-                dl = dot2(w[p].w, x.l[p].w, dl);
-                d = dh + dl;
+                h = dot2(w[p].x, x.h[p].x, h);
+                l = dot2(w[p].x, x.l[p].x, l);
+                h = dot2(w[p].y, x.h[p].y, h);
+                l = dot2(w[p].y, x.l[p].y, l);
+                h = dot2(w[p].z, x.h[p].z, h);
+                l = dot2(w[p].z, x.l[p].z, l);
+                h = dot2(w[p].w, x.h[p].w, h);
+                l = dot2(w[p].w, x.l[p].w, l);
             } else {
-                const float4 a = x.v[p];
-                d = __uint_as_float(w[p].x) * a.x;
-                d = fmaf(__uint_as_float(w[p].y), a.y, d);
-                d = fmaf(__uint_as_float(w[p].z), a.z, d);
-                d = fmaf(__uint_as_float(w[p].w), a.w, d);
+                const float4 v = x.v[p];
+                h = fmaf(__uint_as_float(w[p].x), v.x, h);
+                l = fmaf(__uint_as_float(w[p].y), v.y, l);
+                h = fmaf(__uint_as_float(w[p].z), v.z, h);
+                l = fmaf(__uint_as_float(w[p].w), v.w, l);
             }
-            if (p & 1)
-                a1 += sub + p * G < nch ? d : 0.f;
-            else
-                a0 += sub + p * G < nch ? d : 0.f;
         }
-        return group_sum<G>(a0 + a1);
+        return group_sum<G>((a[0] + a[1]) + (a[2] + a[3]));
     }
 };
 
@@ -961,22 +960,25 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         XRegs<C::WDT, C::NCD> xr;
         xr.load(vin, s.d, sub, GD);
         uint64_t key = 0ull;
-        while (ta < ntask) {
-            const int row = ta * R + rs;
-            const float y = rn * sa.finish(xr);
+        auto take = [&](const PStream<C::WDT, GD, C::NCD>& st, int t) {
+            const int row = t * R + rs;
+            const float y = rn * st.finish(xr);
             if (row < s.V && sub == 0) {
                 s.logits[row] = y;
                 const uint64_t k = key_word(y, row, epk);
                 key = k > key ? k : key;
             }
-            // the stream just used takes the task after the one in flight
-            const int tn = tb + kPWaves;
-            if (tn < ntask) sa.start(p.wcls, min(tn * R + rs, s.V - 1), s.d, sub, tn * R + rs < s.V);
-            const PStream<C::WDT, GD, C::NCD> tmp = sa;
-            sa = sb;
-            sb = tmp;
-            ta = tb;
-            tb = tn;
+        };
+        // the streams alternate; the one just used takes the task after the one in flight
+        for (int t = ta; t < ntask; t += 2 * kPWaves) {
+            take(sa, t);
+            const int t2 = t + 2 * kPWaves;
+            if (t2 < ntask) sa.start(p.wcls, min(t2 * R + rs, s.V - 1), s.d, sub, t2 * R + rs < s.V);
+            const int u = t + kPWaves;
+            if (u >= ntask) break;
+            take(sb, u);
+            const int u2 = u + 2 * kPWaves;
+            if (u2 < ntask) sb.start(p.wcls, min(u2 * R + rs, s.V - 1), s.d, sub, u2 * R + rs < s.V);
         }
         key = wave_max_u64(key);
         if (lane == 0) {
