@@ -158,6 +158,23 @@ __device__ void block_fetch(const Seg& a, const Seg& b, int32_t* err) {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Loads through the global address space: pointers read out of memory (the
+// layer table) are otherwise accessed with flat instructions, which also
+// count against the LDS wait counter.  16-byte loads go through a native
+// vector type (the HIP vector structs copy through generic pointers).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload_u4(const void* p) {
+    const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 gload_f4(const void* p) {
+    const f32x4 v = *(const __attribute__((address_space(1))) f32x4*)p;
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float gload_f(const float* p) {
+    return *(const __attribute__((address_space(1))) float*)p;
+}
+
 // One poll round of J 16-byte loads (two LL words each) with the cache
 // policy of an agent-scope atomic load (sc1), completed inside the same asm
 // block so that no result is read before it has arrived.  Every 8-byte word
@@ -315,12 +332,13 @@ __device__ float block_norm(const float* xs, int n, const float (&gr)[kPNorm], f
 
 __device__ __forceinline__ void load_gains(float (&gr)[kPNorm], const float* __restrict__ g, int n) {
 #pragma unroll
-    for (int j = 0; j < kPNorm; j++) gr[j] = g[min(own_elem(j), n - 1)];
+    for (int j = 0; j < kPNorm; j++) gr[j] = gload_f(g + min(own_elem(j), n - 1));
 }
 
 // The lane's share of a row product's input: the chunks sub, sub + G, ...
 // (EPC elements each, clamped to the last chunk), read from LDS into
 // registers in one batch so that the products wait for LDS once.
+
 template <int WDT, int NC>
 struct XRegs;
 
@@ -369,8 +387,8 @@ struct PStream {
             w[p] = make_uint4(0u, 0u, 0u, 0u);
             if (c < nchunks) {
                 const size_t e = base + static_cast<size_t>(c) * EPC;
-                w[p] = WDT == kBF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + e)
-                                    : *reinterpret_cast<const uint4*>(static_cast<const float*>(W) + e);
+                w[p] = WDT == kBF16 ? gload_u4(static_cast<const uint16_t*>(W) + e)
+                                    : gload_u4(static_cast<const float*>(W) + e);
             }
         }
     }
@@ -471,11 +489,11 @@ struct KV {
         for (int sl = 0; sl < NK; sl++) {
             const float* src = s.cache + cache_row(s, l, 0, 0, g, min(t0 + sl * 16 + rk, tmax)) + qk * (PD / 4);
 #pragma unroll
-            for (int f = 0; f < KF; f++) k[sl][f] = reinterpret_cast<const float4*>(src)[f];
+            for (int f = 0; f < KF; f++) k[sl][f] = gload_f4(src + 4 * f);
         }
         const float* vb = s.cache + cache_row(s, l, 1, 0, g, 0) + ev;
 #pragma unroll
-        for (int ii = 0; ii < NV; ii++) v[ii] = vb[static_cast<size_t>(min(t0 + ii * RV + rv, tmax)) * PD];
+        for (int ii = 0; ii < NV; ii++) v[ii] = gload_f(vb + static_cast<size_t>(min(t0 + ii * RV + rv, tmax)) * PD);
     }
 
     // acc[j] = sum over the lane's value rows of weight * value for head j,
