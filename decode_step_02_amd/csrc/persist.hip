@@ -307,7 +307,7 @@ __device__ __forceinline__ int own_elem(int j) {
 // RMSNorm of xs[0..n) (n <= 1024, even) for the whole block.  Each thread
 // takes the element pairs it owns, multiplies them by their gains and stores
 // them as the row-product input vin (fp32 or bf16 hi/lo pairs, see put_pair);
-// the function returns 1 / sqrt(mean(x^2) + eps), by which the caller scales
+// the function returns 1 / sqrt(mean(x^2) + eps) (v_rsq_f32, within 1 ulp), by which the caller scales
 // its dot products.  Ends with a barrier, after which vin is complete.
 template <int WDT>
 __device__ float block_norm(const float* xs, int n, const float (&gr)[kPNorm], float eps, float* sm, float* vin) {
@@ -327,7 +327,7 @@ __device__ float block_norm(const float* xs, int n, const float (&gr)[kPNorm], f
     if ((tid & 63) == 0) sm[kPRed + (tid >> 6)] = ss;
     __syncthreads();
     const float tot = (sm[kPRed] + sm[kPRed + 1]) + (sm[kPRed + 2] + sm[kPRed + 3]);
-    return 1.0f / sqrtf(tot / static_cast<float>(n) + eps);
+    return __builtin_amdgcn_rsqf(tot * (1.0f / static_cast<float>(n)) + eps);
 }
 
 __device__ __forceinline__ void load_gains(float (&gr)[kPNorm], const float* __restrict__ g, int n) {
@@ -671,6 +671,12 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
         const LayerW& w = p.layers[l];
         return which == 0 ? w.wq : (which == 1 ? w.wk : w.wv);
     };
+    // the lane's word in the layer-0 Q/K/V words, and its cache element (keys and values)
+    const int g = row / PD, e = row % PD;
+    const int qw = which == 0 ? (g / REP) * GS + (g % REP) * PD + e : g * GS + (which == 1 ? REP : REP + 1) * PD + e;
+    uint64_t* const put_at = p.ll_qkv + sub * p.rstride + qw;
+    float* const crow = s.cache + cache_row(s, 0, which == 2 ? 1 : 0, 0, g, c.pos) + e;
+    const size_t cstride = cache_row(s, 1, 0, 0, 0, 0);  // one layer of the cache
     PStream<C::WDT, G, C::NCD> st;
     float gr[kPNorm];
     st.start(wmat(0), row, d, sub, active);
@@ -693,23 +699,17 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
         if (active) {
             XRegs<C::WDT, C::NCD> xr;
             xr.load(vin, d, sub, G);
-            const float y = rn * st.finish(xr);
-            const int g = row / PD, e = row % PD;
-            if (roped) {
-                const float partner = __shfl_xor(y, 32);
-                const float out = second ? fmaf(partner, sn, y * cs) : fmaf(-partner, sn, y * cs);
-                if (sub < C::LLR) {
-                    if (is_q) {
-                        // query head h = row / D sits in group h / REP at slot h % REP
-                        ll_put(p.ll_qkv + sub * p.rstride + (g / REP) * GS + (g % REP) * PD + e, out, c.ep(l, 0));
-                    } else {
-                        ll_put(p.ll_qkv + sub * p.rstride + g * GS + REP * PD + e, out, c.ep(l, 0));
-                        if (sub == 0) s.cache[cache_row(s, l, 0, 0, g, c.pos) + e] = out;
-                    }
-                }
-            } else if (sub < C::LLR) {
-                ll_put(p.ll_qkv + sub * p.rstride + g * GS + (REP + 1) * PD + e, y, c.ep(l, 0));
-                if (sub == 0) s.cache[cache_row(s, l, 1, 0, g, c.pos) + e] = y;
+            float out = rn * st.finish(xr);
+            if (roped) {  // uniform over the wave
+                // r[0] holds the element of the first half (lane < 32), r[1] its partner
+                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(out), __float_as_uint(out), false, false);
+                const float x0 = __uint_as_float(r[0]), x1 = __uint_as_float(r[1]);
+                out = second ? fmaf(x0, sn, x1 * cs) : fmaf(-x1, sn, x0 * cs);
+            }
+            if (sub < C::LLR) {
+                // query head h = row / D sits in group h / REP at slot h % REP; then key, value
+                ll_put(put_at, out, c.ep(l, 0));
+                if (sub == 0 && which != 0) crow[static_cast<size_t>(l) * cstride] = out;
             }
         }
         if (l + 1 == s.L && bt == 0 && threadIdx.x == 0) ll_put(p.ll_late, 0.f, c.ep(l, 0));
