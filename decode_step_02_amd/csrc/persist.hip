@@ -261,6 +261,31 @@ __device__ __forceinline__ void block_fetch2(const Seg& a, int32_t* err) {
     block_fetch2<J>(a, Seg{a.src, 0, a.ep, a.dst}, err);
 }
 
+// The words of a that thread t owns (own_elem order: 2t, 2t + 1, 2t + 512,
+// 2t + 513), polled like block_fetch2 and kept in registers, 0 past a.n.
+// Needs 2 <= a.n <= 4 * kPThreads, a.n even and a 16-byte aligned segment.
+__device__ void block_fetch_own(const Seg& a, float (&x)[kPNorm], int32_t* err) {
+    static_assert(kPNorm == 4, "two word pairs per thread");
+    const int tid = threadIdx.x;
+    const uint64_t* src[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) src[j] = a.src + min(2 * (tid + kPThreads * j), a.n - 2);
+    u32x4 w[2];
+    long spins = 0;
+    while (true) {
+        poll_wide<2>(w, src);
+        const bool ok = w[0].y == a.ep && w[0].w == a.ep && w[1].y == a.ep && w[1].w == a.ep;
+        if (__all(ok)) break;
+        if (give_up(spins, err)) break;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const bool in = 2 * (tid + kPThreads * j) < a.n;
+        x[2 * j] = in ? __uint_as_float(w[j].x) : 0.f;
+        x[2 * j + 1] = in ? __uint_as_float(w[j].z) : 0.f;
+    }
+}
+
 template <int J>
 __device__ __forceinline__ void block_fetch(const Seg& a, int32_t* err) {
     block_fetch<J>(a, Seg{a.src, 0, a.ep, a.dst}, err);  // an empty second segment (never null)
@@ -304,24 +329,25 @@ __device__ __forceinline__ int own_elem(int j) {
     return 2 * static_cast<int>(threadIdx.x) + (j & 1) + 2 * kPThreads * (j >> 1);
 }
 
-// RMSNorm of xs[0..n) (n <= 1024, even) for the whole block.  Each thread
-// takes the element pairs it owns, multiplies them by their gains and stores
-// them as the row-product input vin (fp32 or bf16 hi/lo pairs, see put_pair);
-// the function returns 1 / sqrt(mean(x^2) + eps) (v_rsq_f32, within 1 ulp), by which the caller scales
-// its dot products.  Ends with a barrier, after which vin is complete.
+// RMSNorm for the whole block of a vector of n <= 1024 elements (n even),
+// each thread holding the elements it owns (x[j] = element own_elem(j), 0
+// past n).  Each thread multiplies its pairs by their gains and stores them
+// as the row-product input vin (fp32 or bf16 hi/lo pairs, see put_pair); the
+// function returns 1 / sqrt(mean(x^2) + eps) (v_rsq_f32, within 1 ulp), by
+// which the caller scales its dot products.  Ends with a barrier, after which
+// vin is complete.
 template <int WDT>
-__device__ float block_norm(const float* xs, int n, const float (&gr)[kPNorm], float eps, float* sm, float* vin) {
+__device__ float block_norm_regs(const float (&x)[kPNorm], int n, const float (&gr)[kPNorm], float eps, float* sm,
+                                 float* vin) {
     const int tid = threadIdx.x;
     float ss = 0.f;
 #pragma unroll
     for (int jj = 0; jj < kPNorm / 2; jj++) {
         const int i = own_elem(2 * jj);  // the pair (i, i + 1)
-        if (i < n) {
-            const float a = xs[i], b = xs[i + 1];
-            ss = fmaf(a, a, ss);
-            ss = fmaf(b, b, ss);
-            put_pair<WDT>(vin, n, i, gr[2 * jj] * a, gr[2 * jj + 1] * b);
-        }
+        const float a = x[2 * jj], b = x[2 * jj + 1];
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
+        if (i < n) put_pair<WDT>(vin, n, i, gr[2 * jj] * a, gr[2 * jj + 1] * b);
     }
     ss = group_sum<64>(ss);
     if ((tid & 63) == 0) sm[kPRed + (tid >> 6)] = ss;
@@ -681,21 +707,21 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     float gr[kPNorm];
     st.start(wmat(0), row, d, sub, active);
     load_gains(gr, p.layers[0].attn_norm, d);
-    float* xs = sm;
-    float* vin = C::WDT == kBF16 ? sm + ((d + 3) & ~3) : xs;  // product input (see put_pair)
+    float* const vin = sm;  // product input (see put_pair)
     for (int l = 0; l < s.L; l++) {
         __syncthreads();  // nobody reads the previous layer's LDS any more
+        float xv[kPNorm];
         if (l == 0) {
 #pragma unroll
             for (int j = 0; j < kPNorm; j++) {
                 const int e = own_elem(j);
-                if (e < d) xs[e] = emb_at<C::WDT>(s, c.tok, e);
+                xv[j] = e < d ? emb_at<C::WDT>(s, c.tok, e) : 0.f;
             }
         } else {
             wait_sample<4, true>(p.ll_x + c.rep, d, c.ep(l - 1, 4), c.err);
-            block_fetch2<2>(Seg{p.ll_x + c.rep, d, c.ep(l - 1, 4), xs}, c.err);
+            block_fetch_own(Seg{p.ll_x + c.rep, d, c.ep(l - 1, 4), nullptr}, xv, c.err);
         }
-        const float rn = block_norm<C::WDT>(xs, d, gr, s.eps, sm, vin);
+        const float rn = block_norm_regs<C::WDT>(xv, d, gr, s.eps, sm, vin);
         if (active) {
             XRegs<C::WDT, C::NCD> xr;
             xr.load(vin, d, sub, G);
@@ -847,18 +873,19 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     s1.start(p.layers[0].w1, valid ? row : 0, d, sub, valid);
     s3.start(p.layers[0].w3, valid ? row : 0, d, sub, valid);
     load_gains(gr, p.layers[0].ffn_norm, d);
-    float* xs = sm;
-    float* vin = C::WDT == kBF16 ? sm + ((d + 3) & ~3) : xs;  // product input (see put_pair)
+    float* const vin = sm;  // product input (see put_pair)
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         wait_sample<4, true>(p.ll_x2 + c.rep, d, c.ep(l, 2), c.err);
-        block_fetch2<2>(Seg{p.ll_x2 + c.rep, d, c.ep(l, 2), xs}, c.err);
-        const float rn = block_norm<C::WDT>(xs, d, gr, s.eps, sm, vin);
+        float xv[kPNorm];
+        block_fetch_own(Seg{p.ll_x2 + c.rep, d, c.ep(l, 2), nullptr}, xv, c.err);
+        const float rn = block_norm_regs<C::WDT>(xv, d, gr, s.eps, sm, vin);
         XRegs<C::WDT, C::NCD> xr;
         xr.load(vin, d, sub, G);
         const float a = rn * s1.finish(xr);
         const float u = rn * s3.finish(xr);
-        if (valid && sub < C::LLR) ll_put(p.ll_h + sub * p.rstride + row, (a / (1.0f + expf(-a))) * u, c.ep(l, 3));
+        if (valid && sub < C::LLR)
+            ll_put(p.ll_h + sub * p.rstride + row, a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * u, c.ep(l, 3));
         if (l + 1 < s.L) {
             s1.start(p.layers[l + 1].w1, valid ? row : 0, d, sub, valid);
             s3.start(p.layers[l + 1].w3, valid ? row : 0, d, sub, valid);
@@ -968,13 +995,13 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         sa.start(p.wcls, min(ta * R + rs, s.V - 1), s.d, sub, ta * R + rs < s.V);
         sb.start(p.wcls, min(tb * R + rs, s.V - 1), s.d, sub, tb * R + rs < s.V);
         load_gains(gr, p.out_norm, s.d);
-        float* xs = sm;
-        float* vin = C::WDT == kBF16 ? sm + ((s.d + 3) & ~3) : xs;  // product input (see put_pair)
+        float* const vin = sm;  // product input (see put_pair)
         __syncthreads();
         wait_word<32>(p.ll_late, c.ep(s.L - 1, 0), c.err);
         wait_sample<4, true>(p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), c.err);
-        block_fetch2<2>(Seg{p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), xs}, c.err);
-        const float rn = block_norm<C::WDT>(xs, s.d, gr, s.eps, sm, vin);
+        float xv[kPNorm];
+        block_fetch_own(Seg{p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), nullptr}, xv, c.err);
+        const float rn = block_norm_regs<C::WDT>(xv, s.d, gr, s.eps, sm, vin);
         XRegs<C::WDT, C::NCD> xr;
         xr.load(vin, s.d, sub, GD);
         uint64_t key = 0ull;
