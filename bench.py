@@ -255,7 +255,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 (bf16 weights widened in registers)",
+        "dtype": "f32 (fp32 accumulation; bf16 weights times fp32 activations as bf16 hi+lo pairs)",
         "data": "synthetic (seeded random weights N(0,0.02), uniform prompt ids)",
         "config": {"workload": w.name, "description": w.description, "batch": B, "ctx": w.ctx,
                    "decode_positions": [int(base.min()), int(base.max() + cycle - 1)],
