@@ -46,8 +46,9 @@ namespace ds {
 constexpr int kPBlocks = 256;
 constexpr int kPThreads = 256;                // 4 waves
 constexpr int kPWaves = kPBlocks * kPThreads / 64;
-constexpr int kPLds = 12288;                  // floats of LDS per block
-constexpr int kPRed = kPLds - 16;             // block-reduction slots at the end of LDS
+constexpr int kPLds = 13312;                  // floats of LDS per block
+constexpr int kPGains = kPLds - 1024;         // the final RMSNorm gains, loaded at the start
+constexpr int kPRed = kPGains - 16;           // block-reduction slots; the roles use LDS below them
 constexpr int kPNorm = 4;                     // normalised elements per thread (d <= 1024)
 constexpr long kPSpin = 1 << 20;              // poll rounds before a wait gives up
 constexpr int kPhases = 5;                    // epochs per layer
@@ -968,6 +969,12 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         c.tok = 0;
     }
     const Roles ro(s.d, s.H, s.Hkv, C::PD, s.F, C::GD, C::GH, C::GF, c.nch);
+    {
+        float g[kPNorm];
+        load_gains(g, p.out_norm, s.d);
+#pragma unroll
+        for (int j = 0; j < kPNorm; j++) sm[kPGains + min(own_elem(j), s.d - 1)] = g[j];  // read back by this thread
+    }
     int bt = blk;
     if (bt < ro.b[0]) {
         role_qkv<C>(s, p, c, bt, sm);
@@ -990,17 +997,25 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         const int ntask = (s.V + R - 1) / R;
         const int rs = lane / GD, sub = lane % GD;
         PStream<C::WDT, GD, C::NCD> sa, sb;
+        const int ta = gw, tb = gw + kPWaves;
+        // Workgroups without a layer role load their first two tasks now.  The
+        // others load theirs once x is in: a poll waits for every load before it.
+        const bool idle = blk >= ro.total();
+        auto start2 = [&]() {
+            sa.start(p.wcls, min(ta * R + rs, s.V - 1), s.d, sub, ta * R + rs < s.V);
+            sb.start(p.wcls, min(tb * R + rs, s.V - 1), s.d, sub, tb * R + rs < s.V);
+        };
+        if (idle) start2();
         float gr[kPNorm];
-        int ta = gw, tb = gw + kPWaves;
-        sa.start(p.wcls, min(ta * R + rs, s.V - 1), s.d, sub, ta * R + rs < s.V);
-        sb.start(p.wcls, min(tb * R + rs, s.V - 1), s.d, sub, tb * R + rs < s.V);
-        load_gains(gr, p.out_norm, s.d);
+#pragma unroll
+        for (int j = 0; j < kPNorm; j++) gr[j] = sm[kPGains + min(own_elem(j), s.d - 1)];  // this thread's own
         float* const vin = sm;  // product input (see put_pair)
         __syncthreads();
-        wait_word<32>(p.ll_late, c.ep(s.L - 1, 0), c.err);
+        if (idle) wait_word<32>(p.ll_late, c.ep(s.L - 1, 0), c.err);  // the others are past the last layer's start
         wait_sample<4, true>(p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), c.err);
         float xv[kPNorm];
         block_fetch_own(Seg{p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), nullptr}, xv, c.err);
+        if (!idle) start2();
         const float rn = block_norm_regs<C::WDT>(xv, s.d, gr, s.eps, sm, vin);
         XRegs<C::WDT, C::NCD> xr;
         xr.load(vin, s.d, sub, GD);
