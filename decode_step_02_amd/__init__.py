@@ -67,6 +67,7 @@ _SIGS = {
     "ds_kv_cache_check": (C.c_int, [_P, _P]),
     "ds_kv_cache_single_launch_ctx": (C.c_int32, [_P]),
     "ds_prefill": (C.c_int, [_P, _P, C.c_int32, C.POINTER(C.c_int32), C.c_int32, _P, _P]),
+    "ds_prefill_batched": (C.c_int, [_P, _P, C.c_int32, C.POINTER(C.c_int32), C.c_int32, _P, _P]),
     "ds_prefill_batch": (C.c_int, [_P, _P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), _P, _P]),
     "ds_decode_step": (C.c_int, [_P, _P, _P, _P, _P]),
     "ds_logits": (C.c_int, [_P, _P, _P]),
@@ -172,6 +173,10 @@ def ds_prefill(model, kv, seq, tokens, d_tok_out=None, stream=None):
     _check(_lib.ds_prefill(model, kv, seq, _i32(tokens), len(tokens), _ptr(d_tok_out), _stream(stream)))
 
 
+def ds_prefill_batched(model, kv, seq, tokens, d_tok_out=None, stream=None):
+    _check(_lib.ds_prefill_batched(model, kv, seq, _i32(tokens), len(tokens), _ptr(d_tok_out), _stream(stream)))
+
+
 def ds_prefill_batch(model, kv, token_lists, d_tok_out=None, stream=None):
     flat = [int(t) for toks in token_lists for t in toks]
     counts = [len(toks) for toks in token_lists]
@@ -263,6 +268,9 @@ class KVCache:
 
     def prefill(self, seq, tokens, d_tok_out=None, stream=None):
         ds_prefill(self.model.handle, self.handle, seq, tokens, d_tok_out, stream)
+
+    def prefill_batched(self, seq, tokens, d_tok_out=None, stream=None):
+        ds_prefill_batched(self.model.handle, self.handle, seq, tokens, d_tok_out, stream)
 
     def prefill_batch(self, token_lists, d_tok_out=None, stream=None):
         ds_prefill_batch(self.model.handle, self.handle, token_lists, d_tok_out, stream)

@@ -124,17 +124,19 @@ WsLayout ws_layout(const ds_config* c, int B, int T) {
         p = round_up(p + bytes, kAlign);
         return at;
     };
-    w.x = take(sizeof(float) * B * c->dim);
-    w.q = take(sizeof(float) * B * HD);
-    w.o = take(sizeof(float) * B * HD);
-    w.h = take(sizeof(float) * B * c->hidden_dim);
-    w.part_o = take(sizeof(float) * B * c->n_heads * S * c->head_dim);
-    w.part_ml = take(sizeof(float) * B * c->n_heads * S * 2);
-    w.logits = take(sizeof(float) * B * static_cast<size_t>(c->vocab_size));
+    // per-item rows: B for a decode step, up to kMaxItems positions for a batched prefill
+    const size_t BI = std::max(B, ds::kMaxItems);
+    w.x = take(sizeof(float) * BI * c->dim);
+    w.q = take(sizeof(float) * BI * HD);
+    w.o = take(sizeof(float) * BI * HD);
+    w.h = take(sizeof(float) * BI * c->hidden_dim);
+    w.part_o = take(sizeof(float) * BI * c->n_heads * S * c->head_dim);
+    w.part_ml = take(sizeof(float) * BI * c->n_heads * S * 2);
+    w.logits = take(sizeof(float) * B * static_cast<size_t>(c->vocab_size));  // by slot
     w.keys = take(sizeof(unsigned long long) * B * static_cast<size_t>(ds::kMaxArgmaxBlocks));
-    w.slot = take(sizeof(int32_t) * B);
-    w.pos = take(sizeof(int32_t) * B);
-    w.flag = take(sizeof(int32_t) * B);
+    w.slot = take(sizeof(int32_t) * BI);
+    w.pos = take(sizeof(int32_t) * BI);
+    w.flag = take(sizeof(int32_t) * BI);
     w.err = take(sizeof(int32_t));
     w.rope_cos = take(sizeof(float) * T * (c->head_dim / 2));
     w.rope_sin = take(sizeof(float) * T * (c->head_dim / 2));
@@ -511,6 +513,42 @@ ds_status ds_prefill(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_t
     }
     kv->mirror[seq] += n;
     return ok();
+}
+
+ds_status ds_prefill_batched(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_tokens, int32_t n,
+                             int32_t* d_tok_out, void* stream) {
+    if (!model || !kv || kv->model != model) return fail(DS_ERR_INVALID_ARG, "model/kv mismatch");
+    if (seq < 0 || seq >= kv->B) return fail(DS_ERR_INVALID_ARG, "seq %d outside [0, %d)", seq, kv->B);
+    if (n <= 0 || !h_tokens) return fail(DS_ERR_INVALID_ARG, "need n > 0 host tokens");
+    if (kv->mirror[seq] + static_cast<int64_t>(n) > kv->T)
+        return fail(DS_ERR_CONTEXT_FULL, "sequence %d has %d of %d positions; %d more do not fit", seq,
+                    kv->mirror[seq], kv->T, n);
+    for (int j = 0; j < n; j++)
+        if (h_tokens[j] < 0 || h_tokens[j] >= kv->s.V)
+            return fail(DS_ERR_BAD_TOKEN, "token %d at %d outside [0, %d)", h_tokens[j], j, kv->s.V);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // positions 0 .. n-2: up to kMaxItems at a time as the items of one step
+    // (projections as GEMMs over the positions, each item attending over the
+    // rows up to its own position), no logits
+    for (int done = 0; done < n - 1;) {
+        const int m = std::min(n - 1 - done, ds::kMaxItems);
+        ds::BeginList list;
+        list.n = m;
+        list.item0 = 0;
+        list.by_value = 1;
+        for (int i = 0; i < m; i++) {
+            list.slot[i] = seq;
+            list.tok[i] = h_tokens[done + i];
+            list.last[i] = 0;
+            list.off[i] = i;
+        }
+        hipError_t e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, nullptr, m, false, 0, nullptr, st);
+        if (e != hipSuccess) return hip_fail(e, "batched prefill");
+        kv->mirror[seq] += m;
+        done += m;
+    }
+    // the last position as in ds_prefill: its logits and token
+    return ds_prefill(model, kv, seq, h_tokens + (n - 1), 1, d_tok_out, stream);
 }
 
 ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens, const int32_t* h_counts,

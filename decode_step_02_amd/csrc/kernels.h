@@ -96,6 +96,7 @@ struct BeginList {
     int32_t slot[kMaxItems];
     int32_t tok[kMaxItems];
     int32_t last[kMaxItems];
+    int32_t off[kMaxItems] = {};  // by_value: position = lengths[slot] + off (several positions of one slot)
 };
 
 struct SetList {

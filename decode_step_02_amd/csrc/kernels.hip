@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs s, BeginList list, const
         if (threadIdx.x == 0) atomicOr(s.err, 1);
         tok = 0;
     }
-    const int pos = s.lengths[slot];
+    const int pos = s.lengths[slot] + (list.by_value ? list.off[li] : 0);
     if (threadIdx.x == 0) {
         s.slot[item] = slot;
         s.pos[item] = pos;
@@ -794,7 +794,8 @@ __global__ __launch_bounds__(256) void k_finalize(StepArgs s, int n_blocks, int3
             d_tok_out[slot] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k));
         }
     }
-    if (threadIdx.x == 0) s.lengths[slot] = s.pos[item] + 1;
+    // items of one slot (consecutive positions of a prompt) leave the largest
+    if (threadIdx.x == 0) atomicMax(s.lengths + slot, s.pos[item] + 1);
 }
 
 // ---- small utility kernels ------------------------------------------------------------------------

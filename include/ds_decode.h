@@ -148,6 +148,20 @@ ds_status ds_kv_cache_check(ds_kv* kv, void* stream);
 ds_status ds_prefill(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_tokens, int32_t n,
                      int32_t* d_tok_out, void* stream);
 
+/* The same result as ds_prefill (within floating-point rounding), with the
+ * prompt's positions run side by side: positions 0 .. n-2 go through the
+ * layers as the items of one pass, up to 64 at a time (the projections as
+ * matrix products over the positions, each position attending over the
+ * cached rows up to and including its own), then the last position runs as
+ * in ds_prefill and gives the token and logits.  This is the whole-prompt
+ * forward pass with the query count above one of "Inside nanochat Part 4",
+ * sections "Attention Mechanism Integration" and "Phase 1: Single Prefill".
+ * Arguments, ownership and errors as for ds_prefill; lengths[seq] grows by n.
+ * The result differs from ds_prefill's in rounding only (the projections of
+ * 16 or more positions accumulate in another order). */
+ds_status ds_prefill_batched(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_tokens, int32_t n,
+                             int32_t* d_tok_out, void* stream);
+
 /* Ragged prefill of many sequences at once: sequence b receives
  * h_counts[b] >= 0 tokens, taken in order from h_tokens (the concatenation
  * over b).  Position by position, every sequence that still has tokens is

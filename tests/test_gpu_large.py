@@ -69,7 +69,11 @@ def check_rows(cache_view, b, rows, what):
     return worst
 
 
-def test_135m_1000_token_context():
+@pytest.mark.parametrize("batched", [False, True], ids=["per_position", "batched"])
+def test_135m_1000_token_context(batched):
+    """The 1000-token prompt through ds_prefill (one position per pass) or
+    ds_prefill_batched (positions as the items of a pass)."""
+    import time
     import torch
     import decode_step_02_amd as dsa
     g = _golden("llama135m_p1000")
@@ -81,8 +85,12 @@ def test_135m_1000_token_context():
     kv = dsa.KVCache(model, 1, w.ctx)
     kv.cache.fill_(float("nan"))
     tok = torch.zeros(1, dtype=torch.int32, device="cuda")
-    kv.prefill(0, [int(t) for t in prompt], tok)
-    _say("prefilled 1000 positions")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    (kv.prefill_batched if batched else kv.prefill)(0, [int(t) for t in prompt], tok)
+    torch.cuda.synchronize()
+    _say(f"prefilled 1000 positions ({'batched' if batched else 'per position'}) in "
+         f"{(time.perf_counter() - t0) * 1e3:.1f} ms")
     steps, idx = g["steps"], g["sample_idx"]
     worst, ties = check_step(kv.logits().cpu().numpy()[0], tok.item(), steps[0], idx, "prefill")
     for k in range(1, len(steps)):
@@ -95,7 +103,8 @@ def test_135m_1000_token_context():
     cv = kv.cache_view().cpu().numpy()
     rows = check_rows(cv, 0, g["cache_rows"], "p1000")
     assert np.all(np.isnan(cv[:, :, 0, :, 1023:]))
-    _say(f"p1000: max|dlogit| {worst:.2e}, near-ties {ties}, max|dcache| {rows:.2e}")
+    _say(f"p1000 {'batched' if batched else 'per position'}: max|dlogit| {worst:.2e}, near-ties {ties}, "
+         f"max|dcache| {rows:.2e}")
 
 
 def test_135m_batch64_ragged():
@@ -183,6 +192,16 @@ def test_8b_full_size():
     kv.prefill(0, [int(t) for t in prompt], tok)
     _say("8b: prefilled 4096 positions")
     rows = check_rows(kv.cache_view().cpu().numpy(), 0, g["prefill_rows"], "8b prefill rows")
+    # the same prompt through the batched prefill, in a second cache
+    kv2 = dsa.KVCache(model, 1, w.ctx)
+    kv2.cache.fill_(float("nan"))
+    tok2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kv2.prefill_batched(0, [int(t) for t in prompt], tok2)
+    rows2 = check_rows(kv2.cache_view().cpu().numpy(), 0, g["prefill_rows"], "8b batched prefill rows")
+    assert kv2.lengths.item() == 4096 and bool(torch.isnan(kv2.cache_view()[:, :, 0, :, 4096:]).all())
+    kv2.check()
+    kv2.close()
+    _say(f"8b: batched prefill max|dcache| {rows2:.2e}")
     for _ in range(w.decode_calls):
         kv.decode_step(tok, tok)
         lg = kv.logits()

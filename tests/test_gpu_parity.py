@@ -30,10 +30,12 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def gpu_run(shape, arena, prompts, feed, T, dispatch=1, use_batch_prefill=True, stream=None):
-    """Prefill the prompts, then one decode step per entry of `feed` (tokens
-    for every sequence).  Returns first tokens/logits, per-step tokens/logits,
-    the cache and lengths as numpy arrays."""
+def gpu_run(shape, arena, prompts, feed, T, dispatch=1, use_batch_prefill=True, stream=None, batched=False):
+    """Prefill the prompts (ds_prefill_batch over the sequences, ds_prefill
+    per sequence, or with `batched` ds_prefill_batched per sequence), then one
+    decode step per entry of `feed` (tokens for every sequence).  Returns
+    first tokens/logits, per-step tokens/logits, the cache and lengths as
+    numpy arrays."""
     torch = _torch()
     import decode_step_02_amd as dsa
     B = len(prompts)
@@ -42,7 +44,10 @@ def gpu_run(shape, arena, prompts, feed, T, dispatch=1, use_batch_prefill=True, 
     kv.set_dispatch(dispatch)
     kv.cache.fill_(float("nan"))
     tok_out = torch.full((B,), -7, dtype=torch.int32, device="cuda")
-    if use_batch_prefill:
+    if batched:
+        for b, p in enumerate(prompts):
+            kv.prefill_batched(b, [int(t) for t in p], tok_out, stream)
+    elif use_batch_prefill:
         kv.prefill_batch([list(p) for p in prompts], tok_out, stream)
     else:
         for b, p in enumerate(prompts):
@@ -148,6 +153,18 @@ def test_ragged_batch_tiny_matches_oracle():
     compare(shape, arena, prompts, 3, 128, "tiny ragged B=7 per-slot prefill", use_batch_prefill=False)
 
 
+def test_batched_prefill_tiny_matches_oracle():
+    """ds_prefill_batched: prompt positions as the items of one pass (up to 64
+    at a time), each attending over the rows up to its own position.  Prompt
+    lengths cover 1 (no batched part), 2, one item under and over the
+    16-item MFMA threshold, exactly 64 + 1, and two chunks plus a tail."""
+    shape = synth.small_shape(n_kv_heads=2, head_dim=32, dim=128, n_heads=4)
+    arena = synth.make_arena(shape, 9, std=0.15, gain_sigma=0.1)
+    lens = [1, 2, 16, 17, 65, 130]
+    prompts = [synth.random_tokens(300 + i, n, shape.vocab_size) for i, n in enumerate(lens)]
+    compare(shape, arena, prompts, 3, 192, "tiny batched prefill", batched=True)
+
+
 def test_attention_chunk_boundaries_tiny():
     """Lengths around multiples of the 64-position attention chunk, up to T."""
     shape = synth.small_shape(n_kv_heads=2, head_dim=32, dim=128, n_heads=4)
@@ -193,6 +210,14 @@ def test_errors_are_reported_without_enqueueing():
 
 MM_SHAPE = synth.small_shape(dim=128, n_heads=4, n_kv_heads=2, head_dim=32, hidden_dim=256, vocab_size=512,
                              weight_dtype=synth.BF16)
+
+
+def test_batched_prefill_bf16_mfma_matches_oracle():
+    """bf16 weights: 16 or more positions take the MFMA projections."""
+    arena = synth.make_arena(MM_SHAPE, 12, std=0.1, gain_sigma=0.1)
+    lens = [40, 3, 100]
+    prompts = [synth.random_tokens(400 + i, n, MM_SHAPE.vocab_size) for i, n in enumerate(lens)]
+    compare(MM_SHAPE, arena, prompts, 2, 128, "bf16 batched prefill", batched=True)
 
 
 @pytest.mark.parametrize("B", [20, 70])
