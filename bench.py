@@ -118,6 +118,44 @@ def cpu_baseline(w: synth.Workload, arena: np.ndarray, budget_s: float) -> dict:
                       f"{len(prompt) + w.decode_calls - 1}, cycled) on one host thread, {dt:.1f} s"}
 
 
+def prefill_bench(dsa, torch, model, w, prompt, stream, reps, per_position=True):
+    """Prompt prefill of one sequence into an empty batch-1 cache: the batched
+    prefill (median of `reps` runs after one warm-up) and the one-position-
+    per-pass prefill (one run after one warm-up), both timed with events on
+    `stream` around the call."""
+    toks = [int(t) for t in prompt]
+    n = len(toks)
+    kv = dsa.KVCache(model, 1, w.ctx)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        kv.reset(0, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn(0, toks, out, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    timed(kv.prefill_batched)
+    ms_b = sorted(timed(kv.prefill_batched) for _ in range(reps))[reps // 2]
+    tok_b = int(out.item())
+    ms_p, tok_p = float("nan"), tok_b
+    if per_position:
+        timed(kv.prefill)
+        ms_p = timed(kv.prefill)
+        tok_p = int(out.item())
+    kv.check(stream)
+    kv.close()
+    return {"metric": f"prefill tok/s ({w.name}, prompt of {n})", "value": n / (ms_b * 1e-3), "unit": "tok/s",
+            "n_gpus": 1, "higher_is_better": True, "ms_per_prefill": ms_b, "reps": reps,
+            "per_position": {"value": n / (ms_p * 1e-3), "ms_per_prefill": ms_p},
+            "speedup": ms_p / ms_b, "same_first_token": tok_b == tok_p,
+            "dtype": "f32 (fp32 accumulation; bf16 weights times fp32 activations as bf16 hi+lo pairs)",
+            "data": "synthetic (seeded random weights N(0,0.02), uniform prompt ids)",
+            "config": {"workload": w.name, "prompt_len": n, "ctx": w.ctx, "batch": 1}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +166,13 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure the prompt prefill of the workload's first prompt instead of decode steps: "
+                         "ds_prefill_batched (positions as the items of a pass) against ds_prefill (one "
+                         "position per pass); prints a prefill tok/s line")
+    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--prefill-batched-only", action="store_true",
+                    help="with --prefill: skip the one-position-per-pass prefill (for kernel profiles)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain copy kernel (read N MB, write N MB) three times, as the "
                          "known-size reference for hardware byte counters; its rate is reported")
@@ -164,6 +209,10 @@ def main():
                         "GBps": 8 * n / (us * 1e-6) / 1e9}
             del src, dst
         model = dsa.Model(m, arena)
+        if args.prefill:
+            print(json.dumps(prefill_bench(dsa, torch, model, w, prompts[0], stream, args.prefill_reps,
+                                           not args.prefill_batched_only)))
+            return
         kv = dsa.KVCache(model, B, w.ctx)
         kv.set_dispatch(1 if args.dispatch == "graph" else 0)
         tok = torch.zeros(B, dtype=torch.int32, device="cuda")

@@ -59,6 +59,9 @@ __global__ __launch_bounds__(256) void k_mm(StepArgs s, LayerW w, int layer, int
     float* gs = reinterpret_cast<float*>(xl + kMmItems * LDK);  // gains [K] (NORM kinds)
     __shared__ float rn[kMmItems];
     __shared__ unsigned long long kred[4][kMmItems];
+    // blockIdx.y picks this block's group of 16 * NG items
+    m0 += static_cast<int>(blockIdx.y) * 16 * NG;
+    n_items = min(n_items - static_cast<int>(blockIdx.y) * 16 * NG, 16 * NG);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int tile = blockIdx.x * 4 + wave;
     const int ti = lane & 15, kq = lane >> 4;
@@ -315,8 +318,12 @@ static hipError_t launch_kind(const StepArgs& s, const LayerW& w, int layer, int
     if (KIND == MM_W13) N = s.F;
     if (KIND == MM_LOGITS) N = s.V;
     constexpr bool norm = KIND == MM_QKV || KIND == MM_W13 || KIND == MM_LOGITS;
-    const dim3 grid((N + 63) / 64);
-    const int ng = (n + 15) / 16;
+    // Few row blocks (every matrix but the vocabulary one): one block per 16
+    // items as well, which fills more CUs at the price of reading each
+    // weight tile once per item group.
+    const int nbx = (N + 63) / 64;
+    const int ng = nbx < 128 ? 1 : (n + 15) / 16;
+    const dim3 grid(nbx, (n + 16 * ng - 1) / (16 * ng));
     const int kt = pick_kt(K);
     const size_t lds = mm_lds(kt, norm, K);
     switch (kt) {
