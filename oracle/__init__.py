@@ -66,6 +66,8 @@ def load(path: str = LIB):
         "orc_attend": (None, [_F, _F, _F, C.c_int32, C.c_int32, _F, _F]),
         "orc_silu_mul": (C.c_float, [C.c_float, C.c_float]),
         "orc_argmax": (C.c_int32, [_F, C.c_int32]),
+        "orc_sample": (C.c_int32, [_F, C.c_int32, C.c_float, C.c_int32, C.c_float, C.c_double, _I,
+                                   C.POINTER(C.c_double), C.POINTER(C.c_int32)]),
         "orc_n_tensors": (C.c_int32, [P]),
         "orc_tensor_offsets": (C.c_size_t, [P, C.POINTER(C.c_size_t), C.c_int32]),
         "orc_cache_index": (C.c_size_t, [P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
@@ -141,6 +143,20 @@ def attend(q, K, V):
 def argmax(v):
     v = np.ascontiguousarray(v, np.float32)
     return int(lib().orc_argmax(v, len(v)))
+
+
+def sample(logits, temperature, top_k, top_p, u):
+    """orc_sample: (token, kept candidates in draw order, their normalised
+    cumulative weights)."""
+    v = np.ascontiguousarray(logits, np.float32)
+    cand = np.zeros(len(v), np.int32)
+    cum = np.zeros(len(v), np.float64)
+    n = C.c_int32(0)
+    tok = lib().orc_sample(v, len(v), float(temperature), int(top_k), float(top_p), float(u), cand,
+                           cum.ctypes.data_as(C.POINTER(C.c_double)), C.byref(n))
+    if tok < 0:
+        raise ValueError("orc_sample: bad argument")
+    return int(tok), cand[:n.value].copy(), cum[:n.value].copy()
 
 
 def tensor_offsets(shape):

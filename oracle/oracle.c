@@ -159,6 +159,85 @@ int32_t orc_argmax(const float* v, int32_t n) {
     return best;
 }
 
+/* [NANO] "Sampling Strategy" ("Temperature Sampling", "Top-K Filtering",
+ * "Combined Temperature and Top-K") and [KAS] "CLI flags" (--top-p):
+ * one draw from the logits.
+ *  - temperature == 0: the greedy token (orc_argmax); *n_out = 1.
+ *  - top_k >= 1: the candidates are the min(top_k, V) largest logits, in
+ *    the order largest first (equal logits: lower index first).  Each gets
+ *    the weight exp((l_j - l_0) / temperature) (binary64; l_0 is the
+ *    largest, so the softmax is unchanged).  top_p < 1 keeps the shortest
+ *    prefix whose weight sum reaches top_p times the sum of all candidate
+ *    weights (the nucleus reading of --top-p, applied after top-k).
+ *  - top_k == 0: every token, in index order, with those weights; top_p
+ *    must be 1.
+ * The draw is the inverse distribution function at u in [0, 1): the first
+ * kept candidate j whose cumulative weight exceeds u times the kept total
+ * (the last kept candidate if rounding leaves none).  cand[] gets the
+ * candidates in draw order and cum[] their cumulative weights divided by
+ * the kept total (both of length *n_out, the kept count).  Returns the
+ * token, or -1 on a bad argument. */
+static int cmp_desc(const void* a, const void* b) {
+    const float* x = (const float*)a;
+    const float* y = (const float*)b;
+    if (x[0] > y[0]) return -1;
+    if (x[0] < y[0]) return 1;
+    return x[1] < y[1] ? -1 : (x[1] > y[1] ? 1 : 0);  /* lower index first */
+}
+
+int32_t orc_sample(const float* logits, int32_t V, float temperature, int32_t top_k, float top_p,
+                   double u, int32_t* cand, double* cum, int32_t* n_out) {
+    if (V <= 0 || !(temperature >= 0.0f) || top_k < 0 || !(top_p > 0.0f && top_p <= 1.0f) ||
+        !(u >= 0.0 && u < 1.0) || (top_k == 0 && top_p < 1.0f))
+        return -1;
+    if (temperature == 0.0f) {
+        cand[0] = orc_argmax(logits, V);
+        cum[0] = 1.0;
+        *n_out = 1;
+        return cand[0];
+    }
+    int32_t n = V;
+    if (top_k >= 1) {
+        /* (value, index) pairs sorted; indices below 2^24 are exact as float */
+        float* pr = (float*)malloc(sizeof(float) * 2 * (size_t)V);
+        if (!pr) return -1;
+        for (int32_t i = 0; i < V; i++) {
+            pr[2 * i] = logits[i];
+            pr[2 * i + 1] = (float)i;
+        }
+        qsort(pr, (size_t)V, 2 * sizeof(float), cmp_desc);
+        n = top_k < V ? top_k : V;
+        for (int32_t j = 0; j < n; j++) cand[j] = (int32_t)pr[2 * j + 1];
+        free(pr);
+    } else {
+        for (int32_t j = 0; j < V; j++) cand[j] = j;
+    }
+    double lmax = logits[cand[0]];
+    if (top_k == 0)
+        for (int32_t j = 1; j < n; j++)
+            if (logits[j] > lmax) lmax = logits[j];
+    double tot = 0.0;
+    for (int32_t j = 0; j < n; j++) {
+        tot += exp(((double)logits[cand[j]] - lmax) / (double)temperature);
+        cum[j] = tot;
+    }
+    int32_t kept = n;
+    if (top_p < 1.0f) {
+        kept = 1;
+        while (kept < n && cum[kept - 1] < (double)top_p * tot) kept++;
+    }
+    const double total = cum[kept - 1];
+    int32_t pick = kept - 1;
+    for (int32_t j = 0; j < kept; j++)
+        if (cum[j] > u * total) {
+            pick = j;
+            break;
+        }
+    for (int32_t j = 0; j < kept; j++) cum[j] /= total;
+    *n_out = kept;
+    return cand[pick];
+}
+
 /* ---- arena layout: [KAS] "On-disk model format (.sllm)" order ----------- */
 enum { ORC_ALIGN = 256 };
 enum { T_ATTN_NORM = 0, T_WQ, T_WK, T_WV, T_WO, T_FFN_NORM, T_W1, T_W3, T_W2, T_PER_LAYER };

@@ -42,6 +42,11 @@ void orc_attend(const float* q, const float* K, const float* V, int32_t n, int32
                 float* probs, float* out);
 float orc_silu_mul(float a, float u);
 int32_t orc_argmax(const float* v, int32_t n);
+/* One sampled token (temperature, top-k, top-p, the uniform draw u); the
+ * kept candidates in draw order and their normalised cumulative weights go
+ * to cand / cum (room for V entries each). */
+int32_t orc_sample(const float* logits, int32_t V, float temperature, int32_t top_k, float top_p,
+                   double u, int32_t* cand, double* cum, int32_t* n_out);
 
 /* ---- arena and cache layout ------------------------------------------ */
 int32_t orc_n_tensors(const orc_config* c);
