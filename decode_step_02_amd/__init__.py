@@ -71,6 +71,7 @@ _SIGS = {
     "ds_prefill_batch": (C.c_int, [_P, _P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), _P, _P]),
     "ds_decode_step": (C.c_int, [_P, _P, _P, _P, _P]),
     "ds_logits": (C.c_int, [_P, _P, _P]),
+    "ds_sample": (C.c_int, [_P, _P, C.c_float, C.c_int32, C.c_float, _P, _P]),
     "ds_set_dispatch": (C.c_int, [_P, C.c_int32]),
     "ds_bench_kernel": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, _P]),
     "ds_last_error": (C.c_char_p, []),
@@ -277,6 +278,12 @@ class KVCache:
 
     def decode_step(self, d_tok_in, d_tok_out, stream=None):
         ds_decode_step(self.model.handle, self.handle, d_tok_in, d_tok_out, stream)
+
+    def sample(self, d_uniform, temperature, top_k, top_p, d_tok_out, stream=None):
+        """Draw one token per sequence from the last step's logits (ds_sample):
+        d_uniform is a device float32[B] of uniforms in [0, 1)."""
+        _check(_lib.ds_sample(self.handle, _ptr(d_uniform), float(temperature), int(top_k), float(top_p),
+                              _ptr(d_tok_out), _stream(stream)))
 
     def logits(self, stream=None):
         ds_logits(self.handle, self.logits_buf, stream)

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libds_decode.so")
-SOURCES = ["kernels.hip", "mfma.hip", "persist.hip", "api.hip"]
+SOURCES = ["kernels.hip", "mfma.hip", "persist.hip", "sample.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

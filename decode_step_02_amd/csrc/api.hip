@@ -686,6 +686,26 @@ ds_status ds_logits(const ds_kv* kv, float* d_out, void* stream) {
     return ok();
 }
 
+ds_status ds_sample(const ds_kv* kv, const float* d_uniform, float temperature, int32_t top_k, float top_p,
+                    int32_t* d_tok_out, void* stream) {
+    if (!kv || !d_uniform || !d_tok_out) return fail(DS_ERR_INVALID_ARG, "NULL argument");
+    if (!aligned(d_uniform, 4) || !aligned(d_tok_out, 4)) return fail(DS_ERR_ALIGNMENT, "uniform / token buffers");
+    if (!(temperature > 0.0f) || !(temperature < INFINITY))
+        return fail(DS_ERR_INVALID_ARG, "temperature %g: needs 0 < t < inf (0 is the greedy step itself)",
+                    static_cast<double>(temperature));
+    if (top_k < 0) return fail(DS_ERR_INVALID_ARG, "top_k %d < 0", top_k);
+    if (!(top_p > 0.0f && top_p <= 1.0f))
+        return fail(DS_ERR_INVALID_ARG, "top_p %g outside (0, 1]", static_cast<double>(top_p));
+    const int k = std::min(top_k, kv->s.V);
+    if (k > ds::kMaxTopK) return fail(DS_ERR_UNSUPPORTED, "top_k %d above %d", top_k, ds::kMaxTopK);
+    if (k == 0 && top_p < 1.0f) return fail(DS_ERR_UNSUPPORTED, "top_p below 1 needs top_k >= 1");
+    const ds::SampleParams prm{temperature, k, top_p};
+    hipError_t e = ds::enqueue_sample(kv->s.logits, kv->B, kv->s.V, d_uniform, prm, d_tok_out,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sample");
+    return ok();
+}
+
 ds_status ds_set_dispatch(ds_kv* kv, int32_t mode) {
     if (!kv) return fail(DS_ERR_INVALID_ARG, "kv is NULL");
     if (mode != 0 && mode != 1) return fail(DS_ERR_INVALID_ARG, "mode must be 0 (eager) or 1 (graph)");

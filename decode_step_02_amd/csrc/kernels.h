@@ -19,7 +19,8 @@ constexpr int kSetChunk = 128;   // lengths per k_set_lengths launch
 constexpr int kMaxArgmaxBlocks = 16384;  // vocabulary blocks per item (argmax partials)
 constexpr int kPMaxChunks = 16;  // attention chunks the persistent step can hold per head
 constexpr int kPKeyWords = 1024; // argmax words of the persistent step (one per wave)
-constexpr int kPRep = 8;          // most replicas of a vector the persistent step publishes
+constexpr int kPRep = 8;
+constexpr int kMaxTopK = 1024;   // largest top-k of the sampling epilogue          // most replicas of a vector the persistent step publishes
 constexpr int kMmItems = 64;     // items per MFMA launch
 constexpr int kMmMin = 16;       // steps with at least this many items use the MFMA projections
 
@@ -153,5 +154,15 @@ hipError_t mm_gemv(int which, const StepArgs& s, const LayerW& w, int layer, int
 // Longest context (a power of two <= min(kShort, T)) whose short-path staging fits in
 // 64 KiB of LDS; 0 if head_dim/4 is not a power of two.
 int short_positions(const StepArgs& s);
+
+// Sampling epilogue (sample.hip): temperature > 0, 0 <= top_k <= kMaxTopK
+// (0: every token), 0 < top_p <= 1 (below 1 only with top_k >= 1).
+struct SampleParams {
+    float temperature;
+    int top_k;
+    float top_p;
+};
+hipError_t enqueue_sample(const float* logits, int B, int V, const float* d_uniform, SampleParams prm,
+                          int32_t* d_tok_out, hipStream_t st);
 
 }  // namespace ds

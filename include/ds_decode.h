@@ -180,6 +180,30 @@ ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens,
 ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, int32_t* d_tok_out,
                          void* stream);
 
+/* Sampling epilogue ("Inside nanochat Part 4", section "Sampling Strategy":
+ * temperature scaling and top-k filtering; "simple-llm / kasahare", section
+ * "CLI flags": --top-p, read as the nucleus).  For every sequence b in
+ * [0, B) it draws one token from the logits the last ds_decode_step /
+ * ds_prefill left for b (rows of sequences that call did not advance hold
+ * older logits) and writes it to d_tok_out[b] (device int32[B]).
+ *  - The candidates: with top_k >= 1 the min(top_k, V) largest logits,
+ *    largest first (equal logits: lower index first); with top_k == 0
+ *    every token in index order.
+ *  - Weights exp((l - l_max) / temperature); top_p < 1 (needs top_k >= 1)
+ *    keeps the shortest prefix of the candidates whose weight reaches top_p
+ *    times their total.
+ *  - The draw is the inverse distribution function at d_uniform[b] (device
+ *    fp32[B], the caller's uniform numbers in [0, 1); values outside are
+ *    clamped into it): the first kept candidate whose running weight exceeds
+ *    d_uniform[b] times the kept total.
+ * Temperature 0 is greedy decoding, which ds_decode_step already does: pass
+ * temperature > 0 here.  Only enqueues work on `stream`.
+ * Errors: DS_ERR_INVALID_ARG (temperature <= 0, top_k < 0, top_p outside
+ * (0, 1]), DS_ERR_UNSUPPORTED (top_k above 1024, or top_p < 1 with
+ * top_k == 0), DS_ERR_ALIGNMENT. */
+ds_status ds_sample(const ds_kv* kv, const float* d_uniform, float temperature, int32_t top_k, float top_p,
+                    int32_t* d_tok_out, void* stream);
+
 /* Launch shape of batch-1 steps.  When B == 1 and the sequence holds at most
  * the returned number of positions after the step, ds_decode_step (and each
  * position of ds_prefill) runs as ONE persistent kernel launch that carries
