@@ -171,6 +171,9 @@ def main():
                          "ds_prefill_batched (positions as the items of a pass) against ds_prefill (one "
                          "position per pass); prints a prefill tok/s line")
     ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--sample", default="",
+                    help="T,K,P: after every decode step draw the next tokens with ds_sample (temperature T, "
+                         "top-k K, top-p P; seeded uniforms) instead of keeping the greedy ones")
     ap.add_argument("--prefill-batched-only", action="store_true",
                     help="with --prefill: skip the one-position-per-pass prefill (for kernel profiles)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -220,11 +223,19 @@ def main():
         base = np.array([len(p) for p in prompts], np.int32)
         cycle = w.decode_calls
 
+        samp = None
+        if args.sample:
+            st_, sk_, sp_ = args.sample.split(",")
+            samp = (float(st_), int(sk_), float(sp_))
+            ubuf = torch.from_numpy(np.random.default_rng(5).random((64, B)).astype(np.float32)).cuda()
+
         def run(n, start):
             for i in range(start, start + n):
                 if i % cycle == 0 and i > 0:
                     kv.set_lengths(base)
                 kv.decode_step(tok, tok)
+                if samp:
+                    kv.sample(ubuf[i % 64], *samp, tok, stream)
 
         run(args.warmup, 0)
         kv.set_lengths(base)
@@ -237,6 +248,16 @@ def main():
         ms_total = ev0.elapsed_time(ev1)
         kv.check()
         ms_step = ms_total / args.steps
+
+        sampler_us = None
+        if samp:  # the sampling kernel alone, on the last step's logits
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for i in range(100):
+                kv.sample(ubuf[i % 64], *samp, tok, stream)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            sampler_us = s0.elapsed_time(s1) * 10.0
 
         lengths_seq = [base + (i % cycle) for i in range(cycle)]
         bytes_step = float(np.mean([step_bytes(m, L) for L in lengths_seq]))
@@ -294,7 +315,8 @@ def main():
     gbps = bytes_step / (ms_step * 1e-3) / 1e9
     traffic, traffic_note = measured_traffic(w.name) if single else (None, "counters taken for the single-launch step only")
     out = {
-        "metric": "decode tok/s (135M-shaped Llama, B=1)" if w.name == "llama135m_p5" else f"decode tok/s ({w.name})",
+        "metric": ("decode tok/s (135M-shaped Llama, B=1)" if w.name == "llama135m_p5" else f"decode tok/s ({w.name})")
+                  + (" with sampling" if samp else ""),
         "value": B * args.steps / (ms_total * 1e-3),
         "unit": "tok/s",
         "n_gpus": 1,
@@ -318,6 +340,9 @@ def main():
         "kernels_us_per_step": {n: round(v["us_per_step"], 2) for n, v in kern.items()},
         "traffic_note": traffic_note,
     }
+    if samp:
+        out["config"]["sampling"] = {"temperature": samp[0], "top_k": samp[1], "top_p": samp[2]}
+        out["sampler_us_per_call"] = sampler_us
     if copy_cal:
         out["copy_calibration"] = copy_cal
     if not args.no_cpu_baseline:

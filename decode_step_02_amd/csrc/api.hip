@@ -699,8 +699,11 @@ ds_status ds_sample(const ds_kv* kv, const float* d_uniform, float temperature, 
     const int k = std::min(top_k, kv->s.V);
     if (k > ds::kMaxTopK) return fail(DS_ERR_UNSUPPORTED, "top_k %d above %d", top_k, ds::kMaxTopK);
     if (k == 0 && top_p < 1.0f) return fail(DS_ERR_UNSUPPORTED, "top_p below 1 needs top_k >= 1");
+    if (kv->s.V > ds::kSampleMaxV) return fail(DS_ERR_UNSUPPORTED, "vocabulary %d above %d", kv->s.V, ds::kSampleMaxV);
     const ds::SampleParams prm{temperature, k, top_p};
-    hipError_t e = ds::enqueue_sample(kv->s.logits, kv->B, kv->s.V, d_uniform, prm, d_tok_out,
+    // scratch: the argmax-key rows of the workspace, which nothing reads between steps
+    hipError_t e = ds::enqueue_sample(kv->s.logits, kv->B, kv->s.V, d_uniform, prm,
+                                      reinterpret_cast<uint64_t*>(kv->s.keys), ds::kMaxArgmaxBlocks, d_tok_out,
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "sample");
     return ok();

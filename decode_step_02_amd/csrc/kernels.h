@@ -20,7 +20,8 @@ constexpr int kMaxArgmaxBlocks = 16384;  // vocabulary blocks per item (argmax p
 constexpr int kPMaxChunks = 16;  // attention chunks the persistent step can hold per head
 constexpr int kPKeyWords = 1024; // argmax words of the persistent step (one per wave)
 constexpr int kPRep = 8;
-constexpr int kMaxTopK = 1024;   // largest top-k of the sampling epilogue          // most replicas of a vector the persistent step publishes
+constexpr int kMaxTopK = 1024;   // largest top-k of the sampling epilogue
+constexpr int kSampleMaxV = 1 << 20;  // largest vocabulary of the sampling epilogue          // most replicas of a vector the persistent step publishes
 constexpr int kMmItems = 64;     // items per MFMA launch
 constexpr int kMmMin = 16;       // steps with at least this many items use the MFMA projections
 
@@ -162,7 +163,10 @@ struct SampleParams {
     int top_k;
     float top_p;
 };
+// scratch: row_words 64-bit words per row (at least sample_scratch_words()
+// for the two-kernel path; the argmax-key region of the workspace).
+size_t sample_scratch_words();
 hipError_t enqueue_sample(const float* logits, int B, int V, const float* d_uniform, SampleParams prm,
-                          int32_t* d_tok_out, hipStream_t st);
+                          uint64_t* scratch, size_t row_words, int32_t* d_tok_out, hipStream_t st);
 
 }  // namespace ds
