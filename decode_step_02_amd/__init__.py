@@ -64,6 +64,8 @@ _SIGS = {
     "ds_kv_cache_reset": (C.c_int, [_P, C.c_int32, _P]),
     "ds_kv_cache_set_lengths": (C.c_int, [_P, C.POINTER(C.c_int32), _P]),
     "ds_kv_cache_get_lengths": (C.c_int, [_P, C.POINTER(C.c_int32)]),
+    "ds_kv_cache_replicate": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, _P]),
+    "ds_decode_step_rows": (C.c_int, [_P, _P, C.POINTER(C.c_int32), C.c_int32, _P, _P, _P]),
     "ds_kv_cache_check": (C.c_int, [_P, _P]),
     "ds_kv_cache_single_launch_ctx": (C.c_int32, [_P]),
     "ds_prefill": (C.c_int, [_P, _P, C.c_int32, C.POINTER(C.c_int32), C.c_int32, _P, _P]),
@@ -278,6 +280,18 @@ class KVCache:
 
     def decode_step(self, d_tok_in, d_tok_out, stream=None):
         ds_decode_step(self.model.handle, self.handle, d_tok_in, d_tok_out, stream)
+
+    def replicate_from(self, src, src_seq, dst_first, count, stream=None):
+        """Copy sequence src_seq of cache `src` (a KVCache, possibly this one)
+        into sequences dst_first .. dst_first + count - 1 of this cache."""
+        _check(_lib.ds_kv_cache_replicate(self.handle, src.handle, int(src_seq), int(dst_first), int(count),
+                                          _stream(stream)))
+
+    def decode_step_rows(self, rows, d_tok_in, d_tok_out, stream=None):
+        """A decode step of the sequences in `rows` only."""
+        rows = [int(r) for r in rows]
+        _check(_lib.ds_decode_step_rows(self.model.handle, self.handle, _i32(rows) if rows else None, len(rows),
+                                        _ptr(d_tok_in), _ptr(d_tok_out), _stream(stream)))
 
     def sample(self, d_uniform, temperature, top_k, top_p, d_tok_out, stream=None):
         """Draw one token per sequence from the last step's logits (ds_sample):

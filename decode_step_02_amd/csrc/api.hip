@@ -457,6 +457,69 @@ ds_status ds_kv_cache_set_lengths(ds_kv* kv, const int32_t* h_lengths, void* str
     return ok();
 }
 
+ds_status ds_kv_cache_replicate(ds_kv* dst, const ds_kv* src, int32_t src_seq, int32_t dst_first, int32_t count,
+                                void* stream) {
+    if (!dst || !src) return fail(DS_ERR_INVALID_ARG, "NULL cache");
+    const ds_config& a = dst->model->cfg;
+    const ds_config& b = src->model->cfg;
+    if (a.n_layers != b.n_layers || a.n_kv_heads != b.n_kv_heads || a.head_dim != b.head_dim)
+        return fail(DS_ERR_INVALID_ARG, "caches of different layer / key-value head / head shapes");
+    if (src_seq < 0 || src_seq >= src->B) return fail(DS_ERR_INVALID_ARG, "src_seq %d outside [0, %d)", src_seq, src->B);
+    if (count < 0 || dst_first < 0 || dst_first + static_cast<int64_t>(count) > dst->B)
+        return fail(DS_ERR_INVALID_ARG, "slots [%d, %d + %d) outside [0, %d)", dst_first, dst_first, count, dst->B);
+    if (dst == src && src_seq >= dst_first && src_seq < dst_first + count)
+        return fail(DS_ERR_INVALID_ARG, "the source slot %d is among the destinations", src_seq);
+    const int n = src->mirror[src_seq];
+    if (n > dst->T) return fail(DS_ERR_CONTEXT_FULL, "%d positions do not fit a cache of %d", n, dst->T);
+    if (count == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = ds::enqueue_replicate(dst->cache, dst->B, dst->T, src->cache, src->B, src->T, a.n_layers,
+                                         a.n_kv_heads, a.head_dim, src_seq, dst_first, count, n, st);
+    std::vector<int32_t> len(static_cast<size_t>(count), n);
+    if (e == hipSuccess) e = ds::enqueue_set_lengths(dst->lengths, len.data(), dst_first, count, st);
+    if (e != hipSuccess) return hip_fail(e, "replicate");
+    for (int i = 0; i < count; i++) dst->mirror[dst_first + i] = n;
+    return ok();
+}
+
+ds_status ds_decode_step_rows(ds_model* model, ds_kv* kv, const int32_t* h_rows, int32_t n_rows,
+                              const int32_t* d_tok_in, int32_t* d_tok_out, void* stream) {
+    if (!model || !kv || kv->model != model) return fail(DS_ERR_INVALID_ARG, "model/kv mismatch");
+    if (!d_tok_in || !d_tok_out || (n_rows > 0 && !h_rows)) return fail(DS_ERR_INVALID_ARG, "NULL argument");
+    if (!aligned(d_tok_in, 4) || !aligned(d_tok_out, 4)) return fail(DS_ERR_ALIGNMENT, "token buffers");
+    if (n_rows < 0 || n_rows > kv->B) return fail(DS_ERR_INVALID_ARG, "n_rows %d outside [0, %d]", n_rows, kv->B);
+    std::vector<char> seen(static_cast<size_t>(kv->B), 0);
+    int max_ctx = 0;
+    for (int i = 0; i < n_rows; i++) {
+        const int r = h_rows[i];
+        if (r < 0 || r >= kv->B || seen[r]) return fail(DS_ERR_INVALID_ARG, "row %d repeated or outside [0, %d)", r, kv->B);
+        seen[r] = 1;
+        if (kv->mirror[r] >= kv->T)
+            return fail(DS_ERR_CONTEXT_FULL, "sequence %d already holds all %d positions", r, kv->T);
+        max_ctx = std::max(max_ctx, kv->mirror[r] + 1);
+    }
+    if (n_rows == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::vector<ds::BeginList> lists;
+    for (int i = 0; i < n_rows; i++) {
+        if (lists.empty() || lists.back().n == ds::kMaxItems) {
+            lists.emplace_back();
+            lists.back().item0 = i;
+            lists.back().by_value = 2;
+        }
+        ds::BeginList& l = lists.back();
+        l.slot[l.n] = h_rows[i];
+        l.tok[l.n] = 0;
+        l.last[l.n] = 1;
+        l.n++;
+    }
+    hipError_t e = ds::enqueue_step(kv->s, model->ptrs, lists.data(), static_cast<int>(lists.size()), d_tok_in, n_rows,
+                                    true, ds::short_rows(kv->s, max_ctx), d_tok_out, st);
+    if (e != hipSuccess) return hip_fail(e, "decode_step_rows");
+    for (int i = 0; i < n_rows; i++) kv->mirror[h_rows[i]] += 1;
+    return ok();
+}
+
 ds_status ds_kv_cache_get_lengths(const ds_kv* kv, int32_t* h_lengths) {
     if (!kv || !h_lengths) return fail(DS_ERR_INVALID_ARG, "NULL argument");
     std::memcpy(h_lengths, kv->mirror.data(), sizeof(int32_t) * kv->B);

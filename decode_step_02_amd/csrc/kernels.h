@@ -100,6 +100,15 @@ struct BeginList {
     int32_t last[kMaxItems];
     int32_t off[kMaxItems] = {};  // by_value: position = lengths[slot] + off (several positions of one slot)
 };
+// by_value: 0 items are the slots 0..n-1 with tokens d_tok_in[slot]; 1 slots
+// and tokens from the arrays (prefill); 2 slots from the array, tokens
+// d_tok_in[slot] (a decode step of some of the sequences).
+
+// Copies rows [0, n) of every (layer, k/v, group) of slot src_slot of one
+// (L, 2, Bs, Hkv, Ts, D) cache to slots dst_first .. dst_first + count - 1
+// of another (L, 2, Bd, Hkv, Td, D) cache (it may be the same one).
+hipError_t enqueue_replicate(float* dst, int Bd, int Td, const float* src, int Bs, int Ts, int L, int Hkv, int D,
+                             int src_slot, int dst_first, int count, int n, hipStream_t st);
 
 struct SetList {
     int first = 0;

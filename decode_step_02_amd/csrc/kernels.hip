@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs s, BeginList list, const
     if (li >= list.n) return;
     const int item = list.item0 + li;
     const int slot = list.by_value ? list.slot[li] : item;
-    int tok = list.by_value ? list.tok[li] : d_tok_in[slot];
+    int tok = list.by_value == 1 ? list.tok[li] : d_tok_in[slot];
     if (tok < 0 || tok >= s.V) {
         if (threadIdx.x == 0) atomicOr(s.err, 1);
         tok = 0;
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs s, BeginList list, const
     if (threadIdx.x == 0) {
         s.slot[item] = slot;
         s.pos[item] = pos;
-        s.flag[item] = list.by_value ? list.last[li] : 1;
+        s.flag[item] = list.by_value == 1 ? list.last[li] : 1;
     }
     float* x = s.x + static_cast<size_t>(item) * s.d;
     const size_t row = static_cast<size_t>(tok) * s.d;
@@ -799,6 +799,18 @@ __global__ __launch_bounds__(256) void k_finalize(StepArgs s, int n_blocks, int3
 }
 
 // ---- small utility kernels ------------------------------------------------------------------------
+// One (layer, k/v, group) and destination slot per block: rows [0, n) of the
+// source slot, n * D contiguous floats on both sides.
+__global__ void k_replicate(float* __restrict__ dst, int Bd, int Td, const float* __restrict__ src, int Bs, int Ts,
+                            int Hkv, int D, int src_slot, int dst_first, int n) {
+    const int lkg = blockIdx.x, c = blockIdx.y;
+    const int g = lkg % Hkv, lk = lkg / Hkv;  // lk = layer * 2 + k/v
+    const size_t so = ((static_cast<size_t>(lk) * Bs + src_slot) * Hkv + g) * static_cast<size_t>(Ts) * D;
+    const size_t dof = ((static_cast<size_t>(lk) * Bd + dst_first + c) * Hkv + g) * static_cast<size_t>(Td) * D;
+    const size_t m = static_cast<size_t>(n) * D;
+    for (size_t i = threadIdx.x; i < m; i += blockDim.x) dst[dof + i] = src[so + i];
+}
+
 __global__ void k_set_lengths(int32_t* lengths, SetList l) {
     for (int i = threadIdx.x; i < l.n; i += blockDim.x) lengths[l.first + i] = l.val[i];
 }
@@ -970,11 +982,19 @@ static hipError_t launch_attn(const StepArgs& s, int layer, int n_items, hipStre
 
 static bool use_mm(const StepArgs& s, int n_items) { return s.mm_ok && n_items >= kMmMin; }
 
+hipError_t enqueue_replicate(float* dst, int Bd, int Td, const float* src, int Bs, int Ts, int L, int Hkv, int D,
+                             int src_slot, int dst_first, int count, int n, hipStream_t st) {
+    if (count <= 0 || n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_replicate, dim3(L * 2 * Hkv, count), dim3(256), 0, st, dst, Bd, Td, src, Bs, Ts, Hkv, D,
+                       src_slot, dst_first, n);
+    return hipGetLastError();
+}
+
 hipError_t enqueue_step(const StepArgs& s, const ModelPtrs& m, const BeginList* lists, int n_lists,
                         const int32_t* d_tok_in, int n_items, bool need_logits, int nload,
                         int32_t* d_tok_out, hipStream_t st) {
     Launch lc;
-    lc.ident = d_tok_in != nullptr;
+    lc.ident = d_tok_in != nullptr && lists[0].by_value == 0;  // item == slot
     const bool mm = use_mm(s, n_items);
     lc.nload = mm ? 0 : nload;  // the MFMA path always takes the split-K attention
     hipError_t e = hipSuccess;

@@ -124,6 +124,20 @@ ds_status ds_kv_cache_reset(ds_kv* kv, int32_t seq, void* stream);
 /* Sets every lengths[b] from h_lengths[0..B) (each in [0, T]); used to rewind
  * or to resume from a saved cache. */
 ds_status ds_kv_cache_set_lengths(ds_kv* kv, const int32_t* h_lengths, void* stream);
+/* Cache replication ("Inside nanochat Part 4", section "Batch Prefilling
+ * via Cache Replication": a batch-1 prefill copied into the rows of a
+ * decode cache, for several completions of one prompt).  Copies the first
+ * n = lengths[src_seq] positions of every layer's key and value rows of
+ * sequence src_seq of `src` into sequences dst_first .. dst_first+count-1
+ * of `dst`, and sets their lengths to n (device lengths and host mirror).
+ * dst and src may be the same cache (the source slot then must not be a
+ * destination).  Positions at or past n of the destinations are not
+ * written.  Both caches must belong to models of equal layer count,
+ * key/value heads and head dim.  Only enqueues work on `stream`.
+ * Errors: DS_ERR_INVALID_ARG (shapes, slot ranges), DS_ERR_CONTEXT_FULL
+ * (n > dst's T). */
+ds_status ds_kv_cache_replicate(ds_kv* dst, const ds_kv* src, int32_t src_seq, int32_t dst_first, int32_t count,
+                                void* stream);
 /* Copies the host-side mirror of the lengths (no device access). */
 ds_status ds_kv_cache_get_lengths(const ds_kv* kv, int32_t* h_lengths);
 /* Synchronises `stream` and reports device-detected errors since the last
@@ -203,6 +217,18 @@ ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, in
  * top_k == 0), DS_ERR_ALIGNMENT. */
 ds_status ds_sample(const ds_kv* kv, const float* d_uniform, float temperature, int32_t top_k, float top_p,
                     int32_t* d_tok_out, void* stream);
+
+/* A decode step of some of the sequences: the n_rows distinct sequence ids
+ * in h_rows (host int32, each in [0, B)) each read d_tok_in[row], append at
+ * lengths[row], advance by one and get their greedy token in d_tok_out[row]
+ * and their logits kept for ds_logits; every other sequence is left as it
+ * is.  This is the per-row completion of "Inside nanochat Part 4", section
+ * "Early Stopping Implementation": rows that have finished stop costing
+ * work.  Always one launch per operation.  n_rows == 0 does nothing.
+ * Errors: DS_ERR_INVALID_ARG (a row repeated or out of range),
+ * DS_ERR_CONTEXT_FULL (a listed row already holds T positions). */
+ds_status ds_decode_step_rows(ds_model* model, ds_kv* kv, const int32_t* h_rows, int32_t n_rows,
+                              const int32_t* d_tok_in, int32_t* d_tok_out, void* stream);
 
 /* Launch shape of batch-1 steps.  When B == 1 and the sequence holds at most
  * the returned number of positions after the step, ds_decode_step (and each
