@@ -156,6 +156,35 @@ def prefill_bench(dsa, torch, model, w, prompt, stream, reps, per_position=True)
             "config": {"workload": w.name, "prompt_len": n, "ctx": w.ctx, "batch": 1}}
 
 
+def replicate_bench(dsa, torch, model, w, prompt, stream, n_rows, reps=10):
+    """Copy one prefilled sequence into n_rows sequences of a decode cache:
+    the rows [0, len) of every layer's keys and values, per destination."""
+    toks = [int(t) for t in prompt]
+    src = dsa.KVCache(model, 1, w.ctx)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    src.prefill_batched(0, toks, out, stream)
+    dst = dsa.KVCache(model, n_rows, w.ctx)
+    dst.replicate_from(src, 0, 0, n_rows, stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        dst.replicate_from(src, 0, 0, n_rows, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1000.0 / reps
+    m = w.model
+    per_row = len(toks) * m.n_layers * 2 * m.n_kv_heads * m.head_dim * 4  # bytes written per row (and read once)
+    dst.check(stream)
+    src.close()
+    dst.close()
+    return {"metric": f"cache replication ({w.name}, {len(toks)} positions into {n_rows} rows)",
+            "value": us, "unit": "us per call", "higher_is_better": False,
+            "bytes_written": per_row * n_rows,
+            "algorithmic_GBps": (per_row * n_rows + per_row) / (us * 1e-6) / 1e9,
+            "n_gpus": 1, "config": {"workload": w.name, "prompt_len": len(toks), "rows": n_rows, "ctx": w.ctx}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +200,9 @@ def main():
                          "ds_prefill_batched (positions as the items of a pass) against ds_prefill (one "
                          "position per pass); prints a prefill tok/s line")
     ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--replicate", type=int, default=0,
+                    help="N: prefill the workload's first prompt once (batched) and time copying its cache rows "
+                         "into N sequences of a decode cache (ds_kv_cache_replicate); prints a replication line")
     ap.add_argument("--sample", default="",
                     help="T,K,P: after every decode step draw the next tokens with ds_sample (temperature T, "
                          "top-k K, top-p P; seeded uniforms) instead of keeping the greedy ones")
@@ -212,6 +244,9 @@ def main():
                         "GBps": 8 * n / (us * 1e-6) / 1e9}
             del src, dst
         model = dsa.Model(m, arena)
+        if args.replicate > 0:
+            print(json.dumps(replicate_bench(dsa, torch, model, w, prompts[0], stream, args.replicate)))
+            return
         if args.prefill:
             print(json.dumps(prefill_bench(dsa, torch, model, w, prompts[0], stream, args.prefill_reps,
                                            not args.prefill_batched_only)))

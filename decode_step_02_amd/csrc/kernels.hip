@@ -808,7 +808,13 @@ __global__ void k_replicate(float* __restrict__ dst, int Bd, int Td, const float
     const size_t so = ((static_cast<size_t>(lk) * Bs + src_slot) * Hkv + g) * static_cast<size_t>(Ts) * D;
     const size_t dof = ((static_cast<size_t>(lk) * Bd + dst_first + c) * Hkv + g) * static_cast<size_t>(Td) * D;
     const size_t m = static_cast<size_t>(n) * D;
-    for (size_t i = threadIdx.x; i < m; i += blockDim.x) dst[dof + i] = src[so + i];
+    if ((D & 3) == 0) {  // rows start on 16-byte boundaries
+        const float4* s4 = reinterpret_cast<const float4*>(src + so);
+        float4* d4 = reinterpret_cast<float4*>(dst + dof);
+        for (size_t i = threadIdx.x; i < m / 4; i += blockDim.x) d4[i] = s4[i];
+    } else {
+        for (size_t i = threadIdx.x; i < m; i += blockDim.x) dst[dof + i] = src[so + i];
+    }
 }
 
 __global__ void k_set_lengths(int32_t* lengths, SetList l) {
