@@ -53,6 +53,7 @@ constexpr int kPNorm = 4;                     // normalised elements per thread 
 constexpr long kPSpin = 1 << 20;              // poll rounds before a wait gives up
 constexpr int kPhases = 5;                    // epochs per layer
 constexpr int kPChunk = 32;                   // positions per attention task
+constexpr int kPSample = 16;                  // words a throttle wait samples (fewer loads on the hot lines)
 
 static_assert(kPWaves == kPKeyWords, "one argmax word per wave");
 
@@ -85,19 +86,21 @@ struct Seg {
     float* dst;
 };
 
-// Wait until 64 words spread over src[0..n) carry epoch ep (ANY: until one
-// of them does).  Wave 0 polls, the other waves wait at the barrier, so a
-// waiting block puts one wave's loads on the memory system; SLEEP spaces the
-// rounds.  Used as a throttle in front of a block_fetch.  Block-uniform call.
+// Wait until kPSample words spread over src[0..n) carry epoch ep (ANY: until
+// one of them does).  Lanes of wave 0 poll, the other waves wait at the
+// barrier, so a waiting block puts a few loads on the memory system; SLEEP
+// spaces the rounds.  Used as a throttle in front of a block_fetch.
+// Block-uniform call.
 template <int SLEEP, bool ANY = false>
 __device__ void wait_sample(const uint64_t* src, int n, uint32_t ep, int32_t* err) {
     if (n <= 0) return;
     if (threadIdx.x < 64) {
-        const uint64_t* q = src + (static_cast<int>(threadIdx.x) * n) / 64;
+        const bool act = threadIdx.x < kPSample;
+        const uint64_t* q = src + (static_cast<int>(threadIdx.x) % kPSample * n) / kPSample;
         long spins = 0;
         while (true) {
-            const bool ok = static_cast<uint32_t>(ll_get(q) >> 32) == ep;
-            if (ANY ? __any(ok) : __all(ok)) break;
+            const bool ok = act && static_cast<uint32_t>(ll_get(q) >> 32) == ep;
+            if (ANY ? __any(ok) : __all(ok || !act)) break;
             if (SLEEP > 0) __builtin_amdgcn_s_sleep(SLEEP);
             if (give_up(spins, err)) break;
         }
@@ -719,7 +722,7 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
                 xv[j] = e < d ? emb_at<C::WDT>(s, c.tok, e) : 0.f;
             }
         } else {
-            wait_sample<4, true>(p.ll_x + c.rep, d, c.ep(l - 1, 4), c.err);
+            wait_sample<2, true>(p.ll_x + c.rep, d, c.ep(l - 1, 4), c.err);
             block_fetch_own(Seg{p.ll_x + c.rep, d, c.ep(l - 1, 4), nullptr}, xv, c.err);
         }
         const float rn = block_norm_regs<C::WDT>(xv, d, gr, s.eps, sm, vin);
@@ -762,7 +765,7 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
     float* pw = sm + ((HD + 2 * KVD + 3) & ~3) + wv * REP * KV<PD, REP>::PWS;  // softmax weights of this wave
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        wait_sample<4, true>(p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), c.err);
+        wait_sample<2, true>(p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), c.err);
         block_fetch2<2>(Seg{p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), qkv}, c.err);
         __syncthreads();
         if (active) {
@@ -812,10 +815,10 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
             rows = Seg{p.ll_x + c.rep + r0, nrows, c.ep(l - 1, 4), xr};
         }
         if (c.fused) {
-            wait_sample<4, true>(p.ll_qkv + c.rep, in_n, c.ep(l, 0), c.err);
+            wait_sample<2, true>(p.ll_qkv + c.rep, in_n, c.ep(l, 0), c.err);
             block_fetch2<2>(Seg{p.ll_qkv + c.rep, in_n, c.ep(l, 0), in}, rows, c.err);
         } else {
-            wait_sample<4, true>(p.ll_part, in_n, c.ep(l, 1), c.err);
+            wait_sample<2, true>(p.ll_part, in_n, c.ep(l, 1), c.err);
             block_fetch2<4>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
         }
         __syncthreads();
@@ -877,7 +880,7 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     float* const vin = sm;  // product input (see put_pair)
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        wait_sample<4, true>(p.ll_x2 + c.rep, d, c.ep(l, 2), c.err);
+        wait_sample<2, true>(p.ll_x2 + c.rep, d, c.ep(l, 2), c.err);
         float xv[kPNorm];
         block_fetch_own(Seg{p.ll_x2 + c.rep, d, c.ep(l, 2), nullptr}, xv, c.err);
         const float rn = block_norm_regs<C::WDT>(xv, d, gr, s.eps, sm, vin);
@@ -913,7 +916,7 @@ __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     st.start(p.layers[0].w2, valid ? row : 0, F, sub, valid);
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        wait_sample<4, true>(p.ll_h + c.rep, F, c.ep(l, 3), c.err);
+        wait_sample<2, true>(p.ll_h + c.rep, F, c.ep(l, 3), c.err);
         block_fetch2<4>(Seg{p.ll_h + c.rep, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + c.rep + r0, nrows, c.ep(l, 2), xr},
                         c.err);
         if (C::WDT == kBF16) {
@@ -1012,7 +1015,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         float* const vin = sm;  // product input (see put_pair)
         __syncthreads();
         if (idle) wait_word<32>(p.ll_late, c.ep(s.L - 1, 0), c.err);  // the others are past the last layer's start
-        wait_sample<4, true>(p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), c.err);
+        wait_sample<2, true>(p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), c.err);
         float xv[kPNorm];
         block_fetch_own(Seg{p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), nullptr}, xv, c.err);
         if (!idle) start2();
