@@ -219,12 +219,16 @@ __device__ __forceinline__ void poll_wide(u32x4 (&w)[J], const uint64_t* const (
 // (2t, 2t+1), (2t+512, 2t+513), ... of the concatenation, J pairs per round.
 // Needs a.n and b.n even (a pair never straddles the segments) and 16-byte
 // aligned segment starts; otherwise it falls back to block_fetch.
-template <int J>
-__device__ void block_fetch2(const Seg& a, const Seg& b, int32_t* err) {
+// sink_a(i, v0, v1) takes the pairs of segment a in place of the stores to
+// a.dst (the other overload stores them).
+template <int J, typename SinkA>
+__device__ void block_fetch2(const Seg& a, const Seg& b, int32_t* err, SinkA sink_a) {
     const bool ok_shape = ((a.n | b.n) & 1) == 0 &&
                           ((reinterpret_cast<uintptr_t>(a.src) | reinterpret_cast<uintptr_t>(b.src)) & 15) == 0;
     if (!ok_shape) {
         block_fetch<2 * J>(a, b, err);
+        __syncthreads();
+        for (int i = 2 * static_cast<int>(threadIdx.x); i < a.n; i += 2 * kPThreads) sink_a(i, a.dst[i], a.dst[i + 1]);
         return;
     }
     const int tid = threadIdx.x;
@@ -251,13 +255,24 @@ __device__ void block_fetch2(const Seg& a, const Seg& b, int32_t* err) {
 #pragma unroll
         for (int j = 0; j < J; j++) {
             const int i = base + 2 * (tid + kPThreads * j);
-            if (i < total) {
-                float* dst = i < a.n ? a.dst + i : b.dst + (i - a.n);
+            if (i < a.n) {
+                sink_a(i, __uint_as_float(w[j].x), __uint_as_float(w[j].z));
+            } else if (i < total) {
+                float* dst = b.dst + (i - a.n);
                 dst[0] = __uint_as_float(w[j].x);
                 dst[1] = __uint_as_float(w[j].z);
             }
         }
     }
+}
+
+template <int J>
+__device__ __forceinline__ void block_fetch2(const Seg& a, const Seg& b, int32_t* err) {
+    float* const d = a.dst;
+    block_fetch2<J>(a, b, err, [d](int i, float v0, float v1) {
+        d[i] = v0;
+        d[i + 1] = v1;
+    });
 }
 
 template <int J>
@@ -917,16 +932,9 @@ __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         wait_sample<2, true>(p.ll_h + c.rep, F, c.ep(l, 3), c.err);
+        // h goes straight into the product input (bf16 hi/lo pairs, or fp32)
         block_fetch2<4>(Seg{p.ll_h + c.rep, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + c.rep + r0, nrows, c.ep(l, 2), xr},
-                        c.err);
-        if (C::WDT == kBF16) {
-            // the pairs block_fetch2 gave this thread: (2t + 512 j, 2t + 512 j + 1)
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-                const int i = 2 * (static_cast<int>(threadIdx.x) + kPThreads * jj);
-                if (i < F) put_pair<C::WDT>(hv, F, i, hs[i], hs[i + 1]);
-            }
-        }
+                        c.err, [&](int i, float v0, float v1) { put_pair<C::WDT>(hv, F, i, v0, v1); });
         __syncthreads();
         XRegs<C::WDT, C::NCF> hx;
         hx.load(hv, F, sub, G);
