@@ -150,7 +150,7 @@ WsLayout ws_layout(const ds_config* c, int B, int T) {
     w.ll_x = take(rbytes);
     w.ll_x2 = take(rbytes);
     w.ll_qkv = take(rbytes);
-    w.ll_part = take(8 * static_cast<size_t>(c->n_heads) * ds::kPMaxChunks * (c->head_dim + 2));
+    w.ll_part = take(8 * static_cast<size_t>(c->n_heads) * ds::kPMaxParts * (c->head_dim + 2));
     w.ll_h = take(rbytes);
     w.ll_keys = take(8 * static_cast<size_t>(ds::kPKeyWords));
     w.ll_late = take(8);

@@ -17,7 +17,8 @@ constexpr int kMaxD = 256;       // head_dim limit of the attention kernels
 constexpr int kMaxItems = 64;    // items per k_begin launch
 constexpr int kSetChunk = 128;   // lengths per k_set_lengths launch
 constexpr int kMaxArgmaxBlocks = 16384;  // vocabulary blocks per item (argmax partials)
-constexpr int kPMaxChunks = 16;  // attention chunks the persistent step can hold per head
+constexpr int kPMaxChunks = 64;  // 32-position attention chunks the persistent step can hold per head
+constexpr int kPMaxParts = kPMaxChunks / 4;  // their partials, one per four chunks
 constexpr int kPKeyWords = 1024; // argmax words of the persistent step (one per wave)
 constexpr int kPRep = 8;
 constexpr int kMaxTopK = 1024;   // largest top-k of the sampling epilogue
@@ -81,7 +82,7 @@ struct PersistArgs {
     uint64_t* ll_x;         // [d]      residual after W2 (value, epoch words)
     uint64_t* ll_x2;        // [d]      residual after Wo
     uint64_t* ll_qkv;       // [Hkv][(rep + 2) * D] per group: rotated queries, new key, new value
-    uint64_t* ll_part;      // [kPMaxChunks][H][D+2] attention partials (m, l, o), chunk-major
+    uint64_t* ll_part;      // [Hkv][kPMaxParts][H/Hkv][D+2] attention partials (m, l, o)
     uint64_t* ll_h;         // [F]      silu(a)*u
     uint64_t* ll_keys;      // [kPKeyWords] argmax words
     uint64_t* ll_late;      // one word in a line of its own: the last layer has begun

@@ -481,7 +481,7 @@ __device__ __forceinline__ uint64_t key_word(float v, int idx, uint32_t ep) {
 // after W2; the argmax words use ep(L, 0).
 struct PCtx {
     uint32_t base;   // epoch base of this step
-    int pos, n, nch, tok;
+    int pos, n, nch, npart, tok;  // npart: attention partials per head (four chunks each)
     bool fused;      // attention recomputed inside the Wo blocks
     int rep;         // word offset of the replica this block reads
     int32_t* err;
@@ -765,36 +765,106 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     }
 }
 
-// ---- role 1: attention partials per (group, 32-position chunk) (a task per wave) ------------------
+// ---- role 1: attention partials, a block per (group, four 32-position chunks) --------------------
+// Each wave scores one chunk; the block folds its waves' (max, sum, weighted
+// values) into one partial per head in LDS, rescaling each by e^(m_w - M),
+// so the Wo blocks fetch a quarter of the partials.
 template <class C>
 __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c, int bt, float* sm) {
-    constexpr int PD = C::PD, REP = C::REP;
+    constexpr int PD = C::PD, REP = C::REP, PS = PD + 2;
     const int wv = threadIdx.x >> 6;
     const int HD = s.H * PD, KVD = s.Hkv * PD;
-    const int t = bt * 4 + wv;
-    const bool active = t < s.Hkv * c.nch;
-    const int g = active ? t % s.Hkv : 0, ck = active ? t / s.Hkv : 0;
+    const int g = bt % s.Hkv, part = bt / s.Hkv, ck = part * 4 + wv;
+    const int nw = min(4, c.nch - part * 4);  // waves with a chunk (>= 1)
+    const bool active = wv < nw;
     KV<PD, REP> kv;
     if (active) kv.load(s, 0, g, ck * kPChunk, c.pos);
     float* qkv = sm;
     float* pw = sm + ((HD + 2 * KVD + 3) & ~3) + wv * REP * KV<PD, REP>::PWS;  // softmax weights of this wave
+    float* cmb = sm + ((HD + 2 * KVD + 3) & ~3) + 4 * REP * KV<PD, REP>::PWS;  // [wave][head][m, l, D]
+    uint64_t* dst = p.ll_part + static_cast<size_t>((g * c.npart + part) * REP) * PS;
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         wait_sample<2, true>(p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), c.err);
         block_fetch2<2>(Seg{p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), qkv}, c.err);
         __syncthreads();
         if (active) {
-            const uint32_t e1 = c.ep(l, 1);
             kv.attend(qkv, g, ck * kPChunk, c.pos, pw, [&](int j, int e, float m, float lsum, float acc, float) {
-                uint64_t* dst = p.ll_part + static_cast<size_t>((g * c.nch + ck) * REP + j) * (PD + 2);
-                ll_put(dst + 2 + e, acc, e1);
+                float* cw = cmb + (wv * REP + j) * PS;
+                cw[2 + e] = acc;
                 if (e == 0) {
-                    ll_put(dst, m, e1);
-                    ll_put(dst + 1, lsum, e1);
+                    cw[0] = m;
+                    cw[1] = lsum;
                 }
             });
-            if (l + 1 < s.L) kv.load(s, l + 1, g, ck * kPChunk, c.pos);
         }
+        __syncthreads();
+        const uint32_t e1 = c.ep(l, 1);
+        for (int idx = threadIdx.x; idx < REP * PD; idx += kPThreads) {
+            const int j = idx / PD, e = idx % PD;
+            float2 ml[4];
+            float v[4];
+#pragma unroll
+            for (int w = 0; w < 4; w++) {  // waves past nw repeat the last one, with weight 0
+                const float* cw = cmb + (min(w, nw - 1) * REP + j) * PS;
+                ml[w] = *reinterpret_cast<const float2*>(cw);
+                v[w] = cw[2 + e];
+            }
+            const float M = OpMax{}(OpMax{}(ml[0].x, ml[1].x), OpMax{}(ml[2].x, ml[3].x));
+            float A = 0.f, L = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                const float f = w < nw ? __expf(ml[w].x - M) : 0.f;  // each wave's max is finite: its chunk holds a position <= pos
+                A = fmaf(f, v[w], A);
+                L = fmaf(f, ml[w].y, L);
+            }
+            ll_put(dst + j * PS + 2 + e, A, e1);
+            if (e == 0) {
+                ll_put(dst + j * PS, M, e1);
+                ll_put(dst + j * PS + 1, L, e1);
+            }
+        }
+        // after the barrier above, which would otherwise wait for these loads
+        if (active && l + 1 < s.L) kv.load(s, l + 1, g, ck * kPChunk, c.pos);
+    }
+}
+
+// Attention output from the block partials in LDS (layout [group][part]
+// [head][m, l, D], np parts): o = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p
+// with M = max_p m_p, four dims per thread in one pass.  NP >= np is the
+// unrolled count: parts past np repeat the last one with weight 0, so every
+// LDS read is issued before the first use.
+template <int PD, int REP, int NP, int WDT>
+__device__ __forceinline__ void merge_parts_t(const float* in, int np, int H, float* o) {
+    constexpr int PS = PD + 2, cstride = REP * PS;
+    const int HD = H * PD;
+    for (int t = threadIdx.x; t < HD / 4; t += kPThreads) {
+        const int h = 4 * t / PD, e = 4 * t % PD;
+        const float* ph = in + static_cast<size_t>((h / REP) * np * REP + h % REP) * PS;
+        float2 ml[NP], a[NP], b[NP];
+#pragma unroll
+        for (int pp = 0; pp < NP; pp++) {
+            const float* q = ph + min(pp, np - 1) * cstride;
+            ml[pp] = *reinterpret_cast<const float2*>(q);
+            a[pp] = *reinterpret_cast<const float2*>(q + 2 + e);
+            b[pp] = *reinterpret_cast<const float2*>(q + 4 + e);
+        }
+        float M = ml[0].x;
+#pragma unroll
+        for (int pp = 1; pp < NP; pp++) M = OpMax{}(M, ml[pp].x);
+        float L = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < NP; pp++) {
+            const float w = pp < np ? __expf(ml[pp].x - M) : 0.f;
+            L = fmaf(w, ml[pp].y, L);
+            a0 = fmaf(w, a[pp].x, a0);
+            a1 = fmaf(w, a[pp].y, a1);
+            a2 = fmaf(w, b[pp].x, a2);
+            a3 = fmaf(w, b[pp].y, a3);
+        }
+        const float inv = 1.0f / L;
+        put_pair<WDT>(o, HD, h * PD + e, a0 * inv, a1 * inv);
+        put_pair<WDT>(o, HD, h * PD + e + 2, a2 * inv, a3 * inv);
     }
 }
 
@@ -812,7 +882,7 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     const bool attn_wave = wv < s.Hkv;  // wave g handles key/value group g
     const int g = attn_wave ? wv : 0;
     // LDS: [Q/K/V words | partials] [o: H*D] [residual rows: 4R] [softmax weights: 4][REP][32]
-    const int in_n = c.fused ? HD + 2 * KVD : c.nch * s.H * (PD + 2);
+    const int in_n = c.fused ? HD + 2 * KVD : c.npart * s.H * (PD + 2);
     float* in = sm;
     float* o = sm + ((in_n + 3) & ~3);
     float* xr = o + HD;
@@ -843,26 +913,14 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
                     const float inv = __builtin_amdgcn_rcpf(lsum);  // lsum >= 1 (the max term is exp(0))
                     if ((e & 1) == 0) put_pair<C::WDT>(o, HD, (g * REP + j) * PD + e, acc * inv, acc1 * inv);
                 });
-            } else {
-                // merge the chunk partials of the group's heads (layout [group][chunk][head][m, l, D])
-                constexpr int cstride = REP * (PD + 2);
-                for (int j = 0; j < REP; j++) {
-                    const float* ph = in + static_cast<size_t>(g * c.nch * REP + j) * (PD + 2);
-                    float M = -INFINITY;
-                    for (int cc = 0; cc < c.nch; cc++) M = fmaxf(M, ph[cc * cstride]);
-                    float Lw = 0.f;
-                    for (int cc = 0; cc < c.nch; cc++) Lw += __expf(ph[cc * cstride] - M) * ph[cc * cstride + 1];
-                    const float inv = 1.0f / Lw;
-                    for (int e = 2 * lane; e < PD; e += 128) {
-                        float a0 = 0.f, a1 = 0.f;
-                        for (int cc = 0; cc < c.nch; cc++) {
-                            const float wc = __expf(ph[cc * cstride] - M);
-                            a0 = fmaf(wc, ph[cc * cstride + 2 + e], a0);
-                            a1 = fmaf(wc, ph[cc * cstride + 3 + e], a1);
-                        }
-                        put_pair<C::WDT>(o, HD, (g * REP + j) * PD + e, a0 * inv, a1 * inv);
-                    }
-                }
+            }
+        }
+        if (!c.fused) {
+            switch ((c.npart + 3) / 4) {  // partial counts unrolled in fours
+                case 1: merge_parts_t<PD, REP, 4, C::WDT>(in, c.npart, s.H, o); break;
+                case 2: merge_parts_t<PD, REP, 8, C::WDT>(in, c.npart, s.H, o); break;
+                case 3: merge_parts_t<PD, REP, 12, C::WDT>(in, c.npart, s.H, o); break;
+                default: merge_parts_t<PD, REP, 16, C::WDT>(in, c.npart, s.H, o); break;
             }
         }
         __syncthreads();
@@ -951,7 +1009,7 @@ struct Roles {
     __host__ __device__ Roles(int d, int H, int Hkv, int D, int F, int gd, int gh, int gf, int nch) {
         const int HD = H * D, KVD = Hkv * D;
         b[0] = ((HD + 2 * KVD) / (64 / gd) + 3) / 4;
-        b[1] = nch <= 1 ? 0 : (Hkv * nch + 3) / 4;
+        b[1] = nch <= 1 ? 0 : Hkv * ((nch + 3) / 4);
         b[2] = (d + 4 * (64 / gh) - 1) / (4 * (64 / gh));
         b[3] = (F + 4 * (64 / gd) - 1) / (4 * (64 / gd));
         b[4] = (d + 4 * (64 / gf) - 1) / (4 * (64 / gf));
@@ -972,6 +1030,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
     c.pos = s.lengths[0];
     c.n = c.pos + 1;
     c.nch = (c.n + kPChunk - 1) / kPChunk;
+    c.npart = (c.nch + 3) / 4;
     c.fused = c.nch == 1;
     c.rep = (blk % C::LLR) * p.rstride;
     c.tok = d_tok_in ? d_tok_in[0] : tok_value;
@@ -1131,12 +1190,14 @@ int persist_max_ctx(const StepArgs& s) {
     const int pws = 4 * (s.H / s.Hkv) * (kPChunk + 4);
     if (2 * HD + 2 * KVD + 4 + 64 + pws > kPRed || 2 * s.F + 4 + 64 > kPRed || (s.F & 1)) return 0;
     if (Roles(s.d, s.H, s.Hkv, s.D, s.F, k->gd, k->gh, k->gf, 1).total() > kPBlocks) return 0;
-    // longer contexts add role 1 blocks and keep every partial in role 2's LDS
+    // longer contexts add role 1 blocks (Q/K/V words, softmax weights, the
+    // waves' partials in LDS) and keep every block partial in role 2's LDS
+    const int attn_lds = ((HD + 2 * KVD + 3) & ~3) + pws + 4 * (s.H / s.Hkv) * (s.D + 2);
     int chunks = 1;
     while (chunks < kPMaxChunks) {
         const int nc = chunks + 1;
         if (Roles(s.d, s.H, s.Hkv, s.D, s.F, k->gd, k->gh, k->gf, nc).total() > kPBlocks) break;
-        if (nc * s.H * (s.D + 2) + 4 + HD + 64 + pws > kPRed) break;
+        if ((nc + 3) / 4 * s.H * (s.D + 2) + 4 + HD + 64 + pws > kPRed || attn_lds > kPRed || s.H * 16 > pws) break;
         chunks = nc;
     }
     const int ctx = chunks * kPChunk;

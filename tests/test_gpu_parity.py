@@ -66,7 +66,7 @@ def gpu_run(shape, arena, prompts, feed, T, dispatch=1, use_batch_prefill=True, 
     kv.check(stream)
     out = dict(first_tok=first_tok, first_lg=first_lg, toks=toks, lgs=lgs,
                cache=kv.cache_view().cpu().numpy(), lengths=kv.lengths.cpu().numpy(),
-               mirror=np.array(kv.get_lengths()))
+               mirror=np.array(kv.get_lengths()), single_launch_ctx=kv.single_launch_ctx())
     kv.close()
     model.close()
     return out
@@ -267,6 +267,28 @@ def test_batch1_single_launch_matches_per_operation_launches(monkeypatch):
     assert_logits_close(a["cache"][:, :, 0, :, :n], b["cache"][:, :, 0, :, :n], "cache")
 
 
+def test_single_launch_several_partials_135m(monkeypatch):
+    """Past 128 positions the single launch's attention blocks each fold four
+    32-position chunks into one partial and the Wo blocks merge the partials:
+    positions 157..168 span five and six chunks, so the second partial holds
+    one or two of them.  Checked against the per-operation launches, which
+    the oracle pins at 1000 positions."""
+    _torch()
+    w = synth.WORKLOADS["llama135m_p5"]
+    arena = synth.make_arena(w.model, w.model_seed)
+    prompts = [synth.random_tokens(504, 157, w.model.vocab_size)]
+    feed = [[int(t)] for t in synth.random_tokens(505, 12, w.model.vocab_size)]
+    a = gpu_run(w.model, arena, prompts, feed, w.ctx)
+    assert a["single_launch_ctx"] >= 169
+    monkeypatch.setenv("DS_PERSIST", "0")
+    b = gpu_run(w.model, arena, prompts, feed, w.ctx)
+    for k in range(len(feed)):
+        assert_logits_close(a["lgs"][k], b["lgs"][k], f"step {k}")
+        check_tokens(a["toks"][k], b["toks"][k], b["lgs"][k], a["lgs"][k], f"step {k}")
+    n = len(prompts[0]) + len(feed)
+    assert_logits_close(a["cache"][:, :, 0, :, :n], b["cache"][:, :, 0, :, :n], "cache")
+
+
 def test_single_launch_step_is_taken_at_batch_1():
     """Batch-1 caches of the instantiated shape classes run their steps as one
     launch (so the parity cases above exercise it); larger batches do not."""
@@ -275,7 +297,7 @@ def test_single_launch_step_is_taken_at_batch_1():
     w = synth.WORKLOADS["llama135m_p5"]
     model = dsa.Model(w.model, synth.make_arena(w.model, w.model_seed))
     kv = dsa.KVCache(model, 1, w.ctx)
-    assert kv.single_launch_ctx() == 512
+    assert kv.single_launch_ctx() == 1024  # the whole context (up to 2048 fit)
     kv.close()
     kv = dsa.KVCache(model, 2, 64)
     assert kv.single_launch_ctx() == 0
