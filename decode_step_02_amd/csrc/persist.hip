@@ -783,10 +783,11 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
     float* pw = sm + ((HD + 2 * KVD + 3) & ~3) + wv * REP * KV<PD, REP>::PWS;  // softmax weights of this wave
     float* cmb = sm + ((HD + 2 * KVD + 3) & ~3) + 4 * REP * KV<PD, REP>::PWS;  // [wave][head][m, l, D]
     uint64_t* dst = p.ll_part + static_cast<size_t>((g * c.npart + part) * REP) * PS;
+    constexpr int GS = (REP + 2) * PD;  // the group's queries, key and value (group-major words)
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
-        wait_sample<2, true>(p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), c.err);
-        block_fetch2<2>(Seg{p.ll_qkv + c.rep, HD + 2 * KVD, c.ep(l, 0), qkv}, c.err);
+        wait_sample<2, true>(p.ll_qkv + c.rep + g * GS, GS, c.ep(l, 0), c.err);
+        block_fetch2<2>(Seg{p.ll_qkv + c.rep + g * GS, GS, c.ep(l, 0), qkv + g * GS}, c.err);
         __syncthreads();
         if (active) {
             kv.attend(qkv, g, ck * kPChunk, c.pos, pw, [&](int j, int e, float m, float lsum, float acc, float) {
