@@ -375,6 +375,9 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     s.mm_ok = ds::mm_supported(s) ? 1 : 0;
     const char* mmenv = std::getenv("DS_MFMA");  // "0" keeps the VALU projections for every batch size
     if (mmenv && std::strcmp(mmenv, "0") == 0) s.mm_ok = 0;
+    s.mm_split = 1;
+    const char* skenv = std::getenv("DS_MM_SPLIT");  // "0" keeps the tiled MFMA kernel for every projection
+    if (skenv && std::strcmp(skenv, "0") == 0) s.mm_split = 0;
     const char* sa = std::getenv("DS_SHORT_ATTN");  // "0" turns the fused short-context path off
     if (sa && std::strcmp(sa, "0") == 0) s.short_n = 0;
     ds::PersistArgs& pa = kv->pa;

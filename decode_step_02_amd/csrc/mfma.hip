@@ -271,6 +271,171 @@ __global__ __launch_bounds__(256) void k_mm(StepArgs s, LayerW w, int layer, int
     }
 }
 
+// ---- split-K variant for the narrow projections ------------------------------------------------
+// Q/K/V, Wo, W1/W3 and W2 of a small model have few weight rows (576..1536),
+// so the tiled kernel above puts only a few dozen blocks on the chip and each
+// wave walks K in dependent tiles.  Here a block is one tile of 16 weight rows
+// x 16 items; its four waves take every fourth 32-wide k-step, issue all of
+// their weight, activation and gain loads at once (the activations straight
+// from global memory into the B-operand layout, split into bf16 hi + lo in
+// registers), run their MFMAs and add their partial tiles (and the items'
+// partial sums of squares) through LDS.  Wave w then finishes row r = w of
+// each lane's four (tile rows kq*4 + w), with the epilogues of k_mm.  The
+// item groups of one row tile are 8 block indices apart, so they run on the
+// same XCD and share its L2 copy of the weight tile.
+template <int KIND, int MAXS>
+__global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, int n_items, int ident, int n_tiles,
+                                                int n_groups) {
+    constexpr bool NORM = KIND == MM_QKV || KIND == MM_W13;
+    constexpr bool TWO = KIND == MM_W13;
+    __shared__ float red[4][9][64];  // [wave][acc 0..3, acc3 0..3, sum of squares][lane]
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int ti = lane & 15, kq = lane >> 4;
+    const int L = blockIdx.x, span = 8 * n_groups;
+    const int grp = (L % span) / 8, tile = (L / span) * 8 + L % 8;
+    if (tile >= n_tiles) return;  // padding of the last eight row tiles (whole block)
+
+    int K = s.d, N = 0;
+    const void* W = nullptr;
+    const void* W3 = nullptr;
+    const float* gain = nullptr;
+    const float* src = s.x;
+    if (KIND == MM_QKV) { N = (s.H + 2 * s.Hkv) * s.D; gain = w.attn_norm; }
+    if (KIND == MM_WO) { K = s.H * s.D; N = s.d; W = w.wo; src = s.o; }
+    if (KIND == MM_W13) { N = s.F; W = w.w1; W3 = w.w3; gain = w.ffn_norm; }
+    if (KIND == MM_W2) { K = s.F; N = s.d; W = w.w2; src = s.h; }
+
+    const int D = s.D, half_d = s.D / 2;
+    const int nq_t = s.H * D / 16, nk_t = s.Hkv * D / 16;
+    int row = 0;
+    bool roped = false, is_q = false;
+    if (KIND == MM_QKV) {
+        roped = tile < nq_t + nk_t;
+        is_q = tile < nq_t;
+        if (roped) {
+            const int p = (is_q ? tile : tile - nq_t) * 8 + (ti & 7);
+            row = (p / half_d) * D + p % half_d + (ti >> 3) * half_d;
+            W = is_q ? w.wq : w.wk;
+        } else {
+            row = (tile - nq_t - nk_t) * 16 + ti;
+            W = w.wv;
+        }
+    } else {
+        row = min(tile * 16 + ti, N - 1);
+    }
+    const int item = grp * 16 + ti;
+    const bool m_ok = item < n_items;
+    const uint16_t* Wrow = static_cast<const uint16_t*>(W) + static_cast<size_t>(row) * K + kq * 8;
+    const uint16_t* W3row = TWO ? static_cast<const uint16_t*>(W3) + static_cast<size_t>(row) * K + kq * 8 : Wrow;
+    const float* xrow = src + static_cast<size_t>(min(item, n_items - 1)) * K + kq * 8;
+    const float* grow = NORM ? gain + kq * 8 : nullptr;
+
+    // every load of the wave's k-steps (wave-uniform count)
+    const int nks = K / 32;
+    uint4 wa[MAXS], wb[MAXS];
+    float4 xa[MAXS], xb[MAXS], ga[MAXS], gb[MAXS];
+#pragma unroll
+    for (int i = 0; i < MAXS; i++) {
+        const int ks = wave + 4 * i;
+        if (ks < nks) {
+            const int k0 = ks * 32;
+            wa[i] = *reinterpret_cast<const uint4*>(Wrow + k0);
+            if (TWO) wb[i] = *reinterpret_cast<const uint4*>(W3row + k0);
+            xa[i] = *reinterpret_cast<const float4*>(xrow + k0);
+            xb[i] = *reinterpret_cast<const float4*>(xrow + k0 + 4);
+            if (NORM) {
+                ga[i] = *reinterpret_cast<const float4*>(grow + k0);
+                gb[i] = *reinterpret_cast<const float4*>(grow + k0 + 4);
+            }
+        }
+    }
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, acc3 = f32x4{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXS; i++) {
+        if (wave + 4 * i < nks) {
+            const float xs[8] = {xa[i].x, xa[i].y, xa[i].z, xa[i].w, xb[i].x, xb[i].y, xb[i].z, xb[i].w};
+            float gv[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+            if constexpr (NORM) {
+                gv[0] = ga[i].x; gv[1] = ga[i].y; gv[2] = ga[i].z; gv[3] = ga[i].w;
+                gv[4] = gb[i].x; gv[5] = gb[i].y; gv[6] = gb[i].z; gv[7] = gb[i].w;
+            }
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int c = 0; c < 8; c++) {
+                const float x = m_ok ? xs[c] : 0.f;
+                ss = fmaf(x, x, ss);
+                const float val = NORM ? gv[c] * x : x;
+                const uint32_t h = bf16_bits_rne(val);
+                const uint32_t l = bf16_bits_rne(val - __uint_as_float(h << 16));
+                if (c & 1) {
+                    hi[c >> 1] |= h << 16;
+                    lo[c >> 1] |= l << 16;
+                } else {
+                    hi[c >> 1] = h;
+                    lo[c >> 1] = l;
+                }
+            }
+            const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]), bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            acc = mfma(wa[i], bh, acc);
+            acc = mfma(wa[i], bl, acc);
+            if (TWO) {
+                acc3 = mfma(wb[i], bh, acc3);
+                acc3 = mfma(wb[i], bl, acc3);
+            }
+        }
+    }
+    if (NORM) {  // the item's sum over the wave's k-steps: lanes ti, ti + 16, ti + 32, ti + 48
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        red[wave][r][lane] = acc[r];
+        if (TWO) red[wave][4 + r][lane] = acc3[r];
+    }
+    if (NORM) red[wave][8][lane] = ss;
+    __syncthreads();
+    const int r = wave;  // this wave finishes tile row kq * 4 + r
+    float y = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
+    float y3 = TWO ? red[0][4 + r][lane] + red[1][4 + r][lane] + red[2][4 + r][lane] + red[3][4 + r][lane] : 0.f;
+    float r_m = 1.f;
+    if (NORM) {
+        const float sq = red[0][8][lane] + red[1][8][lane] + red[2][8][lane] + red[3][8][lane];
+        r_m = 1.0f / sqrtf(sq / static_cast<float>(K) + s.eps);
+    }
+    const int i = kq * 4 + r;
+    if (KIND == MM_QKV) {
+        y *= r_m;
+        const float partner = __shfl_xor(y, 32);  // tile rows i and i ^ 8 of the same item
+        if (!m_ok || tile * 16 >= N) return;
+        const int pos = s.pos[item];
+        const int slot = ident ? item : s.slot[item];
+        if (roped) {
+            const int p = (is_q ? tile : tile - nq_t) * 8 + (i & 7);
+            const int ii = p % half_d, second = i >> 3;
+            const int orow = (p / half_d) * D + ii + second * half_d;
+            const float c = s.rope_cos[static_cast<size_t>(pos) * half_d + ii];
+            const float sn = s.rope_sin[static_cast<size_t>(pos) * half_d + ii];
+            const float out = second ? fmaf(partner, sn, y * c) : fmaf(-partner, sn, y * c);
+            if (is_q)
+                s.q[static_cast<size_t>(item) * s.H * D + orow] = out;
+            else
+                s.cache[cache_row(s, layer, 0, slot, orow / D, pos) + orow % D] = out;
+        } else {
+            const int orow = (tile - nq_t - nk_t) * 16 + i;
+            s.cache[cache_row(s, layer, 1, slot, orow / D, pos) + orow % D] = y;
+        }
+    } else if (KIND == MM_WO || KIND == MM_W2) {
+        const int orow = tile * 16 + i;
+        if (m_ok && orow < N) s.x[static_cast<size_t>(item) * s.d + orow] += y;
+    } else {  // MM_W13
+        const int orow = tile * 16 + i;
+        const float a = y * r_m, u = y3 * r_m;
+        if (m_ok && orow < N) s.h[static_cast<size_t>(item) * s.F + orow] = (a / (1.0f + expf(-a))) * u;
+    }
+}
+
 // ---- launch ----------------------------------------------------------------------------------
 
 bool mm_supported(const StepArgs& s) {
@@ -373,9 +538,65 @@ hipError_t mm_set_attributes(int lds) {
     return e;
 }
 
-// which: 0 qkv, 1 wo, 2 w13, 3 w2, 4 logits; items [0, n_items) in launches of kMmItems.
+// ---- split-K launch: k-steps per wave, 8 or 16 at most (registers) -----------------------------
+template <int KIND>
+static int sk_dims(const StepArgs& s, int& K, int& N) {
+    K = s.d;
+    N = 0;
+    if (KIND == MM_QKV) N = (s.H + 2 * s.Hkv) * s.D;
+    if (KIND == MM_WO) { N = s.d; K = s.H * s.D; }
+    if (KIND == MM_W13) N = s.F;
+    if (KIND == MM_W2) { N = s.d; K = s.F; }
+    const int per_wave = (K / 32 + 3) / 4;
+    constexpr int cap = (KIND == MM_QKV || KIND == MM_W13) ? 8 : 16;
+    if (per_wave > cap) return 0;
+    for (int m : {1, 2, 3, 5, 8, 12, 16})
+        if (per_wave <= m) return m;
+    return 0;
+}
+
+template <int KIND, int MAXS>
+static void launch_sk_one(const StepArgs& s, const LayerW& w, int layer, int n, int ident, int n_tiles, hipStream_t st) {
+    const int n_groups = (n + 15) / 16;
+    const dim3 grid(((n_tiles + 7) / 8) * 8 * n_groups);
+    hipLaunchKernelGGL((k_mm_sk<KIND, MAXS>), grid, dim3(256), 0, st, s, w, layer, n, ident, n_tiles, n_groups);
+}
+
+// false when the split-K kernel does not take this shape (then the tiled one runs)
+template <int KIND>
+static bool launch_sk(const StepArgs& s, const LayerW& w, int layer, int n, int ident, hipStream_t st) {
+    int K = 0, N = 0;
+    const int m = sk_dims<KIND>(s, K, N);
+    const int nt = N / 16;
+    switch (m) {
+        case 1: launch_sk_one<KIND, 1>(s, w, layer, n, ident, nt, st); return true;
+        case 2: launch_sk_one<KIND, 2>(s, w, layer, n, ident, nt, st); return true;
+        case 3: launch_sk_one<KIND, 3>(s, w, layer, n, ident, nt, st); return true;
+        case 5: launch_sk_one<KIND, 5>(s, w, layer, n, ident, nt, st); return true;
+        case 8: launch_sk_one<KIND, 8>(s, w, layer, n, ident, nt, st); return true;
+        case 12: if constexpr (KIND == MM_WO || KIND == MM_W2) { launch_sk_one<KIND, 12>(s, w, layer, n, ident, nt, st); return true; } return false;
+        case 16: if constexpr (KIND == MM_WO || KIND == MM_W2) { launch_sk_one<KIND, 16>(s, w, layer, n, ident, nt, st); return true; } return false;
+        default: return false;
+    }
+}
+
+// which: 0 qkv, 1 wo, 2 w13, 3 w2, 4 logits; items [0, n_items).  The narrow
+// projections take the split-K kernel over every item in one launch when
+// their K fits its registers; the rest run the tiled kernel in launches of
+// kMmItems items.
 hipError_t mm_gemv(int which, const StepArgs& s, const LayerW& w, int layer, int n_items, int ident,
                    const float* out_norm, const void* wcls, hipStream_t st) {
+    if (n_items > 0 && s.mm_split) {
+        bool done = false;
+        switch (which) {
+            case 0: done = launch_sk<MM_QKV>(s, w, layer, n_items, ident, st); break;
+            case 1: done = launch_sk<MM_WO>(s, w, layer, n_items, ident, st); break;
+            case 2: done = launch_sk<MM_W13>(s, w, layer, n_items, ident, st); break;
+            case 3: done = launch_sk<MM_W2>(s, w, layer, n_items, ident, st); break;
+            default: break;
+        }
+        if (done) return hipGetLastError();
+    }
     hipError_t e = hipSuccess;
     for (int m0 = 0; m0 < n_items && e == hipSuccess; m0 += kMmItems) {
         const int n = n_items - m0 < kMmItems ? n_items - m0 : kMmItems;

@@ -212,7 +212,22 @@ MM_SHAPE = synth.small_shape(dim=128, n_heads=4, n_kv_heads=2, head_dim=32, hidd
                              weight_dtype=synth.BF16)
 
 
-def test_batched_prefill_bf16_mfma_matches_oracle():
+# K = 192 is six 32-wide k-steps (two for waves 0 and 1, one for waves 2 and
+# 3 of the split-K kernel); 20 Q/K/V row tiles leave four padding blocks
+MM_SHAPE2 = synth.small_shape(dim=192, n_heads=6, n_kv_heads=2, head_dim=32, hidden_dim=320, vocab_size=640,
+                              weight_dtype=synth.BF16)
+
+
+@pytest.fixture(params=["split", "tiled"])
+def mm_kernel(request, monkeypatch):
+    """Both MFMA projection kernels: split-K (the default for narrow
+    projections) and tiled (DS_MM_SPLIT=0)."""
+    if request.param == "tiled":
+        monkeypatch.setenv("DS_MM_SPLIT", "0")
+    return request.param
+
+
+def test_batched_prefill_bf16_mfma_matches_oracle(mm_kernel):
     """bf16 weights: 16 or more positions take the MFMA projections."""
     arena = synth.make_arena(MM_SHAPE, 12, std=0.1, gain_sigma=0.1)
     lens = [40, 3, 100]
@@ -220,12 +235,11 @@ def test_batched_prefill_bf16_mfma_matches_oracle():
     compare(MM_SHAPE, arena, prompts, 2, 128, "bf16 batched prefill", batched=True)
 
 
-@pytest.mark.parametrize("B", [20, 70])
-def test_batched_mfma_projections_match_oracle(B):
+@pytest.mark.parametrize("B,shape", [(20, MM_SHAPE), (70, MM_SHAPE), (37, MM_SHAPE2)], ids=["20", "70", "37-k192"])
+def test_batched_mfma_projections_match_oracle(B, shape, mm_kernel):
     """Batches of 16+ sequences take the MFMA projections (bf16 weights, fp32
     activations split into two bf16 terms): 20 leaves part of a 16-item MFMA
-    column group empty, 70 needs two 64-item launches."""
-    shape = MM_SHAPE
+    column group empty, 70 needs two 64-item launches of the tiled kernel."""
     arena = synth.make_arena(shape, 11, std=0.1, gain_sigma=0.1)
     rng = np.random.default_rng(B)
     lens = rng.integers(1, 40, size=B)
