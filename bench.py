@@ -254,7 +254,8 @@ def main():
         kv = dsa.KVCache(model, B, w.ctx)
         kv.set_dispatch(1 if args.dispatch == "graph" else 0)
         tok = torch.zeros(B, dtype=torch.int32, device="cuda")
-        kv.prefill_batch([list(p) for p in prompts], tok)
+        for b, p in enumerate(prompts):  # setup, untimed: every prompt's positions as one batch
+            kv.prefill_batched(b, [int(t) for t in p], tok)
         base = np.array([len(p) for p in prompts], np.int32)
         cycle = w.decode_calls
 

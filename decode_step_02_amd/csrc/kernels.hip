@@ -641,23 +641,81 @@ static hipError_t launch_attn(const StepArgs& s, int layer, int n_items, hipStre
 
 // Merge the chunk partials of one (item, head): M = max m_s,
 // o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
-__global__ __launch_bounds__(64) void k_attn_combine(StepArgs s) {
+// Thread (g, e), g < G = 256 / D, holds dim e of chunks g, g + G, ... (NC of
+// them per batch, loaded before the statistics are known, so the partials
+// arrive in one memory round trip); the block then reduces M and the
+// denominator, weights its chunks and sums the G groups through LDS.
+template <int NC>
+__global__ __launch_bounds__(256) void k_attn_combine(StepArgs s) {
+    extern __shared__ float wts[];  // [n_chunks] e^(m_s - M)
+    __shared__ float red[2][4];
+    __shared__ float osum[256];
     const int h = blockIdx.x, item = blockIdx.y;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int n = s.pos[item] + 1;
     const int ns = (n + kChunk - 1) / kChunk;
     const int S = s.n_chunks, D = s.D;
+    const int G = 256 / D, g = t / D, e = t % D;
+    const bool eok = g < G;
     const size_t base = (static_cast<size_t>(item) * s.H + h) * S;
-    float M = -INFINITY;
-    for (int c = 0; c < ns; c++) M = fmaxf(M, s.part_ml[(base + c) * 2]);
-    float L = 0.f;
-    for (int c = 0; c < ns; c++) L += __expf(s.part_ml[(base + c) * 2] - M) * s.part_ml[(base + c) * 2 + 1];
-    const float inv = 1.0f / L;
-    for (int e = threadIdx.x; e < D; e += 64) {
-        float o = 0.f;
-        for (int c = 0; c < ns; c++)
-            o = fmaf(__expf(s.part_ml[(base + c) * 2] - M), s.part_o[(base + c) * D + e], o);
-        s.o[(static_cast<size_t>(item) * s.H + h) * D + e] = o * inv;
+    const float2* ml = reinterpret_cast<const float2*>(s.part_ml) + base;
+    float2 mine = t < ns ? ml[t] : make_float2(-INFINITY, 0.f);
+    float acc = 0.f, L = 0.f, M = -INFINITY;
+    for (int c0 = 0; c0 < ns; c0 += NC * G) {  // one batch unless ns > NC * G (uniform)
+        float ov[NC];
+#pragma unroll
+        for (int i = 0; i < NC; i++) {
+            const int c = min(c0 + g + i * G, ns - 1);
+            ov[i] = eok ? s.part_o[(base + c) * D + e] : 0.f;
+        }
+        if (c0 == 0) {
+            M = mine.x;
+            for (int c = t + 256; c < ns; c += 256) M = fmaxf(M, ml[c].x);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+            if (lane == 0) red[0][wave] = M;
+            __syncthreads();
+            M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+            for (int c = t; c < ns; c += 256) {
+                const float2 v = c == t ? mine : ml[c];
+                const float wv = __expf(v.x - M);
+                wts[c] = wv;
+                L = fmaf(wv, v.y, L);
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+            if (lane == 0) red[1][wave] = L;
+            __syncthreads();  // also publishes wts
+            L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+        }
+#pragma unroll
+        for (int i = 0; i < NC; i++) {
+            const int c = c0 + g + i * G;
+            if (c < ns) acc = fmaf(wts[c], ov[i], acc);
+        }
     }
+    osum[t] = acc;
+    __syncthreads();
+    if (t < D) {
+        float o = 0.f;
+        for (int gg = 0; gg < G; gg++) o += osum[gg * D + t];
+        s.o[(static_cast<size_t>(item) * s.H + h) * D + t] = o / L;
+    }
+}
+
+static hipError_t launch_combine(const StepArgs& s, int n_items, hipStream_t st) {
+    const int per = (s.n_chunks + 256 / s.D - 1) / (256 / s.D);  // chunks per thread, all in one batch if it fits
+    const dim3 grid(s.H, n_items);
+    const size_t lds = sizeof(float) * s.n_chunks;
+    if (per <= 8)
+        hipLaunchKernelGGL(k_attn_combine<8>, grid, dim3(256), lds, st, s);
+    else if (per <= 16)
+        hipLaunchKernelGGL(k_attn_combine<16>, grid, dim3(256), lds, st, s);
+    else if (per <= 32)
+        hipLaunchKernelGGL(k_attn_combine<32>, grid, dim3(256), lds, st, s);
+    else
+        hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(256), lds, st, s);
+    return hipGetLastError();
 }
 
 // ---- k_wo: x += Wo o --------------------------------------------------------------------
@@ -1016,8 +1074,7 @@ hipError_t enqueue_step(const StepArgs& s, const ModelPtrs& m, const BeginList* 
             e = gemv(G_WO_SHORT, s, w, l, n_items, st, lc);
         } else {
             e = launch_attn(s, l, n_items, st);
-            hipLaunchKernelGGL(k_attn_combine, dim3(s.H, n_items), dim3(64), 0, st, s);
-            if (e == hipSuccess) e = hipGetLastError();
+            if (e == hipSuccess) e = launch_combine(s, n_items, st);
             if (e == hipSuccess)
                 e = mm ? mm_gemv(1, s, w, l, n_items, lc.ident, nullptr, nullptr, st) : gemv(G_WO_LONG, s, w, l, n_items, st, lc);
         }
@@ -1051,8 +1108,7 @@ hipError_t enqueue_kernel(int which, int layer, const StepArgs& s, const ModelPt
             return launch_attn(s, layer, n_items, st);
         case K_COMBINE:
             if (lc.nload > 0) return hipErrorInvalidValue;
-            hipLaunchKernelGGL(k_attn_combine, dim3(s.H, n_items), dim3(64), 0, st, s);
-            return hipGetLastError();
+            return launch_combine(s, n_items, st);
         case K_WO:
             if (mm) return mm_gemv(1, s, w, layer, n_items, 1, nullptr, nullptr, st);
             return gemv(lc.nload > 0 ? G_WO_SHORT : G_WO_LONG, s, w, layer, n_items, st, lc);

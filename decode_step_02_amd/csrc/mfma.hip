@@ -330,6 +330,22 @@ __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, 
     const float* xrow = src + static_cast<size_t>(min(item, n_items - 1)) * K + kq * 8;
     const float* grow = NORM ? gain + kq * 8 : nullptr;
 
+    // the epilogue's own loads go first: the residual row (Wo, W2) or the
+    // position, slot and RoPE angle (Q/K/V) of the row this lane finishes
+    const int ri = kq * 4 + wave;  // tile row this lane finishes (r = wave)
+    const int item_c = min(item, n_items - 1);
+    float xres = 0.f, rc = 1.f, rsn = 0.f;
+    int pos = 0, slot = 0;
+    if (KIND == MM_WO || KIND == MM_W2) xres = s.x[static_cast<size_t>(item_c) * s.d + min(tile * 16 + ri, N - 1)];
+    if (KIND == MM_QKV) {
+        pos = s.pos[item_c];
+        slot = ident ? item_c : s.slot[item_c];
+        if (roped) {
+            const int ii = ((is_q ? tile : tile - nq_t) * 8 + (ri & 7)) % half_d;
+            rc = s.rope_cos[static_cast<size_t>(pos) * half_d + ii];
+            rsn = s.rope_sin[static_cast<size_t>(pos) * half_d + ii];
+        }
+    }
     // every load of the wave's k-steps (wave-uniform count)
     const int nks = K / 32;
     uint4 wa[MAXS], wb[MAXS];
@@ -396,7 +412,7 @@ __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, 
     }
     if (NORM) red[wave][8][lane] = ss;
     __syncthreads();
-    const int r = wave;  // this wave finishes tile row kq * 4 + r
+    const int r = wave;  // this wave finishes tile row kq * 4 + r (= ri)
     float y = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
     float y3 = TWO ? red[0][4 + r][lane] + red[1][4 + r][lane] + red[2][4 + r][lane] + red[3][4 + r][lane] : 0.f;
     float r_m = 1.f;
@@ -404,19 +420,16 @@ __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, 
         const float sq = red[0][8][lane] + red[1][8][lane] + red[2][8][lane] + red[3][8][lane];
         r_m = 1.0f / sqrtf(sq / static_cast<float>(K) + s.eps);
     }
-    const int i = kq * 4 + r;
+    const int i = ri;
     if (KIND == MM_QKV) {
         y *= r_m;
         const float partner = __shfl_xor(y, 32);  // tile rows i and i ^ 8 of the same item
         if (!m_ok || tile * 16 >= N) return;
-        const int pos = s.pos[item];
-        const int slot = ident ? item : s.slot[item];
         if (roped) {
             const int p = (is_q ? tile : tile - nq_t) * 8 + (i & 7);
             const int ii = p % half_d, second = i >> 3;
             const int orow = (p / half_d) * D + ii + second * half_d;
-            const float c = s.rope_cos[static_cast<size_t>(pos) * half_d + ii];
-            const float sn = s.rope_sin[static_cast<size_t>(pos) * half_d + ii];
+            const float c = rc, sn = rsn;
             const float out = second ? fmaf(partner, sn, y * c) : fmaf(-partner, sn, y * c);
             if (is_q)
                 s.q[static_cast<size_t>(item) * s.H * D + orow] = out;
@@ -428,7 +441,7 @@ __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, 
         }
     } else if (KIND == MM_WO || KIND == MM_W2) {
         const int orow = tile * 16 + i;
-        if (m_ok && orow < N) s.x[static_cast<size_t>(item) * s.d + orow] += y;
+        if (m_ok && orow < N) s.x[static_cast<size_t>(item) * s.d + orow] = xres + y;
     } else {  // MM_W13
         const int orow = tile * 16 + i;
         const float a = y * r_m, u = y3 * r_m;
