@@ -885,10 +885,13 @@ __global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
 
 // ---- launch configuration ------------------------------------------------------------------------
 
-static int pick_g(int K, int wdt) {
+// Lanes per row: more for longer rows; and two rows per wave instead of four
+// when the launch would otherwise hold fewer than 2048 waves (rows = weight
+// rows x items), so that every CU has the loads of several waves in flight.
+static int pick_g(int K, int wdt, int rows = 1 << 30) {
     const int nch = K / (wdt == kBF16 ? 8 : 4);
     if (nch <= 128) return 8;
-    if (nch <= 512) return 16;
+    if (nch <= 512) return rows >= 4 * 2048 ? 16 : 32;
     return 32;
 }
 
@@ -971,7 +974,12 @@ static hipError_t launch2(Gemv which, int waves, const StepArgs& s, const LayerW
 template <int WDT>
 static hipError_t launch1(Gemv which, int K, int waves, const StepArgs& s, const LayerW& w, int layer,
                           int n_items, hipStream_t st, const float* out_norm, const void* wcls, Launch lc) {
-    switch (pick_g(K, WDT)) {
+    int N = s.d;  // Wo, W2
+    if (which == G_QKV) N = (s.H + 2 * s.Hkv) * s.D;
+    if (which == G_W13) N = s.F;
+    // the logits keep the row-independent choice (their argmax partial count is fixed per shape)
+    const int rows = which == G_LOGITS ? 1 << 30 : N * n_items;
+    switch (pick_g(K, WDT, rows)) {
         case 8: return launch2<WDT, 8>(which, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
         case 16: return launch2<WDT, 16>(which, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
         default: return launch2<WDT, 32>(which, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
