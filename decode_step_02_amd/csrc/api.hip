@@ -378,6 +378,9 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     s.mm_split = 1;
     const char* skenv = std::getenv("DS_MM_SPLIT");  // "0" keeps the tiled MFMA kernel for every projection
     if (skenv && std::strcmp(skenv, "0") == 0) s.mm_split = 0;
+    s.attn_g = 1;
+    const char* agenv = std::getenv("DS_ATTN_G");  // "0" keeps the shuffle-reduced attention kernel
+    if (agenv && std::strcmp(agenv, "0") == 0) s.attn_g = 0;
     const char* sa = std::getenv("DS_SHORT_ATTN");  // "0" turns the fused short-context path off
     if (sa && std::strcmp(sa, "0") == 0) s.short_n = 0;
     ds::PersistArgs& pa = kv->pa;

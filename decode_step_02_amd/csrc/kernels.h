@@ -53,6 +53,7 @@ struct StepArgs {
     int short_n;         // contexts up to this many positions take the fused short path (0: never)
     int mm_ok;           // shapes allow the MFMA projections
     int mm_split;        // the narrow projections may take the split-K MFMA kernel
+    int attn_g;          // head_dim 64 / 128 attention takes the DPP-reduced kernel
     float eps;
     const void* emb;
     float* cache;        // (L, 2, B, Hkv, T, D)

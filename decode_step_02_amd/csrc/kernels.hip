@@ -635,6 +635,157 @@ __global__ __launch_bounds__(256) void k_attn_d(StepArgs s, int layer) {
     (void)GPW;
 }
 
+// Split-K decode attention for head_dim 64 or 128 with REP query heads per
+// key/value head: a block of four waves per 64-position chunk of one (item,
+// group), wave w taking positions t0 + 16w .. t0 + 16w + 15.
+//  - Keys: 8 lanes per row, lane q holding dims 32f + 4q .. 32f + 4q + 3
+//    (f < D/32), so each load instruction reads whole 128-byte lines; the
+//    wave's 16 rows are two slots of 8 rows, and each dot product is reduced
+//    over its 8 lanes with DPP moves.
+//  - Values: D/64 dims per lane, so a load instruction reads one row.
+//  - The softmax weights of the chunk go through LDS; max and sum are taken
+//    over the block, the weighted values summed over the four waves in LDS.
+// Partials as k_attn_d: (m, l) and the weighted sum per (item, head, chunk).
+template <int D, int REP>
+__global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
+    constexpr int KF = D / 32;   // key float4s per lane and row
+    constexpr int DPL = D / 64;  // value dims per lane
+    static_assert(D == 64 || D == 128, "head_dim");
+    static_assert(kChunk == 64, "four waves of 16 positions");
+    __shared__ float pw[REP][kChunk];
+    __shared__ float wred[2][4][REP];
+    __shared__ float ored[4][REP][D];
+    const int chunk = blockIdx.x, g = blockIdx.y, item = blockIdx.z;
+    const int pos = s.pos[item], slot = s.slot[item];
+    const int n = pos + 1;
+    const int t0 = chunk * kChunk;
+    if (t0 >= n) return;  // whole block
+    const int nt = min(kChunk, n - t0);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int kq = lane & 7, rr = lane >> 3;
+    const float* Kb = s.cache + cache_row(s, layer, 0, slot, g, t0);
+    const float* Vb = s.cache + cache_row(s, layer, 1, slot, g, t0);
+    float4 kr[2][KF];
+#pragma unroll
+    for (int sl = 0; sl < 2; sl++) {
+        const int r = min(wave * 16 + sl * 8 + rr, nt - 1);
+#pragma unroll
+        for (int f = 0; f < KF; f++) kr[sl][f] = *reinterpret_cast<const float4*>(Kb + r * D + f * 32 + kq * 4);
+    }
+    float vr[16][DPL];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const float* vp = Vb + min(wave * 16 + i, nt - 1) * D + lane * DPL;
+        if constexpr (DPL == 1) {
+            vr[i][0] = *vp;
+        } else {
+            const float2 v2 = *reinterpret_cast<const float2*>(vp);
+            vr[i][0] = v2.x;
+            vr[i][1] = v2.y;
+        }
+    }
+    const float* qb = s.q + (static_cast<size_t>(item) * s.H + static_cast<size_t>(g) * REP) * D + kq * 4;
+    float4 qv[REP][KF];
+#pragma unroll
+    for (int j = 0; j < REP; j++) {
+#pragma unroll
+        for (int f = 0; f < KF; f++) qv[j][f] = *reinterpret_cast<const float4*>(qb + j * D + f * 32);
+    }
+    // scores of the lane's two rows for every head, reduced over the row's 8 lanes
+    float sc[REP * 2];
+#pragma unroll
+    for (int j = 0; j < REP; j++) {
+#pragma unroll
+        for (int sl = 0; sl < 2; sl++) {
+            float d = 0.f;
+#pragma unroll
+            for (int f = 0; f < KF; f++) {
+                d = fmaf(kr[sl][f].x, qv[j][f].x, d);
+                d = fmaf(kr[sl][f].y, qv[j][f].y, d);
+                d = fmaf(kr[sl][f].z, qv[j][f].z, d);
+                d = fmaf(kr[sl][f].w, qv[j][f].w, d);
+            }
+            sc[j * 2 + sl] = d;
+        }
+    }
+    group_reduce_n<8, OpSum>(sc, OpSum{});
+    const float scale = 1.0f / sqrtf(static_cast<float>(D));
+    float m[REP];
+#pragma unroll
+    for (int j = 0; j < REP; j++) {
+#pragma unroll
+        for (int sl = 0; sl < 2; sl++)
+            sc[j * 2 + sl] = wave * 16 + sl * 8 + rr < nt ? sc[j * 2 + sl] * scale : -INFINITY;
+        m[j] = OpMax{}(sc[j * 2], sc[j * 2 + 1]);
+    }
+    group_reduce_n<64, OpMax, 8>(m, OpMax{});  // over the wave's 8-lane row groups
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < REP; j++) wred[0][wave][j] = m[j];
+    }
+    __syncthreads();
+    float l[REP];
+#pragma unroll
+    for (int j = 0; j < REP; j++) {
+        m[j] = OpMax{}(OpMax{}(wred[0][0][j], wred[0][1][j]), OpMax{}(wred[0][2][j], wred[0][3][j]));
+        l[j] = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < 2; sl++) {
+            const float p = __expf(sc[j * 2 + sl] - m[j]);  // 0 for masked rows (the block max is finite)
+            if (kq == 0) pw[j][wave * 16 + sl * 8 + rr] = p;
+            l[j] += p;
+        }
+    }
+    group_reduce_n<64, OpSum, 8>(l, OpSum{});
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < REP; j++) wred[1][wave][j] = l[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < REP; j++) {
+        const float4* pj = reinterpret_cast<const float4*>(&pw[j][wave * 16]);
+        float4 pe[4];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; c4++) pe[c4] = pj[c4];
+#pragma unroll
+        for (int dd = 0; dd < DPL; dd++) {
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int c4 = 0; c4 < 4; c4++) {
+                a0 = fmaf(pe[c4].x, vr[4 * c4 + 0][dd], a0);
+                a1 = fmaf(pe[c4].y, vr[4 * c4 + 1][dd], a1);
+                a0 = fmaf(pe[c4].z, vr[4 * c4 + 2][dd], a0);
+                a1 = fmaf(pe[c4].w, vr[4 * c4 + 3][dd], a1);
+            }
+            ored[wave][j][lane * DPL + dd] = a0 + a1;
+        }
+    }
+    __syncthreads();
+    const int S = s.n_chunks;
+    for (int idx = threadIdx.x; idx < REP * D; idx += 256) {
+        const int j = idx / D, e = idx % D;
+        const float v = (ored[0][j][e] + ored[1][j][e]) + (ored[2][j][e] + ored[3][j][e]);
+        const size_t pidx = (static_cast<size_t>(item) * s.H + g * REP + j) * S + chunk;
+        s.part_o[pidx * D + e] = v;
+        if (e == 0) {
+            s.part_ml[pidx * 2 + 0] = m[j];
+            s.part_ml[pidx * 2 + 1] = (wred[1][0][j] + wred[1][1][j]) + (wred[1][2][j] + wred[1][3][j]);
+        }
+    }
+}
+
+template <int D>
+static bool launch_attn_g(const StepArgs& s, dim3 grid, int layer, hipStream_t st) {
+    switch (s.H / s.Hkv) {
+        case 1: hipLaunchKernelGGL((k_attn_g<D, 1>), grid, dim3(256), 0, st, s, layer); return true;
+        case 2: hipLaunchKernelGGL((k_attn_g<D, 2>), grid, dim3(256), 0, st, s, layer); return true;
+        case 3: hipLaunchKernelGGL((k_attn_g<D, 3>), grid, dim3(256), 0, st, s, layer); return true;
+        case 4: hipLaunchKernelGGL((k_attn_g<D, 4>), grid, dim3(256), 0, st, s, layer); return true;
+        default: return false;
+    }
+}
+
 static bool attn_d_supported(int D) { return D == 16 || D == 32 || D == 64 || D == 128 || D == 256; }
 
 static hipError_t launch_attn(const StepArgs& s, int layer, int n_items, hipStream_t st);
@@ -711,10 +862,14 @@ static hipError_t launch_combine(const StepArgs& s, int n_items, hipStream_t st)
         hipLaunchKernelGGL(k_attn_combine<8>, grid, dim3(256), lds, st, s);
     else if (per <= 16)
         hipLaunchKernelGGL(k_attn_combine<16>, grid, dim3(256), lds, st, s);
+    else if (per <= 24)
+        hipLaunchKernelGGL(k_attn_combine<24>, grid, dim3(256), lds, st, s);
     else if (per <= 32)
         hipLaunchKernelGGL(k_attn_combine<32>, grid, dim3(256), lds, st, s);
+    else if (per <= 40)
+        hipLaunchKernelGGL(k_attn_combine<40>, grid, dim3(256), lds, st, s);
     else
-        hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(256), lds, st, s);
+        hipLaunchKernelGGL(k_attn_combine<48>, grid, dim3(256), lds, st, s);
     return hipGetLastError();
 }
 
@@ -1041,6 +1196,8 @@ hipError_t set_kernel_attributes(int lds) {
 
 static hipError_t launch_attn(const StepArgs& s, int layer, int n_items, hipStream_t st) {
     const dim3 grid(s.n_chunks, s.Hkv, n_items);
+    if (s.attn_g && s.D == 64 && launch_attn_g<64>(s, grid, layer, st)) return hipGetLastError();
+    if (s.attn_g && s.D == 128 && launch_attn_g<128>(s, grid, layer, st)) return hipGetLastError();
     switch (s.D) {
         case 16: hipLaunchKernelGGL(k_attn_d<16>, grid, dim3(256), 0, st, s, layer); break;
         case 32: hipLaunchKernelGGL(k_attn_d<32>, grid, dim3(256), 0, st, s, layer); break;

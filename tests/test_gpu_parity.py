@@ -247,6 +247,22 @@ def test_batched_mfma_projections_match_oracle(B, shape, mm_kernel):
     compare(shape, arena, prompts, 3, 64, f"mfma B={B}")
 
 
+@pytest.mark.parametrize("D,H,Hkv", [(64, 2, 2), (64, 4, 2), (64, 6, 2), (64, 8, 2), (128, 4, 1)],
+                         ids=["d64-rep1", "d64-rep2", "d64-rep3", "d64-rep4", "d128-rep4"])
+@pytest.mark.parametrize("kernel", ["dpp", "shfl"])
+def test_split_attention_kernels_match_oracle(D, H, Hkv, kernel, monkeypatch):
+    """The split-K attention of head_dim 64 and 128 (DPP-reduced kernel, and
+    the shuffle-reduced one with DS_ATTN_G=0) over 1..3 64-position chunks,
+    the last one ragged, with the short-context path off."""
+    monkeypatch.setenv("DS_SHORT_ATTN", "0")
+    if kernel == "shfl":
+        monkeypatch.setenv("DS_ATTN_G", "0")
+    shape = synth.small_shape(dim=128, n_heads=H, n_kv_heads=Hkv, head_dim=D, hidden_dim=192, vocab_size=256)
+    arena = synth.make_arena(shape, 14, std=0.1, gain_sigma=0.1)
+    prompts = [synth.random_tokens(600 + b, n, shape.vocab_size) for b, n in enumerate([70, 130, 9])]
+    compare(shape, arena, prompts, 3, 160, f"attention D={D} H={H} Hkv={Hkv} {kernel}")
+
+
 def test_batch1_multi_chunk_attention_tiny():
     """Batch-1 steps past 32 positions merge per-chunk attention partials
     (positions 70..99 span three and four 32-position chunks)."""
