@@ -22,6 +22,9 @@ LIB = os.path.join(HERE, "liboracle.so")
 STRICT_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 
+ORC_F32, ORC_BF16, ORC_Q8 = 0, 1, 2
+
+
 def build(out: str = LIB, extra_flags: list[str] | None = None) -> str:
     """Compile oracle.c into a shared object (``extra_flags`` replaces nothing,
     it is appended: tests use it to build a deliberately contracted copy)."""
@@ -60,6 +63,7 @@ def load(path: str = LIB):
         "orc_widen_bf16": (C.c_float, [C.c_uint16]),
         "orc_widen_bf16_array": (None, [_U16, _F, C.c_size_t]),
         "orc_matvec": (None, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, _F, _F]),
+        "orc_weight": (C.c_float, [C.c_void_p, C.c_int32, C.c_size_t, C.c_size_t, C.c_size_t, C.c_size_t]),
         "orc_rmsnorm": (None, [_F, _F, C.c_int32, C.c_float, _F]),
         "orc_rope_angles": (None, [C.c_int32, C.c_int32, C.c_float, _F, _F]),
         "orc_rope_apply": (None, [_F, C.c_int32, _F, _F]),

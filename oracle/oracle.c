@@ -32,8 +32,19 @@ void orc_widen_bf16_array(const uint16_t* src, float* dst, size_t n) {
     for (size_t i = 0; i < n; i++) dst[i] = orc_widen_bf16(src[i]);
 }
 
-static float weight_at(const void* W, int32_t wdtype, size_t idx) {
+/* Element (r, c) of a [rows][cols] matrix.  ORC_Q8 (see oracle.h): the int8
+ * value times its block's fp32 scale, one rounding; the scales start at the
+ * first 256-byte boundary after the rows*cols int8 values. */
+float orc_weight(const void* W, int32_t wdtype, size_t rows, size_t cols, size_t r, size_t c) {
+    size_t idx = r * cols + c;
     if (wdtype == ORC_BF16) return orc_widen_bf16(((const uint16_t*)W)[idx]);
+    if (wdtype == ORC_Q8) {
+        const int8_t* q = (const int8_t*)W;
+        size_t sbase = (rows * cols + 255u) / 256u * 256u;
+        const float* sc = (const float*)((const uint8_t*)W + sbase);
+        float s = sc[r * (cols / 32u) + c / 32u];
+        return s * (float)q[idx];
+    }
     return ((const float*)W)[idx];
 }
 
@@ -45,10 +56,9 @@ static float weight_at(const void* W, int32_t wdtype, size_t idx) {
 void orc_matvec(const void* W, int32_t wdtype, int32_t n_out, int32_t n_in, const float* x,
                 float* y) {
     for (int32_t i = 0; i < n_out; i++) {
-        size_t row = (size_t)i * (size_t)n_in;
         float acc = 0.0f;
         for (int32_t j = 0; j < n_in; j++) {
-            float prod = weight_at(W, wdtype, row + (size_t)j) * x[j];
+            float prod = orc_weight(W, wdtype, (size_t)n_out, (size_t)n_in, (size_t)i, (size_t)j) * x[j];
             acc = acc + prod;
         }
         y[i] = acc;
@@ -247,6 +257,7 @@ int32_t orc_n_tensors(const orc_config* c) {
 }
 
 static size_t mat_bytes(const orc_config* c, size_t rows, size_t cols) {
+    if (c->weight_dtype == ORC_Q8) return (rows * cols + 255u) / 256u * 256u + rows * (cols / 32u) * 4u;
     return rows * cols * (c->weight_dtype == ORC_BF16 ? 2u : 4u);
 }
 
@@ -333,7 +344,7 @@ int32_t orc_forward(const orc_config* c, const uint8_t* arena, float* cache, int
 
     /* embedding row, widened ([GOT] "Loading the model and tokenizer") */
     const void* emb = arena + off[0];
-    for (int32_t j = 0; j < d; j++) x[j] = weight_at(emb, wd, (size_t)token * d + j);
+    for (int32_t j = 0; j < d; j++) x[j] = orc_weight(emb, wd, (size_t)V, (size_t)d, (size_t)token, (size_t)j);
 
     orc_rope_angles(pos, D, c->rope_theta, cs, sn);
     for (int32_t l = 0; l < c->n_layers; l++) {

@@ -21,12 +21,18 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+/* Matrix storage.  ORC_Q8 is the block-quantised int8 reading of "simple-llm
+ * / kasahare" (section "Where to go from here": INT8 weight loading,
+ * block-quantised as in GGUF): a matrix [rows][cols] is int8 q[rows][cols]
+ * row-major, then, from the next 256-byte boundary of the tensor, fp32
+ * s[rows][cols/32]; element (r, c) is the fp32 product s[r][c/32] * q[r][c].
+ * cols is a multiple of 32. */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8 = 2 };
 
 typedef struct {
     int32_t dim, n_layers, n_heads, n_kv_heads, head_dim, hidden_dim, vocab_size;
     int32_t tied_embeddings;
-    int32_t weight_dtype; /* ORC_F32 or ORC_BF16 for matrices; gains are fp32 */
+    int32_t weight_dtype; /* ORC_F32, ORC_BF16 or ORC_Q8 for matrices; gains are fp32 */
     float rope_theta, norm_eps;
 } orc_config;
 
@@ -35,6 +41,8 @@ float orc_widen_bf16(uint16_t h);
 void orc_widen_bf16_array(const uint16_t* src, float* dst, size_t n);
 void orc_matvec(const void* W, int32_t wdtype, int32_t n_out, int32_t n_in,
                 const float* x, float* y);
+/* Element (r, c) of a [rows][cols] matrix stored as wdtype, as fp32. */
+float orc_weight(const void* W, int32_t wdtype, size_t rows, size_t cols, size_t r, size_t c);
 void orc_rmsnorm(const float* x, const float* g, int32_t n, float eps, float* y);
 void orc_rope_angles(int32_t pos, int32_t head_dim, float theta, float* c, float* s);
 void orc_rope_apply(float* v, int32_t head_dim, const float* c, const float* s);

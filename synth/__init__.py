@@ -31,7 +31,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 ALIGN = 256
-F32, BF16 = 0, 1
+F32, BF16, Q8 = 0, 1, 2
+Q8_BLOCK = 32  # weights per fp32 scale of a Q8 matrix row
 _CHUNK = 1 << 22  # elements per independent random stream
 
 
@@ -45,7 +46,7 @@ class ModelShape:
     hidden_dim: int
     vocab_size: int
     tied_embeddings: int
-    weight_dtype: int  # F32 or BF16
+    weight_dtype: int  # F32, BF16 or Q8
     rope_theta: float
     norm_eps: float
 
@@ -59,7 +60,8 @@ class ModelShape:
 
     @property
     def wbytes(self) -> int:
-        return 2 if self.weight_dtype == BF16 else 4
+        """Bytes per matrix element (Q8: the int8 value, its scale not counted)."""
+        return {BF16: 2, Q8: 1}.get(self.weight_dtype, 4)
 
     def as_tuple(self):
         return dataclasses.astuple(self)
@@ -123,9 +125,29 @@ def tensor_table(m: ModelShape):
     out, off = [], 0
     for name, shape, dt in mats:
         out.append((name, off, shape, dt))
-        n = int(np.prod(shape)) * (2 if dt == BF16 else 4)
+        n = tensor_bytes(shape, dt)
         off = (off + n + ALIGN - 1) // ALIGN * ALIGN
     return out, off
+
+
+def tensor_bytes(shape, dt) -> int:
+    """Bytes of one arena tensor.  Q8 [rows][cols]: int8 values, then fp32
+    scales [rows][cols / 32] from the next 256-byte boundary."""
+    n = int(np.prod(shape))
+    if dt == Q8:
+        return (n + ALIGN - 1) // ALIGN * ALIGN + 4 * (n // Q8_BLOCK)
+    return n * (2 if dt == BF16 else 4)
+
+
+def quantize_q8(w: np.ndarray):
+    """Block-quantise fp32 weights (a flat run of whole 32-weight blocks) to
+    int8 values and fp32 scales: s = max|w| / 127 per block, q = round(w / s)
+    to nearest even.  An all-zero block gets s = 1 and q = 0."""
+    b = w.reshape(-1, Q8_BLOCK).astype(np.float32)
+    amax = np.abs(b).max(axis=1)
+    sc = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    q = np.clip(np.rint(b / sc[:, None]), -127, 127).astype(np.int8)
+    return q.reshape(-1), sc
 
 
 def arena_bytes(m: ModelShape) -> int:
@@ -139,7 +161,7 @@ def _round_bf16(f32: np.ndarray) -> np.ndarray:
     return u.astype(np.uint16)
 
 
-def _fill_matrix(dst, n, dtype_code, seed, tensor_index, std):
+def _fill_matrix(dst, n, dtype_code, seed, tensor_index, std, scales=None, exact=False):
     """Fill ``dst`` (flat view, n elements) with N(0, std) draws.
 
     Each block of ``_CHUNK`` elements has its own PCG64 stream keyed by
@@ -155,20 +177,34 @@ def _fill_matrix(dst, n, dtype_code, seed, tensor_index, std):
         g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor_index, c0 // _CHUNK])))
         v = g.standard_normal(c1 - c0, dtype=np.float32)
         v *= np.float32(std)
+        if exact:  # k / 4096 with |k| <= 127: exact in bf16, and q = k with s = 2^-12 in Q8
+            k = np.clip(np.rint(v * np.float32(4096.0)), -127, 127)
+            if dtype_code == Q8:
+                dst[c0:c1] = k.astype(np.int8)
+                scales[c0 // Q8_BLOCK:c1 // Q8_BLOCK] = np.float32(1.0 / 4096.0)
+                return
+            v = (k / np.float32(4096.0)).astype(np.float32)
         if dtype_code == BF16:
             dst[c0:c1] = _round_bf16(v)
+        elif dtype_code == Q8:
+            q, sc = quantize_q8(v)
+            dst[c0:c1] = q
+            scales[c0 // Q8_BLOCK:c1 // Q8_BLOCK] = sc
         else:
             dst[c0:c1] = v
     return jobs, one
 
 
 def make_arena(m: ModelShape, seed: int, std: float = 0.02, gain_sigma: float = 0.0,
-               threads: int | None = None, out: np.ndarray | None = None) -> np.ndarray:
+               threads: int | None = None, out: np.ndarray | None = None, exact: bool = False) -> np.ndarray:
     """Generate the seeded weight arena as a flat uint8 array.
 
-    Matrices ~ N(0, std) rounded to the storage dtype.  Norm gains are 1.0, or
-    1 + N(0, gain_sigma) when ``gain_sigma`` > 0 (used to exercise the gain
-    multiply in small tests).
+    Matrices ~ N(0, std) rounded to the storage dtype (Q8: block-quantised by
+    quantize_q8).  Norm gains are 1.0, or 1 + N(0, gain_sigma) when
+    ``gain_sigma`` > 0 (used to exercise the gain multiply in small tests).
+    With ``exact`` every weight is k / 4096 for an integer |k| <= 127 (the
+    N(0, std) draw rounded to that grid): a BF16 arena and a Q8 arena of the
+    same shape and seed then hold the same weight values.
     """
     table, total = tensor_table(m)
     arena = out if out is not None else np.zeros(total, dtype=np.uint8)
@@ -185,9 +221,15 @@ def make_arena(m: ModelShape, seed: int, std: float = 0.02, gain_sigma: float = 
             else:
                 g[:] = np.float32(1.0)
             continue
-        esz = 2 if dt == BF16 else 4
-        flat = arena[off:off + esz * n].view(np.uint16 if dt == BF16 else np.float32)
-        jobs, fn = _fill_matrix(flat, n, dt, seed, ti, std)
+        scales = None
+        if dt == Q8:
+            flat = arena[off:off + n].view(np.int8)
+            s0 = off + (n + ALIGN - 1) // ALIGN * ALIGN
+            scales = arena[s0:s0 + 4 * (n // Q8_BLOCK)].view(np.float32)
+        else:
+            esz = 2 if dt == BF16 else 4
+            flat = arena[off:off + esz * n].view(np.uint16 if dt == BF16 else np.float32)
+        jobs, fn = _fill_matrix(flat, n, dt, seed, ti, std, scales, exact)
         all_jobs += [(fn, j) for j in jobs]
     if threads <= 1 or len(all_jobs) <= 1:
         for fn, j in all_jobs:
@@ -206,6 +248,11 @@ def views(m: ModelShape, arena: np.ndarray) -> dict:
         n = int(np.prod(shape))
         if dt == BF16:
             out[name] = arena[off:off + 2 * n].view(np.uint16).reshape(shape)
+        elif dt == Q8:
+            s0 = off + (n + ALIGN - 1) // ALIGN * ALIGN
+            out[name] = arena[off:off + n].view(np.int8).reshape(shape)
+            out[name + ".scale"] = arena[s0:s0 + 4 * (n // Q8_BLOCK)].view(np.float32).reshape(
+                shape[0], shape[1] // Q8_BLOCK)
         else:
             out[name] = arena[off:off + 4 * n].view(np.float32).reshape(shape)
     return out
