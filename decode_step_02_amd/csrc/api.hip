@@ -45,7 +45,14 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-size_t wsize(const ds_config* c) { return c->weight_dtype == DS_BF16 ? 2 : 4; }
+size_t wsize(const ds_config* c) { return c->weight_dtype == DS_BF16 ? 2 : c->weight_dtype == DS_Q8 ? 1 : 4; }
+
+// Bytes of one [rows][cols] matrix; DS_Q8: the int8 values, then from the
+// next 256-byte boundary one fp32 scale per 32 values of a row.
+size_t mat_bytes(const ds_config* c, size_t rows, size_t cols) {
+    if (c->weight_dtype == DS_Q8) return round_up(rows * cols, kAlign) + 4 * rows * (cols / 32);
+    return rows * cols * wsize(c);
+}
 
 // Shape checks shared by every entry point.  Returns DS_OK or an error with
 // the reason in g_err.
@@ -54,8 +61,11 @@ ds_status check_config(const ds_config* c) {
     if (c->dim <= 0 || c->n_layers <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
         c->head_dim <= 0 || c->hidden_dim <= 0 || c->vocab_size <= 0)
         return fail(DS_ERR_INVALID_ARG, "every dimension must be positive");
-    if (c->weight_dtype != DS_F32 && c->weight_dtype != DS_BF16)
-        return fail(DS_ERR_INVALID_ARG, "weight_dtype must be DS_F32 or DS_BF16");
+    if (c->weight_dtype != DS_F32 && c->weight_dtype != DS_BF16 && c->weight_dtype != DS_Q8)
+        return fail(DS_ERR_INVALID_ARG, "weight_dtype must be DS_F32, DS_BF16 or DS_Q8");
+    if (c->weight_dtype == DS_Q8 &&
+        (c->dim % 32 || (static_cast<int64_t>(c->n_heads) * c->head_dim) % 32 || c->hidden_dim % 32))
+        return fail(DS_ERR_UNSUPPORTED, "DS_Q8 needs dim, n_heads*head_dim and hidden_dim multiples of 32");
     if (c->n_heads % c->n_kv_heads != 0)
         return fail(DS_ERR_INVALID_ARG, "n_heads (%d) is not a multiple of n_kv_heads (%d)", c->n_heads,
                     c->n_kv_heads);
@@ -83,7 +93,7 @@ int n_tensors(const ds_config* c) { return 1 + 9 * c->n_layers + 1 + (c->tied_em
 // Canonical arena offsets (weight order of "simple-llm / kasahare", section
 // "On-disk model format (.sllm)", 256-byte aligned, untied head last).
 size_t layout(const ds_config* c, std::vector<size_t>* off) {
-    const size_t d = c->dim, F = c->hidden_dim, V = c->vocab_size, w = wsize(c);
+    const size_t d = c->dim, F = c->hidden_dim, V = c->vocab_size;
     const size_t qr = static_cast<size_t>(c->n_heads) * c->head_dim;
     const size_t kvr = static_cast<size_t>(c->n_kv_heads) * c->head_dim;
     size_t p = 0;
@@ -91,20 +101,20 @@ size_t layout(const ds_config* c, std::vector<size_t>* off) {
         if (off) off->push_back(p);
         p = round_up(p + bytes, kAlign);
     };
-    put(V * d * w);
+    put(mat_bytes(c, V, d));
     for (int l = 0; l < c->n_layers; l++) {
         put(d * 4);
-        put(qr * d * w);
-        put(kvr * d * w);
-        put(kvr * d * w);
-        put(d * qr * w);
+        put(mat_bytes(c, qr, d));
+        put(mat_bytes(c, kvr, d));
+        put(mat_bytes(c, kvr, d));
+        put(mat_bytes(c, d, qr));
         put(d * 4);
-        put(F * d * w);
-        put(F * d * w);
-        put(d * F * w);
+        put(mat_bytes(c, F, d));
+        put(mat_bytes(c, F, d));
+        put(mat_bytes(c, d, F));
     }
     put(d * 4);
-    if (!c->tied_embeddings) put(V * d * w);
+    if (!c->tied_embeddings) put(mat_bytes(c, V, d));
     return p;
 }
 

@@ -61,6 +61,35 @@ template <> struct Wt<kBF16> {
     }
 };
 
+// Block-quantised int8: 16 values per chunk (half a 32-value block); the
+// dot product of one chunk, before its block's scale.
+template <> struct Wt<kQ8> {
+    static constexpr int EPC = 16;
+    __device__ static __forceinline__ uint4 load(const void* base, size_t elem) {
+        return *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(base) + elem);
+    }
+    __device__ static __forceinline__ float dot(const uint4 u, const float* xs, float acc) {
+        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float4 a = *reinterpret_cast<const float4*>(xs + 4 * k);
+            const int32_t v = static_cast<int32_t>(wv[k]);
+            acc = fmaf(static_cast<float>((v << 24) >> 24), a.x, acc);
+            acc = fmaf(static_cast<float>((v << 16) >> 24), a.y, acc);
+            acc = fmaf(static_cast<float>((v << 8) >> 24), a.z, acc);
+            acc = fmaf(static_cast<float>(v >> 24), a.w, acc);
+        }
+        return acc;
+    }
+};
+
+// Scales of a Q8 matrix [rows][K]: they start at the first 256-byte boundary
+// after its rows * K int8 values.
+__device__ __forceinline__ const float* q8_scales(const void* W, size_t rows, int K) {
+    const size_t nb = (rows * static_cast<size_t>(K) + 255) / 256 * 256;
+    return reinterpret_cast<const float*>(static_cast<const uint8_t*>(W) + nb);
+}
+
 template <> struct Wt<kF32> {
     static constexpr int EPC = 4;
     __device__ static __forceinline__ uint4 load(const void* base, size_t elem) {
@@ -82,24 +111,30 @@ template <> struct Wt<kF32> {
 template <int WDT, int G>
 struct RowStream {
     static constexpr int EPC = Wt<WDT>::EPC;
+    static constexpr bool Q8 = WDT == kQ8;
     uint4 w[kPrefetch];
+    float sc[Q8 ? kPrefetch : 1];  // Q8: the block scale of each prefetched chunk
     const void* W;
+    const float* S;  // Q8: the row's block scales
     size_t base;
     int nch, sub;
 
     // Loads are unconditional (the chunk index is clamped into the row, the
     // value masked afterwards): a guarded load becomes a branch, and the
-    // compiler then waits for every load before the next one.
-    __device__ __forceinline__ void start(const void* W_, size_t row, int K, int sub_, bool valid) {
+    // compiler then waits for every load before the next one.  `rows` (the
+    // matrix's row count) locates the scales of a Q8 matrix.
+    __device__ __forceinline__ void start(const void* W_, size_t row, int K, int sub_, bool valid, size_t rows = 0) {
         W = W_;
         base = row * static_cast<size_t>(K);
         sub = sub_;
         nch = valid ? K / EPC : 0;
         const int last = K / EPC - 1;
+        if constexpr (Q8) S = q8_scales(W_, rows, K) + row * static_cast<size_t>(K / 32);
 #pragma unroll
         for (int p = 0; p < kPrefetch; p++) {
             const int c = sub + p * G;
             w[p] = Wt<WDT>::load(W, base + static_cast<size_t>(min(c, last)) * EPC);
+            if constexpr (Q8) sc[p] = S[min(c, last) >> 1];
         }
 #pragma unroll
         for (int p = 0; p < kPrefetch; p++) {
@@ -111,14 +146,24 @@ struct RowStream {
         }
     }
 
+    // acc + the chunk's products (times its block scale for Q8)
+    __device__ __forceinline__ static float chunk(uint4 u, float scale, const float* xs, float acc) {
+        if constexpr (Q8) return fmaf(scale, Wt<WDT>::dot(u, xs, 0.f), acc);
+        return Wt<WDT>::dot(u, xs, acc);
+    }
+    __device__ __forceinline__ float scale_of(int c) const {
+        if constexpr (Q8) return S[c >> 1];
+        return 1.f;
+    }
+
     __device__ __forceinline__ float finish(const float* xs) const {
         float a0 = 0.f, a1 = 0.f;
         const int last = nch > 0 ? nch - 1 : 0;
 #pragma unroll
         for (int p = 0; p < kPrefetch; p += 2) {
             // masked chunks are zero; the LDS index is clamped so it stays in range
-            a0 = Wt<WDT>::dot(w[p], xs + min(sub + p * G, last) * EPC, a0);
-            if (p + 1 < kPrefetch) a1 = Wt<WDT>::dot(w[p + 1], xs + min(sub + (p + 1) * G, last) * EPC, a1);
+            a0 = chunk(w[p], sc[Q8 ? p : 0], xs + min(sub + p * G, last) * EPC, a0);
+            if (p + 1 < kPrefetch) a1 = chunk(w[p + 1], sc[Q8 ? p + 1 : 0], xs + min(sub + (p + 1) * G, last) * EPC, a1);
         }
         int c = sub + kPrefetch * G;
         for (; c + 3 * G < nch; c += 4 * G) {
@@ -126,12 +171,13 @@ struct RowStream {
             const uint4 u1 = Wt<WDT>::load(W, base + static_cast<size_t>(c + G) * EPC);
             const uint4 u2 = Wt<WDT>::load(W, base + static_cast<size_t>(c + 2 * G) * EPC);
             const uint4 u3 = Wt<WDT>::load(W, base + static_cast<size_t>(c + 3 * G) * EPC);
-            a0 = Wt<WDT>::dot(u0, xs + c * EPC, a0);
-            a1 = Wt<WDT>::dot(u1, xs + (c + G) * EPC, a1);
-            a0 = Wt<WDT>::dot(u2, xs + (c + 2 * G) * EPC, a0);
-            a1 = Wt<WDT>::dot(u3, xs + (c + 3 * G) * EPC, a1);
+            const float s0 = scale_of(c), s1 = scale_of(c + G), s2 = scale_of(c + 2 * G), s3 = scale_of(c + 3 * G);
+            a0 = chunk(u0, s0, xs + c * EPC, a0);
+            a1 = chunk(u1, s1, xs + (c + G) * EPC, a1);
+            a0 = chunk(u2, s2, xs + (c + 2 * G) * EPC, a0);
+            a1 = chunk(u3, s3, xs + (c + 3 * G) * EPC, a1);
         }
-        for (; c < nch; c += G) a0 = Wt<WDT>::dot(Wt<WDT>::load(W, base + static_cast<size_t>(c) * EPC), xs + c * EPC, a0);
+        for (; c < nch; c += G) a0 = chunk(Wt<WDT>::load(W, base + static_cast<size_t>(c) * EPC), scale_of(c), xs + c * EPC, a0);
         return group_sum<G>(a0 + a1);
     }
 };
@@ -261,6 +307,10 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs s, BeginList list, const
     if (s.wdt == kBF16) {
         const uint16_t* e = static_cast<const uint16_t*>(s.emb) + row;
         for (int j = threadIdx.x; j < s.d; j += 256) x[j] = __uint_as_float(static_cast<uint32_t>(e[j]) << 16);
+    } else if (s.wdt == kQ8) {
+        const int8_t* e = static_cast<const int8_t*>(s.emb) + row;
+        const float* sc = q8_scales(s.emb, s.V, s.d) + static_cast<size_t>(tok) * (s.d / 32);
+        for (int j = threadIdx.x; j < s.d; j += 256) x[j] = sc[j >> 5] * static_cast<float>(e[j]);
     } else {
         const float* e = static_cast<const float*>(s.emb) + row;
         for (int j = threadIdx.x; j < s.d; j += 256) x[j] = e[j];
@@ -305,7 +355,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(StepArgs s, LayerW w, int la
         W = w.wv;
     }
     RowStream<WDT, G> st;
-    st.start(W, row, s.d, sub, valid);
+    st.start(W, row, s.d, sub, valid, static_cast<size_t>(is_q ? s.H : s.Hkv) * D);
     VecStage<64 * WAVES, 4, true> vs;
     vs.issue(s.x + static_cast<size_t>(item) * s.d, w.attn_norm, s.d);
     float c = 1.f, sn = 0.f;
@@ -891,7 +941,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wo(StepArgs s, LayerW w, int lay
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.d;
     RowStream<WDT, G> st;
-    st.start(w.wo, valid ? row : 0, K, sub, valid);
+    st.start(w.wo, valid ? row : 0, K, sub, valid, s.d);
     float* xr = s.x + static_cast<size_t>(item) * s.d + row;
     const float x_old = (valid && sub == 0) ? *xr : 0.f;
     if (SHORT) {
@@ -920,8 +970,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_w13(StepArgs s, LayerW w) {
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.F;
     RowStream<WDT, G> s1, s3;
-    s1.start(w.w1, valid ? row : 0, s.d, sub, valid);
-    s3.start(w.w3, valid ? row : 0, s.d, sub, valid);
+    s1.start(w.w1, valid ? row : 0, s.d, sub, valid, s.F);
+    s3.start(w.w3, valid ? row : 0, s.d, sub, valid, s.F);
     VecStage<64 * WAVES, 4, true> vs;
     vs.issue(s.x + static_cast<size_t>(item) * s.d, w.ffn_norm, s.d);
     vs.template complete_rms<WAVES>(xs, red, s.d, s.eps);
@@ -943,7 +993,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w2(StepArgs s, LayerW w) {
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.d;
     RowStream<WDT, G> st;
-    st.start(w.w2, valid ? row : 0, s.F, sub, valid);
+    st.start(w.w2, valid ? row : 0, s.F, sub, valid, s.d);
     float* xr = s.x + static_cast<size_t>(item) * s.d + row;
     const float x_old = (valid && sub == 0) ? *xr : 0.f;
     VecStage<64 * WAVES, 8, false> vs;
@@ -968,7 +1018,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_logits(StepArgs s, const float* 
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.V;
     RowStream<WDT, G> st;
-    st.start(wcls, valid ? row : 0, s.d, sub, valid);
+    st.start(wcls, valid ? row : 0, s.d, sub, valid, s.V);
     VecStage<64 * WAVES, 4, true> vs;
     vs.issue(s.x + static_cast<size_t>(item) * s.d, out_norm, s.d);
     vs.template complete_rms<WAVES>(xs, red, s.d, s.eps);
@@ -1044,7 +1094,7 @@ __global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
 // when the launch would otherwise hold fewer than 2048 waves (rows = weight
 // rows x items), so that every CU has the loads of several waves in flight.
 static int pick_g(int K, int wdt, int rows = 1 << 30) {
-    const int nch = K / (wdt == kBF16 ? 8 : 4);
+    const int nch = K / (wdt == kQ8 ? 16 : wdt == kBF16 ? 8 : 4);
     if (nch <= 128) return 8;
     if (nch <= 512) return rows >= 4 * 2048 ? 16 : 32;
     return 32;
@@ -1155,6 +1205,7 @@ static hipError_t gemv(Gemv which, const StepArgs& s, const LayerW& w, int layer
     int waves = pick_waves(K);
     if (which == G_LOGITS || which == G_WO_SHORT) waves = 4;
     if (s.wdt == kBF16) return launch1<kBF16>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
+    if (s.wdt == kQ8) return launch1<kQ8>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
     return launch1<kF32>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
 }
 
@@ -1187,6 +1238,7 @@ static hipError_t set_attrs1(int lds) {
 hipError_t set_kernel_attributes(int lds) {
     hipError_t e = set_attrs1<kBF16>(lds);
     if (e == hipSuccess) e = set_attrs1<kF32>(lds);
+    if (e == hipSuccess) e = set_attrs1<kQ8>(lds);
     if (e == hipSuccess)
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     return e;

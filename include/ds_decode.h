@@ -50,7 +50,14 @@ typedef enum {
     DS_ERR_DEVICE = -9        /* a device-side consistency check tripped       */
 } ds_status;
 
-typedef enum { DS_F32 = 0, DS_BF16 = 1 } ds_dtype;
+/* Matrix storage.  DS_Q8 is block-quantised int8, the INT8 weight loading
+ * that "simple-llm / kasahare" (section "Where to go from here") names as
+ * its next step: a matrix [rows][cols] is int8 q[rows][cols] row-major, then,
+ * from the next 256-byte boundary, fp32 s[rows][cols/32]; its element (r, c)
+ * is s[r][c/32] * q[r][c].  dim, n_heads*head_dim and hidden_dim must be
+ * multiples of 32.  DS_Q8 models run one launch per operation at every batch
+ * size (no single-launch step, no MFMA projections). */
+typedef enum { DS_F32 = 0, DS_BF16 = 1, DS_Q8 = 2 } ds_dtype;
 
 /* Model shape.  The field order is part of the ABI. */
 typedef struct {
@@ -78,7 +85,8 @@ typedef struct ds_kv ds_kv;
  * w1 [F][d], w3 [F][d], w2 [d][F]; output_norm [d]; and wcls [V][d] when
  * the embeddings are not tied.  This is the weight order of "simple-llm /
  * kasahare" (section "On-disk model format (.sllm)") with the untied head
- * appended.  Matrices are row-major [out][in] in weight_dtype, gains fp32.
+ * appended.  Matrices are row-major [out][in] in weight_dtype (DS_Q8: the
+ * values, then the scales, as above), gains fp32.
  * Returns 0 for an invalid config. */
 size_t ds_weights_bytes(const ds_config* cfg);
 /* Number of tensors in the arena (1 + 9L + 1, plus 1 when untied). */
