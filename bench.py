@@ -17,6 +17,7 @@ that kernel's mean launch duration.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -33,6 +34,12 @@ HBM_PEAK_GBPS = 8000.0
 KERNELS = ["qkv", "attn", "attn_combine", "wo", "w13", "w2", "logits"]
 
 
+DTYPE = {
+    "bf16": "f32 (fp32 accumulation; bf16 weights times fp32 activations as bf16 hi+lo pairs)",
+    "q8": "f32 (fp32 accumulation; int8 weights with an fp32 scale per 32 values, times fp32 activations)",
+}
+
+
 def step_bytes(m: synth.ModelShape, lengths_before: np.ndarray) -> int:
     """Algorithmic HBM bytes of one decode step: every weight matrix once (the
     tied embedding once, as the vocabulary product), the embedding rows
@@ -40,21 +47,26 @@ def step_bytes(m: synth.ModelShape, lengths_before: np.ndarray) -> int:
     written, and the fp32 logits written."""
     table, _ = synth.tensor_table(m)
     B = len(lengths_before)
-    mats = sum(int(np.prod(s)) * (2 if dt == synth.BF16 else 4) for _, _, s, dt in table if len(s) == 2)
+    mats = sum(synth.tensor_bytes(s, dt) for _, _, s, dt in table if len(s) == 2)
     gains = sum(int(np.prod(s)) * 4 for _, _, s, dt in table if len(s) == 1)
     kv_row = m.n_layers * 2 * m.n_kv_heads * m.head_dim * 4
-    gather = B * m.dim * m.wbytes
+    gather = int(B * m.dim * elem_bytes(m))
     kv_read = int(np.sum(lengths_before.astype(np.int64) + 1)) * kv_row
     kv_write = B * kv_row
     logits = B * m.vocab_size * 4
     return mats + gains + gather + kv_read + kv_write + logits
 
 
+def elem_bytes(m: synth.ModelShape) -> float:
+    """Bytes per matrix element, a Q8 element's share of its block scale included."""
+    return 1.0 + 4.0 / synth.Q8_BLOCK if m.weight_dtype == synth.Q8 else float(m.wbytes)
+
+
 def kernel_bytes(m: synth.ModelShape, which: str, B: int, n_ctx: float) -> float:
     """Algorithmic bytes of one launch of a step kernel (weights + activations
     in and out), n_ctx = mean cached positions read by attention."""
     d, F, V, D = m.dim, m.hidden_dim, m.vocab_size, m.head_dim
-    w = m.wbytes
+    w = elem_bytes(m)
     qr, kvr = m.n_heads * D, m.n_kv_heads * D
     if which == "qkv":
         return (qr + 2 * kvr) * d * w + B * (d * 4 + d * 4 + (qr + 2 * kvr) * 4)
@@ -208,6 +220,9 @@ def main():
                          "top-k K, top-p P; seeded uniforms) instead of keeping the greedy ones")
     ap.add_argument("--prefill-batched-only", action="store_true",
                     help="with --prefill: skip the one-position-per-pass prefill (for kernel profiles)")
+    ap.add_argument("--weights", choices=["bf16", "q8"], default="bf16",
+                    help="matrix storage: the workload's bf16, or block-quantised int8 (an fp32 scale per 32 "
+                         "values) from the same seeded draws")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain copy kernel (read N MB, write N MB) three times, as the "
                          "known-size reference for hardware byte counters; its rate is reported")
@@ -220,6 +235,8 @@ def main():
     import decode_step_02_amd as dsa
 
     w = synth.WORKLOADS[args.workload]
+    if args.weights == "q8":
+        w = dataclasses.replace(w, model=dataclasses.replace(w.model, weight_dtype=synth.Q8))
     m = w.model
     arena = synth.make_arena(m, w.model_seed)
     prompts = synth.prompts(w)
@@ -352,6 +369,7 @@ def main():
     traffic, traffic_note = measured_traffic(w.name) if single else (None, "counters taken for the single-launch step only")
     out = {
         "metric": ("decode tok/s (135M-shaped Llama, B=1)" if w.name == "llama135m_p5" else f"decode tok/s ({w.name})")
+                  + (" int8 weights" if args.weights == "q8" else "")
                   + (" with sampling" if samp else ""),
         "value": B * args.steps / (ms_total * 1e-3),
         "unit": "tok/s",
@@ -362,9 +380,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 (fp32 accumulation; bf16 weights times fp32 activations as bf16 hi+lo pairs)",
+        "dtype": DTYPE[args.weights],
         "data": "synthetic (seeded random weights N(0,0.02), uniform prompt ids)",
-        "config": {"workload": w.name, "description": w.description, "batch": B, "ctx": w.ctx,
+        "config": {"workload": w.name, "description": w.description, "batch": B, "ctx": w.ctx, "weights": args.weights,
                    "decode_positions": [int(base.min()), int(base.max() + cycle - 1)],
                    "dispatch": args.dispatch, "single_launch_step": bool(single)},
         "step_bytes": bytes_step,
