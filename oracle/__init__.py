@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 STRICT_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 
-ORC_F32, ORC_BF16, ORC_Q8 = 0, 1, 2
+ORC_F32, ORC_BF16, ORC_Q8, ORC_Q4 = 0, 1, 2, 3
 
 
 def build(out: str = LIB, extra_flags: list[str] | None = None) -> str:

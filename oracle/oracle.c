@@ -45,6 +45,15 @@ float orc_weight(const void* W, int32_t wdtype, size_t rows, size_t cols, size_t
         float s = sc[r * (cols / 32u) + c / 32u];
         return s * (float)q[idx];
     }
+    if (wdtype == ORC_Q4) {
+        const uint8_t* b = (const uint8_t*)W;
+        int nib = (idx & 1u) ? (b[idx / 2u] >> 4) : (b[idx / 2u] & 15);
+        int q = nib >= 8 ? nib - 16 : nib;
+        size_t sbase = (rows * cols / 2u + 255u) / 256u * 256u;
+        const float* sc = (const float*)(b + sbase);
+        float s = sc[r * (cols / 32u) + c / 32u];
+        return s * (float)q;
+    }
     return ((const float*)W)[idx];
 }
 
@@ -258,6 +267,7 @@ int32_t orc_n_tensors(const orc_config* c) {
 
 static size_t mat_bytes(const orc_config* c, size_t rows, size_t cols) {
     if (c->weight_dtype == ORC_Q8) return (rows * cols + 255u) / 256u * 256u + rows * (cols / 32u) * 4u;
+    if (c->weight_dtype == ORC_Q4) return (rows * cols / 2u + 255u) / 256u * 256u + rows * (cols / 32u) * 4u;
     return rows * cols * (c->weight_dtype == ORC_BF16 ? 2u : 4u);
 }
 

@@ -26,13 +26,16 @@ extern "C" {
  * block-quantised as in GGUF): a matrix [rows][cols] is int8 q[rows][cols]
  * row-major, then, from the next 256-byte boundary of the tensor, fp32
  * s[rows][cols/32]; element (r, c) is the fp32 product s[r][c/32] * q[r][c].
- * cols is a multiple of 32. */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8 = 2 };
+ * cols is a multiple of 32.  ORC_Q4 is the 4-bit variant the same section
+ * names: the values are packed two per byte (value c of a row in byte c/2,
+ * the low nibble for even c), each a two's complement integer in [-8, 7],
+ * rows*cols/2 bytes row-major, then the scales as for ORC_Q8. */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8 = 2, ORC_Q4 = 3 };
 
 typedef struct {
     int32_t dim, n_layers, n_heads, n_kv_heads, head_dim, hidden_dim, vocab_size;
     int32_t tied_embeddings;
-    int32_t weight_dtype; /* ORC_F32, ORC_BF16 or ORC_Q8 for matrices; gains are fp32 */
+    int32_t weight_dtype; /* ORC_F32, ORC_BF16, ORC_Q8 or ORC_Q4 for matrices; gains are fp32 */
     float rope_theta, norm_eps;
 } orc_config;
 

@@ -31,8 +31,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 ALIGN = 256
-F32, BF16, Q8 = 0, 1, 2
-Q8_BLOCK = 32  # weights per fp32 scale of a Q8 matrix row
+F32, BF16, Q8, Q4 = 0, 1, 2, 3
+Q8_BLOCK = 32  # weights per fp32 scale of a Q8 or Q4 matrix row
 _CHUNK = 1 << 22  # elements per independent random stream
 
 
@@ -46,7 +46,7 @@ class ModelShape:
     hidden_dim: int
     vocab_size: int
     tied_embeddings: int
-    weight_dtype: int  # F32, BF16 or Q8
+    weight_dtype: int  # F32, BF16, Q8 or Q4
     rope_theta: float
     norm_eps: float
 
@@ -60,8 +60,8 @@ class ModelShape:
 
     @property
     def wbytes(self) -> int:
-        """Bytes per matrix element (Q8: the int8 value, its scale not counted)."""
-        return {BF16: 2, Q8: 1}.get(self.weight_dtype, 4)
+        """Bytes per matrix element (Q8: the int8 value, Q4: half a byte, the scale not counted)."""
+        return {BF16: 2, Q8: 1, Q4: 0.5}.get(self.weight_dtype, 4)
 
     def as_tuple(self):
         return dataclasses.astuple(self)
@@ -136,7 +136,31 @@ def tensor_bytes(shape, dt) -> int:
     n = int(np.prod(shape))
     if dt == Q8:
         return (n + ALIGN - 1) // ALIGN * ALIGN + 4 * (n // Q8_BLOCK)
+    if dt == Q4:
+        return (n // 2 + ALIGN - 1) // ALIGN * ALIGN + 4 * (n // Q8_BLOCK)
     return n * (2 if dt == BF16 else 4)
+
+
+def _values_bytes(n, dt) -> int:
+    """Bytes of the values of an n-element Q8 / Q4 matrix, before its scales."""
+    return n if dt == Q8 else n // 2
+
+
+def quantize_q4(w: np.ndarray):
+    """Block-quantise fp32 weights to 4-bit values packed two per byte (even
+    index in the low nibble, two's complement) and fp32 scales: s = max|w| / 7
+    per 32-weight block, q = round(w / s) to nearest even, clipped to [-8, 7]."""
+    b = w.reshape(-1, Q8_BLOCK).astype(np.float32)
+    amax = np.abs(b).max(axis=1)
+    sc = np.where(amax > 0, amax / np.float32(7.0), np.float32(1.0)).astype(np.float32)
+    q = np.clip(np.rint(b / sc[:, None]), -8, 7).astype(np.int8).reshape(-1)
+    return pack_q4(q), sc
+
+
+def pack_q4(q: np.ndarray) -> np.ndarray:
+    """Pack int values in [-8, 7] two per byte, even index in the low nibble."""
+    u = (q.astype(np.int16) & 15).astype(np.uint8)
+    return (u[0::2] | (u[1::2] << 4)).astype(np.uint8)
 
 
 def quantize_q8(w: np.ndarray):
@@ -177,18 +201,27 @@ def _fill_matrix(dst, n, dtype_code, seed, tensor_index, std, scales=None, exact
         g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor_index, c0 // _CHUNK])))
         v = g.standard_normal(c1 - c0, dtype=np.float32)
         v *= np.float32(std)
-        if exact:  # k / 4096 with |k| <= 127: exact in bf16, and q = k with s = 2^-12 in Q8
-            k = np.clip(np.rint(v * np.float32(4096.0)), -127, 127)
+        if exact:  # the grid k * step, |k| <= kmax: exact in bf16, and q = k with s = step in Q8 / Q4
+            step, kmax = (1.0 / 512.0, 7) if exact == "q4" else (1.0 / 4096.0, 127)
+            k = np.clip(np.rint(v / np.float32(step)), -kmax, kmax)
             if dtype_code == Q8:
                 dst[c0:c1] = k.astype(np.int8)
-                scales[c0 // Q8_BLOCK:c1 // Q8_BLOCK] = np.float32(1.0 / 4096.0)
+                scales[c0 // Q8_BLOCK:c1 // Q8_BLOCK] = np.float32(step)
                 return
-            v = (k / np.float32(4096.0)).astype(np.float32)
+            if dtype_code == Q4:
+                dst[c0 // 2:c1 // 2] = pack_q4(k.astype(np.int8))
+                scales[c0 // Q8_BLOCK:c1 // Q8_BLOCK] = np.float32(step)
+                return
+            v = (k * np.float32(step)).astype(np.float32)
         if dtype_code == BF16:
             dst[c0:c1] = _round_bf16(v)
         elif dtype_code == Q8:
             q, sc = quantize_q8(v)
             dst[c0:c1] = q
+            scales[c0 // Q8_BLOCK:c1 // Q8_BLOCK] = sc
+        elif dtype_code == Q4:
+            q, sc = quantize_q4(v)
+            dst[c0 // 2:c1 // 2] = q
             scales[c0 // Q8_BLOCK:c1 // Q8_BLOCK] = sc
         else:
             dst[c0:c1] = v
@@ -196,15 +229,16 @@ def _fill_matrix(dst, n, dtype_code, seed, tensor_index, std, scales=None, exact
 
 
 def make_arena(m: ModelShape, seed: int, std: float = 0.02, gain_sigma: float = 0.0,
-               threads: int | None = None, out: np.ndarray | None = None, exact: bool = False) -> np.ndarray:
+               threads: int | None = None, out: np.ndarray | None = None, exact: bool | str = False) -> np.ndarray:
     """Generate the seeded weight arena as a flat uint8 array.
 
     Matrices ~ N(0, std) rounded to the storage dtype (Q8: block-quantised by
     quantize_q8).  Norm gains are 1.0, or 1 + N(0, gain_sigma) when
     ``gain_sigma`` > 0 (used to exercise the gain multiply in small tests).
     With ``exact`` every weight is k / 4096 for an integer |k| <= 127 (the
-    N(0, std) draw rounded to that grid): a BF16 arena and a Q8 arena of the
-    same shape and seed then hold the same weight values.
+    N(0, std) draw rounded to that grid; with ``exact="q4"`` k / 512, |k| <= 7):
+    a BF16 arena and a Q8 (Q4) arena of the same shape and seed then hold the
+    same weight values.
     """
     table, total = tensor_table(m)
     arena = out if out is not None else np.zeros(total, dtype=np.uint8)
@@ -222,9 +256,10 @@ def make_arena(m: ModelShape, seed: int, std: float = 0.02, gain_sigma: float = 
                 g[:] = np.float32(1.0)
             continue
         scales = None
-        if dt == Q8:
-            flat = arena[off:off + n].view(np.int8)
-            s0 = off + (n + ALIGN - 1) // ALIGN * ALIGN
+        if dt in (Q8, Q4):
+            nv = _values_bytes(n, dt)
+            flat = arena[off:off + nv].view(np.int8 if dt == Q8 else np.uint8)
+            s0 = off + (nv + ALIGN - 1) // ALIGN * ALIGN
             scales = arena[s0:s0 + 4 * (n // Q8_BLOCK)].view(np.float32)
         else:
             esz = 2 if dt == BF16 else 4
@@ -248,9 +283,13 @@ def views(m: ModelShape, arena: np.ndarray) -> dict:
         n = int(np.prod(shape))
         if dt == BF16:
             out[name] = arena[off:off + 2 * n].view(np.uint16).reshape(shape)
-        elif dt == Q8:
-            s0 = off + (n + ALIGN - 1) // ALIGN * ALIGN
-            out[name] = arena[off:off + n].view(np.int8).reshape(shape)
+        elif dt in (Q8, Q4):
+            nv = _values_bytes(n, dt)
+            s0 = off + (nv + ALIGN - 1) // ALIGN * ALIGN
+            if dt == Q8:
+                out[name] = arena[off:off + n].view(np.int8).reshape(shape)
+            else:  # packed bytes, two values each
+                out[name] = arena[off:off + nv].reshape(shape[0], shape[1] // 2)
             out[name + ".scale"] = arena[s0:s0 + 4 * (n // Q8_BLOCK)].view(np.float32).reshape(
                 shape[0], shape[1] // Q8_BLOCK)
         else:
