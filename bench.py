@@ -37,6 +37,7 @@ KERNELS = ["qkv", "attn", "attn_combine", "wo", "w13", "w2", "logits"]
 DTYPE = {
     "bf16": "f32 (fp32 accumulation; bf16 weights times fp32 activations as bf16 hi+lo pairs)",
     "q8": "f32 (fp32 accumulation; int8 weights with an fp32 scale per 32 values, times fp32 activations)",
+    "q4": "f32 (fp32 accumulation; int4 weights with an fp32 scale per 32 values, times fp32 activations)",
 }
 
 
@@ -59,7 +60,9 @@ def step_bytes(m: synth.ModelShape, lengths_before: np.ndarray) -> int:
 
 def elem_bytes(m: synth.ModelShape) -> float:
     """Bytes per matrix element, a Q8 element's share of its block scale included."""
-    return 1.0 + 4.0 / synth.Q8_BLOCK if m.weight_dtype == synth.Q8 else float(m.wbytes)
+    if m.weight_dtype in (synth.Q8, synth.Q4):
+        return m.wbytes + 4.0 / synth.Q8_BLOCK
+    return float(m.wbytes)
 
 
 def kernel_bytes(m: synth.ModelShape, which: str, B: int, n_ctx: float) -> float:
@@ -220,9 +223,9 @@ def main():
                          "top-k K, top-p P; seeded uniforms) instead of keeping the greedy ones")
     ap.add_argument("--prefill-batched-only", action="store_true",
                     help="with --prefill: skip the one-position-per-pass prefill (for kernel profiles)")
-    ap.add_argument("--weights", choices=["bf16", "q8"], default="bf16",
-                    help="matrix storage: the workload's bf16, or block-quantised int8 (an fp32 scale per 32 "
-                         "values) from the same seeded draws")
+    ap.add_argument("--weights", choices=["bf16", "q8", "q4"], default="bf16",
+                    help="matrix storage: the workload's bf16, or block-quantised int8 / int4 (an fp32 scale "
+                         "per 32 values) from the same seeded draws")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain copy kernel (read N MB, write N MB) three times, as the "
                          "known-size reference for hardware byte counters; its rate is reported")
@@ -235,8 +238,9 @@ def main():
     import decode_step_02_amd as dsa
 
     w = synth.WORKLOADS[args.workload]
-    if args.weights == "q8":
-        w = dataclasses.replace(w, model=dataclasses.replace(w.model, weight_dtype=synth.Q8))
+    if args.weights in ("q8", "q4"):
+        qdt = synth.Q8 if args.weights == "q8" else synth.Q4
+        w = dataclasses.replace(w, model=dataclasses.replace(w.model, weight_dtype=qdt))
     m = w.model
     arena = synth.make_arena(m, w.model_seed)
     prompts = synth.prompts(w)
@@ -369,7 +373,7 @@ def main():
     traffic, traffic_note = measured_traffic(w.name) if single else (None, "counters taken for the single-launch step only")
     out = {
         "metric": ("decode tok/s (135M-shaped Llama, B=1)" if w.name == "llama135m_p5" else f"decode tok/s ({w.name})")
-                  + (" int8 weights" if args.weights == "q8" else "")
+                  + {"q8": " int8 weights", "q4": " int4 weights"}.get(args.weights, "")
                   + (" with sampling" if samp else ""),
         "value": B * args.steps / (ms_total * 1e-3),
         "unit": "tok/s",

@@ -21,7 +21,7 @@ DS_OK = 0
 STATUS = {0: "DS_OK", -1: "DS_ERR_INVALID_ARG", -2: "DS_ERR_UNSUPPORTED", -3: "DS_ERR_ALIGNMENT",
           -4: "DS_ERR_CONTEXT_FULL", -5: "DS_ERR_BAD_TOKEN", -6: "DS_ERR_WORKSPACE", -7: "DS_ERR_HIP",
           -8: "DS_ERR_STATE", -9: "DS_ERR_DEVICE"}
-DS_F32, DS_BF16, DS_Q8 = 0, 1, 2
+DS_F32, DS_BF16, DS_Q8, DS_Q4 = 0, 1, 2, 3
 
 
 class DSError(RuntimeError):

@@ -45,12 +45,13 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-size_t wsize(const ds_config* c) { return c->weight_dtype == DS_BF16 ? 2 : c->weight_dtype == DS_Q8 ? 1 : 4; }
+size_t wsize(const ds_config* c) { return c->weight_dtype == DS_BF16 ? 2 : (c->weight_dtype == DS_Q8 || c->weight_dtype == DS_Q4) ? 1 : 4; }
 
 // Bytes of one [rows][cols] matrix; DS_Q8: the int8 values, then from the
 // next 256-byte boundary one fp32 scale per 32 values of a row.
 size_t mat_bytes(const ds_config* c, size_t rows, size_t cols) {
     if (c->weight_dtype == DS_Q8) return round_up(rows * cols, kAlign) + 4 * rows * (cols / 32);
+    if (c->weight_dtype == DS_Q4) return round_up(rows * cols / 2, kAlign) + 4 * rows * (cols / 32);
     return rows * cols * wsize(c);
 }
 
@@ -61,11 +62,12 @@ ds_status check_config(const ds_config* c) {
     if (c->dim <= 0 || c->n_layers <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
         c->head_dim <= 0 || c->hidden_dim <= 0 || c->vocab_size <= 0)
         return fail(DS_ERR_INVALID_ARG, "every dimension must be positive");
-    if (c->weight_dtype != DS_F32 && c->weight_dtype != DS_BF16 && c->weight_dtype != DS_Q8)
-        return fail(DS_ERR_INVALID_ARG, "weight_dtype must be DS_F32, DS_BF16 or DS_Q8");
-    if (c->weight_dtype == DS_Q8 &&
+    if (c->weight_dtype != DS_F32 && c->weight_dtype != DS_BF16 && c->weight_dtype != DS_Q8 &&
+        c->weight_dtype != DS_Q4)
+        return fail(DS_ERR_INVALID_ARG, "weight_dtype must be DS_F32, DS_BF16, DS_Q8 or DS_Q4");
+    if ((c->weight_dtype == DS_Q8 || c->weight_dtype == DS_Q4) &&
         (c->dim % 32 || (static_cast<int64_t>(c->n_heads) * c->head_dim) % 32 || c->hidden_dim % 32))
-        return fail(DS_ERR_UNSUPPORTED, "DS_Q8 needs dim, n_heads*head_dim and hidden_dim multiples of 32");
+        return fail(DS_ERR_UNSUPPORTED, "DS_Q8 and DS_Q4 need dim, n_heads*head_dim and hidden_dim multiples of 32");
     if (c->n_heads % c->n_kv_heads != 0)
         return fail(DS_ERR_INVALID_ARG, "n_heads (%d) is not a multiple of n_kv_heads (%d)", c->n_heads,
                     c->n_kv_heads);

@@ -11,6 +11,7 @@ namespace ds {
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kQ8 = 2;   // int8 rows, then an fp32 scale per 32 values of a row
+constexpr int kQ4 = 3;   // 4-bit values two per byte, then an fp32 scale per 32 values of a row
 constexpr int kChunk = 64;       // cache positions per split-K attention block
 constexpr int kShort = 64;       // contexts up to this many positions use the fused short path
 constexpr int kMaxRep = 8;       // query heads per key/value head

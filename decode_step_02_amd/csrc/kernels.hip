@@ -83,10 +83,40 @@ template <> struct Wt<kQ8> {
     }
 };
 
-// Scales of a Q8 matrix [rows][K]: they start at the first 256-byte boundary
-// after its rows * K int8 values.
-__device__ __forceinline__ const float* q8_scales(const void* W, size_t rows, int K) {
-    const size_t nb = (rows * static_cast<size_t>(K) + 255) / 256 * 256;
+// Block-quantised 4-bit: 32 values per chunk (one 32-value block), two per
+// byte with the even index in the low nibble, so value i of a dword is its
+// nibble i; two's complement.  The dot product before the block's scale.
+template <> struct Wt<kQ4> {
+    static constexpr int EPC = 32;
+    __device__ static __forceinline__ uint4 load(const void* base, size_t elem) {
+        return *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) + elem / 2);
+    }
+    __device__ static __forceinline__ float dot(const uint4 u, const float* xs, float acc) {
+        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float4 a = *reinterpret_cast<const float4*>(xs + 8 * k);
+            const float4 b = *reinterpret_cast<const float4*>(xs + 8 * k + 4);
+            const int32_t v = static_cast<int32_t>(wv[k]);
+            acc = fmaf(static_cast<float>((v << 28) >> 28), a.x, acc);
+            acc = fmaf(static_cast<float>((v << 24) >> 28), a.y, acc);
+            acc = fmaf(static_cast<float>((v << 20) >> 28), a.z, acc);
+            acc = fmaf(static_cast<float>((v << 16) >> 28), a.w, acc);
+            acc = fmaf(static_cast<float>((v << 12) >> 28), b.x, acc);
+            acc = fmaf(static_cast<float>((v << 8) >> 28), b.y, acc);
+            acc = fmaf(static_cast<float>((v << 4) >> 28), b.z, acc);
+            acc = fmaf(static_cast<float>(v >> 28), b.w, acc);
+        }
+        return acc;
+    }
+};
+
+// Scales of a Q8 / Q4 matrix [rows][K]: they start at the first 256-byte
+// boundary after its values (rows * K bytes, or half that for Q4).
+template <int WDT>
+__device__ __forceinline__ const float* q_scales(const void* W, size_t rows, int K) {
+    const size_t vb = WDT == kQ4 ? rows * static_cast<size_t>(K) / 2 : rows * static_cast<size_t>(K);
+    const size_t nb = (vb + 255) / 256 * 256;
     return reinterpret_cast<const float*>(static_cast<const uint8_t*>(W) + nb);
 }
 
@@ -111,7 +141,7 @@ template <> struct Wt<kF32> {
 template <int WDT, int G>
 struct RowStream {
     static constexpr int EPC = Wt<WDT>::EPC;
-    static constexpr bool Q8 = WDT == kQ8;
+    static constexpr bool Q8 = WDT == kQ8 || WDT == kQ4;  // block scales (Q8 or Q4)
     uint4 w[kPrefetch];
     float sc[Q8 ? kPrefetch : 1];  // Q8: the block scale of each prefetched chunk
     const void* W;
@@ -129,12 +159,12 @@ struct RowStream {
         sub = sub_;
         nch = valid ? K / EPC : 0;
         const int last = K / EPC - 1;
-        if constexpr (Q8) S = q8_scales(W_, rows, K) + row * static_cast<size_t>(K / 32);
+        if constexpr (Q8) S = q_scales<WDT>(W_, rows, K) + row * static_cast<size_t>(K / 32);
 #pragma unroll
         for (int p = 0; p < kPrefetch; p++) {
             const int c = sub + p * G;
             w[p] = Wt<WDT>::load(W, base + static_cast<size_t>(min(c, last)) * EPC);
-            if constexpr (Q8) sc[p] = S[min(c, last) >> 1];
+            if constexpr (Q8) sc[p] = S[(min(c, last) * EPC) >> 5];
         }
 #pragma unroll
         for (int p = 0; p < kPrefetch; p++) {
@@ -152,7 +182,7 @@ struct RowStream {
         return Wt<WDT>::dot(u, xs, acc);
     }
     __device__ __forceinline__ float scale_of(int c) const {
-        if constexpr (Q8) return S[c >> 1];
+        if constexpr (Q8) return S[(c * EPC) >> 5];
         return 1.f;
     }
 
@@ -309,8 +339,15 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs s, BeginList list, const
         for (int j = threadIdx.x; j < s.d; j += 256) x[j] = __uint_as_float(static_cast<uint32_t>(e[j]) << 16);
     } else if (s.wdt == kQ8) {
         const int8_t* e = static_cast<const int8_t*>(s.emb) + row;
-        const float* sc = q8_scales(s.emb, s.V, s.d) + static_cast<size_t>(tok) * (s.d / 32);
+        const float* sc = q_scales<kQ8>(s.emb, s.V, s.d) + static_cast<size_t>(tok) * (s.d / 32);
         for (int j = threadIdx.x; j < s.d; j += 256) x[j] = sc[j >> 5] * static_cast<float>(e[j]);
+    } else if (s.wdt == kQ4) {
+        const uint8_t* e = static_cast<const uint8_t*>(s.emb) + row / 2;
+        const float* sc = q_scales<kQ4>(s.emb, s.V, s.d) + static_cast<size_t>(tok) * (s.d / 32);
+        for (int j = threadIdx.x; j < s.d; j += 256) {
+            const int nib = (j & 1) ? (e[j >> 1] >> 4) : (e[j >> 1] & 15);
+            x[j] = sc[j >> 5] * static_cast<float>(nib >= 8 ? nib - 16 : nib);
+        }
     } else {
         const float* e = static_cast<const float*>(s.emb) + row;
         for (int j = threadIdx.x; j < s.d; j += 256) x[j] = e[j];
@@ -1094,7 +1131,7 @@ __global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
 // when the launch would otherwise hold fewer than 2048 waves (rows = weight
 // rows x items), so that every CU has the loads of several waves in flight.
 static int pick_g(int K, int wdt, int rows = 1 << 30) {
-    const int nch = K / (wdt == kQ8 ? 16 : wdt == kBF16 ? 8 : 4);
+    const int nch = K / (wdt == kQ4 ? 32 : wdt == kQ8 ? 16 : wdt == kBF16 ? 8 : 4);
     if (nch <= 128) return 8;
     if (nch <= 512) return rows >= 4 * 2048 ? 16 : 32;
     return 32;
@@ -1206,6 +1243,7 @@ static hipError_t gemv(Gemv which, const StepArgs& s, const LayerW& w, int layer
     if (which == G_LOGITS || which == G_WO_SHORT) waves = 4;
     if (s.wdt == kBF16) return launch1<kBF16>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
     if (s.wdt == kQ8) return launch1<kQ8>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
+    if (s.wdt == kQ4) return launch1<kQ4>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
     return launch1<kF32>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
 }
 
@@ -1239,6 +1277,7 @@ hipError_t set_kernel_attributes(int lds) {
     hipError_t e = set_attrs1<kBF16>(lds);
     if (e == hipSuccess) e = set_attrs1<kF32>(lds);
     if (e == hipSuccess) e = set_attrs1<kQ8>(lds);
+    if (e == hipSuccess) e = set_attrs1<kQ4>(lds);
     if (e == hipSuccess)
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     return e;

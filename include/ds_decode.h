@@ -55,9 +55,13 @@ typedef enum {
  * its next step: a matrix [rows][cols] is int8 q[rows][cols] row-major, then,
  * from the next 256-byte boundary, fp32 s[rows][cols/32]; its element (r, c)
  * is s[r][c/32] * q[r][c].  dim, n_heads*head_dim and hidden_dim must be
- * multiples of 32.  DS_Q8 models run one launch per operation at every batch
- * size (no single-launch step, no MFMA projections). */
-typedef enum { DS_F32 = 0, DS_BF16 = 1, DS_Q8 = 2 } ds_dtype;
+ * multiples of 32.  DS_Q4 is the INT4 variant the same section names: the
+ * values are packed two per byte (value c of a row in byte c/2, the low
+ * nibble for even c), each a two's complement integer in [-8, 7], rows*cols/2
+ * bytes row-major, then the scales as for DS_Q8.  DS_Q8 and DS_Q4 models run
+ * one launch per operation at every batch size (no single-launch step, no
+ * MFMA projections). */
+typedef enum { DS_F32 = 0, DS_BF16 = 1, DS_Q8 = 2, DS_Q4 = 3 } ds_dtype;
 
 /* Model shape.  The field order is part of the ABI. */
 typedef struct {

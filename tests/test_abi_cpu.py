@@ -76,18 +76,21 @@ def test_invalid_configs_are_rejected(dsa):
         dsa.ds_weights_offsets(dsa.ds_config.of(dataclasses.replace(base, n_kv_heads=3)))
 
 
+@pytest.mark.parametrize("dt", ["q8", "q4"])
 @pytest.mark.parametrize("name", ["llama135m_p5", "llama8b_p4096"])
-def test_q8_layout_queries_match_the_arena_format(dsa, name):
-    """Block-quantised int8 matrices (DS_Q8): int8 values, then one fp32 scale
-    per 32 values of a row from the next 256-byte boundary."""
+def test_q8_layout_queries_match_the_arena_format(dsa, name, dt):
+    """Block-quantised int8 / int4 matrices (DS_Q8, DS_Q4): the values (one
+    byte, or half a byte each), then one fp32 scale per 32 values of a row
+    from the next 256-byte boundary."""
     import dataclasses
-    m = dataclasses.replace(synth.WORKLOADS[name].model, weight_dtype=synth.Q8)
+    m = dataclasses.replace(synth.WORKLOADS[name].model, weight_dtype=synth.Q8 if dt == "q8" else synth.Q4)
     cfg = dsa.ds_config.of(m)
     table, total = synth.tensor_table(m)
     assert dsa.ds_weights_bytes(cfg) == total
     assert dsa.ds_weights_offsets(cfg) == [t[1] for t in table]
     V, d = m.vocab_size, m.dim
-    assert table[1][1] == ((V * d + 255) // 256 * 256 + 4 * V * d // 32 + 255) // 256 * 256
+    vb = V * d if dt == "q8" else V * d // 2
+    assert table[1][1] == ((vb + 255) // 256 * 256 + 4 * V * d // 32 + 255) // 256 * 256
 
 
 def test_q8_needs_rows_of_whole_blocks(dsa):
