@@ -7,7 +7,7 @@ functions ``ds_*`` mirror the C ABI in ``include/ds_decode.h`` one to one;
 buffers with torch at the sizes the library reports.
 
 Importing this package fails loudly if the library has not been built
-(``python -m decode_step_02_amd.build`` or ``__graft_entry__.build()``).
+(``python -m decode_step_02_amd.build``).
 """
 from __future__ import annotations
 
@@ -35,7 +35,7 @@ class ds_config(C.Structure):
         ("dim", C.c_int32), ("n_layers", C.c_int32), ("n_heads", C.c_int32),
         ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("hidden_dim", C.c_int32),
         ("vocab_size", C.c_int32), ("tied_embeddings", C.c_int32), ("weight_dtype", C.c_int32),
-        ("rope_theta", C.c_float), ("norm_eps", C.c_float),
+        ("rope_theta", C.c_float), ("norm_eps", C.c_float), ("cache_dtype", C.c_int32),
     ]
 
     @classmethod

@@ -39,7 +39,7 @@ class OrcConfig(C.Structure):
         ("dim", C.c_int32), ("n_layers", C.c_int32), ("n_heads", C.c_int32),
         ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("hidden_dim", C.c_int32),
         ("vocab_size", C.c_int32), ("tied_embeddings", C.c_int32), ("weight_dtype", C.c_int32),
-        ("rope_theta", C.c_float), ("norm_eps", C.c_float),
+        ("rope_theta", C.c_float), ("norm_eps", C.c_float), ("cache_dtype", C.c_int32),
     ]
 
 
@@ -61,6 +61,7 @@ def load(path: str = LIB):
     P = C.POINTER(OrcConfig)
     sig = {
         "orc_widen_bf16": (C.c_float, [C.c_uint16]),
+        "orc_round_bf16": (C.c_float, [C.c_float]),
         "orc_widen_bf16_array": (None, [_U16, _F, C.c_size_t]),
         "orc_matvec": (None, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, _F, _F]),
         "orc_weight": (C.c_float, [C.c_void_p, C.c_int32, C.c_size_t, C.c_size_t, C.c_size_t, C.c_size_t]),

@@ -28,6 +28,18 @@ float orc_widen_bf16(uint16_t h) {
     return f;
 }
 
+/* Round to nearest bfloat16, ties to even: keep the top 16 bits after adding
+ * half of the dropped range, less one unless the kept part is odd. */
+float orc_round_bf16(float x) {
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u = (u + 0x7FFFu + lsb) & 0xFFFF0000u;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
 void orc_widen_bf16_array(const uint16_t* src, float* dst, size_t n) {
     for (size_t i = 0; i < n; i++) dst[i] = orc_widen_bf16(src[i]);
 }
@@ -365,6 +377,12 @@ int32_t orc_forward(const orc_config* c, const uint8_t* arena, float* cache, int
         orc_matvec(arena + lo[T_WV], wd, Hkv * D, d, xn, v);
         for (int32_t h = 0; h < H; h++) orc_rope_apply(q + (size_t)h * D, D, cs, sn);
         for (int32_t g = 0; g < Hkv; g++) orc_rope_apply(k + (size_t)g * D, D, cs, sn);
+        if (c->cache_dtype == ORC_BF16) {
+            for (int32_t i = 0; i < Hkv * D; i++) {
+                k[i] = orc_round_bf16(k[i]);
+                v[i] = orc_round_bf16(v[i]);
+            }
+        }
         for (int32_t g = 0; g < Hkv; g++) {
             memcpy(cache + orc_cache_index(c, B, T, l, 0, b, g, pos), k + (size_t)g * D,
                    sizeof(float) * (size_t)D);

@@ -37,10 +37,18 @@ typedef struct {
     int32_t tied_embeddings;
     int32_t weight_dtype; /* ORC_F32, ORC_BF16, ORC_Q8 or ORC_Q4 for matrices; gains are fp32 */
     float rope_theta, norm_eps;
+    /* ORC_F32, or ORC_BF16: every key and value row is rounded to bfloat16
+     * (nearest, ties to even) when it is stored, and attention reads the
+     * rounded values (the bf16 cache that "simple-llm / kasahare", section
+     * "Limitations (intentional)", lists among the cache compressions it
+     * leaves out).  The host cache array stays fp32 and holds those values. */
+    int32_t cache_dtype;
 } orc_config;
 
 /* ---- primitives ------------------------------------------------------- */
 float orc_widen_bf16(uint16_t h);
+/* x rounded to the nearest bfloat16 (ties to even), as fp32; x finite. */
+float orc_round_bf16(float x);
 void orc_widen_bf16_array(const uint16_t* src, float* dst, size_t n);
 void orc_matvec(const void* W, int32_t wdtype, int32_t n_out, int32_t n_in,
                 const float* x, float* y);

@@ -49,6 +49,7 @@ class ModelShape:
     weight_dtype: int  # F32, BF16, Q8 or Q4
     rope_theta: float
     norm_eps: float
+    cache_dtype: int = F32  # F32, or BF16: key/value rows rounded to bf16 when stored
 
     @property
     def q_rows(self) -> int:
