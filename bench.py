@@ -50,7 +50,7 @@ def step_bytes(m: synth.ModelShape, lengths_before: np.ndarray) -> int:
     B = len(lengths_before)
     mats = sum(synth.tensor_bytes(s, dt) for _, _, s, dt in table if len(s) == 2)
     gains = sum(int(np.prod(s)) * 4 for _, _, s, dt in table if len(s) == 1)
-    kv_row = m.n_layers * 2 * m.n_kv_heads * m.head_dim * 4
+    kv_row = m.n_layers * 2 * m.n_kv_heads * m.head_dim * (2 if m.cache_dtype == synth.BF16 else 4)
     gather = int(B * m.dim * elem_bytes(m))
     kv_read = int(np.sum(lengths_before.astype(np.int64) + 1)) * kv_row
     kv_write = B * kv_row
@@ -74,7 +74,7 @@ def kernel_bytes(m: synth.ModelShape, which: str, B: int, n_ctx: float) -> float
     if which == "qkv":
         return (qr + 2 * kvr) * d * w + B * (d * 4 + d * 4 + (qr + 2 * kvr) * 4)
     if which == "attn":
-        return B * (2 * kvr * n_ctx * 4 + qr * 4)
+        return B * (2 * kvr * n_ctx * (2 if m.cache_dtype == synth.BF16 else 4) + qr * 4)
     if which == "wo":
         return d * qr * w + B * (qr * 4 + 2 * d * 4)
     if which == "w13":
@@ -226,6 +226,8 @@ def main():
     ap.add_argument("--weights", choices=["bf16", "q8", "q4"], default="bf16",
                     help="matrix storage: the workload's bf16, or block-quantised int8 / int4 (an fp32 scale "
                          "per 32 values) from the same seeded draws")
+    ap.add_argument("--cache", choices=["f32", "bf16"], default="f32",
+                    help="key/value cache element type (bf16: rows rounded when stored)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain copy kernel (read N MB, write N MB) three times, as the "
                          "known-size reference for hardware byte counters; its rate is reported")
@@ -241,6 +243,8 @@ def main():
     if args.weights in ("q8", "q4"):
         qdt = synth.Q8 if args.weights == "q8" else synth.Q4
         w = dataclasses.replace(w, model=dataclasses.replace(w.model, weight_dtype=qdt))
+    if args.cache == "bf16":
+        w = dataclasses.replace(w, model=dataclasses.replace(w.model, cache_dtype=synth.BF16))
     m = w.model
     arena = synth.make_arena(m, w.model_seed)
     prompts = synth.prompts(w)
@@ -374,6 +378,7 @@ def main():
     out = {
         "metric": ("decode tok/s (135M-shaped Llama, B=1)" if w.name == "llama135m_p5" else f"decode tok/s ({w.name})")
                   + {"q8": " int8 weights", "q4": " int4 weights"}.get(args.weights, "")
+                  + (" bf16 cache" if args.cache == "bf16" else "")
                   + (" with sampling" if samp else ""),
         "value": B * args.steps / (ms_total * 1e-3),
         "unit": "tok/s",
@@ -386,7 +391,7 @@ def main():
         "vs_baseline": None,
         "dtype": DTYPE[args.weights],
         "data": "synthetic (seeded random weights N(0,0.02), uniform prompt ids)",
-        "config": {"workload": w.name, "description": w.description, "batch": B, "ctx": w.ctx, "weights": args.weights,
+        "config": {"workload": w.name, "description": w.description, "batch": B, "ctx": w.ctx, "weights": args.weights, "cache": args.cache,
                    "decode_positions": [int(base.min()), int(base.max() + cycle - 1)],
                    "dispatch": args.dispatch, "single_launch_step": bool(single)},
         "step_bytes": bytes_step,

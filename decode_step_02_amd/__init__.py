@@ -259,13 +259,14 @@ class KVCache:
         import torch
         self.model, self.B, self.T = model, B, T
         self.cache_t = _aligned_empty(ds_kv_cache_bytes(model.cfg, B, T), device)
-        self.cache = self.cache_t.view(torch.float32)
+        self.cache = self.cache_t.view(torch.bfloat16 if model.cfg.cache_dtype == DS_BF16 else torch.float32)
         self.lengths = _aligned_empty(4 * B, device).view(torch.int32)
         self.ws = _aligned_empty(ds_workspace_bytes(model.cfg, B, T), device)
         self.logits_buf = torch.empty(B, model.cfg.vocab_size, dtype=torch.float32, device=device)
         self.handle = ds_kv_cache_create(model.handle, B, T, self.cache_t, self.lengths, self.ws, stream)
 
     def cache_view(self):
+        """The cache as (L, 2, B, Hkv, T, D), in its element type (fp32 or bf16)."""
         c = self.model.cfg
         return self.cache.view(c.n_layers, 2, self.B, c.n_kv_heads, self.T, c.head_dim)
 

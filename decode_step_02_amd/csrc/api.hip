@@ -68,6 +68,11 @@ ds_status check_config(const ds_config* c) {
     if ((c->weight_dtype == DS_Q8 || c->weight_dtype == DS_Q4) &&
         (c->dim % 32 || (static_cast<int64_t>(c->n_heads) * c->head_dim) % 32 || c->hidden_dim % 32))
         return fail(DS_ERR_UNSUPPORTED, "DS_Q8 and DS_Q4 need dim, n_heads*head_dim and hidden_dim multiples of 32");
+    if (c->cache_dtype != DS_F32 && c->cache_dtype != DS_BF16)
+        return fail(DS_ERR_INVALID_ARG, "cache_dtype must be DS_F32 or DS_BF16");
+    if (c->cache_dtype == DS_BF16 && !((c->head_dim == 64 || c->head_dim == 128) && c->n_kv_heads > 0 &&
+                                      c->n_heads % c->n_kv_heads == 0 && c->n_heads / c->n_kv_heads <= 4))
+        return fail(DS_ERR_UNSUPPORTED, "a bf16 cache needs head_dim 64 or 128 and at most 4 query heads per key/value head");
     if (c->n_heads % c->n_kv_heads != 0)
         return fail(DS_ERR_INVALID_ARG, "n_heads (%d) is not a multiple of n_kv_heads (%d)", c->n_heads,
                     c->n_kv_heads);
@@ -234,7 +239,8 @@ ds_status ds_weights_offsets(const ds_config* cfg, size_t* h_off, int32_t n) {
 
 size_t ds_kv_cache_bytes(const ds_config* cfg, int32_t B, int32_t T) {
     if (check_config(cfg) != DS_OK || B <= 0 || T <= 0) return 0;
-    return sizeof(float) * static_cast<size_t>(cfg->n_layers) * 2 * B * cfg->n_kv_heads * T * cfg->head_dim;
+    const size_t esz = cfg->cache_dtype == DS_BF16 ? 2 : 4;
+    return esz * static_cast<size_t>(cfg->n_layers) * 2 * B * cfg->n_kv_heads * T * cfg->head_dim;
 }
 
 size_t ds_workspace_bytes(const ds_config* cfg, int32_t B, int32_t T) {
@@ -383,7 +389,8 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     s.B = B;
     s.T = T;
     s.n_chunks = (T + ds::kChunk - 1) / ds::kChunk;
-    s.short_n = ds::short_positions(s);
+    s.cdt = c->cache_dtype;
+    s.short_n = s.cdt == DS_BF16 ? 0 : ds::short_positions(s);  // the fused short path reads an fp32 cache
     s.mm_ok = ds::mm_supported(s) ? 1 : 0;
     const char* mmenv = std::getenv("DS_MFMA");  // "0" keeps the VALU projections for every batch size
     if (mmenv && std::strcmp(mmenv, "0") == 0) s.mm_ok = 0;
@@ -392,7 +399,7 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     if (skenv && std::strcmp(skenv, "0") == 0) s.mm_split = 0;
     s.attn_g = 1;
     const char* agenv = std::getenv("DS_ATTN_G");  // "0" keeps the shuffle-reduced attention kernel
-    if (agenv && std::strcmp(agenv, "0") == 0) s.attn_g = 0;
+    if (agenv && std::strcmp(agenv, "0") == 0 && s.cdt != DS_BF16) s.attn_g = 0;  // the only bf16-cache reader
     const char* sa = std::getenv("DS_SHORT_ATTN");  // "0" turns the fused short-context path off
     if (sa && std::strcmp(sa, "0") == 0) s.short_n = 0;
     ds::PersistArgs& pa = kv->pa;
@@ -480,8 +487,9 @@ ds_status ds_kv_cache_replicate(ds_kv* dst, const ds_kv* src, int32_t src_seq, i
     if (!dst || !src) return fail(DS_ERR_INVALID_ARG, "NULL cache");
     const ds_config& a = dst->model->cfg;
     const ds_config& b = src->model->cfg;
-    if (a.n_layers != b.n_layers || a.n_kv_heads != b.n_kv_heads || a.head_dim != b.head_dim)
-        return fail(DS_ERR_INVALID_ARG, "caches of different layer / key-value head / head shapes");
+    if (a.n_layers != b.n_layers || a.n_kv_heads != b.n_kv_heads || a.head_dim != b.head_dim ||
+        a.cache_dtype != b.cache_dtype)
+        return fail(DS_ERR_INVALID_ARG, "caches of different layer / key-value head / head shapes or element types");
     if (src_seq < 0 || src_seq >= src->B) return fail(DS_ERR_INVALID_ARG, "src_seq %d outside [0, %d)", src_seq, src->B);
     if (count < 0 || dst_first < 0 || dst_first + static_cast<int64_t>(count) > dst->B)
         return fail(DS_ERR_INVALID_ARG, "slots [%d, %d + %d) outside [0, %d)", dst_first, dst_first, count, dst->B);
@@ -491,8 +499,10 @@ ds_status ds_kv_cache_replicate(ds_kv* dst, const ds_kv* src, int32_t src_seq, i
     if (n > dst->T) return fail(DS_ERR_CONTEXT_FULL, "%d positions do not fit a cache of %d", n, dst->T);
     if (count == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // a bf16 row of D values is copied as D/2 four-byte words
+    const int wpr = a.cache_dtype == DS_BF16 ? a.head_dim / 2 : a.head_dim;
     hipError_t e = ds::enqueue_replicate(dst->cache, dst->B, dst->T, src->cache, src->B, src->T, a.n_layers,
-                                         a.n_kv_heads, a.head_dim, src_seq, dst_first, count, n, st);
+                                         a.n_kv_heads, wpr, src_seq, dst_first, count, n, st);
     std::vector<int32_t> len(static_cast<size_t>(count), n);
     if (e == hipSuccess) e = ds::enqueue_set_lengths(dst->lengths, len.data(), dst_first, count, st);
     if (e != hipSuccess) return hip_fail(e, "replicate");

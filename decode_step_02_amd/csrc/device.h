@@ -28,6 +28,17 @@ __device__ __forceinline__ size_t cache_row(const StepArgs& s, int layer, int kv
     return i * s.D;
 }
 
+// Stores one key or value element: fp32, or rounded to bf16 (nearest, ties
+// to even; finite values) in a bf16 cache.
+__device__ __forceinline__ void cache_put(const StepArgs& s, size_t idx, float v) {
+    if (s.cdt == kBF16) {
+        const uint32_t u = __float_as_uint(v);
+        reinterpret_cast<uint16_t*>(s.cache)[idx] = static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    } else {
+        s.cache[idx] = v;
+    }
+}
+
 // Argmax key: the float's order-preserving 32-bit image in the high word and
 // (2^32 - 1 - index) in the low word, so the largest key is the largest
 // logit and, among equal logits, the lowest index ("Inside nanochat Part 4",

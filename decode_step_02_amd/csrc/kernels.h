@@ -53,12 +53,13 @@ struct StepArgs {
     int d, L, H, Hkv, D, F, V, wdt;
     int B, T, n_chunks;
     int short_n;         // contexts up to this many positions take the fused short path (0: never)
+    int cdt;             // cache element type: kF32, or kBF16 (rows rounded when stored)
     int mm_ok;           // shapes allow the MFMA projections
     int mm_split;        // the narrow projections may take the split-K MFMA kernel
     int attn_g;          // head_dim 64 / 128 attention takes the DPP-reduced kernel
     float eps;
     const void* emb;
-    float* cache;        // (L, 2, B, Hkv, T, D)
+    float* cache;        // (L, 2, B, Hkv, T, D), fp32 or (cdt == kBF16) uint16 bf16 bits
     int32_t* lengths;    // [B]
     // workspace
     float* x;            // [items][d]     residual stream

@@ -411,11 +411,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(StepArgs s, LayerW w, int la
             if (is_q) {
                 s.q[static_cast<size_t>(item) * s.H * D + row] = out;
             } else {
-                s.cache[cache_row(s, layer, 0, slot, row / D, pos) + row % D] = out;
+                cache_put(s, cache_row(s, layer, 0, slot, row / D, pos) + row % D, out);
             }
         }
     } else if (sub == 0) {
-        s.cache[cache_row(s, layer, 1, slot, row / D, pos) + row % D] = y;
+        cache_put(s, cache_row(s, layer, 1, slot, row / D, pos) + row % D, y);
     }
 }
 
@@ -733,7 +733,77 @@ __global__ __launch_bounds__(256) void k_attn_d(StepArgs s, int layer) {
 //  - The softmax weights of the chunk go through LDS; max and sum are taken
 //    over the block, the weighted values summed over the four waves in LDS.
 // Partials as k_attn_d: (m, l) and the weighted sum per (item, head, chunk).
-template <int D, int REP>
+// One lane's share of the keys and values of a wave's 16 rows, fp32 or bf16.
+// fp32 keys: lane q holds dims 32f + 4q .. +3 (f < D/32); bf16 keys: dims
+// 64f + 8q .. +7 (f < D/64, one 16-byte load each): either way D/8 dims,
+// read as whole 128-byte lines per row, and qdim() gives the query offsets
+// that match.  Values: D/64 dims per lane; bf16 ones stay packed until used.
+template <int D, int CDT> struct KVRows;
+template <int D> struct KVRows<D, kF32> {
+    static constexpr int KF = D / 32, DPL = D / 64;
+    float4 k[2][KF];
+    float v[16][DPL];
+    __device__ static __forceinline__ int qdim(int f, int kq) { return f * 32 + kq * 4; }
+    __device__ __forceinline__ void load(const float* Kb, const float* Vb, int r0, int r1, int rv0, int nlast, int kq,
+                                         int lane) {
+        const int rows[2] = {r0, r1};
+#pragma unroll
+        for (int sl = 0; sl < 2; sl++) {
+#pragma unroll
+            for (int f = 0; f < KF; f++) k[sl][f] = *reinterpret_cast<const float4*>(Kb + rows[sl] * D + f * 32 + kq * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const float* vp = Vb + min(rv0 + i, nlast) * D + lane * DPL;
+            if constexpr (DPL == 1) {
+                v[i][0] = *vp;
+            } else {
+                const float2 v2 = *reinterpret_cast<const float2*>(vp);
+                v[i][0] = v2.x;
+                v[i][1] = v2.y;
+            }
+        }
+    }
+    __device__ __forceinline__ float4 key(int sl, int f) const { return k[sl][f]; }
+    __device__ __forceinline__ float val(int i, int dd) const { return v[i][dd]; }
+};
+template <int D> struct KVRows<D, kBF16> {
+    static constexpr int KF = D / 32, DPL = D / 64;
+    uint4 k[2][D / 64];
+    uint32_t v[16];  // the row's DPL bf16 values (D = 128: two, the lower dim in the low half)
+    __device__ static __forceinline__ int qdim(int f, int kq) { return (f >> 1) * 64 + kq * 8 + (f & 1) * 4; }
+    __device__ __forceinline__ void load(const float* Kb, const float* Vb, int r0, int r1, int rv0, int nlast, int kq,
+                                         int lane) {
+        const uint16_t* K16 = reinterpret_cast<const uint16_t*>(Kb);
+        const uint16_t* V16 = reinterpret_cast<const uint16_t*>(Vb);
+        const int rows[2] = {r0, r1};
+#pragma unroll
+        for (int sl = 0; sl < 2; sl++) {
+#pragma unroll
+            for (int f = 0; f < D / 64; f++) k[sl][f] = *reinterpret_cast<const uint4*>(K16 + rows[sl] * D + f * 64 + kq * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint16_t* vp = V16 + min(rv0 + i, nlast) * D + lane * DPL;
+            if constexpr (DPL == 1)
+                v[i] = *vp;
+            else
+                v[i] = *reinterpret_cast<const uint32_t*>(vp);
+        }
+    }
+    // key float4 number f (f < D/32) of slot sl: dims qdim(f, kq) .. +3
+    __device__ __forceinline__ float4 key(int sl, int f) const {
+        const uint4 u = k[sl][f >> 1];
+        const uint32_t a = (f & 1) ? u.z : u.x, b = (f & 1) ? u.w : u.y;
+        return make_float4(__uint_as_float(a << 16), __uint_as_float(a & 0xFFFF0000u), __uint_as_float(b << 16),
+                           __uint_as_float(b & 0xFFFF0000u));
+    }
+    __device__ __forceinline__ float val(int i, int dd) const {
+        return __uint_as_float(dd == 0 ? v[i] << 16 : v[i] & 0xFFFF0000u);
+    }
+};
+
+template <int D, int REP, int CDT>
 __global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
     constexpr int KF = D / 32;   // key float4s per lane and row
     constexpr int DPL = D / 64;  // value dims per lane
@@ -750,33 +820,21 @@ __global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
     const int nt = min(kChunk, n - t0);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int kq = lane & 7, rr = lane >> 3;
-    const float* Kb = s.cache + cache_row(s, layer, 0, slot, g, t0);
-    const float* Vb = s.cache + cache_row(s, layer, 1, slot, g, t0);
-    float4 kr[2][KF];
-#pragma unroll
-    for (int sl = 0; sl < 2; sl++) {
-        const int r = min(wave * 16 + sl * 8 + rr, nt - 1);
-#pragma unroll
-        for (int f = 0; f < KF; f++) kr[sl][f] = *reinterpret_cast<const float4*>(Kb + r * D + f * 32 + kq * 4);
-    }
-    float vr[16][DPL];
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const float* vp = Vb + min(wave * 16 + i, nt - 1) * D + lane * DPL;
-        if constexpr (DPL == 1) {
-            vr[i][0] = *vp;
-        } else {
-            const float2 v2 = *reinterpret_cast<const float2*>(vp);
-            vr[i][0] = v2.x;
-            vr[i][1] = v2.y;
-        }
-    }
-    const float* qb = s.q + (static_cast<size_t>(item) * s.H + static_cast<size_t>(g) * REP) * D + kq * 4;
+    // cache_row counts elements; element e of a bf16 cache is the uint16 at ((uint16_t*)cache)[e]
+    const size_t kidx = cache_row(s, layer, 0, slot, g, t0), vidx = cache_row(s, layer, 1, slot, g, t0);
+    const float* Kb = CDT == kBF16 ? reinterpret_cast<const float*>(reinterpret_cast<const uint16_t*>(s.cache) + kidx)
+                                   : s.cache + kidx;
+    const float* Vb = CDT == kBF16 ? reinterpret_cast<const float*>(reinterpret_cast<const uint16_t*>(s.cache) + vidx)
+                                   : s.cache + vidx;
+    KVRows<D, CDT> kv;
+    kv.load(Kb, Vb, min(wave * 16 + rr, nt - 1), min(wave * 16 + 8 + rr, nt - 1), wave * 16, nt - 1, kq, lane);
+    const float* qb = s.q + (static_cast<size_t>(item) * s.H + static_cast<size_t>(g) * REP) * D;
     float4 qv[REP][KF];
 #pragma unroll
     for (int j = 0; j < REP; j++) {
 #pragma unroll
-        for (int f = 0; f < KF; f++) qv[j][f] = *reinterpret_cast<const float4*>(qb + j * D + f * 32);
+        for (int f = 0; f < KF; f++)
+            qv[j][f] = *reinterpret_cast<const float4*>(qb + j * D + KVRows<D, CDT>::qdim(f, kq));
     }
     // scores of the lane's two rows for every head, reduced over the row's 8 lanes
     float sc[REP * 2];
@@ -787,10 +845,10 @@ __global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
             float d = 0.f;
 #pragma unroll
             for (int f = 0; f < KF; f++) {
-                d = fmaf(kr[sl][f].x, qv[j][f].x, d);
-                d = fmaf(kr[sl][f].y, qv[j][f].y, d);
-                d = fmaf(kr[sl][f].z, qv[j][f].z, d);
-                d = fmaf(kr[sl][f].w, qv[j][f].w, d);
+                d = fmaf(kv.key(sl, f).x, qv[j][f].x, d);
+                d = fmaf(kv.key(sl, f).y, qv[j][f].y, d);
+                d = fmaf(kv.key(sl, f).z, qv[j][f].z, d);
+                d = fmaf(kv.key(sl, f).w, qv[j][f].w, d);
             }
             sc[j * 2 + sl] = d;
         }
@@ -840,10 +898,10 @@ __global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
             float a0 = 0.f, a1 = 0.f;
 #pragma unroll
             for (int c4 = 0; c4 < 4; c4++) {
-                a0 = fmaf(pe[c4].x, vr[4 * c4 + 0][dd], a0);
-                a1 = fmaf(pe[c4].y, vr[4 * c4 + 1][dd], a1);
-                a0 = fmaf(pe[c4].z, vr[4 * c4 + 2][dd], a0);
-                a1 = fmaf(pe[c4].w, vr[4 * c4 + 3][dd], a1);
+                a0 = fmaf(pe[c4].x, kv.val(4 * c4 + 0, dd), a0);
+                a1 = fmaf(pe[c4].y, kv.val(4 * c4 + 1, dd), a1);
+                a0 = fmaf(pe[c4].z, kv.val(4 * c4 + 2, dd), a0);
+                a1 = fmaf(pe[c4].w, kv.val(4 * c4 + 3, dd), a1);
             }
             ored[wave][j][lane * DPL + dd] = a0 + a1;
         }
@@ -862,15 +920,20 @@ __global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
     }
 }
 
-template <int D>
-static bool launch_attn_g(const StepArgs& s, dim3 grid, int layer, hipStream_t st) {
+template <int D, int CDT>
+static bool launch_attn_g2(const StepArgs& s, dim3 grid, int layer, hipStream_t st) {
     switch (s.H / s.Hkv) {
-        case 1: hipLaunchKernelGGL((k_attn_g<D, 1>), grid, dim3(256), 0, st, s, layer); return true;
-        case 2: hipLaunchKernelGGL((k_attn_g<D, 2>), grid, dim3(256), 0, st, s, layer); return true;
-        case 3: hipLaunchKernelGGL((k_attn_g<D, 3>), grid, dim3(256), 0, st, s, layer); return true;
-        case 4: hipLaunchKernelGGL((k_attn_g<D, 4>), grid, dim3(256), 0, st, s, layer); return true;
+        case 1: hipLaunchKernelGGL((k_attn_g<D, 1, CDT>), grid, dim3(256), 0, st, s, layer); return true;
+        case 2: hipLaunchKernelGGL((k_attn_g<D, 2, CDT>), grid, dim3(256), 0, st, s, layer); return true;
+        case 3: hipLaunchKernelGGL((k_attn_g<D, 3, CDT>), grid, dim3(256), 0, st, s, layer); return true;
+        case 4: hipLaunchKernelGGL((k_attn_g<D, 4, CDT>), grid, dim3(256), 0, st, s, layer); return true;
         default: return false;
     }
+}
+
+template <int D>
+static bool launch_attn_g(const StepArgs& s, dim3 grid, int layer, hipStream_t st) {
+    return s.cdt == kBF16 ? launch_attn_g2<D, kBF16>(s, grid, layer, st) : launch_attn_g2<D, kF32>(s, grid, layer, st);
 }
 
 static bool attn_d_supported(int D) { return D == 16 || D == 32 || D == 64 || D == 128 || D == 256; }

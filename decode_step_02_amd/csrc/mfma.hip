@@ -218,10 +218,10 @@ __global__ __launch_bounds__(256) void k_mm(StepArgs s, LayerW w, int layer, int
                     if (is_q)
                         s.q[static_cast<size_t>(item) * s.H * D + orow] = out;
                     else
-                        s.cache[cache_row(s, layer, 0, slot, orow / D, pos) + orow % D] = out;
+                        cache_put(s, cache_row(s, layer, 0, slot, orow / D, pos) + orow % D, out);
                 } else {
                     const int orow = (tile - nq_t - nk_t) * 16 + i;
-                    s.cache[cache_row(s, layer, 1, slot, orow / D, pos) + orow % D] = y;
+                    cache_put(s, cache_row(s, layer, 1, slot, orow / D, pos) + orow % D, y);
                 }
             }
         } else if (KIND == MM_WO || KIND == MM_W2) {
@@ -434,10 +434,10 @@ __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, 
             if (is_q)
                 s.q[static_cast<size_t>(item) * s.H * D + orow] = out;
             else
-                s.cache[cache_row(s, layer, 0, slot, orow / D, pos) + orow % D] = out;
+                cache_put(s, cache_row(s, layer, 0, slot, orow / D, pos) + orow % D, out);
         } else {
             const int orow = (tile - nq_t - nk_t) * 16 + i;
-            s.cache[cache_row(s, layer, 1, slot, orow / D, pos) + orow % D] = y;
+            cache_put(s, cache_row(s, layer, 1, slot, orow / D, pos) + orow % D, y);
         }
     } else if (KIND == MM_WO || KIND == MM_W2) {
         const int orow = tile * 16 + i;

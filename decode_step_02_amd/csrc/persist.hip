@@ -1183,7 +1183,7 @@ static const PKernel* persist_kernel(const StepArgs& s) {
 
 int persist_max_ctx(const StepArgs& s) {
     const int HD = s.H * s.D, KVD = s.Hkv * s.D;
-    const PKernel* k = s.B == 1 ? persist_kernel(s) : nullptr;
+    const PKernel* k = s.B == 1 && s.cdt == kF32 ? persist_kernel(s) : nullptr;  // fp32 cache only
     if (!k) return 0;
     // d even (word pairs), d <= 1024 (four owned elements per thread)
     if (s.d > kPThreads * kPNorm || s.d < 64 || (s.d & 1) || s.Hkv > 4 || s.V > 0x1FFFF) return 0;

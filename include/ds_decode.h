@@ -76,6 +76,7 @@ typedef struct {
     int32_t weight_dtype;    /* ds_dtype of every matrix; norm gains are fp32   */
     float rope_theta;        /* RoPE base                                       */
     float norm_eps;          /* RMSNorm epsilon                                 */
+    int32_t cache_dtype;     /* DS_F32, or DS_BF16: a bf16 key/value cache      */
 } ds_config;
 
 typedef struct ds_model ds_model;
@@ -98,9 +99,15 @@ int32_t ds_weights_count(const ds_config* cfg);
 /* Byte offset of each arena tensor into h_off[0..n); n must be at least
  * ds_weights_count(cfg). */
 ds_status ds_weights_offsets(const ds_config* cfg, size_t* h_off, int32_t n);
-/* Device bytes of the key/value cache: an fp32 tensor of shape
- * (L, 2, B, Hkv, T, D), row-major (the (L,2,B,H,T,D) layout of "Inside
- * nanochat Part 4", section "Cache Architecture", with H = key/value heads). */
+/* Device bytes of the key/value cache: a tensor of shape (L, 2, B, Hkv, T, D),
+ * row-major (the (L,2,B,H,T,D) layout of "Inside nanochat Part 4", section
+ * "Cache Architecture", with H = key/value heads), fp32, or bf16 when
+ * cfg->cache_dtype is DS_BF16.  A bf16 cache holds every key and value row
+ * rounded to bfloat16 (nearest, ties to even) when it is stored, and
+ * attention reads the rounded values: the cache compression that
+ * "simple-llm / kasahare" (section "Limitations (intentional)") leaves out.
+ * It needs head_dim 64 or 128 and at most 4 query heads per key/value head,
+ * and runs one launch per operation (no single-launch step). */
 size_t ds_kv_cache_bytes(const ds_config* cfg, int32_t B, int32_t T);
 /* Device scratch the library needs for a (B, T) cache. */
 size_t ds_workspace_bytes(const ds_config* cfg, int32_t B, int32_t T);

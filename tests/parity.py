@@ -7,6 +7,13 @@ import numpy as np
 
 ABS_TOL = 5e-4   # max |logit_gpu - logit_ref|
 REL_TOL = 1e-4   # max |logit_gpu - logit_ref| / max |logit_ref|
+# With a bf16 key/value cache both sides round each stored value to bf16 from
+# fp32 values that differ in their last bits, so a value near a rounding
+# boundary lands one bf16 step (2^-8 relative) apart, and every later position
+# attends over it.  The logits then move by about 1e-4 relative; the bound is
+# ten times that, and still ten times below the 1e-2 that the rounding itself
+# moves the oracle's logits (test_oracle_bf16cache.py).
+BF16_CACHE_TOL = (4e-3, 1e-3)
 
 
 def logit_errors(got: np.ndarray, ref: np.ndarray):
@@ -16,10 +23,10 @@ def logit_errors(got: np.ndarray, ref: np.ndarray):
     return mx, mx / max(scale, 1e-30)
 
 
-def assert_logits_close(got, ref, what=""):
+def assert_logits_close(got, ref, what="", tol=(ABS_TOL, REL_TOL)):
     assert np.all(np.isfinite(got)), f"{what}: non-finite GPU values"
     mx, rel = logit_errors(got, ref)
-    assert mx <= ABS_TOL and rel <= REL_TOL, f"{what}: max|d|={mx:.3e} rel={rel:.3e}"
+    assert mx <= tol[0] and rel <= tol[1], f"{what}: max|d|={mx:.3e} rel={rel:.3e}"
     return mx
 
 

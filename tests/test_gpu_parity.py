@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import synth
-from parity import assert_logits_close, check_tokens, oracle_run
+from parity import BF16_CACHE_TOL, assert_logits_close, check_tokens, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -65,29 +65,50 @@ def gpu_run(shape, arena, prompts, feed, T, dispatch=1, use_batch_prefill=True, 
         stream.synchronize()
     kv.check(stream)
     out = dict(first_tok=first_tok, first_lg=first_lg, toks=toks, lgs=lgs,
-               cache=kv.cache_view().cpu().numpy(), lengths=kv.lengths.cpu().numpy(),
+               cache=kv.cache_view().float().cpu().numpy(), lengths=kv.lengths.cpu().numpy(),
                mirror=np.array(kv.get_lengths()), single_launch_ctx=kv.single_launch_ctx())
     kv.close()
     model.close()
     return out
 
 
+def bf16_rows_close(got, ref, what):
+    """Cache rows of a bf16 cache.  Where both sides rounded a value near a
+    rounding boundary they land one bf16 step apart, and later rows that
+    attend over it inherit the difference; so every value must be within one
+    bf16 step of the rows' largest magnitude (2^-7 max|ref|), and at least
+    90% of the values must be bit-equal (a different rounding rule, or none,
+    misses that by far)."""
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU values"
+    d = np.abs(got.astype(np.float64) - ref)
+    bound = 2.0 ** -7 * max(float(np.abs(ref).max()), 1.0)
+    assert d.max() <= bound, f"{what}: max|d| {d.max():.3e} above one bf16 step {bound:.3e}"
+    eq = float(np.mean(got.view(np.uint32) == np.ascontiguousarray(ref, np.float32).view(np.uint32)))
+    assert eq >= 0.9, f"{what}: only {eq:.1%} of the values bit-equal"
+    return eq
+
+
 def compare(shape, arena, prompts, decode_calls, T, what, **kw):
     ref_first, ref_first_lg, ref_toks, ref_lgs, om = oracle_run(shape, arena, prompts, decode_calls, T)
     feed = [ref_first] + ref_toks[:-1]
     g = gpu_run(shape, arena, prompts, feed, T, **kw)
+    tol = BF16_CACHE_TOL if shape.cache_dtype == synth.BF16 else None
+    close = (lambda a, b, w: assert_logits_close(a, b, w, tol)) if tol else assert_logits_close
     ties = check_tokens(g["first_tok"], ref_first, ref_first_lg, g["first_lg"], f"{what} prefill")
-    assert_logits_close(g["first_lg"], ref_first_lg, f"{what} prefill")
+    close(g["first_lg"], ref_first_lg, f"{what} prefill")
     worst = 0.0
     for k in range(decode_calls):
-        worst = max(worst, assert_logits_close(g["lgs"][k], ref_lgs[k], f"{what} step {k}"))
+        worst = max(worst, close(g["lgs"][k], ref_lgs[k], f"{what} step {k}"))
         ties += check_tokens(g["toks"][k], ref_toks[k], ref_lgs[k], g["lgs"][k], f"{what} step {k}")
     lengths = np.array([len(p) + decode_calls for p in prompts], np.int32)
     assert np.array_equal(g["lengths"], lengths) and np.array_equal(g["mirror"], lengths)
     ref_cache = om.cache_view()
     for b, n in enumerate(lengths):
         got = g["cache"][:, :, b, :, :n]
-        assert_logits_close(got, ref_cache[:, :, b, :, :n], f"{what} cache seq {b}")
+        if shape.cache_dtype == synth.BF16:
+            bf16_rows_close(got, ref_cache[:, :, b, :, :n], f"{what} cache seq {b}")
+        else:
+            assert_logits_close(got, ref_cache[:, :, b, :, :n], f"{what} cache seq {b}")
         assert np.all(np.isnan(g["cache"][:, :, b, :, n:])), f"{what}: slot beyond length written"
     _say(f"{what}: max|dlogit| {worst:.2e}, near-ties {ties}")
     return g
