@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void k_mm(StepArgs s, LayerW w, int layer, int
 // each lane's four (tile rows kq*4 + w), with the epilogues of k_mm.  The
 // item groups of one row tile are 8 block indices apart, so they run on the
 // same XCD and share its L2 copy of the weight tile.
-template <int KIND, int MAXS>
+template <int KIND, int MAXS, bool LOOP>
 __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, int n_items, int ident, int n_tiles,
                                                 int n_groups) {
     constexpr bool NORM = KIND == MM_QKV || KIND == MM_W13;
@@ -346,60 +346,82 @@ __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, 
             rsn = s.rope_sin[static_cast<size_t>(pos) * half_d + ii];
         }
     }
-    // every load of the wave's k-steps (wave-uniform count)
+    // The wave's k-steps are wave + 4 i.  Without LOOP all of them (at most
+    // MAXS) are loaded at once; with LOOP they go in batches of MAXS, the
+    // next batch's loads issued before this batch's products (long rows).
     const int nks = K / 32;
-    uint4 wa[MAXS], wb[MAXS];
-    float4 xa[MAXS], xb[MAXS], ga[MAXS], gb[MAXS];
+    struct Batch {
+        uint4 wa[MAXS], wb[MAXS];
+        float4 xa[MAXS], xb[MAXS], ga[MAXS], gb[MAXS];
+    };
+    auto load = [&](Batch& bt, int i0) {
 #pragma unroll
-    for (int i = 0; i < MAXS; i++) {
-        const int ks = wave + 4 * i;
-        if (ks < nks) {
-            const int k0 = ks * 32;
-            wa[i] = *reinterpret_cast<const uint4*>(Wrow + k0);
-            if (TWO) wb[i] = *reinterpret_cast<const uint4*>(W3row + k0);
-            xa[i] = *reinterpret_cast<const float4*>(xrow + k0);
-            xb[i] = *reinterpret_cast<const float4*>(xrow + k0 + 4);
-            if (NORM) {
-                ga[i] = *reinterpret_cast<const float4*>(grow + k0);
-                gb[i] = *reinterpret_cast<const float4*>(grow + k0 + 4);
-            }
-        }
-    }
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, acc3 = f32x4{0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < MAXS; i++) {
-        if (wave + 4 * i < nks) {
-            const float xs[8] = {xa[i].x, xa[i].y, xa[i].z, xa[i].w, xb[i].x, xb[i].y, xb[i].z, xb[i].w};
-            float gv[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-            if constexpr (NORM) {
-                gv[0] = ga[i].x; gv[1] = ga[i].y; gv[2] = ga[i].z; gv[3] = ga[i].w;
-                gv[4] = gb[i].x; gv[5] = gb[i].y; gv[6] = gb[i].z; gv[7] = gb[i].w;
-            }
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int c = 0; c < 8; c++) {
-                const float x = m_ok ? xs[c] : 0.f;
-                ss = fmaf(x, x, ss);
-                const float val = NORM ? gv[c] * x : x;
-                const uint32_t h = bf16_bits_rne(val);
-                const uint32_t l = bf16_bits_rne(val - __uint_as_float(h << 16));
-                if (c & 1) {
-                    hi[c >> 1] |= h << 16;
-                    lo[c >> 1] |= l << 16;
-                } else {
-                    hi[c >> 1] = h;
-                    lo[c >> 1] = l;
+        for (int i = 0; i < MAXS; i++) {
+            const int ks = wave + 4 * (i0 + i);
+            if (ks < nks) {
+                const int k0 = ks * 32;
+                bt.wa[i] = *reinterpret_cast<const uint4*>(Wrow + k0);
+                if (TWO) bt.wb[i] = *reinterpret_cast<const uint4*>(W3row + k0);
+                bt.xa[i] = *reinterpret_cast<const float4*>(xrow + k0);
+                bt.xb[i] = *reinterpret_cast<const float4*>(xrow + k0 + 4);
+                if (NORM) {
+                    bt.ga[i] = *reinterpret_cast<const float4*>(grow + k0);
+                    bt.gb[i] = *reinterpret_cast<const float4*>(grow + k0 + 4);
                 }
             }
-            const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]), bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-            acc = mfma(wa[i], bh, acc);
-            acc = mfma(wa[i], bl, acc);
-            if (TWO) {
-                acc3 = mfma(wb[i], bh, acc3);
-                acc3 = mfma(wb[i], bl, acc3);
+        }
+    };
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, acc3 = f32x4{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    auto products = [&](const Batch& bt, int i0) {
+#pragma unroll
+        for (int i = 0; i < MAXS; i++) {
+            if (wave + 4 * (i0 + i) < nks) {
+                const float xs[8] = {bt.xa[i].x, bt.xa[i].y, bt.xa[i].z, bt.xa[i].w,
+                                     bt.xb[i].x, bt.xb[i].y, bt.xb[i].z, bt.xb[i].w};
+                float gv[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+                if constexpr (NORM) {
+                    gv[0] = bt.ga[i].x; gv[1] = bt.ga[i].y; gv[2] = bt.ga[i].z; gv[3] = bt.ga[i].w;
+                    gv[4] = bt.gb[i].x; gv[5] = bt.gb[i].y; gv[6] = bt.gb[i].z; gv[7] = bt.gb[i].w;
+                }
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int c = 0; c < 8; c++) {
+                    const float x = m_ok ? xs[c] : 0.f;
+                    ss = fmaf(x, x, ss);
+                    const float val = NORM ? gv[c] * x : x;
+                    const uint32_t h = bf16_bits_rne(val);
+                    const uint32_t l = bf16_bits_rne(val - __uint_as_float(h << 16));
+                    if (c & 1) {
+                        hi[c >> 1] |= h << 16;
+                        lo[c >> 1] |= l << 16;
+                    } else {
+                        hi[c >> 1] = h;
+                        lo[c >> 1] = l;
+                    }
+                }
+                const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]), bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                acc = mfma(bt.wa[i], bh, acc);
+                acc = mfma(bt.wa[i], bl, acc);
+                if (TWO) {
+                    acc3 = mfma(bt.wb[i], bh, acc3);
+                    acc3 = mfma(bt.wb[i], bl, acc3);
+                }
             }
         }
+    };
+    Batch cur;
+    load(cur, 0);
+    if constexpr (LOOP) {
+        for (int i0 = 0; wave + 4 * i0 < nks; i0 += MAXS) {  // the wave's own batch count
+            Batch nxt;
+            const bool more = wave + 4 * (i0 + MAXS) < nks;
+            if (more) load(nxt, i0 + MAXS);
+            products(cur, i0);
+            if (more) cur = nxt;
+        }
+    } else {
+        products(cur, 0);
     }
     if (NORM) {  // the item's sum over the wave's k-steps: lanes ti, ti + 16, ti + 32, ti + 48
         ss += __shfl_xor(ss, 16);
@@ -562,17 +584,19 @@ static int sk_dims(const StepArgs& s, int& K, int& N) {
     if (KIND == MM_W2) { N = s.d; K = s.F; }
     const int per_wave = (K / 32 + 3) / 4;
     constexpr int cap = (KIND == MM_QKV || KIND == MM_W13) ? 8 : 16;
-    if (per_wave > cap) return 0;
+    // longer rows: batches of 4 k-steps in a loop (not W1/W3, whose tiled
+    // kernel reads each weight once for all 64 items)
+    if (per_wave > cap) return KIND == MM_W13 ? 0 : -4;
     for (int m : {1, 2, 3, 5, 8, 12, 16})
         if (per_wave <= m) return m;
     return 0;
 }
 
-template <int KIND, int MAXS>
+template <int KIND, int MAXS, bool LOOP = false>
 static void launch_sk_one(const StepArgs& s, const LayerW& w, int layer, int n, int ident, int n_tiles, hipStream_t st) {
     const int n_groups = (n + 15) / 16;
     const dim3 grid(((n_tiles + 7) / 8) * 8 * n_groups);
-    hipLaunchKernelGGL((k_mm_sk<KIND, MAXS>), grid, dim3(256), 0, st, s, w, layer, n, ident, n_tiles, n_groups);
+    hipLaunchKernelGGL((k_mm_sk<KIND, MAXS, LOOP>), grid, dim3(256), 0, st, s, w, layer, n, ident, n_tiles, n_groups);
 }
 
 // false when the split-K kernel does not take this shape (then the tiled one runs)
@@ -582,6 +606,7 @@ static bool launch_sk(const StepArgs& s, const LayerW& w, int layer, int n, int 
     const int m = sk_dims<KIND>(s, K, N);
     const int nt = N / 16;
     switch (m) {
+        case -4: launch_sk_one<KIND, 4, true>(s, w, layer, n, ident, nt, st); return true;
         case 1: launch_sk_one<KIND, 1>(s, w, layer, n, ident, nt, st); return true;
         case 2: launch_sk_one<KIND, 2>(s, w, layer, n, ident, nt, st); return true;
         case 3: launch_sk_one<KIND, 3>(s, w, layer, n, ident, nt, st); return true;

@@ -239,6 +239,13 @@ MM_SHAPE2 = synth.small_shape(dim=192, n_heads=6, n_kv_heads=2, head_dim=32, hid
                               weight_dtype=synth.BF16)
 
 
+# Rows long enough for the split-K kernel's batch loop: Q/K/V and W2 inputs
+# of 1152 and 2304 values (9 and 18 k-steps per wave, ragged last batches),
+# Wo's input 36 * 64 = 2304
+MM_SHAPE_LONG = synth.small_shape(dim=1152, n_heads=36, n_kv_heads=12, head_dim=64, hidden_dim=2304,
+                                  vocab_size=512, weight_dtype=synth.BF16)
+
+
 @pytest.fixture(params=["split", "tiled"])
 def mm_kernel(request, monkeypatch):
     """Both MFMA projection kernels: split-K (the default for narrow
@@ -256,7 +263,8 @@ def test_batched_prefill_bf16_mfma_matches_oracle(mm_kernel):
     compare(MM_SHAPE, arena, prompts, 2, 128, "bf16 batched prefill", batched=True)
 
 
-@pytest.mark.parametrize("B,shape", [(20, MM_SHAPE), (70, MM_SHAPE), (37, MM_SHAPE2)], ids=["20", "70", "37-k192"])
+@pytest.mark.parametrize("B,shape", [(20, MM_SHAPE), (70, MM_SHAPE), (37, MM_SHAPE2), (18, MM_SHAPE_LONG)],
+                         ids=["20", "70", "37-k192", "18-long-rows"])
 def test_batched_mfma_projections_match_oracle(B, shape, mm_kernel):
     """Batches of 16+ sequences take the MFMA projections (bf16 weights, fp32
     activations split into two bf16 terms): 20 leaves part of a 16-item MFMA
