@@ -130,8 +130,13 @@ __device__ void pick_digit(const uint32_t* hist, uint32_t rem, uint32_t* dig, ui
     __syncthreads();
 }
 
-// Radix select over the n keys at cand[0..n) (in LDS, NT threads): the
-// k-th largest key (1 <= k <= n).
+// Radix select over the n keys at cand[0..n) (in LDS, NT threads): a
+// threshold such that exactly k keys are >= it (1 <= k <= n; the keys are
+// distinct).  That is the k-th largest key itself, unless a pass finds that
+// every key left in the chosen digit's bucket is among the k: then the
+// prefix so far, with the lower bits zero, already separates them, and the
+// remaining passes are skipped (with distinct logits that is usually the
+// case once the 32 value bits are resolved, after half the passes).
 template <int NT>
 __device__ uint64_t radix_kth(const uint64_t* cand, int n, int k, uint32_t* hist, uint32_t* sh_dig,
                               uint32_t* sh_rem) {
@@ -147,10 +152,13 @@ __device__ uint64_t radix_kth(const uint64_t* cand, int n, int k, uint32_t* hist
             if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFF], 1u);
         }
         pick_digit(hist, rem, sh_dig, sh_rem);
-        prefix |= static_cast<uint64_t>(*sh_dig) << shift;
+        const uint32_t dig = *sh_dig;
+        prefix |= static_cast<uint64_t>(dig) << shift;
         mask |= static_cast<uint64_t>(0xFF) << shift;
         rem = *sh_rem;
-        __syncthreads();
+        const bool whole = hist[dig] == rem;  // the bucket is all in (uniform)
+        __syncthreads();  // before the next pass clears hist
+        if (whole) break;
     }
     return prefix;
 }
