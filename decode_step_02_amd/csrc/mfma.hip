@@ -275,20 +275,21 @@ __global__ __launch_bounds__(256) void k_mm(StepArgs s, LayerW w, int layer, int
 // Q/K/V, Wo, W1/W3 and W2 of a small model have few weight rows (576..1536),
 // so the tiled kernel above puts only a few dozen blocks on the chip and each
 // wave walks K in dependent tiles.  Here a block is one tile of 16 weight rows
-// x 16 items; its four waves take every fourth 32-wide k-step, issue all of
+// x 16 items; its NW waves (4 or 8) take every NW-th 32-wide k-step, issue
 // their weight, activation and gain loads at once (the activations straight
 // from global memory into the B-operand layout, split into bf16 hi + lo in
-// registers), run their MFMAs and add their partial tiles (and the items'
-// partial sums of squares) through LDS.  Wave w then finishes row r = w of
+// registers; rows too long for the registers in batches, the next batch in
+// flight), run their MFMAs and add their partial tiles (and the items'
+// partial sums of squares) through LDS.  Waves w < 4 then finish row r = w of
 // each lane's four (tile rows kq*4 + w), with the epilogues of k_mm.  The
 // item groups of one row tile are 8 block indices apart, so they run on the
 // same XCD and share its L2 copy of the weight tile.
-template <int KIND, int MAXS, bool LOOP>
-__global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, int n_items, int ident, int n_tiles,
-                                                int n_groups) {
+template <int KIND, int MAXS, bool LOOP, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_mm_sk(StepArgs s, LayerW w, int layer, int n_items, int ident, int n_tiles,
+                                                    int n_groups) {
     constexpr bool NORM = KIND == MM_QKV || KIND == MM_W13;
     constexpr bool TWO = KIND == MM_W13;
-    __shared__ float red[4][9][64];  // [wave][acc 0..3, acc3 0..3, sum of squares][lane]
+    __shared__ float red[NW][9][64];  // [wave][acc 0..3, acc3 0..3, sum of squares][lane]
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ti = lane & 15, kq = lane >> 4;
     const int L = blockIdx.x, span = 8 * n_groups;
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, 
     auto load = [&](Batch& bt, int i0) {
 #pragma unroll
         for (int i = 0; i < MAXS; i++) {
-            const int ks = wave + 4 * (i0 + i);
+            const int ks = wave + NW * (i0 + i);
             if (ks < nks) {
                 const int k0 = ks * 32;
                 bt.wa[i] = *reinterpret_cast<const uint4*>(Wrow + k0);
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, 
     auto products = [&](const Batch& bt, int i0) {
 #pragma unroll
         for (int i = 0; i < MAXS; i++) {
-            if (wave + 4 * (i0 + i) < nks) {
+            if (wave + NW * (i0 + i) < nks) {
                 const float xs[8] = {bt.xa[i].x, bt.xa[i].y, bt.xa[i].z, bt.xa[i].w,
                                      bt.xb[i].x, bt.xb[i].y, bt.xb[i].z, bt.xb[i].w};
                 float gv[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
@@ -413,9 +414,9 @@ __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, 
     Batch cur;
     load(cur, 0);
     if constexpr (LOOP) {
-        for (int i0 = 0; wave + 4 * i0 < nks; i0 += MAXS) {  // the wave's own batch count
+        for (int i0 = 0; wave + NW * i0 < nks; i0 += MAXS) {  // the wave's own batch count
             Batch nxt;
-            const bool more = wave + 4 * (i0 + MAXS) < nks;
+            const bool more = wave + NW * (i0 + MAXS) < nks;
             if (more) load(nxt, i0 + MAXS);
             products(cur, i0);
             if (more) cur = nxt;
@@ -434,14 +435,17 @@ __global__ __launch_bounds__(256) void k_mm_sk(StepArgs s, LayerW w, int layer, 
     }
     if (NORM) red[wave][8][lane] = ss;
     __syncthreads();
+    if (wave >= 4) return;  // waves 0..3 finish the tile's rows
     const int r = wave;  // this wave finishes tile row kq * 4 + r (= ri)
-    float y = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
-    float y3 = TWO ? red[0][4 + r][lane] + red[1][4 + r][lane] + red[2][4 + r][lane] + red[3][4 + r][lane] : 0.f;
-    float r_m = 1.f;
-    if (NORM) {
-        const float sq = red[0][8][lane] + red[1][8][lane] + red[2][8][lane] + red[3][8][lane];
-        r_m = 1.0f / sqrtf(sq / static_cast<float>(K) + s.eps);
+    float y = 0.f, y3 = 0.f, sq = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; v++) {
+        y += red[v][r][lane];
+        if (TWO) y3 += red[v][4 + r][lane];
+        if (NORM) sq += red[v][8][lane];
     }
+    float r_m = 1.f;
+    if (NORM) r_m = 1.0f / sqrtf(sq / static_cast<float>(K) + s.eps);
     const int i = ri;
     if (KIND == MM_QKV) {
         y *= r_m;
@@ -573,48 +577,50 @@ hipError_t mm_set_attributes(int lds) {
     return e;
 }
 
-// ---- split-K launch: k-steps per wave, 8 or 16 at most (registers) -----------------------------
+// ---- split-K launch -----------------------------------------------------------------------------
 template <int KIND>
-static int sk_dims(const StepArgs& s, int& K, int& N) {
+static void sk_dims(const StepArgs& s, int& K, int& N) {
     K = s.d;
     N = 0;
     if (KIND == MM_QKV) N = (s.H + 2 * s.Hkv) * s.D;
     if (KIND == MM_WO) { N = s.d; K = s.H * s.D; }
     if (KIND == MM_W13) N = s.F;
     if (KIND == MM_W2) { N = s.d; K = s.F; }
-    const int per_wave = (K / 32 + 3) / 4;
-    constexpr int cap = (KIND == MM_QKV || KIND == MM_W13) ? 8 : 16;
-    // longer rows: batches of 4 k-steps in a loop (not W1/W3, whose tiled
-    // kernel reads each weight once for all 64 items)
-    if (per_wave > cap) return KIND == MM_W13 ? 0 : -4;
-    for (int m : {1, 2, 3, 5, 8, 12, 16})
-        if (per_wave <= m) return m;
-    return 0;
 }
 
-template <int KIND, int MAXS, bool LOOP = false>
+template <int KIND, int MAXS, bool LOOP = false, int NW = 4>
 static void launch_sk_one(const StepArgs& s, const LayerW& w, int layer, int n, int ident, int n_tiles, hipStream_t st) {
     const int n_groups = (n + 15) / 16;
     const dim3 grid(((n_tiles + 7) / 8) * 8 * n_groups);
-    hipLaunchKernelGGL((k_mm_sk<KIND, MAXS, LOOP>), grid, dim3(256), 0, st, s, w, layer, n, ident, n_tiles, n_groups);
+    hipLaunchKernelGGL((k_mm_sk<KIND, MAXS, LOOP, NW>), grid, dim3(64 * NW), 0, st, s, w, layer, n, ident, n_tiles,
+                       n_groups);
 }
 
-// false when the split-K kernel does not take this shape (then the tiled one runs)
+// Rows of up to 8 k-steps per wave (5 for the kinds with gains, registers)
+// take 8-wave blocks with every load issued at once; longer rows take 4-wave
+// blocks that loop over batches of 4 k-steps, except W1/W3, whose tiled
+// kernel reads each weight once for all 64 items.  false: the tiled kernel
+// runs instead.
 template <int KIND>
 static bool launch_sk(const StepArgs& s, const LayerW& w, int layer, int n, int ident, hipStream_t st) {
     int K = 0, N = 0;
-    const int m = sk_dims<KIND>(s, K, N);
+    sk_dims<KIND>(s, K, N);
     const int nt = N / 16;
-    switch (m) {
-        case -4: launch_sk_one<KIND, 4, true>(s, w, layer, n, ident, nt, st); return true;
-        case 1: launch_sk_one<KIND, 1>(s, w, layer, n, ident, nt, st); return true;
-        case 2: launch_sk_one<KIND, 2>(s, w, layer, n, ident, nt, st); return true;
-        case 3: launch_sk_one<KIND, 3>(s, w, layer, n, ident, nt, st); return true;
-        case 5: launch_sk_one<KIND, 5>(s, w, layer, n, ident, nt, st); return true;
-        case 8: launch_sk_one<KIND, 8>(s, w, layer, n, ident, nt, st); return true;
-        case 12: if constexpr (KIND == MM_WO || KIND == MM_W2) { launch_sk_one<KIND, 12>(s, w, layer, n, ident, nt, st); return true; } return false;
-        case 16: if constexpr (KIND == MM_WO || KIND == MM_W2) { launch_sk_one<KIND, 16>(s, w, layer, n, ident, nt, st); return true; } return false;
-        default: return false;
+    const int per8 = (K / 32 + 7) / 8;
+    constexpr int cap8 = (KIND == MM_QKV || KIND == MM_W13) ? 5 : 8;
+    if (per8 <= cap8) {
+        if (per8 <= 1) launch_sk_one<KIND, 1, false, 8>(s, w, layer, n, ident, nt, st);
+        else if (per8 <= 2) launch_sk_one<KIND, 2, false, 8>(s, w, layer, n, ident, nt, st);
+        else if (per8 <= 3) launch_sk_one<KIND, 3, false, 8>(s, w, layer, n, ident, nt, st);
+        else if (per8 <= 5) launch_sk_one<KIND, 5, false, 8>(s, w, layer, n, ident, nt, st);
+        else if constexpr (cap8 == 8) launch_sk_one<KIND, 8, false, 8>(s, w, layer, n, ident, nt, st);
+        return true;
+    }
+    if constexpr (KIND == MM_W13) {
+        return false;
+    } else {
+        launch_sk_one<KIND, 4, true, 4>(s, w, layer, n, ident, nt, st);
+        return true;
     }
 }
 
