@@ -733,27 +733,27 @@ __global__ __launch_bounds__(256) void k_attn_d(StepArgs s, int layer) {
 //  - The softmax weights of the chunk go through LDS; max and sum are taken
 //    over the block, the weighted values summed over the four waves in LDS.
 // Partials as k_attn_d: (m, l) and the weighted sum per (item, head, chunk).
-// One lane's share of the keys and values of a wave's 16 rows, fp32 or bf16.
-// fp32 keys: lane q holds dims 32f + 4q .. +3 (f < D/32); bf16 keys: dims
-// 64f + 8q .. +7 (f < D/64, one 16-byte load each): either way D/8 dims,
-// read as whole 128-byte lines per row, and qdim() gives the query offsets
-// that match.  Values: D/64 dims per lane; bf16 ones stay packed until used.
-template <int D, int CDT> struct KVRows;
-template <int D> struct KVRows<D, kF32> {
-    static constexpr int KF = D / 32, DPL = D / 64;
-    float4 k[2][KF];
-    float v[16][DPL];
+// One lane's share of the keys and values of a wave's RPW rows (16 or 8),
+// fp32 or bf16.  fp32 keys: lane q holds dims 32f + 4q .. +3 (f < D/32);
+// bf16 keys: dims 64f + 8q .. +7 (f < D/64, one 16-byte load each): either
+// way D/8 dims, read as whole 128-byte lines per row, and qdim() gives the
+// query offsets that match.  The rows come in slots of 8 (one per 8 lanes).
+// Values: D/64 dims per lane; bf16 ones stay packed until used.
+template <int D, int CDT, int RPW> struct KVRows;
+template <int D, int RPW> struct KVRows<D, kF32, RPW> {
+    static constexpr int KF = D / 32, DPL = D / 64, NSL = RPW / 8;
+    float4 k[NSL][KF];
+    float v[RPW][DPL];
     __device__ static __forceinline__ int qdim(int f, int kq) { return f * 32 + kq * 4; }
-    __device__ __forceinline__ void load(const float* Kb, const float* Vb, int r0, int r1, int rv0, int nlast, int kq,
-                                         int lane) {
-        const int rows[2] = {r0, r1};
+    __device__ __forceinline__ void load(const float* Kb, const float* Vb, const int (&rows)[NSL], int rv0, int nlast,
+                                         int kq, int lane) {
 #pragma unroll
-        for (int sl = 0; sl < 2; sl++) {
+        for (int sl = 0; sl < NSL; sl++) {
 #pragma unroll
             for (int f = 0; f < KF; f++) k[sl][f] = *reinterpret_cast<const float4*>(Kb + rows[sl] * D + f * 32 + kq * 4);
         }
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
+        for (int i = 0; i < RPW; i++) {
             const float* vp = Vb + min(rv0 + i, nlast) * D + lane * DPL;
             if constexpr (DPL == 1) {
                 v[i][0] = *vp;
@@ -767,23 +767,22 @@ template <int D> struct KVRows<D, kF32> {
     __device__ __forceinline__ float4 key(int sl, int f) const { return k[sl][f]; }
     __device__ __forceinline__ float val(int i, int dd) const { return v[i][dd]; }
 };
-template <int D> struct KVRows<D, kBF16> {
-    static constexpr int KF = D / 32, DPL = D / 64;
-    uint4 k[2][D / 64];
-    uint32_t v[16];  // the row's DPL bf16 values (D = 128: two, the lower dim in the low half)
+template <int D, int RPW> struct KVRows<D, kBF16, RPW> {
+    static constexpr int KF = D / 32, DPL = D / 64, NSL = RPW / 8;
+    uint4 k[NSL][D / 64];
+    uint32_t v[RPW];  // the row's DPL bf16 values (D = 128: two, the lower dim in the low half)
     __device__ static __forceinline__ int qdim(int f, int kq) { return (f >> 1) * 64 + kq * 8 + (f & 1) * 4; }
-    __device__ __forceinline__ void load(const float* Kb, const float* Vb, int r0, int r1, int rv0, int nlast, int kq,
-                                         int lane) {
+    __device__ __forceinline__ void load(const float* Kb, const float* Vb, const int (&rows)[NSL], int rv0, int nlast,
+                                         int kq, int lane) {
         const uint16_t* K16 = reinterpret_cast<const uint16_t*>(Kb);
         const uint16_t* V16 = reinterpret_cast<const uint16_t*>(Vb);
-        const int rows[2] = {r0, r1};
 #pragma unroll
-        for (int sl = 0; sl < 2; sl++) {
+        for (int sl = 0; sl < NSL; sl++) {
 #pragma unroll
             for (int f = 0; f < D / 64; f++) k[sl][f] = *reinterpret_cast<const uint4*>(K16 + rows[sl] * D + f * 64 + kq * 8);
         }
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
+        for (int i = 0; i < RPW; i++) {
             const uint16_t* vp = V16 + min(rv0 + i, nlast) * D + lane * DPL;
             if constexpr (DPL == 1)
                 v[i] = *vp;
@@ -803,15 +802,23 @@ template <int D> struct KVRows<D, kBF16> {
     }
 };
 
-template <int D, int REP, int CDT>
-__global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
+// Split-K decode attention for head_dim 64 or 128 with REP query heads per
+// key/value head: a block of NWV waves per 64-position chunk of one (item,
+// group), wave w taking positions RPW w .. RPW w + RPW - 1 (RPW = 64 / NWV).
+// Each dot product is reduced over its row's 8 lanes with DPP moves; the
+// softmax weights of the chunk go through LDS, with max and sum over the
+// block; the weighted values are summed over the waves in LDS.  Partials
+// (m, l) and the weighted sum per (item, head, chunk).
+template <int D, int REP, int CDT, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_attn_g(StepArgs s, int layer) {
     constexpr int KF = D / 32;   // key float4s per lane and row
     constexpr int DPL = D / 64;  // value dims per lane
+    constexpr int RPW = kChunk / NWV, NSL = RPW / 8;
     static_assert(D == 64 || D == 128, "head_dim");
-    static_assert(kChunk == 64, "four waves of 16 positions");
+    static_assert(kChunk == 64 && (NWV == 4 || NWV == 8), "64 positions over 4 or 8 waves");
     __shared__ float pw[REP][kChunk];
-    __shared__ float wred[2][4][REP];
-    __shared__ float ored[4][REP][D];
+    __shared__ float wred[2][NWV][REP];
+    __shared__ float ored[NWV][REP][D];
     const int chunk = blockIdx.x, g = blockIdx.y, item = blockIdx.z;
     const int pos = s.pos[item], slot = s.slot[item];
     const int n = pos + 1;
@@ -826,31 +833,35 @@ __global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
                                    : s.cache + kidx;
     const float* Vb = CDT == kBF16 ? reinterpret_cast<const float*>(reinterpret_cast<const uint16_t*>(s.cache) + vidx)
                                    : s.cache + vidx;
-    KVRows<D, CDT> kv;
-    kv.load(Kb, Vb, min(wave * 16 + rr, nt - 1), min(wave * 16 + 8 + rr, nt - 1), wave * 16, nt - 1, kq, lane);
+    KVRows<D, CDT, RPW> kv;
+    int rows[NSL];
+#pragma unroll
+    for (int sl = 0; sl < NSL; sl++) rows[sl] = min(wave * RPW + sl * 8 + rr, nt - 1);
+    kv.load(Kb, Vb, rows, wave * RPW, nt - 1, kq, lane);
     const float* qb = s.q + (static_cast<size_t>(item) * s.H + static_cast<size_t>(g) * REP) * D;
     float4 qv[REP][KF];
 #pragma unroll
     for (int j = 0; j < REP; j++) {
 #pragma unroll
         for (int f = 0; f < KF; f++)
-            qv[j][f] = *reinterpret_cast<const float4*>(qb + j * D + KVRows<D, CDT>::qdim(f, kq));
+            qv[j][f] = *reinterpret_cast<const float4*>(qb + j * D + KVRows<D, CDT, RPW>::qdim(f, kq));
     }
-    // scores of the lane's two rows for every head, reduced over the row's 8 lanes
-    float sc[REP * 2];
+    // scores of the lane's rows for every head, reduced over the row's 8 lanes
+    float sc[REP * NSL];
 #pragma unroll
     for (int j = 0; j < REP; j++) {
 #pragma unroll
-        for (int sl = 0; sl < 2; sl++) {
+        for (int sl = 0; sl < NSL; sl++) {
             float d = 0.f;
 #pragma unroll
             for (int f = 0; f < KF; f++) {
-                d = fmaf(kv.key(sl, f).x, qv[j][f].x, d);
-                d = fmaf(kv.key(sl, f).y, qv[j][f].y, d);
-                d = fmaf(kv.key(sl, f).z, qv[j][f].z, d);
-                d = fmaf(kv.key(sl, f).w, qv[j][f].w, d);
+                const float4 kk = kv.key(sl, f);
+                d = fmaf(kk.x, qv[j][f].x, d);
+                d = fmaf(kk.y, qv[j][f].y, d);
+                d = fmaf(kk.z, qv[j][f].z, d);
+                d = fmaf(kk.w, qv[j][f].w, d);
             }
-            sc[j * 2 + sl] = d;
+            sc[j * NSL + sl] = d;
         }
     }
     group_reduce_n<8, OpSum>(sc, OpSum{});
@@ -858,10 +869,12 @@ __global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
     float m[REP];
 #pragma unroll
     for (int j = 0; j < REP; j++) {
+        m[j] = -INFINITY;
 #pragma unroll
-        for (int sl = 0; sl < 2; sl++)
-            sc[j * 2 + sl] = wave * 16 + sl * 8 + rr < nt ? sc[j * 2 + sl] * scale : -INFINITY;
-        m[j] = OpMax{}(sc[j * 2], sc[j * 2 + 1]);
+        for (int sl = 0; sl < NSL; sl++) {
+            sc[j * NSL + sl] = wave * RPW + sl * 8 + rr < nt ? sc[j * NSL + sl] * scale : -INFINITY;
+            m[j] = OpMax{}(m[j], sc[j * NSL + sl]);
+        }
     }
     group_reduce_n<64, OpMax, 8>(m, OpMax{});  // over the wave's 8-lane row groups
     if (lane == 0) {
@@ -872,12 +885,15 @@ __global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
     float l[REP];
 #pragma unroll
     for (int j = 0; j < REP; j++) {
-        m[j] = OpMax{}(OpMax{}(wred[0][0][j], wred[0][1][j]), OpMax{}(wred[0][2][j], wred[0][3][j]));
+        float mm = wred[0][0][j];
+#pragma unroll
+        for (int v = 1; v < NWV; v++) mm = OpMax{}(mm, wred[0][v][j]);
+        m[j] = mm;
         l[j] = 0.f;
 #pragma unroll
-        for (int sl = 0; sl < 2; sl++) {
-            const float p = __expf(sc[j * 2 + sl] - m[j]);  // 0 for masked rows (the block max is finite)
-            if (kq == 0) pw[j][wave * 16 + sl * 8 + rr] = p;
+        for (int sl = 0; sl < NSL; sl++) {
+            const float p = __expf(sc[j * NSL + sl] - m[j]);  // 0 for masked rows (the block max is finite)
+            if (kq == 0) pw[j][wave * RPW + sl * 8 + rr] = p;
             l[j] += p;
         }
     }
@@ -889,15 +905,15 @@ __global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < REP; j++) {
-        const float4* pj = reinterpret_cast<const float4*>(&pw[j][wave * 16]);
-        float4 pe[4];
+        const float4* pj = reinterpret_cast<const float4*>(&pw[j][wave * RPW]);
+        float4 pe[RPW / 4];
 #pragma unroll
-        for (int c4 = 0; c4 < 4; c4++) pe[c4] = pj[c4];
+        for (int c4 = 0; c4 < RPW / 4; c4++) pe[c4] = pj[c4];
 #pragma unroll
         for (int dd = 0; dd < DPL; dd++) {
             float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-            for (int c4 = 0; c4 < 4; c4++) {
+            for (int c4 = 0; c4 < RPW / 4; c4++) {
                 a0 = fmaf(pe[c4].x, kv.val(4 * c4 + 0, dd), a0);
                 a1 = fmaf(pe[c4].y, kv.val(4 * c4 + 1, dd), a1);
                 a0 = fmaf(pe[c4].z, kv.val(4 * c4 + 2, dd), a0);
@@ -908,25 +924,34 @@ __global__ __launch_bounds__(256) void k_attn_g(StepArgs s, int layer) {
     }
     __syncthreads();
     const int S = s.n_chunks;
-    for (int idx = threadIdx.x; idx < REP * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < REP * D; idx += 64 * NWV) {
         const int j = idx / D, e = idx % D;
-        const float v = (ored[0][j][e] + ored[1][j][e]) + (ored[2][j][e] + ored[3][j][e]);
+        float v = 0.f, lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; w++) {
+            v += ored[w][j][e];
+            lsum += wred[1][w][j];
+        }
         const size_t pidx = (static_cast<size_t>(item) * s.H + g * REP + j) * S + chunk;
         s.part_o[pidx * D + e] = v;
         if (e == 0) {
             s.part_ml[pidx * 2 + 0] = m[j];
-            s.part_ml[pidx * 2 + 1] = (wred[1][0][j] + wred[1][1][j]) + (wred[1][2][j] + wred[1][3][j]);
+            s.part_ml[pidx * 2 + 1] = lsum;
         }
     }
 }
 
+constexpr int kAttnWaves = 4;  // waves per 64-position chunk of k_attn_g
+
 template <int D, int CDT>
 static bool launch_attn_g2(const StepArgs& s, dim3 grid, int layer, hipStream_t st) {
+    constexpr int W = kAttnWaves;
+    const dim3 blk(64 * W);
     switch (s.H / s.Hkv) {
-        case 1: hipLaunchKernelGGL((k_attn_g<D, 1, CDT>), grid, dim3(256), 0, st, s, layer); return true;
-        case 2: hipLaunchKernelGGL((k_attn_g<D, 2, CDT>), grid, dim3(256), 0, st, s, layer); return true;
-        case 3: hipLaunchKernelGGL((k_attn_g<D, 3, CDT>), grid, dim3(256), 0, st, s, layer); return true;
-        case 4: hipLaunchKernelGGL((k_attn_g<D, 4, CDT>), grid, dim3(256), 0, st, s, layer); return true;
+        case 1: hipLaunchKernelGGL((k_attn_g<D, 1, CDT, W>), grid, blk, 0, st, s, layer); return true;
+        case 2: hipLaunchKernelGGL((k_attn_g<D, 2, CDT, W>), grid, blk, 0, st, s, layer); return true;
+        case 3: hipLaunchKernelGGL((k_attn_g<D, 3, CDT, W>), grid, blk, 0, st, s, layer); return true;
+        case 4: hipLaunchKernelGGL((k_attn_g<D, 4, CDT, W>), grid, blk, 0, st, s, layer); return true;
         default: return false;
     }
 }
