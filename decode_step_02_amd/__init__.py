@@ -7,7 +7,7 @@ functions ``ds_*`` mirror the C ABI in ``include/ds_decode.h`` one to one;
 buffers with torch at the sizes the library reports.
 
 Importing this package fails loudly if the library has not been built
-(``python -m decode_step_02_amd.build``).
+(``python decode_step_02_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -45,7 +45,7 @@ class ds_config(C.Structure):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m decode_step_02_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python decode_step_02_amd/build.py`")
 
 _lib = C.CDLL(LIB_PATH)
 _P = C.c_void_p
