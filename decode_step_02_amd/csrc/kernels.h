@@ -22,9 +22,9 @@ constexpr int kMaxArgmaxBlocks = 16384;  // vocabulary blocks per item (argmax p
 constexpr int kPMaxChunks = 64;  // 32-position attention chunks the persistent step can hold per head
 constexpr int kPMaxParts = kPMaxChunks / 4;  // their partials, one per four chunks
 constexpr int kPKeyWords = 1024; // argmax words of the persistent step (one per wave)
-constexpr int kPRep = 8;
+constexpr int kPRep = 8;         // most replicas of a vector the persistent step publishes
 constexpr int kMaxTopK = 1024;   // largest top-k of the sampling epilogue
-constexpr int kSampleMaxV = 1 << 20;  // largest vocabulary of the sampling epilogue          // most replicas of a vector the persistent step publishes
+constexpr int kSampleMaxV = 1 << 20;  // largest vocabulary of the sampling epilogue
 constexpr int kMmItems = 64;     // items per MFMA launch
 constexpr int kMmMin = 16;       // steps with at least this many items use the MFMA projections
 
