@@ -1225,7 +1225,7 @@ static int pick_g(int K, int wdt, int rows = 1 << 30) {
     return 32;
 }
 
-// one-wave blocks while the staged vector is small, 4-wave blocks (sharing it) beyond 4096 floats
+// one-wave blocks while the staged vector is small, 4-wave blocks (sharing it) beyond 2048 floats
 static int pick_waves(int K) { return K <= 2048 ? 1 : 4; }
 
 size_t short_lds(const StepArgs& s, int short_n) {
@@ -1298,6 +1298,13 @@ template <int WDT, int G>
 static hipError_t launch2(Gemv which, int waves, const StepArgs& s, const LayerW& w, int layer, int n_items,
                           hipStream_t st, const float* out_norm, const void* wcls, Launch lc) {
     if (waves == 1) return launch3<WDT, G, 1>(which, s, w, layer, n_items, st, out_norm, wcls, lc);
+    if (waves == 8) {  // W2 over long rows only (pick in gemv)
+        if (which != G_W2) return hipErrorInvalidValue;
+        constexpr int RB = 8 * (64 / G);
+        hipLaunchKernelGGL((k_w2<WDT, G, 8>), dim3((s.d + RB - 1) / RB, n_items), dim3(512), sizeof(float) * s.F, st,
+                           s, w);
+        return hipGetLastError();
+    }
     return launch3<WDT, G, 4>(which, s, w, layer, n_items, st, out_norm, wcls, lc);
 }
 
@@ -1329,6 +1336,10 @@ static hipError_t gemv(Gemv which, const StepArgs& s, const LayerW& w, int layer
     if (which == G_W2) K = s.F;
     int waves = pick_waves(K);
     if (which == G_LOGITS || which == G_WO_SHORT) waves = 4;
+    // W2 rows longer than 8192: 8-wave blocks, so half as many blocks stage
+    // the whole h (22 us against 26.6 per launch at the 8B shape; 8 waves for
+    // the other long-row products measured slower)
+    if (which == G_W2 && K > 8192) waves = 8;
     if (s.wdt == kBF16) return launch1<kBF16>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
     if (s.wdt == kQ8) return launch1<kQ8>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
     if (s.wdt == kQ4) return launch1<kQ4>(which, K, waves, s, w, layer, n_items, st, out_norm, wcls, lc);
@@ -1358,6 +1369,9 @@ static hipError_t set_attrs1(int lds) {
     if (e == hipSuccess) e = set_attrs3<WDT, 16, 4>(lds);
     if (e == hipSuccess) e = set_attrs3<WDT, 32, 1>(lds);
     if (e == hipSuccess) e = set_attrs3<WDT, 32, 4>(lds);
+    for (const void* fn : {reinterpret_cast<const void*>(k_w2<WDT, 8, 8>), reinterpret_cast<const void*>(k_w2<WDT, 16, 8>),
+                           reinterpret_cast<const void*>(k_w2<WDT, 32, 8>)})
+        if (e == hipSuccess) e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     return e;
 }
 

@@ -186,6 +186,17 @@ def test_batched_prefill_tiny_matches_oracle():
     compare(shape, arena, prompts, 3, 192, "tiny batched prefill", batched=True)
 
 
+@pytest.mark.parametrize("wdt", ["F32", "BF16"])
+def test_long_ffn_rows_ragged(wdt):
+    """hidden_dim above 8192 takes the 8-wave W2 blocks (16 rows each); dim 40
+    leaves the last block half empty."""
+    shape = synth.small_shape(dim=40, n_heads=4, n_kv_heads=2, head_dim=16, hidden_dim=8200,
+                              weight_dtype=getattr(synth, wdt))
+    arena = synth.make_arena(shape, 12, std=0.05, gain_sigma=0.1)
+    prompts = [synth.random_tokens(400 + i, n, shape.vocab_size) for i, n in enumerate([3, 7])]
+    compare(shape, arena, prompts, 3, 16, f"long ffn rows {wdt}")
+
+
 def test_attention_chunk_boundaries_tiny():
     """Lengths around multiples of the 64-position attention chunk, up to T."""
     shape = synth.small_shape(n_kv_heads=2, head_dim=32, dim=128, n_heads=4)
