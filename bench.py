@@ -393,7 +393,7 @@ def main():
         "data": "synthetic (seeded random weights N(0,0.02), uniform prompt ids)",
         "config": {"workload": w.name, "description": w.description, "batch": B, "ctx": w.ctx, "weights": args.weights, "cache": args.cache,
                    "decode_positions": [int(base.min()), int(base.max() + cycle - 1)],
-                   "dispatch": args.dispatch, "single_launch_step": bool(single)},
+                   "dispatch": "direct" if single else args.dispatch, "single_launch_step": bool(single)},
         "step_bytes": bytes_step,
         "achieved_GBps": gbps,
         "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,

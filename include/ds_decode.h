@@ -274,8 +274,10 @@ ds_status ds_logits(const ds_kv* kv, float* d_out, void* stream);
 
 /* Dispatch of ds_decode_step: 0 = one kernel launch per operation (eager),
  * 1 = the same launches captured once into a HIP graph per (stream, token
- * buffers) and replayed.  The default comes from the environment variable
- * DS_DISPATCH ("eager" or "graph"), else graph. */
+ * buffers) and replayed.  A step that is a single launch (batch 1 within
+ * ds_kv_cache_single_launch_ctx) is launched directly in both modes.  The
+ * default comes from the environment variable DS_DISPATCH ("eager" or
+ * "graph"), else graph. */
 ds_status ds_set_dispatch(ds_kv* kv, int32_t mode);
 
 /* Diagnostics: enqueues `reps` back-to-back launches of one kernel of the
