@@ -1,0 +1,56 @@
+"""Host logic of bench.py (no GPU): the one-GPU rule, the algorithmic byte
+counts behind the roofline entry, and when a committed counter summary is
+taken as the step's measured traffic."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_step_bytes_135m_from_the_parameter_count():
+    # The 135M shape holds 134,515,008 parameters: 134,479,872 in matrices
+    # (the tied 49152 x 576 embedding once, 30 layers of q, k, v, o, w1, w3,
+    # w2) and 35,136 norm gains.  One step at a 5-token context reads every
+    # matrix once as bf16, the gains as fp32, one embedding row, the K/V rows
+    # of positions 0..5 (30 layers x 2 x 3 groups x 64 fp32) and writes one
+    # K/V row per layer and the 49152 fp32 logits.
+    m = synth.M135
+    mats, gains = 134_479_872, 35_136
+    kv_row = 30 * 2 * 3 * 64 * 4
+    want = 2 * mats + 4 * gains + 2 * 576 + 6 * kv_row + kv_row + 4 * 49152
+    assert bench.step_bytes(m, np.array([5], np.int32)) == want == 269_620_608
+
+
+def test_kernel_bytes_8b():
+    m = synth.M8B
+    # W1 and W3: 2 x 14336 x 4096 bf16, plus the fp32 input row read twice
+    # (norm and product) and the 14336-float h written
+    assert bench.kernel_bytes(m, "w13", 1, 0) == 2 * 14336 * 4096 * 2 + 4096 * 4 * 2 + 14336 * 4
+    # attention at 4096 cached positions: 8 groups x 128 dims x (K and V) fp32, and the queries
+    assert bench.kernel_bytes(m, "attn", 1, 4096) == 2 * 8 * 128 * 4096 * 4 + 32 * 128 * 4
+
+
+def test_traffic_summary_follows_the_source_hash(monkeypatch):
+    path = os.path.join(ROOT, "profiles", "k_persist_llama135m_p5_traffic.md")
+    fields = dict(line.split(":", 1) for line in open(path) if line.startswith(("traffic_bytes", "kernel_sources")))
+    h = fields["kernel_sources_sha256_16"].strip()
+    monkeypatch.setattr(bench, "kernel_sources_hash", lambda: h)
+    v, note = bench.measured_traffic("llama135m_p5")
+    assert v == float(fields["traffic_bytes_per_launch"]) and "FETCH_SIZE" in note
+    monkeypatch.setattr(bench, "kernel_sources_hash", lambda: "0" * 16)
+    assert bench.measured_traffic("llama135m_p5") == (None, "kernel changed since the counters were taken")
+    assert bench.measured_traffic("no_such_workload")[0] is None
