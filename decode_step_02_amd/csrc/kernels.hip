@@ -967,10 +967,12 @@ static hipError_t launch_attn(const StepArgs& s, int layer, int n_items, hipStre
 
 // Merge the chunk partials of one (item, head): M = max m_s,
 // o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
-// Thread (g, e), g < G = 256 / D, holds dim e of chunks g, g + G, ... (NC of
-// them per batch, loaded before the statistics are known, so the partials
-// arrive in one memory round trip); the block then reduces M and the
-// denominator, weights its chunks and sums the G groups through LDS.
+// Block z of gridDim.z takes dims [z Dh, (z + 1) Dh), Dh = D / gridDim.z
+// (the launch splits a head over 4 blocks when there are few heads to go
+// round).  Thread (g, e), g < G = 256 / Dh, holds dim e of chunks g, g + G,
+// ... (NC of them per batch, loaded before the statistics are known, so the
+// partials arrive in one memory round trip); the block then reduces M and
+// the denominator, weights its chunks and sums the G groups through LDS.
 template <int NC>
 __global__ __launch_bounds__(256) void k_attn_combine(StepArgs s) {
     extern __shared__ float wts[];  // [n_chunks] e^(m_s - M)
@@ -981,7 +983,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(StepArgs s) {
     const int n = s.pos[item] + 1;
     const int ns = (n + kChunk - 1) / kChunk;
     const int S = s.n_chunks, D = s.D;
-    const int G = 256 / D, g = t / D, e = t % D;
+    const int Dh = D / static_cast<int>(gridDim.z), e0 = static_cast<int>(blockIdx.z) * Dh;  // this block's dims
+    const int G = 256 / Dh, g = t / Dh, e = t % Dh;
     const bool eok = g < G;
     const size_t base = (static_cast<size_t>(item) * s.H + h) * S;
     const float2* ml = reinterpret_cast<const float2*>(s.part_ml) + base;
@@ -992,7 +995,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(StepArgs s) {
 #pragma unroll
         for (int i = 0; i < NC; i++) {
             const int c = min(c0 + g + i * G, ns - 1);
-            ov[i] = eok ? s.part_o[(base + c) * D + e] : 0.f;
+            ov[i] = eok ? s.part_o[(base + c) * D + e0 + e] : 0.f;
         }
         if (c0 == 0) {
             M = mine.x;
@@ -1022,16 +1025,18 @@ __global__ __launch_bounds__(256) void k_attn_combine(StepArgs s) {
     }
     osum[t] = acc;
     __syncthreads();
-    if (t < D) {
+    if (t < Dh) {
         float o = 0.f;
-        for (int gg = 0; gg < G; gg++) o += osum[gg * D + t];
-        s.o[(static_cast<size_t>(item) * s.H + h) * D + t] = o / L;
+        for (int gg = 0; gg < G; gg++) o += osum[gg * Dh + t];
+        s.o[(static_cast<size_t>(item) * s.H + h) * D + e0 + t] = o / L;
     }
 }
 
 static hipError_t launch_combine(const StepArgs& s, int n_items, hipStream_t st) {
-    const int per = (s.n_chunks + 256 / s.D - 1) / (256 / s.D);  // chunks per thread, all in one batch if it fits
-    const dim3 grid(s.H, n_items);
+    const int split = s.H * n_items < 128 && s.D >= 128 ? 4 : 1;  // few heads: each head's dims over 4 blocks
+    const int Dh = s.D / split;
+    const int per = (s.n_chunks + 256 / Dh - 1) / (256 / Dh);  // chunks per thread, all in one batch if it fits
+    const dim3 grid(s.H, n_items, split);
     const size_t lds = sizeof(float) * s.n_chunks;
     if (per <= 8)
         hipLaunchKernelGGL(k_attn_combine<8>, grid, dim3(256), lds, st, s);
