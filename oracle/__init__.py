@@ -17,18 +17,19 @@ import subprocess
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "oracle.c")
+SRCS = [os.path.join(HERE, "oracle.c"), os.path.join(HERE, "batch.c")]
 LIB = os.path.join(HERE, "liboracle.so")
-STRICT_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+STRICT_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread"]
 
 
 ORC_F32, ORC_BF16, ORC_Q8, ORC_Q4 = 0, 1, 2, 3
 
 
 def build(out: str = LIB, extra_flags: list[str] | None = None) -> str:
-    """Compile oracle.c into a shared object (``extra_flags`` replaces nothing,
-    it is appended: tests use it to build a deliberately contracted copy)."""
-    cmd = ["gcc", *STRICT_FLAGS, *(extra_flags or []), SRC, "-o", out + ".tmp", "-lm"]
+    """Compile oracle.c and batch.c into a shared object (``extra_flags``
+    replaces nothing, it is appended: tests use it to build a deliberately
+    contracted copy)."""
+    cmd = ["gcc", *STRICT_FLAGS, *(extra_flags or []), *SRCS, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True, cwd=HERE)
     os.replace(out + ".tmp", out)
     return out
@@ -82,6 +83,8 @@ def load(path: str = LIB):
         "orc_decode_step": (C.c_int32, [P, _U8, _F, C.c_int32, C.c_int32, _I, _I, _I, _F]),
         "orc_generate": (C.c_int32, [P, _U8, _F, C.c_int32, C.c_int32, C.c_int32, _I, C.c_int32,
                                      C.c_int32, C.c_int32, _I, C.c_void_p, C.POINTER(C.c_int64)]),
+        "orc_forward_items": (C.c_int32, [P, _U8, _F, C.c_int32, C.c_int32, C.c_int32, _I, _I, _I, _I,
+                                          C.c_void_p, _I, C.c_int32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -164,6 +167,19 @@ def sample(logits, temperature, top_k, top_p, u):
     return int(tok), cand[:n.value].copy(), cum[:n.value].copy()
 
 
+def default_threads() -> int:
+    """Host threads for the batched evaluation: the CPUs this process may use,
+    at most OMP_NUM_THREADS when that is set, and at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(n, 16))
+
+
 def tensor_offsets(shape):
     cfg = config_of(shape)
     n = lib().orc_n_tensors(C.byref(cfg))
@@ -207,6 +223,54 @@ class Model:
         if r < 0:
             raise ValueError(f"orc_decode_step failed ({r})")
         return tok_out, logits.reshape(B, V)
+
+    # ---- the batched evaluation (batch.c): the same numbers, computed for
+    # many positions at once --------------------------------------------------
+    def forward_items(self, seq, pos, tok, want, threads=None):
+        """orc_forward for every item (seq[i], pos[i], tok[i]), bit for bit,
+        layer by layer for all items together.  Returns (tok_out [n] with -1
+        where not wanted, logits [n_wanted][V] in item order)."""
+        seq = np.ascontiguousarray(seq, np.int32)
+        pos = np.ascontiguousarray(pos, np.int32)
+        tok = np.ascontiguousarray(tok, np.int32)
+        want = np.ascontiguousarray(want, np.int32)
+        n = len(seq)
+        assert len(pos) == n and len(tok) == n and len(want) == n
+        nw = int(np.count_nonzero(want))
+        logits = np.zeros((max(nw, 1), self.shape.vocab_size), np.float32)
+        tok_out = np.zeros(max(n, 1), np.int32)
+        r = lib().orc_forward_items(C.byref(self.cfg), self.arena, self.cache, self.B, self.T, n, seq, pos,
+                                    tok, want, logits.ctypes.data, tok_out,
+                                    int(threads or default_threads()))
+        if r < 0:
+            raise ValueError(f"orc_forward_items failed ({r})")
+        return tok_out[:n], logits[:nw]
+
+    def prefill_fast(self, b, tokens, start=0, chunk=4096, threads=None):
+        """Positions start.. of sequence b fed with `tokens`, in chunks of
+        `chunk` items; returns (greedy token, logits) of the last position."""
+        tokens = np.asarray(tokens, np.int32)
+        n = len(tokens)
+        tok, lg = None, None
+        for c0 in range(0, n, chunk):
+            c1 = min(n, c0 + chunk)
+            k = c1 - c0
+            want = np.zeros(k, np.int32)
+            if c1 == n:
+                want[-1] = 1
+            t, l = self.forward_items(np.full(k, b, np.int32), np.arange(start + c0, start + c1, dtype=np.int32),
+                                      tokens[c0:c1], want, threads)
+            if c1 == n:
+                tok, lg = int(t[-1]), l[0]
+        return tok, lg
+
+    def decode_fast(self, lengths: np.ndarray, tok_in: np.ndarray, threads=None):
+        """decode_step for every sequence at once: same results, bit for bit."""
+        B = self.B
+        tok_out, logits = self.forward_items(np.arange(B, dtype=np.int32), lengths, tok_in,
+                                             np.ones(B, np.int32), threads)
+        lengths += 1
+        return tok_out, logits
 
     def generate(self, b, prompt, n_new, uncached=False, want_logits=True):
         V = self.shape.vocab_size

@@ -95,6 +95,19 @@ int32_t orc_generate(const orc_config* c, const uint8_t* arena, float* cache, in
                      int32_t n_new, int32_t mode, int32_t* out_tokens, float* out_logits,
                      int64_t* passes);
 
+/* The same computation as orc_forward for n items (sequence seq[i],
+ * position pos[i], token tok[i]), bit for bit, evaluated layer by layer for
+ * all items together and spread over nthreads host threads (batch.c).  No
+ * (sequence, position) may appear twice; every item's earlier positions must
+ * already be in the cache (or among the items).  For the items with want[i]
+ * != 0, in item order, the logits go to consecutive rows of logits [.][V]
+ * and tok_out[i] gets the greedy token; tok_out[i] = -1 for the others.
+ * Returns 0, or a negative value on a bad argument (nothing is written). */
+int32_t orc_forward_items(const orc_config* c, const uint8_t* arena, float* cache, int32_t B,
+                          int32_t T, int32_t n, const int32_t* seq, const int32_t* pos,
+                          const int32_t* tok, const int32_t* want, float* logits, int32_t* tok_out,
+                          int32_t nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -126,8 +126,9 @@ def test_written_rows_never_change():
 
 
 def test_batch_rows_are_independent():
-    """Row b of a batched decode equals a batch-1 run of sequence b."""
-    shape = synth.small_shape(n_kv_heads=1)
+    """Row b of a batched decode equals a batch-1 run of sequence b: the
+    tokens and logits, and every cached row of slot b, bit for bit."""
+    shape = synth.small_shape(n_kv_heads=2)
     arena = synth.make_arena(shape, 4, std=0.15)
     B, T = 3, 40
     prompts = [synth.random_tokens(s, n, shape.vocab_size) for s, n in ((1, 4), (2, 9), (3, 1))]
@@ -149,6 +150,30 @@ def test_batch_rows_are_independent():
             assert t1 == tok_b[b] and np.array_equal(lg1, lg_b[b])
         tok = tok_b
     assert longest == 9
+    # the B axis of the (L, 2, B, Hkv, T, D) cache: slot b of the batched
+    # cache holds what slot 0 of sequence b's own cache holds, and nothing
+    # else was written
+    cb = mb.cache_view()
+    for b in range(B):
+        cs = singles[b].cache_view()[:, :, 0]
+        assert np.array_equal(cb[:, :, b].view(np.uint32), cs.view(np.uint32))
+        n = int(lengths[b])
+        assert np.any(cs[:, :, :, :n] != 0) and np.all(cs[:, :, :, n:] == 0)
+
+
+def test_cache_index_is_row_major_over_l_2_b_h_t_d(orc):
+    """[NANO] "Cache Architecture": one (L, 2, B, H, T, D) tensor; element 0
+    of row (l, kv, b, g, t) sits where numpy's row-major order puts it."""
+    import ctypes as C
+    shape = synth.small_shape(n_kv_heads=2)
+    cfg = oracle.config_of(shape)
+    rng = np.random.default_rng(3)
+    L, B, H, T, D = shape.n_layers, 5, shape.n_kv_heads, 37, shape.head_dim
+    dims = (L, 2, B, H, T, D)
+    for _ in range(200):
+        l, kv, b, g, t = (int(rng.integers(0, n)) for n in dims[:5])
+        got = orc.orc_cache_index(C.byref(cfg), B, T, l, kv, b, g, t)
+        assert got == np.ravel_multi_index((l, kv, b, g, t, 0), dims)
 
 
 def test_gqa_equals_mha_with_repeated_kv_rows():
