@@ -1,29 +1,31 @@
-"""Writes the expected values of the large-workload GPU parity tests.
+"""Writes the expected values of the full-size GPU parity tests.
 
 Every number stored here comes from the reference decoder (``oracle/``) run
 on the seeded inputs of ``synth``; nothing comes from the HIP library.  The
-full-size workloads are too slow for the single-threaded reference inside a
-GPU test, so the script stores sampled outputs:
+batched evaluation (``Model.prefill_fast`` / ``Model.decode_fast``, bit-
+identical to the per-position decoder, pinned in tests/test_oracle_batch.py)
+makes the full workloads affordable on the host:
 
-* llama135m_p1000 -- the whole run: 1000-token prompt then 23 greedy steps;
-  per step the top-8 logits, 64 fixed sampled logits, max |logit| and the
-  top-2 gap, plus sampled cache rows.
-* llama135m_b64 -- a few sampled sequences of the 64, each run alone (rows of
-  a batched decode are independent), prompt then 16 greedy steps.
-* llama8b_p4096 -- (a) the full-size model on the first 5 prompt tokens with
-  4 greedy steps; (b) the layer-0 key/value rows of sampled positions of the
-  4096-token prompt, which depend only on that position's token.
+* llama135m_b64.npz -- all 64 sequences of the ragged batch: their prompts
+  (lengths uniform in [1, 1008]), then 16 greedy decode steps of the whole
+  batch.  Per sequence and new token: the greedy token, the top-2 gap, the
+  top-8 logits, 64 fixed sampled logits and max |logit|; sampled cache rows
+  of every sequence.
+* llama8b_p4096.npz -- the 8B-shaped model, 4096-token prompt, then 32
+  greedy decode steps at positions 4096..4127 (T = 4160).  Per new token the
+  same summary with 256 sampled logits; cache rows at layers 0, 15 and 31.
 
-Usage: python tests/golden/make_golden.py [workload ...]   (about 10 min)
+The 1000-token 135M workload is checked against the reference decoder live
+in its GPU test (a couple of seconds on the host), with full logits.
+
+Usage: python tests/golden/make_golden.py [workload ...]
 """
 from __future__ import annotations
 
 import hashlib
-import json
 import os
 import sys
 import time
-from concurrent.futures import ProcessPoolExecutor
 
 import numpy as np
 
@@ -34,7 +36,6 @@ sys.path.insert(0, ROOT)
 import oracle  # noqa: E402
 import synth  # noqa: E402
 
-N_SAMPLE = 64
 N_TOP = 8
 
 
@@ -46,120 +47,126 @@ def fingerprint(shape, arena) -> str:
     return h.hexdigest()
 
 
-def sample_indices(V: int, seed: int) -> list[int]:
-    return sorted(np.random.default_rng(seed).choice(V, N_SAMPLE, replace=False).tolist())
+def sample_indices(V: int, n: int, seed: int) -> np.ndarray:
+    return np.sort(np.random.default_rng(seed).choice(V, n, replace=False)).astype(np.int32)
 
 
-def summarize(logits: np.ndarray, idx: list[int]) -> dict:
-    top = np.argsort(-logits.astype(np.float64), kind="stable")[:N_TOP]
-    s = np.sort(logits.astype(np.float64))
-    return {
-        "token": int(oracle.argmax(logits)),
-        "top_idx": [int(i) for i in top],
-        "top_val": [float(logits[i]) for i in top],
-        "sample_val": [float(logits[i]) for i in idx],
-        "max_abs": float(np.abs(logits).max()),
-        "gap": float(s[-1] - s[-2]),
-    }
+class Summary:
+    """Per new token: greedy token, top-2 gap, top-8 (index, value), the
+    logits at fixed sampled indices, and max |logit|."""
+
+    def __init__(self, idx: np.ndarray):
+        self.idx = idx
+        self.rows = {k: [] for k in ("token", "gap", "top_idx", "top_val", "sample_val", "max_abs")}
+
+    def add(self, logits: np.ndarray):
+        lg = logits.astype(np.float64)
+        top = np.argsort(-lg, kind="stable")[:N_TOP]
+        s = np.sort(lg)
+        self.rows["token"].append(int(oracle.argmax(logits)))
+        self.rows["gap"].append(float(s[-1] - s[-2]))
+        self.rows["top_idx"].append(top.astype(np.int32))
+        self.rows["top_val"].append(logits[top].astype(np.float32))
+        self.rows["sample_val"].append(logits[self.idx].astype(np.float32))
+        self.rows["max_abs"].append(float(np.abs(lg).max()))
+
+    def arrays(self, prefix=""):
+        return {prefix + k: np.array(v) for k, v in self.rows.items()}
 
 
-def run_sequence(shape, arena, prompt, n_new, T, cache_probe=None):
-    """Reference greedy run of one sequence: logits summary per new token and
-    optional cache rows [(layer, kv, group, pos)] read at the end."""
-    m = oracle.Model(shape, arena, 1, T)
-    idx = sample_indices(shape.vocab_size, 7)
-    steps = []
-    tok = None
-    for t, tk in enumerate(prompt):
-        tok, lg = m.forward(0, t, int(tk))
-    steps.append(summarize(lg, idx))
-    pos = len(prompt)
-    for _ in range(n_new - 1):
-        tok, lg = m.forward(0, pos, tok)
-        steps.append(summarize(lg, idx))
-        pos += 1
-    rows = []
-    if cache_probe:
-        cv = m.cache_view()
-        for (l, kv, g, p) in cache_probe:
-            rows.append({"layer": l, "kv": kv, "group": g, "pos": p,
-                         "val": [float(v) for v in cv[l, kv, 0, g, p]]})
-    return {"sample_idx": idx, "steps": steps, "cache_rows": rows}
-
-
-def golden_p1000():
-    w = synth.WORKLOADS["llama135m_p1000"]
-    arena = synth.make_arena(w.model, w.model_seed)
-    prompt = synth.prompts(w)[0]
-    probe = [(l, kv, g, p) for l in (0, 14, 29) for kv in (0, 1) for g in (0, 2) for p in (0, 511, 999, 1022)]
-    t0 = time.time()
-    out = run_sequence(w.model, arena, prompt, w.decode_calls + 1, w.ctx, probe)
-    out.update(workload=w.name, fingerprint=fingerprint(w.model, arena), seconds=time.time() - t0)
-    return out
-
-
-def _b64_one(b):
-    w = synth.WORKLOADS["llama135m_b64"]
-    arena = synth.make_arena(w.model, w.model_seed, threads=1)
-    prompt = synth.prompts(w)[b]
-    n = len(prompt)
-    probe = [(l, kv, 1, p) for l in (0, 29) for kv in (0, 1) for p in sorted({0, n - 1, n + 15})]
-    r = run_sequence(w.model, arena, prompt, w.decode_calls + 1, w.ctx, probe)
-    r["seq"] = int(b)
-    r["prompt_len"] = int(n)
-    return r
+def cache_rows(m: oracle.Model, probe):
+    """probe: (seq, layer, kv, group, pos) tuples -> (meta int32 [R][5], values f32 [R][D])."""
+    cv = m.cache_view()
+    meta = np.array(probe, np.int32)
+    vals = np.stack([cv[l, kv, b, g, p] for (b, l, kv, g, p) in probe]).astype(np.float32)
+    return meta, vals
 
 
 def golden_b64():
     w = synth.WORKLOADS["llama135m_b64"]
-    lens = synth.prompt_lengths(w)
-    order = np.argsort(lens, kind="stable")
-    picks = sorted({int(order[0]), int(order[1]), int(order[len(order) // 2]), int(order[-1])})
-    arena = synth.make_arena(w.model, w.model_seed)
+    m_shape = w.model
+    arena = synth.make_arena(m_shape, w.model_seed)
+    prompts = synth.prompts(w)
+    lens = np.array([len(p) for p in prompts], np.int32)
+    B = len(prompts)
+    m = oracle.Model(m_shape, arena, B, w.ctx)
     t0 = time.time()
-    with ProcessPoolExecutor(len(picks)) as ex:
-        seqs = list(ex.map(_b64_one, picks))
-    return {"workload": w.name, "fingerprint": fingerprint(w.model, arena), "lengths": lens.tolist(),
-            "sequences": seqs, "seconds": time.time() - t0}
+    # every prompt position of every sequence as the items of one pass
+    seq = np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(lens)])
+    pos = np.concatenate([np.arange(n, dtype=np.int32) for n in lens])
+    tok = np.concatenate([np.asarray(p, np.int32) for p in prompts])
+    want = np.concatenate([(np.arange(n) == n - 1).astype(np.int32) for n in lens])
+    tok_out, logits = m.forward_items(seq, pos, tok, want)
+    print(f"b64: prefill of {len(seq)} positions in {time.time() - t0:.0f} s", flush=True)
+    idx = sample_indices(m_shape.vocab_size, 64, 7)
+    sums = [Summary(idx) for _ in range(B)]
+    for b in range(B):
+        sums[b].add(logits[b])
+    cur = tok_out[want == 1].copy()
+    lengths = lens.copy()
+    for k in range(w.decode_calls):
+        cur, lg = m.decode_fast(lengths, cur)
+        for b in range(B):
+            sums[b].add(lg[b])
+    print(f"b64: {w.decode_calls} decode steps done at {time.time() - t0:.0f} s", flush=True)
+    probe = []
+    for b in range(B):
+        n = int(lens[b])
+        for l in (0, 29):
+            for kv in (0, 1):
+                for p in sorted({0, n - 1, n + w.decode_calls - 1}):
+                    probe.append((b, l, kv, b % m_shape.n_kv_heads, p))
+    meta, vals = cache_rows(m, probe)
+    out = {"sample_idx": idx, "lengths": lens, "rows_meta": meta, "rows_val": vals}
+    per = [s.arrays() for s in sums]
+    for k in per[0]:
+        out[k] = np.stack([p[k] for p in per])  # [B][steps][...]
+    out["fingerprint"] = np.array(fingerprint(m_shape, arena))
+    out["seconds"] = np.array(time.time() - t0)
+    return out
 
 
 def golden_8b():
     w = synth.WORKLOADS["llama8b_p4096"]
-    m = w.model
+    ms = w.model
     t0 = time.time()
-    arena = synth.make_arena(m, w.model_seed)
+    arena = synth.make_arena(ms, w.model_seed)
+    fp = fingerprint(ms, arena)
+    print(f"8b: arena in {time.time() - t0:.0f} s", flush=True)
     prompt = synth.prompts(w)[0]
-    short = run_sequence(m, arena, prompt[:5], 5, 16)
-    # layer-0 key/value rows of sampled prompt positions: embedding row ->
-    # attn_norm -> Wk / Wv -> RoPE on k (each needs only that position's token)
-    v = synth.views(m, arena)
-    rows = []
-    for p in (0, 1, 1000, 2047, 4095):
-        tok = int(prompt[p])
-        emb = np.zeros(m.dim, np.float32)
-        oracle.lib().orc_widen_bf16_array(np.ascontiguousarray(v["token_emb"][tok]), emb, m.dim)
-        xn = oracle.rmsnorm(emb, v["l0.attn_norm"], m.norm_eps)
-        k = oracle.matvec(v["l0.wk"], xn)
-        vv = oracle.matvec(v["l0.wv"], xn)
-        for g in (0, m.n_kv_heads - 1):
-            kg = oracle.rope_apply(k[g * m.head_dim:(g + 1) * m.head_dim], p, m.rope_theta)
-            rows.append({"layer": 0, "kv": 0, "group": g, "pos": p, "val": [float(x) for x in kg]})
-            rows.append({"layer": 0, "kv": 1, "group": g, "pos": p,
-                         "val": [float(x) for x in vv[g * m.head_dim:(g + 1) * m.head_dim]]})
-    return {"workload": w.name, "fingerprint": fingerprint(m, arena), "short_prompt": prompt[:5].tolist(),
-            "short": short, "prefill_rows": rows, "seconds": time.time() - t0}
+    m = oracle.Model(ms, arena, 1, w.ctx)
+    t1 = time.time()
+    tok, lg = m.prefill_fast(0, prompt, chunk=len(prompt))
+    print(f"8b: prefill of {len(prompt)} positions in {time.time() - t1:.0f} s", flush=True)
+    idx = sample_indices(ms.vocab_size, 256, 8)
+    s = Summary(idx)
+    s.add(lg)
+    lengths = np.array([len(prompt)], np.int32)
+    cur = np.array([tok], np.int32)
+    for k in range(w.decode_calls):
+        cur, lgs = m.decode_fast(lengths, cur)
+        s.add(lgs[0])
+    print(f"8b: {w.decode_calls} decode steps done at {time.time() - t1:.0f} s", flush=True)
+    n = len(prompt)
+    probe = [(0, l, kv, g, p) for l in (0, 15, 31) for kv in (0, 1) for g in (0, 3, 7)
+             for p in (0, 1, 2047, n - 1, n, n + 15, n + w.decode_calls - 1)]
+    meta, vals = cache_rows(m, probe)
+    out = {"sample_idx": idx, "rows_meta": meta, "rows_val": vals, "prompt_len": np.array(n)}
+    out.update(s.arrays())
+    out["fingerprint"] = np.array(fp)
+    out["seconds"] = np.array(time.time() - t0)
+    return out
 
 
-JOBS = {"llama135m_p1000": golden_p1000, "llama135m_b64": golden_b64, "llama8b_p4096": golden_8b}
+JOBS = {"llama135m_b64": golden_b64, "llama8b_p4096": golden_8b}
 
 
 def main(names):
     for name in names or list(JOBS):
         t0 = time.time()
         data = JOBS[name]()
-        path = os.path.join(HERE, f"{name}.json")
-        with open(path, "w") as f:
-            json.dump(data, f, separators=(",", ":"))
+        path = os.path.join(HERE, f"{name}.npz")
+        np.savez_compressed(path, **data)
         print(f"{name}: {os.path.getsize(path)} bytes in {time.time() - t0:.0f} s", flush=True)
 
 

@@ -52,10 +52,12 @@ def check_tokens(gpu_tok, ref_tok, ref_logits, gpu_logits, what=""):
     return ties
 
 
-def oracle_run(shape, arena, prompts, decode_calls, T, feed=None):
+def oracle_run(shape, arena, prompts, decode_calls, T, feed=None, fast=False):
     """Reference decoder: ragged prompts, then `decode_calls` batched greedy
     steps.  Returns (first tokens, first logits, [tokens per step], [logits per
-    step], oracle model).  feed[k] overrides the tokens fed at step k."""
+    step], oracle model).  feed[k] overrides the tokens fed at step k.  With
+    `fast`, the batched evaluation (bit-identical, pinned in
+    test_oracle_batch.py) does the work: for long prompts."""
     import oracle
     B = len(prompts)
     m = oracle.Model(shape, arena, B, T)
@@ -63,15 +65,18 @@ def oracle_run(shape, arena, prompts, decode_calls, T, feed=None):
     first_tok = np.zeros(B, np.int32)
     first_lg = np.zeros((B, V), np.float32)
     for b, p in enumerate(prompts):
-        for t, tk in enumerate(p):
-            tok, lg = m.forward(b, t, int(tk))
+        if fast:
+            tok, lg = m.prefill_fast(b, p)
+        else:
+            for t, tk in enumerate(p):
+                tok, lg = m.forward(b, t, int(tk))
         first_tok[b], first_lg[b] = tok, lg
     lengths = np.array([len(p) for p in prompts], np.int32)
     toks, lgs = [], []
     cur = first_tok.copy()
     for k in range(decode_calls):
         fed = cur if feed is None else np.asarray(feed[k], np.int32)
-        cur, lg = m.decode_step(lengths, fed)
+        cur, lg = (m.decode_fast if fast else m.decode_step)(lengths, fed)
         toks.append(cur.copy())
         lgs.append(lg.copy())
     return first_tok, first_lg, toks, lgs, m

@@ -1,13 +1,20 @@
 """Parity of the HIP path at the full workload sizes (needs a gfx950 GPU).
 
-Expected values come from tests/golden/*.json, written by
-tests/golden/make_golden.py from the reference decoder only.  The GPU is fed
-the reference's greedy tokens (teacher forcing) and must give, at the sampled
-vocabulary indices, logits within max |d| <= 5e-4 and |d| / max|ref| <= 1e-4,
-the same greedy token (or a near-tie), and the sampled cache rows within the
-same tolerance.
+* 135M, 1000-token prompt, 23 decode steps: checked against the reference
+  decoder run live on the host (its batched evaluation, bit-identical to the
+  per-position one): every logit of every step and every cached value.
+* 135M, 64 ragged sequences, 16 decode steps, and 8B, 4096-token prompt, 32
+  decode steps: checked against tests/golden/*.npz, written by
+  tests/golden/make_golden.py from the reference decoder only: per sequence
+  and step the greedy token, the top-8 logits, fixed sampled logits, and
+  sampled cache rows.
+
+The GPU is fed the reference's greedy tokens (teacher forcing).  Logits must
+satisfy max |d| <= 5e-4 and max |d| / max |ref| <= 1e-4; a different greedy
+token is accepted only as a near-tie (the reference's top-2 gap within twice
+the step's error).  Cache values use the same bound with max(max |ref|, 1) as
+the scale; positions never written keep the NaN sentinel.
 """
-import json
 import os
 import sys
 
@@ -16,6 +23,7 @@ import pytest
 
 import synth
 from conftest import GOLDEN
+from parity import check_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -28,11 +36,11 @@ def _say(*a):
 
 
 def _golden(name):
-    path = os.path.join(GOLDEN, f"{name}.json")
+    path = os.path.join(GOLDEN, f"{name}.npz")
     if not os.path.exists(path):
         pytest.skip(f"{path} missing: run tests/golden/make_golden.py {name}")
-    with open(path) as f:
-        return json.load(f)
+    with np.load(path, allow_pickle=False) as z:
+        return {k: z[k] for k in z.files}
 
 
 def _fingerprint(shape, arena):
@@ -41,82 +49,126 @@ def _fingerprint(shape, arena):
     return fingerprint(shape, arena)
 
 
-def check_step(gpu_logits_row, gpu_tok, ref, idx, what):
-    """Compare one step's GPU logits (full row) with a stored summary."""
-    assert np.all(np.isfinite(gpu_logits_row)), f"{what}: non-finite logits"
-    ii = np.array(list(ref["top_idx"]) + list(idx))
-    rv = np.array(list(ref["top_val"]) + list(ref["sample_val"]), np.float64)
-    d = np.abs(gpu_logits_row[ii].astype(np.float64) - rv)
-    err = float(d.max())
-    assert err <= ABS_TOL and err <= REL_TOL * ref["max_abs"], f"{what}: max|d| {err:.3e} (max|ref| {ref['max_abs']:.3f})"
-    if int(gpu_tok) != ref["token"]:
-        # near-tie: the reference's top-2 gap within twice the error, and the
-        # GPU's pick among the reference's top logits
-        assert ref["gap"] <= 2 * err + 1e-6, f"{what}: token {gpu_tok} != {ref['token']} (gap {ref['gap']:.3e})"
-        assert int(gpu_tok) in ref["top_idx"], f"{what}: token {gpu_tok} not among the reference top-8"
+def check_summary(gpu_row, gpu_tok, g, b, k, what):
+    """One step's GPU logits (full row) against the stored summary of
+    sequence b (None: no sequence axis), new token k."""
+    sel = (lambda a: a[b, k]) if b is not None else (lambda a: a[k])
+    assert np.all(np.isfinite(gpu_row)), f"{what}: non-finite logits"
+    ii = np.concatenate([sel(g["top_idx"]), g["sample_idx"]])
+    rv = np.concatenate([sel(g["top_val"]), sel(g["sample_val"])]).astype(np.float64)
+    err = float(np.abs(gpu_row[ii].astype(np.float64) - rv).max())
+    scale = float(sel(g["max_abs"]))
+    assert err <= ABS_TOL and err <= REL_TOL * scale, f"{what}: max|d| {err:.3e} (max|ref| {scale:.3f})"
+    ref_tok = int(sel(g["token"]))
+    if int(gpu_tok) != ref_tok:
+        gap = float(sel(g["gap"]))
+        assert gap <= 2 * err + 1e-6, f"{what}: token {gpu_tok} != {ref_tok} (gap {gap:.3e})"
+        assert int(gpu_tok) in sel(g["top_idx"]).tolist(), f"{what}: token {gpu_tok} not in the reference top-8"
         return err, 1
     return err, 0
 
 
-def check_rows(cache_view, b, rows, what):
+def check_rows(cache_view, g, what, seq_axis=True):
+    """Stored rows (seq, layer, kv, group, pos) against the GPU cache."""
     worst = 0.0
-    for r in rows:
-        got = cache_view[r["layer"], r["kv"], b, r["group"], r["pos"]].astype(np.float64)
-        ref = np.array(r["val"], np.float64)
+    for (b, l, kv, grp, p), ref in zip(g["rows_meta"], g["rows_val"]):
+        got = cache_view[l, kv, b if seq_axis else 0, grp, p].astype(np.float64)
+        ref = ref.astype(np.float64)
         d = float(np.abs(got - ref).max())
-        assert d <= ABS_TOL and d <= REL_TOL * max(float(np.abs(ref).max()), 1.0), f"{what}: cache row {r}: {d:.3e}"
+        assert d <= ABS_TOL and d <= REL_TOL * max(float(np.abs(ref).max()), 1.0), \
+            f"{what}: cache row seq {b} layer {l} kv {kv} group {grp} pos {p}: {d:.3e}"
         worst = max(worst, d)
     return worst
+
+
+def check_cache(got, ref, what):
+    """Every written value of a cache region, S20 bound per (layer, k/v)."""
+    worst = 0.0
+    for l in range(ref.shape[0]):
+        for kv in range(2):
+            r = ref[l, kv].astype(np.float64)
+            d = float(np.abs(got[l, kv].astype(np.float64) - r).max())
+            assert d <= ABS_TOL and d <= REL_TOL * max(float(np.abs(r).max()), 1.0), \
+                f"{what}: layer {l} kv {kv}: max|d| {d:.3e}"
+            worst = max(worst, d)
+    return worst
+
+
+_P1000 = {}
+
+
+def _p1000_reference():
+    """The reference decoder on the 1000-token workload: the prompt, then 23
+    greedy steps, each fed the reference's own previous token."""
+    if not _P1000:
+        import time
+        import oracle
+        w = synth.WORKLOADS["llama135m_p1000"]
+        arena = synth.make_arena(w.model, w.model_seed)
+        prompt = synth.prompts(w)[0]
+        t0 = time.perf_counter()
+        m = oracle.Model(w.model, arena, 1, w.ctx)
+        tok, lg = m.prefill_fast(0, prompt)
+        toks, lgs = [tok], [lg.copy()]
+        lengths = np.array([len(prompt)], np.int32)
+        for _ in range(w.decode_calls):
+            t, l = m.decode_fast(lengths, np.array([toks[-1]], np.int32))
+            toks.append(int(t[0]))
+            lgs.append(l[0].copy())
+        _say(f"reference decoder: 1000 positions + {w.decode_calls} steps in {time.perf_counter() - t0:.1f} s "
+             f"on {oracle.default_threads()} host threads")
+        _P1000.update(arena=arena, prompt=prompt, toks=toks, lgs=lgs, cache=m.cache_view()[:, :, 0].copy())
+    return _P1000
 
 
 @pytest.mark.parametrize("batched", [False, True], ids=["per_position", "batched"])
 def test_135m_1000_token_context(batched):
     """The 1000-token prompt through ds_prefill (one position per pass) or
-    ds_prefill_batched (positions as the items of a pass)."""
-    import time
+    ds_prefill_batched (positions as the items of a pass), then 23 decode
+    steps (single launch, role-1 attention partials): every logit and every
+    cached value against the reference."""
     import torch
     import decode_step_02_amd as dsa
-    g = _golden("llama135m_p1000")
+    ref = _p1000_reference()
     w = synth.WORKLOADS["llama135m_p1000"]
-    arena = synth.make_arena(w.model, w.model_seed)
-    assert _fingerprint(w.model, arena) == g["fingerprint"]
-    prompt = synth.prompts(w)[0]
-    model = dsa.Model(w.model, arena)
+    model = dsa.Model(w.model, ref["arena"])
     kv = dsa.KVCache(model, 1, w.ctx)
     kv.cache.fill_(float("nan"))
     tok = torch.zeros(1, dtype=torch.int32, device="cuda")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    (kv.prefill_batched if batched else kv.prefill)(0, [int(t) for t in prompt], tok)
-    torch.cuda.synchronize()
-    _say(f"prefilled 1000 positions ({'batched' if batched else 'per position'}) in "
-         f"{(time.perf_counter() - t0) * 1e3:.1f} ms")
-    steps, idx = g["steps"], g["sample_idx"]
-    worst, ties = check_step(kv.logits().cpu().numpy()[0], tok.item(), steps[0], idx, "prefill")
-    for k in range(1, len(steps)):
-        tok.fill_(steps[k - 1]["token"])
-        kv.decode_step(tok, tok)
-        e, t = check_step(kv.logits().cpu().numpy()[0], tok.item(), steps[k], idx, f"step {k}")
-        worst, ties = max(worst, e), ties + t
+    (kv.prefill_batched if batched else kv.prefill)(0, [int(t) for t in ref["prompt"]], tok)
+    worst, ties = 0.0, 0
+    for k in range(len(ref["toks"])):
+        if k > 0:
+            tok.fill_(ref["toks"][k - 1])
+            kv.decode_step(tok, tok)
+        lg = kv.logits().cpu().numpy()
+        r = ref["lgs"][k][None]
+        d = np.abs(lg.astype(np.float64) - r).max()
+        assert np.all(np.isfinite(lg)) and d <= ABS_TOL and d <= REL_TOL * np.abs(r).max(), f"step {k}: {d:.3e}"
+        ties += check_tokens(tok.cpu().numpy(), [ref["toks"][k]], r, lg, f"step {k}")
+        worst = max(worst, float(d))
     kv.check()
-    assert kv.lengths.item() == 1000 + w.decode_calls == 1023
-    cv = kv.cache_view().cpu().numpy()
-    rows = check_rows(cv, 0, g["cache_rows"], "p1000")
-    assert np.all(np.isnan(cv[:, :, 0, :, 1023:]))
-    _say(f"p1000 {'batched' if batched else 'per position'}: max|dlogit| {worst:.2e}, near-ties {ties}, "
-         f"max|dcache| {rows:.2e}")
+    n = 1000 + w.decode_calls
+    assert kv.lengths.item() == n == 1023
+    cv = kv.cache_view().cpu().numpy()[:, :, 0]
+    rows = check_cache(cv[:, :, :, :n], ref["cache"][:, :, :, :n], "p1000 cache")
+    assert np.all(np.isnan(cv[:, :, :, n:]))
+    _say(f"p1000 {'batched' if batched else 'per position'}: max|dlogit| {worst:.2e} over all "
+         f"{len(ref['toks'])} x {w.model.vocab_size} logits, near-ties {ties}, max|dcache| {rows:.2e} over all rows")
 
 
 def test_135m_batch64_ragged():
+    """All 64 sequences of the ragged batch, each teacher-forced with the
+    reference's tokens, every step."""
     import torch
     import decode_step_02_amd as dsa
     g = _golden("llama135m_b64")
     w = synth.WORKLOADS["llama135m_b64"]
     arena = synth.make_arena(w.model, w.model_seed)
-    assert _fingerprint(w.model, arena) == g["fingerprint"]
+    assert _fingerprint(w.model, arena) == str(g["fingerprint"])
     prompts = synth.prompts(w)
     lens = np.array([len(p) for p in prompts])
-    assert lens.tolist() == g["lengths"]
+    assert lens.tolist() == g["lengths"].tolist()
     B = w.batch
     model = dsa.Model(w.model, arena)
     kv = dsa.KVCache(model, B, w.ctx)
@@ -124,41 +176,32 @@ def test_135m_batch64_ragged():
     tok = torch.zeros(B, dtype=torch.int32, device="cuda")
     kv.prefill_batch([[int(t) for t in p] for p in prompts], tok)
     _say(f"prefilled 64 sequences, {int(lens.sum())} positions")
-    seqs = {s["seq"]: s for s in g["sequences"]}
     worst, ties = 0.0, 0
-    lg = kv.logits().cpu().numpy()
-    cur = tok.cpu().numpy()
-    for b, s in seqs.items():
-        e, t = check_step(lg[b], cur[b], s["steps"][0], s["sample_idx"], f"seq {b} prefill")
-        worst, ties = max(worst, e), ties + t
-    for k in range(1, w.decode_calls + 1):
-        feed = cur.copy()
-        for b, s in seqs.items():
-            feed[b] = s["steps"][k - 1]["token"]
-        tok.copy_(torch.from_numpy(feed))
-        kv.decode_step(tok, tok)
+    for k in range(w.decode_calls + 1):
+        if k > 0:
+            tok.copy_(torch.from_numpy(g["token"][:, k - 1].astype(np.int32)))
+            kv.decode_step(tok, tok)
         lg = kv.logits().cpu().numpy()
         cur = tok.cpu().numpy()
-        assert np.all(np.isfinite(lg)) and np.all((cur >= 0) & (cur < w.model.vocab_size))
-        for b, s in seqs.items():
-            e, t = check_step(lg[b], cur[b], s["steps"][k], s["sample_idx"], f"seq {b} step {k}")
+        for b in range(B):
+            e, t = check_summary(lg[b], cur[b], g, b, k, f"seq {b} new token {k}")
             worst, ties = max(worst, e), ties + t
     kv.check()
     assert kv.lengths.cpu().numpy().tolist() == (lens + w.decode_calls).tolist()
-    cv = kv.cache_view()
-    worst_row = 0.0
-    for b, s in seqs.items():
-        worst_row = max(worst_row, check_rows(cv[:, :, b:b + 1].cpu().numpy(), 0, s["cache_rows"], f"seq {b}"))
-    # untouched slots keep the sentinel: the first position past every length
-    L = (lens + w.decode_calls)
+    cv = kv.cache_view().cpu().numpy()
+    worst_row = check_rows(cv, g, "b64")
+    # untouched slots keep the sentinel
+    L = lens + w.decode_calls
     for b in range(B):
-        if L[b] < w.ctx:
-            assert torch.isnan(cv[:, :, b, :, int(L[b])]).all()
-    _say(f"b64: sampled seqs {sorted(seqs)}, max|dlogit| {worst:.2e}, near-ties {ties}, max|dcache| {worst_row:.2e}")
+        assert np.all(np.isnan(cv[:, :, b, :, int(L[b]):]))
+    _say(f"b64: all {B} sequences x {w.decode_calls + 1} new tokens, max|dlogit| {worst:.2e}, near-ties {ties}, "
+         f"max|dcache| {worst_row:.2e} over {len(g['rows_meta'])} rows")
 
 
 @pytest.mark.timeout(900)
 def test_8b_full_size():
+    """The 4096-token prompt (per position, and batched in a second cache),
+    then 32 decode steps at positions 4096..4127 on each cache."""
     import torch
     import decode_step_02_amd as dsa
     g = _golden("llama8b_p4096")
@@ -168,46 +211,32 @@ def test_8b_full_size():
     if free < 24 * 2**30:
         pytest.skip("needs 24 GiB of free device memory")
     arena = synth.make_arena(m, w.model_seed)
-    assert _fingerprint(m, arena) == g["fingerprint"]
+    assert _fingerprint(m, arena) == str(g["fingerprint"])
     model = dsa.Model(m, arena)
     del arena
     _say("8b weights on the device")
-    # (a) the full-size model against the reference on a short prompt
-    kv = dsa.KVCache(model, 1, 16)
-    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
-    kv.prefill(0, g["short_prompt"], tok)
-    steps, idx = g["short"]["steps"], g["short"]["sample_idx"]
-    worst, ties = check_step(kv.logits().cpu().numpy()[0], tok.item(), steps[0], idx, "8b prefill")
-    for k in range(1, len(steps)):
-        tok.fill_(steps[k - 1]["token"])
-        kv.decode_step(tok, tok)
-        e, t = check_step(kv.logits().cpu().numpy()[0], tok.item(), steps[k], idx, f"8b step {k}")
-        worst, ties = max(worst, e), ties + t
-    kv.check()
-    kv.close()
-    # (b) the full 4096-token prefill and 32 decode steps at T = 4160
-    prompt = synth.prompts(w)[0]
-    kv = dsa.KVCache(model, 1, w.ctx)
-    kv.cache.fill_(float("nan"))
-    kv.prefill(0, [int(t) for t in prompt], tok)
-    _say("8b: prefilled 4096 positions")
-    rows = check_rows(kv.cache_view().cpu().numpy(), 0, g["prefill_rows"], "8b prefill rows")
-    # the same prompt through the batched prefill, in a second cache
-    kv2 = dsa.KVCache(model, 1, w.ctx)
-    kv2.cache.fill_(float("nan"))
-    tok2 = torch.zeros(1, dtype=torch.int32, device="cuda")
-    kv2.prefill_batched(0, [int(t) for t in prompt], tok2)
-    rows2 = check_rows(kv2.cache_view().cpu().numpy(), 0, g["prefill_rows"], "8b batched prefill rows")
-    assert kv2.lengths.item() == 4096 and bool(torch.isnan(kv2.cache_view()[:, :, 0, :, 4096:]).all())
-    kv2.check()
-    kv2.close()
-    _say(f"8b: batched prefill max|dcache| {rows2:.2e}")
-    for _ in range(w.decode_calls):
-        kv.decode_step(tok, tok)
-        lg = kv.logits()
-        assert bool(torch.isfinite(lg).all()) and 0 <= tok.item() < m.vocab_size
-    kv.check()
-    n = 4096 + w.decode_calls
-    assert kv.lengths.item() == n
-    assert bool(torch.isnan(kv.cache_view()[:, :, 0, :, n:]).all())
-    _say(f"8b: max|dlogit| {worst:.2e}, near-ties {ties}, max|dcache| {rows:.2e}")
+    prompt = [int(t) for t in synth.prompts(w)[0]]
+    assert len(prompt) == int(g["prompt_len"])
+    for batched in (False, True):
+        what = "8b " + ("batched" if batched else "per position")
+        kv = dsa.KVCache(model, 1, w.ctx)
+        kv.cache.fill_(float("nan"))
+        tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+        (kv.prefill_batched if batched else kv.prefill)(0, prompt, tok)
+        _say(f"{what}: prefilled 4096 positions")
+        worst, ties = 0.0, 0
+        for k in range(w.decode_calls + 1):
+            if k > 0:
+                tok.fill_(int(g["token"][k - 1]))
+                kv.decode_step(tok, tok)
+            e, t = check_summary(kv.logits().cpu().numpy()[0], tok.item(), g, None, k, f"{what} new token {k}")
+            worst, ties = max(worst, e), ties + t
+        kv.check()
+        n = 4096 + w.decode_calls
+        assert kv.lengths.item() == n
+        cv = kv.cache_view()
+        assert bool(torch.isnan(cv[:, :, 0, :, n:]).all())
+        rows = check_rows(cv.cpu().numpy(), g, what, seq_axis=False)
+        kv.close()
+        _say(f"{what}: {w.decode_calls + 1} new tokens, max|dlogit| {worst:.2e}, near-ties {ties}, "
+             f"max|dcache| {rows:.2e} over {len(g['rows_meta'])} rows")
