@@ -79,8 +79,9 @@ ds_status check_config(const ds_config* c) {
     if (c->head_dim % 2 != 0) return fail(DS_ERR_INVALID_ARG, "head_dim must be even");
     if (!(c->norm_eps > 0.f) || !(c->rope_theta > 0.f))
         return fail(DS_ERR_INVALID_ARG, "norm_eps and rope_theta must be positive");
-    if (c->head_dim % 8 != 0 || c->head_dim > ds::kMaxD)
-        return fail(DS_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 and at most %d", ds::kMaxD);
+    if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+        return fail(DS_ERR_UNSUPPORTED, "head_dim %d: the attention kernels are built for 16, 32, 64, 128 and 256",
+                    c->head_dim);
     if (c->n_heads / c->n_kv_heads > ds::kMaxRep)
         return fail(DS_ERR_UNSUPPORTED, "at most %d query heads per key/value head", ds::kMaxRep);
     const size_t ws = wsize(c);
@@ -400,6 +401,11 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     s.attn_g = 1;
     const char* agenv = std::getenv("DS_ATTN_G");  // "0" keeps the shuffle-reduced attention kernel
     if (agenv && std::strcmp(agenv, "0") == 0 && s.cdt != DS_BF16) s.attn_g = 0;  // the only bf16-cache reader
+    // the single-launch step's products: bf16 weights times the input as bf16
+    // hi/lo pairs (default), or DS_PERSIST_IN=f32: weights widened to fp32
+    s.pin = ds::kBF16;
+    const char* pin = std::getenv("DS_PERSIST_IN");
+    if (pin && std::strcmp(pin, "f32") == 0) s.pin = ds::kF32;
     const char* sa = std::getenv("DS_SHORT_ATTN");  // "0" turns the fused short-context path off
     if (sa && std::strcmp(sa, "0") == 0) s.short_n = 0;
     ds::PersistArgs& pa = kv->pa;
@@ -757,15 +763,24 @@ ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t lay
                           void* stream) {
     if (!model || !kv || kv->model != model) return fail(DS_ERR_INVALID_ARG, "model/kv mismatch");
     if (!kv->stepped) return fail(DS_ERR_STATE, "run ds_decode_step before ds_bench_kernel");
-    if (which < 0 || which > 6) return fail(DS_ERR_INVALID_ARG, "which must be in [0, 6]");
+    if (which < 0 || which > 7) return fail(DS_ERR_INVALID_ARG, "which must be in [0, 7]");
     if (layer < 0 || layer >= kv->s.L) return fail(DS_ERR_INVALID_ARG, "layer outside [0, L)");
     if (reps < 1) return fail(DS_ERR_INVALID_ARG, "reps must be positive");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (which == ds::K_FLOOR) {
+        if (kv->B != 1 || kv->mirror[0] + 1 > kv->persist_ctx)
+            return fail(DS_ERR_STATE, "the handoff floor needs a batch-1 cache whose next step is a single launch");
+        for (int r = 0; r < reps; r++) {
+            hipError_t e = ds::enqueue_persist_floor(kv->s, kv->pa, st);
+            if (e != hipSuccess) return hip_fail(e, "bench floor");
+        }
+        return ok();
+    }
     for (int r = 0; r < reps; r++) {
         if (kv->last_nload > 0 && !(kv->s.mm_ok && kv->B >= ds::kMmMin) &&
             (which == ds::K_ATTN || which == ds::K_COMBINE))
             return fail(DS_ERR_STATE, "kernel %d is not part of a short-context step", which);
-        hipError_t e = ds::enqueue_kernel(which, layer, kv->s, model->ptrs, kv->B, kv->last_nload, st);
+        hipError_t e = ds::enqueue_kernel(which, (layer + r) % kv->s.L, kv->s, model->ptrs, kv->B, kv->last_nload, st);
         if (e != hipSuccess) return hip_fail(e, "bench kernel");
     }
     return ok();
@@ -779,9 +794,15 @@ ds_status ds_logits(const ds_kv* kv, float* d_out, void* stream) {
     return ok();
 }
 
-ds_status ds_sample(const ds_kv* kv, const float* d_uniform, float temperature, int32_t top_k, float top_p,
-                    int32_t* d_tok_out, void* stream) {
-    if (!kv || !d_uniform || !d_tok_out) return fail(DS_ERR_INVALID_ARG, "NULL argument");
+}  // extern "C"
+
+namespace {
+
+// Argument checks of ds_sample; on success the
+// effective top-k (at most V) is in *k_out.
+ds_status check_sample_args(int V, const float* d_uniform, float temperature, int32_t top_k, float top_p,
+                            const int32_t* d_tok_out, int* k_out) {
+    if (!d_uniform || !d_tok_out) return fail(DS_ERR_INVALID_ARG, "NULL argument");
     if (!aligned(d_uniform, 4) || !aligned(d_tok_out, 4)) return fail(DS_ERR_ALIGNMENT, "uniform / token buffers");
     if (!(temperature > 0.0f) || !(temperature < INFINITY))
         return fail(DS_ERR_INVALID_ARG, "temperature %g: needs 0 < t < inf (0 is the greedy step itself)",
@@ -789,10 +810,24 @@ ds_status ds_sample(const ds_kv* kv, const float* d_uniform, float temperature, 
     if (top_k < 0) return fail(DS_ERR_INVALID_ARG, "top_k %d < 0", top_k);
     if (!(top_p > 0.0f && top_p <= 1.0f))
         return fail(DS_ERR_INVALID_ARG, "top_p %g outside (0, 1]", static_cast<double>(top_p));
-    const int k = std::min(top_k, kv->s.V);
+    const int k = std::min(top_k, V);
     if (k > ds::kMaxTopK) return fail(DS_ERR_UNSUPPORTED, "top_k %d above %d", top_k, ds::kMaxTopK);
     if (k == 0 && top_p < 1.0f) return fail(DS_ERR_UNSUPPORTED, "top_p below 1 needs top_k >= 1");
-    if (kv->s.V > ds::kSampleMaxV) return fail(DS_ERR_UNSUPPORTED, "vocabulary %d above %d", kv->s.V, ds::kSampleMaxV);
+    if (V > ds::kSampleMaxV) return fail(DS_ERR_UNSUPPORTED, "vocabulary %d above %d", V, ds::kSampleMaxV);
+    *k_out = k;
+    return DS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ds_status ds_sample(const ds_kv* kv, const float* d_uniform, float temperature, int32_t top_k, float top_p,
+                    int32_t* d_tok_out, void* stream) {
+    if (!kv) return fail(DS_ERR_INVALID_ARG, "NULL argument");
+    int k = 0;
+    ds_status cs = check_sample_args(kv->s.V, d_uniform, temperature, top_k, top_p, d_tok_out, &k);
+    if (cs != DS_OK) return cs;
     const ds::SampleParams prm{temperature, k, top_p};
     // scratch: the argmax-key rows of the workspace, which nothing reads between steps
     hipError_t e = ds::enqueue_sample(kv->s.logits, kv->B, kv->s.V, d_uniform, prm,

@@ -57,6 +57,7 @@ struct StepArgs {
     int mm_ok;           // shapes allow the MFMA projections
     int mm_split;        // the narrow projections may take the split-K MFMA kernel
     int attn_g;          // head_dim 64 / 128 attention takes the DPP-reduced kernel
+    int pin;             // single-launch step's product input: kBF16 (hi/lo pairs) or kF32 (widened weights)
     float eps;
     const void* emb;
     float* cache;        // (L, 2, B, Hkv, T, D), fp32 or (cdt == kBF16) uint16 bf16 bits
@@ -123,7 +124,7 @@ struct SetList {
 };
 
 // Kernel ids for enqueue_kernel (diagnostics)
-enum KernelId { K_QKV = 0, K_ATTN = 1, K_COMBINE = 2, K_WO = 3, K_W13 = 4, K_W2 = 5, K_LOGITS = 6 };
+enum KernelId { K_QKV = 0, K_ATTN = 1, K_COMBINE = 2, K_WO = 3, K_W13 = 4, K_W2 = 5, K_LOGITS = 6, K_FLOOR = 7 };
 
 hipError_t set_kernel_attributes(int max_lds_bytes);
 // One decode / prefill position for n_items items.  nload > 0: every item's
@@ -160,6 +161,10 @@ hipError_t persist_prepare(const StepArgs& s);
 // tok_value when d_tok_in is NULL; d_tok_out may be NULL.
 hipError_t enqueue_persist(const StepArgs& s, const PersistArgs& p, const int32_t* d_tok_in, int tok_value,
                            int32_t* d_tok_out, hipStream_t st);
+// The handoff floor of the single launch: the same phases and handoff words
+// with no weight or cache loads and nothing stored outside the handoff words
+// (no cache rows, logits, token or lengths).  Diagnostic only.
+hipError_t enqueue_persist_floor(const StepArgs& s, const PersistArgs& p, hipStream_t st);
 // MFMA projections (mfma.hip): which = 0 qkv, 1 wo, 2 w13, 3 w2, 4 logits.
 bool mm_supported(const StepArgs& s);
 int mm_logits_blocks(const StepArgs& s);

@@ -3,7 +3,7 @@
 // One decode position for n_items sequences (work items) is:
 //   k_begin                      embedding gather + widen, step bookkeeping
 //   per layer: k_qkv             RMSNorm -> Q/K/V GEMV -> RoPE -> K/V append
-//              [long contexts]   k_attn (split-K partials) + k_attn_combine
+//              [long contexts]   k_attn_g / k_attn_d (split-K partials) + k_attn_combine
 //              k_wo              [short contexts: attention itself] Wo GEMV + residual
 //              k_w13             RMSNorm -> W1/W3 GEMV -> silu(a)*u
 //              k_w2              W2 GEMV + residual
@@ -516,98 +516,6 @@ __device__ void attention_short(const StepArgs& s, int layer, int item, int slot
 }
 
 // ---- long-context attention: split-K partials + combine ------------------------------------
-// Block (chunk, kv group g, item) scores positions [chunk*kChunk, ...) of the
-// item's pos+1 cached positions against the rep = H/Hkv query heads of
-// group g and writes the chunk's softmax partials (running max m, sum l,
-// unnormalised output o).  LPR = D/4 lanes hold one 16-byte slice each of a
-// key/value row, so K and V rows are read with full 16-byte coalesced loads.
-__global__ __launch_bounds__(256) void k_attn(StepArgs s, int layer) {
-    extern __shared__ float sm[];
-    const int chunk = blockIdx.x, g = blockIdx.y, item = blockIdx.z;
-    const int pos = s.pos[item], slot = s.slot[item];
-    const int n = pos + 1;
-    const int t0 = chunk * kChunk;
-    if (t0 >= n) return;
-    const int nt = min(kChunk, n - t0);
-    const int D = s.D, rep = s.H / s.Hkv;
-    const int LPR = D / 4, NRG = 256 / LPR;
-    const int e4 = threadIdx.x % LPR, rg = threadIdx.x / LPR;
-    float* qs = sm;                          // [rep][D]
-    float* sc = qs + kMaxRep * kMaxD;        // [rep][kChunk]
-    float* red = sc + kMaxRep * kChunk;      // [rep*4][256] reduction scratch
-    float* ml = red + 256 * kMaxRep * 4;     // [rep][2]
-    const float* q = s.q + static_cast<size_t>(item) * s.H * D + static_cast<size_t>(g) * rep * D;
-    for (int j = threadIdx.x; j < rep * D; j += 256) qs[j] = q[j];
-    __syncthreads();
-    const float* K = s.cache + cache_row(s, layer, 0, slot, g, t0);
-    const float* V = s.cache + cache_row(s, layer, 1, slot, g, t0);
-    const float scale = 1.0f / sqrtf(static_cast<float>(D));
-    for (int t = rg; t < kChunk; t += NRG) {  // uniform trip count per LPR group
-        const bool ok = t < nt;
-        const float4 kv = *reinterpret_cast<const float4*>(K + static_cast<size_t>(min(t, nt - 1)) * D + e4 * 4);
-        for (int j = 0; j < rep; j++) {
-            const float4 qv = *reinterpret_cast<const float4*>(qs + j * D + e4 * 4);
-            float d = kv.x * qv.x;
-            d = fmaf(kv.y, qv.y, d);
-            d = fmaf(kv.z, qv.z, d);
-            d = fmaf(kv.w, qv.w, d);
-            for (int o = LPR / 2; o > 0; o >>= 1) d += __shfl_xor(d, o);
-            if (ok && e4 == 0) sc[j * kChunk + t] = d * scale;
-        }
-    }
-    __syncthreads();
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int j = wave; j < rep; j += 4) {
-        float m = -INFINITY;
-        for (int t = lane; t < nt; t += 64) m = fmaxf(m, sc[j * kChunk + t]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (int t = lane; t < nt; t += 64) {
-            const float p = __expf(sc[j * kChunk + t] - m);
-            sc[j * kChunk + t] = p;
-            l += p;
-        }
-        l = wave_sum(l);
-        if (lane == 0) {
-            ml[j * 2 + 0] = m;
-            ml[j * 2 + 1] = l;
-        }
-    }
-    __syncthreads();
-    float acc[kMaxRep][4];
-    for (int j = 0; j < kMaxRep; j++) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
-    for (int t = rg; t < nt; t += NRG) {
-        const float4 vv = *reinterpret_cast<const float4*>(V + static_cast<size_t>(t) * D + e4 * 4);
-#pragma unroll
-        for (int j = 0; j < kMaxRep; j++) {
-            if (j < rep) {
-                const float p = sc[j * kChunk + t];
-                acc[j][0] = fmaf(p, vv.x, acc[j][0]);
-                acc[j][1] = fmaf(p, vv.y, acc[j][1]);
-                acc[j][2] = fmaf(p, vv.z, acc[j][2]);
-                acc[j][3] = fmaf(p, vv.w, acc[j][3]);
-            }
-        }
-    }
-    for (int j = 0; j < rep; j++)
-        for (int c = 0; c < 4; c++) red[(j * 4 + c) * 256 + threadIdx.x] = acc[j][c];
-    __syncthreads();
-    const int S = s.n_chunks;
-    for (int idx = threadIdx.x; idx < rep * D; idx += 256) {
-        const int j = idx / D, e = idx % D;
-        const int te4 = e / 4, c = e % 4;
-        float v = 0.f;
-        for (int r = 0; r < NRG; r++) v += red[(j * 4 + c) * 256 + r * LPR + te4];
-        const int h = g * rep + j;
-        const size_t pidx = (static_cast<size_t>(item) * s.H + h) * S + chunk;
-        s.part_o[pidx * D + e] = v;
-        if (e == 0) {
-            s.part_ml[pidx * 2 + 0] = ml[j * 2 + 0];
-            s.part_ml[pidx * 2 + 1] = ml[j * 2 + 1];
-        }
-    }
-}
-
 // Register-resident variant for head_dim D (a power of two, 16..256): every
 // K and V load of the block's chunk is issued up front (one memory round
 // trip), scores and the softmax stay in registers, and the row groups are
@@ -1246,13 +1154,8 @@ int short_positions(const StepArgs& s) {
     return 0;
 }
 
-static size_t attn_lds() {
-    return sizeof(float) * (kMaxRep * kMaxD + kMaxRep * kChunk + 256 * kMaxRep * 4 + kMaxRep * 2);
-}
-
 size_t max_lds_bytes(const StepArgs& s) {
-    size_t m = sizeof(float) * static_cast<size_t>(std::max(std::max(s.d, s.H * s.D), s.F));
-    return std::max(m, attn_lds());
+    return sizeof(float) * static_cast<size_t>(std::max(std::max(s.d, s.H * s.D), s.F));
 }
 
 enum Gemv { G_QKV, G_WO_SHORT, G_WO_LONG, G_W13, G_W2, G_LOGITS };
@@ -1385,8 +1288,6 @@ hipError_t set_kernel_attributes(int lds) {
     if (e == hipSuccess) e = set_attrs1<kF32>(lds);
     if (e == hipSuccess) e = set_attrs1<kQ8>(lds);
     if (e == hipSuccess) e = set_attrs1<kQ4>(lds);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     return e;
 }
 
@@ -1402,7 +1303,7 @@ static hipError_t launch_attn(const StepArgs& s, int layer, int n_items, hipStre
         case 64: hipLaunchKernelGGL(k_attn_d<64>, grid, dim3(256), 0, st, s, layer); break;
         case 128: hipLaunchKernelGGL(k_attn_d<128>, grid, dim3(256), 0, st, s, layer); break;
         case 256: hipLaunchKernelGGL(k_attn_d<256>, grid, dim3(256), 0, st, s, layer); break;
-        default: hipLaunchKernelGGL(k_attn, grid, dim3(256), attn_lds(), st, s, layer); break;
+        default: return hipErrorInvalidValue;  // check_config admits only the head sizes above
     }
     return hipGetLastError();
 }

@@ -382,13 +382,15 @@ __device__ __forceinline__ void load_gains(float (&gr)[kPNorm], const float* __r
 
 // The lane's share of a row product's input: the chunks sub, sub + G, ...
 // (EPC elements each, clamped to the last chunk), read from LDS into
-// registers in one batch so that the products wait for LDS once.
+// registers in one batch so that the products wait for LDS once.  IN is the
+// input's representation: kF32 (fp32 values) or kBF16 (bf16 hi/lo pairs,
+// see put_pair); bf16 weights take either.
 
-template <int WDT, int NC>
+template <int WDT, int IN, int NC>
 struct XRegs;
 
 template <int NC>
-struct XRegs<kF32, NC> {
+struct XRegs<kF32, kF32, NC> {
     float4 v[NC];
     __device__ __forceinline__ void load(const float* vin, int n, int sub, int G) {
         const int nchunks = n / 4;
@@ -398,7 +400,22 @@ struct XRegs<kF32, NC> {
 };
 
 template <int NC>
-struct XRegs<kBF16, NC> {
+struct XRegs<kBF16, kF32, NC> {
+    float4 a[NC], b[NC];  // the chunk's 8 fp32 elements
+    __device__ __forceinline__ void load(const float* vin, int n, int sub, int G) {
+        const int nchunks = n / 8;
+        const float4* v = reinterpret_cast<const float4*>(vin);
+#pragma unroll
+        for (int p = 0; p < NC; p++) {
+            const int c = min(sub + p * G, nchunks - 1);
+            a[p] = v[2 * c];
+            b[p] = v[2 * c + 1];
+        }
+    }
+};
+
+template <int NC>
+struct XRegs<kBF16, kBF16, NC> {
     uint4 h[NC], l[NC];  // hi and lo pairs of the chunk's 8 elements
     __device__ __forceinline__ void load(const float* vin, int n, int sub, int G) {
         const int nchunks = n / 8;
@@ -419,13 +436,14 @@ struct XRegs<kBF16, NC> {
 // valid, so that finish() needs no masks: it multiplies them with the
 // matching XRegs in four running sums and reduces over the G lanes,
 // touching no memory.
-template <int WDT, int G, int NC>
+// NOLOAD (the handoff-floor instantiation) issues no loads: every chunk is 0.
+template <int WDT, int G, int NC, bool NOLOAD = false>
 struct PStream {
     static constexpr int EPC = WDT == kBF16 ? 8 : 4;
     uint4 w[NC];
     __device__ __forceinline__ void start(const void* W, int row, int K, int sub, bool valid) {
         const size_t base = static_cast<size_t>(row) * K;
-        const int nchunks = valid ? K / EPC : 0;
+        const int nchunks = valid && !NOLOAD ? K / EPC : 0;
 #pragma unroll
         for (int p = 0; p < NC; p++) {
             const int c = sub + p * G;
@@ -441,7 +459,29 @@ struct PStream {
         return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), __builtin_bit_cast(bf16x2, x2), acc,
                                                 false);
     }
-    __device__ __forceinline__ float finish(const XRegs<WDT, NC>& x) const {
+    // bf16 weights times fp32 inputs: each weight widened to fp32 (the
+    // element at the lower address is the low half of the 32-bit word, so
+    // widening is a 16-bit left shift or a mask of the high half), one fp32
+    // FMA per element.
+    __device__ __forceinline__ float finish(const XRegs<kBF16, kF32, NC>& x) const {
+        static_assert(WDT == kBF16, "widened products need bf16 weights");
+        float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < NC; p++) {
+            float& u = a[2 * (p & 1)];
+            float& v = a[2 * (p & 1) + 1];
+            u = fmaf(__uint_as_float(w[p].x << 16), x.a[p].x, u);
+            v = fmaf(__uint_as_float(w[p].x & 0xFFFF0000u), x.a[p].y, v);
+            u = fmaf(__uint_as_float(w[p].y << 16), x.a[p].z, u);
+            v = fmaf(__uint_as_float(w[p].y & 0xFFFF0000u), x.a[p].w, v);
+            u = fmaf(__uint_as_float(w[p].z << 16), x.b[p].x, u);
+            v = fmaf(__uint_as_float(w[p].z & 0xFFFF0000u), x.b[p].y, v);
+            u = fmaf(__uint_as_float(w[p].w << 16), x.b[p].z, u);
+            v = fmaf(__uint_as_float(w[p].w & 0xFFFF0000u), x.b[p].w, v);
+        }
+        return group_sum<G>((a[0] + a[1]) + (a[2] + a[3]));
+    }
+    __device__ __forceinline__ float finish(const XRegs<WDT, WDT, NC>& x) const {
         float a[4] = {0.f, 0.f, 0.f, 0.f};  // bf16: hi and lo terms of even and odd chunks
 #pragma unroll
         for (int p = 0; p < NC; p++) {
@@ -495,9 +535,14 @@ struct PCtx {
 // rows of d (Q/K/V, W1/W3, vocabulary), H*D (Wo) and F (W2) elements.
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
-template <int WDT_, int PD_, int REP_, int GD_, int NCD_, int GH_, int NCH_, int GF_, int NCF_>
+// IN: how row-product inputs are held (kF32, or kBF16 hi/lo pairs; see
+// put_pair).  FLOOR: the handoff-floor diagnostic -- the same phases and LL
+// words with no weight or cache loads and no stores outside the LL words.
+template <int WDT_, int PD_, int REP_, int GD_, int NCD_, int GH_, int NCH_, int GF_, int NCF_, int IN_ = WDT_,
+          bool FLOOR_ = false>
 struct PCfg {
-    static constexpr int WDT = WDT_, PD = PD_, REP = REP_;
+    static constexpr int WDT = WDT_, PD = PD_, REP = REP_, IN = IN_;
+    static constexpr bool FLOOR = FLOOR_;
     static constexpr int GD = GD_, NCD = NCD_, GH = GH_, NCH = NCH_, GF = GF_, NCF = NCF_;
     // replicas of each published vector: lane `sub` of a row writes replica `sub`
     static constexpr int LLR = cmin(cmin(GD, GH), cmin(GF, kPRep));
@@ -510,7 +555,7 @@ __device__ __forceinline__ float emb_at(const StepArgs& s, int tok, int j) {
                         : static_cast<const float*>(s.emb)[e];
 }
 
-template <int PD, int REP>
+template <int PD, int REP, bool NOLOAD = false>
 struct KV {
     // keys: 4 lanes per row with PD / 4 dims (KF float4) each, 16 rows per slot
     static constexpr int KF = PD / 16;
@@ -528,6 +573,15 @@ struct KV {
     // the wave's cached rows of group g from position t0 on, clamped to the
     // last row an earlier step wrote (pos - 1, or 0)
     __device__ __forceinline__ void load(const StepArgs& s, int l, int g, int t0, int pos) {
+        if constexpr (NOLOAD) {
+#pragma unroll
+            for (int sl = 0; sl < NK; sl++)
+#pragma unroll
+                for (int f = 0; f < KF; f++) k[sl][f] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int ii = 0; ii < NV; ii++) v[ii] = 0.f;
+            return;
+        }
         const int lane = threadIdx.x & 63, rk = lane >> 2, qk = lane & 3, rv = lane / PD, ev = lane % PD;
         const int tmax = pos > 0 ? pos - 1 : 0;
 #pragma unroll
@@ -722,7 +776,7 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     uint64_t* const put_at = p.ll_qkv + sub * p.rstride + qw;
     float* const crow = s.cache + cache_row(s, 0, which == 2 ? 1 : 0, 0, g, c.pos) + e;
     const size_t cstride = cache_row(s, 1, 0, 0, 0, 0);  // one layer of the cache
-    PStream<C::WDT, G, C::NCD> st;
+    PStream<C::WDT, G, C::NCD, C::FLOOR> st;
     float gr[kPNorm];
     st.start(wmat(0), row, d, sub, active);
     load_gains(gr, p.layers[0].attn_norm, d);
@@ -740,9 +794,9 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
             wait_sample<2, true>(p.ll_x + c.rep, d, c.ep(l - 1, 4), c.err);
             block_fetch_own(Seg{p.ll_x + c.rep, d, c.ep(l - 1, 4), nullptr}, xv, c.err);
         }
-        const float rn = block_norm_regs<C::WDT>(xv, d, gr, s.eps, sm, vin);
+        const float rn = block_norm_regs<C::IN>(xv, d, gr, s.eps, sm, vin);
         if (active) {
-            XRegs<C::WDT, C::NCD> xr;
+            XRegs<C::WDT, C::IN, C::NCD> xr;
             xr.load(vin, d, sub, G);
             float out = rn * st.finish(xr);
             if (roped) {  // uniform over the wave
@@ -754,7 +808,7 @@ __device__ void role_qkv(const StepArgs& s, const PersistArgs& p, const PCtx& c,
             if (sub < C::LLR) {
                 // query head h = row / D sits in group h / REP at slot h % REP; then key, value
                 ll_put(put_at, out, c.ep(l, 0));
-                if (sub == 0 && which != 0) crow[static_cast<size_t>(l) * cstride] = out;
+                if (!C::FLOOR && sub == 0 && which != 0) crow[static_cast<size_t>(l) * cstride] = out;
             }
         }
         if (l + 1 == s.L && bt == 0 && threadIdx.x == 0) ll_put(p.ll_late, 0.f, c.ep(l, 0));
@@ -777,7 +831,7 @@ __device__ void role_attn(const StepArgs& s, const PersistArgs& p, const PCtx& c
     const int g = bt % s.Hkv, part = bt / s.Hkv, ck = part * 4 + wv;
     const int nw = min(4, c.nch - part * 4);  // waves with a chunk (>= 1)
     const bool active = wv < nw;
-    KV<PD, REP> kv;
+    KV<PD, REP, C::FLOOR> kv;
     if (active) kv.load(s, 0, g, ck * kPChunk, c.pos);
     float* qkv = sm;
     float* pw = sm + ((HD + 2 * KVD + 3) & ~3) + wv * REP * KV<PD, REP>::PWS;  // softmax weights of this wave
@@ -888,8 +942,8 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     float* o = sm + ((in_n + 3) & ~3);
     float* xr = o + HD;
     float* pw = xr + 64 + wv * REP * KV<PD, REP>::PWS;
-    PStream<C::WDT, G, C::NCH> st;
-    KV<PD, REP> kv;
+    PStream<C::WDT, G, C::NCH, C::FLOOR> st;
+    KV<PD, REP, C::FLOOR> kv;
     st.start(p.layers[0].wo, valid ? row : 0, HD, sub, valid);
     if (c.fused && attn_wave) kv.load(s, 0, g, 0, c.pos);
     for (int l = 0; l < s.L; l++) {
@@ -912,20 +966,20 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
             if (c.fused) {
                 kv.attend(in, g, 0, c.pos, pw, [&](int j, int e, float, float lsum, float acc, float acc1) {
                     const float inv = __builtin_amdgcn_rcpf(lsum);  // lsum >= 1 (the max term is exp(0))
-                    if ((e & 1) == 0) put_pair<C::WDT>(o, HD, (g * REP + j) * PD + e, acc * inv, acc1 * inv);
+                    if ((e & 1) == 0) put_pair<C::IN>(o, HD, (g * REP + j) * PD + e, acc * inv, acc1 * inv);
                 });
             }
         }
         if (!c.fused) {
             switch ((c.npart + 3) / 4) {  // partial counts unrolled in fours
-                case 1: merge_parts_t<PD, REP, 4, C::WDT>(in, c.npart, s.H, o); break;
-                case 2: merge_parts_t<PD, REP, 8, C::WDT>(in, c.npart, s.H, o); break;
-                case 3: merge_parts_t<PD, REP, 12, C::WDT>(in, c.npart, s.H, o); break;
-                default: merge_parts_t<PD, REP, 16, C::WDT>(in, c.npart, s.H, o); break;
+                case 1: merge_parts_t<PD, REP, 4, C::IN>(in, c.npart, s.H, o); break;
+                case 2: merge_parts_t<PD, REP, 8, C::IN>(in, c.npart, s.H, o); break;
+                case 3: merge_parts_t<PD, REP, 12, C::IN>(in, c.npart, s.H, o); break;
+                default: merge_parts_t<PD, REP, 16, C::IN>(in, c.npart, s.H, o); break;
             }
         }
         __syncthreads();
-        XRegs<C::WDT, C::NCH> ox;
+        XRegs<C::WDT, C::IN, C::NCH> ox;
         ox.load(o, HD, sub, G);
         const float y = st.finish(ox);
         if (valid && sub < C::LLR) ll_put(p.ll_x2 + sub * p.rstride + row, xr[row - r0] + y, c.ep(l, 2));
@@ -946,7 +1000,7 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
     const int rs = lane / G, sub = lane % G;
     const int row = bt * 4 * R + wv * R + rs;
     const bool valid = row < F;
-    PStream<C::WDT, G, C::NCD> s1, s3;
+    PStream<C::WDT, G, C::NCD, C::FLOOR> s1, s3;
     float gr[kPNorm];
     s1.start(p.layers[0].w1, valid ? row : 0, d, sub, valid);
     s3.start(p.layers[0].w3, valid ? row : 0, d, sub, valid);
@@ -957,8 +1011,8 @@ __device__ void role_w13(const StepArgs& s, const PersistArgs& p, const PCtx& c,
         wait_sample<2, true>(p.ll_x2 + c.rep, d, c.ep(l, 2), c.err);
         float xv[kPNorm];
         block_fetch_own(Seg{p.ll_x2 + c.rep, d, c.ep(l, 2), nullptr}, xv, c.err);
-        const float rn = block_norm_regs<C::WDT>(xv, d, gr, s.eps, sm, vin);
-        XRegs<C::WDT, C::NCD> xr;
+        const float rn = block_norm_regs<C::IN>(xv, d, gr, s.eps, sm, vin);
+        XRegs<C::WDT, C::IN, C::NCD> xr;
         xr.load(vin, d, sub, G);
         const float a = rn * s1.finish(xr);
         const float u = rn * s3.finish(xr);
@@ -985,17 +1039,17 @@ __device__ void role_w2(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     const bool valid = row < d;
     float* hs = sm;
     float* xr = sm + ((F + 3) & ~3);
-    float* hv = C::WDT == kBF16 ? xr + 64 : hs;  // product input (see put_pair)
-    PStream<C::WDT, G, C::NCF> st;
+    float* hv = C::IN == kBF16 ? xr + 64 : hs;  // product input (see put_pair)
+    PStream<C::WDT, G, C::NCF, C::FLOOR> st;
     st.start(p.layers[0].w2, valid ? row : 0, F, sub, valid);
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         wait_sample<2, true>(p.ll_h + c.rep, F, c.ep(l, 3), c.err);
         // h goes straight into the product input (bf16 hi/lo pairs, or fp32)
         block_fetch2<4>(Seg{p.ll_h + c.rep, F, c.ep(l, 3), hs}, Seg{p.ll_x2 + c.rep + r0, nrows, c.ep(l, 2), xr},
-                        c.err, [&](int i, float v0, float v1) { put_pair<C::WDT>(hv, F, i, v0, v1); });
+                        c.err, [&](int i, float v0, float v1) { put_pair<C::IN>(hv, F, i, v0, v1); });
         __syncthreads();
-        XRegs<C::WDT, C::NCF> hx;
+        XRegs<C::WDT, C::IN, C::NCF> hx;
         hx.load(hv, F, sub, G);
         const float y = st.finish(hx);
         if (valid && sub < C::LLR) ll_put(p.ll_x + sub * p.rstride + row, xr[row - r0] + y, c.ep(l, 4));
@@ -1067,7 +1121,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         const int gw = blk * 4 + wv;
         const int ntask = (s.V + R - 1) / R;
         const int rs = lane / GD, sub = lane % GD;
-        PStream<C::WDT, GD, C::NCD> sa, sb;
+        PStream<C::WDT, GD, C::NCD, C::FLOOR> sa, sb;
         const int ta = gw, tb = gw + kPWaves;
         // Workgroups without a layer role load their first two tasks now.  The
         // others load theirs once x is in: a poll waits for every load before it.
@@ -1087,15 +1141,15 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         float xv[kPNorm];
         block_fetch_own(Seg{p.ll_x + c.rep, s.d, c.ep(s.L - 1, 4), nullptr}, xv, c.err);
         if (!idle) start2();
-        const float rn = block_norm_regs<C::WDT>(xv, s.d, gr, s.eps, sm, vin);
-        XRegs<C::WDT, C::NCD> xr;
+        const float rn = block_norm_regs<C::IN>(xv, s.d, gr, s.eps, sm, vin);
+        XRegs<C::WDT, C::IN, C::NCD> xr;
         xr.load(vin, s.d, sub, GD);
         uint64_t key = 0ull;
-        auto take = [&](const PStream<C::WDT, GD, C::NCD>& st, int t) {
+        auto take = [&](const PStream<C::WDT, GD, C::NCD, C::FLOOR>& st, int t) {
             const int row = t * R + rs;
             const float y = rn * st.finish(xr);
             if (row < s.V && sub == 0) {
-                s.logits[row] = y;
+                if (!C::FLOOR) s.logits[row] = y;
                 const uint64_t k = key_word(y, row, epk);
                 key = k > key ? k : key;
             }
@@ -1137,11 +1191,13 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
         best = wave_max_u64(best);
         if (lane == 0) {
             const int idx = static_cast<int>(0x1FFFFu - static_cast<uint32_t>((best >> 15) & 0x1FFFFu));
-            if (d_tok_out) d_tok_out[0] = idx;
-            s.lengths[0] = c.pos + 1;
-            s.pos[0] = c.pos;
-            s.slot[0] = 0;
-            s.flag[0] = 1;
+            if (!C::FLOOR) {  // the floor diagnostic leaves the token, lengths and step state alone
+                if (d_tok_out) d_tok_out[0] = idx;
+                s.lengths[0] = c.pos + 1;
+                s.pos[0] = c.pos;
+                s.slot[0] = 0;
+                s.flag[0] = 1;
+            }
             *p.epoch = c.base + static_cast<uint32_t>(s.L * kPhases + 2);
         }
     }
@@ -1157,22 +1213,33 @@ static int pnc(int K, int wdt, int g) { return (K / epc(wdt) + g - 1) / g; }
 // model with bf16 weights and the small fp32 test model.  Other shapes take
 // the per-operation path.
 struct PKernel {
-    int wdt, D, rep, gd, ncd, gh, nch, gf, ncf;
+    int wdt, in, floor, D, rep, gd, ncd, gh, nch, gf, ncf;
     const void* fn;
 };
+// The 135M class comes with both product inputs (bf16 hi/lo pairs, and fp32
+// with the weights widened), and every class with its handoff-floor twin.
 using CfgM135 = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12>;
+using CfgM135W = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12, kF32>;
+using CfgM135F = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12, kBF16, true>;
+using CfgM135WF = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12, kF32, true>;
 using CfgTiny = PCfg<kF32, 16, 2, 4, 4, 4, 4, 4, 11>;
+using CfgTinyF = PCfg<kF32, 16, 2, 4, 4, 4, 4, 4, 11, kF32, true>;
 template <class C>
 static constexpr PKernel pk() {
-    return {C::WDT, C::PD, C::REP, C::GD, C::NCD, C::GH, C::NCH, C::GF, C::NCF,
+    return {C::WDT, C::IN, C::FLOOR ? 1 : 0, C::PD, C::REP, C::GD, C::NCD, C::GH, C::NCH, C::GF, C::NCF,
             reinterpret_cast<const void*>(k_persist<C>)};
 }
-static const PKernel kPKernels[] = {pk<CfgM135>(), pk<CfgTiny>()};
+static const PKernel kPKernels[] = {pk<CfgM135>(), pk<CfgM135W>(), pk<CfgM135F>(), pk<CfgM135WF>(),
+                                    pk<CfgTiny>(), pk<CfgTinyF>()};
 
-static const PKernel* persist_kernel(const StepArgs& s) {
+// The kernel for this shape, product input (s.pin; fp32 weights always take
+// fp32 inputs) and floor flag, or nullptr.
+static const PKernel* persist_kernel(const StepArgs& s, bool floor = false) {
     if (s.Hkv <= 0 || s.H % s.Hkv) return nullptr;
+    const int in = s.wdt == kBF16 ? s.pin : kF32;
     for (const PKernel& k : kPKernels) {
-        if (k.wdt != s.wdt || k.D != s.D || k.rep != s.H / s.Hkv) continue;
+        if (k.wdt != s.wdt || k.in != in || k.floor != (floor ? 1 : 0) || k.D != s.D || k.rep != s.H / s.Hkv)
+            continue;
         // every lane's chunks must fit its registers, and every G-lane group must have work
         if (pnc(s.d, s.wdt, k.gd) > k.ncd || pnc(s.H * s.D, s.wdt, k.gh) > k.nch || pnc(s.F, s.wdt, k.gf) > k.ncf)
             continue;
@@ -1207,6 +1274,11 @@ int persist_max_ctx(const StepArgs& s) {
 
 size_t persist_lds() { return sizeof(float) * kPLds; }
 
+// The floor twin holds no weights in registers, so by registers alone two of
+// its workgroups could share a CU; asking for more than half of a CU's 160
+// KiB of LDS keeps it at one workgroup per CU, as the real step runs.
+constexpr int kPFloorLds = 96 * 1024;
+
 // Every workgroup of the single launch must be resident at once (they wait
 // on each other's outputs).  True when the current device can hold all
 // kPBlocks of them (one per CU at this kernel's register use).
@@ -1222,14 +1294,26 @@ bool persist_fits_device(const StepArgs& s) {
 }
 
 hipError_t persist_prepare(const StepArgs& s) {
-    return hipFuncSetAttribute(persist_kernel(s)->fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(persist_lds()));
+    hipError_t e = hipFuncSetAttribute(persist_kernel(s)->fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(persist_lds()));
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(persist_kernel(s, true)->fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kPFloorLds);
+    return e;
 }
 
 hipError_t enqueue_persist(const StepArgs& s, const PersistArgs& p, const int32_t* d_tok_in, int tok_value,
                            int32_t* d_tok_out, hipStream_t st) {
     void* args[] = {const_cast<StepArgs*>(&s), const_cast<PersistArgs*>(&p), &d_tok_in, &tok_value, &d_tok_out};
     return hipLaunchKernel(persist_kernel(s)->fn, dim3(kPBlocks), dim3(kPThreads), args, persist_lds(), st);
+}
+
+hipError_t enqueue_persist_floor(const StepArgs& s, const PersistArgs& p, hipStream_t st) {
+    const int32_t* tok_in = nullptr;
+    int tok_value = 0;
+    int32_t* tok_out = nullptr;
+    void* args[] = {const_cast<StepArgs*>(&s), const_cast<PersistArgs*>(&p), &tok_in, &tok_value, &tok_out};
+    return hipLaunchKernel(persist_kernel(s, true)->fn, dim3(kPBlocks), dim3(kPThreads), args, kPFloorLds, st);
 }
 
 }  // namespace ds

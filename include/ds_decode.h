@@ -69,7 +69,7 @@ typedef struct {
     int32_t n_layers;        /* L                                               */
     int32_t n_heads;         /* H query heads                                   */
     int32_t n_kv_heads;      /* Hkv key/value heads; H % Hkv == 0               */
-    int32_t head_dim;        /* D; even                                         */
+    int32_t head_dim;        /* D: 16, 32, 64, 128 or 256                       */
     int32_t hidden_dim;      /* F: SwiGLU width                                 */
     int32_t vocab_size;      /* V                                               */
     int32_t tied_embeddings; /* 1: logits use token_emb; 0: a separate wcls     */
@@ -115,24 +115,38 @@ size_t ds_workspace_bytes(const ds_config* cfg, int32_t B, int32_t T);
 /* ---- model ---------------------------------------------------------------- */
 
 /* Binds a device weight arena (layout above, `arena_bytes` >= ds_weights_bytes)
- * to a model handle.  The arena is read in place and must stay unchanged
- * while the handle lives.  Checks: cfg consistent (H % Hkv == 0, D even,
- * every matrix row 16-byte aligned: dim, H*D and F times the weight size
- * multiple of 16), d_arena 256-byte aligned.  `stream` is unused (kept for
- * symmetry).  *out receives the handle. */
+ * to a model handle: the model load of "simple-llm / kasahare" (section
+ * "Python binding": a model is loaded once from its weight file, then
+ * called per token), with the weights already in device memory.  The arena
+ * is read in place and must stay unchanged while the handle lives.  Checks:
+ * cfg consistent (H % Hkv == 0; D one of 16, 32, 64, 128, 256; every matrix
+ * row 16-byte aligned: dim, H*D and F times the weight size multiple of 16),
+ * d_arena 256-byte aligned.  `stream` is unused (kept for symmetry).  *out
+ * receives the handle, which the caller frees with ds_model_destroy.
+ * Errors: DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED (a shape the kernels do
+ * not handle), DS_ERR_ALIGNMENT, DS_ERR_WORKSPACE (arena_bytes too small). */
 ds_status ds_load_weights(const ds_config* cfg, const void* d_arena, size_t arena_bytes,
                           void* stream, ds_model** out);
 void ds_model_destroy(ds_model* model);
 
 /* ---- key/value cache ------------------------------------------------------ */
 
-/* Binds a cache of B sequences with T positions each.  d_cache: fp32,
- * ds_kv_cache_bytes(cfg, B, T) bytes; d_lengths: int32[B], the number of
- * cached positions per sequence; d_workspace: ds_workspace_bytes(cfg, B, T)
- * bytes.  All three 256-byte aligned.  Zeroes d_lengths, uploads the RoPE
- * table into the workspace and synchronises `stream` once.  The library never
- * writes cache rows at positions >= lengths[b]; the caller must not write
- * d_lengths other than through the calls below. */
+/* Binds a cache of B sequences with T positions each: the preallocated
+ * (L, 2, B, H, T, D) cache of "Inside nanochat Part 4", section "Cache
+ * Architecture" (H = key/value heads here), with one length per sequence
+ * instead of that page's single position, because sequences of a batch may
+ * hold different lengths.  d_cache: ds_kv_cache_bytes(cfg, B, T) bytes (fp32,
+ * or bf16 values for a bf16 cache; the pointer type is float* either way);
+ * d_lengths: int32[B], the number of cached positions per sequence;
+ * d_workspace: ds_workspace_bytes(cfg, B, T) bytes.  All three are device
+ * memory, 256-byte aligned, owned by the caller and kept alive until
+ * ds_kv_cache_destroy.  Zeroes d_lengths, uploads the RoPE table into the
+ * workspace and synchronises `stream` once.  The library never writes cache
+ * rows at positions >= lengths[b]; the caller must not write d_lengths other
+ * than through the calls below.  *out receives the handle.
+ * Errors: DS_ERR_INVALID_ARG (NULL, B or T <= 0), DS_ERR_ALIGNMENT,
+ * DS_ERR_WORKSPACE (a buffer smaller than its size query), DS_ERR_UNSUPPORTED
+ * (the kernels need more LDS than the device gives), DS_ERR_HIP. */
 ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cache,
                              size_t cache_bytes, int32_t* d_lengths, void* d_workspace,
                              size_t workspace_bytes, void* stream, ds_kv** out);
@@ -171,13 +185,21 @@ ds_status ds_kv_cache_check(ds_kv* kv, void* stream);
 
 /* ---- the decode path ----------------------------------------------------- */
 
-/* Feeds h_tokens[0..n) (host, each in [0, V)) to sequence `seq` at positions
+/* The prompt phase of "Inside nanochat Part 4", sections "Phase 1: Single
+ * Prefill" and "Complete Generation Flow": the prompt's keys and values go
+ * into the cache and the last position's logits give the first new token.
+ * Feeds h_tokens[0..n) (host, each in [0, V)) to sequence `seq` at positions
  * lengths[seq] .. lengths[seq]+n-1, one position at a time through the same
- * kernels as ds_decode_step, and appends their keys and values.  After the
- * call lengths[seq] has grown by n, d_tok_out[seq] holds the greedy token of
- * the last position and the logits of that position are kept for ds_logits.
- * d_tok_out is int32[B] (only entry seq is written) and may be NULL.
- * Errors: DS_ERR_CONTEXT_FULL if lengths[seq] + n > T. */
+ * kernels as ds_decode_step (so a prompt re-fed here reproduces decoded
+ * steps bit for bit: the cached run of "GOTOken", section "About one token
+ * per second"), and appends their keys and values.  A non-empty sequence is
+ * extended.  After the call lengths[seq] has grown by n, d_tok_out[seq]
+ * holds the greedy token of the last position and the logits of that
+ * position are kept for ds_logits.  d_tok_out is device int32[B] (only entry
+ * seq is written) and may be NULL.  The host tokens are read during the call.
+ * Errors: DS_ERR_INVALID_ARG (seq out of range, n <= 0, NULL tokens),
+ * DS_ERR_BAD_TOKEN (a token outside [0, V)), DS_ERR_CONTEXT_FULL if
+ * lengths[seq] + n > T. */
 ds_status ds_prefill(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_tokens, int32_t n,
                      int32_t* d_tok_out, void* stream);
 
@@ -203,13 +225,21 @@ ds_status ds_prefill_batched(ds_model* model, ds_kv* kv, int32_t seq, const int3
 ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens,
                            const int32_t* h_counts, int32_t* d_tok_out, void* stream);
 
-/* One decode step for every sequence b in [0, B): reads d_tok_in[b], runs the
- * token at position lengths[b] through all layers, appends its key and value
- * rows to the cache at that position, writes the greedy next token to
- * d_tok_out[b] and advances lengths[b] by one.  d_tok_in and d_tok_out are
- * device int32[B]; they may be the same buffer.  The fp32 logits [B][V] of
- * the step stay in the workspace for ds_logits.
- * Errors: DS_ERR_CONTEXT_FULL if any lengths[b] == T. */
+/* One decode step for every sequence b in [0, B): the per-token loop of
+ * "Inside nanochat Part 4", sections "Complete Generation Flow" and
+ * "Greedy Decoding" (one new token per sequence, attending over the cached
+ * keys and values, its own key and value appended), computed as the
+ * pre-norm block of "simple-llm / kasahare", section "Architecture".  Reads
+ * d_tok_in[b], runs the token at position lengths[b] through all layers,
+ * appends its key and value rows to the cache at that position, writes the
+ * greedy next token (the lowest index among equal maxima) to d_tok_out[b]
+ * and advances lengths[b] by one.  d_tok_in and d_tok_out are device
+ * int32[B]; they may be the same buffer.  The fp32 logits [B][V] of the step
+ * stay in the workspace for ds_logits.  A token id outside [0, V) is
+ * detected on the device: that sequence reads row 0 and the next
+ * ds_kv_cache_check returns DS_ERR_BAD_TOKEN.
+ * Errors: DS_ERR_INVALID_ARG (NULL buffers, model/cache mismatch),
+ * DS_ERR_ALIGNMENT, DS_ERR_CONTEXT_FULL if any lengths[b] == T, DS_ERR_HIP. */
 ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, int32_t* d_tok_out,
                          void* stream);
 
@@ -267,9 +297,13 @@ ds_status ds_decode_step_rows(ds_model* model, ds_kv* kv, const int32_t* h_rows,
  * for a valid handle (returns -1 for NULL). */
 int32_t ds_kv_cache_single_launch_ctx(const ds_kv* kv);
 
-/* Copies the fp32 logits [B][V] of the last prefill / decode step into d_out
- * (device, B*V floats).  Rows of sequences that the last call did not touch
- * hold what they held before. */
+/* The logits of the last position, as the per-token call of "simple-llm /
+ * kasahare", section "Python binding", returns them (a (vocab,) fp32 vector
+ * per call; here one row per sequence).  Copies the fp32 logits [B][V] of
+ * the last prefill / decode step into d_out (device, B*V floats, row b =
+ * sequence b, owned by the caller).  Rows of sequences that the last call
+ * did not touch hold what they held before.  Only enqueues a device copy on
+ * `stream`.  Errors: DS_ERR_INVALID_ARG (NULL), DS_ERR_HIP. */
 ds_status ds_logits(const ds_kv* kv, float* d_out, void* stream);
 
 /* Dispatch of ds_decode_step: 0 = one kernel launch per operation (eager),
@@ -282,10 +316,16 @@ ds_status ds_set_dispatch(ds_kv* kv, int32_t mode);
 
 /* Diagnostics: enqueues `reps` back-to-back launches of one kernel of the
  * decode step -- 0 Q/K/V projection, 1 attention partials, 2 attention
- * combine, 3 Wo, 4 W1/W3, 5 W2, 6 vocabulary logits -- for layer `layer`,
- * with exactly the arguments and launch shape of the last ds_decode_step on
- * this cache (the same positions are rewritten; Wo and W2 add to the
- * residual again).  Lets a caller time one kernel with events on `stream`.
+ * combine, 3 Wo, 4 W1/W3, 5 W2, 6 vocabulary logits, or 7 the handoff floor
+ * of the single-launch batch-1 step (its phases and handoff words with no
+ * weight or cache loads, storing nothing outside its handoff words: no cache
+ * row, logit, token or length changes; needs B == 1 and a next step that is
+ * a single launch) -- with exactly the
+ * arguments and launch shape of the last ds_decode_step on this cache (the
+ * same positions are rewritten; Wo and W2 add to the residual again).
+ * Launch r uses layer (layer + r) mod L, so consecutive launches stream
+ * different weights and cache rows, as the step itself does.  Lets a caller
+ * time one kernel with events on `stream`.
  * Errors: DS_ERR_STATE before the first ds_decode_step. */
 ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t layer, int32_t reps,
                           void* stream);

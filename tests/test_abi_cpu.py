@@ -69,6 +69,13 @@ def test_invalid_configs_are_rejected(dsa):
         cfg = dsa.ds_config.of(shape)
         assert dsa.ds_weights_bytes(cfg) == 0, k
         assert dsa.ds_last_error() != ""
+    # head sizes the attention kernels are not built for
+    for hd in (8, 24, 48, 96, 512):
+        cfg = dsa.ds_config.of(dataclasses.replace(base, head_dim=hd, dim=128, hidden_dim=192))
+        assert dsa.ds_weights_bytes(cfg) == 0 and "head_dim" in dsa.ds_last_error(), hd
+    for hd in (16, 32, 64, 128, 256):
+        assert dsa.ds_weights_bytes(dsa.ds_config.of(dataclasses.replace(base, head_dim=hd, dim=128,
+                                                                         hidden_dim=192))) > 0, hd
     # bf16 rows of 172 elements are not whole 16-byte chunks
     cfg = dsa.ds_config.of(dataclasses.replace(base, weight_dtype=synth.BF16))
     assert dsa.ds_weights_bytes(cfg) == 0 and "16-byte" in dsa.ds_last_error()

@@ -35,6 +35,22 @@ def test_step_bytes_135m_from_the_parameter_count():
     assert bench.step_bytes(m, np.array([5], np.int32)) == want == 269_620_608
 
 
+def test_step_bytes_8b_untied_counts_the_head_not_the_embedding():
+    # 8B shape, untied: the 32 layers' matrices (6144x4096 q/k/v, 4096x4096 o,
+    # 2 x 14336x4096 w1/w3, 4096x14336 w2) and the 128256x4096 head, all bf16,
+    # are 15,009,316,864 bytes; the embedding table is only gathered (one
+    # 4096-element bf16 row).  Gains: 65 x 4096 fp32.  At 4096 cached
+    # positions the step reads 4097 K/V rows of 32 x 2 x 8 x 128 fp32 and
+    # writes one, and writes 128256 fp32 logits.
+    m = synth.M8B
+    assert m.tied_embeddings == 0
+    kv_row = 32 * 2 * 8 * 128 * 4
+    want = 15_009_316_864 + 65 * 4096 * 4 + 4096 * 2 + 4097 * kv_row + kv_row + 128256 * 4
+    assert bench.step_bytes(m, np.array([4096], np.int32)) == want
+    # about 16.09 GB, not the 17.14 GB the whole embedding table would add
+    assert abs(want / 1e9 - 16.09) < 0.01
+
+
 def test_kernel_bytes_8b():
     m = synth.M8B
     # W1 and W3: 2 x 14336 x 4096 bf16, plus the fp32 input row read twice

@@ -88,8 +88,8 @@ def bf16_rows_close(got, ref, what):
     return eq
 
 
-def compare(shape, arena, prompts, decode_calls, T, what, **kw):
-    ref_first, ref_first_lg, ref_toks, ref_lgs, om = oracle_run(shape, arena, prompts, decode_calls, T)
+def compare(shape, arena, prompts, decode_calls, T, what, fast=False, **kw):
+    ref_first, ref_first_lg, ref_toks, ref_lgs, om = oracle_run(shape, arena, prompts, decode_calls, T, fast=fast)
     feed = [ref_first] + ref_toks[:-1]
     g = gpu_run(shape, arena, prompts, feed, T, **kw)
     tol = BF16_CACHE_TOL if shape.cache_dtype == synth.BF16 else None
@@ -301,6 +301,32 @@ def test_split_attention_kernels_match_oracle(D, H, Hkv, kernel, monkeypatch):
     arena = synth.make_arena(shape, 14, std=0.1, gain_sigma=0.1)
     prompts = [synth.random_tokens(600 + b, n, shape.vocab_size) for b, n in enumerate([70, 130, 9])]
     compare(shape, arena, prompts, 3, 160, f"attention D={D} H={H} Hkv={Hkv} {kernel}")
+
+
+LONG_ATTN = {
+    # head_dim 256 (k_attn_d<256>), few (sequence, head) pairs: each head's
+    # dims over 4 combine blocks; 18 chunks
+    "d256-b1": (256, 2, 1, [1100], 1184),
+    # head_dim 128 (k_attn_g<128>) with the 8B shape's allocated context: 65
+    # chunks, combine over 4 blocks of 32 dims with 16 chunks per thread
+    "d128-b1-T4160": (128, 4, 1, [1100], 4160),
+    # H * B = 128 pairs: one combine block per head (256 dims, one chunk
+    # group), so past 48 chunks (3072 positions) it takes several batches;
+    # the short sequences also run the fused short-context path at D = 256
+    "d256-b16-multibatch": (256, 8, 2, [3100, 3080] + [5 + 3 * i for i in range(14)], 3136),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_ATTN))
+def test_long_context_attention_head_dims(name):
+    """Split-K attention and its combine at long contexts for head_dim 128
+    and 256, against the reference decoder (its batched evaluation)."""
+    D, H, Hkv, lens, T = LONG_ATTN[name]
+    shape = synth.small_shape(dim=128, n_heads=H, n_kv_heads=Hkv, head_dim=D, hidden_dim=192, vocab_size=256)
+    arena = synth.make_arena(shape, 31, std=0.1, gain_sigma=0.1)
+    prompts = [synth.random_tokens(700 + b, n, shape.vocab_size) for b, n in enumerate(lens)]
+    _say(f"long attention {name}: B={len(lens)} longest {max(lens)} T={T}")
+    compare(shape, arena, prompts, 3, T, f"long attention {name}", fast=True)
 
 
 def test_batch1_multi_chunk_attention_tiny():
