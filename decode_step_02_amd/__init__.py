@@ -22,6 +22,7 @@ STATUS = {0: "DS_OK", -1: "DS_ERR_INVALID_ARG", -2: "DS_ERR_UNSUPPORTED", -3: "D
           -4: "DS_ERR_CONTEXT_FULL", -5: "DS_ERR_BAD_TOKEN", -6: "DS_ERR_WORKSPACE", -7: "DS_ERR_HIP",
           -8: "DS_ERR_STATE", -9: "DS_ERR_DEVICE"}
 DS_F32, DS_BF16, DS_Q8, DS_Q4 = 0, 1, 2, 3
+DS_SAMPLE_NOALLOC_MAX_ROWS = 64  # include/ds_decode.h
 
 
 class DSError(RuntimeError):
@@ -74,6 +75,7 @@ _SIGS = {
     "ds_decode_step": (C.c_int, [_P, _P, _P, _P, _P]),
     "ds_logits": (C.c_int, [_P, _P, _P]),
     "ds_sample": (C.c_int, [_P, _P, C.c_float, C.c_int32, C.c_float, _P, _P]),
+    "ds_sample_noalloc": (C.c_int, [_P, C.c_int32, C.c_int32, _P, C.c_float, C.c_int32, C.c_float, _P, _P]),
     "ds_set_dispatch": (C.c_int, [_P, C.c_int32]),
     "ds_bench_kernel": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, _P]),
     "ds_last_error": (C.c_char_p, []),
@@ -197,6 +199,13 @@ def ds_logits(kv, d_out, stream=None):
 
 def ds_set_dispatch(kv, mode: int):
     _check(_lib.ds_set_dispatch(kv, mode))
+
+
+def ds_sample_noalloc(d_logits, B: int, V: int, d_uniform, temperature, top_k, top_p, d_tok_out, stream=None):
+    """ds_sample from caller-owned logits [B][V], with the library's static
+    device scratch instead of a workspace (allocates nothing)."""
+    _check(_lib.ds_sample_noalloc(_ptr(d_logits), int(B), int(V), _ptr(d_uniform), float(temperature), int(top_k),
+                                  float(top_p), _ptr(d_tok_out), _stream(stream)))
 
 
 def ds_bench_kernel(model, kv, which, layer, reps, stream=None):

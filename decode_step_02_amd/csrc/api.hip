@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -798,7 +799,7 @@ ds_status ds_logits(const ds_kv* kv, float* d_out, void* stream) {
 
 namespace {
 
-// Argument checks of ds_sample; on success the
+// Argument checks shared by ds_sample and ds_sample_noalloc; on success the
 // effective top-k (at most V) is in *k_out.
 ds_status check_sample_args(int V, const float* d_uniform, float temperature, int32_t top_k, float top_p,
                             const int32_t* d_tok_out, int* k_out) {
@@ -818,6 +819,43 @@ ds_status check_sample_args(int V, const float* d_uniform, float temperature, in
     return DS_OK;
 }
 
+// The sampling scratch of ds_sample_noalloc: DS_SAMPLE_NOALLOC_MAX_ROWS rows
+// of the per-row words the two-kernel sampler uses (2.5 MiB), held by every
+// device the library runs on until the process ends.  Host code never uses
+// the array's name as an address: each device's address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocRowWords = static_cast<size_t>(ds::kSampleMaxV) / 1024 + 4096;
+static __device__ __align__(256) uint64_t scratch[DS_SAMPLE_NOALLOC_MAX_ROWS * kNoAllocRowWords];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint64_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, or nullptr with the reason in g_err.
+uint64_t* device_scratch() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        hip_fail(e, "hipGetDevice");
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        fail(DS_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = static_cast<uint64_t*>(ptr);
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -834,6 +872,28 @@ ds_status ds_sample(const ds_kv* kv, const float* d_uniform, float temperature, 
                                       reinterpret_cast<uint64_t*>(kv->s.keys), ds::kMaxArgmaxBlocks, d_tok_out,
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "sample");
+    return ok();
+}
+
+ds_status ds_sample_noalloc(const float* d_logits, int32_t B, int32_t V, const float* d_uniform, float temperature,
+                            int32_t top_k, float top_p, int32_t* d_tok_out, void* stream) {
+    if (!d_logits) return fail(DS_ERR_INVALID_ARG, "NULL argument");
+    if (!aligned(d_logits, 4)) return fail(DS_ERR_ALIGNMENT, "logits buffer");
+    if (B < 0 || V <= 0) return fail(DS_ERR_INVALID_ARG, "B %d, V %d: need B >= 0 and V > 0", B, V);
+    if (B > DS_SAMPLE_NOALLOC_MAX_ROWS)
+        return fail(DS_ERR_UNSUPPORTED, "B %d above %d rows of the library's sampling scratch (use ds_sample)", B,
+                    DS_SAMPLE_NOALLOC_MAX_ROWS);
+    int k = 0;
+    ds_status cs = check_sample_args(V, d_uniform, temperature, top_k, top_p, d_tok_out, &k);
+    if (cs != DS_OK) return cs;
+    if (B == 0) return ok();
+    uint64_t* ptr = device_scratch();
+    if (!ptr) return DS_ERR_HIP;
+    static_assert(kNoAllocRowWords >= 1, "row words");
+    const ds::SampleParams prm{temperature, k, top_p};
+    hipError_t e = ds::enqueue_sample(d_logits, B, V, d_uniform, prm, ptr, kNoAllocRowWords, d_tok_out,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sample_noalloc");
     return ok();
 }
 

@@ -267,6 +267,28 @@ ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, in
 ds_status ds_sample(const ds_kv* kv, const float* d_uniform, float temperature, int32_t top_k, float top_p,
                     int32_t* d_tok_out, void* stream);
 
+/* Rows of the library's own sampling scratch (ds_sample_noalloc). */
+#define DS_SAMPLE_NOALLOC_MAX_ROWS 64
+
+/* ds_sample for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same draw as ds_sample, with the same kernels and the same argument rules,
+ * from caller-owned logits d_logits (device fp32 [B][V], row-major, 4-byte
+ * aligned) instead of a cache's last step, into d_tok_out[b] (device
+ * int32[B]), at the uniforms d_uniform[b] (device fp32[B]).  Its scratch is
+ * not a workspace but a static device array inside the library,
+ * DS_SAMPLE_NOALLOC_MAX_ROWS rows (2.5 MiB) that every device the library
+ * runs on holds until the process ends; the call allocates nothing (no
+ * hipMalloc, no library allocation).  Every call on one device shares that
+ * device's array: calls that may overlap on one device (two streams, two
+ * host threads) race and must be serialised by the caller.  No scratch
+ * content carries from one call to the next.  B == 0 does nothing.
+ * Errors: as ds_sample, plus DS_ERR_UNSUPPORTED for B above
+ * DS_SAMPLE_NOALLOC_MAX_ROWS, DS_ERR_INVALID_ARG for B < 0 or V <= 0, and
+ * DS_ERR_HIP if the scratch's device address cannot be obtained. */
+ds_status ds_sample_noalloc(const float* d_logits, int32_t B, int32_t V, const float* d_uniform, float temperature,
+                            int32_t top_k, float top_p, int32_t* d_tok_out, void* stream);
+
 /* A decode step of some of the sequences: the n_rows distinct sequence ids
  * in h_rows (host int32, each in [0, B)) each read d_tok_in[row], append at
  * lengths[row], advance by one and get their greedy token in d_tok_out[row]
