@@ -58,6 +58,7 @@ struct StepArgs {
     int mm_split;        // the narrow projections may take the split-K MFMA kernel
     int attn_g;          // head_dim 64 / 128 attention takes the DPP-reduced kernel
     int pin;             // single-launch step's product input: kBF16 (hi/lo pairs) or kF32 (widened weights)
+    int pcoop;           // single-launch step launched cooperatively (all workgroups resident, or no launch)
     float eps;
     const void* emb;
     float* cache;        // (L, 2, B, Hkv, T, D), fp32 or (cdt == kBF16) uint16 bf16 bits

@@ -1280,14 +1280,22 @@ size_t persist_lds() { return sizeof(float) * kPLds; }
 constexpr int kPFloorLds = 96 * 1024;
 
 // Every workgroup of the single launch must be resident at once (they wait
-// on each other's outputs).  True when the current device can hold all
-// kPBlocks of them (one per CU at this kernel's register use).
+// on each other's outputs).  This check, run when a cache is created, keeps
+// batch-1 steps off the single launch on a device that could never hold all
+// kPBlocks workgroups (one per CU at this kernel's register use), e.g. a
+// partitioned GPU, or (with s.pcoop) one without cooperative launches.  A
+// cooperative launch (s.pcoop) also makes the runtime start it only with
+// every workgroup resident; a plain launch relies on this check and on the
+// bounded waits, which let the grid drain and flag the step if workgroups of
+// another stream's work hold CUs.
 bool persist_fits_device(const StepArgs& s) {
     const PKernel* k = persist_kernel(s);
     if (!k) return false;
-    int dev = 0, ncu = 0, per_cu = 0;
+    int dev = 0, ncu = 0, per_cu = 0, coop = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+    if (s.pcoop && (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop))
+        return false;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k->fn, kPThreads, persist_lds()) != hipSuccess)
         return false;
     return static_cast<long>(per_cu) * ncu >= kPBlocks;
@@ -1302,10 +1310,22 @@ hipError_t persist_prepare(const StepArgs& s) {
     return e;
 }
 
+// Cooperative when asked for (s.pcoop) and the stream is not being captured
+// into a graph; else a plain launch, whose co-residency rests on
+// persist_fits_device and the bounded waits alone.
+static hipError_t launch_persist(const StepArgs& s, const void* fn, void** args, size_t lds, hipStream_t st) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cap);
+    if (e != hipSuccess) return e;
+    if (s.pcoop && cap == hipStreamCaptureStatusNone)
+        return hipLaunchCooperativeKernel(fn, dim3(kPBlocks), dim3(kPThreads), args, lds, st);
+    return hipLaunchKernel(fn, dim3(kPBlocks), dim3(kPThreads), args, lds, st);
+}
+
 hipError_t enqueue_persist(const StepArgs& s, const PersistArgs& p, const int32_t* d_tok_in, int tok_value,
                            int32_t* d_tok_out, hipStream_t st) {
     void* args[] = {const_cast<StepArgs*>(&s), const_cast<PersistArgs*>(&p), &d_tok_in, &tok_value, &d_tok_out};
-    return hipLaunchKernel(persist_kernel(s)->fn, dim3(kPBlocks), dim3(kPThreads), args, persist_lds(), st);
+    return launch_persist(s, persist_kernel(s)->fn, args, persist_lds(), st);
 }
 
 hipError_t enqueue_persist_floor(const StepArgs& s, const PersistArgs& p, hipStream_t st) {
@@ -1313,7 +1333,7 @@ hipError_t enqueue_persist_floor(const StepArgs& s, const PersistArgs& p, hipStr
     int tok_value = 0;
     int32_t* tok_out = nullptr;
     void* args[] = {const_cast<StepArgs*>(&s), const_cast<PersistArgs*>(&p), &tok_in, &tok_value, &tok_out};
-    return hipLaunchKernel(persist_kernel(s, true)->fn, dim3(kPBlocks), dim3(kPThreads), args, kPFloorLds, st);
+    return launch_persist(s, persist_kernel(s, true)->fn, args, kPFloorLds, st);
 }
 
 }  // namespace ds

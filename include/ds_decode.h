@@ -313,7 +313,10 @@ ds_status ds_decode_step_rows(ds_model* model, ds_kv* kv, const int32_t* h_rows,
  * is its own launch.  The single launch occupies every CU while it runs; work
  * that other streams run at the same time can delay it, and if its workgroups
  * cannot all start, its bounded waits give up and the next ds_kv_cache_check
- * returns DS_ERR_DEVICE.
+ * returns DS_ERR_DEVICE.  With DS_PERSIST_COOP=1 in the environment when the
+ * cache was created, it is launched cooperatively instead (except while its
+ * stream is being captured into a graph): the runtime then starts it only
+ * with all its workgroups resident, at about 16 us more per step.
  * Both give the same results within floating-point rounding.  Returns 0 when
  * batch-1 steps never take the single launch.  No device access; never fails
  * for a valid handle (returns -1 for NULL). */

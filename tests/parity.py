@@ -7,13 +7,7 @@ import numpy as np
 
 ABS_TOL = 5e-4   # max |logit_gpu - logit_ref|
 REL_TOL = 1e-4   # max |logit_gpu - logit_ref| / max |logit_ref|
-# With a bf16 key/value cache both sides round each stored value to bf16 from
-# fp32 values that differ in their last bits, so a value near a rounding
-# boundary lands one bf16 step (2^-8 relative) apart, and every later position
-# attends over it.  The logits then move by about 1e-4 relative; the bound is
-# ten times that, and still ten times below the 1e-2 that the rounding itself
-# moves the oracle's logits (test_oracle_bf16cache.py).
-BF16_CACHE_TOL = (4e-3, 1e-3)
+
 
 
 def logit_errors(got: np.ndarray, ref: np.ndarray):
@@ -50,6 +44,75 @@ def check_tokens(gpu_tok, ref_tok, ref_logits, gpu_logits, what=""):
         assert ref_logits[b][int(gpu_tok[b])] >= ref_logits[b].max() - 2 * err
         ties += 1
     return ties
+
+
+def _bf16_steps_apart(a, b):
+    """|a - b| in units in the last place of bf16 at the larger magnitude."""
+    m = np.maximum(np.abs(a), np.abs(b)).astype(np.float64)
+    ulp = np.where(m > 0, 2.0 ** (np.floor(np.log2(np.where(m > 0, m, 1.0))) - 7), 1.0)
+    return np.where(m > 0, np.abs(a.astype(np.float64) - b.astype(np.float64)) / ulp, 0.0)
+
+
+def bf16_teacher_forced(shape, arena, gpu_cache, gpu_lgs, positions, tokens, T, n_samples=8):
+    """Each step of a bf16-cache run recomputed by the oracle from the GPU's
+    own cache, so that the two sides start the step from the same state.
+
+    Both sides round keys and values to bf16 from fp32 numbers computed in
+    different orders, so a value within fp32 rounding of a bf16 rounding
+    boundary lands one bf16 step apart, and later positions attend over it:
+    compared from scratch, the runs drift apart by amounts no fp32 tolerance
+    covers.  Fed the GPU's cached rows, the oracle's step differs from the
+    GPU's only by fp32 rounding and by such flips in the row the step itself
+    writes.  So for step k (positions[k][b], tokens[k][b] for every sequence
+    b), with the oracle's cache set to the GPU's final cache (rows a step reads
+    were final when it ran), the logits must agree within the fp32 tolerance
+    plus an allowance of 2 x (the step's new-row differences, in bf16 steps) x
+    (the largest logit change per bf16 step of one cached value, measured in
+    the oracle on up to n_samples values moved one step).  Returns per step
+    (max |d|, max |ref|, allowance, new-row steps)."""
+    import oracle
+    B = len(positions[0])
+    gc = np.ascontiguousarray(gpu_cache, dtype=np.float32)
+    assert not np.any(gc[np.isfinite(gc)].view(np.uint32) & 0xFFFF), "a cache value is not a bf16 value"
+
+    def step(cache, k, b_only=None):
+        m = oracle.Model(shape, arena, B, T)
+        m.cache[:] = cache.reshape(-1)
+        bs = list(range(B)) if b_only is None else [b_only]
+        _, lg = m.forward_items(bs, [positions[k][b] for b in bs], [int(tokens[k][b]) for b in bs], [1] * len(bs))
+        return m, lg.astype(np.float64)
+
+    # sensitivity: the last step, one cached value it reads moved one bf16 step
+    rng = np.random.default_rng(97)
+    k_last = len(positions) - 1
+    per_step = 0.0
+    base = {}
+    for _ in range(n_samples):
+        b = int(rng.integers(0, B))
+        p = positions[k_last][b]
+        if p < 1:
+            continue
+        if b not in base:
+            base[b] = step(gc, k_last, b)[1][0]
+        l, kv = int(rng.integers(0, shape.n_layers)), int(rng.integers(0, 2))
+        g, t, e = int(rng.integers(0, shape.n_kv_heads)), int(rng.integers(0, p)), int(rng.integers(0, shape.head_dim))
+        c = gc.copy()
+        v = c[l, kv, b, g, t, e]
+        c[l, kv, b, g, t, e] = (np.float32(v).view(np.uint32) + np.uint32(0x10000)).view(np.float32)
+        st = float(_bf16_steps_apart(np.float32(v), c[l, kv, b, g, t, e]))
+        if st > 0:
+            per_step = max(per_step, float(np.abs(step(c, k_last, b)[1][0] - base[b]).max()) / st)
+    out = []
+    for k in range(len(positions)):
+        m, lg = step(gc, k)
+        cv = m.cache_view()
+        new_steps = 0.0
+        for b in range(B):
+            p = positions[k][b]
+            new_steps += float(_bf16_steps_apart(cv[:, :, b, :, p], gc[:, :, b, :, p]).sum())
+        d = float(np.abs(lg - gpu_lgs[k].astype(np.float64)).max())
+        out.append((d, float(np.abs(lg).max()), 2.0 * new_steps * per_step, new_steps))
+    return out
 
 
 def oracle_run(shape, arena, prompts, decode_calls, T, feed=None, fast=False):
