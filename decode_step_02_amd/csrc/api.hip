@@ -414,6 +414,14 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     s.pcoop = 0;
     const char* pco = std::getenv("DS_PERSIST_COOP");
     if (pco && std::strcmp(pco, "1") == 0) s.pcoop = 1;
+    // DS_ATTN_FULL=1: launches with at least kAttnFullMinBlocks (sequence,
+    // group) pairs run attention as one block per pair (k_attn_full), with no
+    // partials or combine launch.  Off by default: at B = 64 (135M) it
+    // measured the same step time as split-K plus its combine (1.444 against
+    // 1.450 ms), its longest sequences' blocks setting the pace.
+    s.attn_full = 0;
+    const char* afenv = std::getenv("DS_ATTN_FULL");
+    if (afenv && std::strcmp(afenv, "1") == 0) s.attn_full = 1;
     const char* sa = std::getenv("DS_SHORT_ATTN");  // "0" turns the fused short-context path off
     if (sa && std::strcmp(sa, "0") == 0) s.short_n = 0;
     ds::PersistArgs& pa = kv->pa;
@@ -788,6 +796,8 @@ ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t lay
         if (kv->last_nload > 0 && !(kv->s.mm_ok && kv->B >= ds::kMmMin) &&
             (which == ds::K_ATTN || which == ds::K_COMBINE))
             return fail(DS_ERR_STATE, "kernel %d is not part of a short-context step", which);
+        if (which == ds::K_COMBINE && ds::attn_full(kv->s, kv->B))
+            return fail(DS_ERR_STATE, "attention runs one block per (sequence, group) here: no combine launch");
         hipError_t e = ds::enqueue_kernel(which, (layer + r) % kv->s.L, kv->s, model->ptrs, kv->B, kv->last_nload, st);
         if (e != hipSuccess) return hip_fail(e, "bench kernel");
     }

@@ -57,6 +57,7 @@ struct StepArgs {
     int mm_ok;           // shapes allow the MFMA projections
     int mm_split;        // the narrow projections may take the split-K MFMA kernel
     int attn_g;          // head_dim 64 / 128 attention takes the DPP-reduced kernel
+    int attn_full;       // launches with many (item, group) pairs take the one-block-per-pair attention
     int pin;             // single-launch step's product input: kBF16 (hi/lo pairs) or kF32 (widened weights)
     int pcoop;           // single-launch step launched cooperatively (all workgroups resident, or no launch)
     float eps;
@@ -126,6 +127,11 @@ struct SetList {
 
 // Kernel ids for enqueue_kernel (diagnostics)
 enum KernelId { K_QKV = 0, K_ATTN = 1, K_COMBINE = 2, K_WO = 3, K_W13 = 4, K_W2 = 5, K_LOGITS = 6, K_FLOOR = 7 };
+
+// (item, key/value group) pairs from which attention runs as one block per
+// pair (k_attn_full: no partials, no combine launch) when s.attn_full is set
+constexpr int kAttnFullMinBlocks = 128;
+bool attn_full(const StepArgs& s, int n_items);
 
 hipError_t set_kernel_attributes(int max_lds_bytes);
 // One decode / prefill position for n_items items.  nload > 0: every item's

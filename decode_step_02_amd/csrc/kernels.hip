@@ -849,6 +849,198 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_g(StepArgs s, int layer) {
     }
 }
 
+// Decode attention of one (item, key/value group) in one block, with no
+// partials and no combine launch: wave w of NWV takes the 16-position runs
+// w, w + NWV, w + 2 NWV, ... of the item's pos + 1 cached positions and keeps
+// an online softmax per head in registers -- running max m, sum l and
+// weighted values o, rescaled by e^(m_old - m_new) when a run raises the max
+// -- loading the next run's rows while it scores the current one.  The
+// waves' (m, l, o) are then merged once through LDS, o = sum_w e^(m_w - M)
+// o_w / sum_w e^(m_w - M) l_w, and written to s.o.  Scores and value rows use
+// the layouts of k_attn_g (8 lanes per key row, D/64 value dims per lane);
+// a run's weights reach the value lanes by readlane from the lanes that
+// hold them.  For launches with enough (item, group) pairs to fill the chip.
+template <int D, int REP, int CDT, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_attn_full(StepArgs s, int layer) {
+    constexpr int KF = D / 32, DPL = D / 64, RPW = 16, NSL = RPW / 8;
+    static_assert(D == 64 || D == 128, "head_dim");
+    __shared__ float wml[NWV][REP][2];
+    __shared__ float wov[NWV][REP][D];
+    const int g = blockIdx.x, item = blockIdx.y;
+    const int pos = s.pos[item], slot = s.slot[item];
+    const int n = pos + 1;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int kq = lane & 7, rr = lane >> 3;
+    const size_t kidx = cache_row(s, layer, 0, slot, g, 0), vidx = cache_row(s, layer, 1, slot, g, 0);
+    const float* Kb = CDT == kBF16 ? reinterpret_cast<const float*>(reinterpret_cast<const uint16_t*>(s.cache) + kidx)
+                                   : s.cache + kidx;
+    const float* Vb = CDT == kBF16 ? reinterpret_cast<const float*>(reinterpret_cast<const uint16_t*>(s.cache) + vidx)
+                                   : s.cache + vidx;
+    const int nrun = (n + RPW - 1) / RPW;
+    using Rows = KVRows<D, CDT, RPW>;
+    auto load = [&](Rows& kv, int run) {
+        int rows[NSL];
+#pragma unroll
+        for (int sl = 0; sl < NSL; sl++) rows[sl] = min(run * RPW + sl * 8 + rr, n - 1);
+        kv.load(Kb, Vb, rows, run * RPW, n - 1, kq, lane);
+    };
+    Rows cur;
+    load(cur, min(wave, nrun - 1));
+    const float* qb = s.q + (static_cast<size_t>(item) * s.H + static_cast<size_t>(g) * REP) * D;
+    float4 qv[REP][KF];
+#pragma unroll
+    for (int j = 0; j < REP; j++) {
+#pragma unroll
+        for (int f = 0; f < KF; f++) qv[j][f] = *reinterpret_cast<const float4*>(qb + j * D + Rows::qdim(f, kq));
+    }
+    const float scale = 1.0f / sqrtf(static_cast<float>(D));
+    float m[REP], l[REP], o[REP][DPL];
+#pragma unroll
+    for (int j = 0; j < REP; j++) {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+#pragma unroll
+        for (int dd = 0; dd < DPL; dd++) o[j][dd] = 0.f;
+    }
+    // One run of rows: the online softmax update of every head.
+    auto step = [&](const Rows& kv, int run) {
+        float sc[REP * NSL];
+#pragma unroll
+        for (int j = 0; j < REP; j++) {
+#pragma unroll
+            for (int sl = 0; sl < NSL; sl++) {
+                float d = 0.f;
+#pragma unroll
+                for (int f = 0; f < KF; f++) {
+                    const float4 kk = kv.key(sl, f);
+                    d = fmaf(kk.x, qv[j][f].x, d);
+                    d = fmaf(kk.y, qv[j][f].y, d);
+                    d = fmaf(kk.z, qv[j][f].z, d);
+                    d = fmaf(kk.w, qv[j][f].w, d);
+                }
+                sc[j * NSL + sl] = d;
+            }
+        }
+        group_reduce_n<8, OpSum>(sc, OpSum{});  // every lane of a row holds its score
+        float mr[REP];
+#pragma unroll
+        for (int j = 0; j < REP; j++) {
+            mr[j] = -INFINITY;
+#pragma unroll
+            for (int sl = 0; sl < NSL; sl++) {
+                const int t = run * RPW + sl * 8 + rr;
+                sc[j * NSL + sl] = t < n ? sc[j * NSL + sl] * scale : -INFINITY;
+                mr[j] = OpMax{}(mr[j], sc[j * NSL + sl]);
+            }
+        }
+        group_reduce_n<64, OpMax, 8>(mr, OpMax{});  // the run's max, on every lane (-inf: run past pos)
+        float ps[REP * NSL], lr[REP];
+#pragma unroll
+        for (int j = 0; j < REP; j++) {
+            // a run wholly past pos (all scores -inf) changes nothing, even
+            // before the first real run (m = -inf)
+            const float mn = OpMax{}(m[j], mr[j]);
+            const bool none = mn == -INFINITY;
+            const float alpha = none ? 1.f : __expf(m[j] - mn);  // 0 on the first real run (m = -inf)
+            m[j] = mn;
+            l[j] *= alpha;
+#pragma unroll
+            for (int dd = 0; dd < DPL; dd++) o[j][dd] *= alpha;
+            lr[j] = 0.f;
+#pragma unroll
+            for (int sl = 0; sl < NSL; sl++) {
+                ps[j * NSL + sl] = none ? 0.f : __expf(sc[j * NSL + sl] - mn);  // 0 for rows past pos
+                lr[j] += ps[j * NSL + sl];
+            }
+        }
+        group_reduce_n<64, OpSum, 8>(lr, OpSum{});  // over the run's 8-lane row groups
+#pragma unroll
+        for (int j = 0; j < REP; j++) {
+            l[j] += lr[j];
+#pragma unroll
+            for (int dd = 0; dd < DPL; dd++) {
+                float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                for (int i = 0; i < RPW; i += 2) {  // row i's weight sits in lane (i % 8) * 8, slot i / 8
+                    const float p0 = __int_as_float(
+                        __builtin_amdgcn_readlane(__float_as_int(ps[j * NSL + i / 8]), (i % 8) * 8));
+                    const float p1 = __int_as_float(
+                        __builtin_amdgcn_readlane(__float_as_int(ps[j * NSL + (i + 1) / 8]), ((i + 1) % 8) * 8));
+                    a0 = fmaf(p0, kv.val(i, dd), a0);
+                    a1 = fmaf(p1, kv.val(i + 1, dd), a1);
+                }
+                o[j][dd] += a0 + a1;
+            }
+        }
+    };
+    // Two row buffers in turn, each loaded one run ahead of its use, with no
+    // branch between a load and its use (the compiler would otherwise sink
+    // the loads to it): the loads are unconditional (a run past the last one
+    // re-reads the last rows) and such a run is wholly masked, a no-op.
+    Rows nxt;
+    for (int run = wave; run < nrun; run += 2 * NWV) {  // per wave: no barrier inside
+        load(nxt, min(run + NWV, nrun - 1));
+        step(cur, run);
+        load(cur, min(run + 2 * NWV, nrun - 1));
+        step(nxt, run + NWV);
+    }
+#pragma unroll
+    for (int j = 0; j < REP; j++) {
+        if (lane == 0) {
+            wml[wave][j][0] = m[j];
+            wml[wave][j][1] = l[j];
+        }
+#pragma unroll
+        for (int dd = 0; dd < DPL; dd++) wov[wave][j][lane * DPL + dd] = o[j][dd];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < REP * D; idx += 64 * NWV) {
+        const int j = idx / D, e = idx % D;
+        float M = wml[0][j][0];  // wave 0 holds position 0: finite
+#pragma unroll
+        for (int w = 1; w < NWV; w++) M = OpMax{}(M, wml[w][j][0]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; w++) {
+            const float f = __expf(wml[w][j][0] - M);  // 0 for waves without a run
+            L = fmaf(f, wml[w][j][1], L);
+            O = fmaf(f, wov[w][j][e], O);
+        }
+        s.o[(static_cast<size_t>(item) * s.H + g * REP + j) * D + e] = O / L;
+    }
+}
+
+// 16 waves (4 per SIMD, at most 128 VGPRs each) where the registers fit,
+// else 8: head_dim 128, and 4 query heads per group at head_dim 64.
+template <int D, int CDT>
+static bool launch_attn_full2(const StepArgs& s, dim3 grid, int layer, hipStream_t st) {
+    constexpr int W = D == 64 ? 16 : 8;
+    switch (s.H / s.Hkv) {
+        case 1: hipLaunchKernelGGL((k_attn_full<D, 1, CDT, W>), grid, dim3(64 * W), 0, st, s, layer); return true;
+        case 2: hipLaunchKernelGGL((k_attn_full<D, 2, CDT, W>), grid, dim3(64 * W), 0, st, s, layer); return true;
+        case 3: hipLaunchKernelGGL((k_attn_full<D, 3, CDT, W>), grid, dim3(64 * W), 0, st, s, layer); return true;
+        case 4: hipLaunchKernelGGL((k_attn_full<D, 4, CDT, 8>), grid, dim3(64 * 8), 0, st, s, layer); return true;
+        default: return false;
+    }
+}
+
+bool attn_full(const StepArgs& s, int n_items) {
+    return s.attn_full && (s.D == 64 || s.D == 128) && s.Hkv > 0 && s.H % s.Hkv == 0 && s.H / s.Hkv <= 4 &&
+           n_items * s.Hkv >= kAttnFullMinBlocks;
+}
+
+static hipError_t launch_attn_full(const StepArgs& s, int layer, int n_items, hipStream_t st) {
+    const dim3 grid(s.Hkv, n_items);
+    bool ok;
+    if (s.D == 64)
+        ok = s.cdt == kBF16 ? launch_attn_full2<64, kBF16>(s, grid, layer, st)
+                            : launch_attn_full2<64, kF32>(s, grid, layer, st);
+    else
+        ok = s.cdt == kBF16 ? launch_attn_full2<128, kBF16>(s, grid, layer, st)
+                            : launch_attn_full2<128, kF32>(s, grid, layer, st);
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
 constexpr int kAttnWaves = 4;  // waves per 64-position chunk of k_attn_g
 
 template <int D, int CDT>
@@ -1337,8 +1529,12 @@ hipError_t enqueue_step(const StepArgs& s, const ModelPtrs& m, const BeginList* 
         if (lc.nload > 0) {
             e = gemv(G_WO_SHORT, s, w, l, n_items, st, lc);
         } else {
-            e = launch_attn(s, l, n_items, st);
-            if (e == hipSuccess) e = launch_combine(s, n_items, st);
+            if (attn_full(s, n_items)) {
+                e = launch_attn_full(s, l, n_items, st);
+            } else {
+                e = launch_attn(s, l, n_items, st);
+                if (e == hipSuccess) e = launch_combine(s, n_items, st);
+            }
             if (e == hipSuccess)
                 e = mm ? mm_gemv(1, s, w, l, n_items, lc.ident, nullptr, nullptr, st) : gemv(G_WO_LONG, s, w, l, n_items, st, lc);
         }
@@ -1369,9 +1565,9 @@ hipError_t enqueue_kernel(int which, int layer, const StepArgs& s, const ModelPt
         case K_QKV: return mm ? mm_gemv(0, s, w, layer, n_items, 1, nullptr, nullptr, st) : gemv(G_QKV, s, w, layer, n_items, st, lc);
         case K_ATTN:
             if (lc.nload > 0) return hipErrorInvalidValue;
-            return launch_attn(s, layer, n_items, st);
+            return attn_full(s, n_items) ? launch_attn_full(s, layer, n_items, st) : launch_attn(s, layer, n_items, st);
         case K_COMBINE:
-            if (lc.nload > 0) return hipErrorInvalidValue;
+            if (lc.nload > 0 || attn_full(s, n_items)) return hipErrorInvalidValue;
             return launch_combine(s, n_items, st);
         case K_WO:
             if (mm) return mm_gemv(1, s, w, layer, n_items, 1, nullptr, nullptr, st);

@@ -404,6 +404,40 @@ def test_single_launch_steps_in_a_captured_graph():
     model.close()
 
 
+FULL_ATTN = {
+    # (head_dim, H, Hkv, cache): 64 sequences x Hkv >= 128 (item, group)
+    # pairs, so decode steps take the one-block-per-pair attention; the
+    # ragged prefill's later passes (fewer sequences) take split-K
+    "d64-rep2": (64, 4, 2, "F32"),
+    "d64-rep3": (64, 6, 2, "F32"),
+    "d64-rep4": (64, 8, 2, "F32"),
+    "d128-rep4": (128, 8, 2, "F32"),
+    "d128-rep1": (128, 2, 2, "F32"),
+    "d64-rep3-bf16": (64, 6, 2, "BF16"),
+    "d128-rep2-bf16": (128, 4, 2, "BF16"),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_ATTN))
+def test_one_block_per_pair_attention(name, monkeypatch):
+    """k_attn_full (DS_ATTN_FULL=1): each (sequence, key/value group) in one
+    block, waves walking 16-position runs with an online softmax, merged once
+    in LDS.
+    Lengths 1 (one wave, one run), 15..17, 255..257 (one and two runs per
+    wave), up to 700, and one sequence of 1100 positions (five runs on some
+    waves)."""
+    monkeypatch.setenv("DS_ATTN_FULL", "1")  # read when the cache is created
+    D, H, Hkv, cdt = FULL_ATTN[name]
+    shape = synth.small_shape(dim=128, n_heads=H, n_kv_heads=Hkv, head_dim=D, hidden_dim=192, vocab_size=256,
+                              cache_dtype=getattr(synth, cdt))
+    arena = synth.make_arena(shape, 41, std=0.1, gain_sigma=0.1)
+    rng = np.random.default_rng(42)
+    lens = [1, 15, 16, 17, 255, 256, 257, 1100] + [int(n) for n in rng.integers(1, 700, 56)]
+    prompts = [synth.random_tokens(900 + b, n, shape.vocab_size) for b, n in enumerate(lens)]
+    _say(f"one block per pair {name}: B=64 longest {max(lens)}")
+    compare(shape, arena, prompts, 3, 1104, f"one block per pair {name}", fast=True)
+
+
 def test_batch1_multi_chunk_attention_tiny():
     """Batch-1 steps past 32 positions merge per-chunk attention partials
     (positions 70..99 span three and four 32-position chunks)."""
