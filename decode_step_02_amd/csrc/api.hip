@@ -40,6 +40,10 @@ ds_status hip_fail(hipError_t e, const char* what) {
     return fail(DS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The current device's copy of ds_sample_noalloc's static scratch (defined
+// with it below), or nullptr with the reason in g_err.
+uint64_t* device_scratch();
+
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -263,6 +267,10 @@ ds_status ds_load_weights(const ds_config* cfg, const void* d_arena, size_t aren
         return fail(DS_ERR_WORKSPACE, "arena has %zu bytes, the layout needs %zu", arena_bytes, need);
     ds_model* m = new (std::nothrow) ds_model();
     if (!m) return fail(DS_ERR_INVALID_ARG, "out of host memory");
+    // set-up of ds_sample_noalloc on this device: its scratch's address, so
+    // that a first call under graph capture need not look it up (a failure
+    // here is reported by that call instead)
+    (void)device_scratch();
     m->cfg = *cfg;
     m->arena = d_arena;
     layout(cfg, &m->off);

@@ -279,7 +279,9 @@ ds_status ds_sample(const ds_kv* kv, const float* d_uniform, float temperature, 
  * not a workspace but a static device array inside the library,
  * DS_SAMPLE_NOALLOC_MAX_ROWS rows (2.5 MiB) that every device the library
  * runs on holds until the process ends; the call allocates nothing (no
- * hipMalloc, no library allocation).  Every call on one device shares that
+ * hipMalloc, no library allocation).  Its device address is looked up once
+ * per device: by ds_load_weights on the device current then, else by the
+ * first call on that device.  Every call on one device shares that
  * device's array: calls that may overlap on one device (two streams, two
  * host threads) race and must be serialised by the caller.  No scratch
  * content carries from one call to the next.  B == 0 does nothing.

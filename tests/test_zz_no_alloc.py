@@ -63,6 +63,40 @@ def test_noalloc_matches_ds_sample_twice_second_smaller():
         model.close()
 
 
+def test_noalloc_in_a_captured_graph():
+    """The caller it is for: ds_sample_noalloc captured into a graph
+    (torch.cuda.CUDAGraph) over fixed input and output buffers, replayed with
+    new uniforms copied in between replays, gives ds_sample's tokens on every
+    replay."""
+    import torch
+    import decode_step_02_amd as dsa
+    shape = dataclasses.replace(synth.TINY, vocab_size=3000)
+    B = 9
+    model, kv = _step_logits(shape, B, 77)
+    logits = kv.logits().clone()
+    u = torch.zeros(B, dtype=torch.float32, device="cuda")
+    got = torch.zeros(B, dtype=torch.int32, device="cuda")
+    st = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            dsa.ds_sample_noalloc(logits, B, shape.vocab_size, u, 0.9, 50, 0.9, got, st)
+    rng = np.random.default_rng(5)
+    for r in range(3):
+        draws = torch.from_numpy(rng.random(B).astype(np.float32)).cuda()
+        u.copy_(draws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+        kv.sample(draws, 0.9, 50, 0.9, ref)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), ref.cpu().numpy()), f"replay {r}"
+    kv.check()
+    kv.close()
+    model.close()
+
+
 def test_noalloc_rejects_rows_above_its_scratch():
     import torch
     import decode_step_02_amd as dsa
