@@ -235,14 +235,15 @@ def kernel_flops(m: synth.ModelShape, which: str, B: int) -> float:
 
 
 def flush_and_copy_peak(torch, stream, mib: int):
-    """Two device buffers of `mib` MiB each: copying one into the other reads
-    and writes 2 x mib MiB, more than the 256 MB Infinity Cache and the L2s
-    hold, so it evicts whatever a step left there.  Returns the buffers and
-    the copy's rate (bytes read + written per second, median of 5), the
-    measured streaming peak the fractions are also reported against."""
+    """Two device buffers of `mib` MiB each (the halves of one): copying one
+    into the other reads and writes 2 x mib MiB, more than the 256 MB Infinity
+    Cache and the L2s hold, so it evicts whatever a step left there.  Returns
+    (half a, half b, the whole) and the copy's rate (bytes read + written per
+    second, median of 5), a measured streaming peak the fractions are also
+    reported against."""
     n = mib * (1 << 20) // 4
-    a = torch.ones(n, dtype=torch.float32, device="cuda")
-    b = torch.empty_like(a)
+    whole = torch.ones(2 * n, dtype=torch.float32, device="cuda")  # the read probe streams all of it
+    a, b = whole[:n], whole[n:]
     with torch.cuda.stream(stream):
         b.copy_(a)
         torch.cuda.synchronize()
@@ -255,11 +256,32 @@ def flush_and_copy_peak(torch, stream, mib: int):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e-3)
     t = sorted(ts)[2]
-    return (a, b), {"bytes_read": 4 * n, "bytes_written": 4 * n, "us_per_copy": t * 1e6,
-                    "GBps": 8 * n / t / 1e9}
+    return (a, b, whole), {"bytes_read": 4 * n, "bytes_written": 4 * n, "us_per_copy": t * 1e6,
+                           "GBps": 8 * n / t / 1e9}
 
 
-def decode_bench(dsa, torch, w, args, stream, steps, warmup, samp=None, flush=None, copy_peak=None) -> dict:
+def read_peak(dsa, torch, stream, buf, reps=5) -> dict:
+    """The library's plain streaming read (ds_bench_stream) over `buf`, median
+    of `reps` launches: the read bandwidth a kernel doing nothing else gets."""
+    out = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        dsa.ds_bench_stream(buf, out, 1, stream)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dsa.ds_bench_stream(buf, out, 1, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(ts)[reps // 2]
+    nbytes = buf.numel() * buf.element_size()
+    return {"bytes_read": nbytes, "us_per_read": t * 1e6, "GBps": nbytes / t / 1e9}
+
+
+def decode_bench(dsa, torch, w, args, stream, steps, warmup, samp=None, flush=None, copy_peak=None,
+                 rpeak=None) -> dict:
     """Decode steps of workload `w`: prompts prefilled (untimed), then `steps`
     chained steps after `warmup`, cycled over the workload's positions
     (lengths rewound every decode_calls steps).  Returns the result record
@@ -334,7 +356,7 @@ def decode_bench(dsa, torch, w, args, stream, steps, warmup, samp=None, flush=No
                 pairs.append((a, b))
             torch.cuda.synchronize()
             kv.check()
-            return 1000.0 * sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+            return [1000.0 * a.elapsed_time(b) for a, b in pairs]
 
         single = B == 1 and kv.single_launch_ctx() >= int(base.max()) + cycle
         kern = {}
@@ -344,7 +366,8 @@ def decode_bench(dsa, torch, w, args, stream, steps, warmup, samp=None, flush=No
             # events around it on the library's stream (eager dispatch, so the
             # events bracket the kernel itself), over the same step sequence.
             kv.set_dispatch(0)
-            us = timed_steps(steps)
+            per = timed_steps(steps)
+            us = float(np.mean(per))
             dom = "k_persist (whole step)"
             dk = {"us_per_launch": us, "launches_per_step": 1, "us_per_step": us, "bytes_per_launch": bytes_step}
             kern[dom] = dk
@@ -383,16 +406,18 @@ def decode_bench(dsa, torch, w, args, stream, steps, warmup, samp=None, flush=No
                               "bytes_per_launch": kernel_bytes(m, name, B, mean_ctx)}
             dom = max(kern, key=lambda n: kern[n]["us_per_step"])
             dk = kern[dom]
+            per = timed_steps(steps)  # each step bracketed by events (graph dispatch)
         achieved = dk["bytes_per_launch"] / (dk["us_per_launch"] * 1e-6) / 1e9
 
         cold = None
         if flush is not None:
-            fa, fb = flush
-            us_cold = timed_steps(min(steps, 4 * cycle), before=lambda: fb.copy_(fa))
+            fa, fb = flush[0], flush[1]
+            us_cold = float(np.mean(timed_steps(min(steps, 4 * cycle), before=lambda: fb.copy_(fa))))
             gb_cold = bytes_step / (us_cold * 1e-6) / 1e9
             cold = {"us_per_step": us_cold, "tok_s": B * 1e6 / us_cold, "achieved_GBps": gb_cold,
                     "frac_of_hbm_peak": gb_cold / HBM_PEAK_GBPS,
                     "frac_of_copy_peak": gb_cold / copy_peak["GBps"] if copy_peak else None,
+                    "frac_of_read_peak": gb_cold / rpeak["GBps"] if rpeak else None,
                     "flush": f"{2 * fa.numel() * 4 >> 20} MiB copied on the same stream before every step, outside "
                              f"the step's events (evicts the 256 MB Infinity Cache and the L2s)"}
         kv.close()
@@ -427,8 +452,12 @@ def decode_bench(dsa, torch, w, args, stream, steps, warmup, samp=None, flush=No
         "achieved_GBps": gbps,
         "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
         "frac_of_copy_peak": gbps / copy_peak["GBps"] if copy_peak else None,
+        "frac_of_read_peak": gbps / rpeak["GBps"] if rpeak else None,
+        "step_us": {"mean": float(np.mean(per)), "median": float(np.median(per)), "min": float(np.min(per)),
+                    "n": len(per), "how": "events around each step on the library's stream"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "frac_of_read_peak": achieved / rpeak["GBps"] if rpeak else None,
                      "us_per_launch": dk["us_per_launch"], "bytes_per_launch": dk["bytes_per_launch"]},
         "kernels_us_per_step": {n: round(v["us_per_step"], 2) for n, v in kern.items()},
         "traffic_note": traffic_note,
@@ -547,15 +576,18 @@ def main():
         st_, sk_, sp_ = args.sample.split(",")
         samp = (float(st_), int(sk_), float(sp_))
     flush, copy_peak = (None, None) if args.no_cold else flush_and_copy_peak(torch, stream, args.flush_mib)
-    out = decode_bench(dsa, torch, w, args, stream, args.steps, args.warmup, samp, flush, copy_peak)
+    rpeak = read_peak(dsa, torch, stream, flush[2]) if flush else None
+    out = decode_bench(dsa, torch, w, args, stream, args.steps, args.warmup, samp, flush, copy_peak, rpeak)
     if copy_peak:
         out["copy_peak"] = copy_peak
+    if rpeak:
+        out["read_peak"] = rpeak
     if (args.workload == "llama135m_p5" and not args.no_b64 and not samp):
         # BASELINE's metric names both batch sizes of the 135M shape: the
         # batch-64 ragged decode rides along as a nested record
         w64 = variant(synth.WORKLOADS["llama135m_b64"])
         out["b64"] = decode_bench(dsa, torch, w64, args, stream, max(args.steps // 16, 16), max(args.warmup, 16),
-                                  None, flush, copy_peak)
+                                  None, flush, copy_peak, rpeak)
     if copy_cal:
         out["copy_calibration"] = copy_cal
     if not args.no_cpu_baseline:

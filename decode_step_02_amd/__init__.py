@@ -78,6 +78,7 @@ _SIGS = {
     "ds_sample_noalloc": (C.c_int, [_P, C.c_int32, C.c_int32, _P, C.c_float, C.c_int32, C.c_float, _P, _P]),
     "ds_set_dispatch": (C.c_int, [_P, C.c_int32]),
     "ds_bench_kernel": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, _P]),
+    "ds_bench_stream": (C.c_int, [_P, C.c_size_t, _P, C.c_int32, _P]),
     "ds_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -210,6 +211,13 @@ def ds_sample_noalloc(d_logits, B: int, V: int, d_uniform, temperature, top_k, t
 
 def ds_bench_kernel(model, kv, which, layer, reps, stream=None):
     _check(_lib.ds_bench_kernel(model, kv, which, layer, reps, _stream(stream)))
+
+
+def ds_bench_stream(d_src, d_out, reps=1, stream=None):
+    """Diagnostic streaming read of the whole tensor d_src (d_out: device
+    int32/uint32 tensor of at least 2048 elements)."""
+    _check(_lib.ds_bench_stream(_ptr(d_src), d_src.numel() * d_src.element_size(), _ptr(d_out), int(reps),
+                                _stream(stream)))
 
 
 def ds_model_destroy(model):

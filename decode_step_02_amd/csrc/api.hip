@@ -812,6 +812,16 @@ ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t lay
     return ok();
 }
 
+ds_status ds_bench_stream(const void* d_src, size_t bytes, uint32_t* d_out, int32_t reps, void* stream) {
+    if (!d_src || !d_out) return fail(DS_ERR_INVALID_ARG, "NULL argument");
+    if (!aligned(d_src, 16) || !aligned(d_out, 4)) return fail(DS_ERR_ALIGNMENT, "source must be 16-byte aligned");
+    if (bytes == 0 || bytes % 16) return fail(DS_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+    if (reps < 1) return fail(DS_ERR_INVALID_ARG, "reps must be positive");
+    hipError_t e = ds::enqueue_stream_read(d_src, bytes, d_out, reps, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "bench stream");
+    return ok();
+}
+
 ds_status ds_logits(const ds_kv* kv, float* d_out, void* stream) {
     if (!kv || !d_out) return fail(DS_ERR_INVALID_ARG, "NULL argument");
     hipError_t e = hipMemcpyAsync(d_out, kv->s.logits, sizeof(float) * kv->B * static_cast<size_t>(kv->s.V),

@@ -116,6 +116,11 @@ struct BeginList {
 // Copies rows [0, n) of every (layer, k/v, group) of slot src_slot of one
 // (L, 2, Bs, Hkv, Ts, D) cache to slots dst_first .. dst_first + count - 1
 // of another (L, 2, Bd, Hkv, Td, D) cache (it may be the same one).
+// Diagnostic streaming read of `bytes` (a multiple of 16) from src, reps
+// times; out receives kStreamBlocks words.
+constexpr int kStreamBlocks = 2048;
+hipError_t enqueue_stream_read(const void* src, size_t bytes, uint32_t* out, int reps, hipStream_t st);
+
 hipError_t enqueue_replicate(float* dst, int Bd, int Td, const float* src, int Bs, int Ts, int L, int Hkv, int D,
                              int src_slot, int dst_first, int count, int n, hipStream_t st);
 

@@ -1502,6 +1502,48 @@ static hipError_t launch_attn(const StepArgs& s, int layer, int n_items, hipStre
 
 static bool use_mm(const StepArgs& s, int n_items) { return s.mm_ok && n_items >= kMmMin; }
 
+// ---- diagnostic: a plain streaming read --------------------------------------------------------
+// Reads n16 16-byte words once: block b streams its own contiguous segment,
+// each round 256 threads x 8 coalesced 16-byte loads (32 KiB) issued before
+// any is used; then one xor of everything it read per block goes to out (so
+// the loads are live).  Its rate is the read bandwidth the chip gives a
+// kernel that does nothing else.
+__global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ src, size_t n16,
+                                                     uint32_t* __restrict__ out) {
+    constexpr int U = 8;
+    __shared__ uint32_t red[4];
+    const size_t seg = (n16 + gridDim.x - 1) / gridDim.x;
+    const size_t lo = static_cast<size_t>(blockIdx.x) * seg;
+    const size_t hi = lo + seg < n16 ? lo + seg : n16;
+    uint32_t acc = 0;
+    size_t i = lo + threadIdx.x;
+    for (; i + (U - 1) * 256 < hi; i += U * 256) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) v[u] = src[i + u * 256];
+#pragma unroll
+        for (int u = 0; u < U; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < hi; i += 256) {
+        const uint4 a = src[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    for (int o = 32; o > 0; o >>= 1) acc ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc), o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+hipError_t enqueue_stream_read(const void* src, size_t bytes, uint32_t* out, int reps, hipStream_t st) {
+    for (int r = 0; r < reps; r++) {
+        hipLaunchKernelGGL(k_stream_read, dim3(kStreamBlocks), dim3(256), 0, st, static_cast<const uint4*>(src),
+                           bytes / 16, out);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t enqueue_replicate(float* dst, int Bd, int Td, const float* src, int Bs, int Ts, int L, int Hkv, int D,
                              int src_slot, int dst_first, int count, int n, hipStream_t st) {
     if (count <= 0 || n <= 0) return hipSuccess;

@@ -357,6 +357,16 @@ ds_status ds_set_dispatch(ds_kv* kv, int32_t mode);
 ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t layer, int32_t reps,
                           void* stream);
 
+/* Diagnostics: enqueues `reps` launches of a plain streaming read of
+ * `bytes` (a positive multiple of 16) from device memory d_src (16-byte
+ * aligned): coalesced 16-byte loads, each byte read once per launch, and one
+ * 32-bit word per block written to d_out (device, at least 2048 words, owned
+ * by the caller).  Its time per launch, with events on `stream`, gives the
+ * read bandwidth a kernel that does nothing else reaches: the measured peak
+ * that streaming kernels are compared with.  Errors: DS_ERR_INVALID_ARG,
+ * DS_ERR_ALIGNMENT, DS_ERR_HIP. */
+ds_status ds_bench_stream(const void* d_src, size_t bytes, uint32_t* d_out, int32_t reps, void* stream);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* ds_last_error(void);
 
