@@ -147,7 +147,7 @@ struct RowStream {
     const void* W;
     const float* S;  // Q8: the row's block scales
     size_t base;
-    int nch, sub;
+    int nch, nall, sub;
 
     // Loads are unconditional (the chunk index is clamped into the row, the
     // value masked afterwards): a guarded load becomes a branch, and the
@@ -158,6 +158,7 @@ struct RowStream {
         base = row * static_cast<size_t>(K);
         sub = sub_;
         nch = valid ? K / EPC : 0;
+        nall = K / EPC;
         const int last = K / EPC - 1;
         if constexpr (Q8) S = q_scales<WDT>(W_, rows, K) + row * static_cast<size_t>(K / 32);
 #pragma unroll
@@ -208,6 +209,43 @@ struct RowStream {
             a1 = chunk(u3, s3, xs + (c + 3 * G) * EPC, a1);
         }
         for (; c < nch; c += G) a0 = chunk(Wt<WDT>::load(W, base + static_cast<size_t>(c) * EPC), scale_of(c), xs + c * EPC, a0);
+        return group_sum<G>(a0 + a1);
+    }
+
+    // finish() with a rolling pipeline: slot p holds chunk j0 + p of this
+    // lane; once used it is refilled with chunk j0 + p + kPrefetch, so
+    // kPrefetch loads stay in flight down the whole row (finish() waits for
+    // each batch of four before issuing the next).  Chunks past the lane's
+    // own are loaded clamped and left out of the sum; the loop count is the
+    // same for every lane.  Taken by W2, the longest rows (the 8B shape's
+    // 14336: 24.5 against 25.7 us per launch); the two-stream W1/W3 would
+    // hold too many registers, and Wo's 4096-long rows gained nothing.
+    __device__ __forceinline__ float finish_roll(const float* xs) {
+        float a0 = 0.f, a1 = 0.f;
+        const int ntot = nch > 0 ? nch : 1;  // masked lanes still walk (clamped, discarded)
+        const int last = ntot - 1;
+        const int nj = (nall + G - 1) / G;    // chunks of the group's lane 0, the most of any lane
+        int j0 = 0;
+        for (; j0 + kPrefetch < nj; j0 += kPrefetch) {
+#pragma unroll
+            for (int p = 0; p < kPrefetch; p++) {
+                const int c = sub + (j0 + p) * G;
+                const float* xc = xs + min(c, last) * EPC;
+                float& a = (p & 1) ? a1 : a0;
+                const float v = chunk(w[p], sc[Q8 ? p : 0], xc, a);
+                a = c < nch ? v : a;
+                const int cn = min(c + kPrefetch * G, last);
+                w[p] = Wt<WDT>::load(W, base + static_cast<size_t>(cn) * EPC);
+                if constexpr (Q8) sc[p] = S[(cn * EPC) >> 5];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < kPrefetch; p++) {
+            const int c = sub + (j0 + p) * G;
+            float& a = (p & 1) ? a1 : a0;
+            const float v = chunk(w[p], sc[Q8 ? p : 0], xs + min(c, last) * EPC, a);
+            a = c < nch ? v : a;
+        }
         return group_sum<G>(a0 + a1);
     }
 };
@@ -270,19 +308,18 @@ struct VecStage {
             const int j = threadIdx.x + u * NT;
             if (j < n4) put(xv[u], gv[GAIN ? u : 0], j);
         }
-        for (int base = threadIdx.x + U * NT; base < n4; base += U * NT) {
+        for (int base = threadIdx.x + U * NT; base < n4; base += U * NT) {  // as in complete_copy
+            float4 t[U], tg[U];
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                const int j = base + u * NT;
-                if (j < n4) {
-                    xv[u] = x4[j];
-                    gv[GAIN ? u : 0] = g4[j];
-                }
+                const int j = min(base + u * NT, n4 - 1);
+                t[u] = x4[j];
+                tg[u] = GAIN ? g4[j] : make_float4(1.f, 1.f, 1.f, 1.f);
             }
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int j = base + u * NT;
-                if (j < n4) put(xv[u], gv[GAIN ? u : 0], j);
+                if (j < n4) put(t[u], tg[u], j);
             }
         }
         ss = block_sum<WAVES>(ss, red);
@@ -301,13 +338,16 @@ struct VecStage {
             const int j = threadIdx.x + u * NT;
             if (j < n4) s4[j] = xv[u];
         }
+        // later rounds load into a local array, unconditionally (clamped):
+        // guarded writes into xv keep it out of registers, in scratch memory,
+        // with every load waited for before the next is issued
         for (int base = threadIdx.x + U * NT; base < n4; base += U * NT) {
+            float4 t[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) t[u] = x4[min(base + u * NT, n4 - 1)];
 #pragma unroll
             for (int u = 0; u < U; u++)
-                if (base + u * NT < n4) xv[u] = x4[base + u * NT];
-#pragma unroll
-            for (int u = 0; u < U; u++)
-                if (base + u * NT < n4) s4[base + u * NT] = xv[u];
+                if (base + u * NT < n4) s4[base + u * NT] = t[u];
         }
         __syncthreads();
     }
@@ -1229,7 +1269,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w2(StepArgs s, LayerW w) {
     VecStage<64 * WAVES, 8, false> vs;
     vs.issue(s.h + static_cast<size_t>(item) * s.F, nullptr, s.F);
     vs.complete_copy(xs);
-    const float y = st.finish(xs);
+    const float y = st.finish_roll(xs);
     if (valid && sub == 0) *xr = x_old + y;
 }
 
