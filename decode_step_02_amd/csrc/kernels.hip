@@ -18,9 +18,9 @@
 // covers R = 64/G output rows with G lanes per row.  Lane (r, sub) streams
 // 16-byte chunks sub, sub+G, sub+2G, ... of its row, so the G lanes of a row
 // read G*16 contiguous bytes per load and a wave issues 64 fully used 16-byte
-// loads per instruction.  The first kPrefetch chunks of every lane are loaded
-// into registers before the block stages its activation vector, so the
-// weight stream is in flight while the RMSNorm prologue runs.  bf16 chunks
+// loads per instruction.  The first 12 or 16 chunks of every lane are in
+// flight while the block stages its activation vector, so the weight stream
+// overlaps the RMSNorm prologue.  bf16 chunks
 // are widened in registers by a 16-bit shift ("GOTOken: An Inference Engine
 // in QBasic", section "Loading the model and tokenizer") and accumulated in
 // fp32 against the LDS copy of the activation vector; the G partial sums of
@@ -35,7 +35,7 @@
 
 namespace ds {
 
-constexpr int kPrefetch = 12;  // 16-byte chunks per lane loaded before the prologue
+constexpr int kPrefetch = 12;  // 16-byte chunks per lane loaded before the prologue (16 for 32-lane rows)
 
 // ---- weight chunks ---------------------------------------------------------------
 
@@ -135,15 +135,20 @@ template <> struct Wt<kF32> {
     }
 };
 
-// One lane's share of one row: the first kPrefetch chunks are loaded by
+// One lane's share of one row: the first PF chunks are loaded by
 // start(), the rest while finish() accumulates.  finish() returns the full
 // row dot product in every lane of the row's G-lane group.
 template <int WDT, int G>
 struct RowStream {
     static constexpr int EPC = Wt<WDT>::EPC;
     static constexpr bool Q8 = WDT == kQ8 || WDT == kQ4;  // block scales (Q8 or Q4)
-    uint4 w[kPrefetch];
-    float sc[Q8 ? kPrefetch : 1];  // Q8: the block scale of each prefetched chunk
+    // chunks in flight per lane: 16 where 32 lanes share a row of bf16 or
+    // fp32 weights (rows of 512 and more chunks), which is a whole 4096-long
+    // bf16 row -- one memory round trip -- and those launches have few waves
+    // per SIMD to hide it (the block-scaled types would spill)
+    static constexpr int PF = (G >= 32 && !Q8) ? 16 : kPrefetch;
+    uint4 w[PF];
+    float sc[Q8 ? PF : 1];  // Q8: the block scale of each prefetched chunk
     const void* W;
     const float* S;  // Q8: the row's block scales
     size_t base;
@@ -162,13 +167,13 @@ struct RowStream {
         const int last = K / EPC - 1;
         if constexpr (Q8) S = q_scales<WDT>(W_, rows, K) + row * static_cast<size_t>(K / 32);
 #pragma unroll
-        for (int p = 0; p < kPrefetch; p++) {
+        for (int p = 0; p < PF; p++) {
             const int c = sub + p * G;
             w[p] = Wt<WDT>::load(W, base + static_cast<size_t>(min(c, last)) * EPC);
             if constexpr (Q8) sc[p] = S[(min(c, last) * EPC) >> 5];
         }
 #pragma unroll
-        for (int p = 0; p < kPrefetch; p++) {
+        for (int p = 0; p < PF; p++) {
             const bool keep = sub + p * G < nch;
             w[p].x = keep ? w[p].x : 0u;
             w[p].y = keep ? w[p].y : 0u;
@@ -191,12 +196,12 @@ struct RowStream {
         float a0 = 0.f, a1 = 0.f;
         const int last = nch > 0 ? nch - 1 : 0;
 #pragma unroll
-        for (int p = 0; p < kPrefetch; p += 2) {
+        for (int p = 0; p < PF; p += 2) {
             // masked chunks are zero; the LDS index is clamped so it stays in range
             a0 = chunk(w[p], sc[Q8 ? p : 0], xs + min(sub + p * G, last) * EPC, a0);
-            if (p + 1 < kPrefetch) a1 = chunk(w[p + 1], sc[Q8 ? p + 1 : 0], xs + min(sub + (p + 1) * G, last) * EPC, a1);
+            if (p + 1 < PF) a1 = chunk(w[p + 1], sc[Q8 ? p + 1 : 0], xs + min(sub + (p + 1) * G, last) * EPC, a1);
         }
-        int c = sub + kPrefetch * G;
+        int c = sub + PF * G;
         for (; c + 3 * G < nch; c += 4 * G) {
             const uint4 u0 = Wt<WDT>::load(W, base + static_cast<size_t>(c) * EPC);
             const uint4 u1 = Wt<WDT>::load(W, base + static_cast<size_t>(c + G) * EPC);
@@ -213,8 +218,8 @@ struct RowStream {
     }
 
     // finish() with a rolling pipeline: slot p holds chunk j0 + p of this
-    // lane; once used it is refilled with chunk j0 + p + kPrefetch, so
-    // kPrefetch loads stay in flight down the whole row (finish() waits for
+    // lane; once used it is refilled with chunk j0 + p + PF, so
+    // PF loads stay in flight down the whole row (finish() waits for
     // each batch of four before issuing the next).  Chunks past the lane's
     // own are loaded clamped and left out of the sum; the loop count is the
     // same for every lane.  Taken by W2, the longest rows (the 8B shape's
@@ -226,21 +231,21 @@ struct RowStream {
         const int last = ntot - 1;
         const int nj = (nall + G - 1) / G;    // chunks of the group's lane 0, the most of any lane
         int j0 = 0;
-        for (; j0 + kPrefetch < nj; j0 += kPrefetch) {
+        for (; j0 + PF < nj; j0 += PF) {
 #pragma unroll
-            for (int p = 0; p < kPrefetch; p++) {
+            for (int p = 0; p < PF; p++) {
                 const int c = sub + (j0 + p) * G;
                 const float* xc = xs + min(c, last) * EPC;
                 float& a = (p & 1) ? a1 : a0;
                 const float v = chunk(w[p], sc[Q8 ? p : 0], xc, a);
                 a = c < nch ? v : a;
-                const int cn = min(c + kPrefetch * G, last);
+                const int cn = min(c + PF * G, last);
                 w[p] = Wt<WDT>::load(W, base + static_cast<size_t>(cn) * EPC);
                 if constexpr (Q8) sc[p] = S[(cn * EPC) >> 5];
             }
         }
 #pragma unroll
-        for (int p = 0; p < kPrefetch; p++) {
+        for (int p = 0; p < PF; p++) {
             const int c = sub + (j0 + p) * G;
             float& a = (p & 1) ? a1 : a0;
             const float v = chunk(w[p], sc[Q8 ? p : 0], xs + min(c, last) * EPC, a);
@@ -267,8 +272,9 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 // Two-phase staging of an n-float activation vector (n % 4 == 0) into LDS.
 // issue() starts the first round of independent 16-byte loads (and of the
-// matching gains when GAIN), so the caller can put other loads in flight
-// before complete_*() waits; vectors longer than U*NT float4 take further
+// matching gains when GAIN); the caller then puts its weight loads in flight
+// before complete_*() waits, which waits for the vector alone because loads
+// complete in issue order.  Vectors longer than U*NT float4 take further
 // rounds inside complete_*().
 template <int NT, int U, bool GAIN>
 struct VecStage {
@@ -296,17 +302,22 @@ struct VecStage {
     __device__ __forceinline__ void complete_rms(float* xs, float* red, int n, float eps) {
         float4* s4 = reinterpret_cast<float4*>(xs);
         float ss = 0.f;
-        auto put = [&](const float4 v, const float4 gg, int j) {
-            ss = fmaf(v.x, v.x, ss);
-            ss = fmaf(v.y, v.y, ss);
-            ss = fmaf(v.z, v.z, ss);
-            ss = fmaf(v.w, v.w, ss);
+        auto put = [&](const float4 v, const float4 gg, int j, bool in) {
+            float t = 0.f;
+            t = fmaf(v.x, v.x, t);
+            t = fmaf(v.y, v.y, t);
+            t = fmaf(v.z, v.z, t);
+            t = fmaf(v.w, v.w, t);
+            ss += in ? t : 0.f;
             s4[j] = make_float4(gg.x * v.x, gg.y * v.y, gg.z * v.z, gg.w * v.w);
         };
+        // Stores past n4 go to the last element with its own value (the loads
+        // were clamped the same way), so no branch: a guarded store lets the
+        // compiler sink its load into the branch and wait for it there.
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int j = threadIdx.x + u * NT;
-            if (j < n4) put(xv[u], gv[GAIN ? u : 0], j);
+            put(xv[u], gv[GAIN ? u : 0], min(j, n4 - 1), j < n4);
         }
         for (int base = threadIdx.x + U * NT; base < n4; base += U * NT) {  // as in complete_copy
             float4 t[U], tg[U];
@@ -319,7 +330,7 @@ struct VecStage {
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int j = base + u * NT;
-                if (j < n4) put(t[u], tg[u], j);
+                put(t[u], tg[u], min(j, n4 - 1), j < n4);
             }
         }
         ss = block_sum<WAVES>(ss, red);
@@ -334,10 +345,7 @@ struct VecStage {
     __device__ __forceinline__ void complete_copy(float* xs) {
         float4* s4 = reinterpret_cast<float4*>(xs);
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int j = threadIdx.x + u * NT;
-            if (j < n4) s4[j] = xv[u];
-        }
+        for (int u = 0; u < U; u++) s4[min(static_cast<int>(threadIdx.x) + u * NT, n4 - 1)] = xv[u];  // as in complete_rms
         // later rounds load into a local array, unconditionally (clamped):
         // guarded writes into xv keep it out of registers, in scratch memory,
         // with every load waited for before the next is issued
@@ -346,8 +354,7 @@ struct VecStage {
 #pragma unroll
             for (int u = 0; u < U; u++) t[u] = x4[min(base + u * NT, n4 - 1)];
 #pragma unroll
-            for (int u = 0; u < U; u++)
-                if (base + u * NT < n4) s4[base + u * NT] = t[u];
+            for (int u = 0; u < U; u++) s4[min(base + u * NT, n4 - 1)] = t[u];
         }
         __syncthreads();
     }
@@ -431,10 +438,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(StepArgs s, LayerW w, int la
         row = valid ? (task - nq - nk) * R + rs : 0;
         W = w.wv;
     }
-    RowStream<WDT, G> st;
-    st.start(W, row, s.d, sub, valid, static_cast<size_t>(is_q ? s.H : s.Hkv) * D);
+    // the vector's loads go first: loads complete in issue order, so the
+    // staging then waits for them alone, not for the weight chunks
     VecStage<64 * WAVES, 4, true> vs;
     vs.issue(s.x + static_cast<size_t>(item) * s.d, w.attn_norm, s.d);
+    RowStream<WDT, G> st;
+    st.start(W, row, s.d, sub, valid, static_cast<size_t>(is_q ? s.H : s.Hkv) * D);
     float c = 1.f, sn = 0.f;
     if (roped && valid) {
         c = s.rope_cos[static_cast<size_t>(pos) * half_d + i];
@@ -1210,19 +1219,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_wo(StepArgs s, LayerW w, int lay
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.d;
+    VecStage<64 * WAVES, 8, false> vs;
+    if constexpr (!SHORT) vs.issue(s.o + static_cast<size_t>(item) * K, nullptr, K);  // first, as in k_qkv
     RowStream<WDT, G> st;
     st.start(w.wo, valid ? row : 0, K, sub, valid, s.d);
     float* xr = s.x + static_cast<size_t>(item) * s.d + row;
     const float x_old = (valid && sub == 0) ? *xr : 0.f;
-    if (SHORT) {
+    if constexpr (SHORT) {
         if (n > nload) {  // the host picks nload >= every context; guard anyway
             if (threadIdx.x == 0) atomicOr(s.err, 2);
             n = nload;
         }
         attention_short<WAVES>(s, layer, item, slot, n, nload, xs, xs + K);
     } else {
-        VecStage<64 * WAVES, 8, false> vs;
-        vs.issue(s.o + static_cast<size_t>(item) * K, nullptr, K);
         vs.complete_copy(xs);
     }
     const float y = st.finish(xs);
@@ -1239,11 +1248,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_w13(StepArgs s, LayerW w) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.F;
+    VecStage<64 * WAVES, 4, true> vs;
+    vs.issue(s.x + static_cast<size_t>(item) * s.d, w.ffn_norm, s.d);  // first, as in k_qkv
     RowStream<WDT, G> s1, s3;
     s1.start(w.w1, valid ? row : 0, s.d, sub, valid, s.F);
     s3.start(w.w3, valid ? row : 0, s.d, sub, valid, s.F);
-    VecStage<64 * WAVES, 4, true> vs;
-    vs.issue(s.x + static_cast<size_t>(item) * s.d, w.ffn_norm, s.d);
     vs.template complete_rms<WAVES>(xs, red, s.d, s.eps);
     const float a = s1.finish(xs);
     const float u = s3.finish(xs);
@@ -1262,12 +1271,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_w2(StepArgs s, LayerW w) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.d;
+    VecStage<64 * WAVES, 8, false> vs;
+    vs.issue(s.h + static_cast<size_t>(item) * s.F, nullptr, s.F);  // first, as in k_qkv
     RowStream<WDT, G> st;
     st.start(w.w2, valid ? row : 0, s.F, sub, valid, s.d);
     float* xr = s.x + static_cast<size_t>(item) * s.d + row;
     const float x_old = (valid && sub == 0) ? *xr : 0.f;
-    VecStage<64 * WAVES, 8, false> vs;
-    vs.issue(s.h + static_cast<size_t>(item) * s.F, nullptr, s.F);
     vs.complete_copy(xs);
     const float y = st.finish_roll(xs);
     if (valid && sub == 0) *xr = x_old + y;
@@ -1287,10 +1296,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_logits(StepArgs s, const float* 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.V;
+    VecStage<64 * WAVES, 4, true> vs;
+    vs.issue(s.x + static_cast<size_t>(item) * s.d, out_norm, s.d);  // first, as in k_qkv
     RowStream<WDT, G> st;
     st.start(wcls, valid ? row : 0, s.d, sub, valid, s.V);
-    VecStage<64 * WAVES, 4, true> vs;
-    vs.issue(s.x + static_cast<size_t>(item) * s.d, out_norm, s.d);
     vs.template complete_rms<WAVES>(xs, red, s.d, s.eps);
     if (!flag) return;
     const float y = st.finish(xs);
