@@ -1181,7 +1181,56 @@ __global__ __launch_bounds__(256) void k_attn_combine(StepArgs s) {
     }
 }
 
+// The same merge for contexts of at most kMergeChunks chunks and head_dim
+// 64 or 128: one wave per (item, head), lane e holding dims e and e + 64.
+// Every chunk slot up to kMergeChunks is loaded without waiting for the
+// item's position (slots past its chunk count hold stale values and are left
+// out by selects, not arithmetic), so the merge is one memory round trip,
+// with no LDS and no barrier.
+constexpr int kMergeChunks = 16;
+template <int D>
+__global__ __launch_bounds__(64) void k_attn_merge(StepArgs s) {
+    constexpr int DPL = D / 64;
+    const int pair = blockIdx.x, item = pair / s.H, lane = threadIdx.x;
+    const int S = s.n_chunks;
+    const size_t base = static_cast<size_t>(pair) * S;  // (item * H + h) * S
+    const float2* ml = reinterpret_cast<const float2*>(s.part_ml) + base;
+    const float* po = s.part_o + base * D + lane;
+    float2 v[kMergeChunks];
+    float o[kMergeChunks][DPL];
+#pragma unroll
+    for (int c = 0; c < kMergeChunks; c++) {
+        const int cc = min(c, S - 1);
+        v[c] = ml[cc];
+#pragma unroll
+        for (int k = 0; k < DPL; k++) o[c][k] = po[static_cast<size_t>(cc) * D + 64 * k];
+    }
+    const int ns = (s.pos[item] + kChunk) / kChunk;  // chunks of this item's n = pos + 1 positions
+    float M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMergeChunks; c++) M = c < ns ? fmaxf(M, v[c].x) : M;
+    float L = 0.f, acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; k++) acc[k] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMergeChunks; c++) {
+        const float wv = c < ns ? __expf(v[c].x - M) : 0.f;
+        L = c < ns ? fmaf(wv, v[c].y, L) : L;
+#pragma unroll
+        for (int k = 0; k < DPL; k++) acc[k] = c < ns ? fmaf(wv, o[c][k], acc[k]) : acc[k];
+    }
+    float* out = s.o + static_cast<size_t>(pair) * D + lane;
+#pragma unroll
+    for (int k = 0; k < DPL; k++) out[64 * k] = acc[k] / L;
+}
+
 static hipError_t launch_combine(const StepArgs& s, int n_items, hipStream_t st) {
+    if (s.n_chunks <= kMergeChunks && (s.D == 64 || s.D == 128)) {
+        const dim3 grid(s.H * n_items);
+        if (s.D == 64) hipLaunchKernelGGL(k_attn_merge<64>, grid, dim3(64), 0, st, s);
+        else hipLaunchKernelGGL(k_attn_merge<128>, grid, dim3(64), 0, st, s);
+        return hipGetLastError();
+    }
     const int split = s.H * n_items < 128 && s.D >= 128 ? 4 : 1;  // few heads: each head's dims over 4 blocks
     const int Dh = s.D / split;
     const int per = (s.n_chunks + 256 / Dh - 1) / (256 / Dh);  // chunks per thread, all in one batch if it fits
