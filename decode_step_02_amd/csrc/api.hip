@@ -625,7 +625,7 @@ ds_status ds_prefill(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_t
         if (kv->B == 1 && ctx <= kv->persist_ctx) {
             // the same kernel as a batch-1 decode step at this position, so a
             // prompt re-fed through prefill reproduces decoded steps bit for bit
-            e = ds::enqueue_persist(kv->s, kv->pa, nullptr, h_tokens[j], j == n - 1 ? d_tok_out : nullptr, st);
+            e = ds::enqueue_persist(kv->s, kv->pa, nullptr, h_tokens[j], j == n - 1 ? d_tok_out : nullptr, ctx, st);
         } else {
             const int nload = ds::short_rows(kv->s, ctx);
             e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, nullptr, 1, j == n - 1, nload, d_tok_out, st);
@@ -743,7 +743,7 @@ ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, in
     const bool persist = kv->B == 1 && max_ctx <= kv->persist_ctx;
     const int nload = persist ? -1 : ds::short_rows(kv->s, max_ctx);  // -1 marks the persistent step
     auto enqueue = [&]() -> hipError_t {
-        if (persist) return ds::enqueue_persist(kv->s, kv->pa, d_tok_in, 0, d_tok_out, st);
+        if (persist) return ds::enqueue_persist(kv->s, kv->pa, d_tok_in, 0, d_tok_out, max_ctx, st);
         return ds::enqueue_step(kv->s, model->ptrs, &list, 1, d_tok_in, kv->B, true, nload, d_tok_out, st);
     };
     hipError_t e = hipSuccess;
@@ -795,7 +795,7 @@ ds_status ds_bench_kernel(ds_model* model, ds_kv* kv, int32_t which, int32_t lay
         if (kv->B != 1 || kv->mirror[0] + 1 > kv->persist_ctx)
             return fail(DS_ERR_STATE, "the handoff floor needs a batch-1 cache whose next step is a single launch");
         for (int r = 0; r < reps; r++) {
-            hipError_t e = ds::enqueue_persist_floor(kv->s, kv->pa, st);
+            hipError_t e = ds::enqueue_persist_floor(kv->s, kv->pa, kv->mirror[0] + 1, st);
             if (e != hipSuccess) return hip_fail(e, "bench floor");
         }
         return ok();

@@ -19,6 +19,7 @@ constexpr int kMaxD = 256;       // head_dim limit of the attention kernels
 constexpr int kMaxItems = 64;    // items per k_begin launch
 constexpr int kSetChunk = 128;   // lengths per k_set_lengths launch
 constexpr int kMaxArgmaxBlocks = 16384;  // vocabulary blocks per item (argmax partials)
+constexpr int kPChunk = 32;      // positions per attention chunk of the persistent step
 constexpr int kPMaxChunks = 64;  // 32-position attention chunks the persistent step can hold per head
 constexpr int kPMaxParts = kPMaxChunks / 4;  // their partials, one per four chunks
 constexpr int kPKeyWords = 1024; // argmax words of the persistent step (one per wave)
@@ -170,13 +171,16 @@ size_t persist_lds();
 bool persist_fits_device(const StepArgs& s);  // all workgroups of the single launch can be resident
 hipError_t persist_prepare(const StepArgs& s);
 // One step of sequence 0 (B == 1): the token comes from d_tok_in[0], or from
-// tok_value when d_tok_in is NULL; d_tok_out may be NULL.
+// tok_value when d_tok_in is NULL; d_tok_out may be NULL.  ctx = the step's
+// context (position + 1) picks the instantiation: one chunk (attention in
+// the Wo blocks) or more (attention partials); a launch whose device
+// context is of the other class flags error bit 2 and does nothing.
 hipError_t enqueue_persist(const StepArgs& s, const PersistArgs& p, const int32_t* d_tok_in, int tok_value,
-                           int32_t* d_tok_out, hipStream_t st);
+                           int32_t* d_tok_out, int ctx, hipStream_t st);
 // The handoff floor of the single launch: the same phases and handoff words
 // with no weight or cache loads and nothing stored outside the handoff words
 // (no cache rows, logits, token or lengths).  Diagnostic only.
-hipError_t enqueue_persist_floor(const StepArgs& s, const PersistArgs& p, hipStream_t st);
+hipError_t enqueue_persist_floor(const StepArgs& s, const PersistArgs& p, int ctx, hipStream_t st);
 // MFMA projections (mfma.hip): which = 0 qkv, 1 wo, 2 w13, 3 w2, 4 logits.
 bool mm_supported(const StepArgs& s);
 int mm_logits_blocks(const StepArgs& s);

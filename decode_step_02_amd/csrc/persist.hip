@@ -52,7 +52,6 @@ constexpr int kPRed = kPGains - 16;           // block-reduction slots; the role
 constexpr int kPNorm = 4;                     // normalised elements per thread (d <= 1024)
 constexpr long kPSpin = 1 << 20;              // poll rounds before a wait gives up
 constexpr int kPhases = 5;                    // epochs per layer
-constexpr int kPChunk = 32;                   // positions per attention task
 constexpr int kPSample = 16;                  // words a throttle wait samples (fewer loads on the hot lines)
 
 static_assert(kPWaves == kPKeyWords, "one argmax word per wave");
@@ -538,11 +537,15 @@ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 // IN: how row-product inputs are held (kF32, or kBF16 hi/lo pairs; see
 // put_pair).  FLOOR: the handoff-floor diagnostic -- the same phases and LL
 // words with no weight or cache loads and no stores outside the LL words.
+// LONG: contexts of more than one chunk (role 1 partials, merged in role
+// 2); otherwise one chunk, attention recomputed in the Wo blocks.  Each
+// instantiation holds only its own path, so neither pays the other's
+// registers.
 template <int WDT_, int PD_, int REP_, int GD_, int NCD_, int GH_, int NCH_, int GF_, int NCF_, int IN_ = WDT_,
-          bool FLOOR_ = false>
+          bool FLOOR_ = false, bool LONG_ = false>
 struct PCfg {
     static constexpr int WDT = WDT_, PD = PD_, REP = REP_, IN = IN_;
-    static constexpr bool FLOOR = FLOOR_;
+    static constexpr bool FLOOR = FLOOR_, LONG = LONG_;
     static constexpr int GD = GD_, NCD = NCD_, GH = GH_, NCH = NCH_, GF = GF_, NCF = NCF_;
     // replicas of each published vector: lane `sub` of a row writes replica `sub`
     static constexpr int LLR = cmin(cmin(GD, GH), cmin(GF, kPRep));
@@ -937,7 +940,7 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     const bool attn_wave = wv < s.Hkv;  // wave g handles key/value group g
     const int g = attn_wave ? wv : 0;
     // LDS: [Q/K/V words | partials] [o: H*D] [residual rows: 4R] [softmax weights: 4][REP][32]
-    const int in_n = c.fused ? HD + 2 * KVD : c.npart * s.H * (PD + 2);
+    const int in_n = !C::LONG ? HD + 2 * KVD : c.npart * s.H * (PD + 2);
     float* in = sm;
     float* o = sm + ((in_n + 3) & ~3);
     float* xr = o + HD;
@@ -945,7 +948,7 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
     PStream<C::WDT, G, C::NCH, C::FLOOR> st;
     KV<PD, REP, C::FLOOR> kv;
     st.start(p.layers[0].wo, valid ? row : 0, HD, sub, valid);
-    if (c.fused && attn_wave) kv.load(s, 0, g, 0, c.pos);
+    if (!C::LONG && attn_wave) kv.load(s, 0, g, 0, c.pos);
     for (int l = 0; l < s.L; l++) {
         __syncthreads();
         Seg rows{p.ll_x, 0, 0u, xr};
@@ -954,23 +957,26 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
         } else {
             rows = Seg{p.ll_x + c.rep + r0, nrows, c.ep(l - 1, 4), xr};
         }
-        if (c.fused) {
+        if constexpr (!C::LONG) {
             wait_sample<2, true>(p.ll_qkv + c.rep, in_n, c.ep(l, 0), c.err);
             block_fetch2<2>(Seg{p.ll_qkv + c.rep, in_n, c.ep(l, 0), in}, rows, c.err);
         } else {
             wait_sample<2, true>(p.ll_part, in_n, c.ep(l, 1), c.err);
-            block_fetch2<4>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
+            // 20 words per thread and round: the partials of a 1024-position
+            // context (8 parts x H x (D + 2) words, 4752 at 135M) arrive in
+            // one memory round trip instead of the three of 2048-word rounds
+            block_fetch<20>(Seg{p.ll_part, in_n, c.ep(l, 1), in}, rows, c.err);
         }
         __syncthreads();
         if (attn_wave) {
-            if (c.fused) {
+            if constexpr (!C::LONG) {
                 kv.attend(in, g, 0, c.pos, pw, [&](int j, int e, float, float lsum, float acc, float acc1) {
                     const float inv = __builtin_amdgcn_rcpf(lsum);  // lsum >= 1 (the max term is exp(0))
                     if ((e & 1) == 0) put_pair<C::IN>(o, HD, (g * REP + j) * PD + e, acc * inv, acc1 * inv);
                 });
             }
         }
-        if (!c.fused) {
+        if constexpr (C::LONG) {
             switch ((c.npart + 3) / 4) {  // partial counts unrolled in fours
                 case 1: merge_parts_t<PD, REP, 4, C::IN>(in, c.npart, s.H, o); break;
                 case 2: merge_parts_t<PD, REP, 8, C::IN>(in, c.npart, s.H, o); break;
@@ -985,7 +991,7 @@ __device__ void role_wo(const StepArgs& s, const PersistArgs& p, const PCtx& c, 
         if (valid && sub < C::LLR) ll_put(p.ll_x2 + sub * p.rstride + row, xr[row - r0] + y, c.ep(l, 2));
         if (l + 1 < s.L) {
             st.start(p.layers[l + 1].wo, valid ? row : 0, HD, sub, valid);
-            if (c.fused && attn_wave) kv.load(s, l + 1, g, 0, c.pos);
+            if (!C::LONG && attn_wave) kv.load(s, l + 1, g, 0, c.pos);
         }
     }
 }
@@ -1087,6 +1093,10 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
     c.nch = (c.n + kPChunk - 1) / kPChunk;
     c.npart = (c.nch + 3) / 4;
     c.fused = c.nch == 1;
+    if (c.fused == C::LONG) {  // launched for the other context class: flag it and do nothing (every block)
+        if (threadIdx.x == 0 && blk == 0) atomicOr(c.err, 2);
+        return;
+    }
     c.rep = (blk % C::LLR) * p.rstride;
     c.tok = d_tok_in ? d_tok_in[0] : tok_value;
     if (c.tok < 0 || c.tok >= s.V) {
@@ -1104,7 +1114,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist(StepArgs s, PersistArg
     if (bt < ro.b[0]) {
         role_qkv<C>(s, p, c, bt, sm);
     } else if ((bt -= ro.b[0]) < ro.b[1]) {
-        role_attn<C>(s, p, c, bt, sm);
+        if constexpr (C::LONG) role_attn<C>(s, p, c, bt, sm);  // no role 1 blocks for one chunk
     } else if ((bt -= ro.b[1]) < ro.b[2]) {
         role_wo<C>(s, p, c, bt, sm);
     } else if ((bt -= ro.b[2]) < ro.b[3]) {
@@ -1213,32 +1223,36 @@ static int pnc(int K, int wdt, int g) { return (K / epc(wdt) + g - 1) / g; }
 // model with bf16 weights and the small fp32 test model.  Other shapes take
 // the per-operation path.
 struct PKernel {
-    int wdt, in, floor, D, rep, gd, ncd, gh, nch, gf, ncf;
+    int wdt, in, floor, long_, D, rep, gd, ncd, gh, nch, gf, ncf;
     const void* fn;
 };
 // The 135M class comes with both product inputs (bf16 hi/lo pairs, and fp32
-// with the weights widened), and every class with its handoff-floor twin.
-using CfgM135 = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12>;
-using CfgM135W = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12, kF32>;
-using CfgM135F = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12, kBF16, true>;
-using CfgM135WF = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12, kF32, true>;
-using CfgTiny = PCfg<kF32, 16, 2, 4, 4, 4, 4, 4, 11>;
-using CfgTinyF = PCfg<kF32, 16, 2, 4, 4, 4, 4, 4, 11, kF32, true>;
+// with the weights widened), and every class with its handoff-floor twin,
+// each for one-chunk and for longer contexts.
+template <int IN, bool FLOOR, bool LONG>
+using CfgM135 = PCfg<kBF16, 64, 3, 8, 9, 8, 9, 16, 12, IN, FLOOR, LONG>;
+template <bool FLOOR, bool LONG>
+using CfgTiny = PCfg<kF32, 16, 2, 4, 4, 4, 4, 4, 11, kF32, FLOOR, LONG>;
 template <class C>
 static constexpr PKernel pk() {
-    return {C::WDT, C::IN, C::FLOOR ? 1 : 0, C::PD, C::REP, C::GD, C::NCD, C::GH, C::NCH, C::GF, C::NCF,
-            reinterpret_cast<const void*>(k_persist<C>)};
+    return {C::WDT, C::IN, C::FLOOR ? 1 : 0, C::LONG ? 1 : 0, C::PD, C::REP, C::GD, C::NCD, C::GH, C::NCH, C::GF,
+            C::NCF, reinterpret_cast<const void*>(k_persist<C>)};
 }
-static const PKernel kPKernels[] = {pk<CfgM135>(), pk<CfgM135W>(), pk<CfgM135F>(), pk<CfgM135WF>(),
-                                    pk<CfgTiny>(), pk<CfgTinyF>()};
+static const PKernel kPKernels[] = {
+    pk<CfgM135<kBF16, false, false>>(), pk<CfgM135<kBF16, false, true>>(), pk<CfgM135<kF32, false, false>>(),
+    pk<CfgM135<kF32, false, true>>(),   pk<CfgM135<kBF16, true, false>>(),  pk<CfgM135<kBF16, true, true>>(),
+    pk<CfgM135<kF32, true, false>>(),   pk<CfgM135<kF32, true, true>>(),    pk<CfgTiny<false, false>>(),
+    pk<CfgTiny<false, true>>(),         pk<CfgTiny<true, false>>(),         pk<CfgTiny<true, true>>()};
 
 // The kernel for this shape, product input (s.pin; fp32 weights always take
-// fp32 inputs) and floor flag, or nullptr.
-static const PKernel* persist_kernel(const StepArgs& s, bool floor = false) {
+// fp32 inputs), floor flag and context class (long: more than one chunk),
+// or nullptr.
+static const PKernel* persist_kernel(const StepArgs& s, bool floor = false, bool long_ = false) {
     if (s.Hkv <= 0 || s.H % s.Hkv) return nullptr;
     const int in = s.wdt == kBF16 ? s.pin : kF32;
     for (const PKernel& k : kPKernels) {
-        if (k.wdt != s.wdt || k.in != in || k.floor != (floor ? 1 : 0) || k.D != s.D || k.rep != s.H / s.Hkv)
+        if (k.wdt != s.wdt || k.in != in || k.floor != (floor ? 1 : 0) || k.long_ != (long_ ? 1 : 0) ||
+            k.D != s.D || k.rep != s.H / s.Hkv)
             continue;
         // every lane's chunks must fit its registers, and every G-lane group must have work
         if (pnc(s.d, s.wdt, k.gd) > k.ncd || pnc(s.H * s.D, s.wdt, k.gh) > k.nch || pnc(s.F, s.wdt, k.gf) > k.ncf)
@@ -1290,23 +1304,31 @@ constexpr int kPFloorLds = 96 * 1024;
 // another stream's work hold CUs.
 bool persist_fits_device(const StepArgs& s) {
     const PKernel* k = persist_kernel(s);
-    if (!k) return false;
+    const PKernel* kl = persist_kernel(s, false, true);
+    if (!k || !kl) return false;
     int dev = 0, ncu = 0, per_cu = 0, coop = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
     if (s.pcoop && (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop))
         return false;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k->fn, kPThreads, persist_lds()) != hipSuccess)
-        return false;
-    return static_cast<long>(per_cu) * ncu >= kPBlocks;
+    for (const PKernel* kk : {k, kl}) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kk->fn, kPThreads, persist_lds()) != hipSuccess)
+            return false;
+        if (static_cast<long>(per_cu) * ncu < kPBlocks) return false;
+    }
+    return true;
 }
 
 hipError_t persist_prepare(const StepArgs& s) {
-    hipError_t e = hipFuncSetAttribute(persist_kernel(s)->fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(persist_lds()));
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute(persist_kernel(s, true)->fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kPFloorLds);
+    hipError_t e = hipSuccess;
+    for (bool long_ : {false, true}) {
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(persist_kernel(s, false, long_)->fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    static_cast<int>(persist_lds()));
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(persist_kernel(s, true, long_)->fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kPFloorLds);
+    }
     return e;
 }
 
@@ -1323,17 +1345,17 @@ static hipError_t launch_persist(const StepArgs& s, const void* fn, void** args,
 }
 
 hipError_t enqueue_persist(const StepArgs& s, const PersistArgs& p, const int32_t* d_tok_in, int tok_value,
-                           int32_t* d_tok_out, hipStream_t st) {
+                           int32_t* d_tok_out, int ctx, hipStream_t st) {
     void* args[] = {const_cast<StepArgs*>(&s), const_cast<PersistArgs*>(&p), &d_tok_in, &tok_value, &d_tok_out};
-    return launch_persist(s, persist_kernel(s)->fn, args, persist_lds(), st);
+    return launch_persist(s, persist_kernel(s, false, ctx > kPChunk)->fn, args, persist_lds(), st);
 }
 
-hipError_t enqueue_persist_floor(const StepArgs& s, const PersistArgs& p, hipStream_t st) {
+hipError_t enqueue_persist_floor(const StepArgs& s, const PersistArgs& p, int ctx, hipStream_t st) {
     const int32_t* tok_in = nullptr;
     int tok_value = 0;
     int32_t* tok_out = nullptr;
     void* args[] = {const_cast<StepArgs*>(&s), const_cast<PersistArgs*>(&p), &tok_in, &tok_value, &tok_out};
-    return launch_persist(s, persist_kernel(s, true)->fn, args, kPFloorLds, st);
+    return launch_persist(s, persist_kernel(s, true, ctx > kPChunk)->fn, args, kPFloorLds, st);
 }
 
 }  // namespace ds

@@ -238,6 +238,12 @@ ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens,
  * stay in the workspace for ds_logits.  A token id outside [0, V) is
  * detected on the device: that sequence reads row 0 and the next
  * ds_kv_cache_check returns DS_ERR_BAD_TOKEN.
+ * A step that the caller captures into a graph replays the launches chosen
+ * for the context at capture: it stays valid while every context stays in
+ * that class (batch 1: one 32-position chunk, or more, within
+ * ds_kv_cache_single_launch_ctx; otherwise the fused short-context rows of
+ * the capture, or split-K).  A replay outside it is reported, not computed
+ * wrong in silence: the next ds_kv_cache_check returns DS_ERR_DEVICE.
  * Errors: DS_ERR_INVALID_ARG (NULL buffers, model/cache mismatch),
  * DS_ERR_ALIGNMENT, DS_ERR_CONTEXT_FULL if any lengths[b] == T, DS_ERR_HIP. */
 ds_status ds_decode_step(ds_model* model, ds_kv* kv, const int32_t* d_tok_in, int32_t* d_tok_out,
