@@ -696,6 +696,29 @@ __global__ __launch_bounds__(256) void k_attn_d(StepArgs s, int layer) {
 // way D/8 dims, read as whole 128-byte lines per row, and qdim() gives the
 // query offsets that match.  The rows come in slots of 8 (one per 8 lanes).
 // Values: D/64 dims per lane; bf16 ones stay packed until used.
+// Loads of cached key/value rows, which a step reads once: with the
+// non-temporal hint they pass through the caches without displacing the
+// weights and activations (B = 64, 135M: 1.412 -> 1.360 ms per step).
+typedef float stream_f4 __attribute__((ext_vector_type(4)));
+typedef float stream_f2 __attribute__((ext_vector_type(2)));
+typedef unsigned int stream_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+    const stream_f4 t = __builtin_nontemporal_load(reinterpret_cast<const stream_f4*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ float2 ld_stream(const float2* p) {
+    const stream_f2 t = __builtin_nontemporal_load(reinterpret_cast<const stream_f2*>(p));
+    return make_float2(t.x, t.y);
+}
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+    const stream_u4 t = __builtin_nontemporal_load(reinterpret_cast<const stream_u4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+    return __builtin_nontemporal_load(p);
+}
+
 template <int D, int CDT, int RPW> struct KVRows;
 template <int D, int RPW> struct KVRows<D, kF32, RPW> {
     static constexpr int KF = D / 32, DPL = D / 64, NSL = RPW / 8;
@@ -707,15 +730,15 @@ template <int D, int RPW> struct KVRows<D, kF32, RPW> {
 #pragma unroll
         for (int sl = 0; sl < NSL; sl++) {
 #pragma unroll
-            for (int f = 0; f < KF; f++) k[sl][f] = *reinterpret_cast<const float4*>(Kb + rows[sl] * D + f * 32 + kq * 4);
+            for (int f = 0; f < KF; f++) k[sl][f] = ld_stream(reinterpret_cast<const float4*>(Kb + rows[sl] * D + f * 32 + kq * 4));
         }
 #pragma unroll
         for (int i = 0; i < RPW; i++) {
             const float* vp = Vb + min(rv0 + i, nlast) * D + lane * DPL;
             if constexpr (DPL == 1) {
-                v[i][0] = *vp;
+                v[i][0] = ld_stream(vp);
             } else {
-                const float2 v2 = *reinterpret_cast<const float2*>(vp);
+                const float2 v2 = ld_stream(reinterpret_cast<const float2*>(vp));
                 v[i][0] = v2.x;
                 v[i][1] = v2.y;
             }
@@ -736,15 +759,15 @@ template <int D, int RPW> struct KVRows<D, kBF16, RPW> {
 #pragma unroll
         for (int sl = 0; sl < NSL; sl++) {
 #pragma unroll
-            for (int f = 0; f < D / 64; f++) k[sl][f] = *reinterpret_cast<const uint4*>(K16 + rows[sl] * D + f * 64 + kq * 8);
+            for (int f = 0; f < D / 64; f++) k[sl][f] = ld_stream(reinterpret_cast<const uint4*>(K16 + rows[sl] * D + f * 64 + kq * 8));
         }
 #pragma unroll
         for (int i = 0; i < RPW; i++) {
             const uint16_t* vp = V16 + min(rv0 + i, nlast) * D + lane * DPL;
             if constexpr (DPL == 1)
-                v[i] = *vp;
+                v[i] = ld_stream(vp);
             else
-                v[i] = *reinterpret_cast<const uint32_t*>(vp);
+                v[i] = ld_stream(reinterpret_cast<const uint32_t*>(vp));
         }
     }
     // key float4 number f (f < D/32) of slot sl: dims qdim(f, kq) .. +3

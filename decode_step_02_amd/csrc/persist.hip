@@ -177,6 +177,15 @@ __device__ __forceinline__ float4 gload_f4(const void* p) {
 __device__ __forceinline__ float gload_f(const float* p) {
     return *(const __attribute__((address_space(1))) float*)p;
 }
+// The same for cached key/value rows, which a step reads once: with the
+// non-temporal hint (1000-token context: 350.4 -> 348.4 us per step).
+__device__ __forceinline__ float4 gload_f4_stream(const void* p) {
+    const f32x4 v = __builtin_nontemporal_load((const __attribute__((address_space(1))) f32x4*)p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float gload_f_stream(const float* p) {
+    return __builtin_nontemporal_load((const __attribute__((address_space(1))) float*)p);
+}
 
 // One poll round of J 16-byte loads (two LL words each) with the cache
 // policy of an agent-scope atomic load (sc1), completed inside the same asm
@@ -591,11 +600,11 @@ struct KV {
         for (int sl = 0; sl < NK; sl++) {
             const float* src = s.cache + cache_row(s, l, 0, 0, g, min(t0 + sl * 16 + rk, tmax)) + qk * (PD / 4);
 #pragma unroll
-            for (int f = 0; f < KF; f++) k[sl][f] = gload_f4(src + 4 * f);
+            for (int f = 0; f < KF; f++) k[sl][f] = gload_f4_stream(src + 4 * f);
         }
         const float* vb = s.cache + cache_row(s, l, 1, 0, g, 0) + ev;
 #pragma unroll
-        for (int ii = 0; ii < NV; ii++) v[ii] = gload_f(vb + static_cast<size_t>(min(t0 + ii * RV + rv, tmax)) * PD);
+        for (int ii = 0; ii < NV; ii++) v[ii] = gload_f_stream(vb + static_cast<size_t>(min(t0 + ii * RV + rv, tmax)) * PD);
     }
 
     // acc[j] = sum over the lane's value rows of weight * value for head j,
