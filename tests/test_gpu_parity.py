@@ -404,6 +404,55 @@ def test_single_launch_steps_in_a_captured_graph():
     model.close()
 
 
+def test_single_launch_replay_outside_its_context_class_is_reported():
+    """A batch-1 single-launch step captured by the caller at a one-chunk
+    context (32 positions) replays correctly in that class; replayed once
+    more, its context (33) is in the longer class, which another
+    instantiation serves: that launch writes nothing and the next check
+    raises DS_ERR_DEVICE.  An eager step then takes the longer class's
+    kernel and proceeds."""
+    torch = _torch()
+    import decode_step_02_amd as dsa
+    w = synth.WORKLOADS["llama135m_p5"]
+    arena = synth.make_arena(w.model, w.model_seed)
+    model = dsa.Model(w.model, arena)
+    kv = dsa.KVCache(model, 1, w.ctx)
+    assert kv.single_launch_ctx() >= 40
+    kv.cache.fill_(float("nan"))
+    prompt = [int(t) for t in synth.random_tokens(77, 31, w.model.vocab_size)]
+    st = torch.cuda.Stream()
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(st):
+        kv.prefill(0, prompt, tok, st)
+        st.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            kv.decode_step(tok, tok, st)  # captured at context 32, not run
+        kv.set_lengths([31], st)
+        st.synchronize()
+        g.replay()  # context 32: the class of the capture
+        st.synchronize()
+        kv.check(st)
+        assert kv.lengths.cpu().tolist() == [32]
+        assert torch.isfinite(kv.cache_view()[:, :, 0, :, 31].float()).all()
+        g.replay()  # context 33: the longer class
+        st.synchronize()
+        with pytest.raises(dsa.DSError) as err:
+            kv.check(st)
+        assert err.value.status == -9  # DS_ERR_DEVICE
+        assert kv.lengths.cpu().tolist() == [32]
+        assert torch.isnan(kv.cache_view()[:, :, 0, :, 32].float()).all()  # nothing written
+        kv.set_lengths([32], st)
+        kv.decode_step(tok, tok, st)  # eager: the longer class's kernel
+        st.synchronize()
+        kv.check(st)
+        assert kv.lengths.cpu().tolist() == [33]
+        assert torch.isfinite(kv.cache_view()[:, :, 0, :, 32].float()).all()
+        assert torch.isfinite(kv.logits(st)).all()
+    kv.close()
+    model.close()
+
+
 FULL_ATTN = {
     # (head_dim, H, Hkv, cache): 64 sequences x Hkv >= 128 (item, group)
     # pairs, so decode steps take the one-block-per-pair attention; the
