@@ -59,6 +59,7 @@ struct StepArgs {
     int mm_split;        // the narrow projections may take the split-K MFMA kernel
     int attn_g;          // head_dim 64 / 128 attention takes the DPP-reduced kernel
     int attn_full;       // launches with many (item, group) pairs take the one-block-per-pair attention
+    int kv_stream;       // cached key/value rows loaded with the non-temporal hint (no item shares another's rows)
     int pin;             // single-launch step's product input: kBF16 (hi/lo pairs) or kF32 (widened weights)
     int pcoop;           // single-launch step launched cooperatively (all workgroups resident, or no launch)
     float eps;

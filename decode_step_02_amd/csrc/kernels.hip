@@ -696,9 +696,11 @@ __global__ __launch_bounds__(256) void k_attn_d(StepArgs s, int layer) {
 // way D/8 dims, read as whole 128-byte lines per row, and qdim() gives the
 // query offsets that match.  The rows come in slots of 8 (one per 8 lanes).
 // Values: D/64 dims per lane; bf16 ones stay packed until used.
-// Loads of cached key/value rows, which a step reads once: with the
+// Loads of cached key/value rows, which a decode step reads once: with the
 // non-temporal hint they pass through the caches without displacing the
-// weights and activations (B = 64, 135M: 1.412 -> 1.360 ms per step).
+// weights and activations (B = 64, 135M: 1.412 -> 1.360 ms per step).  When
+// several items of a launch are positions of one sequence (a batched
+// prefill pass), they share the rows and take plain loads (s.kv_stream 0).
 typedef float stream_f4 __attribute__((ext_vector_type(4)));
 typedef float stream_f2 __attribute__((ext_vector_type(2)));
 typedef unsigned int stream_u4 __attribute__((ext_vector_type(4)));
@@ -718,6 +720,11 @@ template <typename T>
 __device__ __forceinline__ T ld_stream(const T* p) {
     return __builtin_nontemporal_load(p);
 }
+template <bool NT, typename T>
+__device__ __forceinline__ T ld_kv(const T* p) {
+    if constexpr (NT) return ld_stream(p);
+    return *p;
+}
 
 template <int D, int CDT, int RPW> struct KVRows;
 template <int D, int RPW> struct KVRows<D, kF32, RPW> {
@@ -725,25 +732,28 @@ template <int D, int RPW> struct KVRows<D, kF32, RPW> {
     float4 k[NSL][KF];
     float v[RPW][DPL];
     __device__ static __forceinline__ int qdim(int f, int kq) { return f * 32 + kq * 4; }
-    __device__ __forceinline__ void load(const float* Kb, const float* Vb, const int (&rows)[NSL], int rv0, int nlast,
-                                         int kq, int lane) {
+    template <bool NT>
+    __device__ __forceinline__ void load_t(const float* Kb, const float* Vb, const int (&rows)[NSL], int rv0, int nlast,
+                                           int kq, int lane) {
 #pragma unroll
         for (int sl = 0; sl < NSL; sl++) {
 #pragma unroll
-            for (int f = 0; f < KF; f++) k[sl][f] = ld_stream(reinterpret_cast<const float4*>(Kb + rows[sl] * D + f * 32 + kq * 4));
+            for (int f = 0; f < KF; f++)
+                k[sl][f] = ld_kv<NT>(reinterpret_cast<const float4*>(Kb + rows[sl] * D + f * 32 + kq * 4));
         }
 #pragma unroll
         for (int i = 0; i < RPW; i++) {
             const float* vp = Vb + min(rv0 + i, nlast) * D + lane * DPL;
             if constexpr (DPL == 1) {
-                v[i][0] = ld_stream(vp);
+                v[i][0] = ld_kv<NT>(vp);
             } else {
-                const float2 v2 = ld_stream(reinterpret_cast<const float2*>(vp));
+                const float2 v2 = ld_kv<NT>(reinterpret_cast<const float2*>(vp));
                 v[i][0] = v2.x;
                 v[i][1] = v2.y;
             }
         }
     }
+
     __device__ __forceinline__ float4 key(int sl, int f) const { return k[sl][f]; }
     __device__ __forceinline__ float val(int i, int dd) const { return v[i][dd]; }
 };
@@ -752,24 +762,27 @@ template <int D, int RPW> struct KVRows<D, kBF16, RPW> {
     uint4 k[NSL][D / 64];
     uint32_t v[RPW];  // the row's DPL bf16 values (D = 128: two, the lower dim in the low half)
     __device__ static __forceinline__ int qdim(int f, int kq) { return (f >> 1) * 64 + kq * 8 + (f & 1) * 4; }
-    __device__ __forceinline__ void load(const float* Kb, const float* Vb, const int (&rows)[NSL], int rv0, int nlast,
-                                         int kq, int lane) {
+    template <bool NT>
+    __device__ __forceinline__ void load_t(const float* Kb, const float* Vb, const int (&rows)[NSL], int rv0, int nlast,
+                                           int kq, int lane) {
         const uint16_t* K16 = reinterpret_cast<const uint16_t*>(Kb);
         const uint16_t* V16 = reinterpret_cast<const uint16_t*>(Vb);
 #pragma unroll
         for (int sl = 0; sl < NSL; sl++) {
 #pragma unroll
-            for (int f = 0; f < D / 64; f++) k[sl][f] = ld_stream(reinterpret_cast<const uint4*>(K16 + rows[sl] * D + f * 64 + kq * 8));
+            for (int f = 0; f < D / 64; f++)
+                k[sl][f] = ld_kv<NT>(reinterpret_cast<const uint4*>(K16 + rows[sl] * D + f * 64 + kq * 8));
         }
 #pragma unroll
         for (int i = 0; i < RPW; i++) {
             const uint16_t* vp = V16 + min(rv0 + i, nlast) * D + lane * DPL;
             if constexpr (DPL == 1)
-                v[i] = ld_stream(vp);
+                v[i] = ld_kv<NT>(vp);
             else
-                v[i] = ld_stream(reinterpret_cast<const uint32_t*>(vp));
+                v[i] = ld_kv<NT>(reinterpret_cast<const uint32_t*>(vp));
         }
     }
+
     // key float4 number f (f < D/32) of slot sl: dims qdim(f, kq) .. +3
     __device__ __forceinline__ float4 key(int sl, int f) const {
         const uint4 u = k[sl][f >> 1];
@@ -789,7 +802,9 @@ template <int D, int RPW> struct KVRows<D, kBF16, RPW> {
 // softmax weights of the chunk go through LDS, with max and sum over the
 // block; the weighted values are summed over the waves in LDS.  Partials
 // (m, l) and the weighted sum per (item, head, chunk).
-template <int D, int REP, int CDT, int NWV>
+// NT: the cached rows are loaded with the non-temporal hint (no two items
+// of the launch share a sequence; see ld_stream).
+template <int D, int REP, int CDT, int NWV, bool NT>
 __global__ __launch_bounds__(64 * NWV) void k_attn_g(StepArgs s, int layer) {
     constexpr int KF = D / 32;   // key float4s per lane and row
     constexpr int DPL = D / 64;  // value dims per lane
@@ -817,7 +832,7 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_g(StepArgs s, int layer) {
     int rows[NSL];
 #pragma unroll
     for (int sl = 0; sl < NSL; sl++) rows[sl] = min(wave * RPW + sl * 8 + rr, nt - 1);
-    kv.load(Kb, Vb, rows, wave * RPW, nt - 1, kq, lane);
+    kv.template load_t<NT>(Kb, Vb, rows, wave * RPW, nt - 1, kq, lane);
     const float* qb = s.q + (static_cast<size_t>(item) * s.H + static_cast<size_t>(g) * REP) * D;
     float4 qv[REP][KF];
 #pragma unroll
@@ -954,7 +969,7 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_full(StepArgs s, int layer) {
         int rows[NSL];
 #pragma unroll
         for (int sl = 0; sl < NSL; sl++) rows[sl] = min(run * RPW + sl * 8 + rr, n - 1);
-        kv.load(Kb, Vb, rows, run * RPW, n - 1, kq, lane);
+        kv.template load_t<true>(Kb, Vb, rows, run * RPW, n - 1, kq, lane);  // decode: no shared rows
     };
     Rows cur;
     load(cur, min(wave, nrun - 1));
@@ -1115,17 +1130,22 @@ static hipError_t launch_attn_full(const StepArgs& s, int layer, int n_items, hi
 
 constexpr int kAttnWaves = 4;  // waves per 64-position chunk of k_attn_g
 
-template <int D, int CDT>
-static bool launch_attn_g2(const StepArgs& s, dim3 grid, int layer, hipStream_t st) {
+template <int D, int CDT, bool NT>
+static bool launch_attn_g3(const StepArgs& s, dim3 grid, int layer, hipStream_t st) {
     constexpr int W = kAttnWaves;
     const dim3 blk(64 * W);
     switch (s.H / s.Hkv) {
-        case 1: hipLaunchKernelGGL((k_attn_g<D, 1, CDT, W>), grid, blk, 0, st, s, layer); return true;
-        case 2: hipLaunchKernelGGL((k_attn_g<D, 2, CDT, W>), grid, blk, 0, st, s, layer); return true;
-        case 3: hipLaunchKernelGGL((k_attn_g<D, 3, CDT, W>), grid, blk, 0, st, s, layer); return true;
-        case 4: hipLaunchKernelGGL((k_attn_g<D, 4, CDT, W>), grid, blk, 0, st, s, layer); return true;
+        case 1: hipLaunchKernelGGL((k_attn_g<D, 1, CDT, W, NT>), grid, blk, 0, st, s, layer); return true;
+        case 2: hipLaunchKernelGGL((k_attn_g<D, 2, CDT, W, NT>), grid, blk, 0, st, s, layer); return true;
+        case 3: hipLaunchKernelGGL((k_attn_g<D, 3, CDT, W, NT>), grid, blk, 0, st, s, layer); return true;
+        case 4: hipLaunchKernelGGL((k_attn_g<D, 4, CDT, W, NT>), grid, blk, 0, st, s, layer); return true;
         default: return false;
     }
+}
+
+template <int D, int CDT>
+static bool launch_attn_g2(const StepArgs& s, dim3 grid, int layer, hipStream_t st) {
+    return s.kv_stream ? launch_attn_g3<D, CDT, true>(s, grid, layer, st) : launch_attn_g3<D, CDT, false>(s, grid, layer, st);
 }
 
 template <int D>
@@ -1673,9 +1693,16 @@ hipError_t enqueue_replicate(float* dst, int Bd, int Td, const float* src, int B
     return hipGetLastError();
 }
 
-hipError_t enqueue_step(const StepArgs& s, const ModelPtrs& m, const BeginList* lists, int n_lists,
+hipError_t enqueue_step(const StepArgs& s0, const ModelPtrs& m, const BeginList* lists, int n_lists,
                         const int32_t* d_tok_in, int n_items, bool need_logits, int nload,
                         int32_t* d_tok_out, hipStream_t st) {
+    // positions of one sequence in one pass (offsets past its length) share
+    // its cached rows: the attention then loads them through the caches
+    StepArgs s = s0;
+    s.kv_stream = 1;
+    for (int i = 0; i < n_lists; i++)
+        for (int j = 0; j < lists[i].n; j++)
+            if (lists[i].by_value && lists[i].off[j] != 0) s.kv_stream = 0;
     Launch lc;
     lc.ident = d_tok_in != nullptr && lists[0].by_value == 0;  // item == slot
     const bool mm = use_mm(s, n_items);
