@@ -88,20 +88,26 @@ def kernel_bytes(m: synth.ModelShape, which: str, B: int, n_ctx: float) -> float
     return 0.0
 
 
-def kernel_sources_hash() -> str:
-    """First 16 hex digits of the sha256 of the single-launch step's sources."""
+# the sources each counted kernel is built from
+KERNEL_SOURCES = {"k_persist": ("persist.hip", "device.h", "kernels.h"),
+                  "k_attn_g": ("kernels.hip", "device.h", "kernels.h")}
+
+
+def kernel_sources_hash(kernel: str = "k_persist") -> str:
+    """First 16 hex digits of the sha256 of the kernel's sources."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("persist.hip", "device.h", "kernels.h"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "decode_step_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the single-launch step from the committed
-    FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current sources."""
-    path = os.path.join(ROOT, "profiles", f"k_persist_{workload}_traffic.md")
+def measured_traffic(workload: str, kernel: str = "k_persist"):
+    """HBM bytes per launch of `kernel` (the single-launch step, or the split-K
+    attention) from the committed FETCH_SIZE / WRITE_SIZE summary, if it was
+    taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None, "no counter summary for this workload"
     fields = {}
@@ -110,7 +116,7 @@ def measured_traffic(workload: str):
             if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_sources_sha256_16"):
                 k, v = line.split(":", 1)
                 fields[k] = v.strip()
-    if fields.get("kernel_sources_sha256_16") != kernel_sources_hash():
+    if fields.get("kernel_sources_sha256_16") != kernel_sources_hash(kernel):
         return None, "kernel changed since the counters were taken"
     return float(fields["traffic_bytes_per_launch"]), "FETCH_SIZE + WRITE_SIZE, copy-calibrated (" + os.path.relpath(path, ROOT) + ")"
 
@@ -424,8 +430,12 @@ def decode_bench(dsa, torch, w, args, stream, steps, warmup, samp=None, flush=No
         model.close()
 
     gbps = bytes_step / (ms_step * 1e-3) / 1e9
-    traffic, traffic_note = (measured_traffic(w.name) if single
-                             else (None, "counters taken for the single-launch step only"))
+    if single:
+        traffic, traffic_note = measured_traffic(w.name, "k_persist")
+    elif dom == "attn" and args.cache == "f32" and args.weights == "bf16":
+        traffic, traffic_note = measured_traffic(w.name, "k_attn_g")
+    else:
+        traffic, traffic_note = None, "no counter summary for this kernel"
     out = {
         "metric": ("decode tok/s (135M-shaped Llama, B=1)" if w.name == "llama135m_p5"
                    else "decode tok/s (135M-shaped Llama, B=64)" if w.name == "llama135m_b64"

@@ -6,6 +6,7 @@ import subprocess
 import sys
 
 import numpy as np
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -60,13 +61,20 @@ def test_kernel_bytes_8b():
     assert bench.kernel_bytes(m, "attn", 1, 4096) == 2 * 8 * 128 * 4096 * 4 + 32 * 128 * 4
 
 
-def test_traffic_summary_follows_the_source_hash(monkeypatch):
-    path = os.path.join(ROOT, "profiles", "k_persist_llama135m_p5_traffic.md")
+@pytest.mark.parametrize("kernel,workload", [("k_persist", "llama135m_p5"), ("k_attn_g", "llama135m_b64")])
+def test_traffic_summary_follows_the_source_hash(monkeypatch, kernel, workload):
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     fields = dict(line.split(":", 1) for line in open(path) if line.startswith(("traffic_bytes", "kernel_sources")))
     h = fields["kernel_sources_sha256_16"].strip()
-    monkeypatch.setattr(bench, "kernel_sources_hash", lambda: h)
-    v, note = bench.measured_traffic("llama135m_p5")
+    monkeypatch.setattr(bench, "kernel_sources_hash", lambda *a: h)
+    v, note = bench.measured_traffic(workload, kernel)
     assert v == float(fields["traffic_bytes_per_launch"]) and "FETCH_SIZE" in note
-    monkeypatch.setattr(bench, "kernel_sources_hash", lambda: "0" * 16)
-    assert bench.measured_traffic("llama135m_p5") == (None, "kernel changed since the counters were taken")
-    assert bench.measured_traffic("no_such_workload")[0] is None
+    monkeypatch.setattr(bench, "kernel_sources_hash", lambda *a: "0" * 16)
+    assert bench.measured_traffic(workload, kernel) == (None, "kernel changed since the counters were taken")
+    assert bench.measured_traffic("no_such_workload", kernel)[0] is None
+
+
+def test_kernel_source_sets():
+    # the single launch and the split-K attention are hashed over their own sources
+    assert set(bench.KERNEL_SOURCES) == {"k_persist", "k_attn_g"}
+    assert bench.kernel_sources_hash("k_persist") != bench.kernel_sources_hash("k_attn_g")
