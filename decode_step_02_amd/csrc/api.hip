@@ -422,12 +422,12 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     s.pcoop = 0;
     const char* pco = std::getenv("DS_PERSIST_COOP");
     if (pco && std::strcmp(pco, "1") == 0) s.pcoop = 1;
+    s.kv_stream = 1;  // enqueue_step sets it per pass
     // DS_ATTN_FULL=1: launches with at least kAttnFullMinBlocks (sequence,
     // group) pairs run attention as one block per pair (k_attn_full), with no
     // partials or combine launch.  Off by default: at B = 64 (135M) it
     // measured the same step time as split-K plus its combine (1.444 against
     // 1.450 ms), its longest sequences' blocks setting the pace.
-    s.kv_stream = 1;  // enqueue_step sets it per pass
     s.attn_full = 0;
     const char* afenv = std::getenv("DS_ATTN_FULL");
     if (afenv && std::strcmp(afenv, "1") == 0) s.attn_full = 1;
