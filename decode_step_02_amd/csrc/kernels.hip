@@ -273,9 +273,10 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // Two-phase staging of an n-float activation vector (n % 4 == 0) into LDS.
 // issue() starts the first round of independent 16-byte loads (and of the
 // matching gains when GAIN); the caller then puts its weight loads in flight
-// before complete_*() waits, which waits for the vector alone because loads
-// complete in issue order.  Vectors longer than U*NT float4 take further
-// rounds inside complete_*().
+// before complete_*() waits.  The callers issue the vector first, so that
+// (loads completing in issue order) the staging need not wait for the
+// weights; the compiler may still schedule some weight loads ahead of it.
+// Vectors longer than U*NT float4 take further rounds inside complete_*().
 template <int NT, int U, bool GAIN>
 struct VecStage {
     float4 xv[U];
@@ -438,8 +439,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(StepArgs s, LayerW w, int la
         row = valid ? (task - nq - nk) * R + rs : 0;
         W = w.wv;
     }
-    // the vector's loads go first: loads complete in issue order, so the
-    // staging then waits for them alone, not for the weight chunks
+    // the vector's loads go first (see VecStage), then the weight chunks
     VecStage<64 * WAVES, 4, true> vs;
     vs.issue(s.x + static_cast<size_t>(item) * s.d, w.attn_norm, s.d);
     RowStream<WDT, G> st;
