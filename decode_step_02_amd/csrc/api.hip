@@ -12,6 +12,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "ds_decode.h"
@@ -325,8 +326,13 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     probe.wdt = c->weight_dtype;
     const int need_lds = static_cast<int>(ds::max_lds_bytes(probe));
     const int need_mm = ds::mm_supported(probe) ? static_cast<int>(ds::mm_max_lds(probe)) : 0;
-    static int attr_lds = 64 * 1024, attr_mm = 64 * 1024;
-    if (need_lds > attr_lds || need_mm > attr_mm) {
+    // Function attributes belong to a device: the levels already set are
+    // kept per device, under a lock (caches may be created from several
+    // threads and for several devices).
+    if (need_lds > 64 * 1024 || need_mm > 64 * 1024) {
+        static std::mutex attr_mu;
+        static std::vector<std::pair<int, int>> attr_set;  // per device: (lds, mm) levels set
+        std::lock_guard<std::mutex> lock(attr_mu);
         int dev = 0, optin = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev);
@@ -334,15 +340,17 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
         if (std::max(need_lds, need_mm) > optin - 4096)
             return fail(DS_ERR_UNSUPPORTED, "kernels need %d bytes of LDS, the device allows %d",
                         std::max(need_lds, need_mm), optin);
-        if (need_lds > attr_lds) {
+        if (static_cast<int>(attr_set.size()) <= dev) attr_set.resize(dev + 1, {64 * 1024, 64 * 1024});
+        std::pair<int, int>& lv = attr_set[dev];
+        if (need_lds > lv.first) {
             e = ds::set_kernel_attributes(need_lds);
             if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-            attr_lds = need_lds;
+            lv.first = need_lds;
         }
-        if (need_mm > attr_mm) {
+        if (need_mm > lv.second) {
             e = ds::mm_set_attributes(need_mm);
             if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-            attr_mm = need_mm;
+            lv.second = need_mm;
         }
     }
 
@@ -631,7 +639,10 @@ ds_status ds_prefill(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_t
             const int nload = ds::short_rows(kv->s, ctx);
             e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, nullptr, 1, j == n - 1, nload, d_tok_out, st);
         }
-        if (e != hipSuccess) return hip_fail(e, "prefill");
+        if (e != hipSuccess) {
+            kv->mirror[seq] += j;  // the positions already enqueued advance the device lengths
+            return hip_fail(e, "prefill");
+        }
     }
     kv->mirror[seq] += n;
     return ok();
@@ -720,7 +731,11 @@ ds_status ds_prefill_batch(ds_model* model, ds_kv* kv, const int32_t* h_tokens, 
         hipError_t e = ds::enqueue_step(kv->s, model->ptrs, lists.data(), static_cast<int>(lists.size()),
                                         nullptr, items, any_last, ds::short_rows(kv->s, max_ctx), d_tok_out,
                                         st);
-        if (e != hipSuccess) return hip_fail(e, "prefill_batch");
+        if (e != hipSuccess) {
+            // the passes already enqueued advance the device lengths
+            for (int b = 0; b < B; b++) kv->mirror[b] += std::min(h_counts[b], j);
+            return hip_fail(e, "prefill_batch");
+        }
     }
     for (int b = 0; b < B; b++) kv->mirror[b] += h_counts[b];
     return ok();
