@@ -138,15 +138,30 @@ template <> struct Wt<kF32> {
 // One lane's share of one row: the first PF chunks are loaded by
 // start(), the rest while finish() accumulates.  finish() returns the full
 // row dot product in every lane of the row's G-lane group.
-template <int WDT, int G>
+// Staged activation vectors of the block-scaled types leave 4 floats of
+// padding after every chunk's EPC values (a stride of 20 or 36 floats): the
+// lanes of a row read chunks sub, sub + G, ... at once, and with the plain
+// stride of 16 or 32 floats the 8 lanes of one LDS read cycle would all hit
+// the same four banks.
+template <int WDT>
+constexpr int lds_pad_q() { return (WDT == kQ8 || WDT == kQ4) ? Wt<WDT>::EPC / 4 : 0; }  // float4s per padded chunk
+
+// Floats of LDS that a staged vector of n values takes (n a multiple of the chunk).
+__host__ __device__ inline int staged_floats(int wdt, int n) {
+    return wdt == kQ8 ? n + n / 16 * 4 : wdt == kQ4 ? n + n / 32 * 4 : n;
+}
+
+template <int WDT, int G, int PFO = 0, bool XP = false>
 struct RowStream {
     static constexpr int EPC = Wt<WDT>::EPC;
     static constexpr bool Q8 = WDT == kQ8 || WDT == kQ4;  // block scales (Q8 or Q4)
-    // chunks in flight per lane: 16 where 32 lanes share a row of bf16 or
-    // fp32 weights (rows of 512 and more chunks), which is a whole 4096-long
-    // bf16 row -- one memory round trip -- and those launches have few waves
-    // per SIMD to hide it (the block-scaled types would spill)
-    static constexpr int PF = (G >= 32 && !Q8) ? 16 : kPrefetch;
+    static constexpr int XS = XP ? EPC + 4 : EPC;  // LDS floats from one chunk's values to the next's
+    // chunks in flight per lane: PFO where the caller sets it; else 16 where
+    // 32 lanes share a row of bf16 or fp32 weights (rows of 512 and more
+    // chunks), which is a whole 4096-long bf16 row -- one memory round trip
+    // -- and those launches have few waves per SIMD to hide it (the
+    // block-scaled types would spill)
+    static constexpr int PF = PFO ? PFO : (G >= 32 && !Q8) ? 16 : kPrefetch;
     uint4 w[PF];
     float sc[Q8 ? PF : 1];  // Q8: the block scale of each prefetched chunk
     const void* W;
@@ -198,8 +213,8 @@ struct RowStream {
 #pragma unroll
         for (int p = 0; p < PF; p += 2) {
             // masked chunks are zero; the LDS index is clamped so it stays in range
-            a0 = chunk(w[p], sc[Q8 ? p : 0], xs + min(sub + p * G, last) * EPC, a0);
-            if (p + 1 < PF) a1 = chunk(w[p + 1], sc[Q8 ? p + 1 : 0], xs + min(sub + (p + 1) * G, last) * EPC, a1);
+            a0 = chunk(w[p], sc[Q8 ? p : 0], xs + min(sub + p * G, last) * XS, a0);
+            if (p + 1 < PF) a1 = chunk(w[p + 1], sc[Q8 ? p + 1 : 0], xs + min(sub + (p + 1) * G, last) * XS, a1);
         }
         int c = sub + PF * G;
         for (; c + 3 * G < nch; c += 4 * G) {
@@ -208,12 +223,12 @@ struct RowStream {
             const uint4 u2 = Wt<WDT>::load(W, base + static_cast<size_t>(c + 2 * G) * EPC);
             const uint4 u3 = Wt<WDT>::load(W, base + static_cast<size_t>(c + 3 * G) * EPC);
             const float s0 = scale_of(c), s1 = scale_of(c + G), s2 = scale_of(c + 2 * G), s3 = scale_of(c + 3 * G);
-            a0 = chunk(u0, s0, xs + c * EPC, a0);
-            a1 = chunk(u1, s1, xs + (c + G) * EPC, a1);
-            a0 = chunk(u2, s2, xs + (c + 2 * G) * EPC, a0);
-            a1 = chunk(u3, s3, xs + (c + 3 * G) * EPC, a1);
+            a0 = chunk(u0, s0, xs + c * XS, a0);
+            a1 = chunk(u1, s1, xs + (c + G) * XS, a1);
+            a0 = chunk(u2, s2, xs + (c + 2 * G) * XS, a0);
+            a1 = chunk(u3, s3, xs + (c + 3 * G) * XS, a1);
         }
-        for (; c < nch; c += G) a0 = chunk(Wt<WDT>::load(W, base + static_cast<size_t>(c) * EPC), scale_of(c), xs + c * EPC, a0);
+        for (; c < nch; c += G) a0 = chunk(Wt<WDT>::load(W, base + static_cast<size_t>(c) * EPC), scale_of(c), xs + c * XS, a0);
         return group_sum<G>(a0 + a1);
     }
 
@@ -235,7 +250,7 @@ struct RowStream {
 #pragma unroll
             for (int p = 0; p < PF; p++) {
                 const int c = sub + (j0 + p) * G;
-                const float* xc = xs + min(c, last) * EPC;
+                const float* xc = xs + min(c, last) * XS;
                 float& a = (p & 1) ? a1 : a0;
                 const float v = chunk(w[p], sc[Q8 ? p : 0], xc, a);
                 a = c < nch ? v : a;
@@ -248,7 +263,7 @@ struct RowStream {
         for (int p = 0; p < PF; p++) {
             const int c = sub + (j0 + p) * G;
             float& a = (p & 1) ? a1 : a0;
-            const float v = chunk(w[p], sc[Q8 ? p : 0], xs + min(c, last) * EPC, a);
+            const float v = chunk(w[p], sc[Q8 ? p : 0], xs + min(c, last) * XS, a);
             a = c < nch ? v : a;
         }
         return group_sum<G>(a0 + a1);
@@ -277,8 +292,11 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // (loads completing in issue order) the staging need not wait for the
 // weights; the compiler may still schedule some weight loads ahead of it.
 // Vectors longer than U*NT float4 take further rounds inside complete_*().
-template <int NT, int U, bool GAIN>
+// Q > 0: float4 j of the vector goes to LDS float4 j + j / Q (the padded
+// layout of RowStream's XP).
+template <int NT, int U, bool GAIN, int Q = 0>
 struct VecStage {
+    __device__ static __forceinline__ int at(int j) { return Q ? j + j / Q : j; }
     float4 xv[U];
     float4 gv[GAIN ? U : 1];
     const float4* x4;
@@ -310,7 +328,7 @@ struct VecStage {
             t = fmaf(v.z, v.z, t);
             t = fmaf(v.w, v.w, t);
             ss += in ? t : 0.f;
-            s4[j] = make_float4(gg.x * v.x, gg.y * v.y, gg.z * v.z, gg.w * v.w);
+            s4[at(j)] = make_float4(gg.x * v.x, gg.y * v.y, gg.z * v.z, gg.w * v.w);
         };
         // Stores past n4 go to the last element with its own value (the loads
         // were clamped the same way), so no branch: a guarded store lets the
@@ -337,8 +355,8 @@ struct VecStage {
         ss = block_sum<WAVES>(ss, red);
         const float r = 1.0f / sqrtf(ss / static_cast<float>(n) + eps);
         for (int j = threadIdx.x; j < n4; j += NT) {
-            const float4 v = s4[j];
-            s4[j] = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+            const float4 v = s4[at(j)];
+            s4[at(j)] = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
         }
         __syncthreads();
     }
@@ -346,7 +364,7 @@ struct VecStage {
     __device__ __forceinline__ void complete_copy(float* xs) {
         float4* s4 = reinterpret_cast<float4*>(xs);
 #pragma unroll
-        for (int u = 0; u < U; u++) s4[min(static_cast<int>(threadIdx.x) + u * NT, n4 - 1)] = xv[u];  // as in complete_rms
+        for (int u = 0; u < U; u++) s4[at(min(static_cast<int>(threadIdx.x) + u * NT, n4 - 1))] = xv[u];  // as in complete_rms
         // later rounds load into a local array, unconditionally (clamped):
         // guarded writes into xv keep it out of registers, in scratch memory,
         // with every load waited for before the next is issued
@@ -355,7 +373,7 @@ struct VecStage {
 #pragma unroll
             for (int u = 0; u < U; u++) t[u] = x4[min(base + u * NT, n4 - 1)];
 #pragma unroll
-            for (int u = 0; u < U; u++) s4[min(base + u * NT, n4 - 1)] = t[u];
+            for (int u = 0; u < U; u++) s4[at(min(base + u * NT, n4 - 1))] = t[u];
         }
         __syncthreads();
     }
@@ -440,9 +458,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(StepArgs s, LayerW w, int la
         W = w.wv;
     }
     // the vector's loads go first (see VecStage), then the weight chunks
-    VecStage<64 * WAVES, 4, true> vs;
+    VecStage<64 * WAVES, 4, true, lds_pad_q<WDT>()> vs;
     vs.issue(s.x + static_cast<size_t>(item) * s.d, w.attn_norm, s.d);
-    RowStream<WDT, G> st;
+    RowStream<WDT, G, 0, (lds_pad_q<WDT>() > 0)> st;
     st.start(W, row, s.d, sub, valid, static_cast<size_t>(is_q ? s.H : s.Hkv) * D);
     float c = 1.f, sn = 0.f;
     if (roped && valid) {
@@ -1311,9 +1329,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_wo(StepArgs s, LayerW w, int lay
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.d;
-    VecStage<64 * WAVES, 8, false> vs;
+    VecStage<64 * WAVES, 8, false, SHORT ? 0 : lds_pad_q<WDT>()> vs;
     if constexpr (!SHORT) vs.issue(s.o + static_cast<size_t>(item) * K, nullptr, K);  // first, as in k_qkv
-    RowStream<WDT, G> st;
+    RowStream<WDT, G, 0, !SHORT && (lds_pad_q<WDT>() > 0)> st;
     st.start(w.wo, valid ? row : 0, K, sub, valid, s.d);
     float* xr = s.x + static_cast<size_t>(item) * s.d + row;
     const float x_old = (valid && sub == 0) ? *xr : 0.f;
@@ -1340,9 +1358,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_w13(StepArgs s, LayerW w) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.F;
-    VecStage<64 * WAVES, 4, true> vs;
+    VecStage<64 * WAVES, 4, true, lds_pad_q<WDT>()> vs;
     vs.issue(s.x + static_cast<size_t>(item) * s.d, w.ffn_norm, s.d);  // first, as in k_qkv
-    RowStream<WDT, G> s1, s3;
+    // two streams: the block-scaled types prefetch fewer chunks, or the
+    // kernel spills past 256 registers and runs one wave per SIMD
+    RowStream<WDT, G, WDT == kQ8 ? 8 : WDT == kQ4 ? 4 : 0, (lds_pad_q<WDT>() > 0)> s1, s3;
     s1.start(w.w1, valid ? row : 0, s.d, sub, valid, s.F);
     s3.start(w.w3, valid ? row : 0, s.d, sub, valid, s.F);
     vs.template complete_rms<WAVES>(xs, red, s.d, s.eps);
@@ -1363,9 +1383,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_w2(StepArgs s, LayerW w) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.d;
-    VecStage<64 * WAVES, 8, false> vs;
+    VecStage<64 * WAVES, 8, false, lds_pad_q<WDT>()> vs;
     vs.issue(s.h + static_cast<size_t>(item) * s.F, nullptr, s.F);  // first, as in k_qkv
-    RowStream<WDT, G> st;
+    RowStream<WDT, G, 0, (lds_pad_q<WDT>() > 0)> st;
     st.start(w.w2, valid ? row : 0, s.F, sub, valid, s.d);
     float* xr = s.x + static_cast<size_t>(item) * s.d + row;
     const float x_old = (valid && sub == 0) ? *xr : 0.f;
@@ -1388,9 +1408,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_logits(StepArgs s, const float* 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = (blockIdx.x * WAVES + wave) * R + lane / G, sub = lane % G;
     const bool valid = row < s.V;
-    VecStage<64 * WAVES, 4, true> vs;
+    VecStage<64 * WAVES, 4, true, lds_pad_q<WDT>()> vs;
     vs.issue(s.x + static_cast<size_t>(item) * s.d, out_norm, s.d);  // first, as in k_qkv
-    RowStream<WDT, G> st;
+    RowStream<WDT, G, 0, (lds_pad_q<WDT>() > 0)> st;
     st.start(wcls, valid ? row : 0, s.d, sub, valid, s.V);
     vs.template complete_rms<WAVES>(xs, red, s.d, s.eps);
     if (!flag) return;
@@ -1488,7 +1508,7 @@ int short_positions(const StepArgs& s) {
 }
 
 size_t max_lds_bytes(const StepArgs& s) {
-    return sizeof(float) * static_cast<size_t>(std::max(std::max(s.d, s.H * s.D), s.F));
+    return sizeof(float) * static_cast<size_t>(staged_floats(s.wdt, std::max(std::max(s.d, s.H * s.D), s.F)));
 }
 
 enum Gemv { G_QKV, G_WO_SHORT, G_WO_LONG, G_W13, G_W2, G_LOGITS };
@@ -1508,7 +1528,7 @@ static hipError_t launch3(Gemv which, const StepArgs& s, const LayerW& w, int la
         case G_QKV: {
             const int tasks = (s.H + 2 * s.Hkv) * s.D / R;
             hipLaunchKernelGGL((k_qkv<WDT, G, WAVES>), dim3((tasks + WAVES - 1) / WAVES, n_items), blk,
-                               sizeof(float) * s.d, st, s, w, layer, lc.ident);
+                               sizeof(float) * staged_floats(WDT, s.d), st, s, w, layer, lc.ident);
             break;
         }
         case G_WO_SHORT:
@@ -1517,19 +1537,19 @@ static hipError_t launch3(Gemv which, const StepArgs& s, const LayerW& w, int la
             break;
         case G_WO_LONG:
             hipLaunchKernelGGL((k_wo<WDT, G, WAVES, false>), dim3((s.d + RB - 1) / RB, n_items), blk,
-                               sizeof(float) * s.H * s.D, st, s, w, layer, lc.ident, 0);
+                               sizeof(float) * staged_floats(WDT, s.H * s.D), st, s, w, layer, lc.ident, 0);
             break;
         case G_W13:
             hipLaunchKernelGGL((k_w13<WDT, G, WAVES>), dim3((s.F + RB - 1) / RB, n_items), blk,
-                               sizeof(float) * s.d, st, s, w);
+                               sizeof(float) * staged_floats(WDT, s.d), st, s, w);
             break;
         case G_W2:
             hipLaunchKernelGGL((k_w2<WDT, G, WAVES>), dim3((s.d + RB - 1) / RB, n_items), blk,
-                               sizeof(float) * s.F, st, s, w);
+                               sizeof(float) * staged_floats(WDT, s.F), st, s, w);
             break;
         case G_LOGITS:
             hipLaunchKernelGGL((k_logits<WDT, G, WAVES>), dim3((s.V + RB - 1) / RB, n_items), blk,
-                               sizeof(float) * s.d, st, s, out_norm, wcls);
+                               sizeof(float) * staged_floats(WDT, s.d), st, s, out_norm, wcls);
             break;
     }
     return hipGetLastError();
@@ -1542,8 +1562,8 @@ static hipError_t launch2(Gemv which, int waves, const StepArgs& s, const LayerW
     if (waves == 8) {  // W2 over long rows only (pick in gemv)
         if (which != G_W2) return hipErrorInvalidValue;
         constexpr int RB = 8 * (64 / G);
-        hipLaunchKernelGGL((k_w2<WDT, G, 8>), dim3((s.d + RB - 1) / RB, n_items), dim3(512), sizeof(float) * s.F, st,
-                           s, w);
+        hipLaunchKernelGGL((k_w2<WDT, G, 8>), dim3((s.d + RB - 1) / RB, n_items), dim3(512),
+                           sizeof(float) * staged_floats(WDT, s.F), st, s, w);
         return hipGetLastError();
     }
     return launch3<WDT, G, 4>(which, s, w, layer, n_items, st, out_norm, wcls, lc);
