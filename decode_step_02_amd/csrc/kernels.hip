@@ -156,12 +156,14 @@ struct RowStream {
     static constexpr int EPC = Wt<WDT>::EPC;
     static constexpr bool Q8 = WDT == kQ8 || WDT == kQ4;  // block scales (Q8 or Q4)
     static constexpr int XS = XP ? EPC + 4 : EPC;  // LDS floats from one chunk's values to the next's
-    // chunks in flight per lane: PFO where the caller sets it; else 16 where
-    // 32 lanes share a row of bf16 or fp32 weights (rows of 512 and more
-    // chunks), which is a whole 4096-long bf16 row -- one memory round trip
-    // -- and those launches have few waves per SIMD to hide it (the
-    // block-scaled types would spill)
-    static constexpr int PF = PFO ? PFO : (G >= 32 && !Q8) ? 16 : kPrefetch;
+    // chunks in flight per lane: PFO where the caller sets it; else 8 (int8)
+    // or 4 (int4) for the block-scaled types, whose lanes get as many
+    // weights as bf16 lanes do (pick_g) and so 2 or 4 times fewer chunks;
+    // else 16 where 32 lanes share a row of bf16 or fp32 weights (rows of
+    // 512 and more chunks), which is a whole 4096-long bf16 row -- one
+    // memory round trip -- and those launches have few waves per SIMD to
+    // hide it
+    static constexpr int PF = PFO ? PFO : WDT == kQ8 ? 8 : WDT == kQ4 ? 4 : G >= 32 ? 16 : kPrefetch;
     uint4 w[PF];
     float sc[Q8 ? PF : 1];  // Q8: the block scale of each prefetched chunk
     const void* W;
@@ -1360,9 +1362,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w13(StepArgs s, LayerW w) {
     const bool valid = row < s.F;
     VecStage<64 * WAVES, 4, true, lds_pad_q<WDT>()> vs;
     vs.issue(s.x + static_cast<size_t>(item) * s.d, w.ffn_norm, s.d);  // first, as in k_qkv
-    // two streams: the block-scaled types prefetch fewer chunks, or the
-    // kernel spills past 256 registers and runs one wave per SIMD
-    RowStream<WDT, G, WDT == kQ8 ? 8 : WDT == kQ4 ? 4 : 0, (lds_pad_q<WDT>() > 0)> s1, s3;
+    RowStream<WDT, G, 0, (lds_pad_q<WDT>() > 0)> s1, s3;
     s1.start(w.w1, valid ? row : 0, s.d, sub, valid, s.F);
     s3.start(w.w3, valid ? row : 0, s.d, sub, valid, s.F);
     vs.template complete_rms<WAVES>(xs, red, s.d, s.eps);
@@ -1484,8 +1484,11 @@ __global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
 // Lanes per row: more for longer rows; and two rows per wave instead of four
 // when the launch would otherwise hold fewer than 2048 waves (rows = weight
 // rows x items), so that every CU has the loads of several waves in flight.
+// Lanes per row from the row's length in bf16-sized chunks (8 values; the
+// block-scaled types count their values the same way, since a lane's work
+// is one convert and one FMA per value) or fp32 chunks, and the row count.
 static int pick_g(int K, int wdt, int rows = 1 << 30) {
-    const int nch = K / (wdt == kQ4 ? 32 : wdt == kQ8 ? 16 : wdt == kBF16 ? 8 : 4);
+    const int nch = K / (wdt == kF32 ? 4 : 8);
     if (nch <= 128) return 8;
     if (nch <= 512) return rows >= 4 * 2048 ? 16 : 32;
     return 32;
