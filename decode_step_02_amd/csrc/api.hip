@@ -439,6 +439,12 @@ ds_status ds_kv_cache_create(ds_model* model, int32_t B, int32_t T, float* d_cac
     s.attn_full = 0;
     const char* afenv = std::getenv("DS_ATTN_FULL");
     if (afenv && std::strcmp(afenv, "1") == 0) s.attn_full = 1;
+    // batched-prefill passes (positions of one sequence) take the attention
+    // that reads each chunk once for all positions; DS_ATTN_PF=0 keeps the
+    // split-K attention per position
+    s.attn_pf = 1;
+    const char* pfenv = std::getenv("DS_ATTN_PF");
+    if (pfenv && std::strcmp(pfenv, "0") == 0) s.attn_pf = 0;
     const char* sa = std::getenv("DS_SHORT_ATTN");  // "0" turns the fused short-context path off
     if (sa && std::strcmp(sa, "0") == 0) s.short_n = 0;
     ds::PersistArgs& pa = kv->pa;

@@ -59,6 +59,7 @@ struct StepArgs {
     int mm_split;        // the narrow projections may take the split-K MFMA kernel
     int attn_g;          // head_dim 64 / 128 attention takes the DPP-reduced kernel
     int attn_full;       // launches with many (item, group) pairs take the one-block-per-pair attention
+    int attn_pf;         // passes whose items share one sequence (batched prefill) take k_attn_pf
     int kv_stream;       // cached key/value rows loaded with the non-temporal hint (no item shares another's rows)
     int pin;             // single-launch step's product input: kBF16 (hi/lo pairs) or kF32 (widened weights)
     int pcoop;           // single-launch step launched cooperatively (all workgroups resident, or no launch)
@@ -187,6 +188,13 @@ bool mm_supported(const StepArgs& s);
 int mm_logits_blocks(const StepArgs& s);
 size_t mm_max_lds(const StepArgs& s);
 hipError_t mm_set_attributes(int lds);
+// Attention of a pass whose n_items (<= 64) items are positions of one
+// sequence (slot[0]): one block per (chunk, key/value group) on the matrix
+// cores, partials for the merge launch.  head_dim 64 or 128, at most 4 query
+// heads per key/value head, s.attn_pf set.
+bool attn_pf_supported(const StepArgs& s);
+size_t attn_pf_lds(int D, int cdt, int rep);
+hipError_t launch_attn_pf(const StepArgs& s, int layer, int n_items, hipStream_t st);
 hipError_t mm_gemv(int which, const StepArgs& s, const LayerW& w, int layer, int n_items, int ident,
                    const float* out_norm, const void* wcls, hipStream_t st);
 // Longest context (a power of two <= min(kShort, T)) whose short-path staging fits in

@@ -1726,6 +1726,11 @@ hipError_t enqueue_step(const StepArgs& s0, const ModelPtrs& m, const BeginList*
     for (int i = 0; i < n_lists; i++)
         for (int j = 0; j < lists[i].n; j++)
             if (lists[i].by_value && lists[i].off[j] != 0) s.kv_stream = 0;
+    // the items are positions of one sequence (a batched prefill pass): they
+    // share its cached rows, and attention can read them once per chunk
+    bool one_seq = n_lists == 1 && lists[0].by_value == 1 && lists[0].n == n_items && n_items <= kMaxItems;
+    for (int j = 1; one_seq && j < lists[0].n; j++) one_seq = lists[0].slot[j] == lists[0].slot[0];
+    const bool pf = one_seq && s.mm_ok && attn_pf_supported(s);
     Launch lc;
     lc.ident = d_tok_in != nullptr && lists[0].by_value == 0;  // item == slot
     const bool mm = use_mm(s, n_items);
@@ -1744,6 +1749,9 @@ hipError_t enqueue_step(const StepArgs& s0, const ModelPtrs& m, const BeginList*
         } else {
             if (attn_full(s, n_items)) {
                 e = launch_attn_full(s, l, n_items, st);
+            } else if (pf) {
+                e = launch_attn_pf(s, l, n_items, st);
+                if (e == hipSuccess) e = launch_combine(s, n_items, st);
             } else {
                 e = launch_attn(s, l, n_items, st);
                 if (e == hipSuccess) e = launch_combine(s, n_items, st);

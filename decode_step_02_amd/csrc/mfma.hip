@@ -24,6 +24,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -542,6 +543,284 @@ static hipError_t launch_kind(const StepArgs& s, const LayerW& w, int layer, int
     return hipGetLastError();
 }
 
+
+// ---- causal attention over one sequence's positions (batched prefill) ----------------------------
+// In a batched-prefill pass the items are positions of one sequence, so they
+// read the same cached rows.  One block per (64-position chunk, key/value
+// group) stages the chunk's keys (row-major) and values (transposed) in LDS
+// once, as bf16 hi and lo terms, and serves every item of the pass and every
+// query head of the group: wave w takes items 16 (w % 4) .. + 15 of head
+// w / 4 and computes
+//   S = Q K^T   (16 items x 64 positions, D-long products),
+//   the chunk's softmax statistics per item, m = max_p S*scale and
+//   l = sum_p e^(S*scale - m), over the positions up to the item's own,
+//   O = P V     (16 items x D dims, 64-long products, P through LDS),
+// on the matrix cores, every product as hi*hi + hi*lo + lo*hi + lo*lo with
+// fp32 accumulation (the lo terms of a bf16 cache are zero and skipped).
+// The partials (m, l, O) per (item, head, chunk) are those of k_attn_g and go
+// to the same merge launch.  The rows, the queries and the positions are all
+// loaded before the first barrier; rows past the pass's last position are
+// masked out of the scores and zeroed as values; chunks past it exit.
+// n_items <= 64.
+//   A (16 x 32): lane l holds Q[item l%16][d0 + (l/16)*8 .. +8], or P rows
+//   B (32 x 16): lane l holds K[pos l%16][d0 + (l/16)*8 .. +8], or V^T rows
+//   C (16 x 16): lane l holds rows (l/16)*4 + r of column l%16
+constexpr int kPfKP(int D) { return D + 8; }   // key row stride in LDS (bf16): 16-byte rows, fewer conflicts
+constexpr int kPfVP = kChunk + 8;              // transposed value row stride (bf16)
+constexpr int kPfPP = kChunk + 4;              // probability row stride (floats)
+
+size_t attn_pf_lds(int D, int cdt, int rep) {
+    const size_t terms = cdt == kBF16 ? 1 : 2;
+    return sizeof(uint16_t) * terms * (static_cast<size_t>(kChunk) * kPfKP(D) + static_cast<size_t>(D) * kPfVP) +
+           sizeof(float) * 4 * rep * 16 * kPfPP;
+}
+
+// x = hi + lo in bf16 (both nearest even), 8 values into two A/B operands
+__device__ __forceinline__ void split8(const float4 a, const float4 b, uint4& hi, uint4& lo) {
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+        const uint32_t hb = bf16_bits_rne(v[c]);
+        const uint32_t lb = bf16_bits_rne(v[c] - __uint_as_float(hb << 16));
+        if (c & 1) {
+            h[c >> 1] |= hb << 16;
+            l[c >> 1] |= lb << 16;
+        } else {
+            h[c >> 1] = hb;
+            l[c >> 1] = lb;
+        }
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+template <int D, int REP, int CDT>
+__global__ __launch_bounds__(256 * REP) void k_attn_pf(StepArgs s, int layer, int n_items) {
+    constexpr bool LO = CDT != kBF16;
+    constexpr int NT = 256 * REP;
+    constexpr int KP = kPfKP(D), VP = kPfVP, PP = kPfPP;
+    constexpr int KS = D / 32, DT = D / 16, G8 = D / 8;
+    constexpr int NG = kChunk * G8;           // 8-value groups of a chunk's rows
+    constexpr int PER = (NG + NT - 1) / NT;   // per thread
+    using Raw = typename std::conditional<LO, float4, uint4>::type;
+    constexpr int RW = LO ? 2 : 1;            // raw loads per 8 values
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    uint16_t* kh = reinterpret_cast<uint16_t*>(lds);  // [kChunk][KP]
+    uint16_t* kl = kh + kChunk * KP;                  // LO only
+    uint16_t* vh = kh + (LO ? 2 : 1) * kChunk * KP;   // [D][VP]
+    uint16_t* vl = vh + D * VP;                       // LO only
+    float* pw = reinterpret_cast<float*>(vh + (LO ? 2 : 1) * D * VP);  // [4 REP waves][16][PP]
+    __shared__ int smax;
+    const int chunk = blockIdx.x, g = blockIdx.y;
+    const int t0 = chunk * kChunk;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int ig = wave & 3, head = g * REP + (wave >> 2);
+    // (1) everything that does not depend on the pass's last position
+    const int slot = s.slot[0];
+    const size_t kidx = cache_row(s, layer, 0, slot, g, 0), vidx = cache_row(s, layer, 1, slot, g, 0);
+    Raw kraw[PER][RW], vraw[PER][RW];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {  // rows clamped into the sequence's T rows; replaced below where past the last position
+        const int q = min(static_cast<int>(threadIdx.x) + i * NT, NG - 1);
+        const size_t off = static_cast<size_t>(min(t0 + q / G8, s.T - 1)) * D + (q % G8) * 8;
+#pragma unroll
+        for (int h = 0; h < RW; h++) {
+            if constexpr (LO) {
+                kraw[i][h] = *reinterpret_cast<const float4*>(s.cache + kidx + off + 4 * h);
+                vraw[i][h] = *reinterpret_cast<const float4*>(s.cache + vidx + off + 4 * h);
+            } else {
+                const uint16_t* c16 = reinterpret_cast<const uint16_t*>(s.cache);
+                kraw[i][h] = *reinterpret_cast<const uint4*>(c16 + kidx + off);
+                vraw[i][h] = *reinterpret_cast<const uint4*>(c16 + vidx + off);
+            }
+        }
+    }
+    const int ia = min(16 * ig + (lane & 15), n_items - 1);  // this lane's A row (item)
+    const float* qrow = s.q + (static_cast<size_t>(ia) * s.H + head) * D + (lane >> 4) * 8;
+    float4 qv[KS][2];
+#pragma unroll
+    for (int k = 0; k < KS; k++) {
+        qv[k][0] = *reinterpret_cast<const float4*>(qrow + 32 * k);
+        qv[k][1] = *reinterpret_cast<const float4*>(qrow + 32 * k + 4);
+    }
+    int pc[4];
+    bool vc[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {  // the C rows' items
+        const int it = 16 * ig + (lane >> 4) * 4 + r;
+        vc[r] = it < n_items;
+        pc[r] = s.pos[min(it, n_items - 1)];
+    }
+    if (wave == 0) {  // the pass's last position
+        int p = lane < n_items ? s.pos[lane] : -1;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) p = max(p, __shfl_xor(p, o));
+        if (lane == 0) smax = p;
+    }
+    __syncthreads();
+    const int maxpos = smax;
+    if (t0 > maxpos) return;  // whole block
+    const int rlast = min(kChunk - 1, maxpos - t0);
+    // (2) the staged rows: keys as loaded (rows past rlast never pass the
+    // mask), values of rows past rlast as zeros (their weight is 0)
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int q = threadIdx.x + i * NT;
+        if (q < NG) {
+            const int r = q / G8, d0 = (q % G8) * 8;
+            uint4 khi, klo, vhi, vlo;
+            if constexpr (LO) {
+                split8(kraw[i][0], kraw[i][1], khi, klo);
+                split8(vraw[i][0], vraw[i][1], vhi, vlo);
+            } else {
+                khi = kraw[i][0];
+                vhi = vraw[i][0];
+                klo = vlo = make_uint4(0u, 0u, 0u, 0u);
+            }
+            if (r > rlast) vhi = vlo = make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<uint4*>(kh + r * KP + d0) = khi;
+            if constexpr (LO) *reinterpret_cast<uint4*>(kl + r * KP + d0) = klo;
+            const uint32_t vw[4] = {vhi.x, vhi.y, vhi.z, vhi.w}, vlw[4] = {vlo.x, vlo.y, vlo.z, vlo.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                vh[(d0 + e) * VP + r] = static_cast<uint16_t>(vw[e >> 1] >> (16 * (e & 1)));
+                if constexpr (LO) vl[(d0 + e) * VP + r] = static_cast<uint16_t>(vlw[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+    }
+    __syncthreads();
+
+    // (3) S = Q K^T for this wave's 16 items and head
+    f32x4 sacc[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; pt++) sacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; k++) {
+        uint4 ah, al;
+        split8(qv[k][0], qv[k][1], ah, al);
+#pragma unroll
+        for (int pt = 0; pt < 4; pt++) {
+            const int ko = (16 * pt + (lane & 15)) * KP + 32 * k + (lane >> 4) * 8;
+            const uint4 bh = *reinterpret_cast<const uint4*>(kh + ko);
+            sacc[pt] = mfma(ah, bh, sacc[pt]);
+            sacc[pt] = mfma(al, bh, sacc[pt]);
+            if constexpr (LO) {
+                const uint4 bl = *reinterpret_cast<const uint4*>(kl + ko);
+                sacc[pt] = mfma(ah, bl, sacc[pt]);
+                sacc[pt] = mfma(al, bl, sacc[pt]);
+            }
+        }
+    }
+    // (4) the chunk's statistics per item row (16 lanes share a row group)
+    const float scale = 1.0f / sqrtf(static_cast<float>(D));
+    float* pwv = pw + wave * 16 * PP;
+    float mr[4], lr[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int pt = 0; pt < 4; pt++) {
+            const bool in = vc[r] && t0 + 16 * pt + (lane & 15) <= pc[r];
+            sacc[pt][r] = in ? sacc[pt][r] * scale : -INFINITY;
+            m = fmaxf(m, sacc[pt][r]);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        mr[r] = m;
+        float l = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < 4; pt++) {
+            const float p = m == -INFINITY ? 0.f : __expf(sacc[pt][r] - m);
+            pwv[((lane >> 4) * 4 + r) * PP + 16 * pt + (lane & 15)] = p;
+            l += p;
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o);
+        lr[r] = l;
+    }
+    __syncthreads();  // the probabilities in LDS (each wave reads only its own)
+    // (5) O = P V
+    f32x4 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < kChunk / 32; kk++) {
+        const float* prow = pwv + (lane & 15) * PP + 32 * kk + (lane >> 4) * 8;
+        uint4 ph, pl;
+        split8(*reinterpret_cast<const float4*>(prow), *reinterpret_cast<const float4*>(prow + 4), ph, pl);
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            const int vo = (16 * dt + (lane & 15)) * VP + 32 * kk + (lane >> 4) * 8;
+            const uint4 bh = *reinterpret_cast<const uint4*>(vh + vo);
+            oacc[dt] = mfma(ph, bh, oacc[dt]);
+            oacc[dt] = mfma(pl, bh, oacc[dt]);
+            if constexpr (LO) {
+                const uint4 bl = *reinterpret_cast<const uint4*>(vl + vo);
+                oacc[dt] = mfma(ph, bl, oacc[dt]);
+                oacc[dt] = mfma(pl, bl, oacc[dt]);
+            }
+        }
+    }
+    // (6) the partials of the items that reach this chunk
+    const int S = s.n_chunks;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int it = 16 * ig + (lane >> 4) * 4 + r;
+        if (vc[r] && pc[r] >= t0) {
+            const size_t pidx = (static_cast<size_t>(it) * s.H + head) * S + chunk;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) s.part_o[pidx * D + 16 * dt + (lane & 15)] = oacc[dt][r];
+            if ((lane & 15) == 0) {
+                s.part_ml[pidx * 2 + 0] = mr[r];
+                s.part_ml[pidx * 2 + 1] = lr[r];
+            }
+        }
+    }
+}
+
+bool attn_pf_supported(const StepArgs& s) {
+    return s.attn_pf && (s.D == 64 || s.D == 128) && s.Hkv > 0 && s.H % s.Hkv == 0 && s.H / s.Hkv <= 4;
+}
+
+template <int D, int CDT>
+static void launch_pf2(const StepArgs& s, int layer, int n_items, hipStream_t st) {
+    const dim3 grid(s.n_chunks, s.Hkv);
+    const int rep = s.H / s.Hkv;
+    const size_t lds = attn_pf_lds(D, CDT, rep);
+    switch (rep) {
+        case 1: hipLaunchKernelGGL((k_attn_pf<D, 1, CDT>), grid, dim3(256), lds, st, s, layer, n_items); break;
+        case 2: hipLaunchKernelGGL((k_attn_pf<D, 2, CDT>), grid, dim3(512), lds, st, s, layer, n_items); break;
+        case 3: hipLaunchKernelGGL((k_attn_pf<D, 3, CDT>), grid, dim3(768), lds, st, s, layer, n_items); break;
+        default: hipLaunchKernelGGL((k_attn_pf<D, 4, CDT>), grid, dim3(1024), lds, st, s, layer, n_items); break;
+    }
+}
+
+hipError_t launch_attn_pf(const StepArgs& s, int layer, int n_items, hipStream_t st) {
+    if (!attn_pf_supported(s) || n_items < 1 || n_items > 64) return hipErrorInvalidValue;
+    if (s.D == 64) {
+        if (s.cdt == kBF16) launch_pf2<64, kBF16>(s, layer, n_items, st);
+        else launch_pf2<64, kF32>(s, layer, n_items, st);
+    } else {
+        if (s.cdt == kBF16) launch_pf2<128, kBF16>(s, layer, n_items, st);
+        else launch_pf2<128, kF32>(s, layer, n_items, st);
+    }
+    return hipGetLastError();
+}
+
+template <int D, int CDT>
+static hipError_t attrs_pf(int lds) {
+    hipError_t e = hipSuccess;
+    auto one = [&](const void* fn) {
+        if (e == hipSuccess) e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    };
+    one(reinterpret_cast<const void*>(k_attn_pf<D, 1, CDT>));
+    one(reinterpret_cast<const void*>(k_attn_pf<D, 2, CDT>));
+    one(reinterpret_cast<const void*>(k_attn_pf<D, 3, CDT>));
+    one(reinterpret_cast<const void*>(k_attn_pf<D, 4, CDT>));
+    return e;
+}
+
 template <int KIND, int KT>
 static hipError_t attrs_ng(int lds) {
     hipError_t e = hipSuccess;
@@ -568,6 +847,7 @@ size_t mm_max_lds(const StepArgs& s) {
     size_t m = 0;
     const int Ks[3] = {s.d, s.H * s.D, s.F};
     for (int K : Ks) m = std::max(m, mm_lds(pick_kt(K), K == s.d, K));
+    if (s.D == 64 || s.D == 128) m = std::max(m, attn_pf_lds(s.D, kF32, 4));  // the batched prefill's attention
     return m;
 }
 
@@ -577,6 +857,10 @@ hipError_t mm_set_attributes(int lds) {
     if (e == hipSuccess) e = attrs_kind<MM_W13>(lds);
     if (e == hipSuccess) e = attrs_kind<MM_W2>(lds);
     if (e == hipSuccess) e = attrs_kind<MM_LOGITS>(lds);
+    if (e == hipSuccess) e = attrs_pf<64, kF32>(lds);
+    if (e == hipSuccess) e = attrs_pf<64, kBF16>(lds);
+    if (e == hipSuccess) e = attrs_pf<128, kF32>(lds);
+    if (e == hipSuccess) e = attrs_pf<128, kBF16>(lds);
     return e;
 }
 

@@ -301,6 +301,32 @@ def test_batched_prefill_bf16_mfma_matches_oracle(mm_kernel):
     compare(MM_SHAPE, arena, prompts, 2, 128, "bf16 batched prefill", batched=True)
 
 
+PF_ATTN = {
+    # (head_dim, H, Hkv, cache) with bf16 weights
+    "d64-rep3": (64, 9, 3, "F32"),
+    "d64-rep1": (64, 2, 2, "F32"),
+    "d128-rep4": (128, 8, 2, "F32"),
+    "d128-rep2": (128, 4, 2, "F32"),
+    "d64-rep2-bf16": (64, 4, 2, "BF16"),
+    "d128-rep4-bf16": (128, 8, 2, "BF16"),
+}
+
+
+@pytest.mark.parametrize("name", list(PF_ATTN))
+def test_batched_prefill_attention_matches_oracle(name):
+    """ds_prefill_batched with head_dim 64 or 128: the positions of a pass
+    share one sequence, so its attention (k_attn_pf) stages every 64-position
+    chunk once for all of them and multiplies on the matrix cores.  Prompts of
+    2, 17, 64, 65, 130 and 200 tokens: passes of one position and of 64,
+    chunk edges, up to four chunks; then two decode steps."""
+    D, H, Hkv, cdt = PF_ATTN[name]
+    shape = synth.small_shape(dim=128, n_heads=H, n_kv_heads=Hkv, head_dim=D, hidden_dim=192, vocab_size=256,
+                              weight_dtype=synth.BF16, cache_dtype=getattr(synth, cdt))
+    arena = synth.make_arena(shape, 47, std=0.1, gain_sigma=0.1)
+    prompts = [synth.random_tokens(1200 + b, n, shape.vocab_size) for b, n in enumerate([2, 17, 64, 65, 130, 200])]
+    compare(shape, arena, prompts, 2, 256, f"batched prefill attention {name}", batched=True)
+
+
 @pytest.mark.parametrize("B,shape", [(20, MM_SHAPE), (70, MM_SHAPE), (37, MM_SHAPE2), (18, MM_SHAPE_LONG)],
                          ids=["20", "70", "37-k192", "18-long-rows"])
 def test_batched_mfma_projections_match_oracle(B, shape, mm_kernel):
