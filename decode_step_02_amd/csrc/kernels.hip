@@ -1727,8 +1727,11 @@ hipError_t enqueue_step(const StepArgs& s0, const ModelPtrs& m, const BeginList*
         for (int j = 0; j < lists[i].n; j++)
             if (lists[i].by_value && lists[i].off[j] != 0) s.kv_stream = 0;
     // the items are positions of one sequence (a batched prefill pass): they
-    // share its cached rows, and attention can read them once per chunk
-    bool one_seq = n_lists == 1 && lists[0].by_value == 1 && lists[0].n == n_items && n_items <= kMaxItems;
+    // share its cached rows, and attention can read them once per chunk.  A
+    // pass of one position keeps the decode kernels, so that ds_prefill
+    // reproduces decode steps bit for bit.
+    bool one_seq = n_lists == 1 && lists[0].by_value == 1 && lists[0].n == n_items && n_items >= 2 &&
+                   n_items <= kMaxItems;
     for (int j = 1; one_seq && j < lists[0].n; j++) one_seq = lists[0].slot[j] == lists[0].slot[0];
     const bool pf = one_seq && s.mm_ok && attn_pf_supported(s);
     Launch lc;
