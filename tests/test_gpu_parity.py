@@ -192,6 +192,39 @@ def test_tiny_uncached_equals_cached_on_gpu():
     assert passes == 68
 
 
+def test_prefill_reproduces_decode_steps_bitwise_past_the_short_path():
+    """ds_prefill feeds one position per pass through the decode kernels, so
+    re-prefilling a sequence together with its decoded tokens gives the decode
+    steps' logits bit for bit, also with head_dim 64 and bf16 weights, whose
+    multi-position passes take another attention kernel, and past the short
+    path (positions 70.., split-K attention)."""
+    torch = _torch()
+    import decode_step_02_amd as dsa
+    shape = synth.small_shape(dim=128, n_heads=4, n_kv_heads=2, head_dim=64, hidden_dim=192, vocab_size=256,
+                              weight_dtype=synth.BF16)
+    arena = synth.make_arena(shape, 48, std=0.1, gain_sigma=0.1)
+    prompt = [int(t) for t in synth.random_tokens(1300, 70, shape.vocab_size)]
+    model = dsa.Model(shape, arena)
+    kv = dsa.KVCache(model, 2, 128)
+    out = torch.zeros(2, dtype=torch.int32, device="cuda")
+    kv.prefill(1, prompt, out)
+    toks, lgs = [int(out[1].item())], [kv.logits().cpu().numpy()[1].copy()]
+    for _ in range(4):
+        kv.decode_step_rows([1], out, out)
+        toks.append(int(out[1].item()))
+        lgs.append(kv.logits().cpu().numpy()[1].copy())
+    seq = list(prompt)
+    for k in range(5):
+        kv.reset(1)
+        kv.prefill(1, seq, out)
+        assert int(out[1].item()) == toks[k]
+        assert np.array_equal(kv.logits().cpu().numpy()[1].view(np.uint32), lgs[k].view(np.uint32)), f"step {k}"
+        seq.append(toks[k])
+    kv.check()
+    kv.close()
+    model.close()
+
+
 def test_ragged_batch_tiny_matches_oracle():
     shape = dataclasses.replace(synth.TINY, n_kv_heads=1)
     arena = synth.make_arena(shape, 4, std=0.15, gain_sigma=0.1)
