@@ -284,18 +284,22 @@ __global__ __launch_bounds__(256) void k_mm(StepArgs s, LayerW w, int layer, int
 // partial sums of squares) through LDS.  Waves w < 4 then finish row r = w of
 // each lane's four (tile rows kq*4 + w), with the epilogues of k_mm.  The
 // item groups of one row tile are 8 block indices apart, so they run on the
-// same XCD and share its L2 copy of the weight tile.
-template <int KIND, int MAXS, bool LOOP, int NW = 4>
+// same XCD and share its L2 copy of the weight tile.  With RT > 1 a block
+// takes RT row tiles and each wave multiplies every activation operand it
+// loads (and splits) by all of them.
+template <int KIND, int MAXS, bool LOOP, int NW = 4, int RT = 1>
 __global__ __launch_bounds__(64 * NW) void k_mm_sk(StepArgs s, LayerW w, int layer, int n_items, int ident, int n_tiles,
                                                     int n_groups) {
     constexpr bool NORM = KIND == MM_QKV || KIND == MM_W13;
     constexpr bool TWO = KIND == MM_W13;
-    __shared__ float red[NW][9][64];  // [wave][acc 0..3, acc3 0..3, sum of squares][lane]
+    static_assert(!(TWO && RT > 1), "W1/W3 take one row tile per block");
+    constexpr int NR = TWO ? 9 : 4 * RT + 1;  // LDS rows per wave: acc of each tile (acc3), sum of squares
+    __shared__ float red[NW][NR][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ti = lane & 15, kq = lane >> 4;
     const int L = blockIdx.x, span = 8 * n_groups;
-    const int grp = (L % span) / 8, tile = (L / span) * 8 + L % 8;
-    if (tile >= n_tiles) return;  // padding of the last eight row tiles (whole block)
+    const int grp = (L % span) / 8, tg = (L / span) * 8 + L % 8;  // row tiles tg*RT .. tg*RT + RT-1
+    if (tg * RT >= n_tiles) return;  // padding of the last eight tile groups (whole block)
 
     int K = s.d, N = 0;
     const void* W = nullptr;
@@ -309,26 +313,39 @@ __global__ __launch_bounds__(64 * NW) void k_mm_sk(StepArgs s, LayerW w, int lay
 
     const int D = s.D, half_d = s.D / 2;
     const int nq_t = s.H * D / 16, nk_t = s.Hkv * D / 16;
-    int row = 0;
-    bool roped = false, is_q = false;
-    if (KIND == MM_QKV) {
-        roped = tile < nq_t + nk_t;
-        is_q = tile < nq_t;
-        if (roped) {
-            const int p = (is_q ? tile : tile - nq_t) * 8 + (ti & 7);
-            row = (p / half_d) * D + p % half_d + (ti >> 3) * half_d;
-            W = is_q ? w.wq : w.wk;
+    // each of the block's row tiles: its weight rows (tiles past n_tiles are
+    // loaded clamped and not stored)
+    int tl[RT];
+    bool roped[RT], is_q[RT];
+    const uint16_t* Wrow[RT];
+#pragma unroll
+    for (int t = 0; t < RT; t++) {
+        tl[t] = min(tg * RT + t, n_tiles - 1);
+        const int tile = tl[t];
+        int row = 0;
+        const void* Wt = W;
+        roped[t] = is_q[t] = false;
+        if (KIND == MM_QKV) {
+            roped[t] = tile < nq_t + nk_t;
+            is_q[t] = tile < nq_t;
+            if (roped[t]) {
+                const int p = (is_q[t] ? tile : tile - nq_t) * 8 + (ti & 7);
+                row = (p / half_d) * D + p % half_d + (ti >> 3) * half_d;
+                Wt = is_q[t] ? w.wq : w.wk;
+            } else {
+                row = (tile - nq_t - nk_t) * 16 + ti;
+                Wt = w.wv;
+            }
         } else {
-            row = (tile - nq_t - nk_t) * 16 + ti;
-            W = w.wv;
+            row = min(tile * 16 + ti, N - 1);
         }
-    } else {
-        row = min(tile * 16 + ti, N - 1);
+        Wrow[t] = static_cast<const uint16_t*>(Wt) + static_cast<size_t>(row) * K + kq * 8;
     }
     const int item = grp * 16 + ti;
     const bool m_ok = item < n_items;
-    const uint16_t* Wrow = static_cast<const uint16_t*>(W) + static_cast<size_t>(row) * K + kq * 8;
-    const uint16_t* W3row = TWO ? static_cast<const uint16_t*>(W3) + static_cast<size_t>(row) * K + kq * 8 : Wrow;
+    const uint16_t* W3row = TWO ? static_cast<const uint16_t*>(W3) +
+                                      static_cast<size_t>(min(tl[0] * 16 + ti, N - 1)) * K + kq * 8
+                                : Wrow[0];
     const float* xrow = src + static_cast<size_t>(min(item, n_items - 1)) * K + kq * 8;
     const float* grow = NORM ? gain + kq * 8 : nullptr;
 
@@ -336,24 +353,31 @@ __global__ __launch_bounds__(64 * NW) void k_mm_sk(StepArgs s, LayerW w, int lay
     // position, slot and RoPE angle (Q/K/V) of the row this lane finishes
     const int ri = kq * 4 + wave;  // tile row this lane finishes (r = wave)
     const int item_c = min(item, n_items - 1);
-    float xres = 0.f, rc = 1.f, rsn = 0.f;
+    float xres[RT], rc[RT], rsn[RT];
     int pos = 0, slot = 0;
-    if (KIND == MM_WO || KIND == MM_W2) xres = s.x[static_cast<size_t>(item_c) * s.d + min(tile * 16 + ri, N - 1)];
     if (KIND == MM_QKV) {
         pos = s.pos[item_c];
         slot = ident ? item_c : s.slot[item_c];
-        if (roped) {
-            const int ii = ((is_q ? tile : tile - nq_t) * 8 + (ri & 7)) % half_d;
-            rc = s.rope_cos[static_cast<size_t>(pos) * half_d + ii];
-            rsn = s.rope_sin[static_cast<size_t>(pos) * half_d + ii];
+    }
+#pragma unroll
+    for (int t = 0; t < RT; t++) {
+        xres[t] = 0.f;
+        rc[t] = 1.f;
+        rsn[t] = 0.f;
+        if (KIND == MM_WO || KIND == MM_W2) xres[t] = s.x[static_cast<size_t>(item_c) * s.d + min(tl[t] * 16 + ri, N - 1)];
+        if (KIND == MM_QKV && roped[t]) {
+            const int ii = ((is_q[t] ? tl[t] : tl[t] - nq_t) * 8 + (ri & 7)) % half_d;
+            rc[t] = s.rope_cos[static_cast<size_t>(pos) * half_d + ii];
+            rsn[t] = s.rope_sin[static_cast<size_t>(pos) * half_d + ii];
         }
     }
-    // The wave's k-steps are wave + 4 i.  Without LOOP all of them (at most
+    // The wave's k-steps are wave + NW i.  Without LOOP all of them (at most
     // MAXS) are loaded at once; with LOOP they go in batches of MAXS, the
     // next batch's loads issued before this batch's products (long rows).
+    // Each activation operand serves the RT row tiles.
     const int nks = K / 32;
     struct Batch {
-        uint4 wa[MAXS], wb[MAXS];
+        uint4 wa[RT][MAXS], wb[MAXS];
         float4 xa[MAXS], xb[MAXS], ga[MAXS], gb[MAXS];
     };
     auto load = [&](Batch& bt, int i0) {
@@ -362,7 +386,8 @@ __global__ __launch_bounds__(64 * NW) void k_mm_sk(StepArgs s, LayerW w, int lay
             const int ks = wave + NW * (i0 + i);
             if (ks < nks) {
                 const int k0 = ks * 32;
-                bt.wa[i] = *reinterpret_cast<const uint4*>(Wrow + k0);
+#pragma unroll
+                for (int t = 0; t < RT; t++) bt.wa[t][i] = *reinterpret_cast<const uint4*>(Wrow[t] + k0);
                 if (TWO) bt.wb[i] = *reinterpret_cast<const uint4*>(W3row + k0);
                 bt.xa[i] = *reinterpret_cast<const float4*>(xrow + k0);
                 bt.xb[i] = *reinterpret_cast<const float4*>(xrow + k0 + 4);
@@ -373,7 +398,9 @@ __global__ __launch_bounds__(64 * NW) void k_mm_sk(StepArgs s, LayerW w, int lay
             }
         }
     };
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, acc3 = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[RT], acc3 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < RT; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
     auto products = [&](const Batch& bt, int i0) {
 #pragma unroll
@@ -403,8 +430,11 @@ __global__ __launch_bounds__(64 * NW) void k_mm_sk(StepArgs s, LayerW w, int lay
                     }
                 }
                 const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]), bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-                acc = mfma(bt.wa[i], bh, acc);
-                acc = mfma(bt.wa[i], bl, acc);
+#pragma unroll
+                for (int t = 0; t < RT; t++) {
+                    acc[t] = mfma(bt.wa[t][i], bh, acc[t]);
+                    acc[t] = mfma(bt.wa[t][i], bl, acc[t]);
+                }
                 if (TWO) {
                     acc3 = mfma(bt.wb[i], bh, acc3);
                     acc3 = mfma(bt.wb[i], bl, acc3);
@@ -431,48 +461,58 @@ __global__ __launch_bounds__(64 * NW) void k_mm_sk(StepArgs s, LayerW w, int lay
     }
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-        red[wave][r][lane] = acc[r];
+#pragma unroll
+        for (int t = 0; t < RT; t++) red[wave][4 * t + r][lane] = acc[t][r];
         if (TWO) red[wave][4 + r][lane] = acc3[r];
     }
-    if (NORM) red[wave][8][lane] = ss;
+    if (NORM) red[wave][NR - 1][lane] = ss;
     __syncthreads();
-    if (wave >= 4) return;  // waves 0..3 finish the tile's rows
-    const int r = wave;  // this wave finishes tile row kq * 4 + r (= ri)
-    float y = 0.f, y3 = 0.f, sq = 0.f;
+    if (wave >= 4) return;  // waves 0..3 finish the tiles' rows
+    const int r = wave;  // this wave finishes tile row kq * 4 + r (= ri) of every tile
+    float sq = 0.f;
+    if (NORM) {
 #pragma unroll
-    for (int v = 0; v < NW; v++) {
-        y += red[v][r][lane];
-        if (TWO) y3 += red[v][4 + r][lane];
-        if (NORM) sq += red[v][8][lane];
+        for (int v = 0; v < NW; v++) sq += red[v][NR - 1][lane];
     }
     float r_m = 1.f;
     if (NORM) r_m = 1.0f / sqrtf(sq / static_cast<float>(K) + s.eps);
     const int i = ri;
-    if (KIND == MM_QKV) {
-        y *= r_m;
-        const float partner = __shfl_xor(y, 32);  // tile rows i and i ^ 8 of the same item
-        if (!m_ok || tile * 16 >= N) return;
-        if (roped) {
-            const int p = (is_q ? tile : tile - nq_t) * 8 + (i & 7);
-            const int ii = p % half_d, second = i >> 3;
-            const int orow = (p / half_d) * D + ii + second * half_d;
-            const float c = rc, sn = rsn;
-            const float out = second ? fmaf(partner, sn, y * c) : fmaf(-partner, sn, y * c);
-            if (is_q)
-                s.q[static_cast<size_t>(item) * s.H * D + orow] = out;
-            else
-                cache_put(s, cache_row(s, layer, 0, slot, orow / D, pos) + orow % D, out);
-        } else {
-            const int orow = (tile - nq_t - nk_t) * 16 + i;
-            cache_put(s, cache_row(s, layer, 1, slot, orow / D, pos) + orow % D, y);
+#pragma unroll
+    for (int t = 0; t < RT; t++) {
+        const int tile = tl[t];
+        const bool t_ok = tg * RT + t < n_tiles;
+        float y = 0.f, y3 = 0.f;
+#pragma unroll
+        for (int v = 0; v < NW; v++) {
+            y += red[v][4 * t + r][lane];
+            if (TWO) y3 += red[v][4 + r][lane];
         }
-    } else if (KIND == MM_WO || KIND == MM_W2) {
-        const int orow = tile * 16 + i;
-        if (m_ok && orow < N) s.x[static_cast<size_t>(item) * s.d + orow] = xres + y;
-    } else {  // MM_W13
-        const int orow = tile * 16 + i;
-        const float a = y * r_m, u = y3 * r_m;
-        if (m_ok && orow < N) s.h[static_cast<size_t>(item) * s.F + orow] = (a / (1.0f + expf(-a))) * u;
+        if (KIND == MM_QKV) {
+            y *= r_m;
+            const float partner = __shfl_xor(y, 32);  // tile rows i and i ^ 8 of the same item
+            if (!m_ok || !t_ok || tile * 16 >= N) continue;
+            if (roped[t]) {
+                const int p = (is_q[t] ? tile : tile - nq_t) * 8 + (i & 7);
+                const int ii = p % half_d, second = i >> 3;
+                const int orow = (p / half_d) * D + ii + second * half_d;
+                const float c = rc[t], sn = rsn[t];
+                const float out = second ? fmaf(partner, sn, y * c) : fmaf(-partner, sn, y * c);
+                if (is_q[t])
+                    s.q[static_cast<size_t>(item) * s.H * D + orow] = out;
+                else
+                    cache_put(s, cache_row(s, layer, 0, slot, orow / D, pos) + orow % D, out);
+            } else {
+                const int orow = (tile - nq_t - nk_t) * 16 + i;
+                cache_put(s, cache_row(s, layer, 1, slot, orow / D, pos) + orow % D, y);
+            }
+        } else if (KIND == MM_WO || KIND == MM_W2) {
+            const int orow = tile * 16 + i;
+            if (m_ok && t_ok && orow < N) s.x[static_cast<size_t>(item) * s.d + orow] = xres[t] + y;
+        } else {  // MM_W13
+            const int orow = tile * 16 + i;
+            const float a = y * r_m, u = y3 * r_m;
+            if (m_ok && t_ok && orow < N) s.h[static_cast<size_t>(item) * s.F + orow] = (a / (1.0f + expf(-a))) * u;
+        }
     }
 }
 
@@ -875,20 +915,25 @@ static void sk_dims(const StepArgs& s, int& K, int& N) {
     if (KIND == MM_W2) { N = s.d; K = s.F; }
 }
 
-template <int KIND, int MAXS, bool LOOP = false, int NW = 4>
+template <int KIND, int MAXS, bool LOOP = false, int NW = 4, int RT = 1>
 static void launch_sk_one(const StepArgs& s, const LayerW& w, int layer, int n, int ident, int n_tiles, hipStream_t st) {
     const int n_groups = (n + 15) / 16;
-    const dim3 grid(((n_tiles + 7) / 8) * 8 * n_groups);
-    hipLaunchKernelGGL((k_mm_sk<KIND, MAXS, LOOP, NW>), grid, dim3(64 * NW), 0, st, s, w, layer, n, ident, n_tiles,
+    const int n_tg = (n_tiles + RT - 1) / RT;  // groups of RT row tiles
+    const dim3 grid(((n_tg + 7) / 8) * 8 * n_groups);
+    hipLaunchKernelGGL((k_mm_sk<KIND, MAXS, LOOP, NW, RT>), grid, dim3(64 * NW), 0, st, s, w, layer, n, ident, n_tiles,
                        n_groups);
 }
 
 // Rows of up to 8 k-steps per wave (5 for the kinds with gains, registers)
 // take 8-wave blocks (W1/W3 and W2 of up to 48 k-steps: 16-wave blocks) with
-// every load issued at once; longer rows take 4-wave
-// blocks that loop over batches of 4 k-steps, except W1/W3, whose tiled
-// kernel reads each weight once for all 64 items.  false: the tiled kernel
-// runs instead.
+// every load issued at once.  Longer rows take 4-wave blocks that loop over
+// batches of kLoopMaxs k-steps, each wave multiplying every activation
+// operand it loads by kLoopRt row tiles, so the activations are read from L2
+// once per 64 weight rows instead of once per 16 (the 8B 4096-token batched
+// prefill: 979 -> 749 ms; 2 or 8 tiles, and batches of 1 to 4 k-steps,
+// measured slower) -- except W1/W3, whose tiled kernel reads each weight once
+// for all 64 items.  false: the tiled kernel runs instead.
+constexpr int kLoopRt = 4, kLoopMaxs = 2;
 template <int KIND>
 static bool launch_sk(const StepArgs& s, const LayerW& w, int layer, int n, int ident, hipStream_t st) {
     int K = 0, N = 0;
@@ -922,7 +967,7 @@ static bool launch_sk(const StepArgs& s, const LayerW& w, int layer, int n, int 
     if constexpr (KIND == MM_W13) {
         return false;
     } else {
-        launch_sk_one<KIND, 4, true, 4>(s, w, layer, n, ident, nt, st);
+        launch_sk_one<KIND, kLoopMaxs, true, 4, kLoopRt>(s, w, layer, n, ident, nt, st);
         return true;
     }
 }
