@@ -37,9 +37,27 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum MMKind { MM_QKV, MM_WO, MM_W13, MM_W2, MM_LOGITS };
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// x = hi + lo in bf16, both rounded to nearest even, for two values at once:
+// the pair's hi terms packed in one word (element 0 in the low half), and
+// their lo terms in another.  The conversion is gfx950's v_cvt_pk_bf16_f32,
+// one instruction per pair, whose round to nearest even gives the same bits
+// as the integer rounding (u + 0x7FFF + bit 16 of u) >> 16 for finite values.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                          f32x2{a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u)},
+                                          bf16x2));
+}
+
+// 8 values into two A/B operands (hi terms, lo terms)
+__device__ __forceinline__ void split8(const float4 a, const float4 b, uint4& hi, uint4& lo) {
+    split2(a.x, a.y, hi.x, lo.x);
+    split2(a.z, a.w, hi.y, lo.y);
+    split2(b.x, b.y, hi.z, lo.z);
+    split2(b.z, b.w, hi.w, lo.w);
 }
 
 __device__ __forceinline__ f32x4 mfma(const uint4 a, const uint4 b, f32x4 c) {
@@ -132,25 +150,18 @@ __global__ __launch_bounds__(256) void k_mm(StepArgs s, LayerW w, int layer, int
         // fp32 -> bf16 hi + lo into LDS, gains applied
 #pragma unroll
         for (int q = 0; q < SV; q += 2) {
-            uint32_t hi[4], lo[4];
             const float xs[8] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w, xv[q + 1].x, xv[q + 1].y, xv[q + 1].z, xv[q + 1].w};
+            float val[8];
 #pragma unroll
             for (int c = 0; c < 8; c++) {
                 const float x = s_ok ? xs[c] : 0.f;
                 ss = fmaf(x, x, ss);
-                const float val = NORM ? gs[k0 + sk + q * 4 + c] * x : x;
-                const uint32_t h = bf16_bits_rne(val);
-                const uint32_t l = bf16_bits_rne(val - __uint_as_float(h << 16));
-                if (c & 1) {
-                    hi[c >> 1] |= h << 16;
-                    lo[c >> 1] |= l << 16;
-                } else {
-                    hi[c >> 1] = h;
-                    lo[c >> 1] = l;
-                }
+                val[c] = NORM ? gs[k0 + sk + q * 4 + c] * x : x;
             }
-            *reinterpret_cast<uint4*>(xh + sm * LDK + sk + q * 4) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            *reinterpret_cast<uint4*>(xl + sm * LDK + sk + q * 4) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            uint4 hi, lo;
+            split8(make_float4(val[0], val[1], val[2], val[3]), make_float4(val[4], val[5], val[6], val[7]), hi, lo);
+            *reinterpret_cast<uint4*>(xh + sm * LDK + sk + q * 4) = hi;
+            *reinterpret_cast<uint4*>(xl + sm * LDK + sk + q * 4) = lo;
         }
         __syncthreads();
         // the next tile's loads fly while this tile's MFMAs run
@@ -413,23 +424,16 @@ __global__ __launch_bounds__(64 * NW) void k_mm_sk(StepArgs s, LayerW w, int lay
                     gv[0] = bt.ga[i].x; gv[1] = bt.ga[i].y; gv[2] = bt.ga[i].z; gv[3] = bt.ga[i].w;
                     gv[4] = bt.gb[i].x; gv[5] = bt.gb[i].y; gv[6] = bt.gb[i].z; gv[7] = bt.gb[i].w;
                 }
-                uint32_t hi[4], lo[4];
+                float val[8];
 #pragma unroll
                 for (int c = 0; c < 8; c++) {
                     const float x = m_ok ? xs[c] : 0.f;
                     ss = fmaf(x, x, ss);
-                    const float val = NORM ? gv[c] * x : x;
-                    const uint32_t h = bf16_bits_rne(val);
-                    const uint32_t l = bf16_bits_rne(val - __uint_as_float(h << 16));
-                    if (c & 1) {
-                        hi[c >> 1] |= h << 16;
-                        lo[c >> 1] |= l << 16;
-                    } else {
-                        hi[c >> 1] = h;
-                        lo[c >> 1] = l;
-                    }
+                    val[c] = NORM ? gv[c] * x : x;
                 }
-                const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]), bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                uint4 bh, bl;
+                split8(make_float4(val[0], val[1], val[2], val[3]), make_float4(val[4], val[5], val[6], val[7]), bh,
+                       bl);
 #pragma unroll
                 for (int t = 0; t < RT; t++) {
                     acc[t] = mfma(bt.wa[t][i], bh, acc[t]);
@@ -615,25 +619,6 @@ size_t attn_pf_lds(int D, int cdt, int rep) {
            sizeof(float) * 4 * rep * 16 * kPfPP;
 }
 
-// x = hi + lo in bf16 (both nearest even), 8 values into two A/B operands
-__device__ __forceinline__ void split8(const float4 a, const float4 b, uint4& hi, uint4& lo) {
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int c = 0; c < 8; c++) {
-        const uint32_t hb = bf16_bits_rne(v[c]);
-        const uint32_t lb = bf16_bits_rne(v[c] - __uint_as_float(hb << 16));
-        if (c & 1) {
-            h[c >> 1] |= hb << 16;
-            l[c >> 1] |= lb << 16;
-        } else {
-            h[c >> 1] = hb;
-            l[c >> 1] = lb;
-        }
-    }
-    hi = make_uint4(h[0], h[1], h[2], h[3]);
-    lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
 
 template <int D, int REP, int CDT>
 __global__ __launch_bounds__(256 * REP) void k_attn_pf(StepArgs s, int layer, int n_items) {
