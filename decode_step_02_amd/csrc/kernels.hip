@@ -1649,8 +1649,18 @@ hipError_t set_kernel_attributes(int lds) {
 
 // ---- step enqueue ---------------------------------------------------------------------------------
 
+// Workgroups go to the 8 XCDs round-robin by flattened index, chunk +
+// gridDim.x * (group + Hkv * item).  With gridDim.x a multiple of 8, chunk c
+// of every (item, group) lands on XCD c mod 8: at 16 chunks and ragged
+// contexts XCD 0 takes chunks 0 and 8, always or often in use, and XCD 7
+// chunks 7 and 15, often empty, so the busiest XCD streams about 1.4 times
+// the mean.  A grid width of 1 mod 8 shifts each pair's chunks by one XCD
+// from the previous pair's.  The added chunk indices start at or past T, so
+// their blocks return at once (t0 >= n).
+static int attn_grid_x(int n_chunks) { return n_chunks < 8 ? n_chunks : n_chunks + (9 - n_chunks % 8) % 8; }
+
 static hipError_t launch_attn(const StepArgs& s, int layer, int n_items, hipStream_t st) {
-    const dim3 grid(s.n_chunks, s.Hkv, n_items);
+    const dim3 grid(attn_grid_x(s.n_chunks), s.Hkv, n_items);
     if (s.attn_g && s.D == 64 && launch_attn_g<64>(s, grid, layer, st)) return hipGetLastError();
     if (s.attn_g && s.D == 128 && launch_attn_g<128>(s, grid, layer, st)) return hipGetLastError();
     switch (s.D) {
