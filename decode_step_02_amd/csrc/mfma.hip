@@ -576,7 +576,12 @@ static hipError_t launch_kind(const StepArgs& s, const LayerW& w, int layer, int
     // The vocabulary product takes 64-wide k-tiles: a third of the LDS per
     // block, so more of its blocks share a CU (B = 64, 135M: 28.5 against
     // 45.5 us per launch with 192-wide tiles).
-    const int kt = KIND == MM_LOGITS ? 64 : pick_kt(K);
+    // W1/W3 over rows of 2048 or more takes 128-wide k-tiles (8B batched
+    // prefill: 733.5 -> 718.0 ms; 256-wide tiles, or 32 or 16 items per block
+    // with twice or four times the blocks, were slower).
+    const int kt = KIND == MM_LOGITS                ? 64
+                   : KIND == MM_W13 && K >= 2048 ? (K % 128 == 0 ? 128 : 64)
+                                                    : pick_kt(K);
     const size_t lds = mm_lds(kt, norm, K);
     switch (kt) {
         case 256: launch_ng<KIND, 256>(ng, grid, lds, s, w, layer, m0, n, ident, out_norm, wcls, st); break;
