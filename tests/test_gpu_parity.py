@@ -411,6 +411,11 @@ LONG_ATTN = {
     # group), so past 48 chunks (3072 positions) it takes several batches;
     # the short sequences also run the fused short-context path at D = 256
     "d256-b16-multibatch": (256, 8, 2, [3100, 3080] + [5 + 3 * i for i in range(14)], 3136),
+    # head_dim 64 (k_attn_g<64, 3>) with 10 chunk slots: the launch grid is
+    # 17 chunk indices wide (1 mod 8, so each sequence's chunks start on the
+    # next XCD), the 7 past the cache returning at once; lengths reach every
+    # chunk from the first to the last, each sequence ragged in its last
+    "d64-b6-T640-grid17": (64, 6, 2, [600, 530, 70, 260, 129, 3], 640),
 }
 
 
