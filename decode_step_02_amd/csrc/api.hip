@@ -681,6 +681,7 @@ ds_status ds_prefill_batched(ds_model* model, ds_kv* kv, int32_t seq, const int3
             list.last[i] = 0;
             list.off[i] = i;
         }
+        list.last_pos = kv->mirror[seq] + m - 1;  // sizes the attention launch to the chunks in use
         hipError_t e = ds::enqueue_step(kv->s, model->ptrs, &list, 1, nullptr, m, false, 0, nullptr, st);
         if (e != hipSuccess) return hip_fail(e, "batched prefill");
         kv->mirror[seq] += m;

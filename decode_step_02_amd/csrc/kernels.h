@@ -111,6 +111,7 @@ struct BeginList {
     int32_t tok[kMaxItems];
     int32_t last[kMaxItems];
     int32_t off[kMaxItems] = {};  // by_value: position = lengths[slot] + off (several positions of one slot)
+    int last_pos = -1;  // the positions of one slot: the last of them as the host knows it (-1: not known)
 };
 // by_value: 0 items are the slots 0..n-1 with tokens d_tok_in[slot]; 1 slots
 // and tokens from the arrays (prefill); 2 slots from the array, tokens
@@ -191,10 +192,12 @@ hipError_t mm_set_attributes(int lds);
 // Attention of a pass whose n_items (<= 64) items are positions of one
 // sequence (slot[0]): one block per (chunk, key/value group) on the matrix
 // cores, partials for the merge launch.  head_dim 64 or 128, at most 4 query
-// heads per key/value head, s.attn_pf set.
+// heads per key/value head, s.attn_pf set.  Blocks cover chunks [0,
+// n_chunks) (1 <= n_chunks <= s.n_chunks); a pass whose last position on
+// the device lies past them sets error bit 2 (launch shape).
 bool attn_pf_supported(const StepArgs& s);
 size_t attn_pf_lds(int D, int cdt, int rep);
-hipError_t launch_attn_pf(const StepArgs& s, int layer, int n_items, hipStream_t st);
+hipError_t launch_attn_pf(const StepArgs& s, int layer, int n_items, int n_chunks, hipStream_t st);
 hipError_t mm_gemv(int which, const StepArgs& s, const LayerW& w, int layer, int n_items, int ident,
                    const float* out_norm, const void* wcls, hipStream_t st);
 // Longest context (a power of two <= min(kShort, T)) whose short-path staging fits in

@@ -1744,6 +1744,10 @@ hipError_t enqueue_step(const StepArgs& s0, const ModelPtrs& m, const BeginList*
                    n_items <= kMaxItems;
     for (int j = 1; one_seq && j < lists[0].n; j++) one_seq = lists[0].slot[j] == lists[0].slot[0];
     const bool pf = one_seq && s.mm_ok && attn_pf_supported(s);
+    // its attention blocks: the chunks up to the pass's last position when
+    // the host knows it, else every chunk slot of the cache
+    const int pf_chunks = pf && lists[0].last_pos >= 0 ? std::min(s.n_chunks, lists[0].last_pos / kChunk + 1)
+                                                       : s.n_chunks;
     Launch lc;
     lc.ident = d_tok_in != nullptr && lists[0].by_value == 0;  // item == slot
     const bool mm = use_mm(s, n_items);
@@ -1763,7 +1767,7 @@ hipError_t enqueue_step(const StepArgs& s0, const ModelPtrs& m, const BeginList*
             if (attn_full(s, n_items)) {
                 e = launch_attn_full(s, l, n_items, st);
             } else if (pf) {
-                e = launch_attn_pf(s, l, n_items, st);
+                e = launch_attn_pf(s, l, n_items, pf_chunks, st);
                 if (e == hipSuccess) e = launch_combine(s, n_items, st);
             } else {
                 e = launch_attn(s, l, n_items, st);

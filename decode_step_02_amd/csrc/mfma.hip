@@ -690,6 +690,11 @@ __global__ __launch_bounds__(256 * REP) void k_attn_pf(StepArgs s, int layer, in
     }
     __syncthreads();
     const int maxpos = smax;
+    // the host sized the grid from its record of the sequence's length; a
+    // pass that reaches past the grid's chunks (the device's lengths moved
+    // on without the host, e.g. replayed captured steps) misses rows: flag it
+    if (maxpos >= kChunk * static_cast<int>(gridDim.x) && chunk == 0 && g == 0 && threadIdx.x == 0)
+        atomicOr(s.err, 2);
     if (t0 > maxpos) return;  // whole block
     const int rlast = min(kChunk - 1, maxpos - t0);
     // (2) the staged rows: keys as loaded (rows past rlast never pass the
@@ -814,8 +819,8 @@ bool attn_pf_supported(const StepArgs& s) {
 }
 
 template <int D, int CDT>
-static void launch_pf2(const StepArgs& s, int layer, int n_items, hipStream_t st) {
-    const dim3 grid(s.n_chunks, s.Hkv);
+static void launch_pf2(const StepArgs& s, int layer, int n_items, int n_chunks, hipStream_t st) {
+    const dim3 grid(n_chunks, s.Hkv);
     const int rep = s.H / s.Hkv;
     const size_t lds = attn_pf_lds(D, CDT, rep);
     switch (rep) {
@@ -826,14 +831,15 @@ static void launch_pf2(const StepArgs& s, int layer, int n_items, hipStream_t st
     }
 }
 
-hipError_t launch_attn_pf(const StepArgs& s, int layer, int n_items, hipStream_t st) {
-    if (!attn_pf_supported(s) || n_items < 1 || n_items > 64) return hipErrorInvalidValue;
+hipError_t launch_attn_pf(const StepArgs& s, int layer, int n_items, int n_chunks, hipStream_t st) {
+    if (!attn_pf_supported(s) || n_items < 1 || n_items > 64 || n_chunks < 1 || n_chunks > s.n_chunks)
+        return hipErrorInvalidValue;
     if (s.D == 64) {
-        if (s.cdt == kBF16) launch_pf2<64, kBF16>(s, layer, n_items, st);
-        else launch_pf2<64, kF32>(s, layer, n_items, st);
+        if (s.cdt == kBF16) launch_pf2<64, kBF16>(s, layer, n_items, n_chunks, st);
+        else launch_pf2<64, kF32>(s, layer, n_items, n_chunks, st);
     } else {
-        if (s.cdt == kBF16) launch_pf2<128, kBF16>(s, layer, n_items, st);
-        else launch_pf2<128, kF32>(s, layer, n_items, st);
+        if (s.cdt == kBF16) launch_pf2<128, kBF16>(s, layer, n_items, n_chunks, st);
+        else launch_pf2<128, kF32>(s, layer, n_items, n_chunks, st);
     }
     return hipGetLastError();
 }

@@ -213,7 +213,12 @@ ds_status ds_prefill(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_t
  * sections "Attention Mechanism Integration" and "Phase 1: Single Prefill".
  * Arguments, ownership and errors as for ds_prefill; lengths[seq] grows by n.
  * The result differs from ds_prefill's in rounding only (the projections of
- * 16 or more positions accumulate in another order). */
+ * 16 or more positions accumulate in another order).  Each pass's attention
+ * covers the cached rows up to the pass's last position as the host has
+ * recorded the sequence's length (the lengths ds_kv_cache_get_lengths
+ * returns); should the device's lengths have moved past that record, the
+ * launch-shape guard fires and the next ds_kv_cache_check returns
+ * DS_ERR_DEVICE. */
 ds_status ds_prefill_batched(ds_model* model, ds_kv* kv, int32_t seq, const int32_t* h_tokens, int32_t n,
                              int32_t* d_tok_out, void* stream);
 

@@ -528,6 +528,53 @@ def test_single_launch_replay_outside_its_context_class_is_reported():
     model.close()
 
 
+def test_batched_prefill_past_the_host_lengths_is_reported():
+    """ds_prefill_batched sizes each pass's attention launch to the
+    64-position chunks up to the pass's last position as the host recorded
+    the sequence's length.  Replays of a captured decode step move the
+    device's length on without the host: a batched prefill whose positions
+    then fall in a chunk the launch does not cover trips the launch-shape
+    guard (DS_ERR_DEVICE at the next check).  With the lengths set in step
+    again, the same prefill passes the check."""
+    torch = _torch()
+    import decode_step_02_amd as dsa
+    w = synth.WORKLOADS["llama135m_p5"]
+    arena = synth.make_arena(w.model, w.model_seed)
+    model = dsa.Model(w.model, arena)
+    kv = dsa.KVCache(model, 1, w.ctx)
+    prompt = [int(t) for t in synth.random_tokens(78, 60, w.model.vocab_size)]
+    extra = [int(t) for t in synth.random_tokens(79, 3, w.model.vocab_size)]
+    st = torch.cuda.Stream()
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(st):
+        kv.prefill(0, prompt, tok, st)
+        st.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            kv.decode_step(tok, tok, st)  # captured, not run
+        kv.set_lengths([60], st)
+        st.synchronize()
+        for _ in range(4):
+            g.replay()  # the device's length 61 .. 64; the host's stays 60
+        st.synchronize()
+        kv.check(st)
+        assert kv.lengths.cpu().tolist() == [64]
+        # batched positions 60, 61 for the host (chunk 0), 64, 65 on the device (chunk 1)
+        kv.prefill_batched(0, extra, tok, st)
+        st.synchronize()
+        with pytest.raises(dsa.DSError) as err:
+            kv.check(st)
+        assert err.value.status == -9  # DS_ERR_DEVICE
+        kv.set_lengths([64], st)
+        kv.prefill_batched(0, extra, tok, st)
+        st.synchronize()
+        kv.check(st)
+        assert kv.lengths.cpu().tolist() == [67]
+        assert torch.isfinite(kv.logits(st)).all()
+    kv.close()
+    model.close()
+
+
 FULL_ATTN = {
     # (head_dim, H, Hkv, cache): 64 sequences x Hkv >= 128 (item, group)
     # pairs, so decode steps take the one-block-per-pair attention; the
