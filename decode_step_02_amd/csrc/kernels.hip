@@ -1287,7 +1287,11 @@ __global__ __launch_bounds__(64) void k_attn_merge(StepArgs s) {
     for (int k = 0; k < DPL; k++) out[64 * k] = acc[k] / L;
 }
 
-static hipError_t launch_combine(const StepArgs& s, int n_items, hipStream_t st) {
+// max_chunks: the most chunks any item of the launch has as the host knows
+// it (s.n_chunks when it does not); it sizes each thread's batch of chunk
+// partials, and an item with more is still merged, in further batches.
+static hipError_t launch_combine(const StepArgs& s, int n_items, hipStream_t st, int max_chunks = 0) {
+    if (max_chunks < 1 || max_chunks > s.n_chunks) max_chunks = s.n_chunks;
     if (s.n_chunks <= kMergeChunks && (s.D == 64 || s.D == 128)) {
         const dim3 grid(s.H * n_items);
         if (s.D == 64) hipLaunchKernelGGL(k_attn_merge<64>, grid, dim3(64), 0, st, s);
@@ -1296,7 +1300,7 @@ static hipError_t launch_combine(const StepArgs& s, int n_items, hipStream_t st)
     }
     const int split = s.H * n_items < 128 && s.D >= 128 ? 4 : 1;  // few heads: each head's dims over 4 blocks
     const int Dh = s.D / split;
-    const int per = (s.n_chunks + 256 / Dh - 1) / (256 / Dh);  // chunks per thread, all in one batch if it fits
+    const int per = (max_chunks + 256 / Dh - 1) / (256 / Dh);  // chunks per thread, all in one batch if it fits
     const dim3 grid(s.H, n_items, split);
     const size_t lds = sizeof(float) * s.n_chunks;
     if (per <= 8)
@@ -1768,7 +1772,7 @@ hipError_t enqueue_step(const StepArgs& s0, const ModelPtrs& m, const BeginList*
                 e = launch_attn_full(s, l, n_items, st);
             } else if (pf) {
                 e = launch_attn_pf(s, l, n_items, pf_chunks, st);
-                if (e == hipSuccess) e = launch_combine(s, n_items, st);
+                if (e == hipSuccess) e = launch_combine(s, n_items, st, pf_chunks);
             } else {
                 e = launch_attn(s, l, n_items, st);
                 if (e == hipSuccess) e = launch_combine(s, n_items, st);
