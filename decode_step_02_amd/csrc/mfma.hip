@@ -24,6 +24,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device.h"
@@ -930,6 +931,34 @@ static void launch_sk_one(const StepArgs& s, const LayerW& w, int layer, int n, 
 // measured slower) -- except W1/W3, whose tiled kernel reads each weight once
 // for all 64 items.  false: the tiled kernel runs instead.
 constexpr int kLoopRt = 4, kLoopMaxs = 2;
+
+// The device's compute units (cached per device; 256 if the query fails).
+static int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cached[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// Blocks of a long-row launch with rt row tiles per wave (launch_sk_one's grid).
+static int loop_blocks(int nt, int n, int rt) { return ((nt + rt - 1) / rt + 7) / 8 * 8 * ((n + 15) / 16); }
+
+// The long-row loop takes 6 row tiles per wave instead of kLoopRt when that
+// leaves fewer rounds of blocks over the CUs times tiles per block (a
+// block's time grows with its tiles): at the 8B shape, Q/K/V's 384 tiles at
+// 64 items make 384 blocks with 4 (two rounds on 256 CUs) and 256 with 6
+// (one), 692.7 -> 660.2 ms per 4096-token batched prefill (3 tiles, 512
+// blocks: 675.5 ms); W2 and Wo, 256 tiles, keep 4.
+static bool loop_six(int nt, int n) {
+    const int cus = cu_count();
+    const int r4 = (loop_blocks(nt, n, kLoopRt) + cus - 1) / cus, r6 = (loop_blocks(nt, n, 6) + cus - 1) / cus;
+    return r6 * 6 < r4 * kLoopRt;
+}
 template <int KIND>
 static bool launch_sk(const StepArgs& s, const LayerW& w, int layer, int n, int ident, hipStream_t st) {
     int K = 0, N = 0;
@@ -963,7 +992,10 @@ static bool launch_sk(const StepArgs& s, const LayerW& w, int layer, int n, int 
     if constexpr (KIND == MM_W13) {
         return false;
     } else {
-        launch_sk_one<KIND, kLoopMaxs, true, 4, kLoopRt>(s, w, layer, n, ident, nt, st);
+        if (loop_six(nt, n))
+            launch_sk_one<KIND, kLoopMaxs, true, 4, 6>(s, w, layer, n, ident, nt, st);
+        else
+            launch_sk_one<KIND, kLoopMaxs, true, 4, kLoopRt>(s, w, layer, n, ident, nt, st);
         return true;
     }
 }

@@ -384,6 +384,22 @@ def test_batched_mfma_projections_match_oracle(B, shape, std, mm_kernel):
     compare(shape, arena, prompts, 3, 64, f"mfma B={B}")
 
 
+def test_batched_mfma_long_rows_six_tiles_per_wave():
+    """Q/K/V rows of 1344 values (the long-row loop) over (64 + 2 * 16) heads
+    of 64, 384 row tiles: at 64 items the loop takes 6 row tiles per wave
+    (256 blocks) where 4 would give 384 blocks, two rounds of a 256-CU
+    device; Wo (rows of 4096) and W2 keep 4.  64 ragged sequences against
+    the oracle, weights drawn with the six-tile shape's spread of 0.05."""
+    shape = synth.small_shape(dim=1344, n_heads=64, n_kv_heads=16, head_dim=64, hidden_dim=1344, vocab_size=512,
+                              weight_dtype=synth.BF16)
+    arena = synth.make_arena(shape, 12, std=0.05, gain_sigma=0.1)
+    rng = np.random.default_rng(64)
+    lens = rng.integers(1, 40, size=64)
+    prompts = [synth.random_tokens(900 + b, int(n), shape.vocab_size) for b, n in enumerate(lens)]
+    _say(f"six row tiles per wave: B=64, Q/K/V tiles {(64 + 32) * 64 // 16}")
+    compare(shape, arena, prompts, 3, 64, "mfma long rows, 6 tiles per wave", fast=True)
+
+
 @pytest.mark.parametrize("D,H,Hkv", [(64, 2, 2), (64, 4, 2), (64, 6, 2), (64, 8, 2), (128, 4, 1)],
                          ids=["d64-rep1", "d64-rep2", "d64-rep3", "d64-rep4", "d128-rep4"])
 @pytest.mark.parametrize("kernel", ["dpp", "shfl"])
