@@ -1287,6 +1287,48 @@ __global__ __launch_bounds__(64) void k_attn_merge(StepArgs s) {
     for (int k = 0; k < DPL; k++) out[64 * k] = acc[k] / L;
 }
 
+// The same merge for up to 2 * NCL chunks when few (item, head) pairs share
+// the launch (the batch-1 decode of a long context): one wave per (pair, 32
+// dims), its lanes two chunk groups of those 32 dims, lane (g, e) holding
+// dim e of chunks g, g + 2, ... .  Every slot is loaded in one round without
+// waiting for the item's position (slots past its chunk count are left out
+// by selects); max, weights and sums then cross the two groups with one lane
+// exchange each.  No LDS and no barrier.
+constexpr int kMergeLongNcl = 40;
+template <int D, int NCL>
+__global__ __launch_bounds__(64) void k_attn_merge_long(StepArgs s) {
+    constexpr int QD = D / 32;  // 32-dim blocks per head
+    const int pair = blockIdx.x / QD, item = pair / s.H, lane = threadIdx.x;
+    const int g = lane >> 5, e = (blockIdx.x % QD) * 32 + (lane & 31);
+    const int S = s.n_chunks;
+    const size_t base = static_cast<size_t>(pair) * S;  // (item * H + h) * S
+    const float2* ml = reinterpret_cast<const float2*>(s.part_ml) + base;
+    const float* po = s.part_o + base * D + e;
+    float2 v[NCL];
+    float o[NCL];
+#pragma unroll
+    for (int i = 0; i < NCL; i++) {
+        const int c = min(g + 2 * i, S - 1);
+        v[i] = ml[c];
+        o[i] = po[static_cast<size_t>(c) * D];
+    }
+    const int ns = (s.pos[item] + kChunk) / kChunk;  // chunks of this item's n = pos + 1 positions
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NCL; i++) M = g + 2 * i < ns ? fmaxf(M, v[i].x) : M;
+    M = fmaxf(M, __shfl_xor(M, 32));
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCL; i++) {
+        const float wv = g + 2 * i < ns ? __expf(v[i].x - M) : 0.f;
+        L = g + 2 * i < ns ? fmaf(wv, v[i].y, L) : L;
+        acc = g + 2 * i < ns ? fmaf(wv, o[i], acc) : acc;
+    }
+    L += __shfl_xor(L, 32);
+    acc += __shfl_xor(acc, 32);
+    if (g == 0) s.o[static_cast<size_t>(pair) * D + e] = acc / L;
+}
+
 // max_chunks: the most chunks any item of the launch has as the host knows
 // it (s.n_chunks when it does not); it sizes each thread's batch of chunk
 // partials, and an item with more is still merged, in further batches.
@@ -1296,6 +1338,12 @@ static hipError_t launch_combine(const StepArgs& s, int n_items, hipStream_t st,
         const dim3 grid(s.H * n_items);
         if (s.D == 64) hipLaunchKernelGGL(k_attn_merge<64>, grid, dim3(64), 0, st, s);
         else hipLaunchKernelGGL(k_attn_merge<128>, grid, dim3(64), 0, st, s);
+        return hipGetLastError();
+    }
+    if (s.H * n_items < 128 && s.n_chunks <= 2 * kMergeLongNcl && (s.D == 64 || s.D == 128)) {
+        const dim3 grid(s.H * n_items * (s.D / 32));
+        if (s.D == 64) hipLaunchKernelGGL((k_attn_merge_long<64, kMergeLongNcl>), grid, dim3(64), 0, st, s);
+        else hipLaunchKernelGGL((k_attn_merge_long<128, kMergeLongNcl>), grid, dim3(64), 0, st, s);
         return hipGetLastError();
     }
     const int split = s.H * n_items < 128 && s.D >= 128 ? 4 : 1;  // few heads: each head's dims over 4 blocks

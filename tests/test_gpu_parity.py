@@ -432,6 +432,9 @@ LONG_ATTN = {
     # next XCD), the 7 past the cache returning at once; lengths reach every
     # chunk from the first to the last, each sequence ragged in its last
     "d64-b6-T640-grid17": (64, 6, 2, [600, 530, 70, 260, 129, 3], 640),
+    # head_dim 64 with 32 chunk slots and 8 (sequence, head) pairs: the
+    # one-wave merge of up to 80 chunks, a sequence short of half of them
+    "d64-b2-T2048-merge32": (64, 4, 2, [1500, 700], 2048),
 }
 
 
